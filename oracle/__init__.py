@@ -1,0 +1,15 @@
+"""TEST INFRASTRUCTURE ONLY -- the fp64 CPU oracle of the gated delta rule.
+
+Nothing in the product package imports this; only tests, the smoke check
+and the CPU-baseline leg of the benchmark may.  It shares no code with the
+HIP path.
+
+  recurrent_forward / recurrent_step : the definition, token by token
+      (C, fp64; gdn_recurrence.c)
+  chunked_forward  : the chunked UT form with its intermediates (numpy fp64)
+  brute_force_forward, wy_ungated : explicit transition products and WY
+      recursions, used to pin the two above on tiny inputs.
+"""
+from .recurrence import recurrent_forward, recurrent_step, as_f64  # noqa: F401
+from .chunked import chunked_forward  # noqa: F401
+from .brute import brute_force_forward, wy_ungated, transition  # noqa: F401
