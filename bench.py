@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunked gated delta rule forward on one MI355X.
+
+A step is one pass of the whole prefill path (the chunk table for packed
+input, the intra-chunk stage and the state pass with the fused output) over
+the GDN workload B=4, T=4096, H=16, d_k=d_v=128, chunk 64, bf16 q/k/v with
+fp32 beta, gates and states, inputs resident in HBM.  `value` is tokens/s
+(B*T tokens per step).  The same run also times each kernel with HIP events,
+the decode step (256 sequences x 32 heads, fp32 state in place, 64 steps),
+and the fp64 CPU oracle on the host cores.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-decode]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+import gdn_synth  # noqa: E402
+
+# MI355X published peaks
+HBM_PEAK = 8.0e12            # bytes/s
+BF16_PEAK = 2516.6e12        # dense MFMA flop/s (256 CU x 2.4 GHz x 4096)
+METRIC = "GDN chunked-prefill tokens/s + % MFMA peak (H=16,d=128,T=4096); decode % HBM peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_bytes(spec, n_seqs):
+    """Algorithmic HBM bytes of one prefill pass, split by the kernel that
+    must move them: the intra-chunk stage reads q, k, v, beta, g; the state
+    pass writes o and reads h0 / writes ht."""
+    es = 2 if spec.dtype == "bf16" else 4
+    th = spec.B * spec.T * spec.H
+    gate = 4 * (spec.K if spec.gate == "per_key" else 1)
+    intra = th * ((2 * spec.K + spec.V) * es + 4 + gate)
+    state = 4 * spec.K * spec.V * spec.H * n_seqs
+    scan = th * spec.V * es + state * (2 if spec.h0_std is not None else 1)
+    return intra, scan
+
+
+def events_time(fn, reps):
+    """Average duration of fn() over reps back-to-back launches, from HIP
+    events recorded on the current stream (the stream the kernels use)."""
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / 1e3 / reps
+
+
+def bench_prefill(args, gdn):
+    spec = gdn_synth.PREFILL[1]
+    log("generating", spec.name)
+    d = gdn_synth.make_prefill(spec, 1)
+    dev = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    q, k, v, beta, g, h0 = (dev[n] for n in ("q", "k", "v", "beta", "g", "h0"))
+    o = torch.empty_like(v)
+    ht = torch.empty_like(h0)
+    desc = gdn.fwd_desc(q, v, "scalar", 64, d["scale"])
+    ws = torch.empty(gdn.workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+
+    def step():
+        gdn.chunk_fwd(q, k, v, beta, g, d["scale"], h0=h0, o=o, ht=ht, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    log("prefill step %.1f us" % (dt * 1e6))
+
+    # per-kernel durations (HIP events on the launch stream)
+    reps = max(args.steps, 10)
+    t_intra = events_time(lambda: gdn.chunk_intra(q, k, v, beta, g, d["scale"],
+                                                  store_ainv=False, workspace=ws), reps)
+    t_scan = events_time(lambda: gdn.chunk_scan(desc, ws, o, h0=h0, ht=ht), reps)
+    log("intra %.1f us, scan %.1f us" % (t_intra * 1e6, t_scan * 1e6))
+
+    b_intra, b_scan = prefill_bytes(spec, spec.B)
+    th = spec.B * spec.T * spec.H
+    flops = gdn_synth.flops_per_token_head(spec.K, spec.V, spec.chunk) * th
+    kernels = {
+        "intra_kernel": {"us": t_intra * 1e6, "alg_bytes": b_intra,
+                         "GBps": b_intra / t_intra / 1e9},
+        "scan_kernel": {"us": t_scan * 1e6, "alg_bytes": b_scan, "GBps": b_scan / t_scan / 1e9},
+    }
+    dom, t_dom, b_dom = (("intra_kernel", t_intra, b_intra) if t_intra >= t_scan
+                         else ("scan_kernel", t_scan, b_scan))
+    traffic = None
+    tpath = os.path.join(HERE, "profiles", "traffic.json")
+    if os.path.exists(tpath):
+        tr = json.load(open(tpath)).get(dom)
+        if tr:
+            traffic = tr.get("bytes_per_launch")
+    roof = {"bound": "hbm", "kernel": dom, "achieved": b_dom / t_dom / 1e9, "peak": HBM_PEAK / 1e9,
+            "unit": "GB/s", "frac": b_dom / t_dom / HBM_PEAK, "traffic": traffic}
+    path = {"alg_bytes": b_intra + b_scan, "GBps": (b_intra + b_scan) / dt / 1e9,
+            "frac_hbm": (b_intra + b_scan) / dt / HBM_PEAK,
+            "alg_flops": flops, "TFLOPs": flops / dt / 1e12, "frac_mfma_bf16": flops / dt / BF16_PEAK}
+    return spec, dt, roof, path, kernels, d
+
+
+def bench_decode(args, gdn):
+    spec = gdn_synth.DECODE[4]
+    log("generating", spec.name)
+    d = gdn_synth.make_decode(spec, 4)
+    x = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    state = x["state"]
+    o = torch.empty((spec.N, spec.H, spec.V), dtype=x["q"].dtype, device="cuda")
+
+    def run_steps():
+        for s in range(spec.steps):
+            gdn.recurrent_step(x["q"][s], x["k"][s], x["v"][s], x["beta"][s], x["g"][s], state,
+                               d["scale"], o=o)
+
+    t = events_time(run_steps, 1) / spec.steps
+    es = 2 if spec.dtype == "bf16" else 4
+    pairs = spec.N * spec.H
+    gate = 4 * (spec.K if spec.gate == "per_key" else 1)
+    step_bytes = pairs * (2 * 4 * spec.K * spec.V + (2 * spec.K + 2 * spec.V) * es + 4 + gate)
+    log("decode step %.1f us" % (t * 1e6))
+    return {"workload": spec.name, "us_per_step": t * 1e6, "steps": spec.steps,
+            "tokens_per_s": spec.N / t,
+            "roofline": {"bound": "hbm", "kernel": "step_kernel",
+                         "achieved": step_bytes / t / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                         "frac": step_bytes / t / HBM_PEAK, "alg_bytes": step_bytes}}
+
+
+def cpu_baseline(d, min_s=10.0):
+    import oracle
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    cores = min(cores, 16)
+    args = [oracle.as_f64(d[n]) for n in ("q", "k", "v", "beta", "g")]
+    h0 = oracle.as_f64(d["h0"])
+    B, T = d["q"].shape[:2]
+    done, t0 = 0, time.perf_counter()
+    while True:
+        oracle.recurrent_forward(*args, d["scale"], h0=h0, threads=cores)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= min_s or el / done * (done + 1) > 30.0:
+            break
+    return {"value": done * B * T / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "the whole workload (B=4, T=4096, H=16, d=128) run %d times by the fp64 "
+                      "token recurrence, %.1f s wall" % (done, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import gated_delta_rule_14_amd as gdn
+    gdn.load()
+    torch.cuda.init()
+    spec, dt, roof, path, kernels, d = bench_prefill(args, gdn)
+    decode = None if args.no_decode else bench_decode(args, gdn)
+    cpu = None if args.no_cpu else cpu_baseline(d)
+    line = {
+        "metric": METRIC,
+        "value": spec.B * spec.T / dt,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": dt * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "B": spec.B, "T": spec.T, "H": spec.H, "K": spec.K,
+                   "V": spec.V, "chunk": spec.chunk, "gate": spec.gate, "h0": "N(0,0.02^2)"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "path": path,
+        "mfma_pct_of_bf16_peak": 100.0 * path["frac_mfma_bf16"],
+        "kernels": kernels,
+        "decode": decode,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,255 @@
+"""ctypes binding of libgdn.so (include/gdn.h): argument marshalling only.
+
+Tensors are PyTorch device tensors (PyTorch provides memory and streams);
+every step of the computation runs in the HIP kernels behind the C ABI.
+There is no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdn.so")
+ABI_VERSION = 1
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+GATE_SCALAR, GATE_PER_KEY = 0, 1
+STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE", 3: "GDN_ERR_BAD_DTYPE",
+          4: "GDN_ERR_UNSUPPORTED", 5: "GDN_ERR_WORKSPACE_TOO_SMALL", 6: "GDN_ERR_MISALIGNED",
+          7: "GDN_ERR_HIP"}
+EXPORTS = sorted(["gdn_abi_version", "gdn_status_str", "gdn_last_error",
+                  "gdn_chunk_fwd_workspace", "gdn_chunk_fwd", "gdn_workspace_layout_of",
+                  "gdn_chunk_intra", "gdn_chunk_scan", "gdn_recurrent_step"])
+INTRA_STORE_AINV = 1
+
+
+class FwdDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seq_len", ctypes.c_int64),
+                ("num_heads", ctypes.c_int64), ("key_dim", ctypes.c_int64),
+                ("value_dim", ctypes.c_int64), ("num_seqs", ctypes.c_int64),
+                ("chunk", ctypes.c_int32), ("qkv_dtype", ctypes.c_int32),
+                ("gate", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class StepDesc(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int64), ("num_heads", ctypes.c_int64),
+                ("key_dim", ctypes.c_int64), ("value_dim", ctypes.c_int64),
+                ("qkv_dtype", ctypes.c_int32), ("gate", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+class WorkspaceLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in
+                ("gcum", "w", "u", "qs", "kt", "aqk", "ainv", "chunks", "seqs", "total")] + \
+               [("max_chunks", ctypes.c_int64)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__("%s: %s" % (STATUS.get(status, str(status)), detail))
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libgdn.so once; raise if it is missing or of another ABI."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libgdn.so not built (%s): run `python -m gated_delta_rule_14_amd.build`"
+                           % path)
+    lib = ctypes.CDLL(path)
+    P, S = ctypes.c_void_p, ctypes.c_int32
+    lib.gdn_abi_version.restype = ctypes.c_int
+    lib.gdn_status_str.restype = ctypes.c_char_p
+    lib.gdn_status_str.argtypes = [S]
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_chunk_fwd_workspace.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdn_chunk_fwd_workspace.restype = S
+    lib.gdn_workspace_layout_of.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(WorkspaceLayout)]
+    lib.gdn_workspace_layout_of.restype = S
+    lib.gdn_chunk_fwd.argtypes = [ctypes.POINTER(FwdDesc), P, P, P, P, P, P, P, P, P, P,
+                                  ctypes.c_size_t, P]
+    lib.gdn_chunk_fwd.restype = S
+    lib.gdn_chunk_intra.argtypes = [ctypes.POINTER(FwdDesc), P, P, P, P, P, P, P,
+                                    ctypes.c_size_t, ctypes.c_int32, P]
+    lib.gdn_chunk_intra.restype = S
+    lib.gdn_chunk_scan.argtypes = [ctypes.POINTER(FwdDesc), P, P, P, P, P, ctypes.c_size_t, P]
+    lib.gdn_chunk_scan.restype = S
+    lib.gdn_recurrent_step.argtypes = [ctypes.POINTER(StepDesc), P, P, P, P, P, P, P, P]
+    lib.gdn_recurrent_step.restype = S
+    v = lib.gdn_abi_version()
+    if v != ABI_VERSION:
+        raise RuntimeError("libgdn.so ABI %d, binding expects %d" % (v, ABI_VERSION))
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise GdnError(status, _lib.gdn_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError("q/k/v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _need(t, name, dtype=None):
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+
+
+def fwd_desc(q, v, gate="scalar", chunk=64, scale=None, num_seqs=0):
+    B, T, H, K = q.shape
+    return FwdDesc(B, T, H, K, v.shape[-1], num_seqs, chunk, _dtype_code(q),
+                   GATE_PER_KEY if gate == "per_key" else GATE_SCALAR,
+                   float(K ** -0.5 if scale is None else scale))
+
+
+def workspace_layout(desc: FwdDesc) -> WorkspaceLayout:
+    lib = load()
+    out = WorkspaceLayout()
+    _check(lib.gdn_workspace_layout_of(ctypes.byref(desc), ctypes.byref(out)))
+    return out
+
+
+def workspace_bytes(desc: FwdDesc) -> int:
+    lib = load()
+    n = ctypes.c_size_t()
+    _check(lib.gdn_chunk_fwd_workspace(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def _inputs(q, k, v, beta, g, cu_seqlens, gate):
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, q.dtype)
+    _need(beta, "beta", torch.float32)
+    _need(g, "g", torch.float32)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int64)
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or beta.shape != q.shape[:3]:
+        raise ValueError("shape mismatch among q, k, v, beta")
+    want_g = q.shape if gate == "per_key" else q.shape[:3]
+    if tuple(g.shape) != tuple(want_g):
+        raise ValueError("g must have shape %s for gate=%s" % (tuple(want_g), gate))
+
+
+def chunk_fwd(q, k, v, beta, g, scale=None, h0=None, cu_seqlens=None, chunk=64,
+              gate="scalar", output_final_state=True, workspace=None, o=None, ht=None,
+              stream=None):
+    """gdn_chunk_fwd: returns (o, ht) (ht is None unless output_final_state)."""
+    lib = load()
+    _inputs(q, k, v, beta, g, cu_seqlens, gate)
+    N = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+    desc = fwd_desc(q, v, gate, chunk, scale, 0 if cu_seqlens is None else N)
+    H, K, V = q.shape[2], q.shape[3], v.shape[3]
+    if h0 is not None:
+        _need(h0, "h0", torch.float32)
+        if tuple(h0.shape) != (N, H, K, V):
+            raise ValueError("h0 must have shape %s" % ((N, H, K, V),))
+    if o is None:
+        o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+    if output_final_state and ht is None:
+        ht = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device)
+    nbytes = workspace_bytes(desc)
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _check(lib.gdn_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                             _ptr(h0), _ptr(cu_seqlens), _ptr(o),
+                             _ptr(ht) if output_final_state else None, _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, (ht if output_final_state else None)
+
+
+def chunk_intra(q, k, v, beta, g, scale=None, cu_seqlens=None, chunk=64, gate="scalar",
+                store_ainv=True, workspace=None, stream=None):
+    """gdn_chunk_intra: the intra-chunk stage alone.  Returns a dict of views
+    into the workspace: gcum, w, u, qs, kt, aqk, ainv, max_chunks, workspace."""
+    lib = load()
+    _inputs(q, k, v, beta, g, cu_seqlens, gate)
+    N = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+    desc = fwd_desc(q, v, gate, chunk, scale, 0 if cu_seqlens is None else N)
+    L = workspace_layout(desc)
+    if workspace is None or workspace.numel() * workspace.element_size() < L.total:
+        workspace = torch.zeros(L.total, dtype=torch.uint8, device=q.device)
+    ws = workspace
+    _check(lib.gdn_chunk_intra(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                               _ptr(g), _ptr(cu_seqlens), _ptr(ws),
+                               ws.numel() * ws.element_size(),
+                               INTRA_STORE_AINV if store_ainv else 0, _stream(stream)))
+    H, K, V, C, mc = q.shape[2], q.shape[3], v.shape[3], chunk, L.max_chunks
+
+    def view(off, dtype, shape):
+        n = 1
+        for s_ in shape:
+            n *= s_
+        es = torch.empty(0, dtype=dtype).element_size()
+        return ws[off:off + n * es].view(dtype).view(*shape)
+    gshape = (H, mc, C, K) if gate == "per_key" else (H, mc, C)
+    return dict(gcum=view(L.gcum, torch.float32, gshape),
+                w=view(L.w, q.dtype, (H, mc, C, K)), u=view(L.u, q.dtype, (H, mc, C, V)),
+                qs=view(L.qs, q.dtype, (H, mc, C, K)), kt=view(L.kt, q.dtype, (H, mc, K, C)),
+                aqk=view(L.aqk, q.dtype, (H, mc, C, C)),
+                ainv=view(L.ainv, torch.float32, (H, mc, C, C)), max_chunks=mc,
+                workspace=ws, desc=desc)
+
+
+def chunk_scan(desc, workspace, o, h0=None, ht=None, cu_seqlens=None, stream=None):
+    """gdn_chunk_scan: the state pass on a workspace prepared by chunk_intra
+    for the same descriptor and inputs.  Writes o (and ht if given)."""
+    lib = load()
+    _need(o, "o")
+    _check(lib.gdn_chunk_scan(ctypes.byref(desc), _ptr(h0), _ptr(cu_seqlens), _ptr(o), _ptr(ht),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(stream)))
+    return o, ht
+
+
+def recurrent_step(q, k, v, beta, g, state, scale=None, gate="scalar", o=None, stream=None):
+    """gdn_recurrent_step: one token for N sequences; state updated in place.
+    q, k [N, H, K]; v [N, H, V]; beta [N, H]; g [N, H] or [N, H, K]."""
+    lib = load()
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, q.dtype)
+    _need(beta, "beta", torch.float32)
+    _need(g, "g", torch.float32)
+    _need(state, "state", torch.float32)
+    N, H, K = q.shape
+    V = v.shape[-1]
+    if tuple(state.shape) != (N, H, K, V):
+        raise ValueError("state must have shape %s" % ((N, H, K, V),))
+    want_g = (N, H, K) if gate == "per_key" else (N, H)
+    if tuple(g.shape) != want_g or tuple(beta.shape) != (N, H):
+        raise ValueError("beta/g shape mismatch")
+    if o is None:
+        o = torch.empty((N, H, V), dtype=q.dtype, device=q.device)
+    desc = StepDesc(N, H, K, V, _dtype_code(q),
+                    GATE_PER_KEY if gate == "per_key" else GATE_SCALAR,
+                    float(K ** -0.5 if scale is None else scale))
+    _check(lib.gdn_recurrent_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                  _ptr(g), _ptr(state), _ptr(o), _stream(stream)))
+    return o

@@ -1,0 +1,347 @@
+// Host side of the C ABI declared in include/gdn.h: argument checks,
+// workspace layout and the kernel launches.  Nothing here allocates memory or
+// synchronises; every launch goes to the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/gdn.h"
+#include "gdn_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512];
+
+gdn_status fail(gdn_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+gdn_status fail(gdn_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+gdn_status ok() {
+    g_err[0] = 0;
+    return GDN_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+bool aligned8(const void* p) { return ((uintptr_t)p & 7u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool dim_ok(int64_t d) { return d == 64 || d == 128; }
+
+gdn_status check_desc(const gdn_fwd_desc* d, bool packed) {
+    if (!d) return fail(GDN_ERR_NULL_ARG, "desc is NULL");
+    if (d->qkv_dtype != GDN_DTYPE_F32 && d->qkv_dtype != GDN_DTYPE_BF16)
+        return fail(GDN_ERR_BAD_DTYPE, "qkv_dtype %d", d->qkv_dtype);
+    if (d->gate != GDN_GATE_SCALAR && d->gate != GDN_GATE_PER_KEY)
+        return fail(GDN_ERR_BAD_DTYPE, "gate %d", d->gate);
+    if (d->batch <= 0 || d->seq_len < 0 || d->num_heads <= 0 || d->key_dim <= 0 ||
+        d->value_dim <= 0)
+        return fail(GDN_ERR_BAD_SHAPE, "non-positive size (B=%lld T=%lld H=%lld K=%lld V=%lld)",
+                    (long long)d->batch, (long long)d->seq_len, (long long)d->num_heads,
+                    (long long)d->key_dim, (long long)d->value_dim);
+    if (packed && d->batch != 1)
+        return fail(GDN_ERR_BAD_SHAPE, "packed sequences need batch == 1 (got %lld)",
+                    (long long)d->batch);
+    if (packed && d->num_seqs <= 0)
+        return fail(GDN_ERR_BAD_SHAPE, "packed sequences need num_seqs > 0");
+    if (d->batch * d->seq_len >= (int64_t)1 << 31)
+        return fail(GDN_ERR_BAD_SHAPE, "B*T must be below 2^31");
+    if (d->num_heads > 65535) return fail(GDN_ERR_BAD_SHAPE, "num_heads above 65535");
+    if (d->chunk != 64)
+        return fail(GDN_ERR_UNSUPPORTED, "chunk %d (this build implements 64)", d->chunk);
+    if (!dim_ok(d->key_dim) || !dim_ok(d->value_dim))
+        return fail(GDN_ERR_UNSUPPORTED, "K=%lld V=%lld (supported: 64, 128)",
+                    (long long)d->key_dim, (long long)d->value_dim);
+    if (d->qkv_dtype == GDN_DTYPE_F32 && d->gate == GDN_GATE_PER_KEY && d->key_dim == 128)
+        return fail(GDN_ERR_UNSUPPORTED, "fp32 q/k/v with the per-key gate needs K = 64");
+    return GDN_OK;
+}
+
+int64_t max_chunks_of(const gdn_fwd_desc* d, bool packed) {
+    const int64_t nt = (d->seq_len + d->chunk - 1) / d->chunk;
+    return packed ? nt + d->num_seqs : d->batch * nt;
+}
+
+void layout(const gdn_fwd_desc* d, bool packed, gdn_workspace_layout* L) {
+    const int64_t mc = max_chunks_of(d, packed);
+    const int64_t H = d->num_heads, K = d->key_dim, V = d->value_dim, C = d->chunk;
+    const size_t es = d->qkv_dtype == GDN_DTYPE_BF16 ? 2 : 4;
+    const size_t blocks = (size_t)(H * mc);
+    size_t off = 0;
+    L->gcum = off;
+    off = align256(off + blocks * C * (d->gate == GDN_GATE_PER_KEY ? K : 1) * 4);
+    L->w = off;
+    off = align256(off + blocks * C * K * es);
+    L->u = off;
+    off = align256(off + blocks * C * V * es);
+    L->qs = off;
+    off = align256(off + blocks * C * K * es);
+    L->kt = off;
+    off = align256(off + blocks * K * C * es);
+    L->aqk = off;
+    off = align256(off + blocks * C * C * es);
+    L->ainv = off;
+    off = align256(off + blocks * C * C * 4);
+    L->chunks = off;
+    L->seqs = off + (size_t)mc * 16;
+    off = align256(off + (size_t)mc * 16 + (size_t)(packed ? d->num_seqs : 0) * 16);
+    L->total = off;
+    L->max_chunks = mc;
+}
+
+gdn_status hip_fail(hipError_t e, const char* what) {
+    return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct Prepared {
+    gdn::ChunkMap map;
+    gdn::ChunkWs ws;
+};
+
+gdn_status prepare(const gdn_fwd_desc* d, const void* q, const void* k, const void* v,
+                   const float* beta, const float* g, const int64_t* cu_seqlens, void* workspace,
+                   size_t workspace_bytes, bool want_ainv, hipStream_t stream, Prepared* P) {
+    const bool packed = cu_seqlens != nullptr;
+    gdn_status s = check_desc(d, packed);
+    if (s != GDN_OK) return s;
+    if (!packed && d->num_seqs != 0)
+        return fail(GDN_ERR_BAD_SHAPE, "num_seqs must be 0 without cu_seqlens");
+    if (!q || !k || !v || !beta || !g || !workspace)
+        return fail(GDN_ERR_NULL_ARG, "q, k, v, beta, g and workspace are required");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(beta) || !aligned4(g) ||
+        !aligned8(cu_seqlens))
+        return fail(GDN_ERR_MISALIGNED,
+                    "q, k, v need 16-byte, beta and g 4-byte, cu_seqlens 8-byte alignment");
+    if (((uintptr_t)workspace & 255u) != 0)
+        return fail(GDN_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    gdn_workspace_layout L;
+    layout(d, packed, &L);
+    if (workspace_bytes < L.total)
+        return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes,
+                    L.total);
+    char* ws = static_cast<char*>(workspace);
+    P->ws.gcum = reinterpret_cast<float*>(ws + L.gcum);
+    P->ws.w = ws + L.w;
+    P->ws.u = ws + L.u;
+    P->ws.aqk = ws + L.aqk;
+    P->ws.ainv = want_ainv ? reinterpret_cast<float*>(ws + L.ainv) : nullptr;
+    P->ws.qs = ws + L.qs;
+    P->ws.kt = ws + L.kt;
+    P->map.max_chunks = L.max_chunks;
+    P->map.T = d->seq_len;
+    P->map.nt = (d->seq_len + d->chunk - 1) / d->chunk;
+    if (packed) {
+        P->map.table = reinterpret_cast<const int4*>(ws + L.chunks);
+        P->map.seqs = reinterpret_cast<const int4*>(ws + L.seqs);
+        gdn::TableLaunch t;
+        t.cu_seqlens = cu_seqlens;
+        t.N = d->num_seqs;
+        t.T = d->seq_len;
+        t.C = d->chunk;
+        t.table = const_cast<int4*>(P->map.table);
+        t.seqs = const_cast<int4*>(P->map.seqs);
+        t.max_chunks = L.max_chunks;
+        t.stream = stream;
+        hipError_t e = gdn::launch_table(t);
+        if (e != hipSuccess) return hip_fail(e, "chunk table launch");
+    } else {
+        P->map.table = nullptr;
+        P->map.seqs = nullptr;
+    }
+    if (L.max_chunks > 0 && d->seq_len > 0) {
+        gdn::IntraLaunch a;
+        a.q = q;
+        a.k = k;
+        a.v = v;
+        a.beta = beta;
+        a.g = g;
+        a.map = P->map;
+        a.ws = P->ws;
+        a.H = d->num_heads;
+        a.K = (int)d->key_dim;
+        a.V = (int)d->value_dim;
+        a.C = d->chunk;
+        a.scale = d->scale;
+        a.bf16 = d->qkv_dtype == GDN_DTYPE_BF16;
+        a.per_key = d->gate == GDN_GATE_PER_KEY;
+        a.stream = stream;
+        hipError_t e = gdn::launch_intra(a);
+        if (e != hipSuccess) return hip_fail(e, "intra-chunk launch");
+    }
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_str(gdn_status s) {
+    switch (s) {
+        case GDN_OK: return "GDN_OK";
+        case GDN_ERR_NULL_ARG: return "GDN_ERR_NULL_ARG";
+        case GDN_ERR_BAD_SHAPE: return "GDN_ERR_BAD_SHAPE";
+        case GDN_ERR_BAD_DTYPE: return "GDN_ERR_BAD_DTYPE";
+        case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+        case GDN_ERR_WORKSPACE_TOO_SMALL: return "GDN_ERR_WORKSPACE_TOO_SMALL";
+        case GDN_ERR_MISALIGNED: return "GDN_ERR_MISALIGNED";
+        case GDN_ERR_HIP: return "GDN_ERR_HIP";
+        default: return "GDN_ERR_UNKNOWN";
+    }
+}
+
+const char* gdn_last_error(void) { return g_err; }
+
+gdn_status gdn_workspace_layout_of(const gdn_fwd_desc* d, gdn_workspace_layout* out) {
+    if (!out) return fail(GDN_ERR_NULL_ARG, "out is NULL");
+    const bool packed = d && d->num_seqs > 0;
+    gdn_status s = check_desc(d, packed);
+    if (s != GDN_OK) return s;
+    layout(d, packed, out);
+    return ok();
+}
+
+gdn_status gdn_chunk_fwd_workspace(const gdn_fwd_desc* d, size_t* bytes) {
+    if (!bytes) return fail(GDN_ERR_NULL_ARG, "bytes is NULL");
+    gdn_workspace_layout L;
+    gdn_status s = gdn_workspace_layout_of(d, &L);
+    if (s != GDN_OK) return s;
+    *bytes = L.total;
+    return ok();
+}
+
+gdn_status gdn_chunk_intra(const gdn_fwd_desc* d, const void* q, const void* k, const void* v,
+                           const float* beta, const float* g, const int64_t* cu_seqlens,
+                           void* workspace, size_t workspace_bytes, int32_t flags, void* stream) {
+    Prepared P;
+    gdn_status s = prepare(d, q, k, v, beta, g, cu_seqlens, workspace, workspace_bytes,
+                           (flags & GDN_INTRA_STORE_AINV) != 0, static_cast<hipStream_t>(stream),
+                           &P);
+    return s == GDN_OK ? ok() : s;
+}
+
+static gdn_status scan(const gdn_fwd_desc* d, const float* h0, const int64_t* cu_seqlens,
+                       void* o, float* ht, void* workspace, size_t workspace_bytes,
+                       hipStream_t st) {
+    const bool packed = cu_seqlens != nullptr;
+    gdn_status s = check_desc(d, packed);
+    if (s != GDN_OK) return s;
+    if (!o || !workspace) return fail(GDN_ERR_NULL_ARG, "o and workspace are required");
+    if (!aligned16(o) || !aligned4(h0) || !aligned4(ht))
+        return fail(GDN_ERR_MISALIGNED, "o needs 16-byte, h0 and ht 4-byte alignment");
+    if (((uintptr_t)workspace & 255u) != 0)
+        return fail(GDN_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    gdn_workspace_layout L;
+    layout(d, packed, &L);
+    if (workspace_bytes < L.total)
+        return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes,
+                    L.total);
+    char* ws = static_cast<char*>(workspace);
+    gdn::ScanLaunch a;
+    a.map.max_chunks = L.max_chunks;
+    a.map.T = d->seq_len;
+    a.map.nt = (d->seq_len + d->chunk - 1) / d->chunk;
+    a.map.table = packed ? reinterpret_cast<const int4*>(ws + L.chunks) : nullptr;
+    a.map.seqs = packed ? reinterpret_cast<const int4*>(ws + L.seqs) : nullptr;
+    a.ws.gcum = reinterpret_cast<float*>(ws + L.gcum);
+    a.ws.w = ws + L.w;
+    a.ws.u = ws + L.u;
+    a.ws.qs = ws + L.qs;
+    a.ws.kt = ws + L.kt;
+    a.ws.aqk = ws + L.aqk;
+    a.ws.ainv = nullptr;
+    a.h0 = h0;
+    a.ht = ht;
+    a.o = o;
+    a.N = packed ? d->num_seqs : d->batch;
+    a.H = d->num_heads;
+    a.K = (int)d->key_dim;
+    a.V = (int)d->value_dim;
+    a.C = d->chunk;
+    a.bf16 = d->qkv_dtype == GDN_DTYPE_BF16;
+    a.per_key = d->gate == GDN_GATE_PER_KEY;
+    a.stream = st;
+    hipError_t e = gdn::launch_scan(a);
+    if (e != hipSuccess) return hip_fail(e, "state pass launch");
+    return ok();
+}
+
+gdn_status gdn_chunk_scan(const gdn_fwd_desc* d, const float* h0, const int64_t* cu_seqlens,
+                          void* o, float* ht, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    return scan(d, h0, cu_seqlens, o, ht, workspace, workspace_bytes,
+                static_cast<hipStream_t>(stream));
+}
+
+gdn_status gdn_chunk_fwd(const gdn_fwd_desc* d, const void* q, const void* k, const void* v,
+                         const float* beta, const float* g, const float* h0,
+                         const int64_t* cu_seqlens, void* o, float* ht, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    const bool packed = cu_seqlens != nullptr;
+    gdn_status s = check_desc(d, packed);
+    if (s != GDN_OK) return s;
+    if (!o) return fail(GDN_ERR_NULL_ARG, "o is NULL");
+    if (!aligned16(o) || !aligned4(h0) || !aligned4(ht))
+        return fail(GDN_ERR_MISALIGNED, "o needs 16-byte, h0 and ht 4-byte alignment");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    Prepared P;
+    s = prepare(d, q, k, v, beta, g, cu_seqlens, workspace, workspace_bytes, false, st, &P);
+    if (s != GDN_OK) return s;
+    return scan(d, h0, cu_seqlens, o, ht, workspace, workspace_bytes, st);
+}
+
+gdn_status gdn_recurrent_step(const gdn_step_desc* d, const void* q, const void* k,
+                              const void* v, const float* beta, const float* g, float* state,
+                              void* o, void* stream) {
+    if (!d) return fail(GDN_ERR_NULL_ARG, "desc is NULL");
+    if (d->qkv_dtype != GDN_DTYPE_F32 && d->qkv_dtype != GDN_DTYPE_BF16)
+        return fail(GDN_ERR_BAD_DTYPE, "qkv_dtype %d", d->qkv_dtype);
+    if (d->gate != GDN_GATE_SCALAR && d->gate != GDN_GATE_PER_KEY)
+        return fail(GDN_ERR_BAD_DTYPE, "gate %d", d->gate);
+    if (d->num_seqs < 0 || d->num_heads <= 0)
+        return fail(GDN_ERR_BAD_SHAPE, "N=%lld H=%lld", (long long)d->num_seqs,
+                    (long long)d->num_heads);
+    if (!dim_ok(d->key_dim) || !dim_ok(d->value_dim))
+        return fail(GDN_ERR_UNSUPPORTED, "K=%lld V=%lld (supported: 64, 128)",
+                    (long long)d->key_dim, (long long)d->value_dim);
+    if (d->num_seqs * d->num_heads >= (int64_t)1 << 31)
+        return fail(GDN_ERR_BAD_SHAPE, "N*H must be below 2^31");
+    if (!q || !k || !v || !beta || !g || !state || !o)
+        return fail(GDN_ERR_NULL_ARG, "q, k, v, beta, g, state and o are required");
+    const size_t es = d->qkv_dtype == GDN_DTYPE_BF16 ? 2 : 4;
+    if (!aligned16(state) || ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) % es ||
+        !aligned4(beta) || !aligned4(g))
+        return fail(GDN_ERR_MISALIGNED,
+                    "state needs 16-byte alignment, the others their element size");
+    if (d->num_seqs == 0) return ok();
+    gdn::StepLaunch a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.g = g;
+    a.state = state;
+    a.o = o;
+    a.scale = d->scale;
+    a.N = d->num_seqs;
+    a.H = d->num_heads;
+    a.K = (int)d->key_dim;
+    a.V = (int)d->value_dim;
+    a.bf16 = d->qkv_dtype == GDN_DTYPE_BF16;
+    a.per_key = d->gate == GDN_GATE_PER_KEY;
+    a.stream = static_cast<hipStream_t>(stream);
+    hipError_t e = gdn::launch_step(a);
+    if (e != hipSuccess) return hip_fail(e, "step launch");
+    return ok();
+}
+
+}  // extern "C"

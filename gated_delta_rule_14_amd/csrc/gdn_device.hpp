@@ -1,0 +1,186 @@
+// Device-side helpers shared by the gfx950 kernels: element types, bf16
+// conversion, the 16x16 MFMA fragments and small wave utilities.
+//
+// MFMA fragment layouts used throughout (wave64, 16x16 output tile):
+//   bf16 v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8*(l/16) + 0..7] and
+//       B[8*(l/16) + 0..7][l%16]; the f32x4 result holds C[4*(l/16) + 0..3][l%16].
+//   f32  v_mfma_f32_16x16x4_f32:   lane l holds A[l%16][l/16] and
+//       B[l/16][l%16]; the result layout is the same as above.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct bf16 {  // storage-only 16-bit brain float
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// round-to-nearest-even, NaN kept quiet
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// element traits: loads/stores of the q/k/v/o element type through float
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static constexpr int BYTES = 4;
+    __device__ __forceinline__ static float load(const float* p) { return *p; }
+    __device__ __forceinline__ static void store(float* p, float x) { *p = x; }
+};
+template <> struct Elem<bf16> {
+    static constexpr int BYTES = 2;
+    __device__ __forceinline__ static float load(const bf16* p) { return bf16_to_f32(p->bits); }
+    __device__ __forceinline__ static void store(bf16* p, float x) { p->bits = f32_to_bf16(x); }
+};
+
+// A 16-byte vector of T held in a uint4: element access and packing.
+template <typename T> struct Vec16;
+template <> struct Vec16<bf16> {
+    static constexpr int N = 8;
+    __device__ __forceinline__ static float get(const uint4& v, int e) {
+        const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+        return bf16_to_f32((uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
+    }
+    __device__ __forceinline__ static uint4 pack(const float* f) {
+        return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                          pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+    }
+};
+template <> struct Vec16<float> {
+    static constexpr int N = 4;
+    __device__ __forceinline__ static float get(const uint4& v, int e) {
+        return __uint_as_float(e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w);
+    }
+    __device__ __forceinline__ static uint4 pack(const float* f) {
+        return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                          __float_as_uint(f[3]));
+    }
+};
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// MFMA fragments.  `row` points at element (row l%16, k0) of a row-major A
+// tile, or at (col l%16, k0) of a B^T tile (B stored n-major, k contiguous);
+// load() picks this lane's k-slice.  bf16 slices are 16 bytes and must be
+// 16-byte aligned.
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16> {
+    typedef bf16x8 frag;
+    static constexpr int KSTEP = 32;  // k covered by one instruction
+    __device__ __forceinline__ static frag load(const bf16* row, int lane) {
+        return *reinterpret_cast<const bf16x8*>(row + 8 * (lane >> 4));
+    }
+    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <> struct Mma<float> {
+    typedef float frag;
+    static constexpr int KSTEP = 4;
+    __device__ __forceinline__ static frag load(const float* row, int lane) {
+        return row[lane >> 4];
+    }
+    __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+// C(16x16) += A(16 x kn) * B(kn x 16); A row-major at `a` (pitch lda), B
+// stored transposed (n-major, k contiguous) at `bt` (pitch ldb).  Pointers
+// are tile origins; kn is a multiple of Mma<T>::KSTEP.
+template <typename T>
+__device__ __forceinline__ f32x4 mma_tile(const T* a, int lda, const T* bt, int ldb, int kn,
+                                          int lane, f32x4 c) {
+    const T* ar = a + (lane & 15) * lda;
+    const T* br = bt + (lane & 15) * ldb;
+    for (int k0 = 0; k0 < kn; k0 += Mma<T>::KSTEP)
+        c = Mma<T>::mma(Mma<T>::load(ar + k0, lane), Mma<T>::load(br + k0, lane), c);
+    return c;
+}
+
+// fp32 C(16x16) += A(16 x kn) * B(kn x 16) with both A and B row-major
+// (scalar fp32 fragments can be gathered from either layout).
+__device__ __forceinline__ f32x4 mma_f32_rr(const float* a, int lda, const float* b, int ldb,
+                                            int kn, int lane, f32x4 c) {
+    const int r = lane & 15, kk = lane >> 4;
+    for (int k0 = 0; k0 < kn; k0 += 4)
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r * lda + k0 + kk], b[(k0 + kk) * ldb + r], c,
+                                                 0, 0, 0);
+    return c;
+}
+
+// Store element e (0..3) of a 16x16 accumulator: row 4*(l/16)+e, col l%16.
+__device__ __forceinline__ int acc_row(int lane, int e) { return 4 * (lane >> 4) + e; }
+__device__ __forceinline__ int acc_col(int lane) { return lane & 15; }
+
+// Write a 16x16 fp32 accumulator transposed into an n-major T buffer:
+// dst[col * ld + row].  The 4 rows a lane holds are consecutive, so this is
+// one 8-byte (bf16) or 16-byte (f32) LDS store per lane.
+__device__ __forceinline__ void store_acc_t(bf16* dst, int ld, int lane, f32x4 v) {
+    uint2 w;
+    w.x = pack_bf16x2(v[0], v[1]);
+    w.y = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<uint2*>(dst + acc_col(lane) * ld + 4 * (lane >> 4)) = w;
+}
+__device__ __forceinline__ void store_acc_t(float* dst, int ld, int lane, f32x4 v) {
+    *reinterpret_cast<float4*>(dst + acc_col(lane) * ld + 4 * (lane >> 4)) =
+        make_float4(v[0], v[1], v[2], v[3]);
+}
+// ... and row-major: dst[row * ld + col] (element stores)
+template <typename T>
+__device__ __forceinline__ void store_acc(T* dst, int ld, int lane, f32x4 v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Elem<T>::store(dst + acc_row(lane, e) * ld + acc_col(lane), v[e]);
+}
+
+// Copy a rows x cols tile between two row-major buffers with 16-byte vectors.
+// cols * sizeof(T) must be a multiple of 16; pitches are in elements.
+template <typename T>
+__device__ __forceinline__ void copy_tile(T* dst, int64_t ldd, const T* src, int64_t lds, int rows,
+                                          int cols, int tid, int nthreads) {
+    constexpr int EV = 16 / sizeof(T);
+    const int vpr = cols / EV;
+    for (int i = tid; i < rows * vpr; i += nthreads) {
+        const int r = i / vpr, cv = i - r * vpr;
+        *reinterpret_cast<uint4*>(dst + r * ldd + cv * EV) =
+            *reinterpret_cast<const uint4*>(src + r * lds + cv * EV);
+    }
+}
+
+// Wave-wide inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ float wave_incl_scan(float x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+}  // namespace gdn

@@ -1,0 +1,84 @@
+// Internal launcher interface between the host API (gdn_api.hip) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct StepLaunch {
+    const void *q, *k, *v;
+    const float *beta, *g;
+    float* state;
+    void* o;
+    float scale;
+    int64_t N, H;
+    int K, V;
+    bool bf16, per_key;
+    hipStream_t stream;
+};
+
+// Chunk bookkeeping shared by the two prefill stages.  Without packed
+// offsets, chunk c of sequence b covers tokens b*T + j*C .. (j = c % nt).
+// With packed offsets a device-built table gives (first token, count, seq).
+struct ChunkMap {
+    const int4* table;      // [max_chunks] (t0, n, seq, 0) or nullptr
+    const int4* seqs;       // [N] (t0, len, first chunk, nchunks) or nullptr
+    int64_t T;              // tokens per sequence when table == nullptr
+    int64_t nt;             // chunks per sequence when table == nullptr
+    int64_t max_chunks;     // rows of every per-chunk workspace array
+};
+
+// Per-chunk intermediates in the workspace, head-major: array[h][chunk][...].
+struct ChunkWs {
+    float* gcum;   // [H][mc][C] or [H][mc][C][K]   cumulative log2 gate
+    void* w;       // [H][mc][C][K]
+    void* u;       // [H][mc][C][V]
+    void* qs;      // [H][mc][C][K]   scale * Q * gamma
+    void* kt;      // [H][mc][K][C]   (K * gamma_C / gamma)^T
+    void* aqk;     // [H][mc][C][C]
+    float* ainv;   // [H][mc][C][C] or nullptr
+};
+
+struct IntraLaunch {
+    const void *q, *k, *v;
+    const float *beta, *g;
+    ChunkMap map;
+    ChunkWs ws;
+    int64_t H;
+    int K, V, C;
+    float scale;
+    bool bf16, per_key;
+    hipStream_t stream;
+};
+
+struct ScanLaunch {
+    ChunkMap map;
+    ChunkWs ws;
+    const float* h0;
+    float* ht;
+    void* o;
+    int64_t N, H;
+    int K, V, C;
+    bool bf16, per_key;
+    hipStream_t stream;
+};
+
+struct TableLaunch {
+    const int64_t* cu_seqlens;
+    int64_t N, T;
+    int C;
+    int4* table;
+    int4* seqs;
+    int64_t max_chunks;
+    hipStream_t stream;
+};
+
+hipError_t launch_step(const StepLaunch& a);
+hipError_t launch_table(const TableLaunch& a);
+hipError_t launch_intra(const IntraLaunch& a);
+hipError_t launch_scan(const ScanLaunch& a);
+
+}  // namespace gdn

@@ -1,0 +1,131 @@
+// k6: single-token recurrent step, state streamed from HBM once.
+//
+// Per (sequence, head) the step is ("Gated Delta Network（GDN）" §4.4,
+// eq. 12; "DeltaNet 系列线性注意力变体的推导之旅", recurrent KDA: forget,
+// predict, correct, read, in the transposed state layout h = S^T [K][V]):
+//   h' = D h              D = exp(g) (scalar gate) or Diag(exp(g_i))
+//   p  = h'^T k ,   r = beta (v - p)
+//   h  = h' + k r^T
+//   o  = h^T (scale q) = scale (h'^T q + (k . q) r)
+// The last line lets both K-reductions (p and h'^T q) read the old state in
+// the same pass, so the state is read once and written once.
+//
+// Mapping: one 256-thread workgroup per (sequence, head).  Thread t owns the
+// float4 column group t % (V/4) for K*V/1024 rows; a wave reads whole 512-byte
+// state rows, so every load and store is a coalesced 16-byte access.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+template <typename T, int K, int V, bool PER_KEY>
+__global__ __launch_bounds__(256) void step_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                   const T* __restrict__ v,
+                                                   const float* __restrict__ beta,
+                                                   const float* __restrict__ g,
+                                                   float* __restrict__ state, T* __restrict__ o,
+                                                   float scale) {
+    constexpr int CG = V / 4;          // float4 column groups
+    constexpr int RG = 256 / CG;       // row groups
+    constexpr int ROWS = K / RG;       // rows per thread
+    static_assert(RG * CG == 256 && ROWS * RG == K, "shape");
+
+    const int64_t pair = blockIdx.x;   // n * H + h
+    const int tid = threadIdx.x;
+    const int cg = tid % CG, rg = tid / CG;
+
+    __shared__ float s_k[K], s_q[K], s_d[K], s_v[V];
+    __shared__ float4 s_p[RG][CG], s_s[RG][CG];
+    __shared__ float s_kq[RG];
+
+    float4* st = reinterpret_cast<float4*>(state + pair * (int64_t)(K * V));
+    // issue the state loads first: they are the whole cost of the step
+    float4 h[ROWS];
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) h[i] = st[(rg * ROWS + i) * CG + cg];
+
+    for (int i = tid; i < K; i += 256) {
+        s_k[i] = Elem<T>::load(k + pair * K + i);
+        s_q[i] = Elem<T>::load(q + pair * K + i);
+        s_d[i] = PER_KEY ? __expf(g[pair * K + i]) : 0.f;
+    }
+    for (int i = tid; i < V; i += 256) s_v[i] = Elem<T>::load(v + pair * V + i);
+    const float dscal = PER_KEY ? 0.f : __expf(g[pair]);
+    __syncthreads();
+
+    float4 p = {0.f, 0.f, 0.f, 0.f}, s = {0.f, 0.f, 0.f, 0.f};
+    float kq = 0.f;
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {
+        const int r = rg * ROWS + i;
+        const float d = PER_KEY ? s_d[r] : dscal;
+        h[i].x *= d; h[i].y *= d; h[i].z *= d; h[i].w *= d;   // forget
+        const float kr = s_k[r], qr = s_q[r];
+        p.x += h[i].x * kr; p.y += h[i].y * kr; p.z += h[i].z * kr; p.w += h[i].w * kr;
+        s.x += h[i].x * qr; s.y += h[i].y * qr; s.z += h[i].z * qr; s.w += h[i].w * qr;
+        kq += kr * qr;
+    }
+    s_p[rg][cg] = p;
+    s_s[rg][cg] = s;
+    if (cg == 0) s_kq[rg] = kq;
+    __syncthreads();
+
+    float4 P = {0.f, 0.f, 0.f, 0.f}, S = {0.f, 0.f, 0.f, 0.f};
+    float KQ = 0.f;
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+        const float4 a = s_p[j][cg], b = s_s[j][cg];
+        P.x += a.x; P.y += a.y; P.z += a.z; P.w += a.w;
+        S.x += b.x; S.y += b.y; S.z += b.z; S.w += b.w;
+        KQ += s_kq[j];
+    }
+    const float bt = beta[pair];
+    float4 r;                                                  // correction
+    r.x = bt * (s_v[4 * cg + 0] - P.x);
+    r.y = bt * (s_v[4 * cg + 1] - P.y);
+    r.z = bt * (s_v[4 * cg + 2] - P.z);
+    r.w = bt * (s_v[4 * cg + 3] - P.w);
+
+#pragma unroll
+    for (int i = 0; i < ROWS; ++i) {                          // write
+        const float kr = s_k[rg * ROWS + i];
+        float4 x = h[i];
+        x.x += kr * r.x; x.y += kr * r.y; x.z += kr * r.z; x.w += kr * r.w;
+        st[(rg * ROWS + i) * CG + cg] = x;
+    }
+    if (rg == 0) {                                             // read
+        T* op = o + pair * V + 4 * cg;
+        Elem<T>::store(op + 0, scale * (S.x + KQ * r.x));
+        Elem<T>::store(op + 1, scale * (S.y + KQ * r.y));
+        Elem<T>::store(op + 2, scale * (S.z + KQ * r.z));
+        Elem<T>::store(op + 3, scale * (S.w + KQ * r.w));
+    }
+}
+
+template <typename T, int K, int V, bool PK>
+static hipError_t launch_step_t(const StepLaunch& a) {
+    hipLaunchKernelGGL((step_kernel<T, K, V, PK>), dim3((unsigned)(a.N * a.H)), dim3(256), 0,
+                       a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.beta, a.g,
+                       a.state, (T*)a.o, a.scale);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_step_dt(const StepLaunch& a) {
+#define GDN_STEP_CASE(KK, VV)                                                    \
+    if (a.K == KK && a.V == VV)                                                  \
+        return a.per_key ? launch_step_t<T, KK, VV, true>(a)                     \
+                         : launch_step_t<T, KK, VV, false>(a);
+    GDN_STEP_CASE(64, 64)
+    GDN_STEP_CASE(64, 128)
+    GDN_STEP_CASE(128, 64)
+    GDN_STEP_CASE(128, 128)
+#undef GDN_STEP_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_step(const StepLaunch& a) {
+    return a.bf16 ? launch_step_dt<bf16>(a) : launch_step_dt<float>(a);
+}
+
+}  // namespace gdn

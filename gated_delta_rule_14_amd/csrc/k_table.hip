@@ -1,0 +1,63 @@
+// Packed variable-length input: turn the caller's cu_seqlens into the chunk
+// table the two prefill stages walk, without a host round trip.
+//
+// Chunks restart at every sequence start and the last chunk of a sequence is
+// ragged ("Gated Delta Network（GDN）", terminology note: a chunk boundary is
+// not a sequence boundary; "阅读笔记：DeltaNet 在 FLA 中的代码实现笔记",
+// signature of the forward entry: cu_seqlens / chunk_indices).
+//
+// One workgroup.  Offsets are clamped into [0, T] (end >= start), so invalid
+// offsets can give wrong results but never an out-of-bounds access.
+//   seqs[n]  = (first token, length, first chunk, chunk count)
+//   table[c] = (first token, token count, sequence, 0); unused rows have count 0
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+__global__ __launch_bounds__(256) void table_kernel(TableLaunch a) {
+    __shared__ int64_t s_part[256];
+    __shared__ int64_t s_carry;
+    const int tid = threadIdx.x;
+    if (tid == 0) s_carry = 0;
+    __syncthreads();
+    for (int64_t base = 0; base < a.N; base += 256) {
+        const int64_t n = base + tid;
+        int64_t s = 0, len = 0, nc = 0;
+        if (n < a.N) {
+            s = min(max(a.cu_seqlens[n], (int64_t)0), a.T);
+            const int64_t e = min(max(a.cu_seqlens[n + 1], s), a.T);
+            len = e - s;
+            nc = (len + a.C - 1) / a.C;
+        }
+        s_part[tid] = nc;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {          // inclusive scan
+            const int64_t y = tid >= off ? s_part[tid - off] : 0;
+            __syncthreads();
+            s_part[tid] += y;
+            __syncthreads();
+        }
+        const int64_t first = s_carry + s_part[tid] - nc;
+        if (n < a.N) {
+            a.seqs[n] = make_int4((int)s, (int)len, (int)min(first, a.max_chunks), (int)nc);
+            for (int64_t j = 0; j < nc; ++j) {
+                const int64_t c = first + j;
+                if (c >= a.max_chunks) break;
+                a.table[c] = make_int4((int)(s + j * a.C), (int)min((int64_t)a.C, len - j * a.C),
+                                       (int)n, 0);
+            }
+        }
+        __syncthreads();
+        if (tid == 255) s_carry += s_part[255];
+        __syncthreads();
+    }
+    for (int64_t c = s_carry + tid; c < a.max_chunks; c += 256) a.table[c] = make_int4(0, 0, -1, 0);
+}
+
+hipError_t launch_table(const TableLaunch& a) {
+    hipLaunchKernelGGL(table_kernel, dim3(1), dim3(256), 0, a.stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,234 @@
+/*
+ * gdn.h -- C ABI of the MI355X (gfx950) gated delta rule forward library.
+ *
+ * The operation (the "gated delta rule"):
+ *
+ *   S_t = S_{t-1} ( D_t (I - beta_t k_t k_t^T) ) + beta_t v_t k_t^T ,
+ *   o_t = S_t (scale * q_t)
+ *
+ * with D_t = exp(g_t) I for the scalar gate (Gated DeltaNet: page
+ * "TileLang 实战：KDA 从零到一--Gated DeltaNet", introduction and §2.3;
+ * page "Gated Delta Network（GDN）", eq. 4) or D_t = Diag(exp(g_t)) for the
+ * per-key-channel gate (Kimi Delta Attention: page "DeltaNet 系列线性注意力
+ * 变体的推导之旅", KDA section).  g is the natural log of the gate
+ * (g <= 0 for a decaying state).  The state is stored transposed,
+ * h = S^T with shape [K, V], as the pages' kernels store it ("TileLang 实战"
+ * §3.0; "Gated Delta Network（GDN）" §4.1(d): [B, H, K, V]).
+ *
+ * The output of step t reads the state after token t's own write.  q and k are
+ * used as given: L2 normalisation is the caller's precondition ("TileLang
+ * 实战" §0 and §1.2).  beta is used as given (normally in (0, 1)).
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument is device memory owned by the caller (any memory
+ *    a gfx950 kernel can read or write).  The library never allocates,
+ *    never keeps a pointer after returning and never synchronises.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *    Outputs are valid once that stream has reached the enqueued work;
+ *    inputs must stay unchanged until then.  Outputs must not alias inputs,
+ *    except where an entry point says so.
+ *  - All shape and pointer checks happen before the first launch, so a call
+ *    that returns an error status has enqueued nothing and written nothing.
+ *  - Non-finite input values propagate; they are not checked.
+ *  - All entry points are reentrant and thread-safe.
+ *  - Layouts are dense row-major with the shapes given.  Alignment: q, k, v,
+ *    o of the chunked forward and the decode state need 16 bytes (they are
+ *    moved in 16-byte vectors); cu_seqlens needs 8; every other tensor its
+ *    element size; the workspace 256.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef int32_t gdn_status;
+enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL_ARG = 1,        /* a required pointer is NULL */
+    GDN_ERR_BAD_SHAPE = 2,       /* negative/zero sizes, B != 1 with cu_seqlens, ... */
+    GDN_ERR_BAD_DTYPE = 3,       /* unknown dtype or gate code */
+    GDN_ERR_UNSUPPORTED = 4,     /* chunk not in {16,32,64}; K, V not in {64,128} */
+    GDN_ERR_WORKSPACE_TOO_SMALL = 5,
+    GDN_ERR_MISALIGNED = 6,      /* a pointer lacks the alignment stated below */
+    GDN_ERR_HIP = 7              /* a kernel launch failed; see gdn_last_error() */
+};
+
+/* element type of q, k, v and o */
+enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 };
+/* gate shape: one log-gate per (token, head), or one per (token, head, key) */
+enum { GDN_GATE_SCALAR = 0, GDN_GATE_PER_KEY = 1 };
+
+/* Shape of a chunked (prefill) forward call. */
+typedef struct gdn_fwd_desc {
+    int64_t batch;      /* B; must be 1 when cu_seqlens is given */
+    int64_t seq_len;    /* T: tokens per sequence, or all packed tokens */
+    int64_t num_heads;  /* H */
+    int64_t key_dim;    /* K, in {64, 128} */
+    int64_t value_dim;  /* V, in {64, 128} */
+    int64_t num_seqs;   /* N packed sequences when cu_seqlens is given, else 0 */
+    int32_t chunk;      /* C in {16, 32, 64} */
+    int32_t qkv_dtype;  /* GDN_DTYPE_* of q, k, v, o */
+    int32_t gate;       /* GDN_GATE_* */
+    float scale;        /* multiplies q (usually 1/sqrt(K)) */
+} gdn_fwd_desc;
+
+/* Shape of a single-token (decode) step over N independent sequences. */
+typedef struct gdn_step_desc {
+    int64_t num_seqs;   /* N */
+    int64_t num_heads;  /* H */
+    int64_t key_dim;    /* K, in {64, 128} */
+    int64_t value_dim;  /* V, in {64, 128} */
+    int32_t qkv_dtype;  /* GDN_DTYPE_* of q, k, v, o */
+    int32_t gate;       /* GDN_GATE_* */
+    float scale;
+} gdn_step_desc;
+
+/* Integer version of this ABI (GDN_ABI_VERSION), for binding checks. */
+int gdn_abi_version(void);
+
+/* Static name of a status code (never NULL). */
+const char *gdn_status_str(gdn_status s);
+
+/* Detail of the last failing call on this thread (never NULL, may be ""). */
+const char *gdn_last_error(void);
+
+/*
+ * Bytes of device workspace gdn_chunk_fwd and gdn_chunk_intra need for the
+ * shape *d (written to *bytes).  It holds the per-chunk products of the
+ * intra-chunk stage and the chunk table, laid out as gdn_workspace_layout_of
+ * reports.  A descriptor with num_seqs > 0 describes packed input.
+ */
+gdn_status gdn_chunk_fwd_workspace(const gdn_fwd_desc *d, size_t *bytes);
+
+/*
+ * Chunked forward pass ("TileLang 实战" §2.2.4-2.3: UT transform and gated
+ * chunk equations 11-12; "阅读笔记：DeltaNet 在 FLA 中的代码实现笔记",
+ * forward Steps 1-5; signature of its chunk_delta_rule_fwd: q, k, v, beta,
+ * scale, initial_state, output_final_state, cu_seqlens).
+ *
+ *   q, k   [B, T, H, K]   qkv_dtype
+ *   v      [B, T, H, V]   qkv_dtype
+ *   beta   [B, T, H]      float
+ *   g      [B, T, H] (GDN_GATE_SCALAR) or [B, T, H, K] (GDN_GATE_PER_KEY),
+ *          float, natural-log gate
+ *   h0     [N, H, K, V]   float, initial state; NULL means zeros
+ *   cu_seqlens  NULL, or int64 [num_seqs + 1] on the device: packed sequence
+ *          offsets, starting at 0, nondecreasing, ending at T (B must be 1).
+ *          Chunks restart at every sequence start and every sequence starts
+ *          from its own h0 ("Gated Delta Network（GDN）", terminology note:
+ *          a chunk boundary is not a sequence boundary).  Offsets are not
+ *          checked on the device: bad offsets give undefined results.
+ *   o      [B, T, H, V]   qkv_dtype, output
+ *   ht     [N, H, K, V]   float, final state; NULL means not returned.
+ *          ht may equal h0 (in-place carry); no other aliasing is allowed.
+ *   N = B without cu_seqlens, num_seqs with it.
+ *   workspace, workspace_bytes: device scratch of at least
+ *          gdn_chunk_fwd_workspace() bytes, 256-byte aligned.
+ */
+gdn_status gdn_chunk_fwd(const gdn_fwd_desc *d,
+                         const void *q, const void *k, const void *v,
+                         const float *beta, const float *g, const float *h0,
+                         const int64_t *cu_seqlens,
+                         void *o, float *ht,
+                         void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/*
+ * Where gdn_chunk_fwd / gdn_chunk_intra keep each intermediate inside the
+ * workspace (byte offsets from its start).  Every per-chunk array is indexed
+ * [head][chunk][...] with max_chunks chunk slots per head; chunk j of
+ * sequence b is slot b * ceil(T / C) + j without cu_seqlens, and slot
+ * (first chunk of the sequence) + j with it.  Rows of a ragged last chunk
+ * past its end hold zeros.  With G the inclusive cumulative log2 gate inside
+ * the chunk and gamma = 2^G:
+ *   gcum  float [H][mc][C]  (scalar gate) or [H][mc][C][K] (per-key gate): G
+ *   w     [H][mc][C][K]     W = (I+A)^{-1} diag(beta) diag(gamma) K
+ *   u     [H][mc][C][V]     U = (I+A)^{-1} diag(beta) V
+ *   qs    [H][mc][C][K]     scale * diag(gamma) Q
+ *   kt    [H][mc][K][C]     (diag(gamma_C / gamma) K)^T
+ *   aqk   [H][mc][C][C]     scale * (Q K^T masked by Gamma, diagonal kept)
+ *   ainv  float [H][mc][C][C]  (I+A)^{-1}; written only by gdn_chunk_intra
+ *   chunks int32 [mc][4]    (first token, token count, sequence, 0) per chunk
+ *                           slot (packed input only)
+ *   seqs  int32 [N][4]      (first token, length, first chunk slot, chunks)
+ *                           (packed input only)
+ * A = strictLower(diag(beta) (Gamma * K K^T)), Gamma_ij = 2^(G_i - G_j) for
+ * j <= i.  w, u, qs, kt and aqk have the element type qkv_dtype.  For the
+ * per-key gate gamma is per channel and every Gamma factor sits inside the
+ * sum over the key channel.  A descriptor with num_seqs > 0 describes packed
+ * input.
+ */
+typedef struct gdn_workspace_layout {
+    size_t gcum, w, u, qs, kt, aqk, ainv, chunks, seqs;
+    size_t total;        /* == gdn_chunk_fwd_workspace() */
+    int64_t max_chunks;  /* chunk slots per head (mc) */
+} gdn_workspace_layout;
+
+gdn_status gdn_workspace_layout_of(const gdn_fwd_desc *d, gdn_workspace_layout *out);
+
+/*
+ * The two stages of gdn_chunk_fwd, callable one at a time (gdn_chunk_fwd is
+ * exactly gdn_chunk_intra(flags = 0) followed by gdn_chunk_scan on the same
+ * workspace and stream).
+ *
+ * gdn_chunk_intra: the intra-chunk stage ("TileLang 实战" §2.2.4, §2.3 and
+ * §4.1-4.2; "阅读笔记：DeltaNet 在 FLA 中的代码实现笔记", forward Steps 1-3):
+ * cumulative gates, the beta-scaled decay-masked strictly-lower K K^T, its
+ * unit-lower inverse, W, U, Qs, Kt and the causal Q K^T block, left in the
+ * workspace as gdn_workspace_layout_of describes.  With
+ * flags & GDN_INTRA_STORE_AINV the inverse (I+A)^{-1} is written too (for
+ * checking the stage; gdn_chunk_fwd does not write it).  Arguments as for
+ * gdn_chunk_fwd.
+ */
+#define GDN_INTRA_STORE_AINV 1
+gdn_status gdn_chunk_intra(const gdn_fwd_desc *d,
+                           const void *q, const void *k, const void *v,
+                           const float *beta, const float *g,
+                           const int64_t *cu_seqlens,
+                           void *workspace, size_t workspace_bytes,
+                           int32_t flags, void *stream);
+
+/*
+ * gdn_chunk_scan: the inter-chunk state pass with the chunk output ("TileLang
+ * 实战" §2.3 eqs. 11-12; "Gated Delta Network（GDN）" §4.1(d); "阅读笔记"
+ * forward Steps 4-5), serial over the chunks of each sequence:
+ *   V_new = U - W h,  o = Qs h + Aqk V_new,  h <- gamma_C h + Kt V_new.
+ * The workspace must hold what gdn_chunk_intra left there for the same
+ * descriptor, inputs and cu_seqlens (which is only used to know the number
+ * of sequences; the chunk table comes from the workspace).  h0, o, ht as for
+ * gdn_chunk_fwd.
+ */
+gdn_status gdn_chunk_scan(const gdn_fwd_desc *d, const float *h0,
+                          const int64_t *cu_seqlens, void *o, float *ht,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode token for N independent sequences: the recurrent form used
+ * when a single new token arrives ("Gated Delta Network（GDN）" §4.4,
+ * eq. 12; "DeltaNet 系列线性注意力变体的推导之旅", fused recurrent kernel:
+ * forget, predict, correct, read).
+ *
+ *   q, k   [N, H, K]   qkv_dtype
+ *   v      [N, H, V]   qkv_dtype
+ *   beta   [N, H]      float
+ *   g      [N, H] or [N, H, K]   float, natural-log gate
+ *   state  [N, H, K, V]  float, read and updated in place
+ *   o      [N, H, V]   qkv_dtype, output
+ */
+gdn_status gdn_recurrent_step(const gdn_step_desc *d,
+                              const void *q, const void *k, const void *v,
+                              const float *beta, const float *g,
+                              float *state, void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,122 @@
+"""The C ABI on the CPU: the library loads, exports what include/gdn.h
+declares, and rejects bad arguments before launching anything (every call
+below fails validation, so no GPU is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_14_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gdn.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(gdn.EXPORTS) == names
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gdn_abi_version() == gdn.ABI_VERSION
+    for code, name in gdn._binding.STATUS.items():
+        assert lib.gdn_status_str(code).decode() == name
+    assert lib.gdn_status_str(99).decode() == "GDN_ERR_UNKNOWN"
+
+
+def _desc(**kw):
+    d = dict(batch=2, seq_len=256, num_heads=4, key_dim=128, value_dim=128, num_seqs=0, chunk=64,
+             qkv_dtype=1, gate=0, scale=0.088)
+    d.update(kw)
+    return gdn.FwdDesc(**d)
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(chunk=32), 4), (dict(chunk=128), 4), (dict(key_dim=96), 4), (dict(value_dim=256), 4),
+    (dict(qkv_dtype=7), 3), (dict(gate=5), 3), (dict(batch=0), 2), (dict(num_heads=0), 2),
+    (dict(seq_len=-1), 2), (dict(qkv_dtype=0, gate=1, key_dim=128), 4),
+    (dict(batch=2, num_seqs=3), 2),
+])
+def test_descriptor_errors(lib, kw, code):
+    n = ctypes.c_size_t()
+    assert lib.gdn_chunk_fwd_workspace(ctypes.byref(_desc(**kw)), ctypes.byref(n)) == code
+    assert lib.gdn_last_error().decode() != ""
+
+
+def test_workspace_size_and_layout(lib):
+    d = _desc()
+    L = gdn.workspace_layout(d)
+    assert L.max_chunks == 2 * 4
+    blocks = 4 * L.max_chunks
+    assert L.w - L.gcum >= blocks * 64 * 4
+    assert L.u - L.w >= blocks * 64 * 128 * 2
+    assert L.total >= L.chunks
+    offs = [L.gcum, L.w, L.u, L.qs, L.kt, L.aqk, L.ainv, L.chunks, L.total]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert gdn.workspace_bytes(d) == L.total
+    # packed: one extra chunk slot per sequence
+    P = gdn.workspace_layout(_desc(batch=1, seq_len=300, num_seqs=3))
+    assert P.max_chunks == 5 + 3
+
+
+FAKE = ctypes.c_void_p(1 << 20)        # aligned, never dereferenced
+MIS = ctypes.c_void_p((1 << 20) + 4)
+
+
+def _fwd(lib, d, q=FAKE, o=FAKE, ws=FAKE, wsb=1 << 40, cu=None, h0=None):
+    return lib.gdn_chunk_fwd(ctypes.byref(d), q, FAKE, FAKE, FAKE, FAKE, h0, cu, o, None, ws,
+                             wsb, None)
+
+
+def test_chunk_fwd_rejects_before_launch(lib):
+    d = _desc()
+    assert _fwd(lib, d, q=None) == 1
+    assert _fwd(lib, d, o=None) == 1
+    assert _fwd(lib, d, ws=None) == 1
+    assert _fwd(lib, d, q=MIS) == 6
+    assert _fwd(lib, d, h0=ctypes.c_void_p((1 << 20) + 2)) == 6
+    assert _fwd(lib, d, ws=ctypes.c_void_p((1 << 20) + 64)) == 6
+    assert _fwd(lib, d, wsb=1024) == 5
+    assert _fwd(lib, _desc(batch=2, num_seqs=2), cu=FAKE) == 2      # packed needs B == 1
+    assert _fwd(lib, _desc(batch=1), cu=FAKE) == 2                  # packed needs num_seqs
+    assert lib.gdn_chunk_intra(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                               1 << 40, 0, None) == 1
+    assert lib.gdn_chunk_scan(ctypes.byref(d), None, None, None, None, FAKE, 1 << 40, None) == 1
+    assert lib.gdn_chunk_scan(ctypes.byref(d), None, None, FAKE, None, FAKE, 1024, None) == 5
+
+
+def test_step_rejects_before_launch(lib):
+    d = gdn.StepDesc(4, 2, 128, 128, 1, 0, 0.1)
+    args = [FAKE] * 7
+    assert lib.gdn_recurrent_step(ctypes.byref(d), None, *args[1:], None) == 1
+    assert lib.gdn_recurrent_step(ctypes.byref(d), ctypes.c_void_p(3), *args[1:], None) == 6
+    assert lib.gdn_recurrent_step(ctypes.byref(d), *args[:5], MIS, args[6], None) == 6
+    bad = gdn.StepDesc(4, 2, 96, 128, 1, 0, 0.1)
+    assert lib.gdn_recurrent_step(ctypes.byref(bad), *args, None) == 4
+    bad = gdn.StepDesc(4, 2, 128, 128, 9, 0, 0.1)
+    assert lib.gdn_recurrent_step(ctypes.byref(bad), *args, None) == 3
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 64, 1, 64)
+    with pytest.raises(ValueError):
+        gdn.chunk_fwd(q, q, q, torch.zeros(1, 64, 1), torch.zeros(1, 64, 1))
