@@ -49,6 +49,28 @@ def prefill_bytes(spec, n_seqs):
     return intra, scan
 
 
+KERNEL_SOURCES = {"intra_kernel": ["k_intra.hip", "gdn_device.hpp"],
+                  "scan_kernel": ["k_scan.hip", "gdn_device.hpp"],
+                  "step_kernel": ["k_step.hip", "gdn_device.hpp"]}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter summary
+    (profiles/hbm_traffic.json, FETCH_SIZE + WRITE_SIZE scaled by a copy of
+    known size), or None if the kernel's source changed since."""
+    import hashlib
+    path = os.path.join(HERE, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel)
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.join(HERE, "gated_delta_rule_14_amd", "csrc", f), "rb").read())
+    return rec["bytes_per_launch"] if h.hexdigest()[:16] == rec["source_sha"] else None
+
+
 def events_time(fn, reps):
     """Average duration of fn() over reps back-to-back launches, from HIP
     events recorded on the current stream (the stream the kernels use)."""
@@ -104,14 +126,10 @@ def bench_prefill(args, gdn):
     }
     dom, t_dom, b_dom = (("intra_kernel", t_intra, b_intra) if t_intra >= t_scan
                          else ("scan_kernel", t_scan, b_scan))
-    traffic = None
-    tpath = os.path.join(HERE, "profiles", "traffic.json")
-    if os.path.exists(tpath):
-        tr = json.load(open(tpath)).get(dom)
-        if tr:
-            traffic = tr.get("bytes_per_launch")
     roof = {"bound": "hbm", "kernel": dom, "achieved": b_dom / t_dom / 1e9, "peak": HBM_PEAK / 1e9,
-            "unit": "GB/s", "frac": b_dom / t_dom / HBM_PEAK, "traffic": traffic}
+            "unit": "GB/s", "frac": b_dom / t_dom / HBM_PEAK, "traffic": measured_traffic(dom)}
+    for name in kernels:
+        kernels[name]["traffic"] = measured_traffic(name)
     path = {"alg_bytes": b_intra + b_scan, "GBps": (b_intra + b_scan) / dt / 1e9,
             "frac_hbm": (b_intra + b_scan) / dt / HBM_PEAK,
             "alg_flops": flops, "TFLOPs": flops / dt / 1e12, "frac_mfma_bf16": flops / dt / BF16_PEAK}
@@ -141,7 +159,8 @@ def bench_decode(args, gdn):
             "tokens_per_s": spec.N / t,
             "roofline": {"bound": "hbm", "kernel": "step_kernel",
                          "achieved": step_bytes / t / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-                         "frac": step_bytes / t / HBM_PEAK, "alg_bytes": step_bytes}}
+                         "frac": step_bytes / t / HBM_PEAK, "alg_bytes": step_bytes,
+                         "traffic": measured_traffic("step_kernel")}}
 
 
 def cpu_baseline(d, min_s=10.0):
@@ -170,6 +189,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (a known-size kernel to scale "
+                         "hardware byte counters by)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -178,6 +200,13 @@ def main():
     import gated_delta_rule_14_amd as gdn
     gdn.load()
     torch.cuda.init()
+    if args.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     spec, dt, roof, path, kernels, d = bench_prefill(args, gdn)
     decode = None if args.no_decode else bench_decode(args, gdn)
     cpu = None if args.no_cpu else cpu_baseline(d)

@@ -38,18 +38,21 @@ struct IntraSmem {
     static constexpr int LDA = C + 1;         // fp32 [C][C]
     static constexpr int NB = C / 16;
     static constexpr int SCR_ROWS = 2 * 16 + C - 16;   // per-key scaled operands
+    // A (fp32, for the solve) and then (beta V)^T share one region
+    static constexpr size_t AV_BYTES = sizeof(float) * C * LDA > sizeof(T) * V * LDC
+                                           ? sizeof(float) * C * LDA : sizeof(T) * V * LDC;
     static constexpr size_t o_K = 0;
     static constexpr size_t o_Q = o_K + sizeof(T) * C * LDK;
     static constexpr size_t o_KT = o_Q + sizeof(T) * C * LDK;
-    static constexpr size_t o_VT = o_KT + sizeof(T) * K * LDC;
-    static constexpr size_t o_A = o_VT + sizeof(T) * V * LDC;
-    static constexpr size_t o_G = o_A + sizeof(float) * C * LDA;
+    static constexpr size_t o_AV = o_KT + sizeof(T) * K * LDC;
+    static constexpr size_t o_G = o_AV + ((AV_BYTES + 15) / 16) * 16;
     static constexpr size_t o_B = o_G + sizeof(float) * C * (PK ? K : 1);
     static constexpr size_t o_P = o_B + sizeof(float) * C;
     static constexpr size_t o_S = o_P + sizeof(float) * 4 * 16 * 17;
     static constexpr size_t bytes = o_S + (PK ? sizeof(T) * SCR_ROWS * LDK : 0);
     static_assert(C * LDC <= K * LDC, "Aqk staging must fit the K^T buffer");
-    static_assert(C * LDV <= V * LDC, "U staging must fit the V^T buffer");
+    static_assert(sizeof(T) * C * LDV <= AV_BYTES, "U staging must fit the A / V^T region");
+    static_assert(C * LDC <= C * LDK, "Ainv copy must fit the Q buffer");
 };
 
 template <typename T, int K, int V, int C, bool PK, bool STORE_AINV>
@@ -62,8 +65,8 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraLaunch a) {
     T* sK = reinterpret_cast<T*>(smem + L::o_K);
     T* sQ = reinterpret_cast<T*>(smem + L::o_Q);
     T* sKT = reinterpret_cast<T*>(smem + L::o_KT);
-    T* sVT = reinterpret_cast<T*>(smem + L::o_VT);
-    float* sA = reinterpret_cast<float*>(smem + L::o_A);
+    float* sA = reinterpret_cast<float*>(smem + L::o_AV);   // until Ainv is copied out
+    T* sVT = reinterpret_cast<T*>(smem + L::o_AV);          // after that
     float* sG = reinterpret_cast<float*>(smem + L::o_G);
     float* sB = reinterpret_cast<float*>(smem + L::o_B);
     float* sP = reinterpret_cast<float*>(smem + L::o_P);
@@ -126,34 +129,41 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraLaunch a) {
         }
         for (int r = tid; r < C; r += 256) sB[r] = r < n ? a.beta[(t0 + r) * H + h] : 0.f;
     }
-    // K, Q rows into LDS (zeros past n); zero A and the Aqk staging area
-    for (int i = tid; i < C * (K / EV); i += 256) {
-        const int r = i / (K / EV), cv = i - r * (K / EV);
-        uint4 kv = make_uint4(0, 0, 0, 0), qv = kv;
-        if (r < n) {
-            kv = *reinterpret_cast<const uint4*>(k + ((t0 + r) * H + h) * K + cv * EV);
-            qv = *reinterpret_cast<const uint4*>(q + ((t0 + r) * H + h) * K + cv * EV);
+    // K, Q, V rows: every load issued before any is used (zeros past n)
+    constexpr int VK = C * (K / EV), VV = C * (V / EV);
+    constexpr int PK_ = (VK + 255) / 256, PV = (VV + 255) / 256;
+    uint4 kreg[PK_], qreg[PK_], vreg[PV];
+#pragma unroll
+    for (int p = 0; p < PK_; ++p) {
+        const int i = tid + 256 * p, r = i / (K / EV), cv = i - r * (K / EV);
+        kreg[p] = qreg[p] = make_uint4(0, 0, 0, 0);
+        if (i < VK && r < n) {
+            kreg[p] = *reinterpret_cast<const uint4*>(k + ((t0 + r) * H + h) * K + cv * EV);
+            qreg[p] = *reinterpret_cast<const uint4*>(q + ((t0 + r) * H + h) * K + cv * EV);
         }
-        *reinterpret_cast<uint4*>(sK + r * LDK + cv * EV) = kv;
-        *reinterpret_cast<uint4*>(sQ + r * LDK + cv * EV) = qv;
     }
+#pragma unroll
+    for (int p = 0; p < PV; ++p) {
+        const int i = tid + 256 * p, r = i / (V / EV), cv = i - r * (V / EV);
+        vreg[p] = make_uint4(0, 0, 0, 0);
+        if (i < VV && r < n)
+            vreg[p] = *reinterpret_cast<const uint4*>(v + ((t0 + r) * H + h) * V + cv * EV);
+    }
+#pragma unroll
+    for (int p = 0; p < PK_; ++p) {
+        const int i = tid + 256 * p, r = i / (K / EV), cv = i - r * (K / EV);
+        if (i < VK) {
+            *reinterpret_cast<uint4*>(sK + r * LDK + cv * EV) = kreg[p];
+            *reinterpret_cast<uint4*>(sQ + r * LDK + cv * EV) = qreg[p];
+        }
+    }
+    // zero A and the Aqk staging area
     for (int i = tid; i < C * C; i += 256) {
         const int r = i / C, j = i - r * C;
         sA[r * LDA + j] = 0.f;
         Elem<T>::store(sStage + r * LDC + j, 0.f);
     }
     __syncthreads();
-
-    // V^T scaled by beta (the B operand of U = Ainv diag(beta) V)
-    for (int i = tid; i < C * (V / EV); i += 256) {
-        const int r = i / (V / EV), cv = i - r * (V / EV);
-        uint4 vv = make_uint4(0, 0, 0, 0);
-        if (r < n) vv = *reinterpret_cast<const uint4*>(v + ((t0 + r) * H + h) * V + cv * EV);
-        const float bt = sB[r];
-#pragma unroll
-        for (int e = 0; e < EV; ++e)
-            Elem<T>::store(sVT + (cv * EV + e) * LDC + r, bt * Vec16<T>::get(vv, e));
-    }
 
     // ---- a2: beta-scaled decay-masked strictly-lower K K^T and causal Q K^T
     if (!PK) {
@@ -245,10 +255,14 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraLaunch a) {
         T* gaqk = static_cast<T*>(a.ws.aqk) + blk * C * C;
         copy_tile<T>(gaqk, C, sStage, LDC, C, C, tid, 256);
         T* gqs = static_cast<T*>(a.ws.qs) + blk * C * K;
-        for (int i = tid; i < C * K; i += 256) {
-            const int r = i / K, d = i - r * K;
-            const float gm = exp2f(PK ? sG[r * K + d] : sG[r]);
-            Elem<T>::store(gqs + i, a.scale * gm * Elem<T>::load(sQ + r * LDK + d));
+        for (int i = tid; i < C * (K / EV); i += 256) {
+            const int r = i / (K / EV), d0 = (i - r * (K / EV)) * EV;
+            const uint4 x = *reinterpret_cast<const uint4*>(sQ + r * LDK + d0);
+            float f[EV];
+#pragma unroll
+            for (int e = 0; e < EV; ++e)
+                f[e] = a.scale * exp2f(PK ? sG[r * K + d0 + e] : sG[r]) * Vec16<T>::get(x, e);
+            *reinterpret_cast<uint4*>(gqs + r * K + d0) = Vec16<T>::pack(f);
         }
         // Kt[d][r] = k[r][d] * 2^{G_C-1 - G_r}: 8 tokens per 16-byte store (bf16)
         T* gkt = static_cast<T*>(a.ws.kt) + blk * K * C;
@@ -330,6 +344,18 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraLaunch a) {
     for (int i = tid; i < C * C; i += 256) {
         const int r = i / C, j = i - r * C;
         Elem<T>::store(sAb + r * LDC + j, sA[r * LDA + j]);
+    }
+    __syncthreads();
+    // (beta V)^T, the B operand of U, into the region A occupied
+#pragma unroll
+    for (int p = 0; p < PV; ++p) {
+        const int i = tid + 256 * p, r = i / (V / EV), cv = i - r * (V / EV);
+        if (i < VV) {
+            const float bt = sB[r];
+#pragma unroll
+            for (int e = 0; e < EV; ++e)
+                Elem<T>::store(sVT + (cv * EV + e) * LDC + r, bt * Vec16<T>::get(vreg[p], e));
+        }
     }
     __syncthreads();
 

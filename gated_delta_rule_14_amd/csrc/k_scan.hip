@@ -101,29 +101,91 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanLaunch a) {
                         hacc[rt][ct]);
         }
 
+    // ---- chunk operands: W, Qs [C][K], Kt [K][C], Aqk [C][C], U tile [C][VT],
+    // moved as 16-byte vectors.  Chunk j+1 is loaded into registers while
+    // chunk j is computed, then written to LDS.
+    constexpr int EV = 16 / sizeof(T);
+    constexpr int VW = C * K / EV, VQ = C * K / EV, VK = K * C / EV, VA = C * C / EV,
+                  VU = C * VT / EV;
+    constexpr int NV = VW + VQ + VK + VA + VU;
+    constexpr int PER = (NV + 255) / 256;
+    uint4 pre[PER];
+    float pre_d = 0.f;
+    const T* gw = static_cast<const T*>(a.ws.w);
+    const T* gq = static_cast<const T*>(a.ws.qs);
+    const T* gk = static_cast<const T*>(a.ws.kt);
+    const T* ga = static_cast<const T*>(a.ws.aqk);
+    const T* gu = static_cast<const T*>(a.ws.u);
+    auto issue = [&](int64_t blk) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int i = tid + 256 * p;
+            const uint4* src;
+            if (i < VW) src = reinterpret_cast<const uint4*>(gw + blk * C * K) + i;
+            else if (i < VW + VQ) src = reinterpret_cast<const uint4*>(gq + blk * C * K) + (i - VW);
+            else if (i < VW + VQ + VK)
+                src = reinterpret_cast<const uint4*>(gk + blk * K * C) + (i - VW - VQ);
+            else if (i < VW + VQ + VK + VA)
+                src = reinterpret_cast<const uint4*>(ga + blk * C * C) + (i - VW - VQ - VK);
+            else if (i < NV) {
+                const int u = i - (VW + VQ + VK + VA), r = u / (VT / EV), cv = u - r * (VT / EV);
+                src = reinterpret_cast<const uint4*>(gu + blk * C * V + r * V + v0) + cv;
+            } else {
+                src = nullptr;
+            }
+            pre[p] = src ? *src : make_uint4(0, 0, 0, 0);
+        }
+        if (PK) pre_d = tid < K ? a.ws.gcum[(blk * C + (C - 1)) * K + tid] : 0.f;
+        else pre_d = a.ws.gcum[blk * C + (C - 1)];
+    };
+    float dsc = 0.f;
+    auto commit = [&]() {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int i = tid + 256 * p;
+            T* dst;
+            if (i < VW) {
+                const int r = i / (K / EV), cv = i - r * (K / EV);
+                dst = sW + r * LDK + cv * EV;
+            } else if (i < VW + VQ) {
+                const int u = i - VW, r = u / (K / EV), cv = u - r * (K / EV);
+                dst = sQ + r * LDK + cv * EV;
+            } else if (i < VW + VQ + VK) {
+                const int u = i - VW - VQ, r = u / (C / EV), cv = u - r * (C / EV);
+                dst = sKt + r * LDC + cv * EV;
+            } else if (i < VW + VQ + VK + VA) {
+                const int u = i - VW - VQ - VK, r = u / (C / EV), cv = u - r * (C / EV);
+                dst = sAqk + r * LDC + cv * EV;
+            } else if (i < NV) {
+                const int u = i - (VW + VQ + VK + VA), r = u / (VT / EV), cv = u - r * (VT / EV);
+                dst = sU + r * LDT + cv * EV;
+            } else {
+                dst = nullptr;
+            }
+            if (dst) *reinterpret_cast<uint4*>(dst) = pre[p];
+        }
+        if (PK) {
+            if (tid < K) sD[tid] = exp2f(pre_d);
+        } else {
+            dsc = exp2f(pre_d);
+        }
+    };
+
     const int nch = (int)((len + C - 1) / C);
     T* o = static_cast<T*>(a.o);
+    if (nch > 0 && c0 < a.map.max_chunks) {
+        issue(h * a.map.max_chunks + c0);
+        commit();
+    }
+    __syncthreads();
     for (int j = 0; j < nch; ++j) {
         const int64_t c = c0 + j;
         if (c >= a.map.max_chunks) break;
         const int64_t tt0 = t0 + (int64_t)j * C;
         const int ntok = (int)min((int64_t)C, len - (int64_t)j * C);
-        const int64_t blk = h * a.map.max_chunks + c;
-
-        // ---- this chunk's operands into LDS
-        copy_tile<T>(sW, LDK, static_cast<const T*>(a.ws.w) + blk * C * K, K, C, K, tid, 256);
-        copy_tile<T>(sQ, LDK, static_cast<const T*>(a.ws.qs) + blk * C * K, K, C, K, tid, 256);
-        copy_tile<T>(sKt, LDC, static_cast<const T*>(a.ws.kt) + blk * K * C, C, K, C, tid, 256);
-        copy_tile<T>(sAqk, LDC, static_cast<const T*>(a.ws.aqk) + blk * C * C, C, C, C, tid, 256);
-        copy_tile<T>(sU, LDT, static_cast<const T*>(a.ws.u) + blk * C * V + v0, V, C, VT, tid, 256);
-        float dsc = 0.f;
-        if (PK) {
-            for (int d = tid; d < K; d += 256)
-                sD[d] = exp2f(a.ws.gcum[(blk * C + (C - 1)) * K + d]);
-        } else {
-            dsc = exp2f(a.ws.gcum[blk * C + (C - 1)]);
-        }
-        __syncthreads();
+        const bool more = j + 1 < nch && c + 1 < a.map.max_chunks;
+        if (more) issue(h * a.map.max_chunks + c + 1);
+        const float dcur = dsc;
 
         // ---- V_new = U - W h and O = Qs h, one 16-row tile per wave
         f32x4 ov[CT];
@@ -136,6 +198,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanLaunch a) {
             }
             const T* wr = sW + (16 * wave + (lane & 15)) * LDK;
             const T* qr = sQ + (16 * wave + (lane & 15)) * LDK;
+#pragma unroll
             for (int k0 = 0; k0 < K; k0 += KS) {
                 const typename Mma<T>::frag fw = Mma<T>::load(wr + k0, lane);
                 const typename Mma<T>::frag fq = Mma<T>::load(qr + k0, lane);
@@ -176,7 +239,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanLaunch a) {
             for (int ct = 0; ct < CT; ++ct) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    hacc[rt][ct][e] *= PK ? sD[rb + acc_row(lane, e)] : dsc;
+                    hacc[rt][ct][e] *= PK ? sD[rb + acc_row(lane, e)] : dcur;
                 hacc[rt][ct] = mma_tile<T>(sKt + rb * LDC, LDC, sVn + 16 * ct * LDC, LDC, C, lane,
                                            hacc[rt][ct]);
                 store_acc_t(shT + (16 * ct) * LDK + rb, LDK, lane, hacc[rt][ct]);
@@ -184,13 +247,15 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanLaunch a) {
         }
         __syncthreads();
 
-        // ---- O tile to HBM (rows past the end of the sequence are dropped)
-        constexpr int EV = 16 / sizeof(T);
+        // ---- O tile to HBM (rows past the end of the sequence are dropped),
+        // then the prefetched chunk into LDS
         for (int i = tid; i < ntok * (VT / EV); i += 256) {
             const int r = i / (VT / EV), cv = i - r * (VT / EV);
             *reinterpret_cast<uint4*>(o + ((tt0 + r) * a.H + h) * V + v0 + cv * EV) =
                 *reinterpret_cast<const uint4*>(sO + r * LDT + cv * EV);
         }
+        if (more) commit();
+        __syncthreads();
     }
 
     if (a.ht) {
