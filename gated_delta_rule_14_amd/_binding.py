@@ -43,7 +43,7 @@ class StepDesc(ctypes.Structure):
 
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in
-                ("gcum", "w", "u", "qs", "kt", "aqk", "ainv", "chunks", "seqs", "total")] + \
+                ("gcum", "w", "u", "qs", "ks", "aqk", "ainv", "chunks", "seqs", "total")] + \
                [("max_chunks", ctypes.c_int64)]
 
 
@@ -188,7 +188,7 @@ def chunk_fwd(q, k, v, beta, g, scale=None, h0=None, cu_seqlens=None, chunk=64,
 def chunk_intra(q, k, v, beta, g, scale=None, cu_seqlens=None, chunk=64, gate="scalar",
                 store_ainv=True, workspace=None, stream=None):
     """gdn_chunk_intra: the intra-chunk stage alone.  Returns a dict of views
-    into the workspace: gcum, w, u, qs, kt, aqk, ainv, max_chunks, workspace."""
+    into the workspace: gcum, w, u, qs, ks, aqk, ainv, max_chunks, workspace."""
     lib = load()
     _inputs(q, k, v, beta, g, cu_seqlens, gate)
     N = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
@@ -212,7 +212,7 @@ def chunk_intra(q, k, v, beta, g, scale=None, cu_seqlens=None, chunk=64, gate="s
     gshape = (H, mc, C, K) if gate == "per_key" else (H, mc, C)
     return dict(gcum=view(L.gcum, torch.float32, gshape),
                 w=view(L.w, q.dtype, (H, mc, C, K)), u=view(L.u, q.dtype, (H, mc, C, V)),
-                qs=view(L.qs, q.dtype, (H, mc, C, K)), kt=view(L.kt, q.dtype, (H, mc, K, C)),
+                qs=view(L.qs, q.dtype, (H, mc, C, K)), ks=view(L.ks, q.dtype, (H, mc, C, K)),
                 aqk=view(L.aqk, q.dtype, (H, mc, C, C)),
                 ainv=view(L.ainv, torch.float32, (H, mc, C, C)), max_chunks=mc,
                 workspace=ws, desc=desc)

@@ -84,8 +84,8 @@ void layout(const gdn_fwd_desc* d, bool packed, gdn_workspace_layout* L) {
     off = align256(off + blocks * C * V * es);
     L->qs = off;
     off = align256(off + blocks * C * K * es);
-    L->kt = off;
-    off = align256(off + blocks * K * C * es);
+    L->ks = off;
+    off = align256(off + blocks * C * K * es);
     L->aqk = off;
     off = align256(off + blocks * C * C * es);
     L->ainv = off;
@@ -134,7 +134,7 @@ gdn_status prepare(const gdn_fwd_desc* d, const void* q, const void* k, const vo
     P->ws.aqk = ws + L.aqk;
     P->ws.ainv = want_ainv ? reinterpret_cast<float*>(ws + L.ainv) : nullptr;
     P->ws.qs = ws + L.qs;
-    P->ws.kt = ws + L.kt;
+    P->ws.ks = ws + L.ks;
     P->map.max_chunks = L.max_chunks;
     P->map.T = d->seq_len;
     P->map.nt = (d->seq_len + d->chunk - 1) / d->chunk;
@@ -256,7 +256,7 @@ static gdn_status scan(const gdn_fwd_desc* d, const float* h0, const int64_t* cu
     a.ws.w = ws + L.w;
     a.ws.u = ws + L.u;
     a.ws.qs = ws + L.qs;
-    a.ws.kt = ws + L.kt;
+    a.ws.ks = ws + L.ks;
     a.ws.aqk = ws + L.aqk;
     a.ws.ainv = nullptr;
     a.h0 = h0;

@@ -15,6 +15,7 @@ namespace gdn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 struct bf16 {  // storage-only 16-bit brain float
     uint16_t bits;
@@ -24,16 +25,19 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// round-to-nearest-even, NaN kept quiet
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Two floats to packed bf16 (lo in bits 0-15), round-to-nearest-even, one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2v v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    return (uint16_t)(pack_bf16x2(f, 0.f) & 0xffffu);
 }
 
 // element traits: loads/stores of the q/k/v/o element type through float
@@ -87,6 +91,21 @@ template <> struct Mma<bf16> {
     __device__ __forceinline__ static frag load(const bf16* row, int lane) {
         return *reinterpret_cast<const bf16x8*>(row + 8 * (lane >> 4));
     }
+    // Fragment of a k-major tile X[k][m] (m contiguous, pitch ld elements,
+    // `x` at element (k0, m0)): lane 16g+i receives X[k0+8g .. +7][m0+i].
+    // Two ds_read_b64_tr_b16: inside each 16-lane group, lane i's element e
+    // comes from the 4-element chunk addressed by lane 4e + i/4, position
+    // i%4, so lane j addresses row k0+8g+(j>>2) (+4), columns 4(j&3)..+3.
+    __device__ __forceinline__ static frag load_t(const bf16* x, int ld, int lane) {
+        const int g = lane >> 4, j = lane & 15;
+        const bf16* p = x + (8 * g + (j >> 2)) * ld + 4 * (j & 3);
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * ld));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8, v);
+    }
     __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
@@ -97,6 +116,10 @@ template <> struct Mma<float> {
     static constexpr int KSTEP = 4;
     __device__ __forceinline__ static frag load(const float* row, int lane) {
         return row[lane >> 4];
+    }
+    // k-major tile X[k][m]: lane l receives X[k0 + l/16][m0 + l%16]
+    __device__ __forceinline__ static frag load_t(const float* x, int ld, int lane) {
+        return x[(lane >> 4) * ld + (lane & 15)];
     }
     __device__ __forceinline__ static f32x4 mma(frag a, frag b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -143,6 +166,17 @@ __device__ __forceinline__ void store_acc_t(bf16* dst, int ld, int lane, f32x4 v
 __device__ __forceinline__ void store_acc_t(float* dst, int ld, int lane, f32x4 v) {
     *reinterpret_cast<float4*>(dst + acc_col(lane) * ld + 4 * (lane >> 4)) =
         make_float4(v[0], v[1], v[2], v[3]);
+}
+// The 4 values a lane holds in a tile of X^T are 4 consecutive columns of
+// one row of X: store them as one 8-byte (bf16) or 16-byte (f32) write.
+__device__ __forceinline__ void store4(bf16* dst, f32x4 v) {
+    uint2 w;
+    w.x = pack_bf16x2(v[0], v[1]);
+    w.y = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<uint2*>(dst) = w;
+}
+__device__ __forceinline__ void store4(float* dst, f32x4 v) {
+    *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
 }
 // ... and row-major: dst[row * ld + col] (element stores)
 template <typename T>

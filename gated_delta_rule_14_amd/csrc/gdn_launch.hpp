@@ -37,7 +37,7 @@ struct ChunkWs {
     void* w;       // [H][mc][C][K]
     void* u;       // [H][mc][C][V]
     void* qs;      // [H][mc][C][K]   scale * Q * gamma
-    void* kt;      // [H][mc][K][C]   (K * gamma_C / gamma)^T
+    void* ks;      // [H][mc][C][K]   diag(gamma_C / gamma) K
     void* aqk;     // [H][mc][C][C]
     float* ainv;   // [H][mc][C][C] or nullptr
 };

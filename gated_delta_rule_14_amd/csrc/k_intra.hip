@@ -1,6 +1,6 @@
 // Intra-chunk stage: everything about a chunk that does not depend on the
-// state entering it.  One 256-thread workgroup per (chunk, head); all chunks
-// of all heads run in parallel.
+// state entering it.  One 512-thread workgroup (8 waves) per (chunk, head);
+// all chunks of all heads run in parallel.
 //
 // For a chunk of n <= C tokens (rows r), with G the inclusive cumulative
 // log2-gate inside the chunk and gamma_r = 2^{G_r}:
@@ -11,7 +11,7 @@
 //       16x16 diagonal blocks by forward substitution, then
 //       X_IJ = -X_II sum_{m=J}^{I-1} A_Im X_mJ, block row by block row
 //   a4  W = Ainv diag(beta) diag(gamma) K,  U = Ainv diag(beta) V   (k3)
-// and, for the state pass, Qs = scale Q diag(gamma) and Kt = (K gamma_C/gamma)^T.
+// and, for the state pass, Qs = scale diag(gamma) Q and Ks = diag(gamma_C/gamma) K.
 // Sources: "TileLang 实战：KDA 从零到一--Gated DeltaNet" §2.2.4 (UT transform,
 // eqs. 6-7), §2.2.6 (gated substitutions), §2.3 (eqs. 11-12), §4.1 (log-domain
 // cumulative gate, masked before exponentiation), §4.2 (blocked inverse);
@@ -24,54 +24,64 @@
 // b of block I:  sum_d (k_id 2^{G_id - G_bd}) (k_jd 2^{G_bd - G_jd}), both
 // exponents <= 0, so they run on MFMA without overflow; the diagonal blocks
 // are summed pair by pair.  gamma and gamma_C/gamma become per-channel.
+//
+// Layout choices: K, Q and V stay row-major (key- or value-contiguous) in
+// LDS.  Products that contract over tokens read them with transposing LDS
+// loads, and compute X^T rather than X, so that every lane holds 4
+// consecutive columns of one output row and stores them to HBM directly.
+// beta (and gamma) multiply the columns of Ainv instead of the rows of K, V.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
 namespace gdn {
+
+constexpr int INTRA_THREADS = 512;
 
 template <typename T, int K, int V, int C, bool PK>
 struct IntraSmem {
     static constexpr int P = 16 / sizeof(T);  // 16-byte row padding
     static constexpr int LDK = K + P;         // row-major [C][K]
     static constexpr int LDV = V + P;         // row-major [C][V]
-    static constexpr int LDC = C + P;         // n-major [K or V][C]
-    static constexpr int LDA = C + 1;         // fp32 [C][C]
+    static constexpr int LDC = C + P;         // row-major [C][C] in the element type
+    static constexpr int LDA = C + 4;         // fp32 [C][C]
     static constexpr int NB = C / 16;
-    static constexpr int SCR_ROWS = 2 * 16 + C - 16;   // per-key scaled operands
-    // A (fp32, for the solve) and then (beta V)^T share one region
-    static constexpr size_t AV_BYTES = sizeof(float) * C * LDA > sizeof(T) * V * LDC
-                                           ? sizeof(float) * C * LDA : sizeof(T) * V * LDC;
+    static constexpr int SCR_ROWS = 32 + C - 16;   // per-key scaled operands (>= C)
     static constexpr size_t o_K = 0;
     static constexpr size_t o_Q = o_K + sizeof(T) * C * LDK;
-    static constexpr size_t o_KT = o_Q + sizeof(T) * C * LDK;
-    static constexpr size_t o_AV = o_KT + sizeof(T) * K * LDC;
-    static constexpr size_t o_G = o_AV + ((AV_BYTES + 15) / 16) * 16;
+    static constexpr size_t o_V = o_Q + sizeof(T) * C * LDK;
+    static constexpr size_t o_A = o_V + sizeof(T) * C * LDV;
+    static constexpr size_t o_G = o_A + sizeof(float) * C * LDA;
     static constexpr size_t o_B = o_G + sizeof(float) * C * (PK ? K : 1);
-    static constexpr size_t o_P = o_B + sizeof(float) * C;
+    static constexpr size_t o_E = o_B + sizeof(float) * C;     // 2^{G_r}
+    static constexpr size_t o_F = o_E + sizeof(float) * C;     // 2^{G_C-1 - G_r}
+    static constexpr size_t o_P = o_F + sizeof(float) * C;
     static constexpr size_t o_S = o_P + sizeof(float) * 4 * 16 * 17;
     static constexpr size_t bytes = o_S + (PK ? sizeof(T) * SCR_ROWS * LDK : 0);
-    static_assert(C * LDC <= K * LDC, "Aqk staging must fit the K^T buffer");
-    static_assert(sizeof(T) * C * LDV <= AV_BYTES, "U staging must fit the A / V^T region");
-    static_assert(C * LDC <= C * LDK, "Ainv copy must fit the Q buffer");
+    // Ainv diag(beta gamma) goes where Q was, Ainv diag(beta) where A was
+    static_assert(C * LDC * sizeof(T) <= C * LDK * sizeof(T), "A1 fits the Q region");
+    static_assert(C * LDC * sizeof(T) <= C * LDA * sizeof(float), "A2 fits the A region");
 };
 
 template <typename T, int K, int V, int C, bool PK, bool STORE_AINV>
-__global__ __launch_bounds__(256) void intra_kernel(IntraLaunch a) {
+__global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
     typedef IntraSmem<T, K, V, C, PK> L;
+    typedef Mma<T> M;
+    constexpr int NT = INTRA_THREADS, NW = NT / 64;
     constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC, LDA = L::LDA, NB = L::NB;
     constexpr int EV = 16 / sizeof(T);
-    constexpr int KS = Mma<T>::KSTEP;
+    constexpr int KS = M::KSTEP;
     __shared__ __attribute__((aligned(16))) char smem[L::bytes];
     T* sK = reinterpret_cast<T*>(smem + L::o_K);
     T* sQ = reinterpret_cast<T*>(smem + L::o_Q);
-    T* sKT = reinterpret_cast<T*>(smem + L::o_KT);
-    float* sA = reinterpret_cast<float*>(smem + L::o_AV);   // until Ainv is copied out
-    T* sVT = reinterpret_cast<T*>(smem + L::o_AV);          // after that
+    T* sV = reinterpret_cast<T*>(smem + L::o_V);
+    float* sA = reinterpret_cast<float*>(smem + L::o_A);
     float* sG = reinterpret_cast<float*>(smem + L::o_G);
     float* sB = reinterpret_cast<float*>(smem + L::o_B);
+    float* sE = reinterpret_cast<float*>(smem + L::o_E);
+    float* sF = reinterpret_cast<float*>(smem + L::o_F);
     float* sP = reinterpret_cast<float*>(smem + L::o_P);
-    T* sStage = sKT;     // Aqk staging (before K^T is built)
-    T* sAb = sQ;         // Ainv in the element type (after Q is consumed)
+    T* sA1 = sQ;                              // Ainv diag(beta gamma)   (after Q is used)
+    T* sA2 = reinterpret_cast<T*>(sA);        // Ainv diag(beta)         (after A is used)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t c = blockIdx.x, h = blockIdx.y, H = a.H;
@@ -90,10 +100,30 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraLaunch a) {
     }
     if (n <= 0) return;
     const int64_t blk = h * a.map.max_chunks + c;   // workspace block index
-
     const T* q = static_cast<const T*>(a.q);
     const T* k = static_cast<const T*>(a.k);
     const T* v = static_cast<const T*>(a.v);
+
+    // ---- loads: K, Q, V rows (zeros past n), issued before any is used
+    constexpr int NKV = C * K / EV, NVV = C * V / EV;
+    constexpr int PKQ = (NKV + NT - 1) / NT, PV = (NVV + NT - 1) / NT;
+    uint4 kr[PKQ], qr[PKQ], vr[PV];
+#pragma unroll
+    for (int p = 0; p < PKQ; ++p) {
+        const int i = tid + NT * p, r = i / (K / EV), cv = i % (K / EV);
+        kr[p] = qr[p] = make_uint4(0, 0, 0, 0);
+        if (i < NKV && r < n) {
+            kr[p] = *reinterpret_cast<const uint4*>(k + ((t0 + r) * H + h) * K + cv * EV);
+            qr[p] = *reinterpret_cast<const uint4*>(q + ((t0 + r) * H + h) * K + cv * EV);
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < PV; ++p) {
+        const int i = tid + NT * p, r = i / (V / EV), cv = i % (V / EV);
+        vr[p] = make_uint4(0, 0, 0, 0);
+        if (i < NVV && r < n)
+            vr[p] = *reinterpret_cast<const uint4*>(v + ((t0 + r) * H + h) * V + cv * EV);
+    }
 
     // ---- a1: gates and beta; cumulative log2 gate (rows >= n: g = 0, beta = 0)
     if (!PK) {
@@ -105,13 +135,16 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraLaunch a) {
                 bt = a.beta[(t0 + r) * H + h];
             }
             const float G = wave_incl_scan(gl, lane);
+            const float Gc = __shfl(G, C - 1, 64);
             if (r < C) {
                 sG[r] = G;
                 sB[r] = bt;
+                sE[r] = exp2f(G);
+                sF[r] = exp2f(fminf(Gc - G, 0.f));
             }
         }
     } else {
-        for (int d = tid; d < K; d += 256) {
+        for (int d = tid; d < K; d += NT) {
             float acc = 0.f;
             float gv[16];
             for (int r0 = 0; r0 < C; r0 += 16) {
@@ -127,63 +160,97 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraLaunch a) {
                 }
             }
         }
-        for (int r = tid; r < C; r += 256) sB[r] = r < n ? a.beta[(t0 + r) * H + h] : 0.f;
+        for (int r = tid; r < C; r += NT) sB[r] = r < n ? a.beta[(t0 + r) * H + h] : 0.f;
     }
-    // K, Q, V rows: every load issued before any is used (zeros past n)
-    constexpr int VK = C * (K / EV), VV = C * (V / EV);
-    constexpr int PK_ = (VK + 255) / 256, PV = (VV + 255) / 256;
-    uint4 kreg[PK_], qreg[PK_], vreg[PV];
 #pragma unroll
-    for (int p = 0; p < PK_; ++p) {
-        const int i = tid + 256 * p, r = i / (K / EV), cv = i - r * (K / EV);
-        kreg[p] = qreg[p] = make_uint4(0, 0, 0, 0);
-        if (i < VK && r < n) {
-            kreg[p] = *reinterpret_cast<const uint4*>(k + ((t0 + r) * H + h) * K + cv * EV);
-            qreg[p] = *reinterpret_cast<const uint4*>(q + ((t0 + r) * H + h) * K + cv * EV);
+    for (int p = 0; p < PKQ; ++p) {
+        const int i = tid + NT * p, r = i / (K / EV), cv = i % (K / EV);
+        if (i < NKV) {
+            *reinterpret_cast<uint4*>(sK + r * LDK + cv * EV) = kr[p];
+            *reinterpret_cast<uint4*>(sQ + r * LDK + cv * EV) = qr[p];
         }
     }
 #pragma unroll
     for (int p = 0; p < PV; ++p) {
-        const int i = tid + 256 * p, r = i / (V / EV), cv = i - r * (V / EV);
-        vreg[p] = make_uint4(0, 0, 0, 0);
-        if (i < VV && r < n)
-            vreg[p] = *reinterpret_cast<const uint4*>(v + ((t0 + r) * H + h) * V + cv * EV);
-    }
-#pragma unroll
-    for (int p = 0; p < PK_; ++p) {
-        const int i = tid + 256 * p, r = i / (K / EV), cv = i - r * (K / EV);
-        if (i < VK) {
-            *reinterpret_cast<uint4*>(sK + r * LDK + cv * EV) = kreg[p];
-            *reinterpret_cast<uint4*>(sQ + r * LDK + cv * EV) = qreg[p];
-        }
-    }
-    // zero A and the Aqk staging area
-    for (int i = tid; i < C * C; i += 256) {
-        const int r = i / C, j = i - r * C;
-        sA[r * LDA + j] = 0.f;
-        Elem<T>::store(sStage + r * LDC + j, 0.f);
+        const int i = tid + NT * p, r = i / (V / EV), cv = i % (V / EV);
+        if (i < NVV) *reinterpret_cast<uint4*>(sV + r * LDV + cv * EV) = vr[p];
     }
     __syncthreads();
 
-    // ---- a2: beta-scaled decay-masked strictly-lower K K^T and causal Q K^T
-    if (!PK) {
-        constexpr int NT2 = NB * (NB + 1) / 2;
-        for (int job = wave; job < 2 * NT2; job += 4) {
-            const bool isq = job >= NT2;
-            int t = isq ? job - NT2 : job, I = 0;
-            while (t > I) { t -= I + 1; ++I; }
-            const int J = t;
-            const T* A0 = (isq ? sQ : sK) + 16 * I * LDK;
-            f32x4 acc = mma_tile<T>(A0, LDK, sK + 16 * J * LDK, LDK, K, lane, zero4());
+    // ---- outputs that need only G, Q, K (stored straight from registers):
+    // Qs = scale 2^{G} Q, Ks = 2^{G_C - G} K, and the cumulative gate
+    {
+        T* gqs = static_cast<T*>(a.ws.qs) + blk * C * K;
+        T* gks = static_cast<T*>(a.ws.ks) + blk * C * K;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * I + acc_row(lane, e), j = 16 * J + acc_col(lane);
-                const float dec = exp2f(fminf(sG[i] - sG[j], 0.f));
-                if (!isq) {
-                    if (j < i) sA[i * LDA + j] = sB[i] * dec * acc[e];
-                } else if (j <= i) {
-                    Elem<T>::store(sStage + i * LDC + j, a.scale * dec * acc[e]);
+        for (int p = 0; p < PKQ; ++p) {
+            const int i = tid + NT * p, r = i / (K / EV), d0 = (i % (K / EV)) * EV;
+            if (i < NKV) {
+                const uint4 xq = *reinterpret_cast<const uint4*>(sQ + r * LDK + d0);
+                const uint4 xk = *reinterpret_cast<const uint4*>(sK + r * LDK + d0);
+                float fq[EV], fk[EV];
+                if (!PK) {
+                    const float eq = a.scale * sE[r], ek = sF[r];
+#pragma unroll
+                    for (int e = 0; e < EV; ++e) {
+                        fq[e] = eq * Vec16<T>::get(xq, e);
+                        fk[e] = ek * Vec16<T>::get(xk, e);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < EV; ++e) {
+                        const float gr = sG[r * K + d0 + e], gc = sG[(C - 1) * K + d0 + e];
+                        fq[e] = a.scale * exp2f(gr) * Vec16<T>::get(xq, e);
+                        fk[e] = exp2f(fminf(gc - gr, 0.f)) * Vec16<T>::get(xk, e);
+                    }
                 }
+                *reinterpret_cast<uint4*>(gqs + r * K + d0) = Vec16<T>::pack(fq);
+                *reinterpret_cast<uint4*>(gks + r * K + d0) = Vec16<T>::pack(fk);
+            }
+        }
+        float* gg = a.ws.gcum + blk * C * (PK ? K : 1);
+        for (int i = tid; i < C * (PK ? K : 1); i += NT) gg[i] = sG[i];
+    }
+
+    // ---- a2: beta-scaled decay-masked strictly-lower K K^T -> sA (fp32), and
+    // Aqk^T = K Q^T masked -> Aqk rows in HBM (lane: 4 consecutive columns)
+    T* gaqk = static_cast<T*>(a.ws.aqk) + blk * C * C;
+    if (!PK) {
+        constexpr int NT2 = NB * (NB + 1) / 2, NZ = NB * (NB - 1) / 2;
+        for (int job = wave; job < 2 * NT2 + NZ; job += NW) {
+            if (job < 2 * NT2) {
+                const bool isq = job >= NT2;
+                int t = isq ? job - NT2 : job, I = 0;
+                while (t > I) { t -= I + 1; ++I; }
+                const int J = t;
+                // K K^T tile (I, J): rows i in block I, columns j in block J.
+                // Q K^T as its transpose: rows j (block J, from K), columns i (block I, from Q)
+                const T* A0 = sK + 16 * (isq ? J : I) * LDK;
+                const T* B0 = (isq ? sQ : sK) + 16 * (isq ? I : J) * LDK;
+                f32x4 acc = mma_tile<T>(A0, LDK, B0, LDK, K, lane, zero4());
+                if (!isq) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 16 * I + acc_row(lane, e), j = 16 * J + acc_col(lane);
+                        sA[i * LDA + j] = j < i ? sB[i] * exp2f(fminf(sG[i] - sG[j], 0.f)) * acc[e]
+                                                : 0.f;
+                    }
+                } else {
+                    const int i = 16 * I + acc_col(lane);
+                    const float gi = sG[i];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = 16 * J + acc_row(lane, e);
+                        acc[e] = j <= i ? a.scale * exp2f(fminf(gi - sG[j], 0.f)) * acc[e] : 0.f;
+                    }
+                    store4(gaqk + i * C + 16 * J + 4 * (lane >> 4), acc);
+                }
+            } else {
+                // an upper block of Aqk: zeros
+                int t = job - 2 * NT2, I = 0;
+                while (t >= NB - 1 - I) { t -= NB - 1 - I; ++I; }
+                const int J = I + 1 + t;
+                store4(gaqk + (16 * I + acc_col(lane)) * C + 16 * J + 4 * (lane >> 4), zero4());
             }
         }
     } else {
@@ -193,7 +260,7 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraLaunch a) {
             __syncthreads();   // previous I's tiles have read the scratch
             // rows [0,16): K_I 2^{G_I - G_b}; [16,32): Q_I 2^{G_I - G_b};
             // [32, 32 + b): K_J 2^{G_b - G_J} for all J < I
-            for (int i = tid; i < (32 + b) * K; i += 256) {
+            for (int i = tid; i < (32 + b) * K; i += NT) {
                 const int r = i / K, d = i - r * K;
                 float x;
                 if (r < 32) {
@@ -208,92 +275,59 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraLaunch a) {
                 Elem<T>::store(sS + r * LDK + d, x);
             }
             __syncthreads();
-            for (int job = wave; job < 2 * I; job += 4) {
+            for (int job = wave; job < 2 * I; job += NW) {
                 const bool isq = job >= I;
                 const int J = isq ? job - I : job;
-                f32x4 acc = mma_tile<T>(sS + (isq ? 16 : 0) * LDK, LDK, sS + (32 + 16 * J) * LDK,
-                                        LDK, K, lane, zero4());
+                if (!isq) {
+                    f32x4 acc = mma_tile<T>(sS, LDK, sS + (32 + 16 * J) * LDK, LDK, K, lane,
+                                            zero4());
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 16 * I + acc_row(lane, e), j = 16 * J + acc_col(lane);
-                    if (!isq) sA[i * LDA + j] = sB[i] * acc[e];
-                    else Elem<T>::store(sStage + i * LDC + j, a.scale * acc[e]);
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 16 * I + acc_row(lane, e), j = 16 * J + acc_col(lane);
+                        sA[i * LDA + j] = sB[i] * acc[e];
+                    }
+                } else {
+                    // Aqk^T tile: rows j (block J), columns i (block I)
+                    f32x4 acc = mma_tile<T>(sS + (32 + 16 * J) * LDK, LDK, sS + 16 * LDK, LDK, K,
+                                            lane, zero4());
+                    acc *= a.scale;
+                    store4(gaqk + (16 * I + acc_col(lane)) * C + 16 * J + 4 * (lane >> 4), acc);
                 }
             }
         }
-        // diagonal 16x16 blocks, pair by pair: thread = (block, row, quarter of d)
+        // upper blocks of Aqk: zeros (those of A are masked when Ainv is read)
+        for (int i = tid; i < C * C; i += NT) {
+            const int r = i / C, j = i - r * C;
+            if (j / 16 > r / 16) Elem<T>::store(gaqk + i, 0.f);
+        }
+        // diagonal 16x16 blocks, pair by pair: thread = (block, row, slice of d)
         {
-            constexpr int DQ = K / 4;
-            const int I = tid >> 6, i = 16 * I + ((tid & 63) >> 2), s = tid & 3;
-            if (I < NB) {
-                for (int j = 16 * I; j < 16 * I + 16; ++j) {
-                    float akk = 0.f, aqk = 0.f;
-                    if (j <= i) {
-                        for (int d = s * DQ; d < s * DQ + DQ; ++d) {
-                            const float dec = exp2f(fminf(sG[i * K + d] - sG[j * K + d], 0.f));
-                            const float kj = Elem<T>::load(sK + j * LDK + d) * dec;
-                            akk += Elem<T>::load(sK + i * LDK + d) * kj;
-                            aqk += Elem<T>::load(sQ + i * LDK + d) * kj;
-                        }
+            constexpr int SL = NT / (NB * 16);      // threads per row
+            constexpr int DQ = K / SL;
+            const int I = tid / (16 * SL), i = 16 * I + (tid % (16 * SL)) / SL, s = tid % SL;
+            for (int j = 16 * I; j < 16 * I + 16; ++j) {
+                float akk = 0.f, aqk = 0.f;
+                if (j <= i) {
+                    for (int d = s * DQ; d < s * DQ + DQ; ++d) {
+                        const float dec = exp2f(fminf(sG[i * K + d] - sG[j * K + d], 0.f));
+                        const float kj = Elem<T>::load(sK + j * LDK + d) * dec;
+                        akk += Elem<T>::load(sK + i * LDK + d) * kj;
+                        aqk += Elem<T>::load(sQ + i * LDK + d) * kj;
                     }
-                    akk += __shfl_xor(akk, 1, 64);
-                    akk += __shfl_xor(akk, 2, 64);
-                    aqk += __shfl_xor(aqk, 1, 64);
-                    aqk += __shfl_xor(aqk, 2, 64);
-                    if (s == 0 && j <= i) {
-                        if (j < i) sA[i * LDA + j] = sB[i] * akk;
-                        Elem<T>::store(sStage + i * LDC + j, a.scale * aqk);
-                    }
+                }
+#pragma unroll
+                for (int off = 1; off < SL; off <<= 1) {
+                    akk += __shfl_xor(akk, off, 64);
+                    aqk += __shfl_xor(aqk, off, 64);
+                }
+                if (s == 0) {
+                    sA[i * LDA + j] = j < i ? sB[i] * akk : 0.f;
+                    Elem<T>::store(gaqk + i * C + j, j <= i ? a.scale * aqk : 0.f);
                 }
             }
         }
     }
     __syncthreads();
-
-    // ---- outputs that need only G, Q, K: Aqk, Qs, Kt, gcum
-    {
-        T* gaqk = static_cast<T*>(a.ws.aqk) + blk * C * C;
-        copy_tile<T>(gaqk, C, sStage, LDC, C, C, tid, 256);
-        T* gqs = static_cast<T*>(a.ws.qs) + blk * C * K;
-        for (int i = tid; i < C * (K / EV); i += 256) {
-            const int r = i / (K / EV), d0 = (i - r * (K / EV)) * EV;
-            const uint4 x = *reinterpret_cast<const uint4*>(sQ + r * LDK + d0);
-            float f[EV];
-#pragma unroll
-            for (int e = 0; e < EV; ++e)
-                f[e] = a.scale * exp2f(PK ? sG[r * K + d0 + e] : sG[r]) * Vec16<T>::get(x, e);
-            *reinterpret_cast<uint4*>(gqs + r * K + d0) = Vec16<T>::pack(f);
-        }
-        // Kt[d][r] = k[r][d] * 2^{G_C-1 - G_r}: 8 tokens per 16-byte store (bf16)
-        T* gkt = static_cast<T*>(a.ws.kt) + blk * K * C;
-        for (int i = tid; i < K * (C / EV); i += 256) {
-            const int d = i / (C / EV), r0 = (i - d * (C / EV)) * EV;
-            float f[EV];
-#pragma unroll
-            for (int e = 0; e < EV; ++e) {
-                const int r = r0 + e;
-                const float gl = PK ? sG[(C - 1) * K + d] - sG[r * K + d] : sG[C - 1] - sG[r];
-                f[e] = Elem<T>::load(sK + r * LDK + d) * exp2f(fminf(gl, 0.f));
-            }
-            *reinterpret_cast<uint4*>(gkt + d * C + r0) = Vec16<T>::pack(f);
-        }
-        float* gg = a.ws.gcum + blk * C * (PK ? K : 1);
-        for (int i = tid; i < C * (PK ? K : 1); i += 256) gg[i] = sG[i];
-    }
-    __syncthreads();
-
-    // ---- (beta gamma K)^T into sKT: the B operand of W
-    for (int i = tid; i < K * (C / EV); i += 256) {
-        const int d = i / (C / EV), r0 = (i - d * (C / EV)) * EV;
-        float f[EV];
-#pragma unroll
-        for (int e = 0; e < EV; ++e) {
-            const int r = r0 + e;
-            const float gm = exp2f(PK ? sG[r * K + d] : sG[r]);
-            f[e] = sB[r] * gm * Elem<T>::load(sK + r * LDK + d);
-        }
-        *reinterpret_cast<uint4*>(sKT + d * LDC + r0) = Vec16<T>::pack(f);
-    }
 
     // ---- a3: Ainv = (I + A)^{-1}
     // diagonal blocks: wave w inverts block w; lane c < 16 computes column c
@@ -336,86 +370,93 @@ __global__ __launch_bounds__(256) void intra_kernel(IntraLaunch a) {
         }
         __syncthreads();
     }
-    if (STORE_AINV) {
-        float* gai = a.ws.ainv + blk * C * C;
-        for (int i = tid; i < C * C; i += 256) gai[i] = sA[(i / C) * LDA + (i % C)];
-    }
-    // Ainv in the element type, row-major [C][LDC]
-    for (int i = tid; i < C * C; i += 256) {
-        const int r = i / C, j = i - r * C;
-        Elem<T>::store(sAb + r * LDC + j, sA[r * LDA + j]);
-    }
-    __syncthreads();
-    // (beta V)^T, the B operand of U, into the region A occupied
-#pragma unroll
-    for (int p = 0; p < PV; ++p) {
-        const int i = tid + 256 * p, r = i / (V / EV), cv = i - r * (V / EV);
-        if (i < VV) {
-            const float bt = sB[r];
-#pragma unroll
-            for (int e = 0; e < EV; ++e)
-                Elem<T>::store(sVT + (cv * EV + e) * LDC + r, bt * Vec16<T>::get(vreg[p], e));
+
+    // ---- Ainv with its columns scaled: A1 = Ainv diag(beta gamma) (for W),
+    // A2 = Ainv diag(beta) (for U).  Per-key gate: gamma is per channel and
+    // goes into K instead, so W uses A2 too.  Upper blocks were never
+    // written and are taken as zero.
+    {
+        static_assert(C * C == NT * 8, "one 8-column slice per thread");
+        const int r = tid / (C / 8), j0 = (tid % (C / 8)) * 8;
+        const bool up = j0 / 16 > r / 16;
+        float4 x0 = *reinterpret_cast<const float4*>(sA + r * LDA + j0);
+        float4 x1 = *reinterpret_cast<const float4*>(sA + r * LDA + j0 + 4);
+        if (up) x0 = x1 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (STORE_AINV) {
+            float* gai = a.ws.ainv + blk * C * C + r * C + j0;
+            *reinterpret_cast<float4*>(gai) = x0;
+            *reinterpret_cast<float4*>(gai + 4) = x1;
         }
+        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        float y1[8], y2[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int j = j0 + e;
+            y2[e] = x[e] * sB[j];
+            y1[e] = PK ? y2[e] : y2[e] * sE[j];
+        }
+        __syncthreads();   // everyone has read sA before it is overwritten
+#pragma unroll
+        for (int e = 0; e < 8; e += EV) {
+            *reinterpret_cast<uint4*>(sA1 + r * LDC + j0 + e) = Vec16<T>::pack(y1 + e);
+            *reinterpret_cast<uint4*>(sA2 + r * LDC + j0 + e) = Vec16<T>::pack(y2 + e);
+        }
+    }
+    // per-key gate: K 2^{G} (row-major) for W, in the scratch region
+    const T* sKW = sK;
+    const T* sAW = sA1;
+    if (PK) {
+        T* sKg = reinterpret_cast<T*>(smem + L::o_S);
+#pragma unroll
+        for (int p = 0; p < PKQ; ++p) {
+            const int i = tid + NT * p, r = i / (K / EV), d0 = (i % (K / EV)) * EV;
+            if (i < NKV) {
+                const uint4 xk = *reinterpret_cast<const uint4*>(sK + r * LDK + d0);
+                float f[EV];
+#pragma unroll
+                for (int e = 0; e < EV; ++e) f[e] = exp2f(sG[r * K + d0 + e]) * Vec16<T>::get(xk, e);
+                *reinterpret_cast<uint4*>(sKg + r * LDK + d0) = Vec16<T>::pack(f);
+            }
+        }
+        sKW = sKg;
+        sAW = sA2;
     }
     __syncthreads();
 
-    // ---- a4: W = Ainv (beta gamma K), U = Ainv (beta V)
-    constexpr int WJ = NB * (K / 16), UJ = NB * (V / 16);
-    constexpr int WPW = (WJ + 3) / 4, UPW = (UJ + 3) / 4;
-    f32x4 wacc[WPW], uacc[UPW];
-#pragma unroll
-    for (int s = 0; s < WPW; ++s) {
-        const int job = wave + 4 * s;
-        wacc[s] = zero4();
-        if (job < WJ) {
-            const int I = job % NB, D = job / NB;
+    // ---- a4: W^T = K^T A1^T and U^T = V^T A2^T, tile (column block D of K or
+    // V, token block I); the lane's 4 values are W[i][4 consecutive d]
+    {
+        T* gw = static_cast<T*>(a.ws.w) + blk * C * K;
+        T* gu = static_cast<T*>(a.ws.u) + blk * C * V;
+        constexpr int WJ = NB * (K / 16), UJ = NB * (V / 16);
+        for (int job = wave; job < WJ + UJ; job += NW) {
+            const bool isu = job >= WJ;
+            const int jj = isu ? job - WJ : job;
+            const int I = jj % NB, D = jj / NB;
             const int kn = min(C, ((16 * (I + 1) + KS - 1) / KS) * KS);
-            wacc[s] = mma_tile<T>(sAb + 16 * I * LDC, LDC, sKT + 16 * D * LDC, LDC, kn, lane,
-                                  zero4());
+            const T* X = isu ? sV : sKW;              // [token][d]: k-major for X^T
+            const int ldx = isu ? LDV : LDK;
+            const T* Bt = (isu ? sA2 : sAW) + (16 * I + (lane & 15)) * LDC;
+            f32x4 acc = zero4();
+            for (int k0 = 0; k0 < kn; k0 += KS)
+                acc = M::mma(M::load_t(X + k0 * ldx + 16 * D, ldx, lane), M::load(Bt + k0, lane),
+                             acc);
+            const int i = 16 * I + acc_col(lane);
+            if (isu) store4(gu + i * V + 16 * D + 4 * (lane >> 4), acc);
+            else store4(gw + i * K + 16 * D + 4 * (lane >> 4), acc);
         }
     }
-#pragma unroll
-    for (int s = 0; s < UPW; ++s) {
-        const int job = wave + 4 * s;
-        uacc[s] = zero4();
-        if (job < UJ) {
-            const int I = job % NB, D = job / NB;
-            const int kn = min(C, ((16 * (I + 1) + KS - 1) / KS) * KS);
-            uacc[s] = mma_tile<T>(sAb + 16 * I * LDC, LDC, sVT + 16 * D * LDC, LDC, kn, lane,
-                                  zero4());
-        }
-    }
-    __syncthreads();
-    T* sWst = sK;    // [C][LDK]
-    T* sUst = sVT;   // [C][LDV]
-#pragma unroll
-    for (int s = 0; s < WPW; ++s) {
-        const int job = wave + 4 * s;
-        if (job < WJ) {
-            const int I = job % NB, D = job / NB;
-            store_acc<T>(sWst + 16 * I * LDK + 16 * D, LDK, lane, wacc[s]);
-        }
-    }
-#pragma unroll
-    for (int s = 0; s < UPW; ++s) {
-        const int job = wave + 4 * s;
-        if (job < UJ) {
-            const int I = job % NB, D = job / NB;
-            store_acc<T>(sUst + 16 * I * LDV + 16 * D, LDV, lane, uacc[s]);
-        }
-    }
-    __syncthreads();
-    copy_tile<T>(static_cast<T*>(a.ws.w) + blk * C * K, K, sWst, LDK, C, K, tid, 256);
-    copy_tile<T>(static_cast<T*>(a.ws.u) + blk * C * V, V, sUst, LDV, C, V, tid, 256);
 }
 
 template <typename T, int K, int V, int C, bool PK>
 static hipError_t launch_intra_t(const IntraLaunch& a) {
     dim3 grid((unsigned)a.map.max_chunks, (unsigned)a.H);
     if (a.ws.ainv)
-        hipLaunchKernelGGL((intra_kernel<T, K, V, C, PK, true>), grid, dim3(256), 0, a.stream, a);
+        hipLaunchKernelGGL((intra_kernel<T, K, V, C, PK, true>), grid, dim3(INTRA_THREADS), 0,
+                           a.stream, a);
     else
-        hipLaunchKernelGGL((intra_kernel<T, K, V, C, PK, false>), grid, dim3(256), 0, a.stream, a);
+        hipLaunchKernelGGL((intra_kernel<T, K, V, C, PK, false>), grid, dim3(INTRA_THREADS), 0,
+                           a.stream, a);
     return hipGetLastError();
 }
 

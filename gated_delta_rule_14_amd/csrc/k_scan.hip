@@ -3,10 +3,10 @@
 // The state h (K x V, fp32) is carried serially over the chunks of one
 // (sequence, head); the value dimension is split into VT-wide tiles that run
 // as independent workgroups.  Per chunk, with the intra-chunk products in the
-// workspace (W, U, Qs = scale Q diag(gamma), Kt = (K gamma_C/gamma)^T, Aqk):
+// workspace (W, U, Qs = scale diag(gamma) Q, Ks = diag(gamma_C/gamma) K, Aqk):
 //   V_new = U - W h                                    (MFMA)
 //   O     = Qs h + Aqk V_new                           (MFMA)
-//   h    <- gamma_C h + Kt V_new                       (MFMA, fp32 accumulate)
+//   h    <- gamma_C h + Ks^T V_new                     (MFMA, fp32 accumulate)
 // ("TileLang 实战：KDA 从零到一--Gated DeltaNet" §2.3, eqs. 11-12, and §4.4
 // order: the output reads the entering state, the state is decayed before the
 // new contributions are added; "Gated Delta Network（GDN）" §4.1(d): the
@@ -14,57 +14,150 @@
 // K^T V_new; "阅读笔记：DeltaNet 在 FLA 中的代码实现笔记", forward Steps 4-5.)
 // For the per-key gate gamma_C is a vector and decays h row by row.
 //
-// h stays in MFMA accumulators for the whole sequence; a bf16 (or fp32)
-// copy of h^T in LDS is the B operand of the two products that read it.
-// Workgroups of one (sequence, head) are placed on the same XCD (the hardware
-// deals workgroups round-robin over the 8 XCDs), so they share W, Qs, Kt and
-// Aqk through that XCD's L2.
+// Mapping (8 waves): each wave owns one (16-token, 16-value) tile of V_new
+// and the matching transposed tile of O, and K/16 * VT/16 / 8 tiles of h,
+// which stays in MFMA accumulators for the whole sequence.  A bf16 (or fp32)
+// copy of h^T in LDS is the operand of the two products that read h, and
+// V_new^T in LDS feeds the other two.  O is computed transposed so each
+// lane stores 4 consecutive values of one output row straight to HBM.  The
+// next chunk's operands are loaded into registers while the current chunk
+// is computed and written to the other half of a double-buffered LDS area.
+// The workgroups of one (sequence, head) get ids equal modulo 8, so the
+// hardware's round-robin over the 8 XCDs puts them on one XCD and they share
+// W, Qs, Ks and Aqk through its L2.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
 namespace gdn {
 
-template <typename T, int K, int V, int C, int VT>
+constexpr int SCAN_THREADS = 512;
+
+template <typename T, int K, int V, int C, int VT, bool PK>
 struct ScanSmem {
     static constexpr int P = 16 / sizeof(T);
-    static constexpr int LDK = K + P;     // [C][K] row-major, [VT][K] h^T
-    static constexpr int LDC = C + P;     // [K][C] Kt, [C][C] Aqk, [VT][C] V_new^T
-    static constexpr int LDT = VT + P;    // [C][VT] U tile and O tile
-    static constexpr size_t o_W = 0;
-    static constexpr size_t o_Q = o_W + sizeof(T) * C * LDK;
-    static constexpr size_t o_Kt = o_Q + sizeof(T) * C * LDK;
-    static constexpr size_t o_Aqk = o_Kt + sizeof(T) * K * LDC;
-    static constexpr size_t o_U = o_Aqk + sizeof(T) * C * LDC;
-    static constexpr size_t o_O = o_U + sizeof(T) * C * LDT;
-    static constexpr size_t o_hT = o_O + sizeof(T) * C * LDT;
+    static constexpr int LDK = K + P;     // [C][K] row-major: W, Qs, Ks; [VT][K] h^T
+    static constexpr int LDC = C + P;     // [C][C] Aqk, [VT][C] V_new^T
+    static constexpr int LDT = VT + P;    // [C][VT] U tile
+    // one chunk's operands
+    static constexpr size_t b_W = 0;
+    static constexpr size_t b_Q = b_W + sizeof(T) * C * LDK;
+    static constexpr size_t b_K = b_Q + sizeof(T) * C * LDK;
+    static constexpr size_t b_A = b_K + sizeof(T) * C * LDK;
+    static constexpr size_t b_U = b_A + sizeof(T) * C * LDC;
+    static constexpr size_t b_D = b_U + sizeof(T) * C * LDT;
+    static constexpr size_t BUF = ((b_D + sizeof(float) * (PK ? K : 4)) + 15) / 16 * 16;
+    static constexpr size_t FIXED = sizeof(T) * VT * LDK + sizeof(T) * VT * LDC;
+    static constexpr int NBUF = 2 * BUF + FIXED <= 160 * 1024 ? 2 : 1;
+    static constexpr size_t o_hT = NBUF * BUF;
     static constexpr size_t o_Vn = o_hT + sizeof(T) * VT * LDK;
-    static constexpr size_t o_D = o_Vn + sizeof(T) * VT * LDC;
-    static constexpr size_t bytes = o_D + sizeof(float) * K;
+    static constexpr size_t bytes = o_Vn + sizeof(T) * VT * LDC;
+};
+
+// Registers holding the next chunk's operands between its load and its
+// write to LDS.  The region of each slot is fixed at compile time (W, Qs, Ks
+// are C*K/EV vectors each, Aqk C*C/EV, the U tile C*VT/EV; all multiples of
+// 64, so partial passes are wave-uniform).
+template <typename T, int PW, int PA, int PU>
+struct ScanPrefetch {
+    u32x4 w[PW], q[PW], k[PW], a[PA], u[PU];
+    float d;
+
+    template <int K, int V, int C, int VT, int NT, bool PK>
+    __device__ __forceinline__ void issue(const T* gw, const T* gq, const T* gk, const T* ga,
+                                          const T* gu, const float* gcum, int64_t blk, int v0,
+                                          int tid) {
+        constexpr int EV = 16 / sizeof(T);
+        constexpr int NWV = C * K / EV, NAV = C * C / EV, NUV = C * VT / EV;
+        const u32x4* w4 = reinterpret_cast<const u32x4*>(gw + blk * C * K);
+        const u32x4* q4 = reinterpret_cast<const u32x4*>(gq + blk * C * K);
+        const u32x4* k4 = reinterpret_cast<const u32x4*>(gk + blk * C * K);
+        const u32x4* a4 = reinterpret_cast<const u32x4*>(ga + blk * C * C);
+#pragma unroll
+        for (int p = 0; p < PW; ++p) {
+            const int i = tid + NT * p;
+            if (NWV % NT == 0 || i < NWV) {
+                w[p] = w4[i];
+                q[p] = q4[i];
+                k[p] = k4[i];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < PA; ++p) {
+            const int i = tid + NT * p;
+            if (NAV % NT == 0 || i < NAV) a[p] = a4[i];
+        }
+#pragma unroll
+        for (int p = 0; p < PU; ++p) {
+            const int i = tid + NT * p;
+            if (NUV % NT == 0 || i < NUV) {
+                const int r = i / (VT / EV), cv = i % (VT / EV);
+                u[p] = *reinterpret_cast<const u32x4*>(gu + blk * C * V + r * V + v0 + cv * EV);
+            }
+        }
+        if (PK) d = tid < K ? gcum[(blk * C + (C - 1)) * K + tid] : 0.f;
+        else d = gcum[blk * C + (C - 1)];
+    }
+
+    template <typename L, int K, int C, int VT, int NT, bool PK>
+    __device__ __forceinline__ void commit(char* buf, int tid) const {
+        constexpr int EV = 16 / sizeof(T);
+        constexpr int NWV = C * K / EV, NAV = C * C / EV, NUV = C * VT / EV;
+        T* sW = reinterpret_cast<T*>(buf + L::b_W);
+        T* sQ = reinterpret_cast<T*>(buf + L::b_Q);
+        T* sK = reinterpret_cast<T*>(buf + L::b_K);
+        T* sA = reinterpret_cast<T*>(buf + L::b_A);
+        T* sU = reinterpret_cast<T*>(buf + L::b_U);
+        float* sD = reinterpret_cast<float*>(buf + L::b_D);
+#pragma unroll
+        for (int p = 0; p < PW; ++p) {
+            const int i = tid + NT * p;
+            if (NWV % NT == 0 || i < NWV) {
+                const int o = (i / (K / EV)) * L::LDK + (i % (K / EV)) * EV;
+                *reinterpret_cast<u32x4*>(sW + o) = w[p];
+                *reinterpret_cast<u32x4*>(sQ + o) = q[p];
+                *reinterpret_cast<u32x4*>(sK + o) = k[p];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < PA; ++p) {
+            const int i = tid + NT * p;
+            if (NAV % NT == 0 || i < NAV)
+                *reinterpret_cast<u32x4*>(sA + (i / (C / EV)) * L::LDC + (i % (C / EV)) * EV) = a[p];
+        }
+#pragma unroll
+        for (int p = 0; p < PU; ++p) {
+            const int i = tid + NT * p;
+            if (NUV % NT == 0 || i < NUV)
+                *reinterpret_cast<u32x4*>(sU + (i / (VT / EV)) * L::LDT + (i % (VT / EV)) * EV) = u[p];
+        }
+        if (PK) {
+            if (tid < K) sD[tid] = exp2f(d);
+        } else if (tid == 0) {
+            sD[0] = exp2f(d);
+        }
+    }
 };
 
 template <typename T, int K, int V, int C, int VT, bool PK>
-__global__ __launch_bounds__(256) void scan_kernel(ScanLaunch a) {
-    typedef ScanSmem<T, K, V, C, VT> L;
+__global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanLaunch a) {
+    typedef ScanSmem<T, K, V, C, VT, PK> L;
+    typedef Mma<T> M;
+    constexpr int NT = SCAN_THREADS, NW = NT / 64;
     constexpr int LDK = L::LDK, LDC = L::LDC, LDT = L::LDT;
-    constexpr int KS = Mma<T>::KSTEP;
+    constexpr int KS = M::KSTEP;
+    constexpr int EV = 16 / sizeof(T);
     constexpr int NVT = V / VT;
-    constexpr int RT = K / 64;      // 16-row h tiles per wave
-    constexpr int CT = VT / 16;     // 16-col tiles
-    static_assert(K % 64 == 0 && VT % 16 == 0 && V % VT == 0, "tile shape");
+    constexpr int CT = VT / 16;              // value tiles
+    constexpr int TT = C / 16;               // token tiles
+    constexpr int NHT = (K / 16) * CT;       // h tiles
+    constexpr int HPW = (NHT + NW - 1) / NW; // h tiles per wave
+    static_assert(TT * CT <= NW, "one V_new tile per wave");
+    static_assert(K % 16 == 0 && VT % 16 == 0 && V % VT == 0, "tile shape");
     __shared__ __attribute__((aligned(16))) char smem[L::bytes];
-    T* sW = reinterpret_cast<T*>(smem + L::o_W);
-    T* sQ = reinterpret_cast<T*>(smem + L::o_Q);
-    T* sKt = reinterpret_cast<T*>(smem + L::o_Kt);
-    T* sAqk = reinterpret_cast<T*>(smem + L::o_Aqk);
-    T* sU = reinterpret_cast<T*>(smem + L::o_U);
-    T* sO = reinterpret_cast<T*>(smem + L::o_O);
     T* shT = reinterpret_cast<T*>(smem + L::o_hT);
     T* sVn = reinterpret_cast<T*>(smem + L::o_Vn);
-    float* sD = reinterpret_cast<float*>(smem + L::o_D);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // XCD-aware placement: the NVT tiles of a chain get ids that are equal
-    // modulo 8, i.e. land on the same XCD.
     const int64_t bid = blockIdx.x;
     const int vt = (int)((bid >> 3) % NVT);
     const int64_t chain = (bid & 7) + 8 * ((bid >> 3) / NVT);
@@ -84,192 +177,140 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanLaunch a) {
         c0 = n * a.map.nt;
     }
 
-    // h: wave w owns rows [w*K/4, (w+1)*K/4), all VT columns
-    f32x4 hacc[RT][CT];
+    // ---- h tiles owned by this wave: tile id = wave + NW * s -> (row block, value tile)
+    f32x4 hacc[HPW];
     const float* h0 = a.h0 ? a.h0 + (n * a.H + h) * (int64_t)(K * V) : nullptr;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int s = 0; s < HPW; ++s) {
+        const int id = wave + NW * s;
+        hacc[s] = zero4();
+        if (id < NHT) {
+            const int rb = 16 * (id / CT), ct = id % CT;
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = wave * (K / 4) + 16 * rt + acc_row(lane, e);
-                const int col = v0 + 16 * ct + acc_col(lane);
-                hacc[rt][ct][e] = h0 ? h0[row * V + col] : 0.f;
-            }
-            store_acc_t(shT + (16 * ct) * LDK + wave * (K / 4) + 16 * rt, LDK, lane,
-                        hacc[rt][ct]);
+            for (int e = 0; e < 4; ++e)
+                hacc[s][e] = h0 ? h0[(rb + acc_row(lane, e)) * V + v0 + 16 * ct + acc_col(lane)]
+                                : 0.f;
+            store_acc_t(shT + (16 * ct) * LDK + rb, LDK, lane, hacc[s]);
         }
+    }
 
-    // ---- chunk operands: W, Qs [C][K], Kt [K][C], Aqk [C][C], U tile [C][VT],
-    // moved as 16-byte vectors.  Chunk j+1 is loaded into registers while
-    // chunk j is computed, then written to LDS.
-    constexpr int EV = 16 / sizeof(T);
-    constexpr int VW = C * K / EV, VQ = C * K / EV, VK = K * C / EV, VA = C * C / EV,
-                  VU = C * VT / EV;
-    constexpr int NV = VW + VQ + VK + VA + VU;
-    constexpr int PER = (NV + 255) / 256;
-    uint4 pre[PER];
-    float pre_d = 0.f;
+    // ---- chunk operands, 16-byte vectors; the region of each register slot is
+    // fixed at compile time (W, Qs, Ks are C*K/EV vectors each, Aqk C*C/EV,
+    // the U tile C*VT/EV; all multiples of 64, so partial passes are
+    // wave-uniform)
+    constexpr int NWV = C * K / EV, NAV = C * C / EV, NUV = C * VT / EV;
+    constexpr int PW = (NWV + NT - 1) / NT, PA = (NAV + NT - 1) / NT, PU = (NUV + NT - 1) / NT;
+    static_assert(NWV % 64 == 0 && NAV % 64 == 0 && NUV % 64 == 0, "wave-uniform passes");
+    ScanPrefetch<T, PW, PA, PU> pre;
     const T* gw = static_cast<const T*>(a.ws.w);
     const T* gq = static_cast<const T*>(a.ws.qs);
-    const T* gk = static_cast<const T*>(a.ws.kt);
+    const T* gk = static_cast<const T*>(a.ws.ks);
     const T* ga = static_cast<const T*>(a.ws.aqk);
     const T* gu = static_cast<const T*>(a.ws.u);
-    auto issue = [&](int64_t blk) {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int i = tid + 256 * p;
-            const uint4* src;
-            if (i < VW) src = reinterpret_cast<const uint4*>(gw + blk * C * K) + i;
-            else if (i < VW + VQ) src = reinterpret_cast<const uint4*>(gq + blk * C * K) + (i - VW);
-            else if (i < VW + VQ + VK)
-                src = reinterpret_cast<const uint4*>(gk + blk * K * C) + (i - VW - VQ);
-            else if (i < VW + VQ + VK + VA)
-                src = reinterpret_cast<const uint4*>(ga + blk * C * C) + (i - VW - VQ - VK);
-            else if (i < NV) {
-                const int u = i - (VW + VQ + VK + VA), r = u / (VT / EV), cv = u - r * (VT / EV);
-                src = reinterpret_cast<const uint4*>(gu + blk * C * V + r * V + v0) + cv;
-            } else {
-                src = nullptr;
-            }
-            pre[p] = src ? *src : make_uint4(0, 0, 0, 0);
-        }
-        if (PK) pre_d = tid < K ? a.ws.gcum[(blk * C + (C - 1)) * K + tid] : 0.f;
-        else pre_d = a.ws.gcum[blk * C + (C - 1)];
-    };
-    float dsc = 0.f;
-    auto commit = [&]() {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int i = tid + 256 * p;
-            T* dst;
-            if (i < VW) {
-                const int r = i / (K / EV), cv = i - r * (K / EV);
-                dst = sW + r * LDK + cv * EV;
-            } else if (i < VW + VQ) {
-                const int u = i - VW, r = u / (K / EV), cv = u - r * (K / EV);
-                dst = sQ + r * LDK + cv * EV;
-            } else if (i < VW + VQ + VK) {
-                const int u = i - VW - VQ, r = u / (C / EV), cv = u - r * (C / EV);
-                dst = sKt + r * LDC + cv * EV;
-            } else if (i < VW + VQ + VK + VA) {
-                const int u = i - VW - VQ - VK, r = u / (C / EV), cv = u - r * (C / EV);
-                dst = sAqk + r * LDC + cv * EV;
-            } else if (i < NV) {
-                const int u = i - (VW + VQ + VK + VA), r = u / (VT / EV), cv = u - r * (VT / EV);
-                dst = sU + r * LDT + cv * EV;
-            } else {
-                dst = nullptr;
-            }
-            if (dst) *reinterpret_cast<uint4*>(dst) = pre[p];
-        }
-        if (PK) {
-            if (tid < K) sD[tid] = exp2f(pre_d);
-        } else {
-            dsc = exp2f(pre_d);
-        }
-    };
+#define GDN_SCAN_ISSUE(BLK)                                                                   \
+    pre.template issue<K, V, C, VT, NT, PK>(gw, gq, gk, ga, gu, a.ws.gcum, (BLK), v0, tid)
+#define GDN_SCAN_COMMIT(BUF)                                                                  \
+    pre.template commit<L, K, C, VT, NT, PK>((BUF), tid)
 
     const int nch = (int)((len + C - 1) / C);
     T* o = static_cast<T*>(a.o);
+    // this wave's V_new / O tile
+    const int tt = wave % TT, ct = wave / TT;
+    const bool has_tile = wave < TT * CT;
     if (nch > 0 && c0 < a.map.max_chunks) {
-        issue(h * a.map.max_chunks + c0);
-        commit();
+        GDN_SCAN_ISSUE(h * a.map.max_chunks + c0);
+        GDN_SCAN_COMMIT(smem);
     }
     __syncthreads();
     for (int j = 0; j < nch; ++j) {
         const int64_t c = c0 + j;
         if (c >= a.map.max_chunks) break;
+        char* buf = smem + (L::NBUF == 2 ? (j & 1) * L::BUF : 0);
+        const T* sW = reinterpret_cast<const T*>(buf + L::b_W);
+        const T* sQ = reinterpret_cast<const T*>(buf + L::b_Q);
+        const T* sK = reinterpret_cast<const T*>(buf + L::b_K);
+        const T* sA = reinterpret_cast<const T*>(buf + L::b_A);
+        const T* sU = reinterpret_cast<const T*>(buf + L::b_U);
+        const float* sD = reinterpret_cast<const float*>(buf + L::b_D);
         const int64_t tt0 = t0 + (int64_t)j * C;
         const int ntok = (int)min((int64_t)C, len - (int64_t)j * C);
         const bool more = j + 1 < nch && c + 1 < a.map.max_chunks;
-        if (more) issue(h * a.map.max_chunks + c + 1);
-        const float dcur = dsc;
+        if (more) GDN_SCAN_ISSUE(h * a.map.max_chunks + c + 1);
 
-        // ---- V_new = U - W h and O = Qs h, one 16-row tile per wave
-        f32x4 ov[CT];
-        if (wave < C / 16) {
-            f32x4 vn[CT];
+        // ---- V_new = U - W h (tile tokens tt x values ct) and
+        //      O^T = h^T Qs^T (tile values ct x tokens tt); both read the same
+        //      h^T fragment (as B in the first product, as A in the second)
+        f32x4 ov = zero4();
+        if (has_tile) {
+            f32x4 vn = zero4();
+            const T* wr = sW + (16 * tt + (lane & 15)) * LDK;
+            const T* qr = sQ + (16 * tt + (lane & 15)) * LDK;
+            const T* hr = shT + (16 * ct + (lane & 15)) * LDK;
+            float u[4];
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                vn[ct] = zero4();
-                ov[ct] = zero4();
-            }
-            const T* wr = sW + (16 * wave + (lane & 15)) * LDK;
-            const T* qr = sQ + (16 * wave + (lane & 15)) * LDK;
+            for (int e = 0; e < 4; ++e)
+                u[e] = Elem<T>::load(sU + (16 * tt + acc_row(lane, e)) * LDT + 16 * ct +
+                                     acc_col(lane));
 #pragma unroll
             for (int k0 = 0; k0 < K; k0 += KS) {
-                const typename Mma<T>::frag fw = Mma<T>::load(wr + k0, lane);
-                const typename Mma<T>::frag fq = Mma<T>::load(qr + k0, lane);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    const typename Mma<T>::frag fh =
-                        Mma<T>::load(shT + (16 * ct + (lane & 15)) * LDK + k0, lane);
-                    vn[ct] = Mma<T>::mma(fw, fh, vn[ct]);
-                    ov[ct] = Mma<T>::mma(fq, fh, ov[ct]);
-                }
+                const typename M::frag fh = M::load(hr + k0, lane);
+                vn = M::mma(M::load(wr + k0, lane), fh, vn);
+                ov = M::mma(fh, M::load(qr + k0, lane), ov);
             }
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * wave + acc_row(lane, e);
-                    vn[ct][e] = Elem<T>::load(sU + r * LDT + 16 * ct + acc_col(lane)) - vn[ct][e];
-                }
-                store_acc_t(sVn + (16 * ct) * LDC + 16 * wave, LDC, lane, vn[ct]);
-            }
+            for (int e = 0; e < 4; ++e) vn[e] = u[e] - vn[e];
+            store_acc_t(sVn + (16 * ct) * LDC + 16 * tt, LDC, lane, vn);   // V_new^T
         }
         __syncthreads();
 
-        // ---- O += Aqk V_new; h <- gamma_C h + Kt V_new
-        if (wave < C / 16) {
-            const int kn = min(C, ((16 * (wave + 1) + KS - 1) / KS) * KS);
+        // ---- O^T += V_new^T Aqk^T, store O; h <- gamma_C h + Ks^T V_new
+        if (has_tile) {
+            const int kn = min(C, ((16 * (tt + 1) + KS - 1) / KS) * KS);
+            ov = mma_tile<T>(sVn + 16 * ct * LDC, LDC, sA + 16 * tt * LDC, LDC, kn, lane, ov);
+            const int tok = 16 * tt + acc_col(lane);
+            if (tok < ntok)
+                store4(o + ((tt0 + tok) * a.H + h) * V + v0 + 16 * ct + 4 * (lane >> 4), ov);
+        }
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                ov[ct] = mma_tile<T>(sAqk + 16 * wave * LDC, LDC, sVn + 16 * ct * LDC, LDC, kn,
-                                     lane, ov[ct]);
-                store_acc<T>(sO + 16 * wave * LDT + 16 * ct, LDT, lane, ov[ct]);
+        for (int s = 0; s < HPW; ++s) {
+            const int id = wave + NW * s;
+            if (id < NHT) {
+                const int rb = 16 * (id / CT), hc = id % CT;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hacc[s][e] *= PK ? sD[rb + acc_row(lane, e)] : sD[0];
+                const T* vr = sVn + (16 * hc + (lane & 15)) * LDC;
+#pragma unroll
+                for (int k0 = 0; k0 < C; k0 += KS)
+                    hacc[s] = M::mma(M::load_t(sK + k0 * LDK + rb, LDK, lane), M::load(vr + k0, lane),
+                                     hacc[s]);
+                store_acc_t(shT + (16 * hc) * LDK + rb, LDK, lane, hacc[s]);
             }
         }
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int rb = wave * (K / 4) + 16 * rt;
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    hacc[rt][ct][e] *= PK ? sD[rb + acc_row(lane, e)] : dcur;
-                hacc[rt][ct] = mma_tile<T>(sKt + rb * LDC, LDC, sVn + 16 * ct * LDC, LDC, C, lane,
-                                           hacc[rt][ct]);
-                store_acc_t(shT + (16 * ct) * LDK + rb, LDK, lane, hacc[rt][ct]);
+        if (more) {
+            if (L::NBUF == 2) {
+                GDN_SCAN_COMMIT(smem + ((j + 1) & 1) * L::BUF);
+            } else {
+                __syncthreads();   // single buffer: every wave is done with this chunk
+                GDN_SCAN_COMMIT(smem);
             }
         }
-        __syncthreads();
-
-        // ---- O tile to HBM (rows past the end of the sequence are dropped),
-        // then the prefetched chunk into LDS
-        for (int i = tid; i < ntok * (VT / EV); i += 256) {
-            const int r = i / (VT / EV), cv = i - r * (VT / EV);
-            *reinterpret_cast<uint4*>(o + ((tt0 + r) * a.H + h) * V + v0 + cv * EV) =
-                *reinterpret_cast<const uint4*>(sO + r * LDT + cv * EV);
-        }
-        if (more) commit();
         __syncthreads();
     }
 
+#undef GDN_SCAN_ISSUE
+#undef GDN_SCAN_COMMIT
     if (a.ht) {
         float* ht = a.ht + (n * a.H + h) * (int64_t)(K * V);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int s = 0; s < HPW; ++s) {
+            const int id = wave + NW * s;
+            if (id < NHT) {
+                const int rb = 16 * (id / CT), hc = id % CT;
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = wave * (K / 4) + 16 * rt + acc_row(lane, e);
-                    const int col = v0 + 16 * ct + acc_col(lane);
-                    ht[row * V + col] = hacc[rt][ct][e];
-                }
+                for (int e = 0; e < 4; ++e)
+                    ht[(rb + acc_row(lane, e)) * V + v0 + 16 * hc + acc_col(lane)] = hacc[s][e];
+            }
+        }
     }
 }
 
@@ -277,8 +318,8 @@ template <typename T, int K, int V, int C, int VT, bool PK>
 static hipError_t launch_scan_t(const ScanLaunch& a) {
     const int64_t chains = a.N * a.H;
     const int64_t nblk = ((chains + 7) / 8) * 8 * (V / VT);
-    hipLaunchKernelGGL((scan_kernel<T, K, V, C, VT, PK>), dim3((unsigned)nblk), dim3(256), 0,
-                       a.stream, a);
+    hipLaunchKernelGGL((scan_kernel<T, K, V, C, VT, PK>), dim3((unsigned)nblk), dim3(SCAN_THREADS),
+                       0, a.stream, a);
     return hipGetLastError();
 }
 
@@ -298,7 +339,7 @@ static hipError_t launch_scan_dt(const ScanLaunch& a) {
 
 hipError_t launch_scan(const ScanLaunch& a) {
     if (a.C != 64) return hipErrorInvalidValue;
-    return a.bf16 ? launch_scan_dt<bf16, 32>(a) : launch_scan_dt<float, 16>(a);
+    return a.bf16 ? launch_scan_dt<bf16, 32>(a) : launch_scan_dt<float, 32>(a);
 }
 
 }  // namespace gdn

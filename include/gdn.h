@@ -152,7 +152,7 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_desc *d,
  *   w     [H][mc][C][K]     W = (I+A)^{-1} diag(beta) diag(gamma) K
  *   u     [H][mc][C][V]     U = (I+A)^{-1} diag(beta) V
  *   qs    [H][mc][C][K]     scale * diag(gamma) Q
- *   kt    [H][mc][K][C]     (diag(gamma_C / gamma) K)^T
+ *   ks    [H][mc][C][K]     diag(gamma_C / gamma) K
  *   aqk   [H][mc][C][C]     scale * (Q K^T masked by Gamma, diagonal kept)
  *   ainv  float [H][mc][C][C]  (I+A)^{-1}; written only by gdn_chunk_intra
  *   chunks int32 [mc][4]    (first token, token count, sequence, 0) per chunk
@@ -160,13 +160,13 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_desc *d,
  *   seqs  int32 [N][4]      (first token, length, first chunk slot, chunks)
  *                           (packed input only)
  * A = strictLower(diag(beta) (Gamma * K K^T)), Gamma_ij = 2^(G_i - G_j) for
- * j <= i.  w, u, qs, kt and aqk have the element type qkv_dtype.  For the
+ * j <= i.  w, u, qs, ks and aqk have the element type qkv_dtype.  For the
  * per-key gate gamma is per channel and every Gamma factor sits inside the
  * sum over the key channel.  A descriptor with num_seqs > 0 describes packed
  * input.
  */
 typedef struct gdn_workspace_layout {
-    size_t gcum, w, u, qs, kt, aqk, ainv, chunks, seqs;
+    size_t gcum, w, u, qs, ks, aqk, ainv, chunks, seqs;
     size_t total;        /* == gdn_chunk_fwd_workspace() */
     int64_t max_chunks;  /* chunk slots per head (mc) */
 } gdn_workspace_layout;
@@ -181,7 +181,7 @@ gdn_status gdn_workspace_layout_of(const gdn_fwd_desc *d, gdn_workspace_layout *
  * gdn_chunk_intra: the intra-chunk stage ("TileLang 实战" §2.2.4, §2.3 and
  * §4.1-4.2; "阅读笔记：DeltaNet 在 FLA 中的代码实现笔记", forward Steps 1-3):
  * cumulative gates, the beta-scaled decay-masked strictly-lower K K^T, its
- * unit-lower inverse, W, U, Qs, Kt and the causal Q K^T block, left in the
+ * unit-lower inverse, W, U, Qs, Ks and the causal Q K^T block, left in the
  * workspace as gdn_workspace_layout_of describes.  With
  * flags & GDN_INTRA_STORE_AINV the inverse (I+A)^{-1} is written too (for
  * checking the stage; gdn_chunk_fwd does not write it).  Arguments as for
@@ -199,7 +199,7 @@ gdn_status gdn_chunk_intra(const gdn_fwd_desc *d,
  * gdn_chunk_scan: the inter-chunk state pass with the chunk output ("TileLang
  * 实战" §2.3 eqs. 11-12; "Gated Delta Network（GDN）" §4.1(d); "阅读笔记"
  * forward Steps 4-5), serial over the chunks of each sequence:
- *   V_new = U - W h,  o = Qs h + Aqk V_new,  h <- gamma_C h + Kt V_new.
+ *   V_new = U - W h,  o = Qs h + Aqk V_new,  h <- gamma_C h + Ks^T V_new.
  * The workspace must hold what gdn_chunk_intra left there for the same
  * descriptor, inputs and cu_seqlens (which is only used to know the number
  * of sequences; the chunk table comes from the workspace).  h0, o, ht as for

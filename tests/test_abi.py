@@ -69,7 +69,7 @@ def test_workspace_size_and_layout(lib):
     assert L.w - L.gcum >= blocks * 64 * 4
     assert L.u - L.w >= blocks * 64 * 128 * 2
     assert L.total >= L.chunks
-    offs = [L.gcum, L.w, L.u, L.qs, L.kt, L.aqk, L.ainv, L.chunks, L.total]
+    offs = [L.gcum, L.w, L.u, L.qs, L.ks, L.aqk, L.ainv, L.chunks, L.total]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert gdn.workspace_bytes(d) == L.total
     # packed: one extra chunk slot per sequence
