@@ -112,7 +112,7 @@ def bench_prefill(args, gdn):
     # per-kernel durations (HIP events on the launch stream)
     reps = max(args.steps, 10)
     t_intra = events_time(lambda: gdn.chunk_intra(q, k, v, beta, g, d["scale"],
-                                                  store_ainv=False, workspace=ws), reps)
+                                                  store_ainv=False, workspace=ws, views=False), reps)
     t_scan = events_time(lambda: gdn.chunk_scan(desc, ws, o, h0=h0, ht=ht), reps)
     log("intra %.1f us, scan %.1f us" % (t_intra * 1e6, t_scan * 1e6))
 

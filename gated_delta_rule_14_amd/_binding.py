@@ -186,9 +186,12 @@ def chunk_fwd(q, k, v, beta, g, scale=None, h0=None, cu_seqlens=None, chunk=64,
 
 
 def chunk_intra(q, k, v, beta, g, scale=None, cu_seqlens=None, chunk=64, gate="scalar",
-                store_ainv=True, workspace=None, stream=None):
-    """gdn_chunk_intra: the intra-chunk stage alone.  Returns a dict of views
-    into the workspace: gcum, w, u, qs, ks, aqk, ainv, max_chunks, workspace."""
+                store_ainv=True, workspace=None, stream=None, views=True):
+    """gdn_chunk_intra: the intra-chunk stage alone.  Returns a dict: gcum and
+    ainv (views into the workspace), w, u, qs, ks, aqk (row-major copies of
+    the workspace arrays, which the library keeps in MFMA fragment /
+    accumulator order), max_chunks, workspace and desc.  views=False skips
+    the arrays (no work beyond the library call)."""
     lib = load()
     _inputs(q, k, v, beta, g, cu_seqlens, gate)
     N = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
@@ -202,6 +205,8 @@ def chunk_intra(q, k, v, beta, g, scale=None, cu_seqlens=None, chunk=64, gate="s
                                ws.numel() * ws.element_size(),
                                INTRA_STORE_AINV if store_ainv else 0, _stream(stream)))
     H, K, V, C, mc = q.shape[2], q.shape[3], v.shape[3], chunk, L.max_chunks
+    if not views:
+        return dict(max_chunks=mc, workspace=ws, desc=desc)
 
     def view(off, dtype, shape):
         n = 1
@@ -210,12 +215,42 @@ def chunk_intra(q, k, v, beta, g, scale=None, cu_seqlens=None, chunk=64, gate="s
         es = torch.empty(0, dtype=dtype).element_size()
         return ws[off:off + n * es].view(dtype).view(*shape)
     gshape = (H, mc, C, K) if gate == "per_key" else (H, mc, C)
+    lead = (H, mc)
     return dict(gcum=view(L.gcum, torch.float32, gshape),
-                w=view(L.w, q.dtype, (H, mc, C, K)), u=view(L.u, q.dtype, (H, mc, C, V)),
-                qs=view(L.qs, q.dtype, (H, mc, C, K)), ks=view(L.ks, q.dtype, (H, mc, C, K)),
-                aqk=view(L.aqk, q.dtype, (H, mc, C, C)),
+                w=from_frag_order(view(L.w, q.dtype, lead + (C * K,)), C, K),
+                u=from_acc_order(view(L.u, q.dtype, lead + (C * V,)), C, V),
+                qs=from_frag_order(view(L.qs, q.dtype, lead + (C * K,)), C, K),
+                ks=from_frag_order(view(L.ks, q.dtype, lead + (K * C,)), K, C).transpose(-1, -2),
+                aqk=from_frag_order(view(L.aqk, q.dtype, lead + (C * C,)), C, C),
                 ainv=view(L.ainv, torch.float32, (H, mc, C, C)), max_chunks=mc,
                 workspace=ws, desc=desc)
+
+
+def from_frag_order(x, R, D):
+    """An R x D matrix stored in MFMA fragment order (last dim of x, R*D
+    elements) as an [..., R, D] tensor (a reordered copy).  Group (rt, sg),
+    lane l = 16 g + r, element e holds X[16 rt + r][KG sg + col], col = 8 g + e
+    for bf16 (KG 32) and 4 e + g for fp32 (KG 16)."""
+    lead = tuple(x.shape[:-1])
+    n = len(lead)
+    if x.dtype == torch.bfloat16:
+        y = x.reshape(*lead, R // 16, D // 32, 4, 16, 8)           # rt sg g r e
+        order = (0, 3, 1, 2, 4)                                      # rt r sg g e
+    else:
+        y = x.reshape(*lead, R // 16, D // 16, 4, 16, 4)           # rt sg g r e
+        order = (0, 3, 1, 4, 2)                                      # rt r sg e g
+    y = y.permute(*range(n), *(n + o for o in order))
+    return y.reshape(*lead, R, D)
+
+
+def from_acc_order(x, R, D):
+    """An R x D matrix stored in accumulator order (tile (rt, ct), lane
+    l = 16 g + c, element e holds X[16 rt + 4 g + e][16 ct + c]) as [..., R, D]."""
+    lead = tuple(x.shape[:-1])
+    n = len(lead)
+    y = x.reshape(*lead, R // 16, D // 16, 4, 16, 4)                # rt ct g c e
+    y = y.permute(*range(n), *(n + o for o in (0, 2, 4, 1, 3)))     # rt g e ct c
+    return y.reshape(*lead, R, D)
 
 
 def chunk_scan(desc, workspace, o, h0=None, ht=None, cu_seqlens=None, stream=None):

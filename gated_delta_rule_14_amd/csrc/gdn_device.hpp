@@ -42,14 +42,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 
 // element traits: loads/stores of the q/k/v/o element type through float
 template <typename T> struct Elem;
+// Raw / load_raw / from_raw split a load from its conversion, so that a value
+// loaded well ahead of its use is not waited for at the load.
 template <> struct Elem<float> {
     static constexpr int BYTES = 4;
+    typedef float Raw;
     __device__ __forceinline__ static float load(const float* p) { return *p; }
+    __device__ __forceinline__ static Raw load_raw(const float* p) { return *p; }
+    __device__ __forceinline__ static float from_raw(Raw r) { return r; }
     __device__ __forceinline__ static void store(float* p, float x) { *p = x; }
 };
 template <> struct Elem<bf16> {
     static constexpr int BYTES = 2;
+    typedef uint32_t Raw;   // the 16 payload bits, zero-extended
     __device__ __forceinline__ static float load(const bf16* p) { return bf16_to_f32(p->bits); }
+    __device__ __forceinline__ static Raw load_raw(const bf16* p) { return p->bits; }
+    __device__ __forceinline__ static float from_raw(Raw r) { return __uint_as_float(r << 16); }
     __device__ __forceinline__ static void store(bf16* p, float x) { p->bits = f32_to_bf16(x); }
 };
 
@@ -76,6 +84,17 @@ template <> struct Vec16<float> {
                           __float_as_uint(f[3]));
     }
 };
+
+// 2^x with the hardware exponential (one instruction, about 1 ulp).  Every
+// argument here is a log2 decay <= 0, so the result lies in [0, 1]; results
+// below the smallest normal float may flush to zero.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Index of the calling wave in its workgroup, in a scalar register: branches
+// on it are then taken per wave instead of being masked lane by lane.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
@@ -125,6 +144,70 @@ template <> struct Mma<float> {
         return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
     }
 };
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// Four consecutive elements of T: their raw 8 (bf16) or 16 (fp32) bytes, one
+// load, and the floats they hold.
+template <typename T> struct Quad;
+template <> struct Quad<bf16> {
+    typedef u32x2 raw;
+    __device__ __forceinline__ static raw load(const bf16* p) {
+        return *reinterpret_cast<const u32x2*>(p);
+    }
+    __device__ __forceinline__ static f32x4 get(raw r) {
+        return f32x4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                     __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
+    }
+};
+template <> struct Quad<float> {
+    typedef u32x4 raw;
+    __device__ __forceinline__ static raw load(const float* p) {
+        return *reinterpret_cast<const u32x4*>(p);
+    }
+    __device__ __forceinline__ static f32x4 get(raw r) { return __builtin_bit_cast(f32x4, r); }
+};
+
+// Fragment order ("F-order") of an R x D matrix X (R a multiple of 16, D of
+// KG): 16-byte groups, group (rt, sg) holding for lane l the VE elements
+// X[16 rt + l%16][KG sg + col(l, e)], e < VE, at element offset
+// ((rt * D/KG + sg) * 64 + l) * VE.  A bf16 group is exactly the MFMA A
+// fragment of rows 16rt.. and k = 32sg.. (or the B fragment of X^T); an fp32
+// group packs the fragments of 4 consecutive k-steps (element e is k-step
+// 4sg + e).  Loading one fragment is then one coalesced 16-byte load per lane.
+template <typename T> struct FragOrder;
+template <> struct FragOrder<bf16> {
+    static constexpr int VE = 8, KG = 32;
+    __device__ __forceinline__ static int col(int l, int e) { return 8 * (l >> 4) + e; }
+    __device__ __forceinline__ static int64_t off(int r, int d, int D) {
+        const int dd = d & 31;
+        return ((int64_t)(((r >> 4) * (D >> 5) + (d >> 5)) * 64 + (r & 15) + 16 * (dd >> 3)) << 3) +
+               (dd & 7);
+    }
+    __device__ __forceinline__ static Mma<bf16>::frag frag(u32x4 g, int) {
+        return __builtin_bit_cast(bf16x8, g);
+    }
+};
+template <> struct FragOrder<float> {
+    static constexpr int VE = 4, KG = 16;
+    __device__ __forceinline__ static int col(int l, int e) { return 4 * e + (l >> 4); }
+    __device__ __forceinline__ static int64_t off(int r, int d, int D) {
+        const int dd = d & 15;
+        return ((int64_t)(((r >> 4) * (D >> 4) + (d >> 4)) * 64 + (r & 15) + 16 * (dd & 3)) << 2) +
+               (dd >> 2);
+    }
+    __device__ __forceinline__ static Mma<float>::frag frag(u32x4 g, int i) {
+        return __uint_as_float(g[i]);
+    }
+};
+
+// Accumulator order ("C-order") of an R x D matrix: tile (rt, ct) of 64 lanes
+// x 4 elements, lane l holding X[16 rt + 4(l/16) + e][16 ct + l%16], the
+// layout of an MFMA result tile.  Offset of X[r][d] in elements:
+__device__ __forceinline__ int64_t acc_order_off(int r, int d, int D) {
+    return ((int64_t)(((r >> 4) * (D >> 4) + (d >> 4)) * 64 + (d & 15) + 16 * ((r & 15) >> 2))
+            << 2) + (r & 3);
+}
 
 // C(16x16) += A(16 x kn) * B(kn x 16); A row-major at `a` (pitch lda), B
 // stored transposed (n-major, k contiguous) at `bt` (pitch ldb).  Pointers
@@ -177,6 +260,16 @@ __device__ __forceinline__ void store4(bf16* dst, f32x4 v) {
 }
 __device__ __forceinline__ void store4(float* dst, f32x4 v) {
     *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+}
+// 4 consecutive columns d0..d0+3 (d0 % 4 == 0) of row r of an F-order
+// matrix with D columns: one 8-byte store for bf16, four element stores for
+// fp32 (whose consecutive columns sit in different lanes' groups).
+__device__ __forceinline__ void store4_frag(bf16* base, int r, int d0, int D, f32x4 v) {
+    store4(base + FragOrder<bf16>::off(r, d0, D), v);
+}
+__device__ __forceinline__ void store4_frag(float* base, int r, int d0, int D, f32x4 v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) base[FragOrder<float>::off(r, d0 + e, D)] = v[e];
 }
 // ... and row-major: dst[row * ld + col] (element stores)
 template <typename T>

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
     T* sA1 = sQ;                              // Ainv diag(beta gamma)   (after Q is used)
     T* sA2 = reinterpret_cast<T*>(sA);        // Ainv diag(beta)         (after A is used)
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int64_t c = blockIdx.x, h = blockIdx.y, H = a.H;
 
     // ---- which tokens this chunk covers
@@ -104,25 +104,24 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
     const T* k = static_cast<const T*>(a.k);
     const T* v = static_cast<const T*>(a.v);
 
-    // ---- loads: K, Q, V rows (zeros past n), issued before any is used
+    // ---- loads: K, Q, V rows, issued before any is used.  Rows past n (tail
+    // chunk) repeat row n-1: with beta = 0 there, their rows and columns of
+    // A, Ainv diag(beta), W and U come out exactly zero, so they never reach
+    // an output, and the loads need no branch.
     constexpr int NKV = C * K / EV, NVV = C * V / EV;
-    constexpr int PKQ = (NKV + NT - 1) / NT, PV = (NVV + NT - 1) / NT;
-    uint4 kr[PKQ], qr[PKQ], vr[PV];
+    static_assert(NKV % NT == 0 && NVV % NT == 0, "whole passes");
+    constexpr int PKQ = NKV / NT, PV = NVV / NT;
+    u32x4 kr[PKQ], qr[PKQ], vr[PV];
 #pragma unroll
     for (int p = 0; p < PKQ; ++p) {
-        const int i = tid + NT * p, r = i / (K / EV), cv = i % (K / EV);
-        kr[p] = qr[p] = make_uint4(0, 0, 0, 0);
-        if (i < NKV && r < n) {
-            kr[p] = *reinterpret_cast<const uint4*>(k + ((t0 + r) * H + h) * K + cv * EV);
-            qr[p] = *reinterpret_cast<const uint4*>(q + ((t0 + r) * H + h) * K + cv * EV);
-        }
+        const int i = tid + NT * p, r = min(i / (K / EV), n - 1), cv = i % (K / EV);
+        kr[p] = *reinterpret_cast<const u32x4*>(k + ((t0 + r) * H + h) * K + cv * EV);
+        qr[p] = *reinterpret_cast<const u32x4*>(q + ((t0 + r) * H + h) * K + cv * EV);
     }
 #pragma unroll
     for (int p = 0; p < PV; ++p) {
-        const int i = tid + NT * p, r = i / (V / EV), cv = i % (V / EV);
-        vr[p] = make_uint4(0, 0, 0, 0);
-        if (i < NVV && r < n)
-            vr[p] = *reinterpret_cast<const uint4*>(v + ((t0 + r) * H + h) * V + cv * EV);
+        const int i = tid + NT * p, r = min(i / (V / EV), n - 1), cv = i % (V / EV);
+        vr[p] = *reinterpret_cast<const u32x4*>(v + ((t0 + r) * H + h) * V + cv * EV);
     }
 
     // ---- a1: gates and beta; cumulative log2 gate (rows >= n: g = 0, beta = 0)
@@ -139,8 +138,8 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
             if (r < C) {
                 sG[r] = G;
                 sB[r] = bt;
-                sE[r] = exp2f(G);
-                sF[r] = exp2f(fminf(Gc - G, 0.f));
+                sE[r] = exp2_hw(G);
+                sF[r] = exp2_hw(fminf(Gc - G, 0.f));
             }
         }
     } else {
@@ -165,47 +164,66 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
 #pragma unroll
     for (int p = 0; p < PKQ; ++p) {
         const int i = tid + NT * p, r = i / (K / EV), cv = i % (K / EV);
-        if (i < NKV) {
-            *reinterpret_cast<uint4*>(sK + r * LDK + cv * EV) = kr[p];
-            *reinterpret_cast<uint4*>(sQ + r * LDK + cv * EV) = qr[p];
-        }
+        *reinterpret_cast<u32x4*>(sK + r * LDK + cv * EV) = kr[p];
+        *reinterpret_cast<u32x4*>(sQ + r * LDK + cv * EV) = qr[p];
     }
 #pragma unroll
     for (int p = 0; p < PV; ++p) {
         const int i = tid + NT * p, r = i / (V / EV), cv = i % (V / EV);
-        if (i < NVV) *reinterpret_cast<uint4*>(sV + r * LDV + cv * EV) = vr[p];
+        *reinterpret_cast<u32x4*>(sV + r * LDV + cv * EV) = vr[p];
     }
     __syncthreads();
 
-    // ---- outputs that need only G, Q, K (stored straight from registers):
-    // Qs = scale 2^{G} Q, Ks = 2^{G_C - G} K, and the cumulative gate
+    // ---- outputs that need only G, Q, K, in MFMA fragment order (one task =
+    // one 64-lane x 16-byte group): Qs = scale 2^{G} Q (rows = tokens) and
+    // Ks^T = (2^{G_C - G} K)^T (rows = keys), and the cumulative gate
     {
+        typedef FragOrder<T> F;
+        constexpr int VE = F::VE, KG = F::KG;
+        constexpr int NQG = (C / 16) * (K / KG), NKG = (K / 16) * (C / KG);
         T* gqs = static_cast<T*>(a.ws.qs) + blk * C * K;
         T* gks = static_cast<T*>(a.ws.ks) + blk * C * K;
+        for (int task = wave; task < NQG + NKG; task += NW) {
+            float f[VE];
+            if (task < NQG) {
+                const int rt = task / (K / KG), sg = task % (K / KG), r = 16 * rt + (lane & 15);
+                const T* src = sQ + r * LDK + KG * sg;
+                float x[VE];
+                if constexpr (sizeof(T) == 2) {
+                    const typename M::frag fr = M::load(src, lane);
 #pragma unroll
-        for (int p = 0; p < PKQ; ++p) {
-            const int i = tid + NT * p, r = i / (K / EV), d0 = (i % (K / EV)) * EV;
-            if (i < NKV) {
-                const uint4 xq = *reinterpret_cast<const uint4*>(sQ + r * LDK + d0);
-                const uint4 xk = *reinterpret_cast<const uint4*>(sK + r * LDK + d0);
-                float fq[EV], fk[EV];
-                if (!PK) {
-                    const float eq = a.scale * sE[r], ek = sF[r];
-#pragma unroll
-                    for (int e = 0; e < EV; ++e) {
-                        fq[e] = eq * Vec16<T>::get(xq, e);
-                        fk[e] = ek * Vec16<T>::get(xk, e);
-                    }
+                    for (int e = 0; e < VE; ++e) x[e] = (float)fr[e];
                 } else {
 #pragma unroll
-                    for (int e = 0; e < EV; ++e) {
-                        const float gr = sG[r * K + d0 + e], gc = sG[(C - 1) * K + d0 + e];
-                        fq[e] = a.scale * exp2f(gr) * Vec16<T>::get(xq, e);
-                        fk[e] = exp2f(fminf(gc - gr, 0.f)) * Vec16<T>::get(xk, e);
-                    }
+                    for (int e = 0; e < VE; ++e) x[e] = Elem<T>::load(src + F::col(lane, e));
                 }
-                *reinterpret_cast<uint4*>(gqs + r * K + d0) = Vec16<T>::pack(fq);
-                *reinterpret_cast<uint4*>(gks + r * K + d0) = Vec16<T>::pack(fk);
+#pragma unroll
+                for (int e = 0; e < VE; ++e) {
+                    const int d = KG * sg + F::col(lane, e);
+                    f[e] = a.scale * (PK ? exp2_hw(sG[r * K + d]) : sE[r]) * x[e];
+                }
+                *reinterpret_cast<uint4*>(gqs + ((int64_t)task * 64 + lane) * VE) =
+                    Vec16<T>::pack(f);
+            } else {
+                const int t = task - NQG, rt = t / (C / KG), sg = t % (C / KG);
+                const int kd = 16 * rt + (lane & 15);
+                float x[VE];
+                if constexpr (sizeof(T) == 2) {
+                    const typename M::frag fr = M::load_t(sK + KG * sg * LDK + 16 * rt, LDK, lane);
+#pragma unroll
+                    for (int e = 0; e < VE; ++e) x[e] = (float)fr[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < VE; ++e)
+                        x[e] = Elem<T>::load(sK + (KG * sg + F::col(lane, e)) * LDK + kd);
+                }
+#pragma unroll
+                for (int e = 0; e < VE; ++e) {
+                    const int tok = KG * sg + F::col(lane, e);
+                    f[e] = (PK ? exp2_hw(fminf(sG[(C - 1) * K + kd] - sG[tok * K + kd], 0.f))
+                               : sF[tok]) * x[e];
+                }
+                *reinterpret_cast<uint4*>(gks + ((int64_t)t * 64 + lane) * VE) = Vec16<T>::pack(f);
             }
         }
         float* gg = a.ws.gcum + blk * C * (PK ? K : 1);
@@ -216,41 +234,69 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
     // Aqk^T = K Q^T masked -> Aqk rows in HBM (lane: 4 consecutive columns)
     T* gaqk = static_cast<T*>(a.ws.aqk) + blk * C * C;
     if (!PK) {
-        constexpr int NT2 = NB * (NB + 1) / 2, NZ = NB * (NB - 1) / 2;
-        for (int job = wave; job < 2 * NT2 + NZ; job += NW) {
-            if (job < 2 * NT2) {
-                const bool isq = job >= NT2;
-                int t = isq ? job - NT2 : job, I = 0;
-                while (t > I) { t -= I + 1; ++I; }
-                const int J = t;
-                // K K^T tile (I, J): rows i in block I, columns j in block J.
-                // Q K^T as its transpose: rows j (block J, from K), columns i (block I, from Q)
-                const T* A0 = sK + 16 * (isq ? J : I) * LDK;
-                const T* B0 = (isq ? sQ : sK) + 16 * (isq ? I : J) * LDK;
-                f32x4 acc = mma_tile<T>(A0, LDK, B0, LDK, K, lane, zero4());
-                if (!isq) {
+        // waves 0..NB-1: K K^T row block I = wave, all NB column blocks (the
+        // upper ones come out masked to zero); waves NB..2NB-1: Aqk^T for
+        // the columns of token block I = wave - NB.  Every operand fragment
+        // is loaded before the first product.
+        static_assert(2 * NB <= NW, "one row block per wave");
+        constexpr int NKS = K / KS;
+        if (wave < 2 * NB) {
+            const bool isq = wave >= NB;
+            const int I = isq ? wave - NB : wave;
+            // shared operand: K rows of block I (K K^T, as A) or Q rows of block I (Aqk^T, as B)
+            const T* sh = (isq ? sQ : sK) + (16 * I + (lane & 15)) * LDK;
+            typename M::frag fs[NKS], fo[NB][NKS];
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) fs[s] = M::load(sh + s * KS, lane);
+#pragma unroll
+            for (int J = 0; J < NB; ++J)
+#pragma unroll
+                for (int s = 0; s < NKS; ++s)
+                    fo[J][s] = M::load(sK + (16 * J + (lane & 15)) * LDK + s * KS, lane);
+            f32x4 acc[NB];
+#pragma unroll
+            for (int J = 0; J < NB; ++J) acc[J] = zero4();
+            if (!isq) {
+#pragma unroll
+                for (int J = 0; J < NB; ++J)
+#pragma unroll
+                    for (int s = 0; s < NKS; ++s) acc[J] = M::mma(fs[s], fo[J][s], acc[J]);
+                // rows i = 16I + 4(l/16) + e, columns j = 16J + l%16
+                float gi[4], bi[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    gi[e] = sG[16 * I + acc_row(lane, e)];
+                    bi[e] = sB[16 * I + acc_row(lane, e)];
+                }
+#pragma unroll
+                for (int J = 0; J < NB; ++J) {
+                    const int j = 16 * J + acc_col(lane);
+                    const float gj = sG[j];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int i = 16 * I + acc_row(lane, e), j = 16 * J + acc_col(lane);
-                        sA[i * LDA + j] = j < i ? sB[i] * exp2f(fminf(sG[i] - sG[j], 0.f)) * acc[e]
-                                                : 0.f;
+                        const int i = 16 * I + acc_row(lane, e);
+                        const float x = bi[e] * exp2_hw(fminf(gi[e] - gj, 0.f)) * acc[J][e];
+                        sA[i * LDA + j] = j < i ? x : 0.f;
                     }
-                } else {
-                    const int i = 16 * I + acc_col(lane);
-                    const float gi = sG[i];
+                }
+            } else {
+#pragma unroll
+                for (int J = 0; J < NB; ++J)
+#pragma unroll
+                    for (int s = 0; s < NKS; ++s) acc[J] = M::mma(fo[J][s], fs[s], acc[J]);
+                // Aqk^T tiles: rows j = 16J + 4(l/16) + e, column i = 16I + l%16
+                const int i = 16 * I + acc_col(lane);
+                const float gi = sG[i];
+#pragma unroll
+                for (int J = 0; J < NB; ++J) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int j = 16 * J + acc_row(lane, e);
-                        acc[e] = j <= i ? a.scale * exp2f(fminf(gi - sG[j], 0.f)) * acc[e] : 0.f;
+                        const float x = a.scale * exp2_hw(fminf(gi - sG[j], 0.f)) * acc[J][e];
+                        acc[J][e] = j <= i ? x : 0.f;
                     }
-                    store4(gaqk + i * C + 16 * J + 4 * (lane >> 4), acc);
+                    store4_frag(gaqk, i, 16 * J + 4 * (lane >> 4), C, acc[J]);
                 }
-            } else {
-                // an upper block of Aqk: zeros
-                int t = job - 2 * NT2, I = 0;
-                while (t >= NB - 1 - I) { t -= NB - 1 - I; ++I; }
-                const int J = I + 1 + t;
-                store4(gaqk + (16 * I + acc_col(lane)) * C + 16 * J + 4 * (lane >> 4), zero4());
             }
         }
     } else {
@@ -266,11 +312,11 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                 if (r < 32) {
                     const int tok = b + (r & 15);
                     const T* src = (r < 16 ? sK : sQ) + tok * LDK + d;
-                    x = Elem<T>::load(src) * exp2f(fminf(sG[tok * K + d] - sG[b * K + d], 0.f));
+                    x = Elem<T>::load(src) * exp2_hw(fminf(sG[tok * K + d] - sG[b * K + d], 0.f));
                 } else {
                     const int tok = r - 32;
                     x = Elem<T>::load(sK + tok * LDK + d) *
-                        exp2f(fminf(sG[b * K + d] - sG[tok * K + d], 0.f));
+                        exp2_hw(fminf(sG[b * K + d] - sG[tok * K + d], 0.f));
                 }
                 Elem<T>::store(sS + r * LDK + d, x);
             }
@@ -291,14 +337,14 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                     f32x4 acc = mma_tile<T>(sS + (32 + 16 * J) * LDK, LDK, sS + 16 * LDK, LDK, K,
                                             lane, zero4());
                     acc *= a.scale;
-                    store4(gaqk + (16 * I + acc_col(lane)) * C + 16 * J + 4 * (lane >> 4), acc);
+                    store4_frag(gaqk, 16 * I + acc_col(lane), 16 * J + 4 * (lane >> 4), C, acc);
                 }
             }
         }
         // upper blocks of Aqk: zeros (those of A are masked when Ainv is read)
         for (int i = tid; i < C * C; i += NT) {
             const int r = i / C, j = i - r * C;
-            if (j / 16 > r / 16) Elem<T>::store(gaqk + i, 0.f);
+            if (j / 16 > r / 16) Elem<T>::store(gaqk + FragOrder<T>::off(r, j, C), 0.f);
         }
         // diagonal 16x16 blocks, pair by pair: thread = (block, row, slice of d)
         {
@@ -309,7 +355,7 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                 float akk = 0.f, aqk = 0.f;
                 if (j <= i) {
                     for (int d = s * DQ; d < s * DQ + DQ; ++d) {
-                        const float dec = exp2f(fminf(sG[i * K + d] - sG[j * K + d], 0.f));
+                        const float dec = exp2_hw(fminf(sG[i * K + d] - sG[j * K + d], 0.f));
                         const float kj = Elem<T>::load(sK + j * LDK + d) * dec;
                         akk += Elem<T>::load(sK + i * LDK + d) * kj;
                         aqk += Elem<T>::load(sQ + i * LDK + d) * kj;
@@ -322,7 +368,7 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                 }
                 if (s == 0) {
                     sA[i * LDA + j] = j < i ? sB[i] * akk : 0.f;
-                    Elem<T>::store(gaqk + i * C + j, j <= i ? a.scale * aqk : 0.f);
+                    Elem<T>::store(gaqk + FragOrder<T>::off(i, j, C), j <= i ? a.scale * aqk : 0.f);
                 }
             }
         }
@@ -330,7 +376,8 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
     __syncthreads();
 
     // ---- a3: Ainv = (I + A)^{-1}
-    // diagonal blocks: wave w inverts block w; lane c < 16 computes column c
+    // diagonal blocks: wave w inverts block w by forward substitution; lane
+    // c < 16 computes column c
     if (wave < NB && lane < 16) {
         float* blkA = sA + 16 * wave * LDA + 16 * wave;
         float x[16];
@@ -341,6 +388,7 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
             for (int m = 0; m < r; ++m) acc -= blkA[r * LDA + m] * x[m];
             x[r] = acc;
         }
+        // the block is only touched by this wave, whose LDS accesses stay in order
 #pragma unroll
         for (int r = 0; r < 16; ++r) blkA[r * LDA + lane] = x[r];
     }
@@ -414,7 +462,7 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                 const uint4 xk = *reinterpret_cast<const uint4*>(sK + r * LDK + d0);
                 float f[EV];
 #pragma unroll
-                for (int e = 0; e < EV; ++e) f[e] = exp2f(sG[r * K + d0 + e]) * Vec16<T>::get(xk, e);
+                for (int e = 0; e < EV; ++e) f[e] = exp2_hw(sG[r * K + d0 + e]) * Vec16<T>::get(xk, e);
                 *reinterpret_cast<uint4*>(sKg + r * LDK + d0) = Vec16<T>::pack(f);
             }
         }
@@ -423,28 +471,55 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
     }
     __syncthreads();
 
-    // ---- a4: W^T = K^T A1^T and U^T = V^T A2^T, tile (column block D of K or
-    // V, token block I); the lane's 4 values are W[i][4 consecutive d]
+    // ---- a4: W^T = K^T A1^T and U = A2 V.  Wave w takes token block
+    // I = w % NB and every (NW/NB)-th column block D of K and of V; the A1 / A2
+    // rows of block I are loaded once and shared by all its tiles.
     {
+        static_assert(NW % NB == 0 && (K / 16) % (NW / NB) == 0 && (V / 16) % (NW / NB) == 0,
+                      "column blocks split evenly over the waves of a token block");
+        constexpr int G = NW / NB, WD = (K / 16) / G, UD = (V / 16) / G, NKM = C / KS;
         T* gw = static_cast<T*>(a.ws.w) + blk * C * K;
         T* gu = static_cast<T*>(a.ws.u) + blk * C * V;
-        constexpr int WJ = NB * (K / 16), UJ = NB * (V / 16);
-        for (int job = wave; job < WJ + UJ; job += NW) {
-            const bool isu = job >= WJ;
-            const int jj = isu ? job - WJ : job;
-            const int I = jj % NB, D = jj / NB;
-            const int kn = min(C, ((16 * (I + 1) + KS - 1) / KS) * KS);
-            const T* X = isu ? sV : sKW;              // [token][d]: k-major for X^T
-            const int ldx = isu ? LDV : LDK;
-            const T* Bt = (isu ? sA2 : sAW) + (16 * I + (lane & 15)) * LDC;
-            f32x4 acc = zero4();
-            for (int k0 = 0; k0 < kn; k0 += KS)
-                acc = M::mma(M::load_t(X + k0 * ldx + 16 * D, ldx, lane), M::load(Bt + k0, lane),
-                             acc);
-            const int i = 16 * I + acc_col(lane);
-            if (isu) store4(gu + i * V + 16 * D + 4 * (lane >> 4), acc);
-            else store4(gw + i * K + 16 * D + 4 * (lane >> 4), acc);
+        const int I = wave % NB, d0 = wave / NB;
+        const int kn = min(C, ((16 * (I + 1) + KS - 1) / KS) * KS);
+        const T* bw = sAW + (16 * I + (lane & 15)) * LDC;
+        const T* bu = sA2 + (16 * I + (lane & 15)) * LDC;
+        typename M::frag fw[NKM], fu[NKM];
+#pragma unroll
+        for (int s = 0; s < NKM; ++s)
+            if (s * KS < kn) {
+                fw[s] = M::load(bw + s * KS, lane);
+                fu[s] = M::load(bu + s * KS, lane);
+            }
+        f32x4 aw[WD], au[UD];
+#pragma unroll
+        for (int m = 0; m < WD; ++m) {
+            const int D = d0 + G * m;
+            aw[m] = zero4();
+#pragma unroll
+            for (int s = 0; s < NKM; ++s)
+                if (s * KS < kn)
+                    aw[m] = M::mma(M::load_t(sKW + s * KS * LDK + 16 * D, LDK, lane), fw[s], aw[m]);
         }
+#pragma unroll
+        for (int m = 0; m < UD; ++m) {
+            const int D = d0 + G * m;
+            au[m] = zero4();
+#pragma unroll
+            for (int s = 0; s < NKM; ++s)
+                if (s * KS < kn)
+                    au[m] = M::mma(fu[s], M::load_t(sV + s * KS * LDV + 16 * D, LDV, lane), au[m]);
+        }
+        // W^T tiles: lane holds W[i][4 consecutive d] -> fragment order;
+        // U tiles: lane holds U[4 consecutive i][d] -> accumulator order
+        const int i = 16 * I + acc_col(lane);
+#pragma unroll
+        for (int m = 0; m < WD; ++m)
+            store4_frag(gw, i, 16 * (d0 + G * m) + 4 * (lane >> 4), K, aw[m]);
+#pragma unroll
+        for (int m = 0; m < UD; ++m)
+            store4(gu + acc_order_off(16 * I + acc_row(lane, 0), 16 * (d0 + G * m) + acc_col(lane), V),
+                   au[m]);
     }
 }
 

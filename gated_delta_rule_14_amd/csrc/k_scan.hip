@@ -1,7 +1,7 @@
 // Inter-chunk state pass with the chunk output fused in (k4 + k5).
 //
 // The state h (K x V, fp32) is carried serially over the chunks of one
-// (sequence, head); the value dimension is split into VT-wide tiles that run
+// (sequence, head); the value dimension is split into VT-wide slices that run
 // as independent workgroups.  Per chunk, with the intra-chunk products in the
 // workspace (W, U, Qs = scale diag(gamma) Q, Ks = diag(gamma_C/gamma) K, Aqk):
 //   V_new = U - W h                                    (MFMA)
@@ -14,14 +14,19 @@
 // K^T V_new; "阅读笔记：DeltaNet 在 FLA 中的代码实现笔记", forward Steps 4-5.)
 // For the per-key gate gamma_C is a vector and decays h row by row.
 //
-// Mapping (8 waves): each wave owns one (16-token, 16-value) tile of V_new
-// and the matching transposed tile of O, and K/16 * VT/16 / 8 tiles of h,
-// which stays in MFMA accumulators for the whole sequence.  A bf16 (or fp32)
-// copy of h^T in LDS is the operand of the two products that read h, and
-// V_new^T in LDS feeds the other two.  O is computed transposed so each
-// lane stores 4 consecutive values of one output row straight to HBM.  The
-// next chunk's operands are loaded into registers while the current chunk
-// is computed and written to the other half of a double-buffered LDS area.
+// Data path.  W, Qs, Ks^T and Aqk sit in the workspace in MFMA fragment order
+// and U in accumulator order (gdn_device.hpp), so every operand fragment is
+// one coalesced 16-byte load per lane straight into registers, issued PD
+// chunks ahead of its use; no operand is staged through LDS.  LDS holds only
+// the two values that cross waves: h^T (a T copy of the state) and V_new^T.
+// Each operand fragment is loaded by exactly one wave of the workgroup:
+//   V waves (C/32): token rows 32m..32m+31 of V_new = U - W h
+//   O waves (C/32): token columns 32m.. of O^T = h^T Qs^T + V_new^T Aqk^T
+//   H waves (K/32): key rows 32p..32p+31 of h, held in MFMA accumulators
+// Per chunk: V and O waves read h^T, V waves publish V_new^T, barrier; O
+// waves finish and store their rows of O, H waves decay and update h and
+// publish h^T, barrier.
+//
 // The workgroups of one (sequence, head) get ids equal modulo 8, so the
 // hardware's round-robin over the 8 XCDs puts them on one XCD and they share
 // W, Qs, Ks and Aqk through its L2.
@@ -30,305 +35,420 @@
 
 namespace gdn {
 
-constexpr int SCAN_THREADS = 512;
+constexpr int SCAN_MAX_THREADS = 512;
 
-template <typename T, int K, int V, int C, int VT, bool PK>
-struct ScanSmem {
-    static constexpr int P = 16 / sizeof(T);
-    static constexpr int LDK = K + P;     // [C][K] row-major: W, Qs, Ks; [VT][K] h^T
-    static constexpr int LDC = C + P;     // [C][C] Aqk, [VT][C] V_new^T
-    static constexpr int LDT = VT + P;    // [C][VT] U tile
-    // one chunk's operands
-    static constexpr size_t b_W = 0;
-    static constexpr size_t b_Q = b_W + sizeof(T) * C * LDK;
-    static constexpr size_t b_K = b_Q + sizeof(T) * C * LDK;
-    static constexpr size_t b_A = b_K + sizeof(T) * C * LDK;
-    static constexpr size_t b_U = b_A + sizeof(T) * C * LDC;
-    static constexpr size_t b_D = b_U + sizeof(T) * C * LDT;
-    static constexpr size_t BUF = ((b_D + sizeof(float) * (PK ? K : 4)) + 15) / 16 * 16;
-    static constexpr size_t FIXED = sizeof(T) * VT * LDK + sizeof(T) * VT * LDC;
-    static constexpr int NBUF = 2 * BUF + FIXED <= 160 * 1024 ? 2 : 1;
-    static constexpr size_t o_hT = NBUF * BUF;
-    static constexpr size_t o_Vn = o_hT + sizeof(T) * VT * LDK;
-    static constexpr size_t bytes = o_Vn + sizeof(T) * VT * LDC;
-};
-
-// Registers holding the next chunk's operands between its load and its
-// write to LDS.  The region of each slot is fixed at compile time (W, Qs, Ks
-// are C*K/EV vectors each, Aqk C*C/EV, the U tile C*VT/EV; all multiples of
-// 64, so partial passes are wave-uniform).
-template <typename T, int PW, int PA, int PU>
-struct ScanPrefetch {
-    u32x4 w[PW], q[PW], k[PW], a[PA], u[PU];
-    float d;
-
-    template <int K, int V, int C, int VT, int NT, bool PK>
-    __device__ __forceinline__ void issue(const T* gw, const T* gq, const T* gk, const T* ga,
-                                          const T* gu, const float* gcum, int64_t blk, int v0,
-                                          int tid) {
-        constexpr int EV = 16 / sizeof(T);
-        constexpr int NWV = C * K / EV, NAV = C * C / EV, NUV = C * VT / EV;
-        const u32x4* w4 = reinterpret_cast<const u32x4*>(gw + blk * C * K);
-        const u32x4* q4 = reinterpret_cast<const u32x4*>(gq + blk * C * K);
-        const u32x4* k4 = reinterpret_cast<const u32x4*>(gk + blk * C * K);
-        const u32x4* a4 = reinterpret_cast<const u32x4*>(ga + blk * C * C);
-#pragma unroll
-        for (int p = 0; p < PW; ++p) {
-            const int i = tid + NT * p;
-            if (NWV % NT == 0 || i < NWV) {
-                w[p] = w4[i];
-                q[p] = q4[i];
-                k[p] = k4[i];
-            }
-        }
-#pragma unroll
-        for (int p = 0; p < PA; ++p) {
-            const int i = tid + NT * p;
-            if (NAV % NT == 0 || i < NAV) a[p] = a4[i];
-        }
-#pragma unroll
-        for (int p = 0; p < PU; ++p) {
-            const int i = tid + NT * p;
-            if (NUV % NT == 0 || i < NUV) {
-                const int r = i / (VT / EV), cv = i % (VT / EV);
-                u[p] = *reinterpret_cast<const u32x4*>(gu + blk * C * V + r * V + v0 + cv * EV);
-            }
-        }
-        if (PK) d = tid < K ? gcum[(blk * C + (C - 1)) * K + tid] : 0.f;
-        else d = gcum[blk * C + (C - 1)];
-    }
-
-    template <typename L, int K, int C, int VT, int NT, bool PK>
-    __device__ __forceinline__ void commit(char* buf, int tid) const {
-        constexpr int EV = 16 / sizeof(T);
-        constexpr int NWV = C * K / EV, NAV = C * C / EV, NUV = C * VT / EV;
-        T* sW = reinterpret_cast<T*>(buf + L::b_W);
-        T* sQ = reinterpret_cast<T*>(buf + L::b_Q);
-        T* sK = reinterpret_cast<T*>(buf + L::b_K);
-        T* sA = reinterpret_cast<T*>(buf + L::b_A);
-        T* sU = reinterpret_cast<T*>(buf + L::b_U);
-        float* sD = reinterpret_cast<float*>(buf + L::b_D);
-#pragma unroll
-        for (int p = 0; p < PW; ++p) {
-            const int i = tid + NT * p;
-            if (NWV % NT == 0 || i < NWV) {
-                const int o = (i / (K / EV)) * L::LDK + (i % (K / EV)) * EV;
-                *reinterpret_cast<u32x4*>(sW + o) = w[p];
-                *reinterpret_cast<u32x4*>(sQ + o) = q[p];
-                *reinterpret_cast<u32x4*>(sK + o) = k[p];
-            }
-        }
-#pragma unroll
-        for (int p = 0; p < PA; ++p) {
-            const int i = tid + NT * p;
-            if (NAV % NT == 0 || i < NAV)
-                *reinterpret_cast<u32x4*>(sA + (i / (C / EV)) * L::LDC + (i % (C / EV)) * EV) = a[p];
-        }
-#pragma unroll
-        for (int p = 0; p < PU; ++p) {
-            const int i = tid + NT * p;
-            if (NUV % NT == 0 || i < NUV)
-                *reinterpret_cast<u32x4*>(sU + (i / (VT / EV)) * L::LDT + (i % (VT / EV)) * EV) = u[p];
-        }
-        if (PK) {
-            if (tid < K) sD[tid] = exp2f(d);
-        } else if (tid == 0) {
-            sD[0] = exp2f(d);
-        }
-    }
-};
-
-template <typename T, int K, int V, int C, int VT, bool PK>
-__global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(ScanLaunch a) {
-    typedef ScanSmem<T, K, V, C, VT, PK> L;
+template <typename T, int K_, int V_, int C_, int VT_, bool PK_, int PD_>
+struct ScanCfg {
+    typedef T Elt;
     typedef Mma<T> M;
-    constexpr int NT = SCAN_THREADS, NW = NT / 64;
-    constexpr int LDK = L::LDK, LDC = L::LDC, LDT = L::LDT;
-    constexpr int KS = M::KSTEP;
-    constexpr int EV = 16 / sizeof(T);
-    constexpr int NVT = V / VT;
-    constexpr int CT = VT / 16;              // value tiles
-    constexpr int TT = C / 16;               // token tiles
-    constexpr int NHT = (K / 16) * CT;       // h tiles
-    constexpr int HPW = (NHT + NW - 1) / NW; // h tiles per wave
-    static_assert(TT * CT <= NW, "one V_new tile per wave");
-    static_assert(K % 16 == 0 && VT % 16 == 0 && V % VT == 0, "tile shape");
-    __shared__ __attribute__((aligned(16))) char smem[L::bytes];
-    T* shT = reinterpret_cast<T*>(smem + L::o_hT);
-    T* sVn = reinterpret_cast<T*>(smem + L::o_Vn);
+    typedef FragOrder<T> F;
+    static constexpr int K = K_, V = V_, C = C_, VT = VT_, PD = PD_;
+    static constexpr bool PK = PK_;
+    static constexpr int KS = M::KSTEP, KG = F::KG, KSPG = KG / KS;
+    static constexpr int CT = VT / 16;                 // value tiles of the slice
+    static constexpr int NVW = C / 32, NOW = C / 32, NHW = K / 32;
+    static constexpr int NW = NVW + NOW + NHW, NT = 64 * NW;
+    static constexpr int GK = K / KG, GC = C / KG;    // fragment groups along K / C
+    static constexpr int P = 16 / sizeof(T);
+    static constexpr int LDH = K + P;                  // h^T     [VT][K]
+    static constexpr int LDV = C + P;                  // V_new^T [VT][C]
+    static constexpr size_t o_hT = 0;
+    static constexpr size_t o_Vn = sizeof(T) * VT * LDH;
+    static constexpr size_t bytes = o_Vn + sizeof(T) * VT * LDV;
+    static_assert(C == 64, "two token pairs: the O waves are specialised for m = 0, 1");
+    static_assert(K % 32 == 0 && VT % 16 == 0 && V % VT == 0, "tile shape");
+    static_assert(NT <= SCAN_MAX_THREADS, "workgroup size");
+    static_assert(PD >= 1 && PD <= 4, "prefetch distance");
+};
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// One (sequence, head, value slice): chunk range and shared pointers.
+template <typename Cfg>
+struct ScanChain {
+    typedef typename Cfg::Elt T;
+    const ScanLaunch& a;
+    T* shT;
+    T* sVn;
+    int64_t n, h, t0, len, c0;
+    int v0, nch, lane;
+
+    __device__ __forceinline__ ScanChain(const ScanLaunch& la, char* smem, int64_t chain, int vt)
+        : a(la) {
+        shT = reinterpret_cast<T*>(smem + Cfg::o_hT);
+        sVn = reinterpret_cast<T*>(smem + Cfg::o_Vn);
+        n = chain / a.H;
+        h = chain - n * a.H;
+        v0 = vt * Cfg::VT;
+        lane = threadIdx.x & 63;
+        if (a.map.seqs) {
+            const int4 s = a.map.seqs[n];
+            t0 = s.x;
+            len = s.y;
+            c0 = s.z;
+        } else {
+            t0 = n * a.map.T;
+            len = a.map.T;
+            c0 = n * a.map.nt;
+        }
+        nch = (int)((len + Cfg::C - 1) / Cfg::C);
+        // never walk past the chunk slots (only invalid offsets could ask to)
+        if (c0 + nch > a.map.max_chunks) nch = (int)max((int64_t)0, a.map.max_chunks - c0);
+    }
+    // workspace block of chunk j (nch >= 1), clamped to the last chunk:
+    // prefetches past the end reload it, so every step issues the same loads
+    __device__ __forceinline__ int64_t blk(int j) const {
+        return h * a.map.max_chunks + c0 + min(j, nch - 1);
+    }
+    // row r of the B operand read from a transposed LDS buffer X^T[VT][ld]:
+    // the fragment for value tile ct and k-offset k0
+    __device__ __forceinline__ typename Cfg::M::frag lds_frag(const T* x, int ld, int ct,
+                                                             int k0) const {
+        return Cfg::M::load(x + (16 * ct + (lane & 15)) * ld + k0, lane);
+    }
+};
+
+// Run one role over the chain (nch >= 1).  The PD+1 register buffers rotate
+// with the unrolled steps so each keeps a fixed register set: R::step(j,
+// cur, spare) consumes cur and loads chunk j+PD into spare.
+template <int PD, typename R>
+__device__ __forceinline__ void drive(R& r, int nch) {
+    typename R::Pre b[PD + 1];
+#pragma unroll
+    for (int q = 0; q < PD; ++q) r.issue(b[q], q);
+    __syncthreads();   // the initial h^T is published
+    int j = 0;
+    for (; j + PD + 1 <= nch; j += PD + 1) {
+#pragma unroll
+        for (int q = 0; q <= PD; ++q) r.step(j + q, b[q], b[(q + PD) % (PD + 1)]);
+    }
+#pragma unroll
+    for (int q = 0; q < PD; ++q)
+        if (j + q < nch) r.step(j + q, b[q], b[(q + PD) % (PD + 1)]);
+}
+
+// ---- V waves: V_new rows 32m..32m+31 (token tiles 2m, 2m+1), all VT columns
+template <typename Cfg>
+struct ScanV {
+    typedef typename Cfg::Elt T;
+    typedef typename Cfg::M M;
+    typedef typename Cfg::F F;
+    static constexpr int K = Cfg::K, V = Cfg::V, C = Cfg::C, CT = Cfg::CT, GK = Cfg::GK;
+    struct Pre {
+        u32x4 w[2][GK];
+        typename Quad<T>::raw u[2][CT];
+    };
+    const ScanChain<Cfg>& ch;
+    int m;
+
+    __device__ __forceinline__ void issue(Pre& p, int j) const {
+        const int64_t b = ch.blk(j);
+        const u32x4* gw = reinterpret_cast<const u32x4*>(static_cast<const T*>(ch.a.ws.w) + b * C * K);
+        const T* gu = static_cast<const T*>(ch.a.ws.u) + b * C * V;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int sg = 0; sg < GK; ++sg) p.w[t][sg] = gw[((2 * m + t) * GK + sg) * 64 + ch.lane];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                p.u[t][ct] = Quad<T>::load(
+                    gu + ((int64_t)((2 * m + t) * (V / 16) + ch.v0 / 16 + ct) * 64 + ch.lane) * 4);
+    }
+
+    __device__ __forceinline__ void step(int j, const Pre& cur, Pre& spare) const {
+        issue(spare, j + Cfg::PD);
+        f32x4 acc[2][CT];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) acc[t][ct] = zero4();
+#pragma unroll
+        for (int sg = 0; sg < GK; ++sg)
+#pragma unroll
+            for (int i = 0; i < Cfg::KSPG; ++i) {
+                const int k0 = sg * Cfg::KG + i * Cfg::KS;
+                const typename M::frag a0 = F::frag(cur.w[0][sg], i);
+                const typename M::frag a1 = F::frag(cur.w[1][sg], i);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const typename M::frag bh = ch.lds_frag(ch.shT, Cfg::LDH, ct, k0);
+                    acc[0][ct] = M::mma(a0, bh, acc[0][ct]);
+                    acc[1][ct] = M::mma(a1, bh, acc[1][ct]);
+                }
+            }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const f32x4 u = Quad<T>::get(cur.u[t][ct]);
+                store_acc_t(ch.sVn + 16 * ct * Cfg::LDV + 16 * (2 * m + t), Cfg::LDV, ch.lane,
+                            u - acc[t][ct]);
+            }
+        __syncthreads();   // V_new^T published
+        __syncthreads();   // next h^T published
+    }
+};
+
+// ---- O waves: O^T for token tiles 2M, 2M+1 (columns), all VT rows
+template <typename Cfg, int MT>
+struct ScanO {
+    typedef typename Cfg::Elt T;
+    typedef typename Cfg::M M;
+    typedef typename Cfg::F F;
+    static constexpr int K = Cfg::K, V = Cfg::V, C = Cfg::C, CT = Cfg::CT, GK = Cfg::GK;
+    // Aqk groups along j that can be nonzero for tokens < 32(MT+1)
+    static constexpr int NA = (32 * (MT + 1) + Cfg::KG - 1) / Cfg::KG;
+    struct Pre {
+        u32x4 q[2][GK];
+        u32x4 a[2][NA];
+    };
+    const ScanChain<Cfg>& ch;
+
+    __device__ __forceinline__ void issue(Pre& p, int j) const {
+        const int64_t b = ch.blk(j);
+        const u32x4* gq = reinterpret_cast<const u32x4*>(static_cast<const T*>(ch.a.ws.qs) + b * C * K);
+        const u32x4* ga = reinterpret_cast<const u32x4*>(static_cast<const T*>(ch.a.ws.aqk) + b * C * C);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int sg = 0; sg < GK; ++sg) p.q[t][sg] = gq[((2 * MT + t) * GK + sg) * 64 + ch.lane];
+#pragma unroll
+            for (int sg = 0; sg < NA; ++sg)
+                p.a[t][sg] = ga[((2 * MT + t) * Cfg::GC + sg) * 64 + ch.lane];
+        }
+    }
+
+    __device__ __forceinline__ void step(int j, const Pre& cur, Pre& spare) const {
+        issue(spare, j + Cfg::PD);
+        f32x4 acc[CT][2];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) acc[ct][0] = acc[ct][1] = zero4();
+        // h^T Qs^T: the entering state
+#pragma unroll
+        for (int sg = 0; sg < GK; ++sg)
+#pragma unroll
+            for (int i = 0; i < Cfg::KSPG; ++i) {
+                const int k0 = sg * Cfg::KG + i * Cfg::KS;
+                const typename M::frag b0 = F::frag(cur.q[0][sg], i);
+                const typename M::frag b1 = F::frag(cur.q[1][sg], i);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const typename M::frag ah = ch.lds_frag(ch.shT, Cfg::LDH, ct, k0);
+                    acc[ct][0] = M::mma(ah, b0, acc[ct][0]);
+                    acc[ct][1] = M::mma(ah, b1, acc[ct][1]);
+                }
+            }
+        __syncthreads();   // V_new^T published
+        // + V_new^T Aqk^T (Aqk is zero above the diagonal)
+#pragma unroll
+        for (int sg = 0; sg < NA; ++sg)
+#pragma unroll
+            for (int i = 0; i < Cfg::KSPG; ++i) {
+                const int k0 = sg * Cfg::KG + i * Cfg::KS;
+                const typename M::frag b0 = F::frag(cur.a[0][sg], i);
+                const typename M::frag b1 = F::frag(cur.a[1][sg], i);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const typename M::frag av = ch.lds_frag(ch.sVn, Cfg::LDV, ct, k0);
+                    acc[ct][0] = M::mma(av, b0, acc[ct][0]);
+                    acc[ct][1] = M::mma(av, b1, acc[ct][1]);
+                }
+            }
+        // lane: 4 consecutive values of one token row of O
+        const int ntok = (int)min((int64_t)C, ch.len - (int64_t)j * C);
+        const int64_t tt0 = ch.t0 + (int64_t)j * C;
+        T* o = static_cast<T*>(ch.a.o);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int tok = 16 * (2 * MT + t) + acc_col(ch.lane);
+            if (tok < ntok) {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    store4(o + ((tt0 + tok) * ch.a.H + ch.h) * V + ch.v0 + 16 * ct +
+                               4 * (ch.lane >> 4),
+                           acc[ct][t]);
+            }
+        }
+        __syncthreads();   // next h^T published
+    }
+};
+
+// ---- H waves: h rows 32p..32p+31 (key tiles 2p, 2p+1), all VT columns
+template <typename Cfg>
+struct ScanH {
+    typedef typename Cfg::Elt T;
+    typedef typename Cfg::M M;
+    typedef typename Cfg::F F;
+    static constexpr int K = Cfg::K, V = Cfg::V, C = Cfg::C, CT = Cfg::CT, GC = Cfg::GC;
+    static constexpr bool PK = Cfg::PK;
+    struct Pre {
+        u32x4 k[2][GC];
+        float d[PK ? 8 : 1];   // log2 chunk-end decay (per key row for the per-key gate)
+    };
+    const ScanChain<Cfg>& ch;
+    int p;
+    f32x4 hacc[2][CT];
+
+    __device__ __forceinline__ int row(int r, int e) const {
+        return 16 * (2 * p + r) + acc_row(ch.lane, e);
+    }
+
+    __device__ __forceinline__ void issue(Pre& q, int j) const {
+        const int64_t b = ch.blk(j);
+        const u32x4* gk = reinterpret_cast<const u32x4*>(static_cast<const T*>(ch.a.ws.ks) + b * C * K);
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int sg = 0; sg < GC; ++sg) q.k[r][sg] = gk[((2 * p + r) * GC + sg) * 64 + ch.lane];
+        if (PK) {
+            const float* gd = ch.a.ws.gcum + (b * C + (C - 1)) * K;
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) q.d[(PK ? 4 * r + e : 0)] = gd[row(r, e)];
+        } else {
+            q.d[0] = ch.a.ws.gcum[b * C + (C - 1)];
+        }
+    }
+
+    // h <- h0 (or 0); publish h^T
+    __device__ __forceinline__ void init() {
+        const float* h0 = ch.a.h0 ? ch.a.h0 + (ch.n * ch.a.H + ch.h) * (int64_t)(K * V) : nullptr;
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    hacc[r][ct][e] =
+                        h0 ? h0[row(r, e) * V + ch.v0 + 16 * ct + acc_col(ch.lane)] : 0.f;
+                store_acc_t(ch.shT + 16 * ct * Cfg::LDH + 16 * (2 * p + r), Cfg::LDH, ch.lane,
+                            hacc[r][ct]);
+            }
+    }
+
+    __device__ __forceinline__ void step(int j, const Pre& cur, Pre& spare) {
+        issue(spare, j + Cfg::PD);
+        float dec[2][4];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dec[r][e] = exp2_hw(cur.d[PK ? 4 * r + e : 0]);
+        __syncthreads();   // V_new^T published
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hacc[r][ct][e] *= dec[r][e];
+#pragma unroll
+        for (int sg = 0; sg < GC; ++sg)
+#pragma unroll
+            for (int i = 0; i < Cfg::KSPG; ++i) {
+                const int k0 = sg * Cfg::KG + i * Cfg::KS;
+                const typename M::frag a0 = F::frag(cur.k[0][sg], i);
+                const typename M::frag a1 = F::frag(cur.k[1][sg], i);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const typename M::frag bv = ch.lds_frag(ch.sVn, Cfg::LDV, ct, k0);
+                    hacc[0][ct] = M::mma(a0, bv, hacc[0][ct]);
+                    hacc[1][ct] = M::mma(a1, bv, hacc[1][ct]);
+                }
+            }
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                store_acc_t(ch.shT + 16 * ct * Cfg::LDH + 16 * (2 * p + r), Cfg::LDH, ch.lane,
+                            hacc[r][ct]);
+        __syncthreads();   // next h^T published
+    }
+
+    __device__ __forceinline__ void finish() const {
+        if (!ch.a.ht) return;
+        float* ht = ch.a.ht + (ch.n * ch.a.H + ch.h) * (int64_t)(K * V);
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    ht[row(r, e) * V + ch.v0 + 16 * ct + acc_col(ch.lane)] = hacc[r][ct][e];
+    }
+};
+
+template <typename Cfg>
+__global__ __launch_bounds__(SCAN_MAX_THREADS) void scan_kernel(ScanLaunch a) {
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::bytes];
+    constexpr int NVT = Cfg::V / Cfg::VT;
     const int64_t bid = blockIdx.x;
     const int vt = (int)((bid >> 3) % NVT);
     const int64_t chain = (bid & 7) + 8 * ((bid >> 3) / NVT);
     if (chain >= a.N * a.H) return;
-    const int64_t n = chain / a.H, h = chain - n * a.H;
-    const int v0 = vt * VT;
 
-    int64_t t0, len, c0;
-    if (a.map.seqs) {
-        const int4 s = a.map.seqs[n];
-        t0 = s.x;
-        len = s.y;
-        c0 = s.z;
+    const ScanChain<Cfg> ch(a, smem, chain, vt);
+    const int wave = wave_id();
+    if (wave < Cfg::NVW) {
+        ScanV<Cfg> r{ch, wave};
+        if (ch.nch > 0) drive<Cfg::PD>(r, ch.nch);
+    } else if (wave == Cfg::NVW) {
+        ScanO<Cfg, 0> r{ch};
+        if (ch.nch > 0) drive<Cfg::PD>(r, ch.nch);
+    } else if (wave == Cfg::NVW + 1) {
+        ScanO<Cfg, 1> r{ch};
+        if (ch.nch > 0) drive<Cfg::PD>(r, ch.nch);
     } else {
-        t0 = n * a.map.T;
-        len = a.map.T;
-        c0 = n * a.map.nt;
-    }
-
-    // ---- h tiles owned by this wave: tile id = wave + NW * s -> (row block, value tile)
-    f32x4 hacc[HPW];
-    const float* h0 = a.h0 ? a.h0 + (n * a.H + h) * (int64_t)(K * V) : nullptr;
-#pragma unroll
-    for (int s = 0; s < HPW; ++s) {
-        const int id = wave + NW * s;
-        hacc[s] = zero4();
-        if (id < NHT) {
-            const int rb = 16 * (id / CT), ct = id % CT;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                hacc[s][e] = h0 ? h0[(rb + acc_row(lane, e)) * V + v0 + 16 * ct + acc_col(lane)]
-                                : 0.f;
-            store_acc_t(shT + (16 * ct) * LDK + rb, LDK, lane, hacc[s]);
-        }
-    }
-
-    // ---- chunk operands, 16-byte vectors; the region of each register slot is
-    // fixed at compile time (W, Qs, Ks are C*K/EV vectors each, Aqk C*C/EV,
-    // the U tile C*VT/EV; all multiples of 64, so partial passes are
-    // wave-uniform)
-    constexpr int NWV = C * K / EV, NAV = C * C / EV, NUV = C * VT / EV;
-    constexpr int PW = (NWV + NT - 1) / NT, PA = (NAV + NT - 1) / NT, PU = (NUV + NT - 1) / NT;
-    static_assert(NWV % 64 == 0 && NAV % 64 == 0 && NUV % 64 == 0, "wave-uniform passes");
-    ScanPrefetch<T, PW, PA, PU> pre;
-    const T* gw = static_cast<const T*>(a.ws.w);
-    const T* gq = static_cast<const T*>(a.ws.qs);
-    const T* gk = static_cast<const T*>(a.ws.ks);
-    const T* ga = static_cast<const T*>(a.ws.aqk);
-    const T* gu = static_cast<const T*>(a.ws.u);
-#define GDN_SCAN_ISSUE(BLK)                                                                   \
-    pre.template issue<K, V, C, VT, NT, PK>(gw, gq, gk, ga, gu, a.ws.gcum, (BLK), v0, tid)
-#define GDN_SCAN_COMMIT(BUF)                                                                  \
-    pre.template commit<L, K, C, VT, NT, PK>((BUF), tid)
-
-    const int nch = (int)((len + C - 1) / C);
-    T* o = static_cast<T*>(a.o);
-    // this wave's V_new / O tile
-    const int tt = wave % TT, ct = wave / TT;
-    const bool has_tile = wave < TT * CT;
-    if (nch > 0 && c0 < a.map.max_chunks) {
-        GDN_SCAN_ISSUE(h * a.map.max_chunks + c0);
-        GDN_SCAN_COMMIT(smem);
-    }
-    __syncthreads();
-    for (int j = 0; j < nch; ++j) {
-        const int64_t c = c0 + j;
-        if (c >= a.map.max_chunks) break;
-        char* buf = smem + (L::NBUF == 2 ? (j & 1) * L::BUF : 0);
-        const T* sW = reinterpret_cast<const T*>(buf + L::b_W);
-        const T* sQ = reinterpret_cast<const T*>(buf + L::b_Q);
-        const T* sK = reinterpret_cast<const T*>(buf + L::b_K);
-        const T* sA = reinterpret_cast<const T*>(buf + L::b_A);
-        const T* sU = reinterpret_cast<const T*>(buf + L::b_U);
-        const float* sD = reinterpret_cast<const float*>(buf + L::b_D);
-        const int64_t tt0 = t0 + (int64_t)j * C;
-        const int ntok = (int)min((int64_t)C, len - (int64_t)j * C);
-        const bool more = j + 1 < nch && c + 1 < a.map.max_chunks;
-        if (more) GDN_SCAN_ISSUE(h * a.map.max_chunks + c + 1);
-
-        // ---- V_new = U - W h (tile tokens tt x values ct) and
-        //      O^T = h^T Qs^T (tile values ct x tokens tt); both read the same
-        //      h^T fragment (as B in the first product, as A in the second)
-        f32x4 ov = zero4();
-        if (has_tile) {
-            f32x4 vn = zero4();
-            const T* wr = sW + (16 * tt + (lane & 15)) * LDK;
-            const T* qr = sQ + (16 * tt + (lane & 15)) * LDK;
-            const T* hr = shT + (16 * ct + (lane & 15)) * LDK;
-            float u[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                u[e] = Elem<T>::load(sU + (16 * tt + acc_row(lane, e)) * LDT + 16 * ct +
-                                     acc_col(lane));
-#pragma unroll
-            for (int k0 = 0; k0 < K; k0 += KS) {
-                const typename M::frag fh = M::load(hr + k0, lane);
-                vn = M::mma(M::load(wr + k0, lane), fh, vn);
-                ov = M::mma(fh, M::load(qr + k0, lane), ov);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) vn[e] = u[e] - vn[e];
-            store_acc_t(sVn + (16 * ct) * LDC + 16 * tt, LDC, lane, vn);   // V_new^T
-        }
-        __syncthreads();
-
-        // ---- O^T += V_new^T Aqk^T, store O; h <- gamma_C h + Ks^T V_new
-        if (has_tile) {
-            const int kn = min(C, ((16 * (tt + 1) + KS - 1) / KS) * KS);
-            ov = mma_tile<T>(sVn + 16 * ct * LDC, LDC, sA + 16 * tt * LDC, LDC, kn, lane, ov);
-            const int tok = 16 * tt + acc_col(lane);
-            if (tok < ntok)
-                store4(o + ((tt0 + tok) * a.H + h) * V + v0 + 16 * ct + 4 * (lane >> 4), ov);
-        }
-#pragma unroll
-        for (int s = 0; s < HPW; ++s) {
-            const int id = wave + NW * s;
-            if (id < NHT) {
-                const int rb = 16 * (id / CT), hc = id % CT;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) hacc[s][e] *= PK ? sD[rb + acc_row(lane, e)] : sD[0];
-                const T* vr = sVn + (16 * hc + (lane & 15)) * LDC;
-#pragma unroll
-                for (int k0 = 0; k0 < C; k0 += KS)
-                    hacc[s] = M::mma(M::load_t(sK + k0 * LDK + rb, LDK, lane), M::load(vr + k0, lane),
-                                     hacc[s]);
-                store_acc_t(shT + (16 * hc) * LDK + rb, LDK, lane, hacc[s]);
-            }
-        }
-        if (more) {
-            if (L::NBUF == 2) {
-                GDN_SCAN_COMMIT(smem + ((j + 1) & 1) * L::BUF);
-            } else {
-                __syncthreads();   // single buffer: every wave is done with this chunk
-                GDN_SCAN_COMMIT(smem);
-            }
-        }
-        __syncthreads();
-    }
-
-#undef GDN_SCAN_ISSUE
-#undef GDN_SCAN_COMMIT
-    if (a.ht) {
-        float* ht = a.ht + (n * a.H + h) * (int64_t)(K * V);
-#pragma unroll
-        for (int s = 0; s < HPW; ++s) {
-            const int id = wave + NW * s;
-            if (id < NHT) {
-                const int rb = 16 * (id / CT), hc = id % CT;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    ht[(rb + acc_row(lane, e)) * V + v0 + 16 * hc + acc_col(lane)] = hacc[s][e];
-            }
-        }
+        ScanH<Cfg> r{ch, wave - Cfg::NVW - Cfg::NOW, {}};
+        r.init();
+        if (ch.nch > 0) drive<Cfg::PD>(r, ch.nch);
+        r.finish();
     }
 }
 
-template <typename T, int K, int V, int C, int VT, bool PK>
-static hipError_t launch_scan_t(const ScanLaunch& a) {
+template <typename Cfg>
+static hipError_t launch_scan_cfg(const ScanLaunch& a) {
     const int64_t chains = a.N * a.H;
-    const int64_t nblk = ((chains + 7) / 8) * 8 * (V / VT);
-    hipLaunchKernelGGL((scan_kernel<T, K, V, C, VT, PK>), dim3((unsigned)nblk), dim3(SCAN_THREADS),
-                       0, a.stream, a);
+    const int64_t nblk = ((chains + 7) / 8) * 8 * (Cfg::V / Cfg::VT);
+    hipLaunchKernelGGL((scan_kernel<Cfg>), dim3((unsigned)nblk), dim3(Cfg::NT), 0, a.stream, a);
     return hipGetLastError();
 }
 
-template <typename T, int VT>
+// value-slice width: one workgroup per CU when the chains allow it, and the
+// narrowest slices for packed sequences (whose longest chain sets the time)
+// (bf16 slices are at most 64 wide with K = 128: 128 would spill registers)
+static int scan_vt(const ScanLaunch& a, bool bf16) {
+    if (!bf16) return 32;
+    const int min_nvt = (a.K == 128 && a.V == 128) ? 2 : 1;
+    int nvt = a.V / 32;
+    if (!a.map.seqs)
+        while (nvt > min_nvt && a.N * a.H * nvt > 256) nvt /= 2;
+    return a.V / nvt;
+}
+
+// prefetch distance (chunks) of the 32-wide bf16 slices
+#ifndef GDN_SCAN_PD
+#define GDN_SCAN_PD 2
+#endif
+
+template <typename T, int K, int V, bool PK>
+static hipError_t launch_scan_kv(const ScanLaunch& a, int vt) {
+    constexpr bool B = sizeof(T) == 2;
+    if (vt == 32) return launch_scan_cfg<ScanCfg<T, K, V, 64, 32, PK, B ? GDN_SCAN_PD : 1>>(a);
+    if constexpr (B) {
+        if (vt == 64) return launch_scan_cfg<ScanCfg<T, K, V, 64, 64, PK, 2>>(a);
+        if constexpr (V == 128 && K == 64)
+            if (vt == 128) return launch_scan_cfg<ScanCfg<T, K, V, 64, 128, PK, 1>>(a);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
 static hipError_t launch_scan_dt(const ScanLaunch& a) {
-#define GDN_SCAN_CASE(KK, VV)                                                    \
-    if (a.K == KK && a.V == VV)                                                  \
-        return a.per_key ? launch_scan_t<T, KK, VV, 64, VT, true>(a)             \
-                         : launch_scan_t<T, KK, VV, 64, VT, false>(a);
+    const int vt = scan_vt(a, sizeof(T) == 2);
+#define GDN_SCAN_CASE(KK, VV)                                                         \
+    if (a.K == KK && a.V == VV)                                                       \
+        return a.per_key ? launch_scan_kv<T, KK, VV, true>(a, vt)                     \
+                         : launch_scan_kv<T, KK, VV, false>(a, vt);
     GDN_SCAN_CASE(64, 64)
     GDN_SCAN_CASE(64, 128)
     GDN_SCAN_CASE(128, 64)
@@ -339,7 +459,7 @@ static hipError_t launch_scan_dt(const ScanLaunch& a) {
 
 hipError_t launch_scan(const ScanLaunch& a) {
     if (a.C != 64) return hipErrorInvalidValue;
-    return a.bf16 ? launch_scan_dt<bf16, 32>(a) : launch_scan_dt<float, 32>(a);
+    return a.bf16 ? launch_scan_dt<bf16>(a) : launch_scan_dt<float>(a);
 }
 
 }  // namespace gdn
