@@ -85,6 +85,25 @@ def events_time(fn, reps):
     return s.elapsed_time(e) / 1e3 / reps
 
 
+def step_kernel_times(first, second, reps):
+    """Average durations of first() and second() when launched alternately,
+    as in a step, from HIP events recorded between the launches."""
+    first()
+    second()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * reps)]
+    for r in range(reps):
+        ev[3 * r].record()
+        first()
+        ev[3 * r + 1].record()
+        second()
+        ev[3 * r + 2].record()
+    ev[-1].synchronize()
+    a = sum(ev[3 * r].elapsed_time(ev[3 * r + 1]) for r in range(reps)) / reps / 1e3
+    b = sum(ev[3 * r + 1].elapsed_time(ev[3 * r + 2]) for r in range(reps)) / reps / 1e3
+    return a, b
+
+
 def bench_prefill(args, gdn):
     spec = gdn_synth.PREFILL[1]
     log("generating", spec.name)
@@ -109,11 +128,13 @@ def bench_prefill(args, gdn):
     dt = (time.perf_counter() - t0) / args.steps
     log("prefill step %.1f us" % (dt * 1e6))
 
-    # per-kernel durations (HIP events on the launch stream)
+    # per-kernel durations inside the step sequence (intra, scan, intra, ...),
+    # from HIP events recorded on the launch stream between the two launches
     reps = max(args.steps, 10)
-    t_intra = events_time(lambda: gdn.chunk_intra(q, k, v, beta, g, d["scale"],
-                                                  store_ainv=False, workspace=ws, views=False), reps)
-    t_scan = events_time(lambda: gdn.chunk_scan(desc, ws, o, h0=h0, ht=ht), reps)
+    t_intra, t_scan = step_kernel_times(
+        lambda: gdn.chunk_intra(q, k, v, beta, g, d["scale"], store_ainv=False, workspace=ws,
+                                views=False),
+        lambda: gdn.chunk_scan(desc, ws, o, h0=h0, ht=ht), reps)
     log("intra %.1f us, scan %.1f us" % (t_intra * 1e6, t_scan * 1e6))
 
     b_intra, b_scan = prefill_bytes(spec, spec.B)

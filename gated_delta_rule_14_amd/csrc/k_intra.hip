@@ -84,7 +84,18 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
     T* sA2 = reinterpret_cast<T*>(sA);        // Ainv diag(beta)         (after A is used)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-    const int64_t c = blockIdx.x, h = blockIdx.y, H = a.H;
+    // Workgroups run roughly in id order; ids go to the chunks in decreasing
+    // position inside their sequence (all heads of a chunk together), so the
+    // first chunks, which the state pass reads first, are written last and
+    // are the ones still held in the memory-side cache when it starts.
+    const int64_t H = a.H, bid = blockIdx.x, h = bid % H, cr = bid / H;
+    int64_t c;
+    if (a.map.table) {
+        c = a.map.max_chunks - 1 - cr;
+    } else {
+        const int64_t B = a.map.max_chunks / a.map.nt;
+        c = (cr % B) * a.map.nt + (a.map.nt - 1 - cr / B);
+    }
 
     // ---- which tokens this chunk covers
     int64_t t0;
@@ -525,7 +536,7 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
 
 template <typename T, int K, int V, int C, bool PK>
 static hipError_t launch_intra_t(const IntraLaunch& a) {
-    dim3 grid((unsigned)a.map.max_chunks, (unsigned)a.H);
+    dim3 grid((unsigned)(a.map.max_chunks * a.H));
     if (a.ws.ainv)
         hipLaunchKernelGGL((intra_kernel<T, K, V, C, PK, true>), grid, dim3(INTRA_THREADS), 0,
                            a.stream, a);

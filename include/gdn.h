@@ -145,16 +145,16 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_desc *d,
  * workspace (byte offsets from its start).  Every per-chunk array is indexed
  * [head][chunk][...] with max_chunks chunk slots per head; chunk j of
  * sequence b is slot b * ceil(T / C) + j without cu_seqlens, and slot
- * (first chunk of the sequence) + j with it.  Rows of a ragged last chunk
- * past its end hold zeros.  With G the inclusive cumulative log2 gate inside
- * the chunk and gamma = 2^G:
+ * (first chunk of the sequence) + j with it.  With G the inclusive cumulative
+ * log2 gate inside the chunk and gamma = 2^G:
  *   gcum  float [H][mc][C]  (scalar gate) or [H][mc][C][K] (per-key gate): G
- *   w     [H][mc][C][K]     W = (I+A)^{-1} diag(beta) diag(gamma) K
- *   u     [H][mc][C][V]     U = (I+A)^{-1} diag(beta) V
- *   qs    [H][mc][C][K]     scale * diag(gamma) Q
- *   ks    [H][mc][C][K]     diag(gamma_C / gamma) K
- *   aqk   [H][mc][C][C]     scale * (Q K^T masked by Gamma, diagonal kept)
- *   ainv  float [H][mc][C][C]  (I+A)^{-1}; written only by gdn_chunk_intra
+ *   w     [H][mc] x (C x K)  W = (I+A)^{-1} diag(beta) diag(gamma) K      F
+ *   u     [H][mc] x (C x V)  U = (I+A)^{-1} diag(beta) V                  A
+ *   qs    [H][mc] x (C x K)  scale * diag(gamma) Q                        F
+ *   ks    [H][mc] x (K x C)  (diag(gamma_C / gamma) K)^T                  F
+ *   aqk   [H][mc] x (C x C)  scale * (Q K^T masked by Gamma, diagonal kept)  F
+ *   ainv  float [H][mc][C][C]  (I+A)^{-1}, row-major; written only by
+ *                           gdn_chunk_intra
  *   chunks int32 [mc][4]    (first token, token count, sequence, 0) per chunk
  *                           slot (packed input only)
  *   seqs  int32 [N][4]      (first token, length, first chunk slot, chunks)
@@ -164,6 +164,19 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_desc *d,
  * per-key gate gamma is per channel and every Gamma factor sits inside the
  * sum over the key channel.  A descriptor with num_seqs > 0 describes packed
  * input.
+ *
+ * Element order of an R x D block X (the orders the MFMA instructions of the
+ * state pass read without rearranging):
+ *   F (fragment order): 16-byte groups of 64 lanes; group (rt, sg), rt <
+ *     R/16, sg < D/KG, lane l, element e < VE holds X[16 rt + l%16][KG sg + c]
+ *     at element ((rt * D/KG + sg) * 64 + l) * VE + e, with c = 8 (l/16) + e,
+ *     KG = 32, VE = 8 for bf16 and c = 4 e + l/16, KG = 16, VE = 4 for fp32.
+ *   A (accumulator order): tile (rt, ct), rt < R/16, ct < D/16, lane l,
+ *     element e < 4 holds X[16 rt + 4 (l/16) + e][16 ct + l%16] at element
+ *     ((rt * D/16 + ct) * 64 + l) * 4 + e.
+ * Rows of W and U past the end of a ragged last chunk are zero; there the
+ * rows of qs and aqk and the columns of ks repeat the chunk's last token and
+ * never reach an output.
  */
 typedef struct gdn_workspace_layout {
     size_t gcum, w, u, qs, ks, aqk, ainv, chunks, seqs;
