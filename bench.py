@@ -1,11 +1,13 @@
 #!/usr/bin/env python3
 """Benchmark of the chunked gated delta rule forward on one MI355X.
 
-A step is one pass of the whole prefill path (the chunk table for packed
-input, the intra-chunk stage and the state pass with the fused output) over
-the GDN workload B=4, T=4096, H=16, d_k=d_v=128, chunk 64, bf16 q/k/v with
-fp32 beta, gates and states, inputs resident in HBM.  `value` is tokens/s
-(B*T tokens per step).  The same run also times each kernel with HIP events,
+A step is one pass of the whole prefill path (one gdn_chunk_fwd: for this
+shape the fused kernel, which builds every intra-chunk product in LDS and
+runs the state pass with the output in the same launch) over the GDN workload
+B=4, T=4096, H=16, d_k=d_v=128, chunk 64, bf16 q/k/v with fp32 beta, gates
+and states, inputs resident in HBM.  `value` is tokens/s (B*T tokens per
+step).  The same run times the kernel of every step with HIP events on its
+stream, the two-stage path (intra-chunk stage + state pass) for comparison,
 the decode step (256 sequences x 32 heads, fp32 state in place, 64 steps),
 and the fp64 CPU oracle on the host cores.
 
@@ -37,9 +39,10 @@ def log(*a):
 
 
 def prefill_bytes(spec, n_seqs):
-    """Algorithmic HBM bytes of one prefill pass, split by the kernel that
-    must move them: the intra-chunk stage reads q, k, v, beta, g; the state
-    pass writes o and reads h0 / writes ht."""
+    """Algorithmic HBM bytes of one prefill pass, split by what must move
+    them: the inputs q, k, v, beta, g (read by the intra-chunk stage, or by
+    the fused kernel), and o, h0, ht (written / read by the state pass, or by
+    the fused kernel)."""
     es = 2 if spec.dtype == "bf16" else 4
     th = spec.B * spec.T * spec.H
     gate = 4 * (spec.K if spec.gate == "per_key" else 1)
@@ -49,7 +52,8 @@ def prefill_bytes(spec, n_seqs):
     return intra, scan
 
 
-KERNEL_SOURCES = {"intra_kernel": ["k_intra.hip", "gdn_device.hpp"],
+KERNEL_SOURCES = {"fused_kernel": ["k_fused.hip", "gdn_device.hpp"],
+                  "intra_kernel": ["k_intra.hip", "gdn_device.hpp"],
                   "scan_kernel": ["k_scan.hip", "gdn_device.hpp"],
                   "step_kernel": ["k_step.hip", "gdn_device.hpp"]}
 
@@ -120,41 +124,56 @@ def bench_prefill(args, gdn):
 
     for _ in range(args.warmup):
         step()
+    # timed region: wall clock around the K steps, and a HIP event pair around
+    # each step's kernel on the stream it is launched on
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        ev[2 * i].record()
         step()
+        ev[2 * i + 1].record()
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / args.steps
-    log("prefill step %.1f us" % (dt * 1e6))
+    t_fused = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)) / args.steps / 1e3
+    log("prefill step %.1f us (fused kernel %.1f us)" % (dt * 1e6, t_fused * 1e6))
 
-    # per-kernel durations inside the step sequence (intra, scan, intra, ...),
-    # from HIP events recorded on the launch stream between the two launches
+    # the two-stage path on the same inputs, for comparison: per-kernel
+    # durations inside its step sequence (intra, scan, intra, ...)
+    L = gdn.workspace_layout(desc)
+    ws2 = torch.empty(L.total, dtype=torch.uint8, device="cuda")
+    o2 = torch.empty_like(o)
+    ht2 = torch.empty_like(ht)
     reps = max(args.steps, 10)
     t_intra, t_scan = step_kernel_times(
-        lambda: gdn.chunk_intra(q, k, v, beta, g, d["scale"], store_ainv=False, workspace=ws,
+        lambda: gdn.chunk_intra(q, k, v, beta, g, d["scale"], store_ainv=False, workspace=ws2,
                                 views=False),
-        lambda: gdn.chunk_scan(desc, ws, o, h0=h0, ht=ht), reps)
-    log("intra %.1f us, scan %.1f us" % (t_intra * 1e6, t_scan * 1e6))
+        lambda: gdn.chunk_scan(desc, ws2, o2, h0=h0, ht=ht2), reps)
+    del ws2
+    log("two-stage path: intra %.1f us, scan %.1f us" % (t_intra * 1e6, t_scan * 1e6))
 
-    b_intra, b_scan = prefill_bytes(spec, spec.B)
+    b_in, b_out = prefill_bytes(spec, spec.B)
+    b_all = b_in + b_out
     th = spec.B * spec.T * spec.H
     flops = gdn_synth.flops_per_token_head(spec.K, spec.V, spec.chunk) * th
     kernels = {
-        "intra_kernel": {"us": t_intra * 1e6, "alg_bytes": b_intra,
-                         "GBps": b_intra / t_intra / 1e9},
-        "scan_kernel": {"us": t_scan * 1e6, "alg_bytes": b_scan, "GBps": b_scan / t_scan / 1e9},
+        "fused_kernel": {"us": t_fused * 1e6, "alg_bytes": b_all, "GBps": b_all / t_fused / 1e9,
+                         "TFLOPs": flops / t_fused / 1e12,
+                         "frac_mfma_bf16": flops / t_fused / BF16_PEAK},
     }
-    dom, t_dom, b_dom = (("intra_kernel", t_intra, b_intra) if t_intra >= t_scan
-                         else ("scan_kernel", t_scan, b_scan))
-    roof = {"bound": "hbm", "kernel": dom, "achieved": b_dom / t_dom / 1e9, "peak": HBM_PEAK / 1e9,
-            "unit": "GB/s", "frac": b_dom / t_dom / HBM_PEAK, "traffic": measured_traffic(dom)}
-    for name in kernels:
-        kernels[name]["traffic"] = measured_traffic(name)
-    path = {"alg_bytes": b_intra + b_scan, "GBps": (b_intra + b_scan) / dt / 1e9,
-            "frac_hbm": (b_intra + b_scan) / dt / HBM_PEAK,
+    two_stage = {
+        "intra_kernel": {"us": t_intra * 1e6, "alg_bytes": b_in, "GBps": b_in / t_intra / 1e9},
+        "scan_kernel": {"us": t_scan * 1e6, "alg_bytes": b_out, "GBps": b_out / t_scan / 1e9},
+    }
+    roof = {"bound": "hbm", "kernel": "fused_kernel", "achieved": b_all / t_fused / 1e9,
+            "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": b_all / t_fused / HBM_PEAK,
+            "traffic": measured_traffic("fused_kernel")}
+    kernels["fused_kernel"]["traffic"] = roof["traffic"]
+    for name in two_stage:
+        two_stage[name]["traffic"] = measured_traffic(name)
+    path = {"alg_bytes": b_all, "GBps": b_all / dt / 1e9, "frac_hbm": b_all / dt / HBM_PEAK,
             "alg_flops": flops, "TFLOPs": flops / dt / 1e12, "frac_mfma_bf16": flops / dt / BF16_PEAK}
-    return spec, dt, roof, path, kernels, d
+    return spec, dt, roof, path, kernels, two_stage, d
 
 
 def bench_decode(args, gdn):
@@ -228,7 +247,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    spec, dt, roof, path, kernels, d = bench_prefill(args, gdn)
+    spec, dt, roof, path, kernels, two_stage, d = bench_prefill(args, gdn)
     decode = None if args.no_decode else bench_decode(args, gdn)
     cpu = None if args.no_cpu else cpu_baseline(d)
     line = {
@@ -251,6 +270,7 @@ def main():
         "path": path,
         "mfma_pct_of_bf16_peak": 100.0 * path["frac_mfma_bf16"],
         "kernels": kernels,
+        "two_stage": two_stage,
         "decode": decode,
         "device": torch.cuda.get_device_name(0),
     }

@@ -97,6 +97,22 @@ void layout(const gdn_fwd_desc* d, bool packed, gdn_workspace_layout* L) {
     L->max_chunks = mc;
 }
 
+// gdn_chunk_fwd runs the fused kernel for these shapes; its workspace holds
+// only the per-sequence records of packed input
+bool fused_path(const gdn_fwd_desc* d) {
+    gdn::FusedLaunch f{};
+    f.bf16 = d->qkv_dtype == GDN_DTYPE_BF16;
+    f.per_key = d->gate == GDN_GATE_PER_KEY;
+    f.K = (int)d->key_dim;
+    f.V = (int)d->value_dim;
+    f.C = d->chunk;
+    return gdn::fused_supported(f);
+}
+
+size_t fused_workspace(const gdn_fwd_desc* d, bool packed) {
+    return align256((size_t)(packed ? d->num_seqs : 1) * 16);
+}
+
 gdn_status hip_fail(hipError_t e, const char* what) {
     return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -215,7 +231,7 @@ gdn_status gdn_chunk_fwd_workspace(const gdn_fwd_desc* d, size_t* bytes) {
     gdn_workspace_layout L;
     gdn_status s = gdn_workspace_layout_of(d, &L);
     if (s != GDN_OK) return s;
-    *bytes = L.total;
+    *bytes = fused_path(d) ? fused_workspace(d, d->num_seqs > 0) : L.total;
     return ok();
 }
 
@@ -282,6 +298,64 @@ gdn_status gdn_chunk_scan(const gdn_fwd_desc* d, const float* h0, const int64_t*
                 static_cast<hipStream_t>(stream));
 }
 
+static gdn_status fused_fwd(const gdn_fwd_desc* d, const void* q, const void* k, const void* v,
+                            const float* beta, const float* g, const float* h0,
+                            const int64_t* cu_seqlens, void* o, float* ht, void* workspace,
+                            size_t workspace_bytes, hipStream_t st) {
+    const bool packed = cu_seqlens != nullptr;
+    if (!packed && d->num_seqs != 0)
+        return fail(GDN_ERR_BAD_SHAPE, "num_seqs must be 0 without cu_seqlens");
+    if (!q || !k || !v || !beta || !g || !workspace)
+        return fail(GDN_ERR_NULL_ARG, "q, k, v, beta, g and workspace are required");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned4(beta) || !aligned4(g) ||
+        !aligned8(cu_seqlens))
+        return fail(GDN_ERR_MISALIGNED,
+                    "q, k, v need 16-byte, beta and g 4-byte, cu_seqlens 8-byte alignment");
+    if (((uintptr_t)workspace & 255u) != 0)
+        return fail(GDN_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    const size_t need = fused_workspace(d, packed);
+    if (workspace_bytes < need)
+        return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes,
+                    need);
+    gdn::FusedLaunch a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.beta = beta;
+    a.g = g;
+    a.h0 = h0;
+    a.ht = ht;
+    a.o = o;
+    a.seqs = nullptr;
+    a.T = d->seq_len;
+    a.N = packed ? d->num_seqs : d->batch;
+    a.H = d->num_heads;
+    a.K = (int)d->key_dim;
+    a.V = (int)d->value_dim;
+    a.C = d->chunk;
+    a.scale = d->scale;
+    a.bf16 = true;
+    a.per_key = false;
+    a.stream = st;
+    if (packed) {
+        gdn::TableLaunch t;
+        t.cu_seqlens = cu_seqlens;
+        t.N = d->num_seqs;
+        t.T = d->seq_len;
+        t.C = d->chunk;
+        t.table = nullptr;
+        t.seqs = static_cast<int4*>(workspace);
+        t.max_chunks = max_chunks_of(d, true);
+        t.stream = st;
+        hipError_t e = gdn::launch_table(t);
+        if (e != hipSuccess) return hip_fail(e, "sequence table launch");
+        a.seqs = static_cast<const int4*>(workspace);
+    }
+    hipError_t e = gdn::launch_fused(a);
+    if (e != hipSuccess) return hip_fail(e, "fused forward launch");
+    return ok();
+}
+
 gdn_status gdn_chunk_fwd(const gdn_fwd_desc* d, const void* q, const void* k, const void* v,
                          const float* beta, const float* g, const float* h0,
                          const int64_t* cu_seqlens, void* o, float* ht, void* workspace,
@@ -293,6 +367,8 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_desc* d, const void* q, const void* k, co
     if (!aligned16(o) || !aligned4(h0) || !aligned4(ht))
         return fail(GDN_ERR_MISALIGNED, "o needs 16-byte, h0 and ht 4-byte alignment");
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (fused_path(d)) return fused_fwd(d, q, k, v, beta, g, h0, cu_seqlens, o, ht, workspace,
+                                        workspace_bytes, st);
     Prepared P;
     s = prepare(d, q, k, v, beta, g, cu_seqlens, workspace, workspace_bytes, false, st, &P);
     if (s != GDN_OK) return s;

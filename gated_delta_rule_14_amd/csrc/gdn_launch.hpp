@@ -66,11 +66,28 @@ struct ScanLaunch {
     hipStream_t stream;
 };
 
+// The fused forward (bf16 q/k/v, scalar gate, K = V = 128, C = 64): one
+// kernel per call, no per-chunk intermediates in HBM.
+struct FusedLaunch {
+    const void *q, *k, *v;
+    const float *beta, *g;
+    const float* h0;
+    float* ht;
+    void* o;
+    const int4* seqs;       // [N] (t0, len, ...) for packed input, else nullptr
+    int64_t T;              // tokens per sequence when seqs == nullptr
+    int64_t N, H;
+    int K, V, C;
+    float scale;
+    bool bf16, per_key;
+    hipStream_t stream;
+};
+
 struct TableLaunch {
     const int64_t* cu_seqlens;
     int64_t N, T;
     int C;
-    int4* table;
+    int4* table;            // nullptr: write only seqs
     int4* seqs;
     int64_t max_chunks;
     hipStream_t stream;
@@ -80,5 +97,7 @@ hipError_t launch_step(const StepLaunch& a);
 hipError_t launch_table(const TableLaunch& a);
 hipError_t launch_intra(const IntraLaunch& a);
 hipError_t launch_scan(const ScanLaunch& a);
+bool fused_supported(const FusedLaunch& a);
+hipError_t launch_fused(const FusedLaunch& a);
 
 }  // namespace gdn

@@ -10,6 +10,7 @@
 // offsets can give wrong results but never an out-of-bounds access.
 //   seqs[n]  = (first token, length, first chunk, chunk count)
 //   table[c] = (first token, token count, sequence, 0); unused rows have count 0
+// (the table is skipped when its pointer is null: the fused forward needs only seqs)
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
@@ -41,7 +42,7 @@ __global__ __launch_bounds__(256) void table_kernel(TableLaunch a) {
         const int64_t first = s_carry + s_part[tid] - nc;
         if (n < a.N) {
             a.seqs[n] = make_int4((int)s, (int)len, (int)min(first, a.max_chunks), (int)nc);
-            for (int64_t j = 0; j < nc; ++j) {
+            for (int64_t j = 0; a.table && j < nc; ++j) {
                 const int64_t c = first + j;
                 if (c >= a.max_chunks) break;
                 a.table[c] = make_int4((int)(s + j * a.C), (int)min((int64_t)a.C, len - j * a.C),
@@ -52,7 +53,9 @@ __global__ __launch_bounds__(256) void table_kernel(TableLaunch a) {
         if (tid == 255) s_carry += s_part[255];
         __syncthreads();
     }
-    for (int64_t c = s_carry + tid; c < a.max_chunks; c += 256) a.table[c] = make_int4(0, 0, -1, 0);
+    if (a.table)
+        for (int64_t c = s_carry + tid; c < a.max_chunks; c += 256)
+            a.table[c] = make_int4(0, 0, -1, 0);
 }
 
 hipError_t launch_table(const TableLaunch& a) {

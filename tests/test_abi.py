@@ -71,7 +71,12 @@ def test_workspace_size_and_layout(lib):
     assert L.total >= L.chunks
     offs = [L.gcum, L.w, L.u, L.qs, L.ks, L.aqk, L.ainv, L.chunks, L.total]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
-    assert gdn.workspace_bytes(d) == L.total
+    # the two-stage path (here fp32) needs the whole layout; the fused path
+    # (bf16, scalar gate, K = V = 128) only the per-sequence records
+    assert gdn.workspace_bytes(_desc(qkv_dtype=0)) == gdn.workspace_layout(_desc(qkv_dtype=0)).total
+    assert gdn.workspace_bytes(_desc(gate=1)) == gdn.workspace_layout(_desc(gate=1)).total
+    assert gdn.workspace_bytes(d) == 256
+    assert gdn.workspace_bytes(_desc(batch=1, seq_len=300, num_seqs=40)) == 768
     # packed: one extra chunk slot per sequence
     P = gdn.workspace_layout(_desc(batch=1, seq_len=300, num_seqs=3))
     assert P.max_chunks == 5 + 3
@@ -94,7 +99,8 @@ def test_chunk_fwd_rejects_before_launch(lib):
     assert _fwd(lib, d, q=MIS) == 6
     assert _fwd(lib, d, h0=ctypes.c_void_p((1 << 20) + 2)) == 6
     assert _fwd(lib, d, ws=ctypes.c_void_p((1 << 20) + 64)) == 6
-    assert _fwd(lib, d, wsb=1024) == 5
+    assert _fwd(lib, d, wsb=128) == 5
+    assert _fwd(lib, _desc(qkv_dtype=0), wsb=1024) == 5
     assert _fwd(lib, _desc(batch=2, num_seqs=2), cu=FAKE) == 2      # packed needs B == 1
     assert _fwd(lib, _desc(batch=1), cu=FAKE) == 2                  # packed needs num_seqs
     assert lib.gdn_chunk_intra(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, None, FAKE,
