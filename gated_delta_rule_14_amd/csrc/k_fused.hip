@@ -433,10 +433,12 @@ __constant__ int AO_J[6] = {0, 1, 2, 0, 1, 0};
 // values in registers, and the wave index inside the role is a runtime value
 // so that the kernel's code (three loops) stays well inside the instruction
 // cache.  Every wave executes the same barriers in the same order.
-template <int R>
+template <int R, int SUB>
 __device__ __forceinline__ void run_role(Ctx& x, const FusedLaunch& a, int64_t n) {
     constexpr bool VW = R == 0, OW = R == 1, HW = R == 2;
-    const int W = x.wave;   // 0..7, uniform over the wave
+    // wave index: a compile-time constant for the V and O waves (whose work
+    // differs by block), a runtime value for the four H waves
+    const int W = HW ? x.wave : (VW ? SUB : 2 + SUB);
     const int lane = x.lane;
     f32x4 hacc[2][CT];   // H waves: h rows 32p.., fp32
     if constexpr (HW) {
@@ -469,7 +471,7 @@ __device__ __forceinline__ void run_role(Ctx& x, const FusedLaunch& a, int64_t n
         bf16x4 aq[2][4];     // O waves: causal Q K^T blocks (J, I), 16x16x16 B operands
         // wave 2 owns token blocks 0 and 3, wave 3 blocks 1 and 2: both then
         // have five causal Q K^T blocks
-        const int ib0 = W == 3 ? 1 : 0, ib1 = W == 3 ? 2 : 3;
+        constexpr int ib0 = SUB == 1 ? 1 : 0, ib1 = SUB == 1 ? 2 : 3;
         // ================= P1
         // Staged inputs are stored unconditionally (clamped duplicates for
         // chunks past the end land in slots no live chunk uses), so that no
@@ -478,7 +480,7 @@ __device__ __forceinline__ void run_role(Ctx& x, const FusedLaunch& a, int64_t n
         if constexpr (VW) {
             if (scan) {
                 // R = diag(beta) (V - diag(gamma) K h) for token rows 32m..32m+31
-                const int m = W;
+                constexpr int m = SUB;
                 const bf16* kk = x.sK(j);
                 f32x4 acc[2][CT];
 #pragma unroll
@@ -577,7 +579,7 @@ __device__ __forceinline__ void run_role(Ctx& x, const FusedLaunch& a, int64_t n
             if (scan) {
                 // V_new = T R for token rows 32m..32m+31 (T is zero above the
                 // diagonal, so k-steps past the rows' own block add nothing)
-                const int m = W;
+                constexpr int m = SUB;
                 const float* T = x.sT(j);
                 const float* tail = x.gate(j, G_TAIL);
                 f32x4 vn[2][CT];
@@ -631,35 +633,44 @@ __device__ __forceinline__ void run_role(Ctx& x, const FusedLaunch& a, int64_t n
                     sqd[0] = M::mma(k0, b0, sqd[0]);
                     sqd[1] = M::mma(k1, b1, sqd[1]);
                 }
+                // every gate value the masks need, read before any is used
                 const float* G = x.gate(j, G_LOG);
+                const float* ROW = x.gate(j, G_ROW);
+                const int g4 = 4 * (lane >> 4);
+                float gi[2], si[2];
+                float4 gd[2], cj[2][3];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const int I = t ? ib1 : ib0, i = 16 * I + (lane & 15);
-                    const float gi = G[i];
-                    const float si = x.scale * x.gate(j, G_ROW)[i];
+                    gi[t] = G[i];
+                    si[t] = x.scale * ROW[i];
+                    gd[t] = *reinterpret_cast<const float4*>(G + 16 * I + g4);
+#pragma unroll
+                    for (int J = 0; J < I; ++J)
+                        cj[t][J] =
+                            *reinterpret_cast<const float4*>(x.gate(j, G_COL + I - 1) + 16 * J + g4);
+                }
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int I = t ? ib1 : ib0, i = 16 * I + (lane & 15);
                     // lane 16g+n of tile (J, I) holds S[i = 16I+n][j = 16J+4g+e];
                     // off-diagonal blocks use the factored decay, the diagonal
                     // block the direct one and the causal mask
 #pragma unroll
-                    for (int J = 0; J < 4; ++J) {
-                        if (J > I) continue;
-                        const int j0 = 16 * J + 4 * (lane >> 4);
-                        f32x4 av;
-                        if (J < I) {
-                            const float4 cj =
-                                *reinterpret_cast<const float4*>(x.gate(j, G_COL + I - 1) + j0);
-                            av = f32x4{si * cj.x * sq[t][J][0], si * cj.y * sq[t][J][1],
-                                       si * cj.z * sq[t][J][2], si * cj.w * sq[t][J][3]};
-                        } else {
+                    for (int J = 0; J < I; ++J)
+                        aq[t][J] = to_bf4(f32x4{si[t] * cj[t][J].x * sq[t][J][0],
+                                                si[t] * cj[t][J].y * sq[t][J][1],
+                                                si[t] * cj[t][J].z * sq[t][J][2],
+                                                si[t] * cj[t][J].w * sq[t][J][3]});
+                    const float gdv[4] = {gd[t].x, gd[t].y, gd[t].z, gd[t].w};
+                    f32x4 av;
 #pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                av[e] = j0 + e <= i
-                                            ? x.scale * exp2_hw(fminf(gi - G[j0 + e], 0.f)) *
-                                                  sqd[t][e]
-                                            : 0.f;
-                        }
-                        aq[t][J] = to_bf4(av);
+                    for (int e = 0; e < 4; ++e) {
+                        const int jj = 16 * I + g4 + e;
+                        av[e] = jj <= i ? x.scale * exp2_hw(fminf(gi[t] - gdv[e], 0.f)) * sqd[t][e]
+                                        : 0.f;
                     }
+                    aq[t][I] = to_bf4(av);
                 }
             }
         }
@@ -680,10 +691,10 @@ __device__ __forceinline__ void run_role(Ctx& x, const FusedLaunch& a, int64_t n
         // ================= P3
         x.store_q(s);
         // gates of chunk j+2 (first read in the next iteration's first phase)
-        if (W == 0) x.store_gates(s, c2);
+        if constexpr (VW && SUB == 0) x.store_gates(s, c2);
         x.load_for(s, j + PD);
         if constexpr (VW) {
-            if (in1) compose(x, c1, W);
+            if (in1) compose(x, c1, SUB);
         }
         if constexpr (OW) {
             if (scan) {
@@ -804,12 +815,13 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedLaunch a) {
     // zero both T slots: their upper blocks are read as zeros
     for (int i = x.tid; i < 2 * C * LDT; i += NT) x.sT(0)[i] = 0.f;
 
-    if (x.wave < 2)
-        run_role<0>(x, a, n);
-    else if (x.wave < 4)
-        run_role<1>(x, a, n);
-    else
-        run_role<2>(x, a, n);
+    switch (x.wave) {
+        case 0: run_role<0, 0>(x, a, n); break;
+        case 1: run_role<0, 1>(x, a, n); break;
+        case 2: run_role<1, 0>(x, a, n); break;
+        case 3: run_role<1, 1>(x, a, n); break;
+        default: run_role<2, 0>(x, a, n); break;
+    }
 }
 
 }  // namespace fz
