@@ -220,6 +220,9 @@ struct Ctx {
         return reinterpret_cast<const char*>(base + ((t0 + (int64_t)c * C) * H + h) * D);
     }
     // everything iteration j stores: K_{j+2} and gates_{j+2}, V_{j+1}, Q_{j+1}
+    // (the gates only in the wave that stores them: a load whose register is
+    // never read would make the compiler wait for it before reusing the register)
+    template <bool GATES>
     __device__ __forceinline__ void load_for(Stage& s, int j) const {
         const int cv = clampc(j + 1), ck = clampc(j + 2);
         const char* vb = chunk_row0(v, cv, V) + v0 * 2;
@@ -232,14 +235,12 @@ struct Ctx {
             s.k[p] = *reinterpret_cast<const u32x4*>(kb + roff(ck, i >> 4, K, (i & 15) * 16));
             s.q[p] = *reinterpret_cast<const u32x4*>(qb + roff(cv, i >> 4, K, (i & 15) * 16));
         }
-        // gates: every wave loads them (one wave stores them) so that all
-        // waves issue the same loads
-        const bool in = lane < rows(ck);
-        const uint32_t go = (uint32_t)min(lane, rows(ck) - 1) * (uint32_t)(H * 4);
-        const float gv = *reinterpret_cast<const float*>(chunk_row0(g, ck, 1) + go);
-        const float bv = *reinterpret_cast<const float*>(chunk_row0(beta, ck, 1) + go);
-        s.g = in ? gv : 0.f;
-        s.b = in ? bv : 0.f;
+        if constexpr (GATES) {
+            // rows past a ragged end re-read the last row; store_gates zeroes them
+            const uint32_t go = (uint32_t)min(lane, rows(ck) - 1) * (uint32_t)(H * 4);
+            s.g = *reinterpret_cast<const float*>(chunk_row0(g, ck, 1) + go);
+            s.b = *reinterpret_cast<const float*>(chunk_row0(beta, ck, 1) + go);
+        }
     }
 
     // ---- LDS stores of staged inputs
@@ -265,11 +266,13 @@ struct Ctx {
     // cumulative log2 gate and the per-row factors derived from it (one wave,
     // lane = row; rows past the chunk end carry g = 0 and beta = 0)
     __device__ __forceinline__ void store_gates(const Stage& s, int c) const {
-        const float G = wave_scan_dpp(s.g * LOG2E);
+        const bool in = lane < rows(c);
+        const float G = wave_scan_dpp(in ? s.g * LOG2E : 0.f);
+        const float bt = in ? s.b : 0.f;
         const float Gc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), C - 1));
         const float gam = exp2_hw(G);
         gate(c, G_LOG)[lane] = G;
-        gate(c, G_BETA)[lane] = s.b;
+        gate(c, G_BETA)[lane] = bt;
         gate(c, G_OUT)[lane] = scale * gam;
         gate(c, G_TAIL)[lane] = exp2_hw(fminf(Gc - G, 0.f));
         gate(c, G_GAM)[lane] = gam;
@@ -309,10 +312,11 @@ __device__ __forceinline__ f32x4 kk_t(const bf16* a_rows, const bf16* b_rows, in
 // off-diagonal block (I, J), I > J, of A: beta_i 2^{G_i - G_j} k_i.k_j -> sA (bf16)
 __device__ __forceinline__ void a_offdiag(const Ctx& x, int c, int I, int J) {
     const bf16* kk = x.sK(c);
-    const f32x4 s = kk_t(kk + 16 * J * LDK, kk + 16 * I * LDK, x.lane);
     const int i = 16 * I + (x.lane & 15), j0 = 16 * J + 4 * (x.lane >> 4);
-    const float ri = x.gate(c, G_BETA)[i] * x.gate(c, G_ROW)[i];
+    const float bi = x.gate(c, G_BETA)[i], rw = x.gate(c, G_ROW)[i];
     const float4 cj = *reinterpret_cast<const float4*>(x.gate(c, G_COL + I - 1) + j0);
+    const f32x4 s = kk_t(kk + 16 * J * LDK, kk + 16 * I * LDK, x.lane);
+    const float ri = bi * rw;
     store4(x.sA() + (i - 16) * LDA + j0,
            f32x4{ri * cj.x * s[0], ri * cj.y * s[1], ri * cj.z * s[2], ri * cj.w * s[3]});
 }
@@ -323,21 +327,22 @@ __device__ __forceinline__ void a_diag(const Ctx& x, int c, int b) {
     M::frag f[K / 32];
 #pragma unroll
     for (int k0 = 0; k0 < K / 32; ++k0) f[k0] = M::load(kb + 32 * k0, x.lane);
-    f32x4 s = zero4();
-#pragma unroll
-    for (int k0 = 0; k0 < K / 32; ++k0) s = M::mma(f[k0], f[k0], s);
     // lane 16g+n: S[16b + 4g + e][16b + n], i.e. A row m = 4g+e, column r = n
     const float* G = x.gate(c, G_LOG) + 16 * b;
     const float* B = x.gate(c, G_BETA) + 16 * b;
     const int r = x.lane & 15, m0 = 4 * (x.lane >> 4);
     const float gr = G[r];
+    const float4 gm4 = *reinterpret_cast<const float4*>(G + m0);
+    const float4 bm4 = *reinterpret_cast<const float4*>(B + m0);
+    f32x4 s = zero4();
+#pragma unroll
+    for (int k0 = 0; k0 < K / 32; ++k0) s = M::mma(f[k0], f[k0], s);
+    const float gm[4] = {gm4.x, gm4.y, gm4.z, gm4.w}, bm[4] = {bm4.x, bm4.y, bm4.z, bm4.w};
     float4 o;
     float* op = &o.x;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int m = m0 + e;
-        op[e] = r < m ? B[m] * exp2_hw(fminf(G[m] - gr, 0.f)) * s[e] : 0.f;
-    }
+    for (int e = 0; e < 4; ++e)
+        op[e] = r < m0 + e ? bm[e] * exp2_hw(fminf(gm[e] - gr, 0.f)) * s[e] : 0.f;
     *reinterpret_cast<float4*>(x.sN() + b * NBS + r * LDN + m0) = o;
 }
 
@@ -436,6 +441,7 @@ __constant__ int AO_J[6] = {0, 1, 2, 0, 1, 0};
 template <int R, int SUB>
 __device__ __forceinline__ void run_role(Ctx& x, const FusedLaunch& a, int64_t n) {
     constexpr bool VW = R == 0, OW = R == 1, HW = R == 2;
+    constexpr bool GW = VW && SUB == 0;   // the wave that computes the gate arrays
     // wave index: a compile-time constant for the V and O waves (whose work
     // differs by block), a runtime value for the four H waves
     const int W = HW ? x.wave : (VW ? SUB : 2 + SUB);
@@ -460,7 +466,7 @@ __device__ __forceinline__ void run_role(Ctx& x, const FusedLaunch& a, int64_t n
     Stage st[PD];
     if (x.nch > 0) {
 #pragma unroll
-    for (int s = 0; s < PD; ++s) x.load_for(st[s], s - 2);
+    for (int s = 0; s < PD; ++s) x.load_for<GW>(st[s], s - 2);
 
     auto iteration = [&](Stage& s, int j) __attribute__((always_inline)) {
         const int c1 = j + 1, c2 = j + 2;
@@ -482,6 +488,20 @@ __device__ __forceinline__ void run_role(Ctx& x, const FusedLaunch& a, int64_t n
                 // R = diag(beta) (V - diag(gamma) K h) for token rows 32m..32m+31
                 constexpr int m = SUB;
                 const bf16* kk = x.sK(j);
+                const float* bt = x.gate(j, G_BETA);
+                const float* gm = x.gate(j, G_GAM);
+                float4 b4[2], g4[2];
+                bf16x4 vv[2][CT];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int r0 = 32 * m + 16 * t;
+                    b4[t] = *reinterpret_cast<const float4*>(bt + r0 + 4 * (lane >> 4));
+                    g4[t] = *reinterpret_cast<const float4*>(gm + r0 + 4 * (lane >> 4));
+                    // V rows r0+4g+e, column 16ct+n: the accumulator's layout
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+                        vv[t][ct] = tr_b16(x.sV() + r0 * LDVS + 16 * ct, LDVS, lane);
+                }
                 f32x4 acc[2][CT];
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
@@ -500,21 +520,16 @@ __device__ __forceinline__ void run_role(Ctx& x, const FusedLaunch& a, int64_t n
                         acc[1][ct] = M::mma(a1, bh, acc[1][ct]);
                     }
                 }
-                const float* bt = x.gate(j, G_BETA);
-                const float* gm = x.gate(j, G_GAM);
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const int r0 = 32 * m + 16 * t;
-                    const float4 b4 = *reinterpret_cast<const float4*>(bt + r0 + 4 * (lane >> 4));
-                    const float4 g4 = *reinterpret_cast<const float4*>(gm + r0 + 4 * (lane >> 4));
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) {
-                        // V rows r0+4g+e, column 16ct+n: the accumulator's layout
-                        const bf16x4 vv = tr_b16(x.sV() + r0 * LDVS + 16 * ct, LDVS, lane);
-                        const f32x4 r{b4.x * ((float)vv[0] - g4.x * acc[t][ct][0]),
-                                      b4.y * ((float)vv[1] - g4.y * acc[t][ct][1]),
-                                      b4.z * ((float)vv[2] - g4.z * acc[t][ct][2]),
-                                      b4.w * ((float)vv[3] - g4.w * acc[t][ct][3])};
+                        const bf16x4 v4 = vv[t][ct];
+                        const f32x4 r{b4[t].x * ((float)v4[0] - g4[t].x * acc[t][ct][0]),
+                                      b4[t].y * ((float)v4[1] - g4[t].y * acc[t][ct][1]),
+                                      b4[t].z * ((float)v4[2] - g4[t].z * acc[t][ct][2]),
+                                      b4[t].w * ((float)v4[3] - g4[t].w * acc[t][ct][3])};
                         store_acc_t(x.sR() + 16 * ct * LDVN + r0, LDVN, lane, r);
                     }
                 }
@@ -525,6 +540,8 @@ __device__ __forceinline__ void run_role(Ctx& x, const FusedLaunch& a, int64_t n
                 // O^T = h^T Q^T for the two token blocks, and the
                 // off-diagonal causal blocks S^T(J, I) = K_J Q_I^T, J < I
                 const bf16* kk = x.sK(j);
+                const float* og = x.gate(j, G_OUT);
+                const float s0 = og[16 * ib0 + (lane & 15)], s1 = og[16 * ib1 + (lane & 15)];
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) oacc[ct][0] = oacc[ct][1] = zero4();
 #pragma unroll
@@ -553,8 +570,6 @@ __device__ __forceinline__ void run_role(Ctx& x, const FusedLaunch& a, int64_t n
                         if (J < ib1) sq[1][J] = M::mma(kf, b1, sq[1][J]);
                     }
                 }
-                const float* og = x.gate(j, G_OUT);
-                const float s0 = og[16 * ib0 + (lane & 15)], s1 = og[16 * ib1 + (lane & 15)];
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
                     oacc[ct][0] *= s0;
@@ -582,6 +597,10 @@ __device__ __forceinline__ void run_role(Ctx& x, const FusedLaunch& a, int64_t n
                 constexpr int m = SUB;
                 const float* T = x.sT(j);
                 const float* tail = x.gate(j, G_TAIL);
+                float4 f4[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    f4[t] = *reinterpret_cast<const float4*>(tail + 32 * m + 16 * t + 4 * (lane >> 4));
                 f32x4 vn[2][CT];
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
@@ -605,7 +624,7 @@ __device__ __forceinline__ void run_role(Ctx& x, const FusedLaunch& a, int64_t n
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const int r0 = 32 * m + 16 * t;
-                    const float4 f = *reinterpret_cast<const float4*>(tail + r0 + 4 * (lane >> 4));
+                    const float4 f = f4[t];
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) {
                         const f32x4 v = vn[t][ct];
@@ -691,8 +710,8 @@ __device__ __forceinline__ void run_role(Ctx& x, const FusedLaunch& a, int64_t n
         // ================= P3
         x.store_q(s);
         // gates of chunk j+2 (first read in the next iteration's first phase)
-        if constexpr (VW && SUB == 0) x.store_gates(s, c2);
-        x.load_for(s, j + PD);
+        if constexpr (GW) x.store_gates(s, c2);
+        x.load_for<GW>(s, j + PD);
         if constexpr (VW) {
             if (in1) compose(x, c1, SUB);
         }
