@@ -1,162 +1,172 @@
-// Fused chunked forward: the intra-chunk products and the inter-chunk state
-// pass in one kernel, for bf16 q/k/v with the scalar gate and K = V = 128.
+// Fused chunked forward with the state held in MFMA accumulators, for bf16
+// q/k/v with the scalar gate and K = V = 128.
 //
 // One workgroup (8 waves) per (sequence, head, 32-wide value slice) walks the
-// chunks of its sequence in order.  Everything a chunk needs besides the state
-// -- the cumulative gate, the masked products and the unit-lower inverse -- is
-// built in LDS a step ahead of the state pass that consumes it, so no
-// intermediate ever goes to HBM: the kernel reads q, k, v, beta, g and h0 once
-// and writes o and ht once.
-//
-// Per chunk of n <= C = 64 tokens (rows r), with G the inclusive cumulative
-// log2-gate inside the chunk and gamma_r = 2^{G_r} ("TileLang 实战：KDA 从零到一--
-// Gated DeltaNet" §2.3 eqs. 11-12 and §4.1; "Gated Delta Network（GDN）"
-// §4.1(a)-(d)):
+// chunks of its sequence in order.  Per chunk of n <= C = 64 tokens, with G
+// the inclusive cumulative log2-gate inside the chunk and gamma_r = 2^{G_r}
+// ("TileLang 实战：KDA 从零到一--Gated DeltaNet" §2.3 eqs. 11-12 and §4.1;
+// "Gated Delta Network（GDN）" §4.1(a)-(d)):
 //   A_ij   = beta_i 2^{G_i - G_j} k_i.k_j       (j < i)
 //   T      = (I + A)^{-1}
 //   Aqk_ij = scale 2^{G_i - G_j} q_i.k_j       (j <= i)
-//   R      = diag(beta) (V - diag(gamma) K h)
+//   R      = diag(beta) V - diag(beta gamma) K h
 //   V_new  = T R
 //   O      = diag(scale gamma) Q h + Aqk V_new
 //   h     <- gamma_C h + K^T diag(gamma_C / gamma) V_new
-// T R equals the pages' U - W h with W = T diag(beta gamma) K and
-// U = T diag(beta) V ("TileLang 实战" §2.2.4-2.2.6): the same product taken
-// in the other order, so W and U are never formed.  The output reads the
-// state entering the chunk; h is decayed before the chunk's contributions are
-// added ("TileLang 实战" §4.4).
+// T R is the pages' U - W h (W = T diag(beta gamma) K, U = T diag(beta) V,
+// "TileLang 实战" §2.2.4-2.2.6) taken in the other order, so W and U are never
+// formed.  The output reads the state entering the chunk; h is decayed before
+// the chunk's contributions are added ("TileLang 实战" §4.4).
 //
-// The inverse: the four 16x16 diagonal blocks of I + A by forward
-// substitution in fp32 (one wave, one lane per column), then the off-diagonal
-// blocks from T_IJ = -T_II sum_{m=J}^{I-1} A_Im T_mJ on bf16 MFMA
-// ("阅读笔记：DeltaNet 在 FLA 中的代码实现笔记", forward Step 2: 16x16 blocks
-// solved first and combined block-wise; "TileLang 实战" §4.2).
+// The state.  Waves 0 and 1 each own 16 of the 32 value columns and keep
+// their 128 x 16 slice of h in fp32 MFMA accumulators for the whole sequence.
+// v_mfma_f32_16x16x32_bf16 contracts over 32 k per instruction, lane group g
+// supplying k = 8g..8g+7, and leaves rows 4g..4g+3 of column n of its 16x16
+// result in lane 16g+n.  Two result tiles therefore hold, per lane, exactly
+// the eight k one lane group supplies to the next instruction, once the k
+// are assigned to the tiles' rows in the right order:
+//   - over tokens (T R, V_new^T Aqk^T, K^T V_new), the eight k of lane group
+//     g of step p are tokens 32p+4g.. and 32p+16+4g.. (rows 4g..4g+3 of token
+//     tiles 2p and 2p+1);
+//   - over key channels (K h, (Q h)^T), they are channels 32kk+8g..+7, and row
+//     4g+e of state tile r is channel 32(r/2) + 8g + 4(r%2) + e.
+// So K h, (Q h)^T, T R, V_new^T Aqk^T and K^T V_new take h, R and V_new
+// straight from registers: the serial chain from one chunk's state to the
+// next touches LDS only for the chunk's own inputs.
 //
-// Schedule.  Iteration j runs the state pass of chunk j and builds the
-// inverse of chunk j+1, in three phases separated by workgroup barriers:
-//   P1  V waves: K h and R; O waves: Q h; H waves: decay h, diagonal K K^T
-//       blocks of chunk j+1
-//   P2  V waves: V_new = T R; O waves: the causal Q K^T blocks; H waves:
-//       forward substitution and off-diagonal K K^T blocks of chunk j+1
-//   P3  O waves: + Aqk V_new, store O; H waves: update h; V waves: compose the
-//       off-diagonal blocks of chunk j+1's inverse
-// Wave roles: waves 0-1 own token rows 32m..32m+31 of R and V_new, waves 2-3
-// the token blocks {0, 3} and {1, 2} of O, waves 4-7 key rows 32p..32p+31 of h
-// (fp32, in MFMA accumulators).  Chunk inputs arrive through registers loaded
-// PD iterations ahead; K has three LDS slots and T two.
+// The inverse (wave 2): the eight 8x8 diagonal blocks of I + A by forward
+// substitution (fp32, one lane per column), one doubling step to the 16x16
+// blocks, T_bb = D - D X D (D = the 8x8 inverses, X = the 8x8 block below
+// the diagonal), then the off-diagonal 16x16 blocks from
+// T_IJ = -T_II sum_{m=J}^{I-1} A_Im T_mJ on bf16 MFMA, every product taken as
+// (a matrix in LDS) x (an accumulator) ("阅读笔记：DeltaNet 在 FLA 中的代码实现笔记",
+// forward Step 2: small diagonal blocks solved first, combined block-wise;
+// "TileLang 实战" §4.2).
+//
+// Schedule.  Iteration j (one workgroup barrier at its end):
+//   waves 0-1   the state pass of chunk j (waits for T_j)
+//   wave 2      composes T_j, signals it; inverts the diagonal blocks of
+//               chunk j+1 once they are signalled
+//   wave 3      the K K^T blocks of chunk j+1 (once its inputs are
+//               signalled): the diagonal ones first (signalled), then the
+//               off-diagonal ones
+//   waves 7,4,5 the causal Q K^T blocks of chunk j+1
+//   wave 6      signals that chunk j+1's inputs have landed, derives the
+//               gate arrays of chunk j+2 and starts the loads of K, Q, V of
+//               chunk j+2 and of g, beta of chunk j+3 straight into LDS
+//               (buffer loads with the LDS destination: no registers, rows
+//               past a ragged end read as 0)
+// Signals are LDS words written with release and polled with acquire
+// semantics; every wait is bounded.  The barrier waits for LDS traffic only,
+// so the loads stay in flight across it.
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
 namespace gdn {
 namespace fz {
 
-constexpr int C = 64, K = 128, V = 128, VT = 32, CT = VT / 16, NVT = V / VT;
-constexpr int NW = 8, NT = 64 * NW, PD = 2;
-// Row pitches: 16-byte fragment reads from rows 288 or 160 bytes apart are
-// free of LDS bank conflicts on gfx950, rows 272 or 144 bytes apart are not;
-// transposing reads are conflict-free at either.
-constexpr int LDK = K + 16;    // bf16 [C][LDK]    K, Q rows (288 B)
-constexpr int LDVS = VT + 16;  // bf16 [C][LDVS]   V slice rows (transposing reads)
-constexpr int LDA = 56;        // bf16 [48][LDA]   A rows 16..63, columns 0..47
-constexpr int LDT = C + 8;     // fp32 [C][LDT]    T (288 B)
-constexpr int LDN = 20;        // fp32 [4][NBS]    diagonal blocks of A, transposed
-constexpr int NBS = 16 * LDN + 4;   // block stride: the four blocks start on different banks
-constexpr int LDH = K + 16;    // bf16 [VT][LDH]   h^T (288 B)
-constexpr int LDVN = C + 16;   // bf16 [VT][LDVN]  R^T, V_new^T, (V_new scaled)^T (160 B)
-constexpr int NGA = 10;        // gate arrays per chunk slot
-// Per token r of a chunk: G_LOG the cumulative log2 gate G_r; G_BETA beta_r;
-// G_OUT scale 2^{G_r}; G_TAIL 2^{G_C - G_r}; G_GAM 2^{G_r}; G_END 2^{G_C}
-// (every entry); G_ROW 2^{G_r - G_b}, b the first token of r's 16-token block;
-// G_COL + I - 1 (I = 1, 2, 3): 2^{G_16I - G_r} for tokens r < 16I.
-// Off-diagonal 16x16 blocks take their decay 2^{G_i - G_j} as
-// G_ROW[i] * G_COL[I][j]: both factors lie in [0, 1], so neither overflows.
-enum { G_LOG = 0, G_BETA = 1, G_OUT = 2, G_TAIL = 3, G_GAM = 4, G_END = 5, G_ROW = 6, G_COL = 7 };
+constexpr int C = 64, K = 128, V = 128, VT = 32, NVT = V / VT;
+constexpr int NT = 512;
 
-constexpr size_t SZ_KQ = sizeof(bf16) * C * LDK;
-constexpr size_t SZ_T = sizeof(float) * C * LDT;
-constexpr size_t SZ_VN = sizeof(bf16) * VT * LDVN;
-constexpr size_t o_K = 0;                                     // 3 slots
-constexpr size_t o_Q = o_K + 3 * SZ_KQ;
-constexpr size_t o_V = o_Q + SZ_KQ;
-constexpr size_t o_A = o_V + sizeof(bf16) * C * LDVS;
-constexpr size_t o_N = o_A + sizeof(bf16) * 48 * LDA;
-constexpr size_t o_T = o_N + sizeof(float) * 4 * NBS;         // 2 slots
-constexpr size_t o_hT = o_T + 2 * SZ_T;
-constexpr size_t o_R = o_hT + sizeof(bf16) * VT * LDH;
-constexpr size_t o_Vn = o_R + SZ_VN;
-constexpr size_t o_Vt = o_Vn + SZ_VN;
-constexpr size_t o_Gt = o_Vt + SZ_VN;
-constexpr size_t BYTES = o_Gt + sizeof(float) * 3 * NGA * C;
+// ---------------------------------------------------------------- LDS layout
+// K, Q: 64 rows of 256 bytes; the 16-byte group holding columns 8q..8q+7 of
+// row r sits at position q ^ (2r mod 16).  V (the 32-column slice): 64 rows of
+// 64 bytes, group q of row r at q ^ 2((r/4)%2).  Pitches and permutations are
+// the ones measured free of LDS bank conflicts on gfx950 for the reads made
+// here: 16-byte row fragments need rows an odd multiple of 32 bytes apart
+// (or this permutation of 256-byte rows, which also serves the transposing
+// K^T reads), 8-byte row reads an odd multiple of 8 bytes.
+constexpr int SZ_KQ = C * 256;
+constexpr int SZ_V = C * VT * 2;
+constexpr int SZ_RAW = 2 * C * 4;    // g and beta as loaded
+constexpr int NGA = 10;              // gate arrays per chunk
+constexpr int SZ_G = NGA * C * 4;
+constexpr int SZ_AQ = 6 * 64 * 16;   // six causal 16x16x32 fragments of Aqk
+constexpr int LDTT = 80;             // bf16 per row of T^T (160 bytes)
+constexpr int SZ_TT = C * LDTT * 2;
+constexpr int LDAB = 20;             // bf16 per row of an off-diagonal A block (40 bytes)
+constexpr int SZ_AB = 16 * LDAB * 2;
+constexpr int SZ_A = 6 * SZ_AB;
+constexpr int LDD = 24;              // fp32 per row of a diagonal A block (96 bytes)
+constexpr int SZ_DB = 16 * LDD * 4;
+constexpr int LDDT = 20;             // bf16 per row of a 16x16 block of D^T (40 bytes)
+constexpr int SZ_DT = 16 * LDDT * 2;
+
+constexpr int o_K = 0;                       // 3 slots
+constexpr int o_Q = o_K + 3 * SZ_KQ;         // 3 slots
+constexpr int o_V = o_Q + 3 * SZ_KQ;         // 3 slots
+constexpr int o_RAW = o_V + 3 * SZ_V;        // 2 slots
+constexpr int o_G = o_RAW + 2 * SZ_RAW;      // 3 slots
+constexpr int o_AQ = o_G + 3 * SZ_G;         // 2 slots
+constexpr int o_TT = o_AQ + 2 * SZ_AQ;
+constexpr int o_A = o_TT + SZ_TT;            // 2 slots
+constexpr int o_D = o_A + 2 * SZ_A;
+constexpr int o_DT = o_D + 4 * SZ_DB;
+constexpr int o_F = o_DT + 4 * SZ_DT;        // signal words
+constexpr int BYTES = o_F + 64;
 static_assert(BYTES <= 160 * 1024, "LDS budget of one workgroup");
-static_assert(o_A % 16 == 0 && o_N % 16 == 0 && o_T % 16 == 0 && o_hT % 16 == 0 &&
-                  o_R % 16 == 0 && o_Gt % 16 == 0,
+static_assert(o_V % 16 == 0 && o_RAW % 16 == 0 && o_G % 16 == 0 && o_AQ % 16 == 0 && o_TT % 16 == 0 &&
+                  o_A % 16 == 0 && o_D % 16 == 0 && o_DT % 16 == 0 && o_F % 16 == 0,
               "alignment");
 
+// Gate arrays, per token r of a chunk: GA_G the cumulative log2 gate G_r;
+// GA_B beta_r; GA_BG beta_r 2^{G_r}; GA_TAIL 2^{G_C - G_r}; GA_OUT
+// scale 2^{G_r}; GA_ROW 2^{G_r - G_b}, b the first token of r's 16-token
+// block; GA_COL + I - 1 (I = 1, 2, 3): 2^{G_16I - G_r}; GA_END 2^{G_C} (every
+// entry).  Off-diagonal 16x16 blocks take 2^{G_i - G_j} as
+// GA_ROW[i] * GA_COL[I][j]: both factors lie in [0, 1].
+enum { GA_G = 0, GA_B, GA_BG, GA_TAIL, GA_OUT, GA_ROW, GA_COL, GA_END = GA_COL + 3 };
+static_assert(GA_END + 1 == NGA, "gate arrays");
+
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef Mma<bf16> M;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mma32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
-__device__ __forceinline__ bf16x4 to_bf4(f32x4 v) {
-    return __builtin_bit_cast(bf16x4, u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])});
+__device__ __forceinline__ f32x4 mma16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a),
+                                                     __builtin_bit_cast(bf16x4, b), c, 0, 0, 0);
 }
-// 16x16x16 A operand of a 16x16 block at `p` (row-major): lane 16g+m holds
-// X[m][4g..4g+3]
-__device__ __forceinline__ bf16x4 frag_a16(const float* p, int ld, int lane) {
-    const float4 x = *reinterpret_cast<const float4*>(p + (lane & 15) * ld + 4 * (lane >> 4));
-    return to_bf4(f32x4{x.x, x.y, x.z, x.w});
+__device__ __forceinline__ u32x2 pk4(f32x4 v) {
+    return u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
-__device__ __forceinline__ bf16x4 frag_a16(const bf16* p, int ld, int lane) {
-    return *reinterpret_cast<const bf16x4*>(p + (lane & 15) * ld + 4 * (lane >> 4));
+__device__ __forceinline__ u32x2 pk4(float4 v) {
+    return u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
 }
-// 16x16x16 B operand of a 16x16 block at `p` (row-major): lane 16g+n holds
-// X[4g..4g+3][n]
-__device__ __forceinline__ bf16x4 frag_b16(const float* p, int ld, int lane) {
-    const float* q = p + 4 * (lane >> 4) * ld + (lane & 15);
-    return to_bf4(f32x4{q[0], q[ld], q[2 * ld], q[3 * ld]});
+// two accumulator tiles (rows 4g..4g+3 of each) as one 16x16x32 operand
+__device__ __forceinline__ u32x4 pk8(f32x4 lo, f32x4 hi) {
+    return u32x4{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[0], hi[1]),
+                 pack_bf16x2(hi[2], hi[3])};
 }
-// the same 4 x 16 slice of a row-major bf16 block with one transposing read
-// (lane j of each 16-lane group addresses row 4g + j/4, columns 4(j%4)..+3)
-__device__ __forceinline__ bf16x4 tr_b16(const bf16* p, int ld, int lane) {
-    const int g = lane >> 4, j = lane & 15;
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4*)(p + (4 * g + (j >> 2)) * ld + 4 * (j & 3)));
-    return __builtin_bit_cast(bf16x4, v);
+__device__ __forceinline__ u32x4 cat(u32x2 lo, u32x2 hi) { return u32x4{lo[0], lo[1], hi[0], hi[1]}; }
+__device__ __forceinline__ f32x4 unpk4(u32x2 w) {
+    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                 __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
 }
-// an accumulator tile used as the next 16x16x16 B operand (same layout)
-__device__ __forceinline__ bf16x4 acc_b16(f32x4 v) { return to_bf4(v); }
-// store a 16x16 accumulator tile into a row-major fp32 block
-__device__ __forceinline__ void store_blk(float* p, int ld, int lane, f32x4 v) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) p[(4 * (lane >> 4) + e) * ld + (lane & 15)] = v[e];
+// Transposing read of a 16x16 bf16 block: lane j of 16-lane group g passes the
+// address of its row 4g + j/4, columns 4(j%4)..+3, and lane 16g+n receives
+// X[4g..4g+3][n].
+__device__ __forceinline__ u32x2 tr_read(const void* p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p));
 }
-// the same wave reads back what it wrote to LDS
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only: leave vector-memory loads in flight
-    __builtin_amdgcn_wave_barrier();
-}
-// 16x16x32 A operand of rows of T (fp32, row-major): lane 16g+m holds
-// T[m][k0+8g..k0+8g+7]
-__device__ __forceinline__ M::frag frag_t(const float* trow, int k0, int lane) {
-    const int c0 = k0 + 8 * (lane >> 4);
-    const float4 x0 = *reinterpret_cast<const float4*>(trow + c0);
-    const float4 x1 = *reinterpret_cast<const float4*>(trow + c0 + 4);
-    const u32x4 w{pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w), pack_bf16x2(x1.x, x1.y),
-                  pack_bf16x2(x1.z, x1.w)};
-    return __builtin_bit_cast(bf16x8, w);
-}
+__device__ __forceinline__ u32x4 ld16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x2 ld8(const char* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ float4 ldf4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
-// Inclusive prefix sum over the 64 lanes with DPP moves (row shifts inside
-// each 16-lane row, then the row-15 and row-31 broadcasts across rows): no
-// LDS traffic, unlike a shuffle-based scan.  Lanes whose source is outside
-// the row, or whose row is masked off, add 0.
+__device__ __forceinline__ int kq_sw(int r) { return (2 * r) & 14; }
+// byte offset of 16-byte group `grp` of row r of a K/Q slot
+__device__ __forceinline__ int kq_off(int r, int grp) { return r * 256 + ((grp ^ kq_sw(r)) << 4); }
+
+// Inclusive prefix sum over the 64 lanes with DPP row shifts and row
+// broadcasts (no LDS traffic).
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float add_dpp(float v) {
     return v + __int_as_float(
                    __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
 }
-__device__ __forceinline__ float wave_scan_dpp(float x) {
+__device__ __forceinline__ float wave_scan(float x) {
     x = add_dpp<0x111, 0xf>(x);   // row_shr:1
     x = add_dpp<0x112, 0xf>(x);   // row_shr:2
     x = add_dpp<0x114, 0xf>(x);   // row_shr:4
@@ -165,648 +175,611 @@ __device__ __forceinline__ float wave_scan_dpp(float x) {
     x = add_dpp<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
     return x;
 }
+__device__ __forceinline__ float lane_of(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
 
-// Chunk inputs held in registers between their load and their LDS store.
-struct Stage {
-    u32x4 k[2], q[2];
-    u32x2 v;
-    float g, b;
-};
+// Signals between waves: a release store after the data it covers, an
+// acquire poll before the data is read.  The poll gives up after a bounded
+// number of tries (a schedule error then shows as wrong results, never as a
+// wave that does not finish).
+typedef __attribute__((address_space(3))) int lds_int;
+__device__ __forceinline__ void signal(lds_int* f, int v) {
+    __hip_atomic_store(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void wait_for(lds_int* f, int v) {
+    for (int it = 0; it < (1 << 16); ++it) {
+        if (__hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= v) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+// Workgroup barrier that waits for this wave's LDS traffic only (loads into
+// LDS stay in flight across it; they are covered by signals).
+__device__ __forceinline__ void wg_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+}
+// buffer loads with the LDS destination: lane l's 16 (or 4) bytes land at
+// lds + 16 l (4 l); offsets at or past `bytes` read as zero
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ void to_lds16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void to_lds4(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, off, 0, 0, 0);
+}
+// the same wave reads back what it wrote to LDS
+__device__ __forceinline__ void own_lds_sync() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
+    __builtin_amdgcn_wave_barrier();
+}
 
 struct Ctx {
+    char* sm;
     const bf16 *q, *k, *v;
     const float *beta, *g;
     int64_t H, h, t0, len;
-    int v0, nch, tid, lane, wave;
+    int v0, nch, lane, wave;
     float scale;
-    char* smem;
 
-    __device__ __forceinline__ bf16* sK(int c) const {
-        return reinterpret_cast<bf16*>(smem + o_K + SZ_KQ * (c % 3));
+    // slot accessors take chunk indices >= 0
+    __device__ __forceinline__ char* sK(int c) const { return sm + o_K + SZ_KQ * (c % 3); }
+    __device__ __forceinline__ char* sQ(int c) const { return sm + o_Q + SZ_KQ * (c % 3); }
+    __device__ __forceinline__ char* sV(int c) const { return sm + o_V + SZ_V * (c % 3); }
+    __device__ __forceinline__ char* sRaw(int c) const { return sm + o_RAW + SZ_RAW * (c & 1); }
+    __device__ __forceinline__ float* gate(int c, int a) const {
+        return reinterpret_cast<float*>(sm + o_G + SZ_G * (c % 3)) + a * C;
     }
-    __device__ __forceinline__ bf16* sQ() const { return reinterpret_cast<bf16*>(smem + o_Q); }
-    __device__ __forceinline__ bf16* sV() const { return reinterpret_cast<bf16*>(smem + o_V); }
-    // off-diagonal blocks of A: row i (16 <= i < 64) at row i - 16, column j < 48
-    __device__ __forceinline__ bf16* sA() const { return reinterpret_cast<bf16*>(smem + o_A); }
-    __device__ __forceinline__ float* sN() const { return reinterpret_cast<float*>(smem + o_N); }
-    __device__ __forceinline__ float* sT(int c) const {
-        return reinterpret_cast<float*>(smem + o_T + SZ_T * (c & 1));
+    __device__ __forceinline__ char* sAQ(int c) const { return sm + o_AQ + SZ_AQ * (c & 1); }
+    __device__ __forceinline__ char* sTT() const { return sm + o_TT; }
+    __device__ __forceinline__ char* sA(int c) const { return sm + o_A + SZ_A * (c & 1); }
+    __device__ __forceinline__ float* sD(int b) const {
+        return reinterpret_cast<float*>(sm + o_D + SZ_DB * b);
     }
-    __device__ __forceinline__ bf16* shT() const { return reinterpret_cast<bf16*>(smem + o_hT); }
-    __device__ __forceinline__ bf16* sR() const { return reinterpret_cast<bf16*>(smem + o_R); }
-    __device__ __forceinline__ bf16* sVn() const { return reinterpret_cast<bf16*>(smem + o_Vn); }
-    __device__ __forceinline__ bf16* sVt() const { return reinterpret_cast<bf16*>(smem + o_Vt); }
-    __device__ __forceinline__ float* gate(int c, int which) const {
-        return reinterpret_cast<float*>(smem + o_Gt) + ((c % 3) * NGA + which) * C;
-    }
+    __device__ __forceinline__ char* sDT(int b) const { return sm + o_DT + SZ_DT * b; }
+    __device__ __forceinline__ lds_int* tflag() const { return (lds_int*)(sm + o_F); }
+    __device__ __forceinline__ lds_int* dflag() const { return (lds_int*)(sm + o_F) + 1; }
+    __device__ __forceinline__ lds_int* lflag() const { return (lds_int*)(sm + o_F) + 5; }
+
     __device__ __forceinline__ bool valid(int c) const { return c >= 0 && c < nch; }
     __device__ __forceinline__ int rows(int c) const {
         return (int)min((int64_t)C, len - (int64_t)c * C);
     }
-
-    // ---- loads into registers.  Chunk indices are clamped into [0, nch) so
-    // that every wave issues the same loads every iteration: the compiler can
-    // then count them and wait only for the ones a store needs, not for the
-    // loads issued for later iterations.  (Loads of clamped indices land in
-    // slots no live chunk uses.)
     __device__ __forceinline__ int clampc(int c) const { return min(max(c, 0), nch - 1); }
     // byte offset of row r (clamped to the chunk's last row) from the chunk's
-    // first row, plus a column offset; rows are H*D elements apart
-    __device__ __forceinline__ uint32_t roff(int c, int r, int D, int colbytes) const {
-        return (uint32_t)min(r, rows(c) - 1) * (uint32_t)(H * D * 2) + (uint32_t)colbytes;
+    // first row; rows are H*D elements of `eb` bytes apart
+    __device__ __forceinline__ uint32_t roff(int c, int r, int D, int eb) const {
+        return (uint32_t)min(r, rows(c) - 1) * (uint32_t)(H * D * eb);
     }
     template <typename P>
-    __device__ __forceinline__ const char* chunk_row0(const P* base, int c, int D) const {
+    __device__ __forceinline__ const char* row0(const P* base, int c, int D) const {
         return reinterpret_cast<const char*>(base + ((t0 + (int64_t)c * C) * H + h) * D);
-    }
-    // everything iteration j stores: K_{j+2} and gates_{j+2}, V_{j+1}, Q_{j+1}
-    // (the gates only in the wave that stores them: a load whose register is
-    // never read would make the compiler wait for it before reusing the register)
-    template <bool GATES>
-    __device__ __forceinline__ void load_for(Stage& s, int j) const {
-        const int cv = clampc(j + 1), ck = clampc(j + 2);
-        const char* vb = chunk_row0(v, cv, V) + v0 * 2;
-        const char* kb = chunk_row0(k, ck, K);
-        const char* qb = chunk_row0(q, cv, K);
-        s.v = *reinterpret_cast<const u32x2*>(vb + roff(cv, tid >> 3, V, (tid & 7) * 8));
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int i = tid + NT * p;
-            s.k[p] = *reinterpret_cast<const u32x4*>(kb + roff(ck, i >> 4, K, (i & 15) * 16));
-            s.q[p] = *reinterpret_cast<const u32x4*>(qb + roff(cv, i >> 4, K, (i & 15) * 16));
-        }
-        if constexpr (GATES) {
-            // rows past a ragged end re-read the last row; store_gates zeroes them
-            const uint32_t go = (uint32_t)min(lane, rows(ck) - 1) * (uint32_t)(H * 4);
-            s.g = *reinterpret_cast<const float*>(chunk_row0(g, ck, 1) + go);
-            s.b = *reinterpret_cast<const float*>(chunk_row0(beta, ck, 1) + go);
-        }
-    }
-
-    // ---- LDS stores of staged inputs
-    __device__ __forceinline__ void store_k(const Stage& s, int c) const {
-        bf16* d = sK(c);
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int i = tid + NT * p;
-            *reinterpret_cast<u32x4*>(d + (i >> 4) * LDK + (i & 15) * 8) = s.k[p];
-        }
-    }
-    __device__ __forceinline__ void store_q(const Stage& s) const {
-        bf16* d = sQ();
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int i = tid + NT * p;
-            *reinterpret_cast<u32x4*>(d + (i >> 4) * LDK + (i & 15) * 8) = s.q[p];
-        }
-    }
-    __device__ __forceinline__ void store_v(const Stage& s) const {
-        *reinterpret_cast<u32x2*>(sV() + (tid >> 3) * LDVS + (tid & 7) * 4) = s.v;
-    }
-    // cumulative log2 gate and the per-row factors derived from it (one wave,
-    // lane = row; rows past the chunk end carry g = 0 and beta = 0)
-    __device__ __forceinline__ void store_gates(const Stage& s, int c) const {
-        const bool in = lane < rows(c);
-        const float G = wave_scan_dpp(in ? s.g * LOG2E : 0.f);
-        const float bt = in ? s.b : 0.f;
-        const float Gc = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), C - 1));
-        const float gam = exp2_hw(G);
-        gate(c, G_LOG)[lane] = G;
-        gate(c, G_BETA)[lane] = bt;
-        gate(c, G_OUT)[lane] = scale * gam;
-        gate(c, G_TAIL)[lane] = exp2_hw(fminf(Gc - G, 0.f));
-        gate(c, G_GAM)[lane] = gam;
-        gate(c, G_END)[lane] = exp2_hw(Gc);
-        // G at the first token of each 16-token block
-        float Gs[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I)
-            Gs[I] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), 16 * I));
-        const int bl = lane >> 4;
-        const float Gb = bl == 0 ? Gs[0] : bl == 1 ? Gs[1] : bl == 2 ? Gs[2] : Gs[3];
-        gate(c, G_ROW)[lane] = exp2_hw(fminf(G - Gb, 0.f));
-#pragma unroll
-        for (int I = 1; I < 4; ++I)
-            gate(c, G_COL + I - 1)[lane] = exp2_hw(fminf(Gs[I] - G, 0.f));
     }
 };
 
-// ---------------------------------------------------------------- intra parts
-// S^T tile (J, I) = X_J Y_I^T over the full key dimension (X, Y row blocks of
-// K or Q): lane 16g+n holds S[16I + n][16J + 4g + e]
-__device__ __forceinline__ f32x4 kk_t(const bf16* a_rows, const bf16* b_rows, int lane) {
-    f32x4 acc = zero4();
-    const bf16* ar = a_rows + (lane & 15) * LDK;
-    const bf16* br = b_rows + (lane & 15) * LDK;
-    M::frag fa[K / 32], fb[K / 32];
+// index of the causal 16x16x32 Aqk / T fragment (t, p), p <= t/2
+__device__ __forceinline__ constexpr int frag_ix(int t, int p) { return t < 2 ? t : 2 * t - 2 + p; }
+// index of the off-diagonal A block (I, J), J < I
+__device__ __forceinline__ constexpr int ab_ix(int I, int J) { return I * (I - 1) / 2 + J; }
+
+// ---------------------------------------------------------------- wave 6: loads and gates
+__device__ __forceinline__ void role_load(const Ctx& x) {
+    const int lane = x.lane;
+    const uint32_t skq = (uint32_t)(x.H * K * 2), sv = (uint32_t)(x.H * V * 2);
+    const uint32_t sg = (uint32_t)(x.H * 4);
+    // source offsets inside a chunk: K/Q load s fills rows 4s..4s+3 (lane l:
+    // row 4s + l/16, LDS group l%16), V load s rows 16s..16s+15 (lane l: row
+    // 16s + l/4, LDS group l%4)
+    uint32_t okq[16], ov[4];
 #pragma unroll
-    for (int s = 0; s < K / 32; ++s) {
-        fa[s] = M::load(ar + 32 * s, lane);
-        fb[s] = M::load(br + 32 * s, lane);
+    for (int s = 0; s < 16; ++s) {
+        const int r = 4 * s + (lane >> 4);
+        okq[s] = (uint32_t)r * skq + 16u * (uint32_t)((lane & 15) ^ kq_sw(r));
     }
 #pragma unroll
-    for (int s = 0; s < K / 32; ++s) acc = M::mma(fa[s], fb[s], acc);
-    return acc;
-}
-
-// off-diagonal block (I, J), I > J, of A: beta_i 2^{G_i - G_j} k_i.k_j -> sA (bf16)
-__device__ __forceinline__ void a_offdiag(const Ctx& x, int c, int I, int J) {
-    const bf16* kk = x.sK(c);
-    const int i = 16 * I + (x.lane & 15), j0 = 16 * J + 4 * (x.lane >> 4);
-    const float bi = x.gate(c, G_BETA)[i], rw = x.gate(c, G_ROW)[i];
-    const float4 cj = *reinterpret_cast<const float4*>(x.gate(c, G_COL + I - 1) + j0);
-    const f32x4 s = kk_t(kk + 16 * J * LDK, kk + 16 * I * LDK, x.lane);
-    const float ri = bi * rw;
-    store4(x.sA() + (i - 16) * LDA + j0,
-           f32x4{ri * cj.x * s[0], ri * cj.y * s[1], ri * cj.z * s[2], ri * cj.w * s[3]});
-}
-
-// diagonal block b of A (strictly lower), transposed into sN[b]: sN[b][r][m] = A[16b+m][16b+r]
-__device__ __forceinline__ void a_diag(const Ctx& x, int c, int b) {
-    const bf16* kb = x.sK(c) + 16 * b * LDK + (x.lane & 15) * LDK;
-    M::frag f[K / 32];
+    for (int s = 0; s < 4; ++s) {
+        const int r = 16 * s + (lane >> 2);
+        ov[s] = (uint32_t)r * sv + (uint32_t)x.v0 * 2 + 16u * (uint32_t)((lane & 3) ^ (2 * ((r >> 2) & 1)));
+    }
+    const uint32_t lg = (uint32_t)lane * sg;
+    // g and beta of chunk c into raw slot c (rows past a ragged end read as 0)
+    auto load_raw = [&](int c) __attribute__((always_inline)) {
+        const int cc = x.clampc(c);
+        const uint32_t nb = (uint32_t)x.rows(cc) * sg;
+        to_lds4(rsrc(x.row0(x.g, cc, 1), nb), x.sRaw(c), lg);
+        to_lds4(rsrc(x.row0(x.beta, cc, 1), nb), x.sRaw(c) + C * 4, lg);
+    };
+    load_raw(0);
+    for (int j = -2; j < x.nch; ++j) {
+        // everything started an iteration ago has landed: K, Q, V of chunk j+1
+        // (signalled to the product waves) and g, beta of chunk j+2
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        signal(x.lflag(), j + 2);
+        // gate arrays of chunk j+2, read from the next iteration on
+        const int c2 = j + 2;
+        if (x.valid(c2)) {
+            const float* raw = reinterpret_cast<const float*>(x.sRaw(c2));
+            const float G = wave_scan(raw[lane] * LOG2E);
+            const float bt = raw[C + lane];
+            const float Gc = lane_of(G, C - 1);
+            const float gam = exp2_hw(G);
+            x.gate(c2, GA_G)[lane] = G;
+            x.gate(c2, GA_B)[lane] = bt;
+            x.gate(c2, GA_BG)[lane] = bt * gam;
+            x.gate(c2, GA_TAIL)[lane] = exp2_hw(fminf(Gc - G, 0.f));
+            x.gate(c2, GA_OUT)[lane] = x.scale * gam;
+            float Gs[4];
 #pragma unroll
-    for (int k0 = 0; k0 < K / 32; ++k0) f[k0] = M::load(kb + 32 * k0, x.lane);
-    // lane 16g+n: S[16b + 4g + e][16b + n], i.e. A row m = 4g+e, column r = n
-    const float* G = x.gate(c, G_LOG) + 16 * b;
-    const float* B = x.gate(c, G_BETA) + 16 * b;
-    const int r = x.lane & 15, m0 = 4 * (x.lane >> 4);
-    const float gr = G[r];
-    const float4 gm4 = *reinterpret_cast<const float4*>(G + m0);
-    const float4 bm4 = *reinterpret_cast<const float4*>(B + m0);
-    f32x4 s = zero4();
+            for (int I = 0; I < 4; ++I) Gs[I] = lane_of(G, 16 * I);
+            const int bl = lane >> 4;
+            const float Gb = bl == 0 ? Gs[0] : bl == 1 ? Gs[1] : bl == 2 ? Gs[2] : Gs[3];
+            x.gate(c2, GA_ROW)[lane] = exp2_hw(fminf(G - Gb, 0.f));
 #pragma unroll
-    for (int k0 = 0; k0 < K / 32; ++k0) s = M::mma(f[k0], f[k0], s);
-    const float gm[4] = {gm4.x, gm4.y, gm4.z, gm4.w}, bm[4] = {bm4.x, bm4.y, bm4.z, bm4.w};
-    float4 o;
-    float* op = &o.x;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-        op[e] = r < m0 + e ? bm[e] * exp2_hw(fminf(gm[e] - gr, 0.f)) * s[e] : 0.f;
-    *reinterpret_cast<float4*>(x.sN() + b * NBS + r * LDN + m0) = o;
-}
-
-// forward substitution of the four 16x16 diagonal blocks of I + A (one wave;
-// lane 16b+c computes column c of (I + N_b)^{-1}), written into the diagonal
-// blocks of T.  Column sweep: after step r, x_r is final and later rows have
-// subtracted N[m][r] x_r.  Rows of N^T are read LA steps ahead; the compiler
-// barrier keeps it from hoisting every read (which would take ~240 VGPRs).
-__device__ __forceinline__ void diag_inverse(const Ctx& x, int c) {
-    constexpr int LA = 3;
-    const int b = x.lane >> 4, col = x.lane & 15;
-    const float* nb = x.sN() + b * NBS;
-    float xv[16];
-#pragma unroll
-    for (int m = 0; m < 16; ++m) xv[m] = (m == col) ? 1.f : 0.f;
-    float4 buf[LA + 1][4];
-#pragma unroll
-    for (int r = 0; r < LA; ++r)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-            buf[r][q4] = *reinterpret_cast<const float4*>(nb + r * LDN + 4 * q4);
-#pragma unroll
-    for (int r = 0; r < 15; ++r) {
-        if (r + LA < 15) {
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
-                buf[(r + LA) % (LA + 1)][q4] =
-                    *reinterpret_cast<const float4*>(nb + (r + LA) * LDN + 4 * q4);
+            for (int I = 1; I < 4; ++I)
+                x.gate(c2, GA_COL + I - 1)[lane] = exp2_hw(fminf(Gs[I] - G, 0.f));
+            x.gate(c2, GA_END)[lane] = exp2_hw(Gc);
         }
-        const float* cl = reinterpret_cast<const float*>(buf[r % (LA + 1)]);
+        // start the loads of K, Q, V of chunk j+2 and g, beta of chunk j+3 (a
+        // clamped duplicate past the end: its slot is free either way)
+        const int ck = x.clampc(c2);
+        const uint32_t nr = (uint32_t)x.rows(ck);
+        const __amdgpu_buffer_rsrc_t rk = rsrc(x.row0(x.k, ck, K), nr * skq);
+        const __amdgpu_buffer_rsrc_t rq = rsrc(x.row0(x.q, ck, K), nr * skq);
+        const __amdgpu_buffer_rsrc_t rv = rsrc(x.row0(x.v, ck, V), nr * sv);
 #pragma unroll
-        for (int m = r + 1; m < 16; ++m) xv[m] -= cl[m] * xv[r];
-        __asm__ volatile("" ::: "memory");
+        for (int s = 0; s < 16; ++s) {
+            to_lds16(rk, x.sK(c2) + 1024 * s, okq[s]);
+            to_lds16(rq, x.sQ(c2) + 1024 * s, okq[s]);
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) to_lds16(rv, x.sV(c2) + 1024 * s, ov[s]);
+        load_raw(j + 3);
+        wg_barrier();
     }
-    float* tb = x.sT(c) + 16 * b * LDT + 16 * b + col;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) tb[m * LDT] = xv[m];
+    // no load may land in LDS after the workgroup has ended
+    __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-// Off-diagonal blocks of T from the diagonal ones (bf16 MFMA, fp32 results):
-// wave 0 writes T10, T20, T21; wave 1 writes T32, T30, T31 (and recomputes the
-// T10 it needs in registers).
-__device__ __forceinline__ void compose(const Ctx& x, int c, int which) {
-    float* T = x.sT(c);
-    const bf16* A = x.sA();
-    const int l = x.lane;
-    auto Tb = [&](int I, int J) { return T + 16 * I * LDT + 16 * J; };
-    auto Ab = [&](int I, int J) { return A + (16 * I - 16) * LDA + 16 * J; };
-    const bf16x4 t00b = frag_b16(Tb(0, 0), LDT, l), t11b = frag_b16(Tb(1, 1), LDT, l);
-    // T10 = -T11 (A10 T00)
-    const f32x4 x10 = mma16(frag_a16(Ab(1, 0), LDA, l), t00b, zero4());
-    const f32x4 t10 = mma16(frag_a16(Tb(1, 1), LDT, l), acc_b16(-x10), zero4());
-    const bf16x4 t10b = acc_b16(t10);
-    const bf16x4 a21 = frag_a16(Ab(2, 1), LDA, l);
-    // P20 = A20 T00 + A21 T10, P21 = A21 T11
-    f32x4 p20 = mma16(frag_a16(Ab(2, 0), LDA, l), t00b, zero4());
-    p20 = mma16(a21, t10b, p20);
-    const f32x4 p21 = mma16(a21, t11b, zero4());
-    if (which == 0) {
-        store_blk(Tb(1, 0), LDT, l, t10);
-        const bf16x4 t22a = frag_a16(Tb(2, 2), LDT, l);
-        store_blk(Tb(2, 0), LDT, l, mma16(t22a, acc_b16(-p20), zero4()));
-        store_blk(Tb(2, 1), LDT, l, mma16(t22a, acc_b16(-p21), zero4()));
-    } else {
-        // T32 = -T33 (A32 T22)
-        const f32x4 x32 = mma16(frag_a16(Ab(3, 2), LDA, l), frag_b16(Tb(2, 2), LDT, l), zero4());
-        const bf16x4 t33a = frag_a16(Tb(3, 3), LDT, l);
-        const f32x4 t32 = mma16(t33a, acc_b16(-x32), zero4());
-        store_blk(Tb(3, 2), LDT, l, t32);
-        const bf16x4 a31 = frag_a16(Ab(3, 1), LDA, l);
-        f32x4 p30 = mma16(frag_a16(Ab(3, 0), LDA, l), t00b, zero4());
-        p30 = mma16(a31, t10b, p30);
-        const f32x4 p31 = mma16(a31, t11b, zero4());
-        wave_lds_sync();
-        const bf16x4 t32a = frag_a16(Tb(3, 2), LDT, l);
-        // T3J = -(T32 P2J + T33 P3J)
-        f32x4 t30 = mma16(t32a, acc_b16(-p20), zero4());
-        t30 = mma16(t33a, acc_b16(-p30), t30);
-        f32x4 t31 = mma16(t32a, acc_b16(-p21), zero4());
-        t31 = mma16(t33a, acc_b16(-p31), t31);
-        store_blk(Tb(3, 0), LDT, l, t30);
-        store_blk(Tb(3, 1), LDT, l, t31);
+// ---------------------------------------------------------------- waves 3,4,5,7: masked products
+// Blocks (I, J) of chunk c: lane 16g+n of each result holds S[16I+n][16J+4g+e]
+// (row 16I+n, key column 16J+4g+e), with A = K_J rows and B = K_I or Q_I rows.
+
+// wave 3: A = beta_i 2^{G_i - G_j} k_i.k_j, the four diagonal blocks first
+// (signalled to the inverse), then the six below them
+__device__ __forceinline__ void role_keys(const Ctx& x) {
+    const int lane = x.lane, m = lane & 15, g = lane >> 4;
+    for (int j = -2; j < x.nch; ++j) {
+        const int c = j + 1;
+        if (x.valid(c)) {
+            wait_for(x.lflag(), c + 1);   // K, Q of chunk c have landed
+            const char* kb = x.sK(c);
+            u32x4 kf[4][4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) kf[I][kk] = ld16(kb + kq_off(16 * I + m, 4 * kk + g));
+            float Gi[4], bi[4];
+            float4 Gj[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                Gi[I] = x.gate(c, GA_G)[16 * I + m];
+                bi[I] = x.gate(c, GA_B)[16 * I + m];
+                Gj[I] = ldf4(x.gate(c, GA_G) + 16 * I + 4 * g);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 sd[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                sd[I] = zero4();
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) sd[I] = mma32(kf[I][kk], kf[I][kk], sd[I]);
+            }
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                float4 ad;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    (&ad.x)[e] = 4 * g + e < m ? bi[I] * exp2_hw(fminf(Gi[I] - (&Gj[I].x)[e], 0.f)) * sd[I][e]
+                                               : 0.f;
+                *reinterpret_cast<float4*>(x.sD(I) + m * LDD + 4 * g) = ad;
+            }
+            signal(x.dflag(), c + 1);
+            // off-diagonal blocks: decay ROW[i] COL_I[j]
+#pragma unroll
+            for (int I = 1; I < 4; ++I) {
+                const float bri = bi[I] * x.gate(c, GA_ROW)[16 * I + m];
+                const float* colI = x.gate(c, GA_COL + I - 1);
+#pragma unroll
+                for (int J = 0; J < I; ++J) {
+                    f32x4 s = zero4();
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) s = mma32(kf[J][kk], kf[I][kk], s);
+                    const float4 cj = ldf4(colI + 16 * J + 4 * g);
+                    f32x4 av;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) av[e] = bri * (&cj.x)[e] * s[e];
+                    *reinterpret_cast<u32x2*>(x.sA(c) + ab_ix(I, J) * SZ_AB + m * (LDAB * 2) + 8 * g) =
+                        pk4(av);
+                }
+            }
+        }
+        wg_barrier();
     }
+}
+
+// waves 7, 4, 5: Aqk = scale 2^{G_i - G_j} q_i.k_j (j <= i), as the state
+// pass's 16x16x32 operand fragments.  Set 0 takes the diagonal blocks and
+// (1,0), set 1 (2,0) and (2,1), set 2 (3,0), (3,1) and (3,2).
+template <int SET>
+__device__ __forceinline__ void role_queries(const Ctx& x) {
+    constexpr int NB = SET == 0 ? 5 : SET == 1 ? 2 : 3;
+    constexpr int BI[3][5] = {{0, 1, 2, 3, 1}, {2, 2, 0, 0, 0}, {3, 3, 3, 0, 0}};
+    constexpr int BJ[3][5] = {{0, 1, 2, 3, 0}, {0, 1, 0, 0, 0}, {0, 1, 2, 0, 0}};
+    const int lane = x.lane, m = lane & 15, g = lane >> 4;
+    for (int j = -2; j < x.nch; ++j) {
+        const int c = j + 1;
+        if (x.valid(c)) {
+            wait_for(x.lflag(), c + 1);   // K, Q of chunk c have landed
+            const char* kb = x.sK(c);
+            const char* qb = x.sQ(c);
+            u32x4 kf[4][4], qf[4][4];
+            bool needk[4] = {false, false, false, false}, needq[4] = {false, false, false, false};
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                needk[BJ[SET][b]] = true;
+                needq[BI[SET][b]] = true;
+            }
+#pragma unroll
+            for (int J = 0; J < 4; ++J)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    if (needk[J]) kf[J][kk] = ld16(kb + kq_off(16 * J + m, 4 * kk + g));
+                    if (needq[J]) qf[J][kk] = ld16(qb + kq_off(16 * J + m, 4 * kk + g));
+                }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int I = BI[SET][b], J = BJ[SET][b];
+                f32x4 s = zero4();
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) s = mma32(kf[J][kk], qf[I][kk], s);
+                f32x4 q;
+                if (J == I) {
+                    const float Gi = x.gate(c, GA_G)[16 * I + m];
+                    const float4 Gj = ldf4(x.gate(c, GA_G) + 16 * I + 4 * g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        q[e] = 4 * g + e <= m ? x.scale * exp2_hw(fminf(Gi - (&Gj.x)[e], 0.f)) * s[e] : 0.f;
+                } else {
+                    const float sri = x.scale * x.gate(c, GA_ROW)[16 * I + m];
+                    const float4 cj = ldf4(x.gate(c, GA_COL + I - 1) + 16 * J + 4 * g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) q[e] = sri * (&cj.x)[e] * s[e];
+                }
+                *reinterpret_cast<u32x2*>(x.sAQ(c) + frag_ix(I, J >> 1) * 1024 + lane * 16 +
+                                          8 * (J & 1)) = pk4(q);
+            }
+        }
+        wg_barrier();
+    }
+}
+
+// ---------------------------------------------------------------- wave 2: the inverse
+// T^T in LDS: row c holds column c of T (bf16, LDTT per row).
+// TT block (I, J) of T, from an accumulator tile holding T_IJ[4g+e][n]:
+__device__ __forceinline__ void put_tt(char* tt, int I, int J, int lane, f32x4 v) {
+    *reinterpret_cast<u32x2*>(tt + ((16 * J + (lane & 15)) * LDTT + 16 * I + 4 * (lane >> 4)) * 2) =
+        pk4(v);
+}
+// 16x16x16 A operand of T_bb (lane 16g+m: T_bb[m][4g..4g+3])
+__device__ __forceinline__ u32x2 tt_a(const char* tt, int b, int lane) {
+    const int g = lane >> 4, jl = lane & 15;
+    return tr_read(tt + ((16 * b + 4 * g + (jl >> 2)) * LDTT + 16 * b + 4 * (jl & 3)) * 2);
+}
+// 16x16x16 A operand of the off-diagonal A block (I, J)
+__device__ __forceinline__ u32x2 ab_a(const char* a, int I, int J, int lane) {
+    return ld8(a + ab_ix(I, J) * SZ_AB + (lane & 15) * (LDAB * 2) + 8 * (lane >> 4));
+}
+__device__ __forceinline__ u32x2 neg4(f32x4 v) { return pk4(-v); }
+
+// T_j from the diagonal-block inverses tbb (accumulator tiles) and the
+// off-diagonal A blocks
+__device__ __forceinline__ void compose(const Ctx& x, int j, const f32x4 (&tbb)[4]) {
+    const int lane = x.lane;
+    char* tt = x.sTT();
+#pragma unroll
+    for (int b = 0; b < 4; ++b) put_tt(tt, b, b, lane, tbb[b]);
+    const char* a = x.sA(j);
+    const u32x2 a10 = ab_a(a, 1, 0, lane), a20 = ab_a(a, 2, 0, lane), a21 = ab_a(a, 2, 1, lane);
+    const u32x2 a30 = ab_a(a, 3, 0, lane), a31 = ab_a(a, 3, 1, lane), a32 = ab_a(a, 3, 2, lane);
+    const u32x2 t00 = pk4(tbb[0]), t11 = pk4(tbb[1]), t22 = pk4(tbb[2]);
+    // products that need only the diagonal inverses
+    const f32x4 y1 = mma16(a10, t00, zero4());     // A10 T00
+    const f32x4 x32 = mma16(a32, t22, zero4());    // A32 T22
+    const f32x4 y01 = mma16(a21, t11, zero4());    // A21 T11
+    const f32x4 y11 = mma16(a31, t11, zero4());    // A31 T11
+    f32x4 y00 = mma16(a20, t00, zero4());          // A20 T00 + ...
+    f32x4 y10 = mma16(a30, t00, zero4());          // A30 T00 + ...
+    own_lds_sync();                                // the diagonal blocks of T^T are in LDS
+    const u32x2 t11a = tt_a(tt, 1, lane), t22a = tt_a(tt, 2, lane), t33a = tt_a(tt, 3, lane);
+    const f32x4 t10 = mma16(t11a, neg4(y1), zero4());    // T10 = -T11 A10 T00
+    const f32x4 t32 = mma16(t33a, neg4(x32), zero4());   // T32 = -T33 A32 T22
+    const f32x4 t21 = mma16(t22a, neg4(y01), zero4());   // T21 = -T22 A21 T11
+    const u32x2 t10b = pk4(t10);
+    y00 = mma16(a21, t10b, y00);                         // A20 T00 + A21 T10
+    y10 = mma16(a31, t10b, y10);                         // A30 T00 + A31 T10
+    const f32x4 w11 = mma16(a32, pk4(t21), y11);         // A31 T11 + A32 T21
+    const f32x4 t20 = mma16(t22a, neg4(y00), zero4());   // T20 = -T22 (A20 T00 + A21 T10)
+    const f32x4 t31 = mma16(t33a, neg4(w11), zero4());   // T31 = -T33 (A31 T11 + A32 T21)
+    const f32x4 w10 = mma16(a32, pk4(t20), y10);         // A30 T00 + A31 T10 + A32 T20
+    const f32x4 t30 = mma16(t33a, neg4(w10), zero4());   // T30
+    put_tt(tt, 1, 0, lane, t10);
+    put_tt(tt, 3, 2, lane, t32);
+    put_tt(tt, 2, 1, lane, t21);
+    put_tt(tt, 2, 0, lane, t20);
+    put_tt(tt, 3, 1, lane, t31);
+    put_tt(tt, 3, 0, lane, t30);
+    signal(x.tflag(), j + 1);
+}
+
+// Inverses of the four 16x16 diagonal blocks of I + A of chunk c, as
+// accumulator tiles (lane 16g+n: T_bb[4g+e][n]).
+__device__ __forceinline__ void diag_inverse(const Ctx& x, f32x4 (&tbb)[4]) {
+    const int lane = x.lane;
+    // forward substitution of the 8x8 block s of 16x16 block b, column c
+    {
+        const int b = lane >> 4, s = (lane >> 3) & 1, col = lane & 7;
+        const float* d = x.sD(b) + 8 * s * LDD + 8 * s;
+        float4 rw[8][2];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) {
+            rw[i][0] = ldf4(d + i * LDD);
+            rw[i][1] = ldf4(d + i * LDD + 4);
+        }
+        float xv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float acc = i == col ? 1.f : 0.f;
+#pragma unroll
+            for (int mm = 0; mm < i; ++mm)
+                acc -= (mm < 4 ? (&rw[i][0].x)[mm] : (&rw[i][1].x)[mm - 4]) * xv[mm];
+            xv[i] = acc;
+        }
+        // row (8s + col) of D_b^T: column 8s+col of D_b, zero outside block s
+        const u32x2 w0{pack_bf16x2(xv[0], xv[1]), pack_bf16x2(xv[2], xv[3])};
+        const u32x2 w1{pack_bf16x2(xv[4], xv[5]), pack_bf16x2(xv[6], xv[7])};
+        const u32x2 z{0u, 0u};
+        char* dt = x.sDT(b) + (8 * s + col) * (LDDT * 2);
+        *reinterpret_cast<u32x2*>(dt) = s ? z : w0;
+        *reinterpret_cast<u32x2*>(dt + 8) = s ? z : w1;
+        *reinterpret_cast<u32x2*>(dt + 16) = s ? w0 : z;
+        *reinterpret_cast<u32x2*>(dt + 24) = s ? w1 : z;
+    }
+    own_lds_sync();
+    // T_bb = D - D (X D), X = the lower-left 8x8 block of A_bb
+    const int g = lane >> 4, mrow = lane & 15;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const float4 xr = ldf4(x.sD(b) + mrow * LDD + 4 * g);
+        const bool live = mrow >= 8 && g < 2;
+        const u32x2 xa = live ? pk4(xr) : u32x2{0u, 0u};
+        const u32x2 db = ld8(x.sDT(b) + mrow * (LDDT * 2) + 8 * g);   // D[4g+e][n], n = lane & 15
+        const f32x4 y = mma16(xa, db, zero4());
+        const u32x2 da = tr_read(x.sDT(b) + (4 * g + (mrow >> 2)) * (LDDT * 2) + 8 * (mrow & 3));
+        tbb[b] = mma16(da, neg4(y), unpk4(db));
+    }
+}
+
+__device__ __forceinline__ void role_inverse(const Ctx& x) {
+    f32x4 tbb[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) tbb[b] = zero4();
+    for (int j = -2; j < x.nch; ++j) {
+        if (x.valid(j)) compose(x, j, tbb);
+        const int c = j + 1;
+        if (x.valid(c)) {
+            wait_for(x.dflag(), c + 1);   // the diagonal blocks of A
+            diag_inverse(x, tbb);
+        }
+        wg_barrier();
+    }
+}
+
+// ---------------------------------------------------------------- waves 0,1: the state pass
+__device__ __forceinline__ void role_state(const Ctx& x, const FusedLaunch& a, int64_t n) {
+    __builtin_amdgcn_s_setprio(2);
+    const int lane = x.lane, m = lane & 15, g = lane >> 4;
+    const int n0 = 16 * x.wave;
+    const int64_t hbase = (n * a.H + x.h) * (int64_t)(K * V) + x.v0 + n0 + m;
+    // row 4g+e of state tile r is key channel 32(r/2) + 8g + 4(r%2) + e
+    auto chan = [&](int r, int e) { return 32 * (r >> 1) + 8 * g + 4 * (r & 1) + e; };
+    f32x4 hacc[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            hacc[r][e] = a.h0 ? a.h0[hbase + (int64_t)chan(r, e) * V] : 0.f;
+    bf16* o = static_cast<bf16*>(a.o);
+
+    for (int j = -2; j < x.nch; ++j) {
+        if (x.valid(j)) {
+            const char* kb = x.sK(j);
+            const char* qb = x.sQ(j);
+            // h as 16x16x32 operands: key channels 32kk+8g..+7 of column m
+            u32x4 hb[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) hb[kk] = pk8(hacc[2 * kk], hacc[2 * kk + 1]);
+            // The reads of each step are issued in batches ahead of the
+            // products that use them (scheduling barriers keep the compiler
+            // from sinking them next to their uses, which would expose one LDS
+            // latency per product).
+            // ---- X = K h (token rows 16t+4g+e, column m) and (Q h)^T (column
+            // 4g+e, token 16t+m)
+            u32x4 kf[4][4], qf[4][4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    kf[kk][t] = ld16(kb + kq_off(16 * t + m, 4 * kk + g));
+                    qf[kk][t] = ld16(qb + kq_off(16 * t + m, 4 * kk + g));
+                }
+                if (kk == 1) __builtin_amdgcn_sched_barrier(0);
+            }
+            f32x4 xa[4], oa[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) xa[t] = oa[t] = zero4();
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    xa[t] = mma32(kf[kk][t], hb[kk], xa[t]);
+                    oa[t] = mma32(hb[kk], qf[kk][t], oa[t]);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            // V rows 16t+4g+e, column n0+m (the accumulator's layout), and the
+            // gates of R
+            const float* gb = x.gate(j, GA_B);
+            const float* gbg = x.gate(j, GA_BG);
+            u32x2 vr[4];
+            float4 b4[4], bg4[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int r = 16 * t + 4 * g + (m >> 2);
+                const int q = (2 * x.wave + ((m & 3) >> 1)) ^ (2 * ((r >> 2) & 1));
+                vr[t] = tr_read(x.sV(j) + r * (VT * 2) + 16 * q + 8 * (m & 1));
+                b4[t] = ldf4(gb + 16 * t + 4 * g);
+                bg4[t] = ldf4(gbg + 16 * t + 4 * g);
+            }
+#pragma unroll
+            for (int kk = 2; kk < 4; ++kk)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    xa[t] = mma32(kf[kk][t], hb[kk], xa[t]);
+                    oa[t] = mma32(hb[kk], qf[kk][t], oa[t]);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- R = beta V - beta gamma X
+            u32x4 rb[2];
+            f32x4 rt[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const f32x4 vv = unpk4(vr[t]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rt[t][e] = (&b4[t].x)[e] * vv[e] - (&bg4[t].x)[e] * xa[t][e];
+            }
+#pragma unroll
+            for (int p = 0; p < 2; ++p) rb[p] = pk8(rt[2 * p], rt[2 * p + 1]);
+            // ---- V_new = T R; the later steps' operands are read meanwhile
+            wait_for(x.tflag(), j + 1);
+            const char* tt = x.sTT();
+            u32x4 tf[4][2];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    if (2 * p > t) continue;
+                    const char* base = tt + ((32 * p + 4 * g + (m >> 2)) * LDTT + 16 * t + 4 * (m & 3)) * 2;
+                    tf[t][p] = cat(tr_read(base), tr_read(base + 16 * LDTT * 2));
+                }
+            const float* gtl = x.gate(j, GA_TAIL);
+            const float* gout = x.gate(j, GA_OUT);
+            const char* aq = x.sAQ(j);
+            float4 tl[4];
+            float so[4];
+            u32x4 af[4][2];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                tl[t] = ldf4(gtl + 16 * t + 4 * g);
+                so[t] = gout[16 * t + m];
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+                    if (2 * p <= t) af[t][p] = ld16(aq + frag_ix(t, p) * 1024 + lane * 16);
+            }
+            const float gC = x.gate(j, GA_END)[0];
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 va[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                va[t] = zero4();
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+                    if (2 * p <= t) va[t] = mma32(tf[t][p], rb[p], va[t]);
+            }
+            // decayed V_new for the state, V_new for the output
+            u32x4 vsb[2], vnb[2];
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                f32x4 s0, s1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    s0[e] = (&tl[2 * p].x)[e] * va[2 * p][e];
+                    s1[e] = (&tl[2 * p + 1].x)[e] * va[2 * p + 1][e];
+                }
+                vsb[p] = pk8(s0, s1);
+                vnb[p] = pk8(va[2 * p], va[2 * p + 1]);
+            }
+            // ---- h <- gamma_C h + K^T (decayed V_new): K^T operand by
+            // transposing reads of token rows {32p+4g.., 32p+16+4g..}; lane j of
+            // a 16-lane group addresses channels 32(r/2) + 8(j%4) + 4(r%2)..+3,
+            // i.e. the channels of state tile r's rows 4(j%4)..+3
+            u32x4 kt[8][2];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const int r0 = 32 * p + 4 * g + (m >> 2), r1 = r0 + 16;
+                    const int grp = 4 * (r >> 1) + (m & 3), hf = 8 * (r & 1);
+                    kt[r][p] = cat(tr_read(kb + kq_off(r0, grp) + hf), tr_read(kb + kq_off(r1, grp) + hf));
+                }
+                if (r == 3) __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                hacc[r] *= gC;
+#pragma unroll
+                for (int p = 0; p < 2; ++p) hacc[r] = mma32(kt[r][p], vsb[p], hacc[r]);
+                if (r == 3) __builtin_amdgcn_sched_barrier(0);
+            }
+            // ---- O^T = diag(scale gamma) (Q h)^T + V_new^T Aqk^T, stored from registers
+            const int ntok = x.rows(j);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                oa[t] *= so[t];
+#pragma unroll
+                for (int p = 0; p < 2; ++p)
+                    if (2 * p <= t) oa[t] = mma32(vnb[p], af[t][p], oa[t]);
+                const int tok = 16 * t + m;
+                if (tok < ntok)
+                    *reinterpret_cast<u32x2*>(
+                        o + ((x.t0 + (int64_t)j * C + tok) * x.H + x.h) * V + x.v0 + n0 + 4 * g) =
+                        pk4(oa[t]);
+            }
+        }
+        wg_barrier();
+    }
+    if (a.ht)
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a.ht[hbase + (int64_t)chan(r, e) * V] = hacc[r][e];
 }
 
 // ---------------------------------------------------------------- the kernel
-// off-diagonal K K^T blocks (I, J) of waves 5, 6, 7 (two each) in the second phase
-__constant__ int AO_I[6] = {3, 3, 3, 2, 2, 1};
-__constant__ int AO_J[6] = {0, 1, 2, 0, 1, 0};
-
-// Everything a wave of role R (0: V waves, 1: O waves, 2: H waves) does; the
-// role is a compile-time constant so that each loop holds only its role's
-// values in registers, and the wave index inside the role is a runtime value
-// so that the kernel's code (three loops) stays well inside the instruction
-// cache.  Every wave executes the same barriers in the same order.
-template <int R, int SUB>
-__device__ __forceinline__ void run_role(Ctx& x, const FusedLaunch& a, int64_t n) {
-    constexpr bool VW = R == 0, OW = R == 1, HW = R == 2;
-    constexpr bool GW = VW && SUB == 0;   // the wave that computes the gate arrays
-    // wave index: a compile-time constant for the V and O waves (whose work
-    // differs by block), a runtime value for the four H waves
-    const int W = HW ? x.wave : (VW ? SUB : 2 + SUB);
-    const int lane = x.lane;
-    f32x4 hacc[2][CT];   // H waves: h rows 32p.., fp32
-    if constexpr (HW) {
-        const int p = W - 4;
-        const float* h0 = a.h0 ? a.h0 + (n * a.H + x.h) * (int64_t)(K * V) : nullptr;
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    hacc[r][ct][e] = h0 ? h0[(16 * (2 * p + r) + acc_row(lane, e)) * V + x.v0 +
-                                             16 * ct + acc_col(lane)]
-                                        : 0.f;
-                store_acc_t(x.shT() + 16 * ct * LDH + 16 * (2 * p + r), LDH, lane, hacc[r][ct]);
-            }
-    }
-
-    Stage st[PD];
-    if (x.nch > 0) {
-#pragma unroll
-    for (int s = 0; s < PD; ++s) x.load_for<GW>(st[s], s - 2);
-
-    auto iteration = [&](Stage& s, int j) __attribute__((always_inline)) {
-        const int c1 = j + 1, c2 = j + 2;
-        const bool scan = j >= 0, in1 = x.valid(c1);
-        f32x4 oacc[CT][2];   // O waves: O^T of their token blocks
-        f32x4 sq[2][4];      // O waves: off-diagonal causal blocks (J, I), J < I, fp32
-        f32x4 sqd[2] = {zero4(), zero4()};   // O waves: diagonal causal blocks
-        bf16x4 aq[2][4];     // O waves: causal Q K^T blocks (J, I), 16x16x16 B operands
-        // wave 2 owns token blocks 0 and 3, wave 3 blocks 1 and 2: both then
-        // have five causal Q K^T blocks
-        constexpr int ib0 = SUB == 1 ? 1 : 0, ib1 = SUB == 1 ? 2 : 3;
-        // ================= P1
-        // Staged inputs are stored unconditionally (clamped duplicates for
-        // chunks past the end land in slots no live chunk uses), so that no
-        // staged register is left with a load in flight on some path.
-        x.store_k(s, c2);
-        if constexpr (VW) {
-            if (scan) {
-                // R = diag(beta) (V - diag(gamma) K h) for token rows 32m..32m+31
-                constexpr int m = SUB;
-                const bf16* kk = x.sK(j);
-                const float* bt = x.gate(j, G_BETA);
-                const float* gm = x.gate(j, G_GAM);
-                float4 b4[2], g4[2];
-                bf16x4 vv[2][CT];
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int r0 = 32 * m + 16 * t;
-                    b4[t] = *reinterpret_cast<const float4*>(bt + r0 + 4 * (lane >> 4));
-                    g4[t] = *reinterpret_cast<const float4*>(gm + r0 + 4 * (lane >> 4));
-                    // V rows r0+4g+e, column 16ct+n: the accumulator's layout
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct)
-                        vv[t][ct] = tr_b16(x.sV() + r0 * LDVS + 16 * ct, LDVS, lane);
-                }
-                f32x4 acc[2][CT];
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) acc[t][ct] = zero4();
-#pragma unroll
-                for (int sg = 0; sg < K / 32; ++sg) {
-                    const M::frag a0 = M::load(kk + (32 * m + (lane & 15)) * LDK + 32 * sg, lane);
-                    const M::frag a1 =
-                        M::load(kk + (32 * m + 16 + (lane & 15)) * LDK + 32 * sg, lane);
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) {
-                        const M::frag bh =
-                            M::load(x.shT() + (16 * ct + (lane & 15)) * LDH + 32 * sg, lane);
-                        acc[0][ct] = M::mma(a0, bh, acc[0][ct]);
-                        acc[1][ct] = M::mma(a1, bh, acc[1][ct]);
-                    }
-                }
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int r0 = 32 * m + 16 * t;
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) {
-                        const bf16x4 v4 = vv[t][ct];
-                        const f32x4 r{b4[t].x * ((float)v4[0] - g4[t].x * acc[t][ct][0]),
-                                      b4[t].y * ((float)v4[1] - g4[t].y * acc[t][ct][1]),
-                                      b4[t].z * ((float)v4[2] - g4[t].z * acc[t][ct][2]),
-                                      b4[t].w * ((float)v4[3] - g4[t].w * acc[t][ct][3])};
-                        store_acc_t(x.sR() + 16 * ct * LDVN + r0, LDVN, lane, r);
-                    }
-                }
-            }
-        }
-        if constexpr (OW) {
-            if (scan) {
-                // O^T = h^T Q^T for the two token blocks, and the
-                // off-diagonal causal blocks S^T(J, I) = K_J Q_I^T, J < I
-                const bf16* kk = x.sK(j);
-                const float* og = x.gate(j, G_OUT);
-                const float s0 = og[16 * ib0 + (lane & 15)], s1 = og[16 * ib1 + (lane & 15)];
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) oacc[ct][0] = oacc[ct][1] = zero4();
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int J = 0; J < 4; ++J) sq[t][J] = zero4();
-#pragma unroll
-                for (int sg = 0; sg < K / 32; ++sg) {
-                    const M::frag b0 =
-                        M::load(x.sQ() + (16 * ib0 + (lane & 15)) * LDK + 32 * sg, lane);
-                    const M::frag b1 =
-                        M::load(x.sQ() + (16 * ib1 + (lane & 15)) * LDK + 32 * sg, lane);
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) {
-                        const M::frag ah =
-                            M::load(x.shT() + (16 * ct + (lane & 15)) * LDH + 32 * sg, lane);
-                        oacc[ct][0] = M::mma(ah, b0, oacc[ct][0]);
-                        oacc[ct][1] = M::mma(ah, b1, oacc[ct][1]);
-                    }
-#pragma unroll
-                    for (int J = 0; J < 3; ++J) {
-                        if (J >= ib0 && J >= ib1) continue;
-                        const M::frag kf =
-                            M::load(kk + (16 * J + (lane & 15)) * LDK + 32 * sg, lane);
-                        if (J < ib0) sq[0][J] = M::mma(kf, b0, sq[0][J]);
-                        if (J < ib1) sq[1][J] = M::mma(kf, b1, sq[1][J]);
-                    }
-                }
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    oacc[ct][0] *= s0;
-                    oacc[ct][1] *= s1;
-                }
-            }
-        }
-        if constexpr (HW) {
-            if (scan) {
-                const float dec = x.gate(j, G_END)[0];
-#pragma unroll
-                for (int r = 0; r < 2; ++r)
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) hacc[r][ct] *= dec;
-            }
-            if (in1) a_diag(x, c1, W - 4);
-        }
-        __syncthreads();
-        // ================= P2
-        x.store_v(s);
-        if constexpr (VW) {
-            if (scan) {
-                // V_new = T R for token rows 32m..32m+31 (T is zero above the
-                // diagonal, so k-steps past the rows' own block add nothing)
-                constexpr int m = SUB;
-                const float* T = x.sT(j);
-                const float* tail = x.gate(j, G_TAIL);
-                float4 f4[2];
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    f4[t] = *reinterpret_cast<const float4*>(tail + 32 * m + 16 * t + 4 * (lane >> 4));
-                f32x4 vn[2][CT];
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) vn[t][ct] = zero4();
-#pragma unroll
-                for (int sg = 0; sg < 2; ++sg) {
-                    if (sg > m) break;
-                    M::frag bt[CT];
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct)
-                        bt[ct] = M::load(x.sR() + (16 * ct + (lane & 15)) * LDVN + 32 * sg, lane);
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const M::frag at =
-                            frag_t(T + (32 * m + 16 * t + (lane & 15)) * LDT, 32 * sg, lane);
-#pragma unroll
-                        for (int ct = 0; ct < CT; ++ct) vn[t][ct] = M::mma(at, bt[ct], vn[t][ct]);
-                    }
-                }
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int r0 = 32 * m + 16 * t;
-                    const float4 f = f4[t];
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) {
-                        const f32x4 v = vn[t][ct];
-                        store_acc_t(x.sVn() + 16 * ct * LDVN + r0, LDVN, lane, v);
-                        store_acc_t(x.sVt() + 16 * ct * LDVN + r0, LDVN, lane,
-                                    f32x4{f.x * v[0], f.y * v[1], f.z * v[2], f.w * v[3]});
-                    }
-                }
-            }
-        }
-        if constexpr (OW) {
-            if (scan) {
-                // the diagonal causal blocks S^T(I, I) = K_I Q_I^T
-                const bf16* kk = x.sK(j);
-#pragma unroll
-                for (int sg = 0; sg < K / 32; ++sg) {
-                    const M::frag b0 =
-                        M::load(x.sQ() + (16 * ib0 + (lane & 15)) * LDK + 32 * sg, lane);
-                    const M::frag b1 =
-                        M::load(x.sQ() + (16 * ib1 + (lane & 15)) * LDK + 32 * sg, lane);
-                    const M::frag k0 =
-                        M::load(kk + (16 * ib0 + (lane & 15)) * LDK + 32 * sg, lane);
-                    const M::frag k1 =
-                        M::load(kk + (16 * ib1 + (lane & 15)) * LDK + 32 * sg, lane);
-                    sqd[0] = M::mma(k0, b0, sqd[0]);
-                    sqd[1] = M::mma(k1, b1, sqd[1]);
-                }
-                // every gate value the masks need, read before any is used
-                const float* G = x.gate(j, G_LOG);
-                const float* ROW = x.gate(j, G_ROW);
-                const int g4 = 4 * (lane >> 4);
-                float gi[2], si[2];
-                float4 gd[2], cj[2][3];
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int I = t ? ib1 : ib0, i = 16 * I + (lane & 15);
-                    gi[t] = G[i];
-                    si[t] = x.scale * ROW[i];
-                    gd[t] = *reinterpret_cast<const float4*>(G + 16 * I + g4);
-#pragma unroll
-                    for (int J = 0; J < I; ++J)
-                        cj[t][J] =
-                            *reinterpret_cast<const float4*>(x.gate(j, G_COL + I - 1) + 16 * J + g4);
-                }
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int I = t ? ib1 : ib0, i = 16 * I + (lane & 15);
-                    // lane 16g+n of tile (J, I) holds S[i = 16I+n][j = 16J+4g+e];
-                    // off-diagonal blocks use the factored decay, the diagonal
-                    // block the direct one and the causal mask
-#pragma unroll
-                    for (int J = 0; J < I; ++J)
-                        aq[t][J] = to_bf4(f32x4{si[t] * cj[t][J].x * sq[t][J][0],
-                                                si[t] * cj[t][J].y * sq[t][J][1],
-                                                si[t] * cj[t][J].z * sq[t][J][2],
-                                                si[t] * cj[t][J].w * sq[t][J][3]});
-                    const float gdv[4] = {gd[t].x, gd[t].y, gd[t].z, gd[t].w};
-                    f32x4 av;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int jj = 16 * I + g4 + e;
-                        av[e] = jj <= i ? x.scale * exp2_hw(fminf(gi[t] - gdv[e], 0.f)) * sqd[t][e]
-                                        : 0.f;
-                    }
-                    aq[t][I] = to_bf4(av);
-                }
-            }
-        }
-        if constexpr (HW) {
-            if (in1) {
-                if (W == 4) {
-                    // on the SIMD it shares with wave 0, whose second phase is light
-                    diag_inverse(x, c1);
-                } else {
-                    // waves 5, 6, 7 take blocks (3,0) (3,1) | (3,2) (2,0) | (2,1) (1,0)
-                    const int q = W - 5;
-                    a_offdiag(x, c1, AO_I[2 * q], AO_J[2 * q]);
-                    a_offdiag(x, c1, AO_I[2 * q + 1], AO_J[2 * q + 1]);
-                }
-            }
-        }
-        __syncthreads();
-        // ================= P3
-        x.store_q(s);
-        // gates of chunk j+2 (first read in the next iteration's first phase)
-        if constexpr (GW) x.store_gates(s, c2);
-        x.load_for<GW>(s, j + PD);
-        if constexpr (VW) {
-            if (in1) compose(x, c1, SUB);
-        }
-        if constexpr (OW) {
-            if (scan) {
-                // + V_new^T Aqk^T over the causal blocks J <= I (16x16x16:
-                // lane 16g+m reads V_new^T[16ct+m][16J+4g..+3])
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int I = t ? ib1 : ib0;
-#pragma unroll
-                    for (int J = 0; J < 4; ++J) {
-                        if (J > I) continue;
-#pragma unroll
-                        for (int ct = 0; ct < CT; ++ct)
-                            oacc[ct][t] = mma16(
-                                frag_a16(x.sVn() + 16 * ct * LDVN + 16 * J, LDVN, lane), aq[t][J],
-                                oacc[ct][t]);
-                    }
-                }
-                const int ntok = x.rows(j);
-                const int64_t tt0 = x.t0 + (int64_t)j * C;
-                bf16* o = static_cast<bf16*>(a.o);
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    const int tk = 16 * (t ? ib1 : ib0) + acc_col(lane);
-                    if (tk < ntok) {
-#pragma unroll
-                        for (int ct = 0; ct < CT; ++ct)
-                            store4(o + ((tt0 + tk) * a.H + x.h) * V + x.v0 + 16 * ct +
-                                       4 * (lane >> 4),
-                                   oacc[ct][t]);
-                    }
-                }
-            }
-        }
-        if constexpr (HW) {
-            if (scan) {
-                const int p = W - 4;
-                const bf16* kk = x.sK(j);
-#pragma unroll
-                for (int sg = 0; sg < C / 32; ++sg) {
-                    const M::frag a0 = M::load_t(kk + 32 * sg * LDK + 32 * p, LDK, lane);
-                    const M::frag a1 = M::load_t(kk + 32 * sg * LDK + 32 * p + 16, LDK, lane);
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct) {
-                        const M::frag bv =
-                            M::load(x.sVt() + (16 * ct + (lane & 15)) * LDVN + 32 * sg, lane);
-                        hacc[0][ct] = M::mma(a0, bv, hacc[0][ct]);
-                        hacc[1][ct] = M::mma(a1, bv, hacc[1][ct]);
-                    }
-                }
-#pragma unroll
-                for (int r = 0; r < 2; ++r)
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct)
-                        store_acc_t(x.shT() + 16 * ct * LDH + 16 * (2 * p + r), LDH, lane,
-                                    hacc[r][ct]);
-            }
-        }
-        __syncthreads();
-    };
-
-    int j = -2;
-    for (; j + PD <= x.nch; j += PD) {
-        iteration(st[0], j);
-        iteration(st[1], j + 1);
-    }
-    if (j < x.nch) iteration(st[0], j);
-    }
-
-    if constexpr (HW) {
-        if (a.ht) {
-            const int p = W - 4;
-            float* ht = a.ht + (n * a.H + x.h) * (int64_t)(K * V);
-#pragma unroll
-            for (int r = 0; r < 2; ++r)
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        ht[(16 * (2 * p + r) + acc_row(lane, e)) * V + x.v0 + 16 * ct +
-                           acc_col(lane)] = hacc[r][ct][e];
-        }
-    }
-}
-
 __global__ __launch_bounds__(NT) void fused_kernel(FusedLaunch a) {
     __shared__ __attribute__((aligned(16))) char smem[BYTES];
     const int64_t bid = blockIdx.x;
+    // the four value slices of a (sequence, head) run on one XCD (workgroups
+    // are dealt to the eight XCDs round-robin), where they share K, Q in L2
     const int vt = (int)((bid >> 3) % NVT);
     const int64_t chain = (bid & 7) + 8 * ((bid >> 3) / NVT);
     if (chain >= a.N * a.H) return;
 
     Ctx x;
+    x.sm = smem;
     x.q = static_cast<const bf16*>(a.q);
     x.k = static_cast<const bf16*>(a.k);
     x.v = static_cast<const bf16*>(a.v);
@@ -816,11 +789,9 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedLaunch a) {
     const int64_t n = chain / a.H;
     x.h = chain - n * a.H;
     x.v0 = vt * VT;
-    x.tid = threadIdx.x;
     x.lane = threadIdx.x & 63;
     x.wave = wave_id();
     x.scale = a.scale;
-    x.smem = smem;
     if (a.seqs) {
         const int4 s = a.seqs[n];
         x.t0 = s.x;
@@ -831,15 +802,26 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedLaunch a) {
     }
     x.nch = (int)((x.len + C - 1) / C);
 
-    // zero both T slots: their upper blocks are read as zeros
-    for (int i = x.tid; i < 2 * C * LDT; i += NT) x.sT(0)[i] = 0.f;
+    // Aqk fragments and T^T start zero: their blocks above the diagonal are
+    // read as zeros and never written
+    for (int i = threadIdx.x; i < (2 * SZ_AQ + SZ_TT) / 16; i += NT)
+        reinterpret_cast<u32x4*>(smem + o_AQ)[i] = u32x4{0u, 0u, 0u, 0u};
+    if (threadIdx.x < 16) reinterpret_cast<int*>(smem + o_F)[threadIdx.x] = 0;
+    __syncthreads();
 
+    // waves w and w+4 share a SIMD: the two state waves (60 MFMAs per chunk
+    // each) pair with the lightest product waves (8 and 12 MFMAs), the
+    // inverse (latency-bound) with the loads, the two heaviest product waves
+    // (40 and 20) with each other
     switch (x.wave) {
-        case 0: run_role<0, 0>(x, a, n); break;
-        case 1: run_role<0, 1>(x, a, n); break;
-        case 2: run_role<1, 0>(x, a, n); break;
-        case 3: run_role<1, 1>(x, a, n); break;
-        default: run_role<2, 0>(x, a, n); break;
+        case 0:
+        case 1: role_state(x, a, n); break;
+        case 2: role_inverse(x); break;
+        case 6: role_load(x); break;
+        case 3: role_keys(x); break;
+        case 7: role_queries<0>(x); break;
+        case 4: role_queries<1>(x); break;
+        default: role_queries<2>(x); break;
     }
 }
 

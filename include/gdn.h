@@ -100,10 +100,15 @@ const char *gdn_status_str(gdn_status s);
 const char *gdn_last_error(void);
 
 /*
- * Bytes of device workspace gdn_chunk_fwd and gdn_chunk_intra need for the
- * shape *d (written to *bytes).  It holds the per-chunk products of the
- * intra-chunk stage and the chunk table, laid out as gdn_workspace_layout_of
- * reports.  A descriptor with num_seqs > 0 describes packed input.
+ * Bytes of device workspace gdn_chunk_fwd needs for the shape *d (written to
+ * *bytes).  A descriptor with num_seqs > 0 describes packed input.
+ *   - bf16 inputs, scalar gate, K = V = 128, chunk 64 (the single-pass
+ *     kernel): only the per-sequence table of packed input, 16 bytes per
+ *     sequence rounded up to 256 (256 bytes without cu_seqlens).
+ *   - every other shape (two stages): the per-chunk products of the
+ *     intra-chunk stage and the chunk table, gdn_workspace_layout_of().total.
+ * gdn_chunk_intra and gdn_chunk_scan always need
+ * gdn_workspace_layout_of().total.
  */
 gdn_status gdn_chunk_fwd_workspace(const gdn_fwd_desc *d, size_t *bytes);
 
@@ -112,6 +117,12 @@ gdn_status gdn_chunk_fwd_workspace(const gdn_fwd_desc *d, size_t *bytes);
  * chunk equations 11-12; "阅读笔记：DeltaNet 在 FLA 中的代码实现笔记",
  * forward Steps 1-5; signature of its chunk_delta_rule_fwd: q, k, v, beta,
  * scale, initial_state, output_final_state, cu_seqlens).
+ *
+ * bf16 inputs with the scalar gate at K = V = 128, chunk 64 run as one
+ * kernel that builds each chunk's intra-chunk products on chip while it
+ * carries the state; every other shape runs gdn_chunk_intra then
+ * gdn_chunk_scan.  The two routes compute the same quantities in a
+ * different order: they agree to rounding, not bit for bit.
  *
  *   q, k   [B, T, H, K]   qkv_dtype
  *   v      [B, T, H, V]   qkv_dtype
@@ -141,7 +152,8 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_desc *d,
                          void *stream);
 
 /*
- * Where gdn_chunk_fwd / gdn_chunk_intra keep each intermediate inside the
+ * Where gdn_chunk_intra / gdn_chunk_scan (and the two-stage route of
+ * gdn_chunk_fwd) keep each intermediate inside the
  * workspace (byte offsets from its start).  Every per-chunk array is indexed
  * [head][chunk][...] with max_chunks chunk slots per head; chunk j of
  * sequence b is slot b * ceil(T / C) + j without cu_seqlens, and slot
@@ -180,16 +192,18 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_desc *d,
  */
 typedef struct gdn_workspace_layout {
     size_t gcum, w, u, qs, ks, aqk, ainv, chunks, seqs;
-    size_t total;        /* == gdn_chunk_fwd_workspace() */
+    size_t total;        /* bytes the two stages need */
     int64_t max_chunks;  /* chunk slots per head (mc) */
 } gdn_workspace_layout;
 
 gdn_status gdn_workspace_layout_of(const gdn_fwd_desc *d, gdn_workspace_layout *out);
 
 /*
- * The two stages of gdn_chunk_fwd, callable one at a time (gdn_chunk_fwd is
- * exactly gdn_chunk_intra(flags = 0) followed by gdn_chunk_scan on the same
- * workspace and stream).
+ * The two stages of the forward pass, callable one at a time, for every
+ * supported shape (for shapes without the single-pass kernel gdn_chunk_fwd
+ * is exactly gdn_chunk_intra(flags = 0) followed by gdn_chunk_scan on the
+ * same workspace and stream).  The workspace holds
+ * gdn_workspace_layout_of().total bytes.
  *
  * gdn_chunk_intra: the intra-chunk stage ("TileLang 实战" §2.2.4, §2.3 and
  * §4.1-4.2; "阅读笔记：DeltaNet 在 FLA 中的代码实现笔记", forward Steps 1-3):
