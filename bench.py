@@ -124,18 +124,19 @@ def bench_prefill(args, gdn):
 
     for _ in range(args.warmup):
         step()
-    # timed region: wall clock around the K steps, and a HIP event pair around
-    # each step's kernel on the stream it is launched on
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    # timed region: wall clock around the K steps, and a HIP event pair on the
+    # stream the kernel is launched on (one kernel per step, launched back to
+    # back: the average launch duration is the pair's time over K)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev[0].record()
     for i in range(args.steps):
-        ev[2 * i].record()
         step()
-        ev[2 * i + 1].record()
+    ev[1].record()
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / args.steps
-    t_fused = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)) / args.steps / 1e3
+    t_fused = ev[0].elapsed_time(ev[1]) / args.steps / 1e3
     log("prefill step %.1f us (fused kernel %.1f us)" % (dt * 1e6, t_fused * 1e6))
 
     # the two-stage path on the same inputs, for comparison: per-kernel
@@ -225,8 +226,9 @@ def cpu_baseline(d, min_s=10.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    # the GPU clock settles during the first ~100 launches
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
