@@ -754,9 +754,10 @@ __device__ __forceinline__ void role_state(const Ctx& x, const FusedLaunch& a, i
                     if (2 * p <= t) oa[t] = mma32(vnb[p], af[t][p], oa[t]);
                 const int tok = 16 * t + m;
                 if (tok < ntok)
-                    *reinterpret_cast<u32x2*>(
-                        o + ((x.t0 + (int64_t)j * C + tok) * x.H + x.h) * V + x.v0 + n0 + 4 * g) =
-                        pk4(oa[t]);
+                    // non-temporal: o is not read again here
+                    __builtin_nontemporal_store(
+                        pk4(oa[t]), reinterpret_cast<u32x2*>(o + ((x.t0 + (int64_t)j * C + tok) * x.H +
+                                                                  x.h) * V + x.v0 + n0 + 4 * g));
             }
         }
         wg_barrier();
