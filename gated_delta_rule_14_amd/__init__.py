@@ -5,9 +5,9 @@ include/gdn.h (libgdn.so, built by `python -m gated_delta_rule_14_amd.build`);
 this package is a thin binding over it.  Loading is lazy: importing works
 without a GPU, every compute call needs the built library and a device.
 """
-from ._binding import (ABI_VERSION, EXPORTS, LIB_PATH, FwdDesc, GdnError, StepDesc,  # noqa: F401
-                       WorkspaceLayout, chunk_fwd, chunk_intra, chunk_scan, fwd_desc, load,
-                       recurrent_step, workspace_bytes, workspace_layout)
+from ._binding import (ABI_VERSION, EXPORTS, LIB_PATH, Activation, FwdDesc, GdnError,  # noqa: F401
+                       StepDesc, WorkspaceLayout, activation, chunk_fwd, chunk_intra, chunk_scan,
+                       fwd_desc, load, recurrent_step, workspace_bytes, workspace_layout)
 
-__all__ = ["load", "chunk_fwd", "chunk_intra", "chunk_scan", "recurrent_step", "workspace_bytes",
+__all__ = ["load", "activation", "chunk_fwd", "chunk_intra", "chunk_scan", "recurrent_step", "workspace_bytes",
            "workspace_layout", "fwd_desc", "GdnError", "LIB_PATH", "EXPORTS"]

@@ -13,7 +13,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_SCALAR, GATE_PER_KEY = 0, 1
@@ -22,8 +22,10 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE", 3: "GDN_ER
           7: "GDN_ERR_HIP"}
 EXPORTS = sorted(["gdn_abi_version", "gdn_status_str", "gdn_last_error",
                   "gdn_chunk_fwd_workspace", "gdn_chunk_fwd", "gdn_workspace_layout_of",
-                  "gdn_chunk_intra", "gdn_chunk_scan", "gdn_recurrent_step"])
+                  "gdn_chunk_intra", "gdn_chunk_scan", "gdn_recurrent_step",
+                  "gdn_chunk_fwd_act", "gdn_recurrent_step_act"])
 INTRA_STORE_AINV = 1
+ACT_GATE, ACT_BETA_SIGMOID, ACT_BETA_NEG_EIG = 1, 2, 4
 
 
 class FwdDesc(ctypes.Structure):
@@ -39,6 +41,10 @@ class StepDesc(ctypes.Structure):
                 ("key_dim", ctypes.c_int64), ("value_dim", ctypes.c_int64),
                 ("qkv_dtype", ctypes.c_int32), ("gate", ctypes.c_int32),
                 ("scale", ctypes.c_float)]
+
+
+class Activation(ctypes.Structure):
+    _fields_ = [("flags", ctypes.c_int32), ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p)]
 
 
 class WorkspaceLayout(ctypes.Structure):
@@ -84,6 +90,12 @@ def load(path: str = LIB_PATH):
     lib.gdn_chunk_scan.restype = S
     lib.gdn_recurrent_step.argtypes = [ctypes.POINTER(StepDesc), P, P, P, P, P, P, P, P]
     lib.gdn_recurrent_step.restype = S
+    lib.gdn_chunk_fwd_act.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(Activation), P, P, P,
+                                      P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.gdn_chunk_fwd_act.restype = S
+    lib.gdn_recurrent_step_act.argtypes = [ctypes.POINTER(StepDesc), ctypes.POINTER(Activation),
+                                           P, P, P, P, P, P, P, P]
+    lib.gdn_recurrent_step_act.restype = S
     v = lib.gdn_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError("libgdn.so ABI %d, binding expects %d" % (v, ABI_VERSION))
@@ -144,6 +156,32 @@ def workspace_bytes(desc: FwdDesc) -> int:
     return n.value
 
 
+def activation(gate_logits=False, beta_sigmoid=False, neg_eig=False, A_log=None, dt_bias=None):
+    """The optional in-kernel input activation (gdn_activation): with
+    gate_logits, g holds raw logits a and log alpha = -exp(A_log) softplus(a +
+    dt_bias) (A_log [H], dt_bias [H] or [H, K] float32 device tensors); with
+    beta_sigmoid, beta holds raw logits b and beta = sigmoid(b), times 2 with
+    neg_eig (beta in (0, 2))."""
+    flags = (ACT_GATE if gate_logits else 0) | (ACT_BETA_SIGMOID if beta_sigmoid else 0) | \
+        (ACT_BETA_NEG_EIG if neg_eig else 0)
+    if gate_logits:
+        _need(A_log, "A_log", torch.float32)
+        _need(dt_bias, "dt_bias", torch.float32)
+    act = Activation(flags, _ptr(A_log) if gate_logits else None,
+                     _ptr(dt_bias) if gate_logits else None)
+    act._keep = (A_log, dt_bias)   # the tensors outlive the struct's use
+    return act
+
+
+def _act_shapes(act, H, K, gate):
+    if act is None or not (act.flags & ACT_GATE):
+        return
+    A_log, dt_bias = act._keep
+    want_dt = (H, K) if gate == "per_key" else (H,)
+    if tuple(A_log.shape) != (H,) or tuple(dt_bias.shape) != want_dt:
+        raise ValueError("A_log must have shape %s and dt_bias %s" % ((H,), want_dt))
+
+
 def _inputs(q, k, v, beta, g, cu_seqlens, gate):
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, name, q.dtype)
@@ -160,8 +198,9 @@ def _inputs(q, k, v, beta, g, cu_seqlens, gate):
 
 def chunk_fwd(q, k, v, beta, g, scale=None, h0=None, cu_seqlens=None, chunk=64,
               gate="scalar", output_final_state=True, workspace=None, o=None, ht=None,
-              stream=None):
-    """gdn_chunk_fwd: returns (o, ht) (ht is None unless output_final_state)."""
+              stream=None, act=None):
+    """gdn_chunk_fwd (gdn_chunk_fwd_act when act, from activation(), is given):
+    returns (o, ht) (ht is None unless output_final_state)."""
     lib = load()
     _inputs(q, k, v, beta, g, cu_seqlens, gate)
     N = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
@@ -178,10 +217,14 @@ def chunk_fwd(q, k, v, beta, g, scale=None, h0=None, cu_seqlens=None, chunk=64,
     nbytes = workspace_bytes(desc)
     if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    _check(lib.gdn_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
-                             _ptr(h0), _ptr(cu_seqlens), _ptr(o),
-                             _ptr(ht) if output_final_state else None, _ptr(workspace),
-                             workspace.numel() * workspace.element_size(), _stream(stream)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0), _ptr(cu_seqlens), _ptr(o),
+            _ptr(ht) if output_final_state else None, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    if act is None:
+        _check(lib.gdn_chunk_fwd(ctypes.byref(desc), *args))
+    else:
+        _act_shapes(act, H, K, gate)
+        _check(lib.gdn_chunk_fwd_act(ctypes.byref(desc), ctypes.byref(act), *args))
     return o, (ht if output_final_state else None)
 
 
@@ -264,9 +307,11 @@ def chunk_scan(desc, workspace, o, h0=None, ht=None, cu_seqlens=None, stream=Non
     return o, ht
 
 
-def recurrent_step(q, k, v, beta, g, state, scale=None, gate="scalar", o=None, stream=None):
-    """gdn_recurrent_step: one token for N sequences; state updated in place.
-    q, k [N, H, K]; v [N, H, V]; beta [N, H]; g [N, H] or [N, H, K]."""
+def recurrent_step(q, k, v, beta, g, state, scale=None, gate="scalar", o=None, stream=None,
+                   act=None):
+    """gdn_recurrent_step (gdn_recurrent_step_act with act): one token for N
+    sequences; state updated in place.  q, k [N, H, K]; v [N, H, V];
+    beta [N, H]; g [N, H] or [N, H, K]."""
     lib = load()
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, name, q.dtype)
@@ -285,6 +330,10 @@ def recurrent_step(q, k, v, beta, g, state, scale=None, gate="scalar", o=None, s
     desc = StepDesc(N, H, K, V, _dtype_code(q),
                     GATE_PER_KEY if gate == "per_key" else GATE_SCALAR,
                     float(K ** -0.5 if scale is None else scale))
-    _check(lib.gdn_recurrent_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
-                                  _ptr(g), _ptr(state), _ptr(o), _stream(stream)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(state), _ptr(o), _stream(stream))
+    if act is None:
+        _check(lib.gdn_recurrent_step(ctypes.byref(desc), *args))
+    else:
+        _act_shapes(act, H, K, gate)
+        _check(lib.gdn_recurrent_step_act(ctypes.byref(desc), ctypes.byref(act), *args))
     return o

@@ -122,9 +122,34 @@ struct Prepared {
     gdn::ChunkWs ws;
 };
 
+static_assert(GDN_ACT_GATE == gdn::ACT_GATE && GDN_ACT_BETA_SIGMOID == gdn::ACT_BETA_SIGMOID &&
+                  GDN_ACT_BETA_NEG_EIG == gdn::ACT_BETA_NEG_EIG,
+              "activation bits");
+
+// the optional input activation (NULL: g and beta are used as given)
+gdn_status check_act(const gdn_activation* act, gdn::Act* out) {
+    *out = gdn::Act{};
+    if (!act || act->flags == 0) return GDN_OK;
+    const int known = GDN_ACT_GATE | GDN_ACT_BETA_SIGMOID | GDN_ACT_BETA_NEG_EIG;
+    if (act->flags & ~known) return fail(GDN_ERR_UNSUPPORTED, "activation flags 0x%x", act->flags);
+    if ((act->flags & GDN_ACT_BETA_NEG_EIG) && !(act->flags & GDN_ACT_BETA_SIGMOID))
+        return fail(GDN_ERR_UNSUPPORTED, "GDN_ACT_BETA_NEG_EIG needs GDN_ACT_BETA_SIGMOID");
+    if (act->flags & GDN_ACT_GATE) {
+        if (!act->A_log || !act->dt_bias)
+            return fail(GDN_ERR_NULL_ARG, "GDN_ACT_GATE needs A_log and dt_bias");
+        if (!aligned4(act->A_log) || !aligned4(act->dt_bias))
+            return fail(GDN_ERR_MISALIGNED, "A_log and dt_bias need 4-byte alignment");
+    }
+    out->flags = act->flags;
+    out->A_log = act->A_log;
+    out->dt_bias = act->dt_bias;
+    return GDN_OK;
+}
+
 gdn_status prepare(const gdn_fwd_desc* d, const void* q, const void* k, const void* v,
                    const float* beta, const float* g, const int64_t* cu_seqlens, void* workspace,
-                   size_t workspace_bytes, bool want_ainv, hipStream_t stream, Prepared* P) {
+                   size_t workspace_bytes, bool want_ainv, hipStream_t stream, Prepared* P,
+                   const gdn::Act& act = gdn::Act{}) {
     const bool packed = cu_seqlens != nullptr;
     gdn_status s = check_desc(d, packed);
     if (s != GDN_OK) return s;
@@ -188,6 +213,7 @@ gdn_status prepare(const gdn_fwd_desc* d, const void* q, const void* k, const vo
         a.scale = d->scale;
         a.bf16 = d->qkv_dtype == GDN_DTYPE_BF16;
         a.per_key = d->gate == GDN_GATE_PER_KEY;
+        a.act = act;
         a.stream = stream;
         hipError_t e = gdn::launch_intra(a);
         if (e != hipSuccess) return hip_fail(e, "intra-chunk launch");
@@ -301,7 +327,7 @@ gdn_status gdn_chunk_scan(const gdn_fwd_desc* d, const float* h0, const int64_t*
 static gdn_status fused_fwd(const gdn_fwd_desc* d, const void* q, const void* k, const void* v,
                             const float* beta, const float* g, const float* h0,
                             const int64_t* cu_seqlens, void* o, float* ht, void* workspace,
-                            size_t workspace_bytes, hipStream_t st) {
+                            size_t workspace_bytes, hipStream_t st, const gdn::Act& act) {
     const bool packed = cu_seqlens != nullptr;
     if (!packed && d->num_seqs != 0)
         return fail(GDN_ERR_BAD_SHAPE, "num_seqs must be 0 without cu_seqlens");
@@ -336,6 +362,7 @@ static gdn_status fused_fwd(const gdn_fwd_desc* d, const void* q, const void* k,
     a.scale = d->scale;
     a.bf16 = true;
     a.per_key = false;
+    a.act = act;
     a.stream = st;
     if (packed) {
         gdn::TableLaunch t;
@@ -356,29 +383,43 @@ static gdn_status fused_fwd(const gdn_fwd_desc* d, const void* q, const void* k,
     return ok();
 }
 
-gdn_status gdn_chunk_fwd(const gdn_fwd_desc* d, const void* q, const void* k, const void* v,
-                         const float* beta, const float* g, const float* h0,
-                         const int64_t* cu_seqlens, void* o, float* ht, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+gdn_status gdn_chunk_fwd_act(const gdn_fwd_desc* d, const gdn_activation* act_in, const void* q,
+                             const void* k, const void* v, const float* beta, const float* g,
+                             const float* h0, const int64_t* cu_seqlens, void* o, float* ht,
+                             void* workspace, size_t workspace_bytes, void* stream) {
     const bool packed = cu_seqlens != nullptr;
     gdn_status s = check_desc(d, packed);
+    if (s != GDN_OK) return s;
+    gdn::Act act;
+    s = check_act(act_in, &act);
     if (s != GDN_OK) return s;
     if (!o) return fail(GDN_ERR_NULL_ARG, "o is NULL");
     if (!aligned16(o) || !aligned4(h0) || !aligned4(ht))
         return fail(GDN_ERR_MISALIGNED, "o needs 16-byte, h0 and ht 4-byte alignment");
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (fused_path(d)) return fused_fwd(d, q, k, v, beta, g, h0, cu_seqlens, o, ht, workspace,
-                                        workspace_bytes, st);
+                                        workspace_bytes, st, act);
     Prepared P;
-    s = prepare(d, q, k, v, beta, g, cu_seqlens, workspace, workspace_bytes, false, st, &P);
+    s = prepare(d, q, k, v, beta, g, cu_seqlens, workspace, workspace_bytes, false, st, &P, act);
     if (s != GDN_OK) return s;
     return scan(d, h0, cu_seqlens, o, ht, workspace, workspace_bytes, st);
 }
 
-gdn_status gdn_recurrent_step(const gdn_step_desc* d, const void* q, const void* k,
-                              const void* v, const float* beta, const float* g, float* state,
-                              void* o, void* stream) {
+gdn_status gdn_chunk_fwd(const gdn_fwd_desc* d, const void* q, const void* k, const void* v,
+                         const float* beta, const float* g, const float* h0,
+                         const int64_t* cu_seqlens, void* o, float* ht, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    return gdn_chunk_fwd_act(d, nullptr, q, k, v, beta, g, h0, cu_seqlens, o, ht, workspace,
+                             workspace_bytes, stream);
+}
+
+gdn_status gdn_recurrent_step_act(const gdn_step_desc* d, const gdn_activation* act_in,
+                                  const void* q, const void* k, const void* v, const float* beta,
+                                  const float* g, float* state, void* o, void* stream) {
     if (!d) return fail(GDN_ERR_NULL_ARG, "desc is NULL");
+    gdn::Act act;
+    gdn_status s = check_act(act_in, &act);
+    if (s != GDN_OK) return s;
     if (d->qkv_dtype != GDN_DTYPE_F32 && d->qkv_dtype != GDN_DTYPE_BF16)
         return fail(GDN_ERR_BAD_DTYPE, "qkv_dtype %d", d->qkv_dtype);
     if (d->gate != GDN_GATE_SCALAR && d->gate != GDN_GATE_PER_KEY)
@@ -414,10 +455,17 @@ gdn_status gdn_recurrent_step(const gdn_step_desc* d, const void* q, const void*
     a.V = (int)d->value_dim;
     a.bf16 = d->qkv_dtype == GDN_DTYPE_BF16;
     a.per_key = d->gate == GDN_GATE_PER_KEY;
+    a.act = act;
     a.stream = static_cast<hipStream_t>(stream);
     hipError_t e = gdn::launch_step(a);
     if (e != hipSuccess) return hip_fail(e, "step launch");
     return ok();
+}
+
+gdn_status gdn_recurrent_step(const gdn_step_desc* d, const void* q, const void* k,
+                              const void* v, const float* beta, const float* g, float* state,
+                              void* o, void* stream) {
+    return gdn_recurrent_step_act(d, nullptr, q, k, v, beta, g, state, o, stream);
 }
 
 }  // extern "C"

@@ -310,4 +310,16 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 constexpr float LOG2E = 1.4426950408889634f;
 
+// Input activations ("Gated Delta Network（GDN）" §3.1 eq. 5): the natural-log
+// gate -exp(A_log) softplus(a + dt_bias) from a raw gate logit a, and beta as
+// sigmoid(b) (times 2 for beta in (0, 2)) from a raw logit b.
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
+__device__ __forceinline__ float act_log_gate(float a, float A_log, float dt_bias) {
+    return -expf(A_log) * softplus_f(a + dt_bias);
+}
+__device__ __forceinline__ float act_beta(float b, bool neg_eig) {
+    const float s = 1.f / (1.f + expf(-b));
+    return neg_eig ? 2.f * s : s;
+}
+
 }  // namespace gdn

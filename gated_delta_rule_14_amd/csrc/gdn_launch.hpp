@@ -8,7 +8,18 @@
 
 namespace gdn {
 
+// In-kernel input activation (the same bits as GDN_ACT_* in gdn.h): the gate
+// and beta inputs hold raw logits ("Gated Delta Network（GDN）" §3.1 eq. 5,
+// §5 gate fusion).
+enum { ACT_GATE = 1, ACT_BETA_SIGMOID = 2, ACT_BETA_NEG_EIG = 4 };
+struct Act {
+    int flags = 0;
+    const float* A_log = nullptr;     // [H]
+    const float* dt_bias = nullptr;   // [H] (scalar gate) or [H][K] (per-key gate)
+};
+
 struct StepLaunch {
+    Act act;
     const void *q, *k, *v;
     const float *beta, *g;
     float* state;
@@ -43,6 +54,7 @@ struct ChunkWs {
 };
 
 struct IntraLaunch {
+    Act act;
     const void *q, *k, *v;
     const float *beta, *g;
     ChunkMap map;
@@ -69,6 +81,7 @@ struct ScanLaunch {
 // The fused forward (bf16 q/k/v, scalar gate, K = V = 128, C = 64): one
 // kernel per call, no per-chunk intermediates in HBM.
 struct FusedLaunch {
+    Act act;
     const void *q, *k, *v;
     const float *beta, *g;
     const float* h0;

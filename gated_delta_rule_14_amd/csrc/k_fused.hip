@@ -225,6 +225,8 @@ struct Ctx {
     int64_t H, h, t0, len;
     int v0, nch, lane, wave;
     float scale;
+    Act act;
+    float a_log, dt_bias;   // this head's gate-activation parameters
 
     // slot accessors take chunk indices >= 0
     __device__ __forceinline__ char* sK(int c) const { return sm + o_K + SZ_KQ * (c % 3); }
@@ -303,8 +305,15 @@ __device__ __forceinline__ void role_load(const Ctx& x) {
         const int c2 = j + 2;
         if (x.valid(c2)) {
             const float* raw = reinterpret_cast<const float*>(x.sRaw(c2));
-            const float G = wave_scan(raw[lane] * LOG2E);
-            const float bt = raw[C + lane];
+            float gl = raw[lane], bt = raw[C + lane];
+            if (x.act.flags) {
+                // raw logits: rows past a ragged end must stay g = 0, beta = 0
+                const bool in = lane < x.rows(c2);
+                if (x.act.flags & ACT_GATE) gl = in ? act_log_gate(gl, x.a_log, x.dt_bias) : 0.f;
+                if (x.act.flags & ACT_BETA_SIGMOID)
+                    bt = in ? act_beta(bt, x.act.flags & ACT_BETA_NEG_EIG) : 0.f;
+            }
+            const float G = wave_scan(gl * LOG2E);
             const float Gc = lane_of(G, C - 1);
             const float gam = exp2_hw(G);
             x.gate(c2, GA_G)[lane] = G;
@@ -793,6 +802,9 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedLaunch a) {
     x.lane = threadIdx.x & 63;
     x.wave = wave_id();
     x.scale = a.scale;
+    x.act = a.act;
+    x.a_log = (a.act.flags & ACT_GATE) ? a.act.A_log[x.h] : 0.f;
+    x.dt_bias = (a.act.flags & ACT_GATE) ? a.act.dt_bias[x.h] : 0.f;
     if (a.seqs) {
         const int4 s = a.seqs[n];
         x.t0 = s.x;

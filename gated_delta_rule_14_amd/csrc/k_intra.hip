@@ -141,8 +141,10 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
             const int r = lane;
             float gl = 0.f, bt = 0.f;
             if (r < n) {
-                gl = a.g[(t0 + r) * H + h] * LOG2E;
-                bt = a.beta[(t0 + r) * H + h];
+                const float gr = a.g[(t0 + r) * H + h], br = a.beta[(t0 + r) * H + h];
+                gl = ((a.act.flags & ACT_GATE) ? act_log_gate(gr, a.act.A_log[h], a.act.dt_bias[h]) : gr) *
+                     LOG2E;
+                bt = (a.act.flags & ACT_BETA_SIGMOID) ? act_beta(br, a.act.flags & ACT_BETA_NEG_EIG) : br;
             }
             const float G = wave_incl_scan(gl, lane);
             const float Gc = __shfl(G, C - 1, 64);
@@ -161,7 +163,10 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int r = r0 + i;
-                    gv[i] = r < n ? a.g[((t0 + r) * H + h) * K + d] * LOG2E : 0.f;
+                    float gr = r < n ? a.g[((t0 + r) * H + h) * K + d] : 0.f;
+                    if (r < n && (a.act.flags & ACT_GATE))
+                        gr = act_log_gate(gr, a.act.A_log[h], a.act.dt_bias[h * K + d]);
+                    gv[i] = gr * LOG2E;
                 }
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -170,7 +175,12 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                 }
             }
         }
-        for (int r = tid; r < C; r += NT) sB[r] = r < n ? a.beta[(t0 + r) * H + h] : 0.f;
+        for (int r = tid; r < C; r += NT) {
+            const float br = r < n ? a.beta[(t0 + r) * H + h] : 0.f;
+            sB[r] = r >= n ? 0.f
+                    : (a.act.flags & ACT_BETA_SIGMOID) ? act_beta(br, a.act.flags & ACT_BETA_NEG_EIG)
+                                                        : br;
+        }
     }
 #pragma unroll
     for (int p = 0; p < PKQ; ++p) {

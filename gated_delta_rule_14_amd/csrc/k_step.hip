@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void step_kernel(const T* __restrict__ q, cons
                                                    const float* __restrict__ beta,
                                                    const float* __restrict__ g,
                                                    float* __restrict__ state, T* __restrict__ o,
-                                                   float scale) {
+                                                   float scale, Act act, int64_t H) {
     constexpr int CG = V / 4;          // float4 column groups
     constexpr int RG = 256 / CG;       // row groups
     constexpr int ROWS = K / RG;       // rows per thread
@@ -46,13 +46,22 @@ __global__ __launch_bounds__(256) void step_kernel(const T* __restrict__ q, cons
 #pragma unroll
     for (int i = 0; i < ROWS; ++i) h[i] = st[(rg * ROWS + i) * CG + cg];
 
+    // raw gate / beta logits when the activation is fused in
+    const int64_t hh = pair % H;
+    const bool ag = act.flags & ACT_GATE;
     for (int i = tid; i < K; i += 256) {
         s_k[i] = Elem<T>::load(k + pair * K + i);
         s_q[i] = Elem<T>::load(q + pair * K + i);
-        s_d[i] = PER_KEY ? __expf(g[pair * K + i]) : 0.f;
+        if (PER_KEY) {
+            const float gi = g[pair * K + i];
+            s_d[i] = __expf(ag ? act_log_gate(gi, act.A_log[hh], act.dt_bias[hh * K + i]) : gi);
+        } else {
+            s_d[i] = 0.f;
+        }
     }
     for (int i = tid; i < V; i += 256) s_v[i] = Elem<T>::load(v + pair * V + i);
-    const float dscal = PER_KEY ? 0.f : __expf(g[pair]);
+    const float dscal =
+        PER_KEY ? 0.f : __expf(ag ? act_log_gate(g[pair], act.A_log[hh], act.dt_bias[hh]) : g[pair]);
     __syncthreads();
 
     float4 p = {0.f, 0.f, 0.f, 0.f}, s = {0.f, 0.f, 0.f, 0.f};
@@ -81,7 +90,9 @@ __global__ __launch_bounds__(256) void step_kernel(const T* __restrict__ q, cons
         S.x += b.x; S.y += b.y; S.z += b.z; S.w += b.w;
         KQ += s_kq[j];
     }
-    const float bt = beta[pair];
+    const float bt = (act.flags & ACT_BETA_SIGMOID)
+                         ? act_beta(beta[pair], act.flags & ACT_BETA_NEG_EIG)
+                         : beta[pair];
     float4 r;                                                  // correction
     r.x = bt * (s_v[4 * cg + 0] - P.x);
     r.y = bt * (s_v[4 * cg + 1] - P.y);
@@ -112,7 +123,7 @@ template <typename T, int K, int V, bool PK>
 static hipError_t launch_step_t(const StepLaunch& a) {
     hipLaunchKernelGGL((step_kernel<T, K, V, PK>), dim3((unsigned)(a.N * a.H)), dim3(256), 0,
                        a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.beta, a.g,
-                       a.state, (T*)a.o, a.scale);
+                       a.state, (T*)a.o, a.scale, a.act, a.H);
     return hipGetLastError();
 }
 

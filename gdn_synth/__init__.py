@@ -160,7 +160,7 @@ def _cast(x: np.ndarray, dtype: str) -> torch.Tensor:
     return t.to(torch.bfloat16 if dtype == "bf16" else torch.float32)
 
 
-def make_prefill(spec, seed: int = None) -> dict:
+def make_prefill(spec, seed: int = None, logits: bool = False) -> dict:
     """Draw one prefill workload.
 
     Returns a dict of CPU torch tensors in the layouts of the library:
@@ -169,6 +169,10 @@ def make_prefill(spec, seed: int = None) -> dict:
       h0 [N, H, K, V] f32 or None, cu_seqlens int64 [N+1] or None,
     plus 'scale', 'chunk', 'gate', 'lengths', 'spec'.
     Packed workloads are returned with B = 1 and T = total tokens.
+    With logits=True, beta and g hold the raw draws (the logits before the
+    sigmoid and before the gate's softplus) and the dict adds 'A_log' [H] and
+    'dt_bias' ([H], or [H, K] for the per-key gate) f32: the same draws as
+    without it.
     """
     if isinstance(spec, int):
         spec = PREFILL[spec]
@@ -188,8 +192,12 @@ def make_prefill(spec, seed: int = None) -> dict:
         ks.append(_unit_cast(_blocked(seed, n, "k", L, (H, K), "f32"), spec.dtype))
         vs.append(_cast(_blocked(seed, n, "v", L, (H, V), "f32"), spec.dtype))
         bn = _blocked(seed, n, "beta", L, (H,), "f64")
-        bs.append(torch.from_numpy(_sigmoid(bn).astype(np.float32)))
         gn = _blocked(seed, n, "g", L, (H, K) if per_key else (H,), "f64")
+        if logits:
+            bs.append(torch.from_numpy(bn.astype(np.float32)))
+            gs.append(torch.from_numpy(gn.astype(np.float32)))
+            continue
+        bs.append(torch.from_numpy(_sigmoid(bn).astype(np.float32)))
         a = A[None, :, None] if per_key else A[None, :]
         gs.append(torch.from_numpy((-a * _softplus(gn + spec.gate_shift)).astype(np.float32)))
     N = len(lengths)
@@ -208,9 +216,13 @@ def make_prefill(spec, seed: int = None) -> dict:
         cat = lambda xs: torch.stack(xs, 0)
         cu = None
     scale = spec.scale if spec.scale is not None else 1.0 / math.sqrt(K)
-    return dict(q=cat(qs), k=cat(ks), v=cat(vs), beta=cat(bs), g=cat(gs),
-                h0=h0, cu_seqlens=cu, scale=float(scale), chunk=spec.chunk,
-                gate=spec.gate, lengths=lengths, spec=spec)
+    out = dict(q=cat(qs), k=cat(ks), v=cat(vs), beta=cat(bs), g=cat(gs),
+               h0=h0, cu_seqlens=cu, scale=float(scale), chunk=spec.chunk,
+               gate=spec.gate, lengths=lengths, spec=spec)
+    if logits:
+        out["A_log"] = torch.from_numpy(np.log(A).astype(np.float32))
+        out["dt_bias"] = torch.full((H, K) if per_key else (H,), spec.gate_shift, dtype=torch.float32)
+    return out
 
 
 def draw_lengths(spec, seed: int = None):
@@ -222,13 +234,15 @@ def draw_lengths(spec, seed: int = None):
     return _draw_lengths(rng, spec)
 
 
-def make_decode(spec, seed: int = None) -> dict:
+def make_decode(spec, seed: int = None, logits: bool = False) -> dict:
     """Draw a decode workload: an initial state plus `steps` tokens.
 
     Returns state [N, H, K, V] f32 and per-step q, k [S, N, H, K],
     v [S, N, H, V] (dtype), beta [S, N, H] f32, g [S, N, H] (or [..., K]).
     Step s plays the role of sequence index s in the block recipe; the state
     is drawn in blocks of BLOCK sequences under the index S (= steps).
+    logits=True: raw beta and g logits plus 'A_log' and 'dt_bias', as in
+    make_prefill.
     """
     if isinstance(spec, int):
         spec = DECODE[spec]
@@ -247,12 +261,18 @@ def make_decode(spec, seed: int = None) -> dict:
     a = A[None, None, :, None] if per_key else A[None, None, :]
     state = _blocked(seed, S, "h0", N, (H, K, V), "f32") * np.float32(spec.state_std)
     scale = spec.scale if spec.scale is not None else 1.0 / math.sqrt(K)
-    return dict(q=_unit_cast(q, spec.dtype), k=_unit_cast(k, spec.dtype),
-                v=_cast(v, spec.dtype),
-                beta=torch.from_numpy(_sigmoid(bn).astype(np.float32)),
-                g=torch.from_numpy((-a * _softplus(gn + spec.gate_shift)).astype(np.float32)),
-                state=torch.from_numpy(state), scale=float(scale), gate=spec.gate,
-                spec=spec)
+    out = dict(q=_unit_cast(q, spec.dtype), k=_unit_cast(k, spec.dtype),
+               v=_cast(v, spec.dtype),
+               beta=torch.from_numpy(_sigmoid(bn).astype(np.float32)),
+               g=torch.from_numpy((-a * _softplus(gn + spec.gate_shift)).astype(np.float32)),
+               state=torch.from_numpy(state), scale=float(scale), gate=spec.gate,
+               spec=spec)
+    if logits:
+        out["beta"] = torch.from_numpy(bn.astype(np.float32))
+        out["g"] = torch.from_numpy(gn.astype(np.float32))
+        out["A_log"] = torch.from_numpy(np.log(A).astype(np.float32))
+        out["dt_bias"] = torch.full((H, K) if per_key else (H,), spec.gate_shift, dtype=torch.float32)
+    return out
 
 
 def flops_per_token_head(K: int, V: int, C: int) -> float:

@@ -17,7 +17,9 @@
  *
  * The output of step t reads the state after token t's own write.  q and k are
  * used as given: L2 normalisation is the caller's precondition ("TileLang
- * 实战" §0 and §1.2).  beta is used as given (normally in (0, 1)).
+ * 实战" §0 and §1.2).  beta is used as given (normally in (0, 1); any value in
+ * (0, 2) gives the write a negative eigenvalue 1 - beta), unless the
+ * *_act entry points are asked to activate it (gdn_activation below).
  *
  * Conventions shared by every entry point
  *  - Every pointer argument is device memory owned by the caller (any memory
@@ -46,7 +48,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef int32_t gdn_status;
 enum {
@@ -89,6 +91,30 @@ typedef struct gdn_step_desc {
     int32_t gate;       /* GDN_GATE_* */
     float scale;
 } gdn_step_desc;
+
+/*
+ * Optional in-kernel input activation ("Gated Delta Network（GDN）" §3.1,
+ * eq. 5: log alpha = -e^{A_log} softplus(W_alpha x + b_alpha), beta =
+ * sigmoid(W_beta x); §5: the activation fused into the chunk kernel, and
+ * beta in (0, 2) for negative eigenvalues).  With a flag set, the matching
+ * input holds the raw logits instead of the activated values:
+ *   GDN_ACT_GATE          g = a (raw):  log alpha = -exp(A_log[h]) * softplus(a + dt_bias)
+ *                         with dt_bias[h] for the scalar gate and
+ *                         dt_bias[h][kc] (key channel kc) for the per-key gate
+ *   GDN_ACT_BETA_SIGMOID  beta = sigmoid(b)
+ *   GDN_ACT_BETA_NEG_EIG  with GDN_ACT_BETA_SIGMOID: beta = 2 sigmoid(b), in
+ *                         (0, 2), so the eigenvalue 1 - beta of the write
+ *                         ranges over (-1, 1)
+ * A_log [H] and dt_bias ([H] or [H, K]) are float device arrays, required
+ * with GDN_ACT_GATE and otherwise ignored.  Unknown bits, or NEG_EIG without
+ * BETA_SIGMOID, give GDN_ERR_UNSUPPORTED.
+ */
+enum { GDN_ACT_GATE = 1, GDN_ACT_BETA_SIGMOID = 2, GDN_ACT_BETA_NEG_EIG = 4 };
+typedef struct gdn_activation {
+    int32_t flags;           /* GDN_ACT_* */
+    const float *A_log;      /* [H] */
+    const float *dt_bias;    /* [H] (scalar gate) or [H, K] (per-key gate) */
+} gdn_activation;
 
 /* Integer version of this ABI (GDN_ABI_VERSION), for binding checks. */
 int gdn_abi_version(void);
@@ -150,6 +176,19 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_desc *d,
                          void *o, float *ht,
                          void *workspace, size_t workspace_bytes,
                          void *stream);
+
+/*
+ * gdn_chunk_fwd with the input activation applied inside the kernels (act
+ * may be NULL: then exactly gdn_chunk_fwd).  Rows past the end of a
+ * sequence are never activated: they stay outside every result.
+ */
+gdn_status gdn_chunk_fwd_act(const gdn_fwd_desc *d, const gdn_activation *act,
+                             const void *q, const void *k, const void *v,
+                             const float *beta, const float *g, const float *h0,
+                             const int64_t *cu_seqlens,
+                             void *o, float *ht,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream);
 
 /*
  * Where gdn_chunk_intra / gdn_chunk_scan (and the two-stage route of
@@ -253,6 +292,12 @@ gdn_status gdn_recurrent_step(const gdn_step_desc *d,
                               const void *q, const void *k, const void *v,
                               const float *beta, const float *g,
                               float *state, void *o, void *stream);
+
+/* gdn_recurrent_step with the input activation (act may be NULL). */
+gdn_status gdn_recurrent_step_act(const gdn_step_desc *d, const gdn_activation *act,
+                                  const void *q, const void *k, const void *v,
+                                  const float *beta, const float *g,
+                                  float *state, void *o, void *stream);
 
 #ifdef __cplusplus
 }

@@ -9,7 +9,10 @@ HIP path.
   chunked_forward  : the chunked UT form with its intermediates (numpy fp64)
   brute_force_forward, wy_ungated : explicit transition products and WY
       recursions, used to pin the two above on tiny inputs.
+  activation.log_gate / beta_from_logits : the gate and beta activations
+      from raw logits (the in-kernel activation's reference).
 """
 from .recurrence import recurrent_forward, recurrent_step, as_f64  # noqa: F401
 from .chunked import chunked_forward  # noqa: F401
 from .brute import brute_force_forward, wy_ungated, transition  # noqa: F401
+from . import activation  # noqa: F401

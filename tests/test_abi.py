@@ -126,3 +126,28 @@ def test_binding_refuses_host_tensors():
     q = torch.zeros(1, 64, 1, 64)
     with pytest.raises(ValueError):
         gdn.chunk_fwd(q, q, q, torch.zeros(1, 64, 1), torch.zeros(1, 64, 1))
+
+
+def test_activation_rejects_before_launch(lib):
+    """gdn_chunk_fwd_act / gdn_recurrent_step_act check the activation
+    arguments before anything else is launched."""
+    d = _desc()
+    odd = ctypes.c_void_p((1 << 20) + 2)
+
+    def fwd(flags, A_log, dt_bias):
+        a = gdn.Activation(flags, A_log, dt_bias)
+        return lib.gdn_chunk_fwd_act(ctypes.byref(d), ctypes.byref(a), FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, None, None, FAKE, None, FAKE, 1 << 40, None)
+
+    def step(flags, A_log, dt_bias):
+        s = gdn.StepDesc(4, 2, 128, 128, 1, 0, 0.1)
+        a = gdn.Activation(flags, A_log, dt_bias)
+        return lib.gdn_recurrent_step_act(ctypes.byref(s), ctypes.byref(a), *([FAKE] * 7), None)
+
+    for fn in (fwd, step):
+        assert fn(8, None, None) == 4            # unknown bit
+        assert fn(4, None, None) == 4            # NEG_EIG without BETA_SIGMOID
+        assert fn(1, None, FAKE) == 1            # GATE needs A_log
+        assert fn(1 | 2, FAKE, None) == 1        # ... and dt_bias
+        assert fn(1, odd, FAKE) == 6             # 4-byte alignment
+        assert lib.gdn_last_error().decode() != ""
