@@ -13,7 +13,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_SCALAR, GATE_PER_KEY = 0, 1
@@ -33,14 +33,15 @@ class FwdDesc(ctypes.Structure):
                 ("num_heads", ctypes.c_int64), ("key_dim", ctypes.c_int64),
                 ("value_dim", ctypes.c_int64), ("num_seqs", ctypes.c_int64),
                 ("chunk", ctypes.c_int32), ("qkv_dtype", ctypes.c_int32),
-                ("gate", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("gate", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("num_v_heads", ctypes.c_int64)]
 
 
 class StepDesc(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int64), ("num_heads", ctypes.c_int64),
                 ("key_dim", ctypes.c_int64), ("value_dim", ctypes.c_int64),
                 ("qkv_dtype", ctypes.c_int32), ("gate", ctypes.c_int32),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("num_v_heads", ctypes.c_int64)]
 
 
 class Activation(ctypes.Structure):
@@ -136,10 +137,13 @@ def _need(t, name, dtype=None):
 
 
 def fwd_desc(q, v, gate="scalar", chunk=64, scale=None, num_seqs=0):
+    """Descriptor of q [B, T, H, K] and v [B, T, H_V, V] (H_V a multiple of H:
+    grouped value heads when H_V > H)."""
     B, T, H, K = q.shape
+    HV = v.shape[2]
     return FwdDesc(B, T, H, K, v.shape[-1], num_seqs, chunk, _dtype_code(q),
                    GATE_PER_KEY if gate == "per_key" else GATE_SCALAR,
-                   float(K ** -0.5 if scale is None else scale))
+                   float(K ** -0.5 if scale is None else scale), HV if HV != H else 0)
 
 
 def workspace_layout(desc: FwdDesc) -> WorkspaceLayout:
@@ -189,9 +193,11 @@ def _inputs(q, k, v, beta, g, cu_seqlens, gate):
     _need(g, "g", torch.float32)
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", torch.int64)
-    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or beta.shape != q.shape[:3]:
-        raise ValueError("shape mismatch among q, k, v, beta")
-    want_g = q.shape if gate == "per_key" else q.shape[:3]
+    HV = v.shape[2]
+    if k.shape != q.shape or v.shape[:2] != q.shape[:2] or HV % q.shape[2] != 0 or \
+            tuple(beta.shape) != tuple(v.shape[:3]):
+        raise ValueError("shape mismatch among q, k, v, beta (v may have a multiple of q's heads)")
+    want_g = tuple(v.shape[:3]) + ((q.shape[3],) if gate == "per_key" else ())
     if tuple(g.shape) != tuple(want_g):
         raise ValueError("g must have shape %s for gate=%s" % (tuple(want_g), gate))
 
@@ -205,7 +211,7 @@ def chunk_fwd(q, k, v, beta, g, scale=None, h0=None, cu_seqlens=None, chunk=64,
     _inputs(q, k, v, beta, g, cu_seqlens, gate)
     N = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
     desc = fwd_desc(q, v, gate, chunk, scale, 0 if cu_seqlens is None else N)
-    H, K, V = q.shape[2], q.shape[3], v.shape[3]
+    H, K, V = v.shape[2], q.shape[3], v.shape[3]   # state heads: the value heads
     if h0 is not None:
         _need(h0, "h0", torch.float32)
         if tuple(h0.shape) != (N, H, K, V):
@@ -247,7 +253,7 @@ def chunk_intra(q, k, v, beta, g, scale=None, cu_seqlens=None, chunk=64, gate="s
                                _ptr(g), _ptr(cu_seqlens), _ptr(ws),
                                ws.numel() * ws.element_size(),
                                INTRA_STORE_AINV if store_ainv else 0, _stream(stream)))
-    H, K, V, C, mc = q.shape[2], q.shape[3], v.shape[3], chunk, L.max_chunks
+    H, K, V, C, mc = v.shape[2], q.shape[3], v.shape[3], chunk, L.max_chunks
     if not views:
         return dict(max_chunks=mc, workspace=ws, desc=desc)
 
@@ -318,18 +324,18 @@ def recurrent_step(q, k, v, beta, g, state, scale=None, gate="scalar", o=None, s
     _need(beta, "beta", torch.float32)
     _need(g, "g", torch.float32)
     _need(state, "state", torch.float32)
-    N, H, K = q.shape
-    V = v.shape[-1]
+    N, Hq, K = q.shape
+    H, V = v.shape[1], v.shape[-1]    # value heads (a multiple of q's: grouped value heads)
     if tuple(state.shape) != (N, H, K, V):
         raise ValueError("state must have shape %s" % ((N, H, K, V),))
     want_g = (N, H, K) if gate == "per_key" else (N, H)
-    if tuple(g.shape) != want_g or tuple(beta.shape) != (N, H):
+    if tuple(g.shape) != want_g or tuple(beta.shape) != (N, H) or H % Hq != 0:
         raise ValueError("beta/g shape mismatch")
     if o is None:
         o = torch.empty((N, H, V), dtype=q.dtype, device=q.device)
-    desc = StepDesc(N, H, K, V, _dtype_code(q),
+    desc = StepDesc(N, Hq, K, V, _dtype_code(q),
                     GATE_PER_KEY if gate == "per_key" else GATE_SCALAR,
-                    float(K ** -0.5 if scale is None else scale))
+                    float(K ** -0.5 if scale is None else scale), H if H != Hq else 0)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(state), _ptr(o), _stream(stream))
     if act is None:
         _check(lib.gdn_recurrent_step(ctypes.byref(desc), *args))

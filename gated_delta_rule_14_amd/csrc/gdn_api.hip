@@ -36,6 +36,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool dim_ok(int64_t d) { return d == 64 || d == 128; }
 
+// value heads (GVA: a multiple of the q/k heads)
+int64_t vheads(const gdn_fwd_desc* d) { return d->num_v_heads > 0 ? d->num_v_heads : d->num_heads; }
+
 gdn_status check_desc(const gdn_fwd_desc* d, bool packed) {
     if (!d) return fail(GDN_ERR_NULL_ARG, "desc is NULL");
     if (d->qkv_dtype != GDN_DTYPE_F32 && d->qkv_dtype != GDN_DTYPE_BF16)
@@ -55,6 +58,10 @@ gdn_status check_desc(const gdn_fwd_desc* d, bool packed) {
     if (d->batch * d->seq_len >= (int64_t)1 << 31)
         return fail(GDN_ERR_BAD_SHAPE, "B*T must be below 2^31");
     if (d->num_heads > 65535) return fail(GDN_ERR_BAD_SHAPE, "num_heads above 65535");
+    if (d->num_v_heads < 0 || (d->num_v_heads > 0 && (d->num_v_heads % d->num_heads != 0 ||
+                                                      d->num_v_heads > 65535)))
+        return fail(GDN_ERR_BAD_SHAPE, "num_v_heads %lld must be 0 or a multiple of num_heads %lld",
+                    (long long)d->num_v_heads, (long long)d->num_heads);
     if (d->chunk != 64)
         return fail(GDN_ERR_UNSUPPORTED, "chunk %d (this build implements 64)", d->chunk);
     if (!dim_ok(d->key_dim) || !dim_ok(d->value_dim))
@@ -72,7 +79,7 @@ int64_t max_chunks_of(const gdn_fwd_desc* d, bool packed) {
 
 void layout(const gdn_fwd_desc* d, bool packed, gdn_workspace_layout* L) {
     const int64_t mc = max_chunks_of(d, packed);
-    const int64_t H = d->num_heads, K = d->key_dim, V = d->value_dim, C = d->chunk;
+    const int64_t H = vheads(d), K = d->key_dim, V = d->value_dim, C = d->chunk;
     const size_t es = d->qkv_dtype == GDN_DTYPE_BF16 ? 2 : 4;
     const size_t blocks = (size_t)(H * mc);
     size_t off = 0;
@@ -206,7 +213,8 @@ gdn_status prepare(const gdn_fwd_desc* d, const void* q, const void* k, const vo
         a.g = g;
         a.map = P->map;
         a.ws = P->ws;
-        a.H = d->num_heads;
+        a.H = vheads(d);
+        a.Hq = d->num_heads;
         a.K = (int)d->key_dim;
         a.V = (int)d->value_dim;
         a.C = d->chunk;
@@ -305,7 +313,7 @@ static gdn_status scan(const gdn_fwd_desc* d, const float* h0, const int64_t* cu
     a.ht = ht;
     a.o = o;
     a.N = packed ? d->num_seqs : d->batch;
-    a.H = d->num_heads;
+    a.H = vheads(d);
     a.K = (int)d->key_dim;
     a.V = (int)d->value_dim;
     a.C = d->chunk;
@@ -355,7 +363,8 @@ static gdn_status fused_fwd(const gdn_fwd_desc* d, const void* q, const void* k,
     a.seqs = nullptr;
     a.T = d->seq_len;
     a.N = packed ? d->num_seqs : d->batch;
-    a.H = d->num_heads;
+    a.H = vheads(d);
+    a.Hq = d->num_heads;
     a.K = (int)d->key_dim;
     a.V = (int)d->value_dim;
     a.C = d->chunk;
@@ -430,8 +439,12 @@ gdn_status gdn_recurrent_step_act(const gdn_step_desc* d, const gdn_activation* 
     if (!dim_ok(d->key_dim) || !dim_ok(d->value_dim))
         return fail(GDN_ERR_UNSUPPORTED, "K=%lld V=%lld (supported: 64, 128)",
                     (long long)d->key_dim, (long long)d->value_dim);
-    if (d->num_seqs * d->num_heads >= (int64_t)1 << 31)
-        return fail(GDN_ERR_BAD_SHAPE, "N*H must be below 2^31");
+    if (d->num_v_heads < 0 || (d->num_v_heads > 0 && d->num_v_heads % d->num_heads != 0))
+        return fail(GDN_ERR_BAD_SHAPE, "num_v_heads %lld must be 0 or a multiple of num_heads %lld",
+                    (long long)d->num_v_heads, (long long)d->num_heads);
+    const int64_t HV = d->num_v_heads > 0 ? d->num_v_heads : d->num_heads;
+    if (d->num_seqs * HV >= (int64_t)1 << 31)
+        return fail(GDN_ERR_BAD_SHAPE, "N*H_V must be below 2^31");
     if (!q || !k || !v || !beta || !g || !state || !o)
         return fail(GDN_ERR_NULL_ARG, "q, k, v, beta, g, state and o are required");
     const size_t es = d->qkv_dtype == GDN_DTYPE_BF16 ? 2 : 4;
@@ -450,7 +463,8 @@ gdn_status gdn_recurrent_step_act(const gdn_step_desc* d, const gdn_activation* 
     a.o = o;
     a.scale = d->scale;
     a.N = d->num_seqs;
-    a.H = d->num_heads;
+    a.H = HV;
+    a.Hq = d->num_heads;
     a.K = (int)d->key_dim;
     a.V = (int)d->value_dim;
     a.bf16 = d->qkv_dtype == GDN_DTYPE_BF16;

@@ -20,6 +20,7 @@ struct Act {
 
 struct StepLaunch {
     Act act;
+    int64_t Hq = 0;         // q/k heads (value heads H are a multiple of it)
     const void *q, *k, *v;
     const float *beta, *g;
     float* state;
@@ -55,6 +56,7 @@ struct ChunkWs {
 
 struct IntraLaunch {
     Act act;
+    int64_t Hq = 0;         // q/k heads (value heads H are a multiple of it)
     const void *q, *k, *v;
     const float *beta, *g;
     ChunkMap map;
@@ -82,6 +84,7 @@ struct ScanLaunch {
 // kernel per call, no per-chunk intermediates in HBM.
 struct FusedLaunch {
     Act act;
+    int64_t Hq = 0;         // q/k heads (value heads H are a multiple of it)
     const void *q, *k, *v;
     const float *beta, *g;
     const float* h0;

@@ -222,7 +222,8 @@ struct Ctx {
     char* sm;
     const bf16 *q, *k, *v;
     const float *beta, *g;
-    int64_t H, h, t0, len;
+    int64_t H, h, t0, len;   // value heads (the state's head), this value head
+    int64_t Hq, hq;          // q/k heads, the q/k head this value head reads (GVA)
     int v0, nch, lane, wave;
     float scale;
     Act act;
@@ -261,6 +262,10 @@ struct Ctx {
     __device__ __forceinline__ const char* row0(const P* base, int c, int D) const {
         return reinterpret_cast<const char*>(base + ((t0 + (int64_t)c * C) * H + h) * D);
     }
+    // first row of chunk c of q or k (H_q heads)
+    __device__ __forceinline__ const char* row0_qk(const bf16* base, int c) const {
+        return reinterpret_cast<const char*>(base + ((t0 + (int64_t)c * C) * Hq + hq) * K);
+    }
 };
 
 // index of the causal 16x16x32 Aqk / T fragment (t, p), p <= t/2
@@ -271,7 +276,7 @@ __device__ __forceinline__ constexpr int ab_ix(int I, int J) { return I * (I - 1
 // ---------------------------------------------------------------- wave 6: loads and gates
 __device__ __forceinline__ void role_load(const Ctx& x) {
     const int lane = x.lane;
-    const uint32_t skq = (uint32_t)(x.H * K * 2), sv = (uint32_t)(x.H * V * 2);
+    const uint32_t skq = (uint32_t)(x.Hq * K * 2), sv = (uint32_t)(x.H * V * 2);
     const uint32_t sg = (uint32_t)(x.H * 4);
     // source offsets inside a chunk: K/Q load s fills rows 4s..4s+3 (lane l:
     // row 4s + l/16, LDS group l%16), V load s rows 16s..16s+15 (lane l: row
@@ -336,8 +341,8 @@ __device__ __forceinline__ void role_load(const Ctx& x) {
         // clamped duplicate past the end: its slot is free either way)
         const int ck = x.clampc(c2);
         const uint32_t nr = (uint32_t)x.rows(ck);
-        const __amdgpu_buffer_rsrc_t rk = rsrc(x.row0(x.k, ck, K), nr * skq);
-        const __amdgpu_buffer_rsrc_t rq = rsrc(x.row0(x.q, ck, K), nr * skq);
+        const __amdgpu_buffer_rsrc_t rk = rsrc(x.row0_qk(x.k, ck), nr * skq);
+        const __amdgpu_buffer_rsrc_t rq = rsrc(x.row0_qk(x.q, ck), nr * skq);
         const __amdgpu_buffer_rsrc_t rv = rsrc(x.row0(x.v, ck, V), nr * sv);
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
@@ -798,6 +803,8 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedLaunch a) {
     x.H = a.H;
     const int64_t n = chain / a.H;
     x.h = chain - n * a.H;
+    x.Hq = a.Hq > 0 ? a.Hq : a.H;
+    x.hq = x.h / (a.H / x.Hq);
     x.v0 = vt * VT;
     x.lane = threadIdx.x & 63;
     x.wave = wave_id();

@@ -89,6 +89,8 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
     // first chunks, which the state pass reads first, are written last and
     // are the ones still held in the memory-side cache when it starts.
     const int64_t H = a.H, bid = blockIdx.x, h = bid % H, cr = bid / H;
+    // GVA: q and k have Hq heads; value head h reads q/k head h / (H / Hq)
+    const int64_t Hq = a.Hq > 0 ? a.Hq : H, hq = h / (H / Hq);
     int64_t c;
     if (a.map.table) {
         c = a.map.max_chunks - 1 - cr;
@@ -126,8 +128,8 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
 #pragma unroll
     for (int p = 0; p < PKQ; ++p) {
         const int i = tid + NT * p, r = min(i / (K / EV), n - 1), cv = i % (K / EV);
-        kr[p] = *reinterpret_cast<const u32x4*>(k + ((t0 + r) * H + h) * K + cv * EV);
-        qr[p] = *reinterpret_cast<const u32x4*>(q + ((t0 + r) * H + h) * K + cv * EV);
+        kr[p] = *reinterpret_cast<const u32x4*>(k + ((t0 + r) * Hq + hq) * K + cv * EV);
+        qr[p] = *reinterpret_cast<const u32x4*>(q + ((t0 + r) * Hq + hq) * K + cv * EV);
     }
 #pragma unroll
     for (int p = 0; p < PV; ++p) {

@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void step_kernel(const T* __restrict__ q, cons
                                                    const float* __restrict__ beta,
                                                    const float* __restrict__ g,
                                                    float* __restrict__ state, T* __restrict__ o,
-                                                   float scale, Act act, int64_t H) {
+                                                   float scale, Act act, int64_t H, int64_t Hq) {
     constexpr int CG = V / 4;          // float4 column groups
     constexpr int RG = 256 / CG;       // row groups
     constexpr int ROWS = K / RG;       // rows per thread
@@ -48,10 +48,12 @@ __global__ __launch_bounds__(256) void step_kernel(const T* __restrict__ q, cons
 
     // raw gate / beta logits when the activation is fused in
     const int64_t hh = pair % H;
+    // GVA: value head hh reads q/k head hh / (H / Hq)
+    const int64_t qk = (pair / H) * Hq + hh / (H / Hq);
     const bool ag = act.flags & ACT_GATE;
     for (int i = tid; i < K; i += 256) {
-        s_k[i] = Elem<T>::load(k + pair * K + i);
-        s_q[i] = Elem<T>::load(q + pair * K + i);
+        s_k[i] = Elem<T>::load(k + qk * K + i);
+        s_q[i] = Elem<T>::load(q + qk * K + i);
         if (PER_KEY) {
             const float gi = g[pair * K + i];
             s_d[i] = __expf(ag ? act_log_gate(gi, act.A_log[hh], act.dt_bias[hh * K + i]) : gi);
@@ -123,7 +125,7 @@ template <typename T, int K, int V, bool PK>
 static hipError_t launch_step_t(const StepLaunch& a) {
     hipLaunchKernelGGL((step_kernel<T, K, V, PK>), dim3((unsigned)(a.N * a.H)), dim3(256), 0,
                        a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.beta, a.g,
-                       a.state, (T*)a.o, a.scale, a.act, a.H);
+                       a.state, (T*)a.o, a.scale, a.act, a.H, a.Hq > 0 ? a.Hq : a.H);
     return hipGetLastError();
 }
 

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef int32_t gdn_status;
 enum {
@@ -79,6 +79,7 @@ typedef struct gdn_fwd_desc {
     int32_t qkv_dtype;  /* GDN_DTYPE_* of q, k, v, o */
     int32_t gate;       /* GDN_GATE_* */
     float scale;        /* multiplies q (usually 1/sqrt(K)) */
+    int64_t num_v_heads;  /* H_V value heads (0: H_V = H); see GVA below */
 } gdn_fwd_desc;
 
 /* Shape of a single-token (decode) step over N independent sequences. */
@@ -90,7 +91,17 @@ typedef struct gdn_step_desc {
     int32_t qkv_dtype;  /* GDN_DTYPE_* of q, k, v, o */
     int32_t gate;       /* GDN_GATE_* */
     float scale;
+    int64_t num_v_heads;  /* H_V value heads (0: H_V = H); see GVA below */
 } gdn_step_desc;
+
+/*
+ * GVA, grouped value heads ("Gated Delta Network（GDN）" §5): q and k have H
+ * heads, v has H_V = m H heads (m a positive integer) and the state is kept
+ * per value head.  Value head hv reads q/k head hv / m (integer division),
+ * like grouped-query attention.  Everything that belongs to a state -- v, o,
+ * beta, g, h0, ht, A_log, dt_bias -- has H_V heads; the shapes below then read
+ * H_V wherever the head count of those tensors appears.
+ */
 
 /*
  * Optional in-kernel input activation ("Gated Delta Network（GDN）" §3.1,

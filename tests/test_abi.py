@@ -53,7 +53,8 @@ def _status(fn, *args):
     (dict(chunk=32), 4), (dict(chunk=128), 4), (dict(key_dim=96), 4), (dict(value_dim=256), 4),
     (dict(qkv_dtype=7), 3), (dict(gate=5), 3), (dict(batch=0), 2), (dict(num_heads=0), 2),
     (dict(seq_len=-1), 2), (dict(qkv_dtype=0, gate=1, key_dim=128), 4),
-    (dict(batch=2, num_seqs=3), 2),
+    (dict(batch=2, num_seqs=3), 2), (dict(num_heads=4, num_v_heads=6), 2),
+    (dict(num_v_heads=-1), 2),
 ])
 def test_descriptor_errors(lib, kw, code):
     n = ctypes.c_size_t()
