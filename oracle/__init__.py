@@ -11,8 +11,13 @@ HIP path.
       recursions, used to pin the two above on tiny inputs.
   activation.log_gate / beta_from_logits : the gate and beta activations
       from raw logits (the in-kernel activation's reference).
+  backward.recurrent_backward : gradients (dq, dk, dv, dbeta, dg, dh0) by
+      autograd through the fp64 token recurrence (PyTorch CPU)
+  backward.chunked_backward : the chunkwise backward steps with the gate
+      terms (numpy fp64), pinned to the former.
 """
 from .recurrence import recurrent_forward, recurrent_step, as_f64  # noqa: F401
 from .chunked import chunked_forward  # noqa: F401
 from .brute import brute_force_forward, wy_ungated, transition  # noqa: F401
 from . import activation  # noqa: F401
+from . import backward  # noqa: F401
