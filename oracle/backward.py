@@ -21,6 +21,9 @@ chunked_backward
     of the state update and gamma_C on the carried state), plus the gate
     gradient, which the pages do not give: dG per row of the chunk-local
     cumulative gate, then dg = reverse cumulative sum of dG inside the chunk.
+    Every decay ratio is taken in the log domain (gamma_C / gamma_i as
+    exp(G_C - G_i)), as the forward's Gamma is: with strong gates gamma
+    itself underflows to 0.
     Scalar gate only.  It is pinned to recurrent_backward, which is in turn
     pinned by central finite differences of the independent C recurrence.
 """
@@ -101,6 +104,7 @@ def _chunk_fwd(Qc, Kc, Vc, bc, gc, h, scale):
     Gam = np.where(incl, np.exp(np.where(incl, D, 0.0)), 0.0)
     gam = np.exp(G)
     end = gam[-1]
+    rest = np.exp(G[-1] - G)          # gamma_C / gamma_i in the log domain (no 0/0)
     KK = Kc @ Kc.T
     A = np.tril(bc[:, None] * Gam * KK, -1)
     Ainv = np.linalg.inv(np.eye(n) + A)
@@ -108,8 +112,8 @@ def _chunk_fwd(Qc, Kc, Vc, bc, gc, h, scale):
     W = Ainv @ ((bc * gam)[:, None] * Kc)
     U = Ainv @ (bc[:, None] * Vc)
     Vnew = U - W @ h
-    Ks = (end / gam)[:, None] * Kc
-    return dict(G=G, Gam=Gam, gam=gam, end=end, KK=KK, A=A, Ainv=Ainv, Aqk=Aqk, W=W, U=U,
+    Ks = rest[:, None] * Kc
+    return dict(G=G, Gam=Gam, gam=gam, end=end, rest=rest, KK=KK, A=A, Ainv=Ainv, Aqk=Aqk, W=W, U=U,
                 Vnew=Vnew, Ks=Ks, h_in=h, h_out=end * h + Ks.T @ Vnew)
 
 
@@ -132,7 +136,7 @@ def _chunk_bwd(Qc, Kc, Vc, bc, f, dOc, dH, scale):
     dQ_inter = scale * gam[:, None] * (dOc @ h.T)
     dQ = dQ_inter + scale * (dAqk * Gam) @ Kc
     dKs = Vnew @ dH.T                                     # gradient of K*gamma_C/gamma
-    dK = (end / gam)[:, None] * dKs + scale * (dAqk * Gam).T @ Qc
+    dK = f["rest"][:, None] * dKs + scale * (dAqk * Gam).T @ Qc
     dW = -dVnew @ h.T
     # Step 6: WY backward.  W = Ainv diag(beta gamma) K, U = Ainv diag(beta) V.
     AtdW = Ainv.T @ dW

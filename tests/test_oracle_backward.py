@@ -140,6 +140,21 @@ def test_chunked_backward_matches_autograd(chunk, T):
         assert _rel(got[name], ref[name]) < 1e-10, name
 
 
+def test_chunked_backward_strong_decay():
+    """The pages' strongest gates (A up to 16): gamma underflows to 0 inside
+    a 64-token chunk, and the chunked backward still matches (no 0/0)."""
+    d = draw(45, B=1, T=150, H=2, K=8, V=6, A=(8.0, 16.0))
+    do, dht = _extras(45, d, 1)
+    ref = recurrent_backward(d["q"], d["k"], d["v"], d["beta"], d["g"], 0.35, do,
+                             h0=d["h0"], dht=dht)
+    with np.errstate(divide="raise", invalid="raise"):
+        got = chunked_backward(d["q"], d["k"], d["v"], d["beta"], d["g"], 0.35, do,
+                               h0=d["h0"], dht=dht, chunk=64)
+    assert np.exp(np.cumsum(d["g"][0, :64, 0]))[-1] == 0.0   # the case is the underflowing one
+    for name in NAMES:
+        assert _rel(got[name], ref[name]) < 1e-10, name
+
+
 def test_chunked_backward_packed_wide_beta():
     d = draw(40, B=1, T=90, H=2, K=6, V=5)
     rng = np.random.default_rng(40)
