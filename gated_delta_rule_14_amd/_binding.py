@@ -13,7 +13,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_SCALAR, GATE_PER_KEY = 0, 1
@@ -23,7 +23,8 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE", 3: "GDN_ER
 EXPORTS = sorted(["gdn_abi_version", "gdn_status_str", "gdn_last_error",
                   "gdn_chunk_fwd_workspace", "gdn_chunk_fwd", "gdn_workspace_layout_of",
                   "gdn_chunk_intra", "gdn_chunk_scan", "gdn_recurrent_step",
-                  "gdn_chunk_fwd_act", "gdn_recurrent_step_act"])
+                  "gdn_chunk_fwd_act", "gdn_recurrent_step_act",
+                  "gdn_chunk_bwd_workspace", "gdn_chunk_bwd"])
 INTRA_STORE_AINV = 1
 ACT_GATE, ACT_BETA_SIGMOID, ACT_BETA_NEG_EIG = 1, 2, 4
 
@@ -97,6 +98,10 @@ def load(path: str = LIB_PATH):
     lib.gdn_recurrent_step_act.argtypes = [ctypes.POINTER(StepDesc), ctypes.POINTER(Activation),
                                            P, P, P, P, P, P, P, P]
     lib.gdn_recurrent_step_act.restype = S
+    lib.gdn_chunk_bwd_workspace.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdn_chunk_bwd_workspace.restype = S
+    lib.gdn_chunk_bwd.argtypes = [ctypes.POINTER(FwdDesc)] + [P] * 16 + [ctypes.c_size_t, P]
+    lib.gdn_chunk_bwd.restype = S
     v = lib.gdn_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError("libgdn.so ABI %d, binding expects %d" % (v, ABI_VERSION))
@@ -232,6 +237,55 @@ def chunk_fwd(q, k, v, beta, g, scale=None, h0=None, cu_seqlens=None, chunk=64,
         _act_shapes(act, H, K, gate)
         _check(lib.gdn_chunk_fwd_act(ctypes.byref(desc), ctypes.byref(act), *args))
     return o, (ht if output_final_state else None)
+
+
+def bwd_workspace_bytes(desc: FwdDesc) -> int:
+    lib = load()
+    n = ctypes.c_size_t()
+    _check(lib.gdn_chunk_bwd_workspace(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def chunk_bwd(q, k, v, beta, g, do, scale=None, h0=None, dht=None, cu_seqlens=None, chunk=64,
+              want_dh0=True, workspace=None, out=None, stream=None):
+    """gdn_chunk_bwd: gradients of <do, o> + <dht, ht> of the chunked forward
+    with respect to q, k, v, beta, g (scalar gate) and h0.  Returns a dict
+    dq, dk, dv (dtype of q), dbeta, dg, dh0 (float32; dh0 None unless
+    want_dh0).  `out` may supply any of these tensors."""
+    lib = load()
+    _inputs(q, k, v, beta, g, cu_seqlens, "scalar")
+    _need(do, "do", q.dtype)
+    if do.shape != v.shape:
+        raise ValueError("do must have the shape of v")
+    N = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+    desc = fwd_desc(q, v, "scalar", chunk, scale, 0 if cu_seqlens is None else N)
+    H, K, V = v.shape[2], q.shape[3], v.shape[3]
+    for t, name in ((h0, "h0"), (dht, "dht")):
+        if t is not None:
+            _need(t, name, torch.float32)
+            if tuple(t.shape) != (N, H, K, V):
+                raise ValueError("%s must have shape %s" % (name, (N, H, K, V)))
+    out = dict(out or {})
+    dev = q.device
+    for name, shape, dt in (("dq", q.shape, q.dtype), ("dk", k.shape, q.dtype),
+                            ("dv", v.shape, q.dtype), ("dbeta", beta.shape, torch.float32),
+                            ("dg", g.shape, torch.float32)):
+        if out.get(name) is None:
+            out[name] = torch.empty(shape, dtype=dt, device=dev)
+        _need(out[name], name, dt)
+    if want_dh0 and out.get("dh0") is None:
+        out["dh0"] = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+    if not want_dh0:
+        out["dh0"] = None
+    nbytes = bwd_workspace_bytes(desc)
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _check(lib.gdn_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                             _ptr(h0), _ptr(cu_seqlens), _ptr(do), _ptr(dht), _ptr(out["dq"]),
+                             _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
+                             _ptr(out["dg"]), _ptr(out["dh0"]), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
 
 
 def chunk_intra(q, k, v, beta, g, scale=None, cu_seqlens=None, chunk=64, gate="scalar",

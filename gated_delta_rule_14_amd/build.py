@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.hip", "k_step.hip", "k_table.hip", "k_intra.hip", "k_scan.hip",
+SOURCES = ["gdn_api.hip", "k_step.hip", "k_table.hip", "k_intra.hip", "k_scan.hip", "k_bwd.hip",
            "k_fused.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -104,6 +104,48 @@ void layout(const gdn_fwd_desc* d, bool packed, gdn_workspace_layout* L) {
     L->max_chunks = mc;
 }
 
+// Backward workspace: the forward layout (intra stage in backward mode, the
+// chunk table), then the extra operand orders, the entry states, V_new and
+// the two gradients the reverse pass leaves for the per-chunk kernel.
+struct BwdLayout {
+    gdn_workspace_layout f;
+    size_t ksr, wt, hs, dhs, vn, dvn, total;
+};
+
+void bwd_layout(const gdn_fwd_desc* d, bool packed, BwdLayout* L) {
+    layout(d, packed, &L->f);
+    const int64_t mc = L->f.max_chunks;
+    const int64_t H = vheads(d), K = d->key_dim, V = d->value_dim, C = d->chunk;
+    const size_t es = d->qkv_dtype == GDN_DTYPE_BF16 ? 2 : 4;
+    const size_t blocks = (size_t)(H * mc);
+    size_t off = L->f.total;
+    L->ksr = off;
+    off = align256(off + blocks * C * K * es);
+    L->wt = off;
+    off = align256(off + blocks * C * K * es);
+    L->hs = off;
+    off = align256(off + blocks * K * V * es);
+    L->dhs = off;
+    off = align256(off + blocks * K * V * es);
+    L->vn = off;
+    off = align256(off + blocks * C * V * es);
+    L->dvn = off;
+    off = align256(off + blocks * C * V * es);
+    L->total = off;
+}
+
+gdn_status check_bwd_desc(const gdn_fwd_desc* d, bool packed) {
+    gdn_status s = check_desc(d, packed);
+    if (s != GDN_OK) return s;
+    if (d->gate != GDN_GATE_SCALAR)
+        return fail(GDN_ERR_UNSUPPORTED, "the backward pass implements the scalar gate");
+    if (d->num_v_heads != 0 && d->num_v_heads != d->num_heads)
+        return fail(GDN_ERR_UNSUPPORTED, "the backward pass has no grouped value heads");
+    if (d->qkv_dtype == GDN_DTYPE_F32 && (d->key_dim != 64 || d->value_dim != 64))
+        return fail(GDN_ERR_UNSUPPORTED, "fp32 backward needs K = V = 64");
+    return GDN_OK;
+}
+
 // gdn_chunk_fwd runs the fused kernel for these shapes; its workspace holds
 // only the per-sequence records of packed input
 bool fused_path(const gdn_fwd_desc* d) {
@@ -420,6 +462,172 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_desc* d, const void* q, const void* k, co
                          size_t workspace_bytes, void* stream) {
     return gdn_chunk_fwd_act(d, nullptr, q, k, v, beta, g, h0, cu_seqlens, o, ht, workspace,
                              workspace_bytes, stream);
+}
+
+gdn_status gdn_chunk_bwd_workspace(const gdn_fwd_desc* d, size_t* bytes) {
+    if (!bytes) return fail(GDN_ERR_NULL_ARG, "bytes is NULL");
+    const bool packed = d && d->num_seqs > 0;
+    gdn_status s = check_bwd_desc(d, packed);
+    if (s != GDN_OK) return s;
+    BwdLayout L;
+    bwd_layout(d, packed, &L);
+    *bytes = L.total;
+    return ok();
+}
+
+gdn_status gdn_chunk_bwd(const gdn_fwd_desc* d, const void* q, const void* k, const void* v,
+                         const float* beta, const float* g, const float* h0,
+                         const int64_t* cu_seqlens, const void* dout, const float* dht,
+                         void* dq, void* dk, void* dv, float* dbeta, float* dg, float* dh0,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    const bool packed = cu_seqlens != nullptr;
+    gdn_status s = check_bwd_desc(d, packed);
+    if (s != GDN_OK) return s;
+    if (!packed && d->num_seqs != 0)
+        return fail(GDN_ERR_BAD_SHAPE, "num_seqs must be 0 without cu_seqlens");
+    if (!q || !k || !v || !beta || !g || !dout || !dq || !dk || !dv || !dbeta || !dg || !workspace)
+        return fail(GDN_ERR_NULL_ARG,
+                    "q, k, v, beta, g, dout, dq, dk, dv, dbeta, dg and workspace are required");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv))
+        return fail(GDN_ERR_MISALIGNED, "q, k, v, dout, dq, dk, dv need 16-byte alignment");
+    if (!aligned4(beta) || !aligned4(g) || !aligned4(h0) || !aligned4(dht) || !aligned4(dbeta) ||
+        !aligned4(dg) || !aligned4(dh0) || !aligned8(cu_seqlens))
+        return fail(GDN_ERR_MISALIGNED, "float tensors need 4-byte, cu_seqlens 8-byte alignment");
+    if (((uintptr_t)workspace & 255u) != 0)
+        return fail(GDN_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+    BwdLayout L;
+    bwd_layout(d, packed, &L);
+    if (workspace_bytes < L.total)
+        return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes,
+                    L.total);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    const bool bf16 = d->qkv_dtype == GDN_DTYPE_BF16;
+    gdn::ChunkMap map;
+    map.max_chunks = L.f.max_chunks;
+    map.T = d->seq_len;
+    map.nt = (d->seq_len + d->chunk - 1) / d->chunk;
+    map.table = packed ? reinterpret_cast<const int4*>(ws + L.f.chunks) : nullptr;
+    map.seqs = packed ? reinterpret_cast<const int4*>(ws + L.f.seqs) : nullptr;
+    gdn::ChunkWs cw;
+    cw.gcum = reinterpret_cast<float*>(ws + L.f.gcum);
+    cw.w = ws + L.f.w;
+    cw.u = ws + L.f.u;
+    cw.qs = ws + L.f.qs;       // Qs^T in the backward mode
+    cw.ks = ws + L.f.ks;
+    cw.aqk = ws + L.f.aqk;     // Aqk^T in the backward mode
+    cw.ainv = reinterpret_cast<float*>(ws + L.f.ainv);
+    cw.ksr = ws + L.ksr;
+    cw.wt = ws + L.wt;
+    const int64_t H = d->num_heads;
+    const int64_t N = packed ? d->num_seqs : d->batch;
+    hipError_t e;
+    if (packed) {
+        gdn::TableLaunch t;
+        t.cu_seqlens = cu_seqlens;
+        t.N = d->num_seqs;
+        t.T = d->seq_len;
+        t.C = d->chunk;
+        t.table = const_cast<int4*>(map.table);
+        t.seqs = const_cast<int4*>(map.seqs);
+        t.max_chunks = map.max_chunks;
+        t.stream = st;
+        if ((e = gdn::launch_table(t)) != hipSuccess) return hip_fail(e, "chunk table launch");
+    }
+    const bool work = map.max_chunks > 0 && d->seq_len > 0;
+    if (work) {   // Step 1: U, W (and the other per-chunk operands) recomputed
+        gdn::IntraLaunch a;
+        a.q = q;
+        a.k = k;
+        a.v = v;
+        a.beta = beta;
+        a.g = g;
+        a.map = map;
+        a.ws = cw;
+        a.H = H;
+        a.Hq = H;
+        a.K = (int)d->key_dim;
+        a.V = (int)d->value_dim;
+        a.C = d->chunk;
+        a.scale = d->scale;
+        a.bf16 = bf16;
+        a.per_key = false;
+        a.bwd = true;
+        a.stream = st;
+        if ((e = gdn::launch_intra(a)) != hipSuccess) return hip_fail(e, "intra-chunk launch");
+    }
+    {   // Step 2: the chunk entry states and V_new recomputed
+        gdn::ScanLaunch a;
+        a.map = map;
+        a.ws = cw;
+        a.h0 = h0;
+        a.ht = nullptr;
+        a.o = nullptr;
+        a.hs = ws + L.hs;
+        a.vn = ws + L.vn;
+        a.N = N;
+        a.H = H;
+        a.K = (int)d->key_dim;
+        a.V = (int)d->value_dim;
+        a.C = d->chunk;
+        a.bf16 = bf16;
+        a.per_key = false;
+        a.stream = st;
+        if ((e = gdn::launch_scan(a)) != hipSuccess) return hip_fail(e, "state pass launch");
+    }
+    {   // Steps 3-4: the reverse state-gradient recurrence
+        gdn::BwdScanLaunch a;
+        a.map = map;
+        a.gcum = cw.gcum;
+        a.ksr = cw.ksr;
+        a.aqkt = cw.aqk;
+        a.qst = cw.qs;
+        a.wt = cw.wt;
+        a.dout = dout;
+        a.dht = dht;
+        a.dh0 = dh0;
+        a.dhs = ws + L.dhs;
+        a.dvn = ws + L.dvn;
+        a.N = N;
+        a.H = H;
+        a.K = (int)d->key_dim;
+        a.V = (int)d->value_dim;
+        a.C = d->chunk;
+        a.bf16 = bf16;
+        a.stream = st;
+        if ((e = gdn::launch_bwd_scan(a)) != hipSuccess) return hip_fail(e, "reverse pass launch");
+    }
+    if (work) {   // Steps 5-6 and the gate
+        gdn::BwdLocalLaunch a;
+        a.map = map;
+        a.q = q;
+        a.k = k;
+        a.v = v;
+        a.dout = dout;
+        a.beta = beta;
+        a.gcum = cw.gcum;
+        a.ainv = cw.ainv;
+        a.hs = ws + L.hs;
+        a.dhs = ws + L.dhs;
+        a.vn = ws + L.vn;
+        a.dvn = ws + L.dvn;
+        a.dq = dq;
+        a.dk = dk;
+        a.dv = dv;
+        a.dbeta = dbeta;
+        a.dg = dg;
+        a.H = H;
+        a.K = (int)d->key_dim;
+        a.V = (int)d->value_dim;
+        a.C = d->chunk;
+        a.scale = d->scale;
+        a.bf16 = bf16;
+        a.stream = st;
+        if ((e = gdn::launch_bwd_local(a)) != hipSuccess)
+            return hip_fail(e, "per-chunk gradient launch");
+    }
+    return ok();
 }
 
 gdn_status gdn_recurrent_step_act(const gdn_step_desc* d, const gdn_activation* act_in,

@@ -308,6 +308,26 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// Run one role of a serial chunk walk over its nch >= 1 steps (every wave
+// of the workgroup walks the same number of steps).  The PD+1 register
+// buffers rotate with the unrolled steps so each keeps a fixed register set:
+// R::step(j, cur, spare) consumes cur and loads step j+PD into spare.
+template <int PD, typename R>
+__device__ __forceinline__ void drive(R& r, int nch) {
+    typename R::Pre b[PD + 1];
+#pragma unroll
+    for (int q = 0; q < PD; ++q) r.issue(b[q], q);
+    __syncthreads();   // the initial carried value is published
+    int j = 0;
+    for (; j + PD + 1 <= nch; j += PD + 1) {
+#pragma unroll
+        for (int q = 0; q <= PD; ++q) r.step(j + q, b[q], b[(q + PD) % (PD + 1)]);
+    }
+#pragma unroll
+    for (int q = 0; q < PD; ++q)
+        if (j + q < nch) r.step(j + q, b[q], b[(q + PD) % (PD + 1)]);
+}
+
 constexpr float LOG2E = 1.4426950408889634f;
 
 // Input activations ("Gated Delta Network（GDN）" §3.1 eq. 5): the natural-log

@@ -52,6 +52,10 @@ struct ChunkWs {
     void* ks;      // [H][mc][C][K]   diag(gamma_C / gamma) K
     void* aqk;     // [H][mc][C][C]
     float* ainv;   // [H][mc][C][C] or nullptr
+    // backward mode of the intra stage: qs and aqk then hold Qs^T [K][C] and
+    // Aqk^T [C][C] in fragment order, and these two are written as well
+    void* ksr = nullptr;   // [H][mc][C][K]   Ks in fragment order (rows = tokens)
+    void* wt = nullptr;    // [H][mc][K][C]   W^T in fragment order
 };
 
 struct IntraLaunch {
@@ -65,6 +69,7 @@ struct IntraLaunch {
     int K, V, C;
     float scale;
     bool bf16, per_key;
+    bool bwd = false;       // write the backward operand orders (scalar gate only)
     hipStream_t stream;
 };
 
@@ -73,10 +78,47 @@ struct ScanLaunch {
     ChunkWs ws;
     const float* h0;
     float* ht;
-    void* o;
+    void* o;                // nullptr: the output is not computed
+    void* hs = nullptr;     // [H][mc][K][V] state entering each chunk, or nullptr
+    void* vn = nullptr;     // [H][mc][C][V] V_new of each chunk, or nullptr
     int64_t N, H;
     int K, V, C;
     bool bf16, per_key;
+    hipStream_t stream;
+};
+
+// Backward, reverse state-gradient pass: serial over the chunks of one
+// (sequence, head), last chunk first, parallel over value slices.
+struct BwdScanLaunch {
+    ChunkMap map;
+    const float* gcum;      // [H][mc][C] cumulative log2 gate
+    const void* ksr;        // Ks, Aqk^T, Qs^T, W^T per chunk in fragment order
+    const void* aqkt;
+    const void* qst;
+    const void* wt;
+    const void* dout;       // [B,T,H,V] output gradient
+    const float* dht;       // [N,H,K,V] or nullptr
+    float* dh0;             // [N,H,K,V] or nullptr
+    void* dhs;              // [H][mc][K][V] gradient of the state leaving each chunk
+    void* dvn;              // [H][mc][C][V] gradient of V_new
+    int64_t N, H;
+    int K, V, C;
+    bool bf16;
+    hipStream_t stream;
+};
+
+// Backward, per-chunk gradients: one workgroup per (chunk, head).
+struct BwdLocalLaunch {
+    ChunkMap map;
+    const void *q, *k, *v, *dout;
+    const float *beta, *gcum, *ainv;
+    const void *hs, *dhs, *vn, *dvn;
+    void *dq, *dk, *dv;
+    float *dbeta, *dg;
+    int64_t H;
+    int K, V, C;
+    float scale;
+    bool bf16;
     hipStream_t stream;
 };
 
@@ -115,5 +157,7 @@ hipError_t launch_intra(const IntraLaunch& a);
 hipError_t launch_scan(const ScanLaunch& a);
 bool fused_supported(const FusedLaunch& a);
 hipError_t launch_fused(const FusedLaunch& a);
+hipError_t launch_bwd_scan(const BwdScanLaunch& a);
+hipError_t launch_bwd_local(const BwdLocalLaunch& a);
 
 }  // namespace gdn

@@ -1,0 +1,828 @@
+// Backward pass of the chunked gated delta rule (scalar gate, C = 64).
+//
+// "阅读笔记：DeltaNet 在 FLA 中的代码实现笔记" (二、反向传播) lays the backward out
+// in six steps: recompute U, W (Step 1) and the chunk entry states (Step 2);
+// the intra-chunk part of dU (Step 3); a reverse recurrence for the state
+// gradient (Step 4); dQ, dK part 1, dW (Step 5); the WY backward for dV,
+// dK part 2 and dbeta (Step 6).  The pages write it for the ungated DeltaNet;
+// with the gate, per chunk of n <= C tokens (G the inclusive cumulative gate,
+// gamma = 2^G in log2 units, Gamma_ij = gamma_i / gamma_j for j <= i,
+// Ks = diag(gamma_C / gamma) K, Qs = scale diag(gamma) Q, T = (I + A)^{-1},
+// h the state entering the chunk and dH the gradient of the one leaving it):
+//   dVn  = Aqk^T dO + Ks dH                               (Steps 3-4)
+//   dH  <- gamma_C dH + Qs^T dO - W^T dVn                  (Step 4)
+//   dQ   = scale diag(gamma) dO h^T + Pm K,   Pm = scale (dO Vn^T) * Gamma (j <= i)
+//   dK   = diag(gamma_C / gamma) Vn dH^T + Pm^T Q          (Step 5)
+//        + diag(beta gamma) T^T dW + (Z + Z^T) K           (Step 6)
+//   dV   = diag(beta) T^T dVn,  dW = -dVn h^T
+//   dA   = -T^T (dVn (diag(beta) V)^T + dW (diag(beta gamma) K)^T) T^T,
+//   Z    = diag(beta) (dA * Gamma)  (strictly lower)
+//   dbeta_i = (T^T dVn)_i . v_i + gamma_i (T^T dW)_i . k_i + sum_j (dA * Gamma)_ij k_i . k_j
+// and the gate, which the pages do not cover: the gradient dG_i of the
+// cumulative gate collects every place where gamma_i, or a Gamma entry of
+// row or column i, enters (the output's state term, Aqk and A by rows minus
+// columns, W's diag(gamma), Ks, and gamma_C on the carried state and on Ks
+// for the last row), and dg = the reverse cumulative sum of dG in the chunk.
+//
+// Two kernels here; the forward intra stage (backward mode) and the forward
+// state pass (storing entry states and V_new) run before them:
+//   bwd_scan_kernel   the reverse recurrence, serial over chunks, one
+//                     workgroup per (sequence, head, 32-column value slice)
+//   bwd_local_kernel  every per-chunk gradient, one workgroup per (chunk, head)
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+// =====================================================================
+// Reverse state-gradient pass.  The mirror of the forward state pass: the
+// carried dH (K x VT, fp32) lives in MFMA accumulators of the dH waves; the
+// operands Ks, Aqk^T, Qs^T, W^T come from the intra stage in fragment order
+// (one coalesced 16-byte load per lane, issued PD steps ahead); dO is staged
+// row-major in LDS one chunk ahead and read with transposing loads.
+//   dV waves (C/32): token rows 32m..32m+31 of dVn = Ks dH + Aqk^T dO
+//   dH waves (K/32): key rows 32p..32p+31 of dH
+// Per step: dV waves read dH^T, publish dVn^T and the next chunk's dO,
+// barrier; dH waves add Qs^T dO (before it) and -W^T dVn (after it), decay,
+// publish dH^T, barrier.
+// =====================================================================
+
+constexpr int BSCAN_MAX_THREADS = 384;
+
+template <typename T, int K_, int V_, int VT_, int PD_>
+struct BScanCfg {
+    typedef T Elt;
+    typedef Mma<T> M;
+    typedef FragOrder<T> F;
+    static constexpr int K = K_, V = V_, C = 64, VT = VT_, PD = PD_;
+    static constexpr int KS = M::KSTEP, KG = F::KG, KSPG = KG / KS;
+    static constexpr int CT = VT / 16;
+    static constexpr int NVW = C / 32, NHW = K / 32, NW = NVW + NHW, NT = 64 * NW;
+    static constexpr int GK = K / KG, GC = C / KG;
+    static constexpr int P = 16 / sizeof(T);
+    static constexpr int LDH = K + P;      // dH^T   [VT][K]
+    static constexpr int LDV = C + P;      // dVn^T  [VT][C]
+    static constexpr int LDO = VT + P;     // dO     [C][VT], two buffers
+    static constexpr int NPC = VT * (int)sizeof(T) / 16;   // 16-byte pieces per dO row
+    static constexpr int PPL = 32 * NPC / 64;              // pieces per lane (32 rows a wave)
+    static constexpr size_t o_hT = 0;
+    static constexpr size_t o_Vn = o_hT + sizeof(T) * VT * LDH;
+    static constexpr size_t o_dO = o_Vn + sizeof(T) * VT * LDV;
+    static constexpr size_t bytes = o_dO + 2 * sizeof(T) * C * LDO;
+    static_assert(NT <= BSCAN_MAX_THREADS && PPL >= 1, "shape");
+};
+
+template <typename Cfg>
+struct BChain {
+    typedef typename Cfg::Elt T;
+    const BwdScanLaunch& a;
+    T *shT, *sVn, *sdO;
+    int64_t n, h, t0, len, c0;
+    int v0, nch, lane;
+
+    __device__ __forceinline__ BChain(const BwdScanLaunch& la, char* smem, int64_t chain, int vt)
+        : a(la) {
+        shT = reinterpret_cast<T*>(smem + Cfg::o_hT);
+        sVn = reinterpret_cast<T*>(smem + Cfg::o_Vn);
+        sdO = reinterpret_cast<T*>(smem + Cfg::o_dO);
+        n = chain / a.H;
+        h = chain - n * a.H;
+        v0 = vt * Cfg::VT;
+        lane = threadIdx.x & 63;
+        if (a.map.seqs) {
+            const int4 s = a.map.seqs[n];
+            t0 = s.x;
+            len = s.y;
+            c0 = s.z;
+        } else {
+            t0 = n * a.map.T;
+            len = a.map.T;
+            c0 = n * a.map.nt;
+        }
+        nch = (int)((len + Cfg::C - 1) / Cfg::C);
+        if (c0 + nch > a.map.max_chunks) nch = (int)max((int64_t)0, a.map.max_chunks - c0);
+    }
+    // chunk processed at step s (last chunk first), clamped into the chain
+    __device__ __forceinline__ int chunk_of(int s) const { return max(nch - 1 - s, 0); }
+    __device__ __forceinline__ int64_t blk(int j) const { return h * a.map.max_chunks + c0 + j; }
+    __device__ __forceinline__ T* dO_buf(int s) const { return sdO + (s & 1) * Cfg::C * Cfg::LDO; }
+    // B fragment (value tile ct, k-offset k0) from a transposed buffer X^T[VT][ld]
+    __device__ __forceinline__ typename Cfg::M::frag lds_frag(const T* x, int ld, int ct,
+                                                             int k0) const {
+        return Cfg::M::load(x + (16 * ct + (lane & 15)) * ld + k0, lane);
+    }
+    // raw dO pieces of rows 32m.. of chunk j (zero past the sequence end)
+    __device__ __forceinline__ void load_dO(u32x4* d, int m, int j, bool any) const {
+        const T* dout = static_cast<const T*>(a.dout);
+#pragma unroll
+        for (int p = 0; p < Cfg::PPL; ++p) {
+            const int i = lane + 64 * p, r = 32 * m + i / Cfg::NPC, cp = i % Cfg::NPC;
+            const int64_t tok = (int64_t)j * Cfg::C + r;
+            d[p] = u32x4{0u, 0u, 0u, 0u};
+            if (any && tok < len)
+                d[p] = *reinterpret_cast<const u32x4*>(dout + ((t0 + tok) * a.H + h) * Cfg::V + v0 +
+                                                      cp * (16 / sizeof(T)));
+        }
+    }
+    __device__ __forceinline__ void put_dO(const u32x4* d, int m, T* buf) const {
+#pragma unroll
+        for (int p = 0; p < Cfg::PPL; ++p) {
+            const int i = lane + 64 * p, r = 32 * m + i / Cfg::NPC, cp = i % Cfg::NPC;
+            *reinterpret_cast<u32x4*>(buf + r * Cfg::LDO + cp * (16 / sizeof(T))) = d[p];
+        }
+    }
+};
+
+// ---- dV waves: dVn rows 32m..32m+31, all VT columns
+template <typename Cfg>
+struct BScanDV {
+    typedef typename Cfg::Elt T;
+    typedef typename Cfg::M M;
+    typedef typename Cfg::F F;
+    static constexpr int K = Cfg::K, V = Cfg::V, C = Cfg::C, CT = Cfg::CT, GK = Cfg::GK,
+                         GC = Cfg::GC;
+    struct Pre {
+        u32x4 ks[2][GK];
+        u32x4 aq[2][GC];
+        u32x4 dnext[Cfg::PPL];   // dO of the chunk of the following step
+    };
+    const BChain<Cfg>& ch;
+    int m;
+
+    __device__ __forceinline__ void issue(Pre& p, int s) const {
+        const int64_t b = ch.blk(ch.chunk_of(s));
+        const u32x4* gk = reinterpret_cast<const u32x4*>(static_cast<const T*>(ch.a.ksr) + b * C * K);
+        const u32x4* ga = reinterpret_cast<const u32x4*>(static_cast<const T*>(ch.a.aqkt) + b * C * C);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int sg = 0; sg < GK; ++sg) p.ks[t][sg] = gk[((2 * m + t) * GK + sg) * 64 + ch.lane];
+#pragma unroll
+            for (int sg = 0; sg < GC; ++sg) p.aq[t][sg] = ga[((2 * m + t) * GC + sg) * 64 + ch.lane];
+        }
+        ch.load_dO(p.dnext, m, ch.nch - 2 - s, s + 1 < ch.nch);
+    }
+
+    // dO of the first step (the last chunk) into buffer 0
+    __device__ __forceinline__ void init() const {
+        u32x4 d[Cfg::PPL];
+        ch.load_dO(d, m, ch.nch - 1, ch.nch > 0);
+        ch.put_dO(d, m, ch.dO_buf(0));
+    }
+
+    __device__ __forceinline__ void step(int s, const Pre& cur, Pre& spare) const {
+        issue(spare, s + Cfg::PD);
+        const T* sdo = ch.dO_buf(s);
+        f32x4 acc[2][CT];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) acc[t][ct] = zero4();
+        // Ks dH
+#pragma unroll
+        for (int sg = 0; sg < GK; ++sg)
+#pragma unroll
+            for (int i = 0; i < Cfg::KSPG; ++i) {
+                const int k0 = sg * Cfg::KG + i * Cfg::KS;
+                const typename M::frag a0 = F::frag(cur.ks[0][sg], i);
+                const typename M::frag a1 = F::frag(cur.ks[1][sg], i);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const typename M::frag bh = ch.lds_frag(ch.shT, Cfg::LDH, ct, k0);
+                    acc[0][ct] = M::mma(a0, bh, acc[0][ct]);
+                    acc[1][ct] = M::mma(a1, bh, acc[1][ct]);
+                }
+            }
+        // + Aqk^T dO
+#pragma unroll
+        for (int sg = 0; sg < GC; ++sg)
+#pragma unroll
+            for (int i = 0; i < Cfg::KSPG; ++i) {
+                const int k0 = sg * Cfg::KG + i * Cfg::KS;
+                const typename M::frag a0 = F::frag(cur.aq[0][sg], i);
+                const typename M::frag a1 = F::frag(cur.aq[1][sg], i);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const typename M::frag bo = M::load_t(sdo + k0 * Cfg::LDO + 16 * ct, Cfg::LDO, ch.lane);
+                    acc[0][ct] = M::mma(a0, bo, acc[0][ct]);
+                    acc[1][ct] = M::mma(a1, bo, acc[1][ct]);
+                }
+            }
+        T* dvn = static_cast<T*>(ch.a.dvn) + ch.blk(ch.chunk_of(s)) * C * V;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                store_acc_t(ch.sVn + 16 * ct * Cfg::LDV + 16 * (2 * m + t), Cfg::LDV, ch.lane,
+                            acc[t][ct]);
+                store_acc(dvn + 16 * (2 * m + t) * V + ch.v0 + 16 * ct, V, ch.lane, acc[t][ct]);
+            }
+        // the other buffer was last read in the previous step
+        ch.put_dO(cur.dnext, m, ch.dO_buf(s + 1));
+        __syncthreads();   // dVn^T and the next dO published
+        __syncthreads();   // next dH^T published
+    }
+};
+
+// ---- dH waves: dH rows 32p..32p+31 (key tiles 2p, 2p+1), all VT columns
+template <typename Cfg>
+struct BScanDH {
+    typedef typename Cfg::Elt T;
+    typedef typename Cfg::M M;
+    typedef typename Cfg::F F;
+    static constexpr int K = Cfg::K, V = Cfg::V, C = Cfg::C, CT = Cfg::CT, GC = Cfg::GC;
+    struct Pre {
+        u32x4 qs[2][GC];
+        u32x4 wt[2][GC];
+        float d;   // log2 chunk-end decay
+    };
+    const BChain<Cfg>& ch;
+    int p;
+    f32x4 hacc[2][CT];
+
+    __device__ __forceinline__ int row(int r, int e) const {
+        return 16 * (2 * p + r) + acc_row(ch.lane, e);
+    }
+
+    __device__ __forceinline__ void issue(Pre& q, int s) const {
+        const int64_t b = ch.blk(ch.chunk_of(s));
+        const u32x4* gq = reinterpret_cast<const u32x4*>(static_cast<const T*>(ch.a.qst) + b * C * K);
+        const u32x4* gw = reinterpret_cast<const u32x4*>(static_cast<const T*>(ch.a.wt) + b * C * K);
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int sg = 0; sg < GC; ++sg) {
+                q.qs[r][sg] = gq[((2 * p + r) * GC + sg) * 64 + ch.lane];
+                q.wt[r][sg] = gw[((2 * p + r) * GC + sg) * 64 + ch.lane];
+            }
+        q.d = ch.a.gcum[b * C + (C - 1)];
+    }
+
+    // dH <- dht (or 0); publish dH^T
+    __device__ __forceinline__ void init() {
+        const float* dht = ch.a.dht ? ch.a.dht + (ch.n * ch.a.H + ch.h) * (int64_t)(K * V) : nullptr;
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    hacc[r][ct][e] =
+                        dht ? dht[row(r, e) * V + ch.v0 + 16 * ct + acc_col(ch.lane)] : 0.f;
+                store_acc_t(ch.shT + 16 * ct * Cfg::LDH + 16 * (2 * p + r), Cfg::LDH, ch.lane,
+                            hacc[r][ct]);
+            }
+    }
+
+    __device__ __forceinline__ void step(int s, const Pre& cur, Pre& spare) {
+        issue(spare, s + Cfg::PD);
+        {   // the gradient of the state leaving this chunk
+            T* dhs = static_cast<T*>(ch.a.dhs) + ch.blk(ch.chunk_of(s)) * K * V;
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    store_acc(dhs + 16 * (2 * p + r) * V + ch.v0 + 16 * ct, V, ch.lane, hacc[r][ct]);
+        }
+        const T* sdo = ch.dO_buf(s);
+        f32x4 acc[2][CT], neg[2][CT];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) acc[r][ct] = neg[r][ct] = zero4();
+        // Qs^T dO
+#pragma unroll
+        for (int sg = 0; sg < GC; ++sg)
+#pragma unroll
+            for (int i = 0; i < Cfg::KSPG; ++i) {
+                const int k0 = sg * Cfg::KG + i * Cfg::KS;
+                const typename M::frag a0 = F::frag(cur.qs[0][sg], i);
+                const typename M::frag a1 = F::frag(cur.qs[1][sg], i);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const typename M::frag bo = M::load_t(sdo + k0 * Cfg::LDO + 16 * ct, Cfg::LDO, ch.lane);
+                    acc[0][ct] = M::mma(a0, bo, acc[0][ct]);
+                    acc[1][ct] = M::mma(a1, bo, acc[1][ct]);
+                }
+            }
+        const float dec = exp2_hw(cur.d);
+        __syncthreads();   // dVn^T published
+        // W^T dVn
+#pragma unroll
+        for (int sg = 0; sg < GC; ++sg)
+#pragma unroll
+            for (int i = 0; i < Cfg::KSPG; ++i) {
+                const int k0 = sg * Cfg::KG + i * Cfg::KS;
+                const typename M::frag a0 = F::frag(cur.wt[0][sg], i);
+                const typename M::frag a1 = F::frag(cur.wt[1][sg], i);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const typename M::frag bv = ch.lds_frag(ch.sVn, Cfg::LDV, ct, k0);
+                    neg[0][ct] = M::mma(a0, bv, neg[0][ct]);
+                    neg[1][ct] = M::mma(a1, bv, neg[1][ct]);
+                }
+            }
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                hacc[r][ct] = dec * hacc[r][ct] + acc[r][ct] - neg[r][ct];
+                store_acc_t(ch.shT + 16 * ct * Cfg::LDH + 16 * (2 * p + r), Cfg::LDH, ch.lane,
+                            hacc[r][ct]);
+            }
+        __syncthreads();   // next dH^T published
+    }
+
+    __device__ __forceinline__ void finish() const {
+        if (!ch.a.dh0) return;
+        float* d0 = ch.a.dh0 + (ch.n * ch.a.H + ch.h) * (int64_t)(K * V);
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    d0[row(r, e) * V + ch.v0 + 16 * ct + acc_col(ch.lane)] = hacc[r][ct][e];
+    }
+};
+
+template <typename Cfg>
+__global__ __launch_bounds__(BSCAN_MAX_THREADS) void bwd_scan_kernel(BwdScanLaunch a) {
+    __shared__ __attribute__((aligned(16))) char smem[Cfg::bytes];
+    constexpr int NVT = Cfg::V / Cfg::VT;
+    // the workgroups of one (sequence, head) share an id modulo 8: one XCD
+    // and its L2 for the operands they all read
+    const int64_t bid = blockIdx.x;
+    const int vt = (int)((bid >> 3) % NVT);
+    const int64_t chain = (bid & 7) + 8 * ((bid >> 3) / NVT);
+    if (chain >= a.N * a.H) return;
+
+    const BChain<Cfg> ch(a, smem, chain, vt);
+    const int wave = wave_id();
+    if (wave < Cfg::NVW) {
+        BScanDV<Cfg> r{ch, wave};
+        if (ch.nch > 0) {
+            r.init();
+            drive<Cfg::PD>(r, ch.nch);
+        }
+    } else {
+        BScanDH<Cfg> r{ch, wave - Cfg::NVW, {}};
+        r.init();
+        if (ch.nch > 0) drive<Cfg::PD>(r, ch.nch);
+        r.finish();
+    }
+}
+
+template <typename Cfg>
+static hipError_t launch_bscan_cfg(const BwdScanLaunch& a) {
+    const int64_t chains = a.N * a.H;
+    const int64_t nblk = ((chains + 7) / 8) * 8 * (Cfg::V / Cfg::VT);
+    hipLaunchKernelGGL((bwd_scan_kernel<Cfg>), dim3((unsigned)nblk), dim3(Cfg::NT), 0, a.stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_scan(const BwdScanLaunch& a) {
+    if (a.C != 64) return hipErrorInvalidValue;
+    if (!a.bf16) {   // the fp32 backward covers K = V = 64 (the per-chunk kernel's LDS)
+        if (a.K == 64 && a.V == 64) return launch_bscan_cfg<BScanCfg<float, 64, 64, 32, 1>>(a);
+        return hipErrorInvalidValue;
+    }
+    if (a.K == 64 && a.V == 64) return launch_bscan_cfg<BScanCfg<bf16, 64, 64, 32, 2>>(a);
+    if (a.K == 64 && a.V == 128) return launch_bscan_cfg<BScanCfg<bf16, 64, 128, 32, 2>>(a);
+    if (a.K == 128 && a.V == 64) return launch_bscan_cfg<BScanCfg<bf16, 128, 64, 32, 2>>(a);
+    if (a.K == 128 && a.V == 128) return launch_bscan_cfg<BScanCfg<bf16, 128, 128, 32, 2>>(a);
+    return hipErrorInvalidValue;
+}
+
+// =====================================================================
+// Per-chunk gradients.  One 512-thread workgroup (8 waves) per (chunk,
+// head), everything in LDS; the products, by phase:
+//   A  dO h^T, Vn dH^T, -dVn h^T (C x K; h and dH fragments straight from
+//      HBM, each loaded by one wave), dO Vn^T, Q K^T, K K^T (C x C)
+//   B  Pm K, Pm^T Q, T^T dW (C x K), T^T dVn (C x V), dVn V^T, dW K^T (C x C)
+//   C  Y = dAinv T^T
+//   D  dA = -T^T Y, masked, gated, with the K K^T tile of phase A
+//   E  (Z + Z^T) K
+// A C x K (C x V) output tile stays in one wave's accumulators from phase A
+// to its store.  Per-row sums (dbeta, dG) are reduced across the 16 lanes of
+// a row inside a wave and kept per wave in LDS, then summed over the waves.
+// Rows past the chunk's n tokens are loaded as zero (and beta as 0), so they
+// add nothing to any valid row; they are never stored.
+// =====================================================================
+
+constexpr int BLOCAL_THREADS = 512;
+
+template <typename T, int K, int V>
+struct LocalSmem {
+    static constexpr int C = 64, NW = BLOCAL_THREADS / 64;
+    static constexpr int P = 16 / sizeof(T);
+    static constexpr int LDK = K + P, LDV = V + P, LDC = C + P;
+    static constexpr int LDX = (K > V ? K : V) + P;
+    static constexpr int LDN = LDV > LDC ? LDV : LDC;
+    static constexpr size_t o_Q = 0;
+    static constexpr size_t o_K = o_Q + sizeof(T) * C * LDK;
+    static constexpr size_t o_V = o_K + sizeof(T) * C * LDK;
+    static constexpr size_t o_DVN = o_V + sizeof(T) * C * LDV;
+    static constexpr size_t o_DO = o_DVN + sizeof(T) * C * LDV;   // dO [LDV], then dW [LDK]
+    static constexpr size_t o_VN = o_DO + sizeof(T) * C * LDX;    // Vn [LDV], then T [LDC]
+    static constexpr size_t o_PM = o_VN + sizeof(T) * C * LDN;    // Pm, then Y
+    static constexpr size_t o_DA = o_PM + sizeof(T) * C * LDC;    // dAinv, then Z + Z^T
+    static constexpr size_t o_G = o_DA + sizeof(T) * C * LDC;
+    static constexpr size_t o_E = o_G + 4 * C;
+    static constexpr size_t o_B = o_E + 4 * C;
+    static constexpr size_t o_RB = o_B + 4 * C;                   // [NW][C] dbeta partials
+    static constexpr size_t o_RG = o_RB + 4 * NW * C;             // [NW][C] dG partials
+    static constexpr size_t bytes = o_RG + 4 * NW * C;
+    static_assert(bytes <= 160 * 1024, "LDS");
+};
+
+// sum of each of the 4 rows a lane holds over the 16 lanes of its row group
+__device__ __forceinline__ f32x4 row_sum16(f32x4 v) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += __shfl_xor(v[e], off, 64);
+    return v;
+}
+// sum over the 16 rows of a tile for the lane's column (valid in every lane)
+__device__ __forceinline__ float col_sum16(f32x4 v) {
+    float x = v[0] + v[1] + v[2] + v[3];
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
+template <typename T, int K, int V>
+__global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunch a) {
+    typedef LocalSmem<T, K, V> L;
+    typedef Mma<T> M;
+    typedef typename M::frag Frag;
+    constexpr int C = 64, NW = L::NW, KS = M::KSTEP, EV = 16 / sizeof(T);
+    constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC;
+    constexpr int NKT = K / 16, NVT = V / 16;
+    constexpr int TPK = NKT * (C / 16) / NW, TPV = NVT * (C / 16) / NW;
+    static_assert(TPK >= 1 && TPV >= 1 && NW % NKT == 0 && NW % NVT == 0, "tile split");
+    __shared__ __attribute__((aligned(16))) char smem[L::bytes];
+    T* sQ = reinterpret_cast<T*>(smem + L::o_Q);
+    T* sK = reinterpret_cast<T*>(smem + L::o_K);
+    T* sV = reinterpret_cast<T*>(smem + L::o_V);
+    T* sDVN = reinterpret_cast<T*>(smem + L::o_DVN);
+    T* sDO = reinterpret_cast<T*>(smem + L::o_DO);
+    T* sDW = sDO;
+    T* sVN = reinterpret_cast<T*>(smem + L::o_VN);
+    T* sT = sVN;
+    T* sPM = reinterpret_cast<T*>(smem + L::o_PM);
+    T* sY = sPM;
+    T* sDA = reinterpret_cast<T*>(smem + L::o_DA);
+    T* sS = sDA;
+    float* sG = reinterpret_cast<float*>(smem + L::o_G);
+    float* sE = reinterpret_cast<float*>(smem + L::o_E);
+    float* sB = reinterpret_cast<float*>(smem + L::o_B);
+    float* sRB = reinterpret_cast<float*>(smem + L::o_RB);
+    float* sRG = reinterpret_cast<float*>(smem + L::o_RG);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int64_t H = a.H, h = blockIdx.x % H, c = blockIdx.x / H;
+    int64_t t0;
+    int n;
+    if (a.map.table) {
+        const int4 e = a.map.table[c];
+        t0 = e.x;
+        n = e.y;
+    } else {
+        const int64_t b = c / a.map.nt, j = c - b * a.map.nt;
+        t0 = b * a.map.T + j * C;
+        n = (int)min((int64_t)C, a.map.T - j * C);
+    }
+    if (n <= 0) return;
+    const int64_t blk = h * a.map.max_chunks + c;
+
+    // ---- loads (rows >= n as zero)
+    {
+        const T* q = static_cast<const T*>(a.q);
+        const T* k = static_cast<const T*>(a.k);
+        const T* v = static_cast<const T*>(a.v);
+        const T* dout = static_cast<const T*>(a.dout);
+        const T* vn = static_cast<const T*>(a.vn) + blk * C * V;
+        const T* dvn = static_cast<const T*>(a.dvn) + blk * C * V;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        for (int i = tid; i < C * K / EV; i += BLOCAL_THREADS) {
+            const int r = i / (K / EV), cv = (i % (K / EV)) * EV;
+            const int64_t g = ((t0 + r) * H + h) * K + cv;
+            *reinterpret_cast<u32x4*>(sQ + r * LDK + cv) = r < n ? *reinterpret_cast<const u32x4*>(q + g) : z;
+            *reinterpret_cast<u32x4*>(sK + r * LDK + cv) = r < n ? *reinterpret_cast<const u32x4*>(k + g) : z;
+        }
+        for (int i = tid; i < C * V / EV; i += BLOCAL_THREADS) {
+            const int r = i / (V / EV), cv = (i % (V / EV)) * EV;
+            const int64_t g = ((t0 + r) * H + h) * V + cv;
+            const bool in = r < n;
+            *reinterpret_cast<u32x4*>(sV + r * LDV + cv) = in ? *reinterpret_cast<const u32x4*>(v + g) : z;
+            *reinterpret_cast<u32x4*>(sDO + r * LDV + cv) = in ? *reinterpret_cast<const u32x4*>(dout + g) : z;
+            *reinterpret_cast<u32x4*>(sVN + r * LDV + cv) =
+                in ? *reinterpret_cast<const u32x4*>(vn + r * V + cv) : z;
+            *reinterpret_cast<u32x4*>(sDVN + r * LDV + cv) =
+                in ? *reinterpret_cast<const u32x4*>(dvn + r * V + cv) : z;
+        }
+        if (tid < C) {
+            const float G = a.gcum[blk * C + tid];
+            sG[tid] = G;
+            sE[tid] = exp2_hw(G);
+            sB[tid] = tid < n ? a.beta[(t0 + tid) * H + h] : 0.f;
+        }
+        for (int i = tid; i < 2 * NW * C; i += BLOCAL_THREADS) sRB[i] = 0.f;   // sRB, sRG
+    }
+    // T = (I + A)^{-1} (fp32, row-major) into registers: row tid/8, columns 8(tid%8)..
+    const int tr = tid / 8, tc = (tid % 8) * 8;
+    const float4 ta = *reinterpret_cast<const float4*>(a.ainv + blk * C * C + tr * C + tc);
+    const float4 tb = *reinterpret_cast<const float4*>(a.ainv + blk * C * C + tr * C + tc + 4);
+    __syncthreads();
+
+    const float Gend = sG[C - 1];
+    float* myRB = sRB + wave * C;
+    float* myRG = sRG + wave * C;
+    // row sums of the 4 rows r0 + 4(l/16) + e, added by one lane per row
+    auto add_rows = [&](float* dst, int r0, f32x4 x) {
+        x = row_sum16(x);
+        if ((lane & 15) == 0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[r0 + acc_row(lane, e)] += x[e];
+        }
+    };
+    // column sums of a 16x16 tile (column c0 + l%16), added (sign s) by lanes 0..15
+    auto add_cols = [&](float* dst, int c0, f32x4 x, float s) {
+        const float y = col_sum16(x);
+        if (lane < 16) dst[c0 + lane] += s * y;
+    };
+
+    // ================= phase A
+    const int kt = wave % NKT;
+    int rtk[TPK];
+#pragma unroll
+    for (int j = 0; j < TPK; ++j) rtk[j] = wave / NKT + (NW / NKT) * j;
+    f32x4 dq[TPK], dk[TPK], dw[TPK];
+    {
+        constexpr int NS = V / KS;
+        const T* hrow = static_cast<const T*>(a.hs) + blk * K * V + (16 * kt + (lane & 15)) * V;
+        const T* drow = static_cast<const T*>(a.dhs) + blk * K * V + (16 * kt + (lane & 15)) * V;
+        Frag bh[NS], bd[NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            bh[s] = M::load(hrow + s * KS, lane);
+            bd[s] = M::load(drow + s * KS, lane);
+        }
+        f32x4 dks[TPK];
+#pragma unroll
+        for (int j = 0; j < TPK; ++j) dq[j] = dks[j] = dw[j] = zero4();
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int j = 0; j < TPK; ++j) {
+                const int r = 16 * rtk[j] + (lane & 15);
+                dq[j] = M::mma(M::load(sDO + r * LDV + s * KS, lane), bh[s], dq[j]);
+                dks[j] = M::mma(M::load(sVN + r * LDV + s * KS, lane), bd[s], dks[j]);
+                dw[j] = M::mma(M::load(sDVN + r * LDV + s * KS, lane), bh[s], dw[j]);
+            }
+        // <dH, h>: each (key, value) element once, by the waves w < NKT
+        float hd = 0.f;
+        if (wave < NKT) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) hd += (float)bh[s][e] * (float)bd[s][e];
+                } else {
+                    hd += bh[s] * bd[s];
+                }
+            }
+        }
+        hd = wave_sum(hd);
+        // dQ's state term, dK's Ks term, and their gate terms
+        float stot = 0.f;
+        const int col = 16 * kt + acc_col(lane);
+#pragma unroll
+        for (int j = 0; j < TPK; ++j) {
+            f32x4 rg;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rtk[j] + acc_row(lane, e);
+                dq[j][e] *= a.scale * sE[r];
+                dks[j][e] *= exp2_hw(fminf(Gend - sG[r], 0.f));
+                const float s_ = Elem<T>::load(sK + r * LDK + col) * dks[j][e];
+                rg[e] = Elem<T>::load(sQ + r * LDK + col) * dq[j][e] - s_;
+                stot += s_;
+            }
+            add_rows(myRG, 16 * rtk[j], rg);
+            dk[j] = dks[j];
+        }
+        stot = wave_sum(stot);
+        if (lane == 0) myRG[C - 1] += stot + exp2_hw(Gend) * hd;
+    }
+    // C x C tiles of this wave: (I, J) = divmod(2 * wave + u, 4); lower ones only
+    f32x4 kk[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int id = 2 * wave + u, I = id / 4, J = id % 4;
+        kk[u] = zero4();
+        if (J > I) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                Elem<T>::store(sPM + (16 * I + acc_row(lane, e)) * LDC + 16 * J + acc_col(lane), 0.f);
+            continue;
+        }
+        const f32x4 dqk = mma_tile<T>(sDO + 16 * I * LDV, LDV, sVN + 16 * J * LDV, LDV, V, lane, zero4());
+        const f32x4 qk = mma_tile<T>(sQ + 16 * I * LDK, LDK, sK + 16 * J * LDK, LDK, K, lane, zero4());
+        kk[u] = mma_tile<T>(sK + 16 * I * LDK, LDK, sK + 16 * J * LDK, LDK, K, lane, zero4());
+        f32x4 pr;
+        const int j = 16 * J + acc_col(lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * I + acc_row(lane, e);
+            const float pm = j <= i ? a.scale * exp2_hw(fminf(sG[i] - sG[j], 0.f)) * dqk[e] : 0.f;
+            Elem<T>::store(sPM + i * LDC + j, pm);
+            pr[e] = pm * qk[e];
+        }
+        add_rows(myRG, 16 * I, pr);
+        add_cols(myRG, 16 * J, pr, -1.f);
+    }
+    __syncthreads();   // dO and Vn are read: their regions take dW and T
+#pragma unroll
+    for (int j = 0; j < TPK; ++j) store_acc(sDW + 16 * rtk[j] * LDK + 16 * kt, LDK, lane, -dw[j]);
+    {
+        const float x[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
+#pragma unroll
+        for (int e = 0; e < 8; e += EV)
+            *reinterpret_cast<uint4*>(sT + tr * LDC + tc + e) = Vec16<T>::pack(x + e);
+    }
+    __syncthreads();
+
+    // ================= phase B
+    {
+        f32x4 atdw[TPK];
+#pragma unroll
+        for (int j = 0; j < TPK; ++j) atdw[j] = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += KS) {
+            const Frag bk = M::load_t(sK + k0 * LDK + 16 * kt, LDK, lane);
+            const Frag bq = M::load_t(sQ + k0 * LDK + 16 * kt, LDK, lane);
+            const Frag bw = M::load_t(sDW + k0 * LDK + 16 * kt, LDK, lane);
+#pragma unroll
+            for (int j = 0; j < TPK; ++j) {
+                const int r0 = 16 * rtk[j];
+                dq[j] = M::mma(M::load(sPM + (r0 + (lane & 15)) * LDC + k0, lane), bk, dq[j]);
+                dk[j] = M::mma(M::load_t(sPM + k0 * LDC + r0, LDC, lane), bq, dk[j]);
+                atdw[j] = M::mma(M::load_t(sT + k0 * LDC + r0, LDC, lane), bw, atdw[j]);
+            }
+        }
+        const int col = 16 * kt + acc_col(lane);
+        T* gdq = static_cast<T*>(a.dq);
+#pragma unroll
+        for (int j = 0; j < TPK; ++j) {
+            f32x4 rb, rg;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rtk[j] + acc_row(lane, e);
+                const float bg = sB[r] * sE[r];
+                const float kx = Elem<T>::load(sK + r * LDK + col) * atdw[j][e];
+                dk[j][e] += bg * atdw[j][e];
+                rb[e] = sE[r] * kx;
+                rg[e] = bg * kx;
+                if (r < n) Elem<T>::store(gdq + ((t0 + r) * H + h) * K + col, dq[j][e]);
+            }
+            add_rows(myRB, 16 * rtk[j], rb);
+            add_rows(myRG, 16 * rtk[j], rg);
+        }
+    }
+    {   // dV = diag(beta) T^T dVn, and its dbeta term
+        const int vt = wave % NVT;
+        T* gdv = static_cast<T*>(a.dv);
+#pragma unroll
+        for (int j = 0; j < TPV; ++j) {
+            const int r0 = 16 * (wave / NVT + (NW / NVT) * j);
+            f32x4 x = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < C; k0 += KS)
+                x = M::mma(M::load_t(sT + k0 * LDC + r0, LDC, lane),
+                           M::load_t(sDVN + k0 * LDV + 16 * vt, LDV, lane), x);
+            const int col = 16 * vt + acc_col(lane);
+            f32x4 rb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = r0 + acc_row(lane, e);
+                rb[e] = x[e] * Elem<T>::load(sV + r * LDV + col);
+                if (r < n) Elem<T>::store(gdv + ((t0 + r) * H + h) * V + col, sB[r] * x[e]);
+            }
+            add_rows(myRB, r0, rb);
+        }
+    }
+    // dAinv = dVn (diag(beta) V)^T + dW (diag(beta gamma) K)^T
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int id = 2 * wave + u, I = id / 4, J = id % 4;
+        const f32x4 x1 = mma_tile<T>(sDVN + 16 * I * LDV, LDV, sV + 16 * J * LDV, LDV, V, lane, zero4());
+        const f32x4 x2 = mma_tile<T>(sDW + 16 * I * LDK, LDK, sK + 16 * J * LDK, LDK, K, lane, zero4());
+        const int j = 16 * J + acc_col(lane);
+        const float bj = sB[j], bgj = sB[j] * sE[j];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            Elem<T>::store(sDA + (16 * I + acc_row(lane, e)) * LDC + j, bj * x1[e] + bgj * x2[e]);
+    }
+    __syncthreads();
+
+    // ================= phase C: Y = dAinv T^T
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int id = 2 * wave + u, I = id / 4, J = id % 4;
+        const f32x4 y = mma_tile<T>(sDA + 16 * I * LDC, LDC, sT + 16 * J * LDC, LDC, C, lane, zero4());
+        store_acc(sY + 16 * I * LDC + 16 * J, LDC, lane, y);
+    }
+    __syncthreads();
+
+    // ================= phase D: dA = -T^T Y, strictly lower, gated
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int id = 2 * wave + u, I = id / 4, J = id % 4;
+        if (J > I) continue;
+        f32x4 x = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += KS)
+            x = M::mma(M::load_t(sT + k0 * LDC + 16 * I, LDC, lane),
+                       M::load_t(sY + k0 * LDC + 16 * J, LDC, lane), x);
+        const int j = 16 * J + acc_col(lane);
+        f32x4 rb, rr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * I + acc_row(lane, e);
+            const float dag = j < i ? -x[e] * exp2_hw(fminf(sG[i] - sG[j], 0.f)) : 0.f;
+            const float z = sB[i] * dag;
+            rb[e] = dag * kk[u][e];
+            rr[e] = z * kk[u][e];
+            // Z + Z^T, each position written once: (i, j) for j <= i, its
+            // mirror (j, i) for j < i (on a diagonal tile the upper half
+            // comes only from the mirrors)
+            if (j <= i) Elem<T>::store(sS + i * LDC + j, z);
+            if (j < i) Elem<T>::store(sS + j * LDC + i, z);
+        }
+        add_rows(myRB, 16 * I, rb);
+        add_rows(myRG, 16 * I, rr);
+        add_cols(myRG, 16 * J, rr, -1.f);
+    }
+    __syncthreads();
+
+    // ================= phase E: dK += (Z + Z^T) K; stores
+    {
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += KS) {
+            const Frag bk = M::load_t(sK + k0 * LDK + 16 * kt, LDK, lane);
+#pragma unroll
+            for (int j = 0; j < TPK; ++j)
+                dk[j] = M::mma(M::load(sS + (16 * rtk[j] + (lane & 15)) * LDC + k0, lane), bk, dk[j]);
+        }
+        const int col = 16 * kt + acc_col(lane);
+        T* gdk = static_cast<T*>(a.dk);
+#pragma unroll
+        for (int j = 0; j < TPK; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = 16 * rtk[j] + acc_row(lane, e);
+                if (r < n) Elem<T>::store(gdk + ((t0 + r) * H + h) * K + col, dk[j][e]);
+            }
+    }
+    __syncthreads();
+    // dbeta and dg = reverse cumulative sum of dG over the chunk
+    if (wave == 0) {
+        float db = 0.f, dG = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            db += sRB[w * C + lane];
+            dG += sRG[w * C + lane];
+        }
+        const float rev = __shfl(dG, C - 1 - lane, 64);
+        const float suf = wave_incl_scan(rev, lane);   // at lane l: sum of dG[C-1-l ..]
+        const int r = C - 1 - lane;
+        if (r < n) a.dg[(t0 + r) * H + h] = suf;
+        if (lane < n) a.dbeta[(t0 + lane) * H + h] = db;
+    }
+}
+
+template <typename T, int K, int V>
+static hipError_t launch_blocal_t(const BwdLocalLaunch& a) {
+    hipLaunchKernelGGL((bwd_local_kernel<T, K, V>), dim3((unsigned)(a.map.max_chunks * a.H)),
+                       dim3(BLOCAL_THREADS), 0, a.stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_local(const BwdLocalLaunch& a) {
+    if (a.C != 64) return hipErrorInvalidValue;
+    if (!a.bf16) {
+        // fp32 operands fit the LDS only at K = V = 64
+        if (a.K == 64 && a.V == 64) return launch_blocal_t<float, 64, 64>(a);
+        return hipErrorInvalidValue;
+    }
+    if (a.K == 64 && a.V == 64) return launch_blocal_t<bf16, 64, 64>(a);
+    if (a.K == 64 && a.V == 128) return launch_blocal_t<bf16, 64, 128>(a);
+    if (a.K == 128 && a.V == 64) return launch_blocal_t<bf16, 128, 64>(a);
+    if (a.K == 128 && a.V == 128) return launch_blocal_t<bf16, 128, 128>(a);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

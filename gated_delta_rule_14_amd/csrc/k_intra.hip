@@ -62,8 +62,9 @@ struct IntraSmem {
     static_assert(C * LDC * sizeof(T) <= C * LDA * sizeof(float), "A2 fits the A region");
 };
 
-template <typename T, int K, int V, int C, bool PK, bool STORE_AINV>
+template <typename T, int K, int V, int C, bool PK, bool STORE_AINV, bool BWD = false>
 __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
+    static_assert(!(BWD && PK), "the backward mode is for the scalar gate");
     typedef IntraSmem<T, K, V, C, PK> L;
     typedef Mma<T> M;
     constexpr int NT = INTRA_THREADS, NW = NT / 64;
@@ -199,54 +200,70 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
 
     // ---- outputs that need only G, Q, K, in MFMA fragment order (one task =
     // one 64-lane x 16-byte group): Qs = scale 2^{G} Q (rows = tokens) and
-    // Ks^T = (2^{G_C - G} K)^T (rows = keys), and the cumulative gate
+    // Ks^T = (2^{G_C - G} K)^T (rows = keys), and the cumulative gate.  The
+    // backward mode writes Ks (rows = tokens) and Qs^T (rows = keys) as well
+    // as Ks^T, and no Qs.
     {
         typedef FragOrder<T> F;
         constexpr int VE = F::VE, KG = F::KG;
         constexpr int NQG = (C / 16) * (K / KG), NKG = (K / 16) * (C / KG);
         T* gqs = static_cast<T*>(a.ws.qs) + blk * C * K;
         T* gks = static_cast<T*>(a.ws.ks) + blk * C * K;
-        for (int task = wave; task < NQG + NKG; task += NW) {
-            float f[VE];
-            if (task < NQG) {
-                const int rt = task / (K / KG), sg = task % (K / KG), r = 16 * rt + (lane & 15);
-                const T* src = sQ + r * LDK + KG * sg;
-                float x[VE];
-                if constexpr (sizeof(T) == 2) {
-                    const typename M::frag fr = M::load(src, lane);
+        T* gksr = BWD ? static_cast<T*>(a.ws.ksr) + blk * C * K : nullptr;
+        // group `task` of a token-row matrix  f(r) * X[r][d]  (X = sQ or sK)
+        auto row_group = [&](const T* sX, bool q_side, T* dst, int task) {
+            const int rt = task / (K / KG), sg = task % (K / KG), r = 16 * rt + (lane & 15);
+            const T* src = sX + r * LDK + KG * sg;
+            float x[VE], f[VE];
+            if constexpr (sizeof(T) == 2) {
+                const typename M::frag fr = M::load(src, lane);
 #pragma unroll
-                    for (int e = 0; e < VE; ++e) x[e] = (float)fr[e];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < VE; ++e) x[e] = Elem<T>::load(src + F::col(lane, e));
-                }
-#pragma unroll
-                for (int e = 0; e < VE; ++e) {
-                    const int d = KG * sg + F::col(lane, e);
-                    f[e] = a.scale * (PK ? exp2_hw(sG[r * K + d]) : sE[r]) * x[e];
-                }
-                *reinterpret_cast<uint4*>(gqs + ((int64_t)task * 64 + lane) * VE) =
-                    Vec16<T>::pack(f);
+                for (int e = 0; e < VE; ++e) x[e] = (float)fr[e];
             } else {
-                const int t = task - NQG, rt = t / (C / KG), sg = t % (C / KG);
-                const int kd = 16 * rt + (lane & 15);
-                float x[VE];
-                if constexpr (sizeof(T) == 2) {
-                    const typename M::frag fr = M::load_t(sK + KG * sg * LDK + 16 * rt, LDK, lane);
 #pragma unroll
-                    for (int e = 0; e < VE; ++e) x[e] = (float)fr[e];
-                } else {
+                for (int e = 0; e < VE; ++e) x[e] = Elem<T>::load(src + F::col(lane, e));
+            }
 #pragma unroll
-                    for (int e = 0; e < VE; ++e)
-                        x[e] = Elem<T>::load(sK + (KG * sg + F::col(lane, e)) * LDK + kd);
-                }
+            for (int e = 0; e < VE; ++e) {
+                const int d = KG * sg + F::col(lane, e);
+                f[e] = q_side ? a.scale * (PK ? exp2_hw(sG[r * K + d]) : sE[r]) * x[e]
+                              : (PK ? exp2_hw(fminf(sG[(C - 1) * K + d] - sG[r * K + d], 0.f))
+                                    : sF[r]) * x[e];
+            }
+            *reinterpret_cast<uint4*>(dst + ((int64_t)task * 64 + lane) * VE) = Vec16<T>::pack(f);
+        };
+        // group `t` of a key-row matrix  (f(tok) * X[tok][kd])^T
+        auto col_group = [&](const T* sX, bool q_side, T* dst, int t) {
+            const int rt = t / (C / KG), sg = t % (C / KG);
+            const int kd = 16 * rt + (lane & 15);
+            float x[VE], f[VE];
+            if constexpr (sizeof(T) == 2) {
+                const typename M::frag fr = M::load_t(sX + KG * sg * LDK + 16 * rt, LDK, lane);
 #pragma unroll
-                for (int e = 0; e < VE; ++e) {
-                    const int tok = KG * sg + F::col(lane, e);
-                    f[e] = (PK ? exp2_hw(fminf(sG[(C - 1) * K + kd] - sG[tok * K + kd], 0.f))
-                               : sF[tok]) * x[e];
-                }
-                *reinterpret_cast<uint4*>(gks + ((int64_t)t * 64 + lane) * VE) = Vec16<T>::pack(f);
+                for (int e = 0; e < VE; ++e) x[e] = (float)fr[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    x[e] = Elem<T>::load(sX + (KG * sg + F::col(lane, e)) * LDK + kd);
+            }
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                const int tok = KG * sg + F::col(lane, e);
+                f[e] = q_side ? a.scale * (PK ? exp2_hw(sG[tok * K + kd]) : sE[tok]) * x[e]
+                              : (PK ? exp2_hw(fminf(sG[(C - 1) * K + kd] - sG[tok * K + kd], 0.f))
+                                    : sF[tok]) * x[e];
+            }
+            *reinterpret_cast<uint4*>(dst + ((int64_t)t * 64 + lane) * VE) = Vec16<T>::pack(f);
+        };
+        constexpr int NTASK = NQG + NKG + (BWD ? NKG : 0);
+        for (int task = wave; task < NTASK; task += NW) {
+            if (task < NQG) {
+                if (BWD) row_group(sK, false, gksr, task);
+                else row_group(sQ, true, gqs, task);
+            } else if (task < NQG + NKG) {
+                col_group(sK, false, gks, task - NQG);
+            } else {
+                col_group(sQ, true, gqs, task - NQG - NKG);
             }
         }
         float* gg = a.ws.gcum + blk * C * (PK ? K : 1);
@@ -317,8 +334,9 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                         const int j = 16 * J + acc_row(lane, e);
                         const float x = a.scale * exp2_hw(fminf(gi - sG[j], 0.f)) * acc[J][e];
                         acc[J][e] = j <= i ? x : 0.f;
+                        if (BWD) Elem<T>::store(gaqk + FragOrder<T>::off(j, i, C), acc[J][e]);
                     }
-                    store4_frag(gaqk, i, 16 * J + 4 * (lane >> 4), C, acc[J]);
+                    if (!BWD) store4_frag(gaqk, i, 16 * J + 4 * (lane >> 4), C, acc[J]);
                 }
             }
         }
@@ -539,6 +557,15 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
 #pragma unroll
         for (int m = 0; m < WD; ++m)
             store4_frag(gw, i, 16 * (d0 + G * m) + 4 * (lane >> 4), K, aw[m]);
+        if (BWD) {   // W^T in fragment order as well (rows = keys)
+            T* gwt = static_cast<T*>(a.ws.wt) + blk * C * K;
+#pragma unroll
+            for (int m = 0; m < WD; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    Elem<T>::store(gwt + FragOrder<T>::off(16 * (d0 + G * m) + 4 * (lane >> 4) + e, i, C),
+                                   aw[m][e]);
+        }
 #pragma unroll
         for (int m = 0; m < UD; ++m)
             store4(gu + acc_order_off(16 * I + acc_row(lane, 0), 16 * (d0 + G * m) + acc_col(lane), V),
@@ -549,6 +576,15 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
 template <typename T, int K, int V, int C, bool PK>
 static hipError_t launch_intra_t(const IntraLaunch& a) {
     dim3 grid((unsigned)(a.map.max_chunks * a.H));
+    if (a.bwd) {
+        if constexpr (!PK) {
+            if (!a.ws.ainv || !a.ws.ksr || !a.ws.wt) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((intra_kernel<T, K, V, C, false, true, true>), grid,
+                               dim3(INTRA_THREADS), 0, a.stream, a);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
     if (a.ws.ainv)
         hipLaunchKernelGGL((intra_kernel<T, K, V, C, PK, true>), grid, dim3(INTRA_THREADS), 0,
                            a.stream, a);

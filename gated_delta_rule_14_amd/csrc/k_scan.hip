@@ -27,6 +27,11 @@
 // waves finish and store their rows of O, H waves decay and update h and
 // publish h^T, barrier.
 //
+// For the backward pass the same walk runs without the output (o == nullptr:
+// the O waves only keep the barriers) and stores, per chunk, the state that
+// enters it and V_new ("阅读笔记：DeltaNet 在 FLA 中的代码实现笔记", backward
+// Steps 1-2: the states and U, W are recomputed, not kept from the forward).
+//
 // The workgroups of one (sequence, head) get ids equal modulo 8, so the
 // hardware's round-robin over the 8 XCDs puts them on one XCD and they share
 // W, Qs, Ks and Aqk through its L2.
@@ -106,25 +111,6 @@ struct ScanChain {
     }
 };
 
-// Run one role over the chain (nch >= 1).  The PD+1 register buffers rotate
-// with the unrolled steps so each keeps a fixed register set: R::step(j,
-// cur, spare) consumes cur and loads chunk j+PD into spare.
-template <int PD, typename R>
-__device__ __forceinline__ void drive(R& r, int nch) {
-    typename R::Pre b[PD + 1];
-#pragma unroll
-    for (int q = 0; q < PD; ++q) r.issue(b[q], q);
-    __syncthreads();   // the initial h^T is published
-    int j = 0;
-    for (; j + PD + 1 <= nch; j += PD + 1) {
-#pragma unroll
-        for (int q = 0; q <= PD; ++q) r.step(j + q, b[q], b[(q + PD) % (PD + 1)]);
-    }
-#pragma unroll
-    for (int q = 0; q < PD; ++q)
-        if (j + q < nch) r.step(j + q, b[q], b[(q + PD) % (PD + 1)]);
-}
-
 // ---- V waves: V_new rows 32m..32m+31 (token tiles 2m, 2m+1), all VT columns
 template <typename Cfg>
 struct ScanV {
@@ -176,6 +162,7 @@ struct ScanV {
                     acc[1][ct] = M::mma(a1, bh, acc[1][ct]);
                 }
             }
+        T* vn = ch.a.vn ? static_cast<T*>(ch.a.vn) + ch.blk(j) * C * V : nullptr;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -183,6 +170,9 @@ struct ScanV {
                 const f32x4 u = Quad<T>::get(cur.u[t][ct]);
                 store_acc_t(ch.sVn + 16 * ct * Cfg::LDV + 16 * (2 * m + t), Cfg::LDV, ch.lane,
                             u - acc[t][ct]);
+                if (vn)
+                    store_acc(vn + 16 * (2 * m + t) * V + ch.v0 + 16 * ct, V, ch.lane,
+                              u - acc[t][ct]);
             }
         __syncthreads();   // V_new^T published
         __syncthreads();   // next h^T published
@@ -329,6 +319,14 @@ struct ScanH {
 
     __device__ __forceinline__ void step(int j, const Pre& cur, Pre& spare) {
         issue(spare, j + Cfg::PD);
+        if (ch.a.hs) {   // the state entering chunk j
+            T* hs = static_cast<T*>(ch.a.hs) + ch.blk(j) * K * V;
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    store_acc(hs + 16 * (2 * p + r) * V + ch.v0 + 16 * ct, V, ch.lane, hacc[r][ct]);
+        }
         float dec[2][4];
 #pragma unroll
         for (int r = 0; r < 2; ++r)
@@ -377,6 +375,16 @@ struct ScanH {
     }
 };
 
+// ---- O waves of a walk without output: only the barriers of a step
+struct ScanNop {
+    struct Pre {};
+    __device__ __forceinline__ void issue(Pre&, int) const {}
+    __device__ __forceinline__ void step(int, const Pre&, Pre&) const {
+        __syncthreads();
+        __syncthreads();
+    }
+};
+
 template <typename Cfg>
 __global__ __launch_bounds__(SCAN_MAX_THREADS) void scan_kernel(ScanLaunch a) {
     __shared__ __attribute__((aligned(16))) char smem[Cfg::bytes];
@@ -390,6 +398,9 @@ __global__ __launch_bounds__(SCAN_MAX_THREADS) void scan_kernel(ScanLaunch a) {
     const int wave = wave_id();
     if (wave < Cfg::NVW) {
         ScanV<Cfg> r{ch, wave};
+        if (ch.nch > 0) drive<Cfg::PD>(r, ch.nch);
+    } else if (wave < Cfg::NVW + Cfg::NOW && !a.o) {
+        ScanNop r;
         if (ch.nch > 0) drive<Cfg::PD>(r, ch.nch);
     } else if (wave == Cfg::NVW) {
         ScanO<Cfg, 0> r{ch};

@@ -36,7 +36,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-__all__ = ["PrefillSpec", "DecodeSpec", "PREFILL", "DECODE", "make_prefill",
+__all__ = ["PrefillSpec", "DecodeSpec", "PREFILL", "DECODE", "make_prefill", "make_grads",
            "make_decode", "prefill_spec", "draw_lengths", "flops_per_token_head"]
 
 
@@ -121,7 +121,7 @@ def _draw_lengths(rng, spec: PrefillSpec):
 
 
 BLOCK = 4096
-TAG = {"q": 1, "k": 2, "v": 3, "beta": 4, "g": 5, "h0": 6}
+TAG = {"q": 1, "k": 2, "v": 3, "beta": 4, "g": 5, "h0": 6, "do": 7, "dht": 8}
 _THREADS = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
                       else (os.cpu_count() or 1)))
 
@@ -223,6 +223,28 @@ def make_prefill(spec, seed: int = None, logits: bool = False) -> dict:
         out["A_log"] = torch.from_numpy(np.log(A).astype(np.float32))
         out["dt_bias"] = torch.full((H, K) if per_key else (H,), spec.gate_shift, dtype=torch.float32)
     return out
+
+
+def make_grads(d: dict, seed: int = None, dht_std: Optional[float] = 0.1) -> dict:
+    """Upstream gradients for a backward call on the prefill workload d (as
+    returned by make_prefill): 'do' shaped like v, float32 standard normals
+    rounded to the q/k/v dtype, drawn per sequence and block like v (tag
+    'do'); 'dht' [N, H, K, V] float32 N(0, dht_std^2), one stream per
+    sequence (tag 'dht'), or None when dht_std is None."""
+    spec = d["spec"]
+    seed = 0 if seed is None else seed
+    lengths = d["lengths"]
+    H, K, V = spec.H, spec.K, spec.V
+    parts = [_cast(_blocked(seed, n, "do", L, (H, V), "f32"), spec.dtype)
+             for n, L in enumerate(lengths)]
+    do = torch.cat(parts, 0).unsqueeze(0) if d["cu_seqlens"] is not None else torch.stack(parts, 0)
+    dht = None
+    if dht_std is not None:
+        dht = torch.empty((len(lengths), H, K, V), dtype=torch.float32)
+        for n in range(len(lengths)):
+            dht[n] = torch.from_numpy(_stream(seed, n, "dht", 0).standard_normal(
+                (H, K, V), dtype=np.float32) * np.float32(dht_std))
+    return dict(do=do, dht=dht)
 
 
 def draw_lengths(spec, seed: int = None):

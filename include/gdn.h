@@ -1,5 +1,6 @@
 /*
- * gdn.h -- C ABI of the MI355X (gfx950) gated delta rule forward library.
+ * gdn.h -- C ABI of the MI355X (gfx950) gated delta rule library: the
+ * chunked forward, the single-token decode step and the chunked backward.
  *
  * The operation (the "gated delta rule"):
  *
@@ -48,7 +49,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef int32_t gdn_status;
 enum {
@@ -309,6 +310,41 @@ gdn_status gdn_recurrent_step_act(const gdn_step_desc *d, const gdn_activation *
                                   const void *q, const void *k, const void *v,
                                   const float *beta, const float *g,
                                   float *state, void *o, void *stream);
+
+/*
+ * Backward pass of the chunked forward ("阅读笔记：DeltaNet 在 FLA 中的代码实现
+ * 笔记", 二、反向传播, Steps 1-6, written there for the ungated DeltaNet; the
+ * gate enters by the chain rule through the same chunked forward).  Given
+ * the gradient dout of o and dht of ht, it writes the gradients of
+ * L = <dout, o> + <dht, ht> with respect to q, k, v, beta, g and h0.  The
+ * forward quantities (U, W, the chunk entry states) are recomputed from the
+ * inputs, as the pages' Steps 1-2 do; nothing is kept from a forward call.
+ *
+ *   q, k, v, beta, g, h0, cu_seqlens, scale: as for gdn_chunk_fwd
+ *   dout       [B, T, H, V]  qkv_dtype
+ *   dht        [N, H, K, V]  float, or NULL: no final-state gradient
+ *   dq, dk     [B, T, H, K]  qkv_dtype, written
+ *   dv         [B, T, H, V]  qkv_dtype, written
+ *   dbeta      [B, T, H]     float, written
+ *   dg         [B, T, H]     float, written: the gradient of the natural-log gate
+ *   dh0        [N, H, K, V]  float, written, or NULL: not computed
+ *
+ * Supported: the scalar gate, no grouped value heads (num_v_heads 0 or H),
+ * chunk 64; bf16 q/k/v with K, V in {64, 128}, fp32 with K = V = 64.  Other
+ * shapes give GDN_ERR_UNSUPPORTED.  dout, dq, dk, dv need 16-byte alignment.
+ * The workspace (gdn_chunk_bwd_workspace bytes, 256-byte aligned) holds the
+ * recomputed per-chunk quantities, the chunk entry states and the state
+ * gradients; its contents on return are unspecified.  No output may alias an
+ * input or another output.
+ */
+gdn_status gdn_chunk_bwd_workspace(const gdn_fwd_desc *d, size_t *bytes);
+gdn_status gdn_chunk_bwd(const gdn_fwd_desc *d,
+                         const void *q, const void *k, const void *v,
+                         const float *beta, const float *g, const float *h0,
+                         const int64_t *cu_seqlens,
+                         const void *dout, const float *dht,
+                         void *dq, void *dk, void *dv, float *dbeta, float *dg, float *dh0,
+                         void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

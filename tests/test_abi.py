@@ -152,3 +152,37 @@ def test_activation_rejects_before_launch(lib):
         assert fn(1 | 2, FAKE, None) == 1        # ... and dt_bias
         assert fn(1, odd, FAKE) == 6             # 4-byte alignment
         assert lib.gdn_last_error().decode() != ""
+
+
+def test_chunk_bwd_rejects_before_launch(lib):
+    """The backward's shape limits and argument checks fail before any launch."""
+    n = ctypes.c_size_t()
+    ws = lambda d: lib.gdn_chunk_bwd_workspace(ctypes.byref(d), ctypes.byref(n))  # noqa: E731
+    assert ws(_desc()) == 0 and n.value > 0
+    assert ws(_desc(gate=1)) == 4                       # scalar gate only
+    assert ws(_desc(num_v_heads=8)) == 4                # no grouped value heads
+    assert ws(_desc(num_v_heads=4)) == 0                # H_V == H is allowed
+    assert ws(_desc(qkv_dtype=0)) == 4                  # fp32 needs K = V = 64
+    assert ws(_desc(qkv_dtype=0, key_dim=64, value_dim=64)) == 0
+    assert ws(_desc(chunk=32)) == 4
+    # the workspace grows with the per-chunk states: above the forward layout
+    assert n.value > gdn.workspace_layout(_desc(qkv_dtype=0, key_dim=64, value_dim=64)).total
+    d = _desc()
+
+    def bwd(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=FAKE, h0=None, cu=None, do=FAKE, dht=None,
+                 dq=FAKE, dk=FAKE, dv=FAKE, dbeta=FAKE, dg=FAKE, dh0=None, ws=FAKE, wsb=1 << 40)
+        a.update(kw)
+        return lib.gdn_chunk_bwd(ctypes.byref(kw.pop("desc", d)), a["q"], a["k"], a["v"], a["beta"],
+                                 a["g"], a["h0"], a["cu"], a["do"], a["dht"], a["dq"], a["dk"],
+                                 a["dv"], a["dbeta"], a["dg"], a["dh0"], a["ws"], a["wsb"], None)
+    for name in ("q", "do", "dq", "dk", "dv", "dbeta", "dg", "ws"):
+        assert bwd(**{name: None}) == 1, name
+    for name in ("q", "do", "dq", "dv"):
+        assert bwd(**{name: MIS}) == 6, name
+    assert bwd(dht=ctypes.c_void_p((1 << 20) + 2)) == 6
+    assert bwd(ws=ctypes.c_void_p((1 << 20) + 64)) == 6
+    assert bwd(wsb=1024) == 5
+    assert bwd(desc=_desc(gate=1)) == 4
+    assert bwd(desc=_desc(batch=1), cu=FAKE) == 2
+    assert lib.gdn_last_error().decode() != ""
