@@ -9,9 +9,11 @@ and states, inputs resident in HBM.  `value` is tokens/s (B*T tokens per
 step).  The same run times the kernel of every step with HIP events on its
 stream, the two-stage path (intra-chunk stage + state pass) for comparison,
 the decode step (256 sequences x 32 heads, fp32 state in place, 64 steps),
-and the fp64 CPU oracle on the host cores.
+the chunked backward on the prefill workload (gradients of q, k, v, beta, g
+and h0 from seeded dO and dht), and the fp64 CPU oracle on the host cores.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-decode]
+                  [--no-backward]
 """
 from __future__ import annotations
 
@@ -204,6 +206,42 @@ def bench_decode(args, gdn):
                          "traffic": measured_traffic("step_kernel")}}
 
 
+def bench_backward(args, gdn, d):
+    """The chunked backward on the prefill workload: four kernels per call
+    (intra-chunk recompute, state recompute, reverse state-gradient pass,
+    per-chunk gradients), timed with HIP events over back-to-back calls."""
+    spec = d["spec"]
+    gr = gdn_synth.make_grads(d, 1)
+    x = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    q, k, v, beta, g, h0 = (x[n] for n in ("q", "k", "v", "beta", "g", "h0"))
+    do, dht = gr["do"].cuda(), gr["dht"].cuda()
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dbeta=torch.empty_like(beta), dg=torch.empty_like(g), dh0=torch.empty_like(h0))
+    desc = gdn.fwd_desc(q, v, "scalar", spec.chunk, d["scale"])
+    ws = torch.empty(gdn.bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+
+    def call():
+        gdn.chunk_bwd(q, k, v, beta, g, do, d["scale"], h0=h0, dht=dht, workspace=ws, out=out)
+
+    for _ in range(max(args.warmup // 10, 5)):
+        call()
+    reps = max(args.steps // 5, 5)
+    t = events_time(call, reps)
+    th = spec.B * spec.T * spec.H
+    es = 2 if spec.dtype == "bf16" else 4
+    state = 4 * spec.K * spec.V * spec.H * spec.B
+    # inputs q, k, v, dO, beta, g, h0, dht; outputs dq, dk, dv, dbeta, dg, dh0
+    alg_bytes = th * ((2 * spec.K + 2 * spec.V) * es + 8) + 2 * state + \
+        th * ((2 * spec.K + spec.V) * es + 8) + state
+    flops = gdn_synth.bwd_flops_per_token_head(spec.K, spec.V, spec.chunk) * th
+    log("backward %.1f us per call" % (t * 1e6))
+    return {"workload": spec.name, "us_per_call": t * 1e6, "calls": reps,
+            "tokens_per_s": spec.B * spec.T / t, "alg_flops": flops,
+            "TFLOPs": flops / t / 1e12, "frac_mfma_bf16": flops / t / BF16_PEAK,
+            "alg_bytes": alg_bytes, "GBps": alg_bytes / t / 1e9, "frac_hbm": alg_bytes / t / HBM_PEAK,
+            "workspace_bytes": ws.numel()}
+
+
 def cpu_baseline(d, min_s=10.0):
     import oracle
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
@@ -231,6 +269,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (a known-size kernel to scale "
                          "hardware byte counters by)")
@@ -251,6 +290,7 @@ def main():
         del src, dst
     spec, dt, roof, path, kernels, two_stage, d = bench_prefill(args, gdn)
     decode = None if args.no_decode else bench_decode(args, gdn)
+    backward = None if args.no_backward else bench_backward(args, gdn, d)
     cpu = None if args.no_cpu else cpu_baseline(d)
     line = {
         "metric": METRIC,
@@ -274,6 +314,7 @@ def main():
         "kernels": kernels,
         "two_stage": two_stage,
         "decode": decode,
+        "backward": backward,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line), flush=True)

@@ -404,8 +404,8 @@ hipError_t launch_bwd_scan(const BwdScanLaunch& a) {
 //   D  dA = -T^T Y, masked, gated, with the K K^T tile of phase A
 //   E  (Z + Z^T) K
 // A C x K (C x V) output tile stays in one wave's accumulators from phase A
-// to its store.  Per-row sums (dbeta, dG) are reduced across the 16 lanes of
-// a row inside a wave and kept per wave in LDS, then summed over the waves.
+// to its store.  Per-row sums (dbeta, dG) are reduced inside a wave and kept
+// per wave in LDS, then summed over the waves.
 // Rows past the chunk's n tokens are loaded as zero (and beta as 0), so they
 // add nothing to any valid row; they are never stored.
 // =====================================================================
@@ -436,17 +436,27 @@ struct LocalSmem {
     static_assert(bytes <= 160 * 1024, "LDS");
 };
 
-// sum of each of the 4 rows a lane holds over the 16 lanes of its row group
+// Sum over the 16 lanes of each DPP row (lanes 16g .. 16g+15) of each of the
+// 4 values a lane holds: an inclusive scan by row shifts, whose total lands
+// in the row's last lane (l % 16 == 15).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ f32x4 row_sum16(f32x4 v) {
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += __shfl_xor(v[e], off, 64);
+    for (int e = 0; e < 4; ++e) {
+        float x = v[e];
+        x = dpp_add<0x111>(x);   // row_shr:1
+        x = dpp_add<0x112>(x);   // row_shr:2
+        x = dpp_add<0x114>(x);   // row_shr:4
+        x = dpp_add<0x118>(x);   // row_shr:8
+        v[e] = x;
+    }
     return v;
 }
-// sum over the 16 rows of a tile for the lane's column (valid in every lane)
-__device__ __forceinline__ float col_sum16(f32x4 v) {
-    float x = v[0] + v[1] + v[2] + v[3];
+// Sum over the 4 lanes l % 16 == c of one value each (valid in every lane).
+__device__ __forceinline__ float sum_groups(float x) {
     x += __shfl_xor(x, 16, 64);
     x += __shfl_xor(x, 32, 64);
     return x;
@@ -497,6 +507,28 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
     if (n <= 0) return;
     const int64_t blk = h * a.map.max_chunks + c;
 
+    // This wave's C x K output tiles: key tile kt and token tiles rtk[j].  They
+    // are computed transposed (MFMA operands swapped), so lane l holds token
+    // 16 rtk[j] + l%16 and its 4 consecutive keys kc .. kc+3: per-token sums
+    // are in-lane plus two shuffles, and rows move as 8- (bf16) or 16-byte
+    // vectors.  C x V tiles likewise.
+    const int kt = wave % NKT, tl = lane & 15, kc = 16 * kt + 4 * (lane >> 4);
+    int rtk[TPK];
+#pragma unroll
+    for (int j = 0; j < TPK; ++j) rtk[j] = wave / NKT + (NW / NKT) * j;
+
+    // h and dH rows of key tile kt for phase A, issued first (the longest wait)
+    constexpr int NS = V / KS;
+    Frag bh[NS], bd[NS];
+    {
+        const T* hrow = static_cast<const T*>(a.hs) + blk * K * V + (16 * kt + tl) * V;
+        const T* drow = static_cast<const T*>(a.dhs) + blk * K * V + (16 * kt + tl) * V;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            bh[s] = M::load(hrow + s * KS, lane);
+            bd[s] = M::load(drow + s * KS, lane);
+        }
+    }
     // ---- loads (rows >= n as zero)
     {
         const T* q = static_cast<const T*>(a.q);
@@ -540,36 +572,29 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
     const float Gend = sG[C - 1];
     float* myRB = sRB + wave * C;
     float* myRG = sRG + wave * C;
-    // row sums of the 4 rows r0 + 4(l/16) + e, added by one lane per row
+    // C x C tile (rows 16 I + 4(l/16) + e, column 16 J + l%16): row sums,
+    // added by the last lane of each row group
     auto add_rows = [&](float* dst, int r0, f32x4 x) {
         x = row_sum16(x);
-        if ((lane & 15) == 0) {
+        if ((lane & 15) == 15) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) dst[r0 + acc_row(lane, e)] += x[e];
         }
     };
-    // column sums of a 16x16 tile (column c0 + l%16), added (sign s) by lanes 0..15
+    // ... column sums (sign s), added by lanes 0..15
     auto add_cols = [&](float* dst, int c0, f32x4 x, float s) {
-        const float y = col_sum16(x);
+        const float y = sum_groups(x[0] + x[1] + x[2] + x[3]);
         if (lane < 16) dst[c0 + lane] += s * y;
+    };
+    // transposed tile of token tile r0: this lane's partial x of token r0 + l%16
+    auto add_tok = [&](float* dst, int r0, float x) {
+        x = sum_groups(x);
+        if (lane < 16) dst[r0 + lane] += x;
     };
 
     // ================= phase A
-    const int kt = wave % NKT;
-    int rtk[TPK];
-#pragma unroll
-    for (int j = 0; j < TPK; ++j) rtk[j] = wave / NKT + (NW / NKT) * j;
     f32x4 dq[TPK], dk[TPK], dw[TPK];
     {
-        constexpr int NS = V / KS;
-        const T* hrow = static_cast<const T*>(a.hs) + blk * K * V + (16 * kt + (lane & 15)) * V;
-        const T* drow = static_cast<const T*>(a.dhs) + blk * K * V + (16 * kt + (lane & 15)) * V;
-        Frag bh[NS], bd[NS];
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            bh[s] = M::load(hrow + s * KS, lane);
-            bd[s] = M::load(drow + s * KS, lane);
-        }
         f32x4 dks[TPK];
 #pragma unroll
         for (int j = 0; j < TPK; ++j) dq[j] = dks[j] = dw[j] = zero4();
@@ -577,10 +602,10 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
         for (int s = 0; s < NS; ++s)
 #pragma unroll
             for (int j = 0; j < TPK; ++j) {
-                const int r = 16 * rtk[j] + (lane & 15);
-                dq[j] = M::mma(M::load(sDO + r * LDV + s * KS, lane), bh[s], dq[j]);
-                dks[j] = M::mma(M::load(sVN + r * LDV + s * KS, lane), bd[s], dks[j]);
-                dw[j] = M::mma(M::load(sDVN + r * LDV + s * KS, lane), bh[s], dw[j]);
+                const int r = 16 * rtk[j] + tl;
+                dq[j] = M::mma(bh[s], M::load(sDO + r * LDV + s * KS, lane), dq[j]);
+                dks[j] = M::mma(bd[s], M::load(sVN + r * LDV + s * KS, lane), dks[j]);
+                dw[j] = M::mma(bh[s], M::load(sDVN + r * LDV + s * KS, lane), dw[j]);
             }
         // <dH, h>: each (key, value) element once, by the waves w < NKT
         float hd = 0.f;
@@ -598,20 +623,22 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
         hd = wave_sum(hd);
         // dQ's state term, dK's Ks term, and their gate terms
         float stot = 0.f;
-        const int col = 16 * kt + acc_col(lane);
 #pragma unroll
         for (int j = 0; j < TPK; ++j) {
-            f32x4 rg;
+            const int r = 16 * rtk[j] + tl;
+            const float gq = a.scale * sE[r], gk = exp2_hw(fminf(Gend - sG[r], 0.f));
+            const f32x4 qv = Quad<T>::get(Quad<T>::load(sQ + r * LDK + kc));
+            const f32x4 kv = Quad<T>::get(Quad<T>::load(sK + r * LDK + kc));
+            float qd = 0.f, s_ = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rtk[j] + acc_row(lane, e);
-                dq[j][e] *= a.scale * sE[r];
-                dks[j][e] *= exp2_hw(fminf(Gend - sG[r], 0.f));
-                const float s_ = Elem<T>::load(sK + r * LDK + col) * dks[j][e];
-                rg[e] = Elem<T>::load(sQ + r * LDK + col) * dq[j][e] - s_;
-                stot += s_;
+                dq[j][e] *= gq;
+                dks[j][e] *= gk;
+                qd += qv[e] * dq[j][e];
+                s_ += kv[e] * dks[j][e];
             }
-            add_rows(myRG, 16 * rtk[j], rg);
+            add_tok(myRG, 16 * rtk[j], qd - s_);
+            stot += s_;
             dk[j] = dks[j];
         }
         stot = wave_sum(stot);
@@ -646,7 +673,7 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
     }
     __syncthreads();   // dO and Vn are read: their regions take dW and T
 #pragma unroll
-    for (int j = 0; j < TPK; ++j) store_acc(sDW + 16 * rtk[j] * LDK + 16 * kt, LDK, lane, -dw[j]);
+    for (int j = 0; j < TPK; ++j) store4(sDW + (16 * rtk[j] + tl) * LDK + kc, -dw[j]);
     {
         const float x[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
 #pragma unroll
@@ -668,50 +695,40 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
 #pragma unroll
             for (int j = 0; j < TPK; ++j) {
                 const int r0 = 16 * rtk[j];
-                dq[j] = M::mma(M::load(sPM + (r0 + (lane & 15)) * LDC + k0, lane), bk, dq[j]);
-                dk[j] = M::mma(M::load_t(sPM + k0 * LDC + r0, LDC, lane), bq, dk[j]);
-                atdw[j] = M::mma(M::load_t(sT + k0 * LDC + r0, LDC, lane), bw, atdw[j]);
+                dq[j] = M::mma(bk, M::load(sPM + (r0 + tl) * LDC + k0, lane), dq[j]);
+                dk[j] = M::mma(bq, M::load_t(sPM + k0 * LDC + r0, LDC, lane), dk[j]);
+                atdw[j] = M::mma(bw, M::load_t(sT + k0 * LDC + r0, LDC, lane), atdw[j]);
             }
         }
-        const int col = 16 * kt + acc_col(lane);
         T* gdq = static_cast<T*>(a.dq);
 #pragma unroll
         for (int j = 0; j < TPK; ++j) {
-            f32x4 rb, rg;
+            const int r = 16 * rtk[j] + tl;
+            const float bg = sB[r] * sE[r];
+            const f32x4 kv = Quad<T>::get(Quad<T>::load(sK + r * LDK + kc));
+            float kx = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rtk[j] + acc_row(lane, e);
-                const float bg = sB[r] * sE[r];
-                const float kx = Elem<T>::load(sK + r * LDK + col) * atdw[j][e];
-                dk[j][e] += bg * atdw[j][e];
-                rb[e] = sE[r] * kx;
-                rg[e] = bg * kx;
-                if (r < n) Elem<T>::store(gdq + ((t0 + r) * H + h) * K + col, dq[j][e]);
-            }
-            add_rows(myRB, 16 * rtk[j], rb);
-            add_rows(myRG, 16 * rtk[j], rg);
+            for (int e = 0; e < 4; ++e) kx += kv[e] * atdw[j][e];
+            dk[j] += bg * atdw[j];
+            add_tok(myRB, 16 * rtk[j], sE[r] * kx);
+            add_tok(myRG, 16 * rtk[j], bg * kx);
+            if (r < n) store4(gdq + ((t0 + r) * H + h) * K + kc, dq[j]);
         }
     }
-    {   // dV = diag(beta) T^T dVn, and its dbeta term
-        const int vt = wave % NVT;
+    {   // dV = diag(beta) T^T dVn (transposed tiles), and its dbeta term
+        const int vt = wave % NVT, vc = 16 * vt + 4 * (lane >> 4);
         T* gdv = static_cast<T*>(a.dv);
 #pragma unroll
         for (int j = 0; j < TPV; ++j) {
-            const int r0 = 16 * (wave / NVT + (NW / NVT) * j);
+            const int r0 = 16 * (wave / NVT + (NW / NVT) * j), r = r0 + tl;
             f32x4 x = zero4();
 #pragma unroll
             for (int k0 = 0; k0 < C; k0 += KS)
-                x = M::mma(M::load_t(sT + k0 * LDC + r0, LDC, lane),
-                           M::load_t(sDVN + k0 * LDV + 16 * vt, LDV, lane), x);
-            const int col = 16 * vt + acc_col(lane);
-            f32x4 rb;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = r0 + acc_row(lane, e);
-                rb[e] = x[e] * Elem<T>::load(sV + r * LDV + col);
-                if (r < n) Elem<T>::store(gdv + ((t0 + r) * H + h) * V + col, sB[r] * x[e]);
-            }
-            add_rows(myRB, r0, rb);
+                x = M::mma(M::load_t(sDVN + k0 * LDV + 16 * vt, LDV, lane),
+                           M::load_t(sT + k0 * LDC + r0, LDC, lane), x);
+            const f32x4 vv = Quad<T>::get(Quad<T>::load(sV + r * LDV + vc));
+            add_tok(myRB, r0, x[0] * vv[0] + x[1] * vv[1] + x[2] * vv[2] + x[3] * vv[3]);
+            if (r < n) store4(gdv + ((t0 + r) * H + h) * V + vc, sB[r] * x);
         }
     }
     // dAinv = dVn (diag(beta) V)^T + dW (diag(beta gamma) K)^T
@@ -775,17 +792,14 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
             const Frag bk = M::load_t(sK + k0 * LDK + 16 * kt, LDK, lane);
 #pragma unroll
             for (int j = 0; j < TPK; ++j)
-                dk[j] = M::mma(M::load(sS + (16 * rtk[j] + (lane & 15)) * LDC + k0, lane), bk, dk[j]);
+                dk[j] = M::mma(bk, M::load(sS + (16 * rtk[j] + tl) * LDC + k0, lane), dk[j]);
         }
-        const int col = 16 * kt + acc_col(lane);
         T* gdk = static_cast<T*>(a.dk);
 #pragma unroll
-        for (int j = 0; j < TPK; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rtk[j] + acc_row(lane, e);
-                if (r < n) Elem<T>::store(gdk + ((t0 + r) * H + h) * K + col, dk[j][e]);
-            }
+        for (int j = 0; j < TPK; ++j) {
+            const int r = 16 * rtk[j] + tl;
+            if (r < n) store4(gdk + ((t0 + r) * H + h) * K + kc, dk[j]);
+        }
     }
     __syncthreads();
     // dbeta and dg = reverse cumulative sum of dG over the chunk

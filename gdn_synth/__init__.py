@@ -37,7 +37,8 @@ import numpy as np
 import torch
 
 __all__ = ["PrefillSpec", "DecodeSpec", "PREFILL", "DECODE", "make_prefill", "make_grads",
-           "make_decode", "prefill_spec", "draw_lengths", "flops_per_token_head"]
+           "make_decode", "prefill_spec", "draw_lengths", "flops_per_token_head",
+           "bwd_flops_per_token_head"]
 
 
 @dataclass(frozen=True)
@@ -307,3 +308,24 @@ def flops_per_token_head(K: int, V: int, C: int) -> float:
     """
     return (6 * K * V + (C - 1) * K + (C + 1) * K + (C + 1) * V
             + (C + 1) * K + (C + 1) * V + C * C / 3.0)
+
+
+def bwd_flops_per_token_head(K: int, V: int, C: int) -> float:
+    """Algorithmic MFMA flops per token-head of the chunked backward, each
+    product of its six steps counted once (2 flops per multiply-add,
+    triangular operands at their average row length, as above):
+      recompute: K K^T, the inverse, W, U, the causal Q K^T, V_new = U - W h
+        and the state update (2 K V each);
+      state-gradient recurrence: Ks dH, Qs^T dO, W^T dVn (2 K V each) and
+        Aqk^T dO;
+      per chunk: dO h^T, Vn dH^T, dVn h^T (2 K V each), the causal dO Vn^T,
+        Pm K, Pm^T Q, T^T dVn, T^T dW, dVn V^T and dW K^T (full C x C),
+        T^T dAinv T^T (two triangular C x C x C products) and the two
+        strictly-lower dA K products.
+    """
+    kv = 16 * K * V
+    k = ((C - 1) + 3 * (C + 1)          # K K^T, W, Q K^T
+         + 2 * (C + 1) + (C + 1)        # Pm K, Pm^T Q, T^T dW
+         + 2 * C + 2 * (C - 1)) * K     # dW K^T, dA K (both sides)
+    v = (4 * (C + 1) + 2 * C) * V       # U, Aqk^T dO, dO Vn^T, T^T dVn, dVn V^T
+    return float(kv + k + v + C * C / 3.0 + 2 * C * C)
