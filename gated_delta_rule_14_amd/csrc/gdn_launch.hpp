@@ -51,7 +51,7 @@ struct ChunkWs {
     void* qs;      // [H][mc][C][K]   scale * Q * gamma
     void* ks;      // [H][mc][C][K]   diag(gamma_C / gamma) K
     void* aqk;     // [H][mc][C][C]
-    float* ainv;   // [H][mc][C][C] or nullptr
+    float* ainv;   // [H][mc][C][C] or nullptr (fp32; the element type in backward mode)
     // backward mode of the intra stage: qs and aqk then hold Qs^T [K][C] and
     // Aqk^T [C][C] in fragment order, and these two are written as well
     void* ksr = nullptr;   // [H][mc][C][K]   Ks in fragment order (rows = tokens)
@@ -111,7 +111,8 @@ struct BwdScanLaunch {
 struct BwdLocalLaunch {
     ChunkMap map;
     const void *q, *k, *v, *dout;
-    const float *beta, *gcum, *ainv;
+    const float *beta, *gcum;
+    const void* ainv;       // [H][mc][C][C] (I + A)^{-1}, element type, row-major
     const void *hs, *dhs, *vn, *dvn;
     void *dq, *dk, *dv;
     float *dbeta, *dg;

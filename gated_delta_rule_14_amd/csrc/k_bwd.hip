@@ -563,10 +563,15 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
         }
         for (int i = tid; i < 2 * NW * C; i += BLOCAL_THREADS) sRB[i] = 0.f;   // sRB, sRG
     }
-    // T = (I + A)^{-1} (fp32, row-major) into registers: row tid/8, columns 8(tid%8)..
+    // T = (I + A)^{-1} (element type, row-major) into registers: row tid/8,
+    // columns 8(tid%8)..
     const int tr = tid / 8, tc = (tid % 8) * 8;
-    const float4 ta = *reinterpret_cast<const float4*>(a.ainv + blk * C * C + tr * C + tc);
-    const float4 tb = *reinterpret_cast<const float4*>(a.ainv + blk * C * C + tr * C + tc + 4);
+    u32x4 traw[8 / EV];
+    {
+        const T* ai = static_cast<const T*>(a.ainv) + blk * C * C + tr * C + tc;
+#pragma unroll
+        for (int e = 0; e < 8 / EV; ++e) traw[e] = *reinterpret_cast<const u32x4*>(ai + e * EV);
+    }
     __syncthreads();
 
     const float Gend = sG[C - 1];
@@ -674,12 +679,8 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
     __syncthreads();   // dO and Vn are read: their regions take dW and T
 #pragma unroll
     for (int j = 0; j < TPK; ++j) store4(sDW + (16 * rtk[j] + tl) * LDK + kc, -dw[j]);
-    {
-        const float x[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
 #pragma unroll
-        for (int e = 0; e < 8; e += EV)
-            *reinterpret_cast<uint4*>(sT + tr * LDC + tc + e) = Vec16<T>::pack(x + e);
-    }
+    for (int e = 0; e < 8 / EV; ++e) *reinterpret_cast<u32x4*>(sT + tr * LDC + tc + e * EV) = traw[e];
     __syncthreads();
 
     // ================= phase B

@@ -319,7 +319,7 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                         sA[i * LDA + j] = j < i ? x : 0.f;
                     }
                 }
-            } else {
+            } else if (!BWD) {
 #pragma unroll
                 for (int J = 0; J < NB; ++J)
 #pragma unroll
@@ -334,9 +334,27 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                         const int j = 16 * J + acc_row(lane, e);
                         const float x = a.scale * exp2_hw(fminf(gi - sG[j], 0.f)) * acc[J][e];
                         acc[J][e] = j <= i ? x : 0.f;
-                        if (BWD) Elem<T>::store(gaqk + FragOrder<T>::off(j, i, C), acc[J][e]);
                     }
-                    if (!BWD) store4_frag(gaqk, i, 16 * J + 4 * (lane >> 4), C, acc[J]);
+                    store4_frag(gaqk, i, 16 * J + 4 * (lane >> 4), C, acc[J]);
+                }
+            } else {
+                // backward mode: Aqk tiles (rows i = 16I + 4(l/16) + e, column
+                // j = 16J + l%16), stored as 4 consecutive columns of Aqk^T
+#pragma unroll
+                for (int J = 0; J < NB; ++J)
+#pragma unroll
+                    for (int s = 0; s < NKS; ++s) acc[J] = M::mma(fs[s], fo[J][s], acc[J]);
+#pragma unroll
+                for (int J = 0; J < NB; ++J) {
+                    const int j = 16 * J + acc_col(lane);
+                    const float gj = sG[j];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 16 * I + acc_row(lane, e);
+                        const float x = a.scale * exp2_hw(fminf(sG[i] - gj, 0.f)) * acc[J][e];
+                        acc[J][e] = j <= i ? x : 0.f;
+                    }
+                    store4_frag(gaqk, j, 16 * I + 4 * (lane >> 4), C, acc[J]);
                 }
             }
         }
@@ -471,12 +489,17 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
         float4 x0 = *reinterpret_cast<const float4*>(sA + r * LDA + j0);
         float4 x1 = *reinterpret_cast<const float4*>(sA + r * LDA + j0 + 4);
         if (up) x0 = x1 = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (STORE_AINV) {
+        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        if (STORE_AINV && !BWD) {
             float* gai = a.ws.ainv + blk * C * C + r * C + j0;
             *reinterpret_cast<float4*>(gai) = x0;
             *reinterpret_cast<float4*>(gai + 4) = x1;
         }
-        const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        if (BWD) {   // the backward takes it as an MFMA operand: element type, row-major
+            T* gai = reinterpret_cast<T*>(a.ws.ainv) + blk * C * C + r * C + j0;
+#pragma unroll
+            for (int e = 0; e < 8; e += EV) *reinterpret_cast<uint4*>(gai + e) = Vec16<T>::pack(x + e);
+        }
         float y1[8], y2[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -557,14 +580,19 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
 #pragma unroll
         for (int m = 0; m < WD; ++m)
             store4_frag(gw, i, 16 * (d0 + G * m) + 4 * (lane >> 4), K, aw[m]);
-        if (BWD) {   // W^T in fragment order as well (rows = keys)
+        if (BWD) {   // W^T in fragment order as well (rows = keys): W tiles,
+                     // 4 consecutive tokens of one key per lane
             T* gwt = static_cast<T*>(a.ws.wt) + blk * C * K;
 #pragma unroll
-            for (int m = 0; m < WD; ++m)
+            for (int m = 0; m < WD; ++m) {
+                const int D = d0 + G * m;
+                f32x4 wn = zero4();
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    Elem<T>::store(gwt + FragOrder<T>::off(16 * (d0 + G * m) + 4 * (lane >> 4) + e, i, C),
-                                   aw[m][e]);
+                for (int s = 0; s < NKM; ++s)
+                    if (s * KS < kn)
+                        wn = M::mma(fw[s], M::load_t(sKW + s * KS * LDK + 16 * D, LDK, lane), wn);
+                store4_frag(gwt, 16 * D + acc_col(lane), 16 * I + 4 * (lane >> 4), C, wn);
+            }
         }
 #pragma unroll
         for (int m = 0; m < UD; ++m)
