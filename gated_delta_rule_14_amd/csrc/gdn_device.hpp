@@ -308,6 +308,34 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// Store an R x D matrix X, of which an LDS buffer holds the VT columns
+// v0 .. v0+VT transposed (X^T rows, pitch ld elements), as fragment-order
+// groups of rows 16 rt0 .. 16 (rt0 + nrt) - 1: one 16-byte group per lane,
+// each group 1 KB contiguous in HBM.  The transposing LDS reads are those of
+// Mma::load_t (bf16) or four element reads (fp32).
+template <typename T, int VT>
+__device__ __forceinline__ void store_frag_groups(const T* xt, int ld, T* dst, int D, int v0,
+                                                  int rt0, int nrt, int lane) {
+    typedef FragOrder<T> F;
+    constexpr int KG = F::KG, VE = F::VE;
+    static_assert(VT % KG == 0, "whole groups");
+    for (int rt = rt0; rt < rt0 + nrt; ++rt) {
+#pragma unroll
+        for (int q = 0; q < VT / KG; ++q) {
+            u32x4 g;
+            if constexpr (sizeof(T) == 2) {
+                g = __builtin_bit_cast(u32x4, Mma<T>::load_t(xt + KG * q * ld + 16 * rt, ld, lane));
+            } else {
+#pragma unroll
+                for (int e = 0; e < VE; ++e)
+                    g[e] = __float_as_uint(xt[(KG * q + F::col(lane, e)) * ld + 16 * rt + (lane & 15)]);
+            }
+            const int sg = v0 / KG + q;
+            *reinterpret_cast<u32x4*>(dst + ((int64_t)(rt * (D / KG) + sg) * 64 + lane) * VE) = g;
+        }
+    }
+}
+
 // Run one role of a serial chunk walk over its nch >= 1 steps (every wave
 // of the workgroup walks the same number of steps).  The PD+1 register
 // buffers rotate with the unrolled steps so each keeps a fixed register set:

@@ -79,8 +79,8 @@ struct ScanLaunch {
     const float* h0;
     float* ht;
     void* o;                // nullptr: the output is not computed
-    void* hs = nullptr;     // [H][mc][K][V] state entering each chunk, or nullptr
-    void* vn = nullptr;     // [H][mc][C][V] V_new of each chunk, or nullptr
+    void* hs = nullptr;     // [H][mc][K x V] state entering each chunk (fragment order), or nullptr
+    void* vn = nullptr;     // [H][mc][C x V] V_new of each chunk (fragment order), or nullptr
     int64_t N, H;
     int K, V, C;
     bool bf16, per_key;
@@ -99,8 +99,8 @@ struct BwdScanLaunch {
     const void* dout;       // [B,T,H,V] output gradient
     const float* dht;       // [N,H,K,V] or nullptr
     float* dh0;             // [N,H,K,V] or nullptr
-    void* dhs;              // [H][mc][K][V] gradient of the state leaving each chunk
-    void* dvn;              // [H][mc][C][V] gradient of V_new
+    void* dhs;              // [H][mc][K x V] gradient of the state leaving each chunk (fragment order)
+    void* dvn;              // [H][mc][C x V] gradient of V_new (fragment order)
     int64_t N, H;
     int K, V, C;
     bool bf16;

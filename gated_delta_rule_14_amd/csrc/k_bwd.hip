@@ -42,12 +42,14 @@ namespace gdn {
 // row-major in LDS one chunk ahead and read with transposing loads.
 //   dV waves (C/32): token rows 32m..32m+31 of dVn = Ks dH + Aqk^T dO
 //   dH waves (K/32): key rows 32p..32p+31 of dH
+//   one store wave: dH and dVn of every chunk to HBM in fragment order
 // Per step: dV waves read dH^T, publish dVn^T and the next chunk's dO,
 // barrier; dH waves add Qs^T dO (before it) and -W^T dVn (after it), decay,
-// publish dH^T, barrier.
+// publish dH^T, barrier.  The store wave reads dH^T before the first barrier
+// (still the gradient leaving the chunk) and dVn^T between the two.
 // =====================================================================
 
-constexpr int BSCAN_MAX_THREADS = 384;
+constexpr int BSCAN_MAX_THREADS = 512;
 
 template <typename T, int K_, int V_, int VT_, int PD_>
 struct BScanCfg {
@@ -57,7 +59,7 @@ struct BScanCfg {
     static constexpr int K = K_, V = V_, C = 64, VT = VT_, PD = PD_;
     static constexpr int KS = M::KSTEP, KG = F::KG, KSPG = KG / KS;
     static constexpr int CT = VT / 16;
-    static constexpr int NVW = C / 32, NHW = K / 32, NW = NVW + NHW, NT = 64 * NW;
+    static constexpr int NVW = C / 32, NHW = K / 32, NW = NVW + NHW + 1, NT = 64 * NW;
     static constexpr int GK = K / KG, GC = C / KG;
     static constexpr int P = 16 / sizeof(T);
     static constexpr int LDH = K + P;      // dH^T   [VT][K]
@@ -208,15 +210,12 @@ struct BScanDV {
                     acc[1][ct] = M::mma(a1, bo, acc[1][ct]);
                 }
             }
-        T* dvn = static_cast<T*>(ch.a.dvn) + ch.blk(ch.chunk_of(s)) * C * V;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
+            for (int ct = 0; ct < CT; ++ct)
                 store_acc_t(ch.sVn + 16 * ct * Cfg::LDV + 16 * (2 * m + t), Cfg::LDV, ch.lane,
                             acc[t][ct]);
-                store_acc(dvn + 16 * (2 * m + t) * V + ch.v0 + 16 * ct, V, ch.lane, acc[t][ct]);
-            }
         // the other buffer was last read in the previous step
         ch.put_dO(cur.dnext, m, ch.dO_buf(s + 1));
         __syncthreads();   // dVn^T and the next dO published
@@ -276,14 +275,6 @@ struct BScanDH {
 
     __device__ __forceinline__ void step(int s, const Pre& cur, Pre& spare) {
         issue(spare, s + Cfg::PD);
-        {   // the gradient of the state leaving this chunk
-            T* dhs = static_cast<T*>(ch.a.dhs) + ch.blk(ch.chunk_of(s)) * K * V;
-#pragma unroll
-            for (int r = 0; r < 2; ++r)
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-                    store_acc(dhs + 16 * (2 * p + r) * V + ch.v0 + 16 * ct, V, ch.lane, hacc[r][ct]);
-        }
         const T* sdo = ch.dO_buf(s);
         f32x4 acc[2][CT], neg[2][CT];
 #pragma unroll
@@ -346,6 +337,25 @@ struct BScanDH {
     }
 };
 
+// ---- the store wave
+template <typename Cfg>
+struct BScanStore {
+    typedef typename Cfg::Elt T;
+    static constexpr int K = Cfg::K, V = Cfg::V, C = Cfg::C;
+    struct Pre {};
+    const BChain<Cfg>& ch;
+    __device__ __forceinline__ void issue(Pre&, int) const {}
+    __device__ __forceinline__ void step(int s, const Pre&, Pre&) const {
+        const int64_t b = ch.blk(ch.chunk_of(s));
+        store_frag_groups<T, Cfg::VT>(ch.shT, Cfg::LDH, static_cast<T*>(ch.a.dhs) + b * K * V, V,
+                                      ch.v0, 0, K / 16, ch.lane);
+        __syncthreads();   // dVn^T published
+        store_frag_groups<T, Cfg::VT>(ch.sVn, Cfg::LDV, static_cast<T*>(ch.a.dvn) + b * C * V, V,
+                                      ch.v0, 0, C / 16, ch.lane);
+        __syncthreads();   // next dH^T published
+    }
+};
+
 template <typename Cfg>
 __global__ __launch_bounds__(BSCAN_MAX_THREADS) void bwd_scan_kernel(BwdScanLaunch a) {
     __shared__ __attribute__((aligned(16))) char smem[Cfg::bytes];
@@ -365,11 +375,14 @@ __global__ __launch_bounds__(BSCAN_MAX_THREADS) void bwd_scan_kernel(BwdScanLaun
             r.init();
             drive<Cfg::PD>(r, ch.nch);
         }
-    } else {
+    } else if (wave < Cfg::NVW + Cfg::NHW) {
         BScanDH<Cfg> r{ch, wave - Cfg::NVW, {}};
         r.init();
         if (ch.nch > 0) drive<Cfg::PD>(r, ch.nch);
         r.finish();
+    } else {
+        BScanStore<Cfg> r{ch};
+        if (ch.nch > 0) drive<Cfg::PD>(r, ch.nch);
     }
 }
 
@@ -517,16 +530,18 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
 #pragma unroll
     for (int j = 0; j < TPK; ++j) rtk[j] = wave / NKT + (NW / NKT) * j;
 
-    // h and dH rows of key tile kt for phase A, issued first (the longest wait)
-    constexpr int NS = V / KS;
-    Frag bh[NS], bd[NS];
+    // h and dH rows of key tile kt for phase A (fragment-order groups, one
+    // coalesced 16-byte load per lane each), issued first: the longest wait
+    typedef FragOrder<T> F;
+    constexpr int NS = V / KS, NG = V / F::KG, KSPG = F::KG / KS;
+    u32x4 hg[NG], dg_[NG];
     {
-        const T* hrow = static_cast<const T*>(a.hs) + blk * K * V + (16 * kt + tl) * V;
-        const T* drow = static_cast<const T*>(a.dhs) + blk * K * V + (16 * kt + tl) * V;
+        const u32x4* hsrc = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.hs) + blk * K * V);
+        const u32x4* dsrc = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dhs) + blk * K * V);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            bh[s] = M::load(hrow + s * KS, lane);
-            bd[s] = M::load(drow + s * KS, lane);
+        for (int sg = 0; sg < NG; ++sg) {
+            hg[sg] = hsrc[(kt * NG + sg) * 64 + lane];
+            dg_[sg] = dsrc[(kt * NG + sg) * 64 + lane];
         }
     }
     // ---- loads (rows >= n as zero)
@@ -535,8 +550,8 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
         const T* k = static_cast<const T*>(a.k);
         const T* v = static_cast<const T*>(a.v);
         const T* dout = static_cast<const T*>(a.dout);
-        const T* vn = static_cast<const T*>(a.vn) + blk * C * V;
-        const T* dvn = static_cast<const T*>(a.dvn) + blk * C * V;
+        const u32x4* vn = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.vn) + blk * C * V);
+        const u32x4* dvn = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dvn) + blk * C * V);
         const u32x4 z = {0u, 0u, 0u, 0u};
         for (int i = tid; i < C * K / EV; i += BLOCAL_THREADS) {
             const int r = i / (K / EV), cv = (i % (K / EV)) * EV;
@@ -550,10 +565,22 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
             const bool in = r < n;
             *reinterpret_cast<u32x4*>(sV + r * LDV + cv) = in ? *reinterpret_cast<const u32x4*>(v + g) : z;
             *reinterpret_cast<u32x4*>(sDO + r * LDV + cv) = in ? *reinterpret_cast<const u32x4*>(dout + g) : z;
-            *reinterpret_cast<u32x4*>(sVN + r * LDV + cv) =
-                in ? *reinterpret_cast<const u32x4*>(vn + r * V + cv) : z;
-            *reinterpret_cast<u32x4*>(sDVN + r * LDV + cv) =
-                in ? *reinterpret_cast<const u32x4*>(dvn + r * V + cv) : z;
+        }
+        // V_new and its gradient: fragment-order groups to row-major LDS
+        for (int gi = wave; gi < (C / 16) * NG; gi += NW) {
+            const int r = 16 * (gi / NG) + tl, c0 = F::KG * (gi % NG);
+            const bool in = r < n;
+            const u32x4 x1 = in ? vn[gi * 64 + lane] : z, x2 = in ? dvn[gi * 64 + lane] : z;
+            if constexpr (sizeof(T) == 2) {
+                *reinterpret_cast<u32x4*>(sVN + r * LDV + c0 + F::col(lane, 0)) = x1;
+                *reinterpret_cast<u32x4*>(sDVN + r * LDV + c0 + F::col(lane, 0)) = x2;
+            } else {
+#pragma unroll
+                for (int e = 0; e < F::VE; ++e) {
+                    sVN[r * LDV + c0 + F::col(lane, e)] = __uint_as_float(x1[e]);
+                    sDVN[r * LDV + c0 + F::col(lane, e)] = __uint_as_float(x2[e]);
+                }
+            }
         }
         if (tid < C) {
             const float G = a.gcum[blk * C + tid];
@@ -604,26 +631,31 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
 #pragma unroll
         for (int j = 0; j < TPK; ++j) dq[j] = dks[j] = dw[j] = zero4();
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
+        for (int s = 0; s < NS; ++s) {
+            const Frag bh = F::frag(hg[s / KSPG], s % KSPG), bd = F::frag(dg_[s / KSPG], s % KSPG);
 #pragma unroll
             for (int j = 0; j < TPK; ++j) {
                 const int r = 16 * rtk[j] + tl;
-                dq[j] = M::mma(bh[s], M::load(sDO + r * LDV + s * KS, lane), dq[j]);
-                dks[j] = M::mma(bd[s], M::load(sVN + r * LDV + s * KS, lane), dks[j]);
-                dw[j] = M::mma(bh[s], M::load(sDVN + r * LDV + s * KS, lane), dw[j]);
+                dq[j] = M::mma(bh, M::load(sDO + r * LDV + s * KS, lane), dq[j]);
+                dks[j] = M::mma(bd, M::load(sVN + r * LDV + s * KS, lane), dks[j]);
+                dw[j] = M::mma(bh, M::load(sDVN + r * LDV + s * KS, lane), dw[j]);
             }
+        }
         // <dH, h>: each (key, value) element once, by the waves w < NKT
         float hd = 0.f;
         if (wave < NKT) {
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                if constexpr (sizeof(T) == 2) {
+            for (int sg = 0; sg < NG; ++sg)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) hd += (float)bh[s][e] * (float)bd[s][e];
-                } else {
-                    hd += bh[s] * bd[s];
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (sizeof(T) == 2) {
+                        hd += __uint_as_float(hg[sg][e] << 16) * __uint_as_float(dg_[sg][e] << 16) +
+                              __uint_as_float(hg[sg][e] & 0xffff0000u) *
+                                  __uint_as_float(dg_[sg][e] & 0xffff0000u);
+                    } else {
+                        hd += __uint_as_float(hg[sg][e]) * __uint_as_float(dg_[sg][e]);
+                    }
                 }
-            }
         }
         hd = wave_sum(hd);
         // dQ's state term, dK's Ks term, and their gate terms

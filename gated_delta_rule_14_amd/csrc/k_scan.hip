@@ -27,9 +27,9 @@
 // waves finish and store their rows of O, H waves decay and update h and
 // publish h^T, barrier.
 //
-// For the backward pass the same walk runs without the output (o == nullptr:
-// the O waves only keep the barriers) and stores, per chunk, the state that
-// enters it and V_new ("阅读笔记：DeltaNet 在 FLA 中的代码实现笔记", backward
+// For the backward pass the same walk runs without the output (o == nullptr)
+// and its O waves store, per chunk, the state that enters it and V_new in
+// fragment order ("阅读笔记：DeltaNet 在 FLA 中的代码实现笔记", backward
 // Steps 1-2: the states and U, W are recomputed, not kept from the forward).
 //
 // The workgroups of one (sequence, head) get ids equal modulo 8, so the
@@ -162,7 +162,6 @@ struct ScanV {
                     acc[1][ct] = M::mma(a1, bh, acc[1][ct]);
                 }
             }
-        T* vn = ch.a.vn ? static_cast<T*>(ch.a.vn) + ch.blk(j) * C * V : nullptr;
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -170,9 +169,6 @@ struct ScanV {
                 const f32x4 u = Quad<T>::get(cur.u[t][ct]);
                 store_acc_t(ch.sVn + 16 * ct * Cfg::LDV + 16 * (2 * m + t), Cfg::LDV, ch.lane,
                             u - acc[t][ct]);
-                if (vn)
-                    store_acc(vn + 16 * (2 * m + t) * V + ch.v0 + 16 * ct, V, ch.lane,
-                              u - acc[t][ct]);
             }
         __syncthreads();   // V_new^T published
         __syncthreads();   // next h^T published
@@ -319,14 +315,6 @@ struct ScanH {
 
     __device__ __forceinline__ void step(int j, const Pre& cur, Pre& spare) {
         issue(spare, j + Cfg::PD);
-        if (ch.a.hs) {   // the state entering chunk j
-            T* hs = static_cast<T*>(ch.a.hs) + ch.blk(j) * K * V;
-#pragma unroll
-            for (int r = 0; r < 2; ++r)
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-                    store_acc(hs + 16 * (2 * p + r) * V + ch.v0 + 16 * ct, V, ch.lane, hacc[r][ct]);
-        }
         float dec[2][4];
 #pragma unroll
         for (int r = 0; r < 2; ++r)
@@ -375,13 +363,27 @@ struct ScanH {
     }
 };
 
-// ---- O waves of a walk without output: only the barriers of a step
-struct ScanNop {
+// ---- O waves of a walk without output: they store, per chunk, the state
+// entering it (read from h^T in LDS before the step's first barrier, while
+// it is still the entering state) and V_new (read from V_new^T after it), in
+// fragment order, half of the row tiles each; or only keep the barriers.
+template <typename Cfg>
+struct ScanStore {
+    typedef typename Cfg::Elt T;
+    static constexpr int K = Cfg::K, V = Cfg::V, C = Cfg::C;
     struct Pre {};
+    const ScanChain<Cfg>& ch;
+    int w;   // 0 or 1
     __device__ __forceinline__ void issue(Pre&, int) const {}
-    __device__ __forceinline__ void step(int, const Pre&, Pre&) const {
-        __syncthreads();
-        __syncthreads();
+    __device__ __forceinline__ void step(int j, const Pre&, Pre&) const {
+        if (ch.a.hs)
+            store_frag_groups<T, Cfg::VT>(ch.shT, Cfg::LDH, static_cast<T*>(ch.a.hs) + ch.blk(j) * K * V,
+                                          V, ch.v0, w * (K / 32), K / 32, ch.lane);
+        __syncthreads();   // V_new^T published
+        if (ch.a.vn)
+            store_frag_groups<T, Cfg::VT>(ch.sVn, Cfg::LDV, static_cast<T*>(ch.a.vn) + ch.blk(j) * C * V,
+                                          V, ch.v0, w * (C / 32), C / 32, ch.lane);
+        __syncthreads();   // next h^T published
     }
 };
 
@@ -400,7 +402,7 @@ __global__ __launch_bounds__(SCAN_MAX_THREADS) void scan_kernel(ScanLaunch a) {
         ScanV<Cfg> r{ch, wave};
         if (ch.nch > 0) drive<Cfg::PD>(r, ch.nch);
     } else if (wave < Cfg::NVW + Cfg::NOW && !a.o) {
-        ScanNop r;
+        ScanStore<Cfg> r{ch, wave - Cfg::NVW};
         if (ch.nch > 0) drive<Cfg::PD>(r, ch.nch);
     } else if (wave == Cfg::NVW) {
         ScanO<Cfg, 0> r{ch};
