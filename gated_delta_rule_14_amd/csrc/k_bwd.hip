@@ -475,6 +475,25 @@ __device__ __forceinline__ float sum_groups(float x) {
     return x;
 }
 
+// Inputs of one (chunk slot, head) item, held in registers from their loads
+// to their LDS stores.
+template <typename T, int K, int V>
+struct LocalItem {
+    static constexpr int C = 64, EV = 16 / sizeof(T), NW = BLOCAL_THREADS / 64;
+    static constexpr int NKQ = C * K / EV / BLOCAL_THREADS;   // 16-byte pieces per thread
+    static constexpr int NVV = C * V / EV / BLOCAL_THREADS;
+    static constexpr int NG = V / FragOrder<T>::KG;
+    static constexpr int NGW = (C / 16) * NG / NW;             // V_new groups per wave
+    static_assert(NKQ * EV * BLOCAL_THREADS == C * K && NVV * EV * BLOCAL_THREADS == C * V &&
+                      NGW * NW == (C / 16) * NG,
+                  "whole pieces");
+    int64_t t0, blk, h;
+    int n;
+    u32x4 q[NKQ], k[NKQ], v[NVV], o[NVV], vn[NGW], dvn[NGW], t[8 / EV];
+    u32x4 hg[NG], dg[NG];
+    float g, b;
+};
+
 template <typename T, int K, int V>
 __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunch a) {
     typedef LocalSmem<T, K, V> L;
@@ -486,39 +505,34 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
     constexpr int TPK = NKT * (C / 16) / NW, TPV = NVT * (C / 16) / NW;
     static_assert(TPK >= 1 && TPV >= 1 && NW % NKT == 0 && NW % NVT == 0, "tile split");
     __shared__ __attribute__((aligned(16))) char smem[L::bytes];
-    T* sQ = reinterpret_cast<T*>(smem + L::o_Q);
-    T* sK = reinterpret_cast<T*>(smem + L::o_K);
-    T* sV = reinterpret_cast<T*>(smem + L::o_V);
-    T* sDVN = reinterpret_cast<T*>(smem + L::o_DVN);
-    T* sDO = reinterpret_cast<T*>(smem + L::o_DO);
-    T* sDW = sDO;
-    T* sVN = reinterpret_cast<T*>(smem + L::o_VN);
-    T* sT = sVN;
-    T* sPM = reinterpret_cast<T*>(smem + L::o_PM);
-    T* sY = sPM;
-    T* sDA = reinterpret_cast<T*>(smem + L::o_DA);
-    T* sS = sDA;
-    float* sG = reinterpret_cast<float*>(smem + L::o_G);
-    float* sE = reinterpret_cast<float*>(smem + L::o_E);
-    float* sB = reinterpret_cast<float*>(smem + L::o_B);
-    float* sRB = reinterpret_cast<float*>(smem + L::o_RB);
-    float* sRG = reinterpret_cast<float*>(smem + L::o_RG);
+    T *sQ, *sK, *sV, *sDVN, *sDO, *sDW, *sVN, *sT, *sPM, *sY, *sDA, *sS;
+    float *sG, *sE, *sB, *sRB, *sRG;
+    // (re)derived at the top of every item from an offset the compiler cannot
+    // see is zero: the addresses are then computed where they are used
+    // instead of being hoisted out of the item loop and held in registers
+    auto bind_lds = [&](int zero) {
+        char* m = smem + zero;
+        sQ = reinterpret_cast<T*>(m + L::o_Q);
+        sK = reinterpret_cast<T*>(m + L::o_K);
+        sV = reinterpret_cast<T*>(m + L::o_V);
+        sDVN = reinterpret_cast<T*>(m + L::o_DVN);
+        sDO = reinterpret_cast<T*>(m + L::o_DO);
+        sDW = sDO;
+        sVN = reinterpret_cast<T*>(m + L::o_VN);
+        sT = sVN;
+        sPM = reinterpret_cast<T*>(m + L::o_PM);
+        sY = sPM;
+        sDA = reinterpret_cast<T*>(m + L::o_DA);
+        sS = sDA;
+        sG = reinterpret_cast<float*>(m + L::o_G);
+        sE = reinterpret_cast<float*>(m + L::o_E);
+        sB = reinterpret_cast<float*>(m + L::o_B);
+        sRB = reinterpret_cast<float*>(m + L::o_RB);
+        sRG = reinterpret_cast<float*>(m + L::o_RG);
+    };
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-    const int64_t H = a.H, h = blockIdx.x % H, c = blockIdx.x / H;
-    int64_t t0;
-    int n;
-    if (a.map.table) {
-        const int4 e = a.map.table[c];
-        t0 = e.x;
-        n = e.y;
-    } else {
-        const int64_t b = c / a.map.nt, j = c - b * a.map.nt;
-        t0 = b * a.map.T + j * C;
-        n = (int)min((int64_t)C, a.map.T - j * C);
-    }
-    if (n <= 0) return;
-    const int64_t blk = h * a.map.max_chunks + c;
+    const int64_t H = a.H;
 
     // This wave's C x K output tiles: key tile kt and token tiles rtk[j].  They
     // are computed transposed (MFMA operands swapped), so lane l holds token
@@ -529,76 +543,140 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
     int rtk[TPK];
 #pragma unroll
     for (int j = 0; j < TPK; ++j) rtk[j] = wave / NKT + (NW / NKT) * j;
-
-    // h and dH rows of key tile kt for phase A (fragment-order groups, one
-    // coalesced 16-byte load per lane each), issued first: the longest wait
     typedef FragOrder<T> F;
     constexpr int NS = V / KS, NG = V / F::KG, KSPG = F::KG / KS;
-    u32x4 hg[NG], dg_[NG];
-    {
-        const u32x4* hsrc = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.hs) + blk * K * V);
-        const u32x4* dsrc = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dhs) + blk * K * V);
+
+    // The workgroup walks items (chunk slot, head) it, it + gridDim.x, ...;
+    // the next item's h, dH and T (the loads phase A waits for longest) are
+    // loaded into registers from phase C of the current one on (they are
+    // dead by then); the other inputs are loaded at the top of its iteration.
+    typedef LocalItem<T, K, V> Item;
+    const int64_t items = a.map.max_chunks * H;
+    auto decode = [&](int64_t it, Item& x) {
+        const int64_t c = it / H;
+        x.h = it - c * H;
+        if (a.map.table) {
+            const int4 e = a.map.table[c];
+            x.t0 = e.x;
+            x.n = e.y;
+        } else {
+            const int64_t b = c / a.map.nt, j = c - b * a.map.nt;
+            x.t0 = b * a.map.T + j * C;
+            x.n = (int)min((int64_t)C, a.map.T - j * C);
+        }
+        x.blk = x.h * a.map.max_chunks + c;
+    };
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    // h and dH rows of key tile kt (fragment-order groups, one coalesced
+    // 16-byte load per lane each)
+    // Every load below is unconditional and in bounds (clamped rows, values
+    // past the end replaced by zero), so that each field is redefined on
+    // every path and its registers are free between its uses.
+    auto issue_state = [&](Item& x) {
+        const u32x4* hsrc = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.hs) + x.blk * K * V);
+        const u32x4* dsrc = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dhs) + x.blk * K * V);
 #pragma unroll
         for (int sg = 0; sg < NG; ++sg) {
-            hg[sg] = hsrc[(kt * NG + sg) * 64 + lane];
-            dg_[sg] = dsrc[(kt * NG + sg) * 64 + lane];
+            x.hg[sg] = hsrc[(kt * NG + sg) * 64 + lane];
+            x.dg[sg] = dsrc[(kt * NG + sg) * 64 + lane];
         }
-    }
-    // ---- loads (rows >= n as zero)
-    {
+    };
+    // everything else (rows >= n as zero)
+    auto issue_small = [&](Item& x) {
+        const T* ai = static_cast<const T*>(a.ainv) + x.blk * C * C + (tid / 8) * C + (tid % 8) * 8;
+#pragma unroll
+        for (int e = 0; e < 8 / EV; ++e) x.t[e] = *reinterpret_cast<const u32x4*>(ai + e * EV);
+        const int rb = min(tid & (C - 1), max(x.n - 1, 0));
+        x.g = a.gcum[x.blk * C + (tid & (C - 1))];
+        const float bv = a.beta[(x.t0 + rb) * H + x.h];
+        x.b = (tid & (C - 1)) < x.n ? bv : 0.f;
+    };
+    auto issue_rest = [&](Item& x) {
         const T* q = static_cast<const T*>(a.q);
         const T* k = static_cast<const T*>(a.k);
         const T* v = static_cast<const T*>(a.v);
         const T* dout = static_cast<const T*>(a.dout);
-        const u32x4* vn = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.vn) + blk * C * V);
-        const u32x4* dvn = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dvn) + blk * C * V);
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        for (int i = tid; i < C * K / EV; i += BLOCAL_THREADS) {
-            const int r = i / (K / EV), cv = (i % (K / EV)) * EV;
-            const int64_t g = ((t0 + r) * H + h) * K + cv;
-            *reinterpret_cast<u32x4*>(sQ + r * LDK + cv) = r < n ? *reinterpret_cast<const u32x4*>(q + g) : z;
-            *reinterpret_cast<u32x4*>(sK + r * LDK + cv) = r < n ? *reinterpret_cast<const u32x4*>(k + g) : z;
+#pragma unroll
+        for (int p = 0; p < Item::NKQ; ++p) {
+            const int i = tid + BLOCAL_THREADS * p, r = i / (K / EV), cv = (i % (K / EV)) * EV;
+            const int64_t g = ((x.t0 + r) * H + x.h) * K + cv;
+            x.q[p] = r < x.n ? *reinterpret_cast<const u32x4*>(q + g) : z;
+            x.k[p] = r < x.n ? *reinterpret_cast<const u32x4*>(k + g) : z;
         }
-        for (int i = tid; i < C * V / EV; i += BLOCAL_THREADS) {
-            const int r = i / (V / EV), cv = (i % (V / EV)) * EV;
-            const int64_t g = ((t0 + r) * H + h) * V + cv;
-            const bool in = r < n;
-            *reinterpret_cast<u32x4*>(sV + r * LDV + cv) = in ? *reinterpret_cast<const u32x4*>(v + g) : z;
-            *reinterpret_cast<u32x4*>(sDO + r * LDV + cv) = in ? *reinterpret_cast<const u32x4*>(dout + g) : z;
+#pragma unroll
+        for (int p = 0; p < Item::NVV; ++p) {
+            const int i = tid + BLOCAL_THREADS * p, r = i / (V / EV), cv = (i % (V / EV)) * EV;
+            const int64_t g = ((x.t0 + r) * H + x.h) * V + cv;
+            x.v[p] = r < x.n ? *reinterpret_cast<const u32x4*>(v + g) : z;
+            x.o[p] = r < x.n ? *reinterpret_cast<const u32x4*>(dout + g) : z;
+        }
+        const u32x4* vn = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.vn) + x.blk * C * V);
+        const u32x4* dvn = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dvn) + x.blk * C * V);
+#pragma unroll
+        for (int p = 0; p < Item::NGW; ++p) {
+            const int gi = wave + NW * p, r = 16 * (gi / NG) + tl;
+            x.vn[p] = r < x.n ? vn[gi * 64 + lane] : z;
+            x.dvn[p] = r < x.n ? dvn[gi * 64 + lane] : z;
+        }
+    };
+    // the loaded inputs to LDS
+    auto put = [&](const Item& x) {
+#pragma unroll
+        for (int p = 0; p < Item::NKQ; ++p) {
+            const int i = tid + BLOCAL_THREADS * p, r = i / (K / EV), cv = (i % (K / EV)) * EV;
+            *reinterpret_cast<u32x4*>(sQ + r * LDK + cv) = x.q[p];
+            *reinterpret_cast<u32x4*>(sK + r * LDK + cv) = x.k[p];
+        }
+#pragma unroll
+        for (int p = 0; p < Item::NVV; ++p) {
+            const int i = tid + BLOCAL_THREADS * p, r = i / (V / EV), cv = (i % (V / EV)) * EV;
+            *reinterpret_cast<u32x4*>(sV + r * LDV + cv) = x.v[p];
+            *reinterpret_cast<u32x4*>(sDO + r * LDV + cv) = x.o[p];
         }
         // V_new and its gradient: fragment-order groups to row-major LDS
-        for (int gi = wave; gi < (C / 16) * NG; gi += NW) {
-            const int r = 16 * (gi / NG) + tl, c0 = F::KG * (gi % NG);
-            const bool in = r < n;
-            const u32x4 x1 = in ? vn[gi * 64 + lane] : z, x2 = in ? dvn[gi * 64 + lane] : z;
+#pragma unroll
+        for (int p = 0; p < Item::NGW; ++p) {
+            const int gi = wave + NW * p, r = 16 * (gi / NG) + tl, c0 = F::KG * (gi % NG);
             if constexpr (sizeof(T) == 2) {
-                *reinterpret_cast<u32x4*>(sVN + r * LDV + c0 + F::col(lane, 0)) = x1;
-                *reinterpret_cast<u32x4*>(sDVN + r * LDV + c0 + F::col(lane, 0)) = x2;
+                *reinterpret_cast<u32x4*>(sVN + r * LDV + c0 + F::col(lane, 0)) = x.vn[p];
+                *reinterpret_cast<u32x4*>(sDVN + r * LDV + c0 + F::col(lane, 0)) = x.dvn[p];
             } else {
 #pragma unroll
                 for (int e = 0; e < F::VE; ++e) {
-                    sVN[r * LDV + c0 + F::col(lane, e)] = __uint_as_float(x1[e]);
-                    sDVN[r * LDV + c0 + F::col(lane, e)] = __uint_as_float(x2[e]);
+                    sVN[r * LDV + c0 + F::col(lane, e)] = __uint_as_float(x.vn[p][e]);
+                    sDVN[r * LDV + c0 + F::col(lane, e)] = __uint_as_float(x.dvn[p][e]);
                 }
             }
         }
         if (tid < C) {
-            const float G = a.gcum[blk * C + tid];
-            sG[tid] = G;
-            sE[tid] = exp2_hw(G);
-            sB[tid] = tid < n ? a.beta[(t0 + tid) * H + h] : 0.f;
+            sG[tid] = x.g;
+            sE[tid] = exp2_hw(x.g);
+            sB[tid] = x.b;
         }
         for (int i = tid; i < 2 * NW * C; i += BLOCAL_THREADS) sRB[i] = 0.f;   // sRB, sRG
+    };
+
+    Item cur;
+    int64_t it = blockIdx.x;
+    decode(it, cur);
+    issue_state(cur);
+    issue_small(cur);
+    while (it < items) {
+    const int64_t itn = min(it + (int64_t)gridDim.x, items - 1);   // (the last one reloads)
+    it += gridDim.x;
+    if (cur.n <= 0) {   // an unused chunk slot (uniform over the workgroup)
+        decode(itn, cur);
+        issue_state(cur);
+        issue_small(cur);
+        continue;
     }
-    // T = (I + A)^{-1} (element type, row-major) into registers: row tid/8,
-    // columns 8(tid%8)..
-    const int tr = tid / 8, tc = (tid % 8) * 8;
-    u32x4 traw[8 / EV];
-    {
-        const T* ai = static_cast<const T*>(a.ainv) + blk * C * C + tr * C + tc;
-#pragma unroll
-        for (int e = 0; e < 8 / EV; ++e) traw[e] = *reinterpret_cast<const u32x4*>(ai + e * EV);
-    }
+    int zero;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+    bind_lds(zero);
+    const int64_t t0 = cur.t0, blk = cur.blk, h = cur.h;
+    const int n = cur.n;
+    issue_rest(cur);
+    put(cur);
     __syncthreads();
 
     const float Gend = sG[C - 1];
@@ -632,7 +710,7 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
         for (int j = 0; j < TPK; ++j) dq[j] = dks[j] = dw[j] = zero4();
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            const Frag bh = F::frag(hg[s / KSPG], s % KSPG), bd = F::frag(dg_[s / KSPG], s % KSPG);
+            const Frag bh = F::frag(cur.hg[s / KSPG], s % KSPG), bd = F::frag(cur.dg[s / KSPG], s % KSPG);
 #pragma unroll
             for (int j = 0; j < TPK; ++j) {
                 const int r = 16 * rtk[j] + tl;
@@ -649,11 +727,11 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     if constexpr (sizeof(T) == 2) {
-                        hd += __uint_as_float(hg[sg][e] << 16) * __uint_as_float(dg_[sg][e] << 16) +
-                              __uint_as_float(hg[sg][e] & 0xffff0000u) *
-                                  __uint_as_float(dg_[sg][e] & 0xffff0000u);
+                        hd += __uint_as_float(cur.hg[sg][e] << 16) * __uint_as_float(cur.dg[sg][e] << 16) +
+                              __uint_as_float(cur.hg[sg][e] & 0xffff0000u) *
+                                  __uint_as_float(cur.dg[sg][e] & 0xffff0000u);
                     } else {
-                        hd += __uint_as_float(hg[sg][e]) * __uint_as_float(dg_[sg][e]);
+                        hd += __uint_as_float(cur.hg[sg][e]) * __uint_as_float(cur.dg[sg][e]);
                     }
                 }
         }
@@ -712,7 +790,8 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
 #pragma unroll
     for (int j = 0; j < TPK; ++j) store4(sDW + (16 * rtk[j] + tl) * LDK + kc, -dw[j]);
 #pragma unroll
-    for (int e = 0; e < 8 / EV; ++e) *reinterpret_cast<u32x4*>(sT + tr * LDC + tc + e * EV) = traw[e];
+    for (int e = 0; e < 8 / EV; ++e)
+        *reinterpret_cast<u32x4*>(sT + (tid / 8) * LDC + (tid % 8) * 8 + e * EV) = cur.t[e];
     __syncthreads();
 
     // ================= phase B
@@ -777,6 +856,11 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
             Elem<T>::store(sDA + (16 * I + acc_row(lane, e)) * LDC + j, bj * x1[e] + bgj * x2[e]);
     }
     __syncthreads();
+
+    // the next item's h, dH and T, into this one's (dead) registers
+    decode(itn, cur);
+    issue_state(cur);
+    issue_small(cur);
 
     // ================= phase C: Y = dAinv T^T
 #pragma unroll
@@ -849,12 +933,32 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
         if (r < n) a.dg[(t0 + r) * H + h] = suf;
         if (lane < n) a.dbeta[(t0 + lane) * H + h] = db;
     }
+    __syncthreads();   // LDS is free for the next item
+    }
+}
+
+// One persistent workgroup per workgroup slot of the device (as many per CU
+// as the LDS allows), or one per item when there are fewer items.
+static int device_cus() {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cus = n;
+        else
+            cus = 256;
+    }
+    return cus;
 }
 
 template <typename T, int K, int V>
 static hipError_t launch_blocal_t(const BwdLocalLaunch& a) {
-    hipLaunchKernelGGL((bwd_local_kernel<T, K, V>), dim3((unsigned)(a.map.max_chunks * a.H)),
-                       dim3(BLOCAL_THREADS), 0, a.stream, a);
+    const int64_t items = a.map.max_chunks * a.H;
+    const int64_t per_cu = (int64_t)(160 * 1024 / LocalSmem<T, K, V>::bytes);
+    const int64_t grid = min(items, (int64_t)device_cus() * per_cu);
+    hipLaunchKernelGGL((bwd_local_kernel<T, K, V>), dim3((unsigned)grid), dim3(BLOCAL_THREADS), 0,
+                       a.stream, a);
     return hipGetLastError();
 }
 
