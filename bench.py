@@ -57,7 +57,11 @@ def prefill_bytes(spec, n_seqs):
 KERNEL_SOURCES = {"fused_kernel": ["k_fused.hip", "gdn_device.hpp"],
                   "intra_kernel": ["k_intra.hip", "gdn_device.hpp"],
                   "scan_kernel": ["k_scan.hip", "gdn_device.hpp"],
-                  "step_kernel": ["k_step.hip", "gdn_device.hpp"]}
+                  "step_kernel": ["k_step.hip", "gdn_device.hpp"],
+                  "bwd_intra_kernel": ["k_intra.hip", "gdn_device.hpp"],
+                  "bwd_state_scan_kernel": ["k_scan.hip", "gdn_device.hpp"],
+                  "bwd_scan_kernel": ["k_bwd.hip", "gdn_device.hpp"],
+                  "bwd_local_kernel": ["k_bwd.hip", "gdn_device.hpp"]}
 
 
 def measured_traffic(kernel):
@@ -239,7 +243,11 @@ def bench_backward(args, gdn, d):
             "tokens_per_s": spec.B * spec.T / t, "alg_flops": flops,
             "TFLOPs": flops / t / 1e12, "frac_mfma_bf16": flops / t / BF16_PEAK,
             "alg_bytes": alg_bytes, "GBps": alg_bytes / t / 1e9, "frac_hbm": alg_bytes / t / HBM_PEAK,
-            "workspace_bytes": ws.numel()}
+            "workspace_bytes": ws.numel(),
+            # HBM bytes per launch of each of its kernels, from the committed
+            # counter summary (None where the source changed since)
+            "traffic": {k: measured_traffic(k) for k in ("bwd_intra_kernel", "bwd_state_scan_kernel",
+                                                         "bwd_scan_kernel", "bwd_local_kernel")}}
 
 
 def cpu_baseline(d, min_s=10.0):
