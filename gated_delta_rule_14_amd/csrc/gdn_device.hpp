@@ -336,6 +336,22 @@ __device__ __forceinline__ void store_frag_groups(const T* xt, int ld, T* dst, i
     }
 }
 
+// Workgroup barrier for LDS hand-offs only: this wave's LDS traffic is done
+// (lgkmcnt(0)), then s_barrier.  Unlike __syncthreads() it does not wait for
+// the wave's global loads and stores (vmcnt), so loads issued ahead stay in
+// flight across it.  Only for kernels whose waves exchange data through LDS
+// alone.  The empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt not waited for
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+// Wait for this wave's global loads and stores (before it ends with loads in
+// flight into registers it no longer reads).
+__device__ __forceinline__ void drain_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Run one role of a serial chunk walk over its nch >= 1 steps (every wave
 // of the workgroup walks the same number of steps).  The PD+1 register
 // buffers rotate with the unrolled steps so each keeps a fixed register set:
@@ -345,7 +361,7 @@ __device__ __forceinline__ void drive(R& r, int nch) {
     typename R::Pre b[PD + 1];
 #pragma unroll
     for (int q = 0; q < PD; ++q) r.issue(b[q], q);
-    __syncthreads();   // the initial carried value is published
+    lds_barrier();   // the initial carried value is published
     int j = 0;
     for (; j + PD + 1 <= nch; j += PD + 1) {
 #pragma unroll

@@ -218,8 +218,8 @@ struct BScanDV {
                             acc[t][ct]);
         // the other buffer was last read in the previous step
         ch.put_dO(cur.dnext, m, ch.dO_buf(s + 1));
-        __syncthreads();   // dVn^T and the next dO published
-        __syncthreads();   // next dH^T published
+        lds_barrier();   // dVn^T and the next dO published
+        lds_barrier();   // next dH^T published
     }
 };
 
@@ -297,7 +297,7 @@ struct BScanDH {
                 }
             }
         const float dec = exp2_hw(cur.d);
-        __syncthreads();   // dVn^T published
+        lds_barrier();   // dVn^T published
         // W^T dVn
 #pragma unroll
         for (int sg = 0; sg < GC; ++sg)
@@ -321,7 +321,7 @@ struct BScanDH {
                 store_acc_t(ch.shT + 16 * ct * Cfg::LDH + 16 * (2 * p + r), Cfg::LDH, ch.lane,
                             hacc[r][ct]);
             }
-        __syncthreads();   // next dH^T published
+        lds_barrier();   // next dH^T published
     }
 
     __device__ __forceinline__ void finish() const {
@@ -349,10 +349,10 @@ struct BScanStore {
         const int64_t b = ch.blk(ch.chunk_of(s));
         store_frag_groups<T, Cfg::VT>(ch.shT, Cfg::LDH, static_cast<T*>(ch.a.dhs) + b * K * V, V,
                                       ch.v0, 0, K / 16, ch.lane);
-        __syncthreads();   // dVn^T published
+        lds_barrier();   // dVn^T published
         store_frag_groups<T, Cfg::VT>(ch.sVn, Cfg::LDV, static_cast<T*>(ch.a.dvn) + b * C * V, V,
                                       ch.v0, 0, C / 16, ch.lane);
-        __syncthreads();   // next dH^T published
+        lds_barrier();   // next dH^T published
     }
 };
 
@@ -384,6 +384,7 @@ __global__ __launch_bounds__(BSCAN_MAX_THREADS) void bwd_scan_kernel(BwdScanLaun
         BScanStore<Cfg> r{ch};
         if (ch.nch > 0) drive<Cfg::PD>(r, ch.nch);
     }
+    drain_vmem();   // the prefetches past the first chunk
 }
 
 template <typename Cfg>
@@ -677,7 +678,7 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
     const int n = cur.n;
     issue_rest(cur);
     put(cur);
-    __syncthreads();
+    lds_barrier();
 
     const float Gend = sG[C - 1];
     float* myRB = sRB + wave * C;
@@ -786,13 +787,13 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
         add_rows(myRG, 16 * I, pr);
         add_cols(myRG, 16 * J, pr, -1.f);
     }
-    __syncthreads();   // dO and Vn are read: their regions take dW and T
+    lds_barrier();   // dO and Vn are read: their regions take dW and T
 #pragma unroll
     for (int j = 0; j < TPK; ++j) store4(sDW + (16 * rtk[j] + tl) * LDK + kc, -dw[j]);
 #pragma unroll
     for (int e = 0; e < 8 / EV; ++e)
         *reinterpret_cast<u32x4*>(sT + (tid / 8) * LDC + (tid % 8) * 8 + e * EV) = cur.t[e];
-    __syncthreads();
+    lds_barrier();
 
     // ================= phase B
     {
@@ -855,7 +856,7 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
         for (int e = 0; e < 4; ++e)
             Elem<T>::store(sDA + (16 * I + acc_row(lane, e)) * LDC + j, bj * x1[e] + bgj * x2[e]);
     }
-    __syncthreads();
+    lds_barrier();
 
     // the next item's h, dH and T, into this one's (dead) registers
     decode(itn, cur);
@@ -869,7 +870,7 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
         const f32x4 y = mma_tile<T>(sDA + 16 * I * LDC, LDC, sT + 16 * J * LDC, LDC, C, lane, zero4());
         store_acc(sY + 16 * I * LDC + 16 * J, LDC, lane, y);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ================= phase D: dA = -T^T Y, strictly lower, gated
 #pragma unroll
@@ -900,7 +901,7 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
         add_rows(myRG, 16 * I, rr);
         add_cols(myRG, 16 * J, rr, -1.f);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ================= phase E: dK += (Z + Z^T) K; stores
     {
@@ -918,7 +919,7 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
             if (r < n) store4(gdk + ((t0 + r) * H + h) * K + kc, dk[j]);
         }
     }
-    __syncthreads();
+    lds_barrier();
     // dbeta and dg = reverse cumulative sum of dG over the chunk
     if (wave == 0) {
         float db = 0.f, dG = 0.f;
@@ -933,8 +934,9 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
         if (r < n) a.dg[(t0 + r) * H + h] = suf;
         if (lane < n) a.dbeta[(t0 + lane) * H + h] = db;
     }
-    __syncthreads();   // LDS is free for the next item
+    lds_barrier();   // LDS is free for the next item
     }
+    drain_vmem();   // the last (unused) prefetch
 }
 
 // One persistent workgroup per workgroup slot of the device (as many per CU

@@ -170,8 +170,8 @@ struct ScanV {
                 store_acc_t(ch.sVn + 16 * ct * Cfg::LDV + 16 * (2 * m + t), Cfg::LDV, ch.lane,
                             u - acc[t][ct]);
             }
-        __syncthreads();   // V_new^T published
-        __syncthreads();   // next h^T published
+        lds_barrier();   // V_new^T published
+        lds_barrier();   // next h^T published
     }
 };
 
@@ -224,7 +224,7 @@ struct ScanO {
                     acc[ct][1] = M::mma(ah, b1, acc[ct][1]);
                 }
             }
-        __syncthreads();   // V_new^T published
+        lds_barrier();   // V_new^T published
         // + V_new^T Aqk^T (Aqk is zero above the diagonal)
 #pragma unroll
         for (int sg = 0; sg < NA; ++sg)
@@ -255,7 +255,7 @@ struct ScanO {
                            acc[ct][t]);
             }
         }
-        __syncthreads();   // next h^T published
+        lds_barrier();   // next h^T published
     }
 };
 
@@ -320,7 +320,7 @@ struct ScanH {
         for (int r = 0; r < 2; ++r)
 #pragma unroll
             for (int e = 0; e < 4; ++e) dec[r][e] = exp2_hw(cur.d[PK ? 4 * r + e : 0]);
-        __syncthreads();   // V_new^T published
+        lds_barrier();   // V_new^T published
 #pragma unroll
         for (int r = 0; r < 2; ++r)
 #pragma unroll
@@ -347,7 +347,7 @@ struct ScanH {
             for (int ct = 0; ct < CT; ++ct)
                 store_acc_t(ch.shT + 16 * ct * Cfg::LDH + 16 * (2 * p + r), Cfg::LDH, ch.lane,
                             hacc[r][ct]);
-        __syncthreads();   // next h^T published
+        lds_barrier();   // next h^T published
     }
 
     __device__ __forceinline__ void finish() const {
@@ -379,11 +379,11 @@ struct ScanStore {
         if (ch.a.hs)
             store_frag_groups<T, Cfg::VT>(ch.shT, Cfg::LDH, static_cast<T*>(ch.a.hs) + ch.blk(j) * K * V,
                                           V, ch.v0, w * (K / 32), K / 32, ch.lane);
-        __syncthreads();   // V_new^T published
+        lds_barrier();   // V_new^T published
         if (ch.a.vn)
             store_frag_groups<T, Cfg::VT>(ch.sVn, Cfg::LDV, static_cast<T*>(ch.a.vn) + ch.blk(j) * C * V,
                                           V, ch.v0, w * (C / 32), C / 32, ch.lane);
-        __syncthreads();   // next h^T published
+        lds_barrier();   // next h^T published
     }
 };
 
@@ -416,6 +416,7 @@ __global__ __launch_bounds__(SCAN_MAX_THREADS) void scan_kernel(ScanLaunch a) {
         if (ch.nch > 0) drive<Cfg::PD>(r, ch.nch);
         r.finish();
     }
+    drain_vmem();   // the prefetches past the last chunk
 }
 
 template <typename Cfg>
