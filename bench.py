@@ -10,10 +10,12 @@ step).  The same run times the kernel of every step with HIP events on its
 stream, the two-stage path (intra-chunk stage + state pass) for comparison,
 the decode step (256 sequences x 32 heads, fp32 state in place, 64 steps),
 the chunked backward on the prefill workload (gradients of q, k, v, beta, g
-and h0 from seeded dO and dht), and the fp64 CPU oracle on the host cores.
+and h0 from seeded dO and dht), the per-key-gate (KDA) prefill B=2, T=8192,
+H=16 (two-stage route), the packed variable-length prefill (16 sequences,
+137 491 tokens, H=32; fused route), and the fp64 CPU oracle on the host cores.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-decode]
-                  [--no-backward]
+                  [--no-backward] [--no-kda] [--no-varlen]
 """
 from __future__ import annotations
 
@@ -250,6 +252,73 @@ def bench_backward(args, gdn, d):
                                                          "bwd_scan_kernel", "bwd_local_kernel")}}
 
 
+def bench_kda(args, gdn):
+    """The per-key-gate workload (two-stage route): whole calls timed with an
+    event pair around back-to-back calls, and its two kernels inside a call."""
+    spec = gdn_synth.PREFILL[3]
+    log("generating", spec.name)
+    d = gdn_synth.make_prefill(spec, 3)
+    x = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    q, k, v, beta, g = (x[n] for n in ("q", "k", "v", "beta", "g"))
+    desc = gdn.fwd_desc(q, v, "per_key", spec.chunk, d["scale"])
+    ws = torch.empty(gdn.workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(v)
+    ht = torch.empty((spec.B, spec.H, spec.K, spec.V), dtype=torch.float32, device="cuda")
+
+    def call():
+        gdn.chunk_fwd(q, k, v, beta, g, d["scale"], gate="per_key", o=o, ht=ht, workspace=ws)
+
+    for _ in range(10):
+        call()
+    reps = max(args.steps // 5, 10)
+    t = events_time(call, reps)
+    t_intra, t_scan = step_kernel_times(
+        lambda: gdn.chunk_intra(q, k, v, beta, g, d["scale"], gate="per_key", store_ainv=False,
+                                workspace=ws, views=False),
+        lambda: gdn.chunk_scan(desc, ws, o, ht=ht), reps)
+    b_in, b_out = prefill_bytes(spec, spec.B)
+    log("KDA prefill %.1f us per call (intra %.1f, scan %.1f)" % (t * 1e6, t_intra * 1e6, t_scan * 1e6))
+    return {"workload": spec.name, "us_per_call": t * 1e6, "tokens_per_s": spec.B * spec.T / t,
+            "alg_bytes": b_in + b_out, "GBps": (b_in + b_out) / t / 1e9,
+            "frac_hbm": (b_in + b_out) / t / HBM_PEAK,
+            "kernels": {"intra_kernel": {"us": t_intra * 1e6, "alg_bytes": b_in,
+                                         "GBps": b_in / t_intra / 1e9},
+                        "scan_kernel": {"us": t_scan * 1e6, "alg_bytes": b_out,
+                                        "GBps": b_out / t_scan / 1e9}}}
+
+
+def bench_varlen(args, gdn):
+    """The packed variable-length workload (fused route; the longest
+    sequence, 65 536 tokens, sets the time): whole calls, events."""
+    spec = gdn_synth.PREFILL[2]
+    log("generating", spec.name)
+    d = gdn_synth.make_prefill(spec, 2)
+    x = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    q, k, v, beta, g, cu = (x[n] for n in ("q", "k", "v", "beta", "g", "cu_seqlens"))
+    N = cu.numel() - 1
+    desc = gdn.fwd_desc(q, v, "scalar", spec.chunk, d["scale"], N)
+    ws = torch.empty(gdn.workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(v)
+    ht = torch.empty((N, spec.H, spec.K, spec.V), dtype=torch.float32, device="cuda")
+
+    def call():
+        gdn.chunk_fwd(q, k, v, beta, g, d["scale"], cu_seqlens=cu, o=o, ht=ht, workspace=ws)
+
+    for _ in range(5):
+        call()
+    reps = 10
+    t = events_time(call, reps)
+    tokens = int(q.shape[1])
+    es = 2
+    alg = tokens * spec.H * ((2 * spec.K + 2 * spec.V) * es + 8) + 4 * spec.K * spec.V * spec.H * N
+    longest = max(d["lengths"])
+    log("varlen prefill %.1f us per call (%d tokens, longest sequence %d)" % (t * 1e6, tokens, longest))
+    return {"workload": spec.name, "us_per_call": t * 1e6, "tokens": tokens, "sequences": N,
+            "longest": longest, "tokens_per_s": tokens / t, "alg_bytes": alg,
+            "GBps": alg / t / 1e9, "frac_hbm": alg / t / HBM_PEAK,
+            "us_per_chunk_of_longest": t * 1e6 / ((longest + spec.chunk - 1) // spec.chunk)}
+
+
 def cpu_baseline(d, min_s=10.0):
     import oracle
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
@@ -278,6 +347,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-kda", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (a known-size kernel to scale "
                          "hardware byte counters by)")
@@ -299,6 +370,8 @@ def main():
     spec, dt, roof, path, kernels, two_stage, d = bench_prefill(args, gdn)
     decode = None if args.no_decode else bench_decode(args, gdn)
     backward = None if args.no_backward else bench_backward(args, gdn, d)
+    kda = None if args.no_kda else bench_kda(args, gdn)
+    varlen = None if args.no_varlen else bench_varlen(args, gdn)
     cpu = None if args.no_cpu else cpu_baseline(d)
     line = {
         "metric": METRIC,
@@ -323,6 +396,8 @@ def main():
         "two_stage": two_stage,
         "decode": decode,
         "backward": backward,
+        "kda": kda,
+        "varlen": varlen,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line), flush=True)

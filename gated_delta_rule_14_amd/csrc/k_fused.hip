@@ -801,8 +801,10 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedLaunch a) {
     x.beta = a.beta;
     x.g = a.g;
     x.H = a.H;
-    const int64_t n = chain / a.H;
-    x.h = chain - n * a.H;
+    // packed input: chains longest sequence first (rank order from the table)
+    const int64_t r = chain / a.H;
+    const int64_t n = a.seqs ? (int64_t)a.seqs[r].w : r;
+    x.h = chain - r * a.H;
     x.Hq = a.Hq > 0 ? a.Hq : a.H;
     x.hq = x.h / (a.H / x.Hq);
     x.v0 = vt * VT;

@@ -80,8 +80,9 @@ struct ScanChain {
         : a(la) {
         shT = reinterpret_cast<T*>(smem + Cfg::o_hT);
         sVn = reinterpret_cast<T*>(smem + Cfg::o_Vn);
-        n = chain / a.H;
-        h = chain - n * a.H;
+        const int64_t r = chain / a.H;   // packed input: longest sequence first
+        n = a.map.seqs ? (int64_t)a.map.seqs[r].w : r;
+        h = chain - r * a.H;
         v0 = vt * Cfg::VT;
         lane = threadIdx.x & 63;
         if (a.map.seqs) {

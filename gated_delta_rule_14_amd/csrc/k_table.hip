@@ -8,17 +8,25 @@
 //
 // One workgroup.  Offsets are clamped into [0, T] (end >= start), so invalid
 // offsets can give wrong results but never an out-of-bounds access.
-//   seqs[n]  = (first token, length, first chunk, chunk count)
+//   seqs[n]  = (first token, length, first chunk, order[n])
 //   table[c] = (first token, token count, sequence, 0); unused rows have count 0
+// order[r] is the sequence of rank r by length, longest first (ties by
+// index): the kernels that walk one sequence's chunks serially take their
+// workgroups longest first, so the longest chain starts with the first wave
+// of workgroups instead of after the short ones (for up to ORDER_MAX
+// sequences; beyond that order[r] = r).
 // (the table is skipped when its pointer is null: the fused forward needs only seqs)
 #include "gdn_device.hpp"
 #include "gdn_launch.hpp"
 
 namespace gdn {
 
+constexpr int ORDER_MAX = 1024;
+
 __global__ __launch_bounds__(256) void table_kernel(TableLaunch a) {
     __shared__ int64_t s_part[256];
     __shared__ int64_t s_carry;
+    __shared__ int s_len[ORDER_MAX];
     const int tid = threadIdx.x;
     if (tid == 0) s_carry = 0;
     __syncthreads();
@@ -41,7 +49,8 @@ __global__ __launch_bounds__(256) void table_kernel(TableLaunch a) {
         }
         const int64_t first = s_carry + s_part[tid] - nc;
         if (n < a.N) {
-            a.seqs[n] = make_int4((int)s, (int)len, (int)min(first, a.max_chunks), (int)nc);
+            a.seqs[n] = make_int4((int)s, (int)len, (int)min(first, a.max_chunks), (int)n);
+            if (a.N <= ORDER_MAX) s_len[n] = (int)len;
             for (int64_t j = 0; a.table && j < nc; ++j) {
                 const int64_t c = first + j;
                 if (c >= a.max_chunks) break;
@@ -56,6 +65,19 @@ __global__ __launch_bounds__(256) void table_kernel(TableLaunch a) {
     if (a.table)
         for (int64_t c = s_carry + tid; c < a.max_chunks; c += 256)
             a.table[c] = make_int4(0, 0, -1, 0);
+    if (a.N <= ORDER_MAX) {   // rank by length: order[rank(n)] = n
+        __syncthreads();      // s_len complete, and the identity orders written above
+        const int N = (int)a.N;
+        for (int n = tid; n < N; n += 256) {
+            const int ln = s_len[n];
+            int rank = 0;
+            for (int m = 0; m < N; ++m) {
+                const int lm = s_len[m];
+                rank += (lm > ln || (lm == ln && m < n)) ? 1 : 0;
+            }
+            a.seqs[rank].w = n;
+        }
+    }
 }
 
 hipError_t launch_table(const TableLaunch& a) {

@@ -220,8 +220,11 @@ gdn_status gdn_chunk_fwd_act(const gdn_fwd_desc *d, const gdn_activation *act,
  *                           gdn_chunk_intra
  *   chunks int32 [mc][4]    (first token, token count, sequence, 0) per chunk
  *                           slot (packed input only)
- *   seqs  int32 [N][4]      (first token, length, first chunk slot, chunks)
- *                           (packed input only)
+ *   seqs  int32 [N][4]      (first token, length, first chunk slot, order[n])
+ *                           (packed input only); order[r] = the sequence of
+ *                           rank r by length, longest first (ties by index;
+ *                           order[r] = r above 1024 sequences): the serial
+ *                           passes take their workgroups in that order
  * A = strictLower(diag(beta) (Gamma * K K^T)), Gamma_ij = 2^(G_i - G_j) for
  * j <= i.  w, u, qs, ks and aqk have the element type qkv_dtype.  For the
  * per-key gate gamma is per channel and every Gamma factor sits inside the
