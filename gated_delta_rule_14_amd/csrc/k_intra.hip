@@ -44,6 +44,10 @@ struct IntraSmem {
     static constexpr int LDV = V + P;         // row-major [C][V]
     static constexpr int LDC = C + P;         // row-major [C][C] in the element type
     static constexpr int LDA = C + 4;         // fp32 [C][C]
+    // per-key gate: fp32 [C][K] rows padded by 8 floats, so that the diagonal
+    // blocks' reads (8 rows x 8 interleaved channels per wave) hit 64
+    // different banks
+    static constexpr int LDG = PK ? K + 8 : 1;
     static constexpr int NB = C / 16;
     static constexpr int SCR_ROWS = 32 + C - 16;   // per-key scaled operands (>= C)
     static constexpr size_t o_K = 0;
@@ -51,7 +55,7 @@ struct IntraSmem {
     static constexpr size_t o_V = o_Q + sizeof(T) * C * LDK;
     static constexpr size_t o_A = o_V + sizeof(T) * C * LDV;
     static constexpr size_t o_G = o_A + sizeof(float) * C * LDA;
-    static constexpr size_t o_B = o_G + sizeof(float) * C * (PK ? K : 1);
+    static constexpr size_t o_B = o_G + sizeof(float) * C * LDG;
     static constexpr size_t o_E = o_B + sizeof(float) * C;     // 2^{G_r}
     static constexpr size_t o_F = o_E + sizeof(float) * C;     // 2^{G_C-1 - G_r}
     static constexpr size_t o_P = o_F + sizeof(float) * C;
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
     typedef IntraSmem<T, K, V, C, PK> L;
     typedef Mma<T> M;
     constexpr int NT = INTRA_THREADS, NW = NT / 64;
-    constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC, LDA = L::LDA, NB = L::NB;
+    constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC, LDA = L::LDA, NB = L::NB, LDG = L::LDG;
     constexpr int EV = 16 / sizeof(T);
     constexpr int KS = M::KSTEP;
     __shared__ __attribute__((aligned(16))) char smem[L::bytes];
@@ -159,25 +163,35 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
             }
         }
     } else {
-        for (int d = tid; d < K; d += NT) {
-            float acc = 0.f;
-            float gv[16];
-            for (int r0 = 0; r0 < C; r0 += 16) {
+        // per channel d: the inclusive sum over the rows, by all threads.
+        // Thread (quarter qq, channel d) loads and scans rows qq*RPT ..
+        // (qq+1)*RPT-1 (all its loads in flight together); the quarter totals
+        // go through LDS (the sP scratch) and each quarter adds those before it.
+        constexpr int TPC = NT / K, RPT = C / TPC;
+        static_assert(TPC * RPT == C && TPC * K <= 4 * 16 * 17, "gate scan split");
+        const int d = tid % K, qq = tid / K;
+        float gv[RPT];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = r0 + i;
-                    float gr = r < n ? a.g[((t0 + r) * H + h) * K + d] : 0.f;
-                    if (r < n && (a.act.flags & ACT_GATE))
-                        gr = act_log_gate(gr, a.act.A_log[h], a.act.dt_bias[h * K + d]);
-                    gv[i] = gr * LOG2E;
-                }
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    acc += gv[i];
-                    sG[(r0 + i) * K + d] = acc;
-                }
-            }
+        for (int i = 0; i < RPT; ++i) {
+            const int r = qq * RPT + i;
+            gv[i] = r < n ? a.g[((t0 + r) * H + h) * K + d] : 0.f;
         }
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = qq * RPT + i;
+            float gr = gv[i];
+            if (r < n && (a.act.flags & ACT_GATE))
+                gr = act_log_gate(gr, a.act.A_log[h], a.act.dt_bias[h * K + d]);
+            acc += gr * LOG2E;
+            gv[i] = acc;
+        }
+        sP[qq * K + d] = acc;
+        __syncthreads();
+        float off = 0.f;
+        for (int q2 = 0; q2 < qq; ++q2) off += sP[q2 * K + d];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) sG[(qq * RPT + i) * LDG + d] = gv[i] + off;
         for (int r = tid; r < C; r += NT) {
             const float br = r < n ? a.beta[(t0 + r) * H + h] : 0.f;
             sB[r] = r >= n ? 0.f
@@ -226,8 +240,8 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
 #pragma unroll
             for (int e = 0; e < VE; ++e) {
                 const int d = KG * sg + F::col(lane, e);
-                f[e] = q_side ? a.scale * (PK ? exp2_hw(sG[r * K + d]) : sE[r]) * x[e]
-                              : (PK ? exp2_hw(fminf(sG[(C - 1) * K + d] - sG[r * K + d], 0.f))
+                f[e] = q_side ? a.scale * (PK ? exp2_hw(sG[r * LDG + d]) : sE[r]) * x[e]
+                              : (PK ? exp2_hw(fminf(sG[(C - 1) * LDG + d] - sG[r * LDG + d], 0.f))
                                     : sF[r]) * x[e];
             }
             *reinterpret_cast<uint4*>(dst + ((int64_t)task * 64 + lane) * VE) = Vec16<T>::pack(f);
@@ -249,8 +263,8 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
 #pragma unroll
             for (int e = 0; e < VE; ++e) {
                 const int tok = KG * sg + F::col(lane, e);
-                f[e] = q_side ? a.scale * (PK ? exp2_hw(sG[tok * K + kd]) : sE[tok]) * x[e]
-                              : (PK ? exp2_hw(fminf(sG[(C - 1) * K + kd] - sG[tok * K + kd], 0.f))
+                f[e] = q_side ? a.scale * (PK ? exp2_hw(sG[tok * LDG + kd]) : sE[tok]) * x[e]
+                              : (PK ? exp2_hw(fminf(sG[(C - 1) * LDG + kd] - sG[tok * LDG + kd], 0.f))
                                     : sF[tok]) * x[e];
             }
             *reinterpret_cast<uint4*>(dst + ((int64_t)t * 64 + lane) * VE) = Vec16<T>::pack(f);
@@ -267,7 +281,7 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
             }
         }
         float* gg = a.ws.gcum + blk * C * (PK ? K : 1);
-        for (int i = tid; i < C * (PK ? K : 1); i += NT) gg[i] = sG[i];
+        for (int i = tid; i < C * (PK ? K : 1); i += NT) gg[i] = PK ? sG[(i / K) * LDG + i % K] : sG[i];
     }
 
     // ---- a2: beta-scaled decay-masked strictly-lower K K^T -> sA (fp32), and
@@ -365,19 +379,22 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
             __syncthreads();   // previous I's tiles have read the scratch
             // rows [0,16): K_I 2^{G_I - G_b}; [16,32): Q_I 2^{G_I - G_b};
             // [32, 32 + b): K_J 2^{G_b - G_J} for all J < I
-            for (int i = tid; i < (32 + b) * K; i += NT) {
-                const int r = i / K, d = i - r * K;
-                float x;
-                if (r < 32) {
-                    const int tok = b + (r & 15);
-                    const T* src = (r < 16 ? sK : sQ) + tok * LDK + d;
-                    x = Elem<T>::load(src) * exp2_hw(fminf(sG[tok * K + d] - sG[b * K + d], 0.f));
-                } else {
-                    const int tok = r - 32;
-                    x = Elem<T>::load(sK + tok * LDK + d) *
-                        exp2_hw(fminf(sG[b * K + d] - sG[tok * K + d], 0.f));
+            for (int i = tid; i < (32 + b) * (K / EV); i += NT) {   // one 16-byte vector each
+                const int r = i / (K / EV), d0 = (i - r * (K / EV)) * EV;
+                const bool later = r < 32;   // rows of block I (scaled to b) or of J < I (from b)
+                const int tok = later ? b + (r & 15) : r - 32;
+                const uint4 xv = *reinterpret_cast<const uint4*>((later && r >= 16 ? sQ : sK) + tok * LDK + d0);
+                float f[EV];
+#pragma unroll
+                for (int e4 = 0; e4 < EV; e4 += 4) {
+                    const float4 gt = *reinterpret_cast<const float4*>(sG + tok * LDG + d0 + e4);
+                    const float4 gb = *reinterpret_cast<const float4*>(sG + b * LDG + d0 + e4);
+                    const float dt[4] = {gt.x - gb.x, gt.y - gb.y, gt.z - gb.z, gt.w - gb.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        f[e4 + e] = Vec16<T>::get(xv, e4 + e) * exp2_hw(fminf(later ? dt[e] : -dt[e], 0.f));
                 }
-                Elem<T>::store(sS + r * LDK + d, x);
+                *reinterpret_cast<uint4*>(sS + r * LDK + d0) = Vec16<T>::pack(f);
             }
             __syncthreads();
             for (int job = wave; job < 2 * I; job += NW) {
@@ -405,31 +422,90 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
             const int r = i / C, j = i - r * C;
             if (j / 16 > r / 16) Elem<T>::store(gaqk + FragOrder<T>::off(r, j, C), 0.f);
         }
-        // diagonal 16x16 blocks, pair by pair: thread = (block, row, slice of d)
+        // diagonal 16x16 blocks, pair by pair: thread = (block, row i, a
+        // contiguous slice of CH channels); row i's keys, queries and gates
+        // stay in registers while j runs over the block, K_j and G_j are
+        // vector reads shared by the wave's 8 rows, and the slice sums are
+        // added over the SL = 8 neighbouring lanes with DPP (the total lands
+        // in slice SL-1).  Wave w takes rows 8(w/4) .. 8(w/4)+7 of block
+        // w%4 and runs j only up to its last row, so the two waves that share
+        // a SIMD (w, w+4) do 8 + 16 steps; pairs j > i inside that range are
+        // computed and dropped (valid pairs have G_i <= G_j, so the decay
+        // exponent needs no clamp there).
         {
             constexpr int SL = NT / (NB * 16);      // threads per row
-            constexpr int DQ = K / SL;
-            const int I = tid / (16 * SL), i = 16 * I + (tid % (16 * SL)) / SL, s = tid % SL;
-            for (int j = 16 * I; j < 16 * I + 16; ++j) {
-                float akk = 0.f, aqk = 0.f;
-                if (j <= i) {
-                    for (int d = s * DQ; d < s * DQ + DQ; ++d) {
-                        const float dec = exp2_hw(fminf(sG[i * K + d] - sG[j * K + d], 0.f));
-                        const float kj = Elem<T>::load(sK + j * LDK + d) * dec;
-                        akk += Elem<T>::load(sK + i * LDK + d) * kj;
-                        aqk += Elem<T>::load(sQ + i * LDK + d) * kj;
-                    }
-                }
+            constexpr int CH = K / SL;              // channels per thread
+            static_assert(SL == 8 && CH % EV == 0 && CH % 4 == 0, "8 lanes per row, whole vectors");
+            static_assert(NW == 2 * NB, "two waves per diagonal block");
+            const int I = wave % NB, half = wave / NB, i = 16 * I + 8 * half + lane / SL, s = lane % SL;
+            const int c0 = CH * s, jend = 16 * I + 8 * half + 8;
+            auto sum8 = [](float x) {
+                x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));  // quad_perm 1,0,3,2
+                x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));  // quad_perm 2,3,0,1
+                x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, false)); // row_shr:4
+                return x;
+            };
+            float ki[CH], qi[CH], gi[CH];
 #pragma unroll
-                for (int off = 1; off < SL; off <<= 1) {
-                    akk += __shfl_xor(akk, off, 64);
-                    aqk += __shfl_xor(aqk, off, 64);
+            for (int v = 0; v < CH / EV; ++v) {
+                const uint4 xk = *reinterpret_cast<const uint4*>(sK + i * LDK + c0 + v * EV);
+                const uint4 xq = *reinterpret_cast<const uint4*>(sQ + i * LDK + c0 + v * EV);
+#pragma unroll
+                for (int e = 0; e < EV; ++e) {
+                    ki[v * EV + e] = Vec16<T>::get(xk, e);
+                    qi[v * EV + e] = Vec16<T>::get(xq, e);
                 }
-                if (s == 0) {
+            }
+#pragma unroll
+            for (int v = 0; v < CH / 4; ++v) {
+                const float4 x = *reinterpret_cast<const float4*>(sG + i * LDG + c0 + 4 * v);
+                gi[4 * v] = x.x;
+                gi[4 * v + 1] = x.y;
+                gi[4 * v + 2] = x.z;
+                gi[4 * v + 3] = x.w;
+            }
+            // K_j and G_j of the next j are read while this one computes
+            uint4 nk[CH / EV];
+            float4 ng[CH / 4];
+            auto fetch = [&](int j) {
+#pragma unroll
+                for (int v = 0; v < CH / EV; ++v)
+                    nk[v] = *reinterpret_cast<const uint4*>(sK + j * LDK + c0 + v * EV);
+#pragma unroll
+                for (int v = 0; v < CH / 4; ++v)
+                    ng[v] = *reinterpret_cast<const float4*>(sG + j * LDG + c0 + 4 * v);
+            };
+            fetch(16 * I);
+            for (int j = 16 * I; j < jend; ++j) {
+                uint4 ck[CH / EV];
+                float gjv[CH];
+#pragma unroll
+                for (int v = 0; v < CH / EV; ++v) ck[v] = nk[v];
+#pragma unroll
+                for (int v = 0; v < CH / 4; ++v) {
+                    gjv[4 * v] = ng[v].x;
+                    gjv[4 * v + 1] = ng[v].y;
+                    gjv[4 * v + 2] = ng[v].z;
+                    gjv[4 * v + 3] = ng[v].w;
+                }
+                fetch(min(j + 1, jend - 1));
+                float akk = 0.f, aqk = 0.f;
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    const float kj = Vec16<T>::get(ck[c / EV], c % EV) * exp2_hw(gi[c] - gjv[c]);
+                    akk += ki[c] * kj;
+                    aqk += qi[c] * kj;
+                }
+                akk = sum8(akk);
+                aqk = sum8(aqk);
+                if (s == SL - 1) {
                     sA[i * LDA + j] = j < i ? sB[i] * akk : 0.f;
                     Elem<T>::store(gaqk + FragOrder<T>::off(i, j, C), j <= i ? a.scale * aqk : 0.f);
                 }
             }
+            // rows of the upper half's columns that the lower half never reached
+            if (half == 0 && s == SL - 1)
+                for (int j = jend; j < 16 * I + 16; ++j) Elem<T>::store(gaqk + FragOrder<T>::off(i, j, C), 0.f);
         }
     }
     __syncthreads();
@@ -526,7 +602,7 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                 const uint4 xk = *reinterpret_cast<const uint4*>(sK + r * LDK + d0);
                 float f[EV];
 #pragma unroll
-                for (int e = 0; e < EV; ++e) f[e] = exp2_hw(sG[r * K + d0 + e]) * Vec16<T>::get(xk, e);
+                for (int e = 0; e < EV; ++e) f[e] = exp2_hw(sG[r * LDG + d0 + e]) * Vec16<T>::get(xk, e);
                 *reinterpret_cast<uint4*>(sKg + r * LDK + d0) = Vec16<T>::pack(f);
             }
         }
