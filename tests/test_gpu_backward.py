@@ -130,3 +130,19 @@ def test_bwd_full_size_sampled(gpu_lib):
     d, gr, got = _case(spec, 1)
     for b, h in ((0, 0), (3, 11)):
         _check(d, got, _ref(d, gr, heads=[h], batch=b), heads=[h], batch=b)
+
+
+@pytest.mark.parametrize("T", [1, 64, 65])
+def test_bwd_chunk_edges(gpu_lib, T):
+    """One token, exactly one chunk, one chunk and one token (bf16, K = V = 128)."""
+    spec = gdn_synth.prefill_spec(1, B=2, T=T, H=2)
+    d, gr, got = _case(spec, 60 + T)
+    _check(d, got, _ref(d, gr))
+
+
+def test_bwd_f32_single_head_strong_gates(gpu_lib):
+    """fp32, one head, the strongest gates of the bench workload (A up to 16)
+    over several chunks: gamma underflows inside chunks."""
+    spec = gdn_synth.prefill_spec(0, B=1, T=320, H=1, A_range=(8.0, 16.0), h0_std=0.1)
+    d, gr, got = _case(spec, 70)
+    _check(d, got, _ref(d, gr))
