@@ -377,13 +377,18 @@ struct ScanStore {
     int w;   // 0 or 1
     __device__ __forceinline__ void issue(Pre&, int) const {}
     __device__ __forceinline__ void step(int j, const Pre&, Pre&) const {
-        if (ch.a.hs)
-            store_frag_groups<T, Cfg::VT>(ch.shT, Cfg::LDH, static_cast<T*>(ch.a.hs) + ch.blk(j) * K * V,
-                                          V, ch.v0, w * (K / 32), K / 32, ch.lane);
+        // (16-wide slices are never chosen with the stores on)
+        if constexpr (Cfg::VT % FragOrder<T>::KG == 0) {
+            if (ch.a.hs)
+                store_frag_groups<T, Cfg::VT>(ch.shT, Cfg::LDH, static_cast<T*>(ch.a.hs) + ch.blk(j) * K * V,
+                                              V, ch.v0, w * (K / 32), K / 32, ch.lane);
+        }
         lds_barrier();   // V_new^T published
-        if (ch.a.vn)
-            store_frag_groups<T, Cfg::VT>(ch.sVn, Cfg::LDV, static_cast<T*>(ch.a.vn) + ch.blk(j) * C * V,
-                                          V, ch.v0, w * (C / 32), C / 32, ch.lane);
+        if constexpr (Cfg::VT % FragOrder<T>::KG == 0) {
+            if (ch.a.vn)
+                store_frag_groups<T, Cfg::VT>(ch.sVn, Cfg::LDV, static_cast<T*>(ch.a.vn) + ch.blk(j) * C * V,
+                                              V, ch.v0, w * (C / 32), C / 32, ch.lane);
+        }
         lds_barrier();   // next h^T published
     }
 };
@@ -433,6 +438,10 @@ static hipError_t launch_scan_cfg(const ScanLaunch& a) {
 // (bf16 slices are at most 64 wide with K = 128: 128 would spill registers)
 static int scan_vt(const ScanLaunch& a, bool bf16) {
     if (!bf16) return 32;
+    // 16-wide slices when even they give at most one workgroup per CU (few
+    // long chains); not for the stores of the backward, which write whole
+    // 32-column fragment groups
+    if (!a.map.seqs && !a.hs && !a.vn && a.N * a.H * (a.V / 16) <= 256) return 16;
     const int min_nvt = (a.K == 128 && a.V == 128) ? 2 : 1;
     int nvt = a.V / 32;
     if (!a.map.seqs)
@@ -450,6 +459,7 @@ static hipError_t launch_scan_kv(const ScanLaunch& a, int vt) {
     constexpr bool B = sizeof(T) == 2;
     if (vt == 32) return launch_scan_cfg<ScanCfg<T, K, V, 64, 32, PK, B ? GDN_SCAN_PD : 1>>(a);
     if constexpr (B) {
+        if (vt == 16) return launch_scan_cfg<ScanCfg<T, K, V, 64, 16, PK, 2>>(a);
         if (vt == 64) return launch_scan_cfg<ScanCfg<T, K, V, 64, 64, PK, 2>>(a);
         if constexpr (V == 128 && K == 64)
             if (vt == 128) return launch_scan_cfg<ScanCfg<T, K, V, 64, 128, PK, 1>>(a);
