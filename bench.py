@@ -63,7 +63,10 @@ KERNEL_SOURCES = {"fused_kernel": ["k_fused.hip", "gdn_device.hpp"],
                   "bwd_intra_kernel": ["k_intra.hip", "gdn_device.hpp"],
                   "bwd_state_scan_kernel": ["k_scan.hip", "gdn_device.hpp"],
                   "bwd_scan_kernel": ["k_bwd.hip", "gdn_device.hpp"],
-                  "bwd_local_kernel": ["k_bwd.hip", "gdn_device.hpp"]}
+                  "bwd_local_kernel": ["k_bwd.hip", "gdn_device.hpp"],
+                  "kda_intra_kernel": ["k_intra.hip", "gdn_device.hpp"],
+                  "kda_scan_kernel": ["k_scan.hip", "gdn_device.hpp"],
+                  "varlen_fused_kernel": ["k_fused.hip", "gdn_device.hpp"]}
 
 
 def measured_traffic(kernel):
@@ -282,9 +285,11 @@ def bench_kda(args, gdn):
             "alg_bytes": b_in + b_out, "GBps": (b_in + b_out) / t / 1e9,
             "frac_hbm": (b_in + b_out) / t / HBM_PEAK,
             "kernels": {"intra_kernel": {"us": t_intra * 1e6, "alg_bytes": b_in,
-                                         "GBps": b_in / t_intra / 1e9},
+                                         "GBps": b_in / t_intra / 1e9,
+                                         "traffic": measured_traffic("kda_intra_kernel")},
                         "scan_kernel": {"us": t_scan * 1e6, "alg_bytes": b_out,
-                                        "GBps": b_out / t_scan / 1e9}}}
+                                        "GBps": b_out / t_scan / 1e9,
+                                        "traffic": measured_traffic("kda_scan_kernel")}}}
 
 
 def bench_varlen(args, gdn):
@@ -316,7 +321,8 @@ def bench_varlen(args, gdn):
     return {"workload": spec.name, "us_per_call": t * 1e6, "tokens": tokens, "sequences": N,
             "longest": longest, "tokens_per_s": tokens / t, "alg_bytes": alg,
             "GBps": alg / t / 1e9, "frac_hbm": alg / t / HBM_PEAK,
-            "us_per_chunk_of_longest": t * 1e6 / ((longest + spec.chunk - 1) // spec.chunk)}
+            "us_per_chunk_of_longest": t * 1e6 / ((longest + spec.chunk - 1) // spec.chunk),
+            "traffic": measured_traffic("varlen_fused_kernel")}
 
 
 def cpu_baseline(d, min_s=10.0):
