@@ -109,7 +109,7 @@ void layout(const gdn_fwd_desc* d, bool packed, gdn_workspace_layout* L) {
 // the two gradients the reverse pass leaves for the per-chunk kernel.
 struct BwdLayout {
     gdn_workspace_layout f;
-    size_t ksr, wt, hs, dhs, vn, dvn, total;
+    size_t ksr, wt, hs, dhs, vn, dvn, dq_part, dk_part, total;
 };
 
 void bwd_layout(const gdn_fwd_desc* d, bool packed, BwdLayout* L) {
@@ -131,6 +131,14 @@ void bwd_layout(const gdn_fwd_desc* d, bool packed, BwdLayout* L) {
     off = align256(off + blocks * C * V * es);
     L->dvn = off;
     off = align256(off + blocks * C * V * es);
+    // grouped value heads: each value head's dq, dk terms (fp32) before the
+    // sum over the heads that share a q/k head
+    const bool gva = H > d->num_heads;
+    const size_t rows = (size_t)(d->batch * d->seq_len);
+    L->dq_part = off;
+    off = align256(off + (gva ? rows * H * K * 4 : 0));
+    L->dk_part = off;
+    off = align256(off + (gva ? rows * H * K * 4 : 0));
     L->total = off;
 }
 
@@ -139,8 +147,6 @@ gdn_status check_bwd_desc(const gdn_fwd_desc* d, bool packed) {
     if (s != GDN_OK) return s;
     if (d->gate != GDN_GATE_SCALAR)
         return fail(GDN_ERR_UNSUPPORTED, "the backward pass implements the scalar gate");
-    if (d->num_v_heads != 0 && d->num_v_heads != d->num_heads)
-        return fail(GDN_ERR_UNSUPPORTED, "the backward pass has no grouped value heads");
     if (d->qkv_dtype == GDN_DTYPE_F32 && (d->key_dim != 64 || d->value_dim != 64))
         return fail(GDN_ERR_UNSUPPORTED, "fp32 backward needs K = V = 64");
     return GDN_OK;
@@ -520,8 +526,9 @@ gdn_status gdn_chunk_bwd(const gdn_fwd_desc* d, const void* q, const void* k, co
     cw.ainv = reinterpret_cast<float*>(ws + L.f.ainv);
     cw.ksr = ws + L.ksr;
     cw.wt = ws + L.wt;
-    const int64_t H = d->num_heads;
+    const int64_t H = vheads(d), Hq = d->num_heads;   // value heads, q/k heads
     const int64_t N = packed ? d->num_seqs : d->batch;
+    const bool gva = H > Hq;
     hipError_t e;
     if (packed) {
         gdn::TableLaunch t;
@@ -546,7 +553,7 @@ gdn_status gdn_chunk_bwd(const gdn_fwd_desc* d, const void* q, const void* k, co
         a.map = map;
         a.ws = cw;
         a.H = H;
-        a.Hq = H;
+        a.Hq = Hq;
         a.K = (int)d->key_dim;
         a.V = (int)d->value_dim;
         a.C = d->chunk;
@@ -617,6 +624,9 @@ gdn_status gdn_chunk_bwd(const gdn_fwd_desc* d, const void* q, const void* k, co
         a.dv = dv;
         a.dbeta = dbeta;
         a.dg = dg;
+        a.dq_part = gva ? reinterpret_cast<float*>(ws + L.dq_part) : nullptr;
+        a.dk_part = gva ? reinterpret_cast<float*>(ws + L.dk_part) : nullptr;
+        a.Hq = Hq;
         a.H = H;
         a.K = (int)d->key_dim;
         a.V = (int)d->value_dim;
@@ -626,6 +636,21 @@ gdn_status gdn_chunk_bwd(const gdn_fwd_desc* d, const void* q, const void* k, co
         a.stream = st;
         if ((e = gdn::launch_bwd_local(a)) != hipSuccess)
             return hip_fail(e, "per-chunk gradient launch");
+        if (gva) {   // dq, dk of each q/k head: the sum over its value heads
+            gdn::GvaSumLaunch sl;
+            sl.rows = d->batch * d->seq_len;
+            sl.H = H;
+            sl.Hq = Hq;
+            sl.K = (int)d->key_dim;
+            sl.bf16 = bf16;
+            sl.stream = st;
+            sl.part = reinterpret_cast<const float*>(ws + L.dq_part);
+            sl.out = dq;
+            if ((e = gdn::launch_gva_sum(sl)) != hipSuccess) return hip_fail(e, "dq group sum launch");
+            sl.part = reinterpret_cast<const float*>(ws + L.dk_part);
+            sl.out = dk;
+            if ((e = gdn::launch_gva_sum(sl)) != hipSuccess) return hip_fail(e, "dk group sum launch");
+        }
     }
     return ok();
 }

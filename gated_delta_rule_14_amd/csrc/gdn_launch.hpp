@@ -116,9 +116,24 @@ struct BwdLocalLaunch {
     const void *hs, *dhs, *vn, *dvn;
     void *dq, *dk, *dv;
     float *dbeta, *dg;
+    // grouped value heads: q/k have Hq heads; value head h reads q/k head
+    // h / (H / Hq) and, when H > Hq, leaves its dq, dk terms in these fp32
+    // [B*T][H][K] buffers for launch_gva_sum (dq, dk unused then)
+    float *dq_part = nullptr, *dk_part = nullptr;
+    int64_t Hq = 0;
     int64_t H;
     int K, V, C;
     float scale;
+    bool bf16;
+    hipStream_t stream;
+};
+
+// dq (dk) of q/k head hq = the sum of the fp32 terms of its H/Hq value heads
+struct GvaSumLaunch {
+    const float* part;      // [rows][H][K]
+    void* out;              // [rows][Hq][K], element type
+    int64_t rows, H, Hq;
+    int K;
     bool bf16;
     hipStream_t stream;
 };
@@ -160,5 +175,6 @@ bool fused_supported(const FusedLaunch& a);
 hipError_t launch_fused(const FusedLaunch& a);
 hipError_t launch_bwd_scan(const BwdScanLaunch& a);
 hipError_t launch_bwd_local(const BwdLocalLaunch& a);
+hipError_t launch_gva_sum(const GvaSumLaunch& a);
 
 }  // namespace gdn

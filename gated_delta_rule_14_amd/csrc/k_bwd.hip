@@ -534,7 +534,7 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
     };
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-    const int64_t H = a.H;
+    const int64_t H = a.H, Hq = a.Hq > 0 ? a.Hq : a.H;
 
     // This wave's C x K output tiles: key tile kt and token tiles rtk[j].  They
     // are computed transposed (MFMA operands swapped), so lane l holds token
@@ -598,10 +598,11 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
         const T* k = static_cast<const T*>(a.k);
         const T* v = static_cast<const T*>(a.v);
         const T* dout = static_cast<const T*>(a.dout);
+        const int64_t hq = x.h / (H / Hq);   // grouped value heads: the shared q/k head
 #pragma unroll
         for (int p = 0; p < Item::NKQ; ++p) {
             const int i = tid + BLOCAL_THREADS * p, r = i / (K / EV), cv = (i % (K / EV)) * EV;
-            const int64_t g = ((x.t0 + r) * H + x.h) * K + cv;
+            const int64_t g = ((x.t0 + r) * Hq + hq) * K + cv;
             x.q[p] = r < x.n ? *reinterpret_cast<const u32x4*>(q + g) : z;
             x.k[p] = r < x.n ? *reinterpret_cast<const u32x4*>(k + g) : z;
         }
@@ -826,7 +827,12 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
             dk[j] += bg * atdw[j];
             add_tok(myRB, 16 * rtk[j], sE[r] * kx);
             add_tok(myRG, 16 * rtk[j], bg * kx);
-            if (r < n) store4(gdq + ((t0 + r) * H + h) * K + kc, dq[j]);
+            if (r < n) {
+                if (a.dq_part)
+                    *reinterpret_cast<f32x4*>(a.dq_part + ((t0 + r) * H + h) * K + kc) = dq[j];
+                else
+                    store4(gdq + ((t0 + r) * H + h) * K + kc, dq[j]);
+            }
         }
     }
     {   // dV = diag(beta) T^T dVn (transposed tiles), and its dbeta term
@@ -917,7 +923,12 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
 #pragma unroll
         for (int j = 0; j < TPK; ++j) {
             const int r = 16 * rtk[j] + tl;
-            if (r < n) store4(gdk + ((t0 + r) * H + h) * K + kc, dk[j]);
+            if (r < n) {
+                if (a.dk_part)
+                    *reinterpret_cast<f32x4*>(a.dk_part + ((t0 + r) * H + h) * K + kc) = dk[j];
+                else
+                    store4(gdk + ((t0 + r) * H + h) * K + kc, dk[j]);
+            }
         }
     }
     lds_barrier();
@@ -977,6 +988,36 @@ hipError_t launch_bwd_local(const BwdLocalLaunch& a) {
     if (a.K == 128 && a.V == 64) return launch_blocal_t<bf16, 128, 64>(a);
     if (a.K == 128 && a.V == 128) return launch_blocal_t<bf16, 128, 128>(a);
     return hipErrorInvalidValue;
+}
+
+}  // namespace gdn
+
+namespace gdn {
+
+// dq (dk) of each q/k head: the sum of its value heads' fp32 terms, 4
+// consecutive channels per thread (grouped value heads in the backward).
+template <typename T>
+__global__ __launch_bounds__(256) void gva_sum_kernel(GvaSumLaunch a) {
+    const int64_t m = a.H / a.Hq, per_row = a.Hq * (a.K / 4);
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= a.rows * per_row) return;
+    const int64_t row = i / per_row, rest = i - row * per_row;
+    const int64_t hq = rest / (a.K / 4), c = (rest - hq * (a.K / 4)) * 4;
+    f32x4 acc = zero4();
+    for (int64_t u = 0; u < m; ++u)
+        acc += *reinterpret_cast<const f32x4*>(a.part + (row * a.H + hq * m + u) * a.K + c);
+    store4(static_cast<T*>(a.out) + (row * a.Hq + hq) * a.K + c, acc);
+}
+
+hipError_t launch_gva_sum(const GvaSumLaunch& a) {
+    const int64_t n = a.rows * a.Hq * (a.K / 4);
+    if (n <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (a.bf16)
+        hipLaunchKernelGGL(gva_sum_kernel<bf16>, grid, dim3(256), 0, a.stream, a);
+    else
+        hipLaunchKernelGGL(gva_sum_kernel<float>, grid, dim3(256), 0, a.stream, a);
+    return hipGetLastError();
 }
 
 }  // namespace gdn

@@ -332,9 +332,11 @@ gdn_status gdn_recurrent_step_act(const gdn_step_desc *d, const gdn_activation *
  *   dg         [B, T, H]     float, written: the gradient of the natural-log gate
  *   dh0        [N, H, K, V]  float, written, or NULL: not computed
  *
- * Supported: the scalar gate, no grouped value heads (num_v_heads 0 or H),
- * chunk 64; bf16 q/k/v with K, V in {64, 128}, fp32 with K = V = 64.  Other
- * shapes give GDN_ERR_UNSUPPORTED.  dout, dq, dk, dv need 16-byte alignment.
+ * Supported: the scalar gate, chunk 64, grouped value heads (see GVA
+ * above: v, dv, beta, dbeta, g, dg, h0, dht, dh0 have H_V heads; q, k, dq, dk
+ * have H, and dq, dk of a q/k head sum the terms of its H_V/H value heads);
+ * bf16 q/k/v with K, V in {64, 128}, fp32 with K = V = 64.  Other shapes give
+ * GDN_ERR_UNSUPPORTED.  dout, dq, dk, dv need 16-byte alignment.
  * The workspace (gdn_chunk_bwd_workspace bytes, 256-byte aligned) holds the
  * recomputed per-chunk quantities, the chunk entry states and the state
  * gradients; its contents on return are unspecified.  No output may alias an

@@ -160,8 +160,11 @@ def test_chunk_bwd_rejects_before_launch(lib):
     ws = lambda d: lib.gdn_chunk_bwd_workspace(ctypes.byref(d), ctypes.byref(n))  # noqa: E731
     assert ws(_desc()) == 0 and n.value > 0
     assert ws(_desc(gate=1)) == 4                       # scalar gate only
-    assert ws(_desc(num_v_heads=8)) == 4                # no grouped value heads
-    assert ws(_desc(num_v_heads=4)) == 0                # H_V == H is allowed
+    assert ws(_desc(num_v_heads=4)) == 0                # H_V == H
+    base = n.value
+    assert ws(_desc(num_v_heads=8)) == 0                # grouped value heads
+    assert n.value > base                               # (room for the per-head dq, dk terms)
+    assert ws(_desc(num_v_heads=6)) == 2                # not a multiple of H
     assert ws(_desc(qkv_dtype=0)) == 4                  # fp32 needs K = V = 64
     assert ws(_desc(qkv_dtype=0, key_dim=64, value_dim=64)) == 0
     assert ws(_desc(chunk=32)) == 4

@@ -146,3 +146,30 @@ def test_bwd_f32_single_head_strong_gates(gpu_lib):
     spec = gdn_synth.prefill_spec(0, B=1, T=320, H=1, A_range=(8.0, 16.0), h0_std=0.1)
     d, gr, got = _case(spec, 70)
     _check(d, got, _ref(d, gr))
+
+
+@pytest.mark.parametrize("dt,cid,K,V,m", [("bf16", 1, 128, 128, 2), ("bf16", 1, 64, 128, 4),
+                                          ("f32", 0, 64, 64, 2)])
+def test_bwd_gva(gpu_lib, dt, cid, K, V, m):
+    """Grouped value heads: q, k with H heads, everything of a state with
+    H_V = m H.  Reference: the oracle on q, k repeated m times along the head
+    axis, its dq, dk summed over each group of m value heads (the chain rule
+    of the repetition)."""
+    import gated_delta_rule_14_amd as gdn
+    spec = gdn_synth.prefill_spec(cid, dtype=dt, B=2, T=150, H=4, K=K, V=V, h0_std=0.05)
+    print("case: gva", spec, "m", m, flush=True)
+    d = gdn_synth.make_prefill(spec, 80 + m)
+    gr = gdn_synth.make_grads(d, 80 + m)
+    q, k = d["q"][:, :, ::m].contiguous(), d["k"][:, :, ::m].contiguous()
+    x = to_dev(d)
+    got = gdn.chunk_bwd(q.cuda(), k.cuda(), x["v"], x["beta"], x["g"], gr["do"].cuda(),
+                        scale=d["scale"], h0=x["h0"], dht=gr["dht"].cuda())
+    torch.cuda.synchronize()
+    qe, ke = q.repeat_interleave(m, dim=2), k.repeat_interleave(m, dim=2)
+    ref = chunked_backward(qe, ke, d["v"], d["beta"], d["g"], d["scale"], gr["do"], h0=d["h0"],
+                           dht=gr["dht"], chunk=d["chunk"])
+    B, T, Hv = d["v"].shape[:3]
+    for name in ("dq", "dk"):
+        ref[name] = ref[name].reshape(B, T, Hv // m, m, K).sum(axis=3)
+    assert tuple(got["dq"].shape) == tuple(q.shape)
+    _check(d, got, ref)
