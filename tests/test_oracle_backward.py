@@ -198,3 +198,36 @@ def test_chunked_backward_mutations_fail(drop, monkeypatch):
     got = ob.chunked_backward(d["q"], d["k"], d["v"], d["beta"], d["g"], 0.5, do,
                               h0=d["h0"], dht=dht, chunk=8)
     assert max(_rel(got[n], ref[n]) for n in NAMES) > 1e-4
+
+
+@pytest.mark.parametrize("neg_eig", [False, True])
+def test_activation_backward_matches_finite_differences(neg_eig):
+    """The activation's chain rule against central differences of
+    L = <dg, log_gate(a, A_log, dt_bias)> + <dbeta, beta_from_logits(b)>
+    through oracle.activation (every element of a, b, A_log, dt_bias)."""
+    from oracle import activation as act
+    from oracle.backward import activation_backward
+    rng = np.random.default_rng(90)
+    B, T, H = 2, 5, 3
+    a, b = rng.standard_normal((B, T, H)) * 2, rng.standard_normal((B, T, H)) * 2
+    A_log, dt_bias = np.log(rng.uniform(0.5, 16, H)), rng.standard_normal(H)
+    dg, dbeta = rng.standard_normal((B, T, H)), rng.standard_normal((B, T, H))
+
+    def loss(a_, b_, A_, d_):
+        return float(np.sum(dg * act.log_gate(a_, A_, d_)) +
+                     np.sum(dbeta * act.beta_from_logits(b_, neg_eig)))
+    got = activation_backward(a, b, A_log, dt_bias, dg, dbeta, neg_eig)
+    args = [a, b, A_log, dt_bias]
+    eps = 1e-6
+    for which in range(4):
+        x = args[which]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            keep = x[idx]
+            x[idx] = keep + eps
+            lp = loss(*args)
+            x[idx] = keep - eps
+            lm = loss(*args)
+            x[idx] = keep
+            fd[idx] = (lp - lm) / (2 * eps)
+        assert np.max(np.abs(got[which] - fd)) <= 1e-7 * max(np.max(np.abs(fd)), 1.0), which
