@@ -13,7 +13,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_SCALAR, GATE_PER_KEY = 0, 1
@@ -24,7 +24,7 @@ EXPORTS = sorted(["gdn_abi_version", "gdn_status_str", "gdn_last_error",
                   "gdn_chunk_fwd_workspace", "gdn_chunk_fwd", "gdn_workspace_layout_of",
                   "gdn_chunk_intra", "gdn_chunk_scan", "gdn_recurrent_step",
                   "gdn_chunk_fwd_act", "gdn_recurrent_step_act",
-                  "gdn_chunk_bwd_workspace", "gdn_chunk_bwd"])
+                  "gdn_chunk_bwd_workspace", "gdn_chunk_bwd", "gdn_chunk_bwd_act"])
 INTRA_STORE_AINV = 1
 ACT_GATE, ACT_BETA_SIGMOID, ACT_BETA_NEG_EIG = 1, 2, 4
 
@@ -102,6 +102,9 @@ def load(path: str = LIB_PATH):
     lib.gdn_chunk_bwd_workspace.restype = S
     lib.gdn_chunk_bwd.argtypes = [ctypes.POINTER(FwdDesc)] + [P] * 16 + [ctypes.c_size_t, P]
     lib.gdn_chunk_bwd.restype = S
+    lib.gdn_chunk_bwd_act.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(Activation)] + \
+        [P] * 18 + [ctypes.c_size_t, P]
+    lib.gdn_chunk_bwd_act.restype = S
     v = lib.gdn_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError("libgdn.so ABI %d, binding expects %d" % (v, ABI_VERSION))
@@ -247,11 +250,14 @@ def bwd_workspace_bytes(desc: FwdDesc) -> int:
 
 
 def chunk_bwd(q, k, v, beta, g, do, scale=None, h0=None, dht=None, cu_seqlens=None, chunk=64,
-              want_dh0=True, workspace=None, out=None, stream=None):
-    """gdn_chunk_bwd: gradients of <do, o> + <dht, ht> of the chunked forward
-    with respect to q, k, v, beta, g (scalar gate) and h0.  Returns a dict
-    dq, dk, dv (dtype of q), dbeta, dg, dh0 (float32; dh0 None unless
-    want_dh0).  `out` may supply any of these tensors."""
+              want_dh0=True, workspace=None, out=None, stream=None, act=None):
+    """gdn_chunk_bwd (gdn_chunk_bwd_act when act, from activation(), is
+    given): gradients of <do, o> + <dht, ht> of the chunked forward with
+    respect to q, k, v, beta, g (scalar gate) and h0.  Returns a dict dq, dk,
+    dv (dtype of q), dbeta, dg, dh0 (float32; dh0 None unless want_dh0).
+    With act, beta and g are the raw logits, dbeta and dg their gradients,
+    and with the gate activation the dict also holds dA_log and ddt_bias
+    ([H] float32).  `out` may supply any of these tensors."""
     lib = load()
     _inputs(q, k, v, beta, g, cu_seqlens, "scalar")
     _need(do, "do", q.dtype)
@@ -277,14 +283,26 @@ def chunk_bwd(q, k, v, beta, g, do, scale=None, h0=None, dht=None, cu_seqlens=No
         out["dh0"] = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
     if not want_dh0:
         out["dh0"] = None
+    act_gate = act is not None and bool(act.flags & ACT_GATE)
+    if act_gate:
+        _act_shapes(act, H, K, "scalar")
+        for name in ("dA_log", "ddt_bias"):
+            if out.get(name) is None:
+                out[name] = torch.empty((H,), dtype=torch.float32, device=dev)
+            _need(out[name], name, torch.float32)
     nbytes = bwd_workspace_bytes(desc)
     if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    _check(lib.gdn_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
-                             _ptr(h0), _ptr(cu_seqlens), _ptr(do), _ptr(dht), _ptr(out["dq"]),
-                             _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
-                             _ptr(out["dg"]), _ptr(out["dh0"]), _ptr(workspace),
-                             workspace.numel() * workspace.element_size(), _stream(stream)))
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0), _ptr(cu_seqlens), _ptr(do),
+            _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
+            _ptr(out["dg"]), _ptr(out["dh0"])]
+    tail = [_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)]
+    if act is None:
+        _check(lib.gdn_chunk_bwd(ctypes.byref(desc), *args, *tail))
+    else:
+        _check(lib.gdn_chunk_bwd_act(ctypes.byref(desc), ctypes.byref(act), *args,
+                                     _ptr(out.get("dA_log")) if act_gate else None,
+                                     _ptr(out.get("ddt_bias")) if act_gate else None, *tail))
     return out
 
 

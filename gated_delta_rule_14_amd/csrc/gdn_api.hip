@@ -109,7 +109,7 @@ void layout(const gdn_fwd_desc* d, bool packed, gdn_workspace_layout* L) {
 // the two gradients the reverse pass leaves for the per-chunk kernel.
 struct BwdLayout {
     gdn_workspace_layout f;
-    size_t ksr, wt, hs, dhs, vn, dvn, dq_part, dk_part, total;
+    size_t ksr, wt, hs, dhs, vn, dvn, dq_part, dk_part, act_part, total;
 };
 
 void bwd_layout(const gdn_fwd_desc* d, bool packed, BwdLayout* L) {
@@ -139,6 +139,9 @@ void bwd_layout(const gdn_fwd_desc* d, bool packed, BwdLayout* L) {
     off = align256(off + (gva ? rows * H * K * 4 : 0));
     L->dk_part = off;
     off = align256(off + (gva ? rows * H * K * 4 : 0));
+    // input activation: per (head, chunk slot) terms of dA_log and ddt_bias
+    L->act_part = off;
+    off = align256(off + blocks * 2 * 4);
     L->total = off;
 }
 
@@ -481,14 +484,23 @@ gdn_status gdn_chunk_bwd_workspace(const gdn_fwd_desc* d, size_t* bytes) {
     return ok();
 }
 
-gdn_status gdn_chunk_bwd(const gdn_fwd_desc* d, const void* q, const void* k, const void* v,
-                         const float* beta, const float* g, const float* h0,
-                         const int64_t* cu_seqlens, const void* dout, const float* dht,
-                         void* dq, void* dk, void* dv, float* dbeta, float* dg, float* dh0,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+gdn_status gdn_chunk_bwd_act(const gdn_fwd_desc* d, const gdn_activation* act_in, const void* q,
+                             const void* k, const void* v, const float* beta, const float* g,
+                             const float* h0, const int64_t* cu_seqlens, const void* dout,
+                             const float* dht, void* dq, void* dk, void* dv, float* dbeta,
+                             float* dg, float* dh0, float* dA_log, float* ddt_bias,
+                             void* workspace, size_t workspace_bytes, void* stream) {
     const bool packed = cu_seqlens != nullptr;
     gdn_status s = check_bwd_desc(d, packed);
     if (s != GDN_OK) return s;
+    gdn::Act act;
+    s = check_act(act_in, &act);
+    if (s != GDN_OK) return s;
+    const bool act_gate = act.flags & gdn::ACT_GATE;
+    if (act_gate && (!dA_log || !ddt_bias))
+        return fail(GDN_ERR_NULL_ARG, "GDN_ACT_GATE needs the dA_log and ddt_bias outputs");
+    if (act_gate && (!aligned4(dA_log) || !aligned4(ddt_bias)))
+        return fail(GDN_ERR_MISALIGNED, "dA_log and ddt_bias need 4-byte alignment");
     if (!packed && d->num_seqs != 0)
         return fail(GDN_ERR_BAD_SHAPE, "num_seqs must be 0 without cu_seqlens");
     if (!q || !k || !v || !beta || !g || !dout || !dq || !dk || !dv || !dbeta || !dg || !workspace)
@@ -561,6 +573,7 @@ gdn_status gdn_chunk_bwd(const gdn_fwd_desc* d, const void* q, const void* k, co
         a.bf16 = bf16;
         a.per_key = false;
         a.bwd = true;
+        a.act = act;
         a.stream = st;
         if ((e = gdn::launch_intra(a)) != hipSuccess) return hip_fail(e, "intra-chunk launch");
     }
@@ -626,6 +639,9 @@ gdn_status gdn_chunk_bwd(const gdn_fwd_desc* d, const void* q, const void* k, co
         a.dg = dg;
         a.dq_part = gva ? reinterpret_cast<float*>(ws + L.dq_part) : nullptr;
         a.dk_part = gva ? reinterpret_cast<float*>(ws + L.dk_part) : nullptr;
+        a.act = act;
+        a.g = g;
+        a.act_part = reinterpret_cast<float*>(ws + L.act_part);
         a.Hq = Hq;
         a.H = H;
         a.K = (int)d->key_dim;
@@ -652,7 +668,27 @@ gdn_status gdn_chunk_bwd(const gdn_fwd_desc* d, const void* q, const void* k, co
             if ((e = gdn::launch_gva_sum(sl)) != hipSuccess) return hip_fail(e, "dk group sum launch");
         }
     }
+    if (act_gate) {   // dA_log, ddt_bias (zeros when there are no tokens)
+        gdn::ActReduceLaunch r;
+        r.map = map;
+        if (!work) r.map.max_chunks = 0;
+        r.part = reinterpret_cast<const float*>(ws + L.act_part);
+        r.dA_log = dA_log;
+        r.ddt_bias = ddt_bias;
+        r.H = H;
+        r.stream = st;
+        if ((e = gdn::launch_act_reduce(r)) != hipSuccess) return hip_fail(e, "dA_log sum launch");
+    }
     return ok();
+}
+
+gdn_status gdn_chunk_bwd(const gdn_fwd_desc* d, const void* q, const void* k, const void* v,
+                         const float* beta, const float* g, const float* h0,
+                         const int64_t* cu_seqlens, const void* dout, const float* dht,
+                         void* dq, void* dk, void* dv, float* dbeta, float* dg, float* dh0,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    return gdn_chunk_bwd_act(d, nullptr, q, k, v, beta, g, h0, cu_seqlens, dout, dht, dq, dk, dv,
+                             dbeta, dg, dh0, nullptr, nullptr, workspace, workspace_bytes, stream);
 }
 
 gdn_status gdn_recurrent_step_act(const gdn_step_desc* d, const gdn_activation* act_in,

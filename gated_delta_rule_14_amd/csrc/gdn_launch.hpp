@@ -120,11 +120,27 @@ struct BwdLocalLaunch {
     // h / (H / Hq) and, when H > Hq, leaves its dq, dk terms in these fp32
     // [B*T][H][K] buffers for launch_gva_sum (dq, dk unused then)
     float *dq_part = nullptr, *dk_part = nullptr;
+    // input activation: beta and g hold raw logits; dbeta and dg are then the
+    // gradients of the logits, and each (head, chunk slot) leaves its sums of
+    // dg * log alpha and of d(logit a) in act_part[h][slot][2] for
+    // launch_act_reduce
+    Act act;
+    const float* g = nullptr;   // the raw gate logits [B*T][H] (with ACT_GATE)
+    float* act_part = nullptr;
     int64_t Hq = 0;
     int64_t H;
     int K, V, C;
     float scale;
     bool bf16;
+    hipStream_t stream;
+};
+
+// dA_log[h], ddt_bias[h]: the sums of the per-chunk terms over the used slots
+struct ActReduceLaunch {
+    ChunkMap map;
+    const float* part;      // [H][max_chunks][2]
+    float *dA_log, *ddt_bias;
+    int64_t H;
     hipStream_t stream;
 };
 
@@ -176,5 +192,6 @@ hipError_t launch_fused(const FusedLaunch& a);
 hipError_t launch_bwd_scan(const BwdScanLaunch& a);
 hipError_t launch_bwd_local(const BwdLocalLaunch& a);
 hipError_t launch_gva_sum(const GvaSumLaunch& a);
+hipError_t launch_act_reduce(const ActReduceLaunch& a);
 
 }  // namespace gdn

@@ -590,7 +590,8 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
         for (int e = 0; e < 8 / EV; ++e) x.t[e] = *reinterpret_cast<const u32x4*>(ai + e * EV);
         const int rb = min(tid & (C - 1), max(x.n - 1, 0));
         x.g = a.gcum[x.blk * C + (tid & (C - 1))];
-        const float bv = a.beta[(x.t0 + rb) * H + x.h];
+        float bv = a.beta[(x.t0 + rb) * H + x.h];
+        if (a.act.flags & ACT_BETA_SIGMOID) bv = act_beta(bv, a.act.flags & ACT_BETA_NEG_EIG);
         x.b = (tid & (C - 1)) < x.n ? bv : 0.f;
     };
     auto issue_rest = [&](Item& x) {
@@ -932,7 +933,8 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
         }
     }
     lds_barrier();
-    // dbeta and dg = reverse cumulative sum of dG over the chunk
+    // dbeta and dg = reverse cumulative sum of dG over the chunk; with the
+    // input activation, their chain rule to the raw logits
     if (wave == 0) {
         float db = 0.f, dG = 0.f;
 #pragma unroll
@@ -941,8 +943,29 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
             dG += sRG[w * C + lane];
         }
         const float rev = __shfl(dG, C - 1 - lane, 64);
-        const float suf = wave_incl_scan(rev, lane);   // at lane l: sum of dG[C-1-l ..]
+        float suf = wave_incl_scan(rev, lane);   // at lane l: sum of dG[C-1-l ..]
         const int r = C - 1 - lane;
+        if (a.act.flags & ACT_GATE) {
+            // log alpha = -e^{A_log} softplus(x), x = a + dt_bias:
+            // d/da = -e^{A_log} sigmoid(x), d/dA_log = log alpha
+            const float araw = a.g[(t0 + min(r, n - 1)) * H + h];
+            const float el = expf(a.act.A_log[h]), xa = araw + a.act.dt_bias[h];
+            const float da = r < n ? -suf * el / (1.f + expf(-xa)) : 0.f;
+            float pl = r < n ? -suf * el * softplus_f(xa) : 0.f, pd = da;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                pl += __shfl_xor(pl, off, 64);
+                pd += __shfl_xor(pd, off, 64);
+            }
+            if (lane == 0) *reinterpret_cast<float2*>(a.act_part + 2 * blk) = make_float2(pl, pd);
+            suf = da;
+        }
+        if (a.act.flags & ACT_BETA_SIGMOID) {
+            // beta = m sigmoid(b): d/db = m sigmoid(b) sigmoid(-b)
+            const float braw = a.beta[(t0 + min(lane, n - 1)) * H + h];
+            const float m = (a.act.flags & ACT_BETA_NEG_EIG) ? 2.f : 1.f;
+            db *= m / ((1.f + expf(-braw)) * (1.f + expf(braw)));
+        }
         if (r < n) a.dg[(t0 + r) * H + h] = suf;
         if (lane < n) a.dbeta[(t0 + lane) * H + h] = db;
     }
@@ -1007,6 +1030,41 @@ __global__ __launch_bounds__(256) void gva_sum_kernel(GvaSumLaunch a) {
     for (int64_t u = 0; u < m; ++u)
         acc += *reinterpret_cast<const f32x4*>(a.part + (row * a.H + hq * m + u) * a.K + c);
     store4(static_cast<T*>(a.out) + (row * a.Hq + hq) * a.K + c, acc);
+}
+
+// dA_log[h] and ddt_bias[h]: one workgroup per head sums the per-chunk
+// terms of the slots in use, in a fixed order (deterministic).
+__global__ __launch_bounds__(256) void act_reduce_kernel(ActReduceLaunch a) {
+    __shared__ float sl[256], sd[256];
+    const int64_t h = blockIdx.x, mc = a.map.max_chunks;
+    const int tid = threadIdx.x;
+    float l = 0.f, d = 0.f;
+    for (int64_t c = tid; c < mc; c += 256) {
+        if (a.map.table && a.map.table[c].y <= 0) continue;
+        const float2 p = *reinterpret_cast<const float2*>(a.part + 2 * (h * mc + c));
+        l += p.x;
+        d += p.y;
+    }
+    sl[tid] = l;
+    sd[tid] = d;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (tid < off) {
+            sl[tid] += sl[tid + off];
+            sd[tid] += sd[tid + off];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        a.dA_log[h] = sl[0];
+        a.ddt_bias[h] = sd[0];
+    }
+}
+
+hipError_t launch_act_reduce(const ActReduceLaunch& a) {
+    if (a.H <= 0) return hipSuccess;
+    hipLaunchKernelGGL(act_reduce_kernel, dim3((unsigned)a.H), dim3(256), 0, a.stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_gva_sum(const GvaSumLaunch& a) {

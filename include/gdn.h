@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef int32_t gdn_status;
 enum {
@@ -350,6 +350,30 @@ gdn_status gdn_chunk_bwd(const gdn_fwd_desc *d,
                          const void *dout, const float *dht,
                          void *dq, void *dk, void *dv, float *dbeta, float *dg, float *dh0,
                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_chunk_bwd with the input activation applied inside the kernels, as
+ * gdn_chunk_fwd_act does it (act may be NULL: then exactly gdn_chunk_bwd).
+ * The gradients of the activated inputs are carried to the raw ones by the
+ * chain rule of "Gated Delta Network（GDN）" §3.1 eq. 5 (x = a + dt_bias[h]):
+ *   dg     d/da = dlog_alpha * (-exp(A_log[h]) * sigmoid(x))   with GDN_ACT_GATE
+ *   dbeta  d/db = dbeta_act * m sigmoid(b) sigmoid(-b)          with GDN_ACT_BETA_SIGMOID
+ *          (m = 2 with GDN_ACT_BETA_NEG_EIG, else 1)
+ *   dA_log   [H_V] float, written with GDN_ACT_GATE (required then):
+ *            sum over the tokens of dlog_alpha * log_alpha
+ *   ddt_bias [H_V] float, written with GDN_ACT_GATE (required then):
+ *            sum over the tokens of d/da
+ * Both are ignored without GDN_ACT_GATE.  Only the scalar gate is supported
+ * (dt_bias [H_V]); the rest is as for gdn_chunk_bwd, with the same workspace.
+ */
+gdn_status gdn_chunk_bwd_act(const gdn_fwd_desc *d, const gdn_activation *act,
+                             const void *q, const void *k, const void *v,
+                             const float *beta, const float *g, const float *h0,
+                             const int64_t *cu_seqlens,
+                             const void *dout, const float *dht,
+                             void *dq, void *dk, void *dv, float *dbeta, float *dg, float *dh0,
+                             float *dA_log, float *ddt_bias,
+                             void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -189,3 +189,24 @@ def test_chunk_bwd_rejects_before_launch(lib):
     assert bwd(desc=_desc(gate=1)) == 4
     assert bwd(desc=_desc(batch=1), cu=FAKE) == 2
     assert lib.gdn_last_error().decode() != ""
+
+
+def test_chunk_bwd_act_rejects_before_launch(lib):
+    """gdn_chunk_bwd_act checks the activation and its extra outputs before
+    any launch."""
+    d = _desc()
+    odd = ctypes.c_void_p((1 << 20) + 2)
+
+    def bwd(flags, A_log=FAKE, dt_bias=FAKE, dA_log=FAKE, ddt_bias=FAKE, desc=d):
+        a = gdn.Activation(flags, A_log, dt_bias)
+        return lib.gdn_chunk_bwd_act(ctypes.byref(desc), ctypes.byref(a), FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, None, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                     None, dA_log, ddt_bias, FAKE, 1 << 40, None)
+    assert bwd(8) == 4                           # unknown bit
+    assert bwd(4) == 4                           # NEG_EIG without BETA_SIGMOID
+    assert bwd(1, A_log=None) == 1               # GATE needs A_log, dt_bias
+    assert bwd(1, dA_log=None) == 1              # ... and the dA_log, ddt_bias outputs
+    assert bwd(1 | 2, ddt_bias=None) == 1
+    assert bwd(1, dA_log=odd) == 6
+    assert bwd(1, desc=_desc(gate=1)) == 4       # scalar gate only
+    assert lib.gdn_last_error().decode() != ""
