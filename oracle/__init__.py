@@ -10,11 +10,14 @@ HIP path.
   brute_force_forward, wy_ungated : explicit transition products and WY
       recursions, used to pin the two above on tiny inputs.
   activation.log_gate / beta_from_logits : the gate and beta activations
-      from raw logits (the in-kernel activation's reference).
+      from raw logits (the in-kernel activation's reference);
+      activation.l2_normalize : q, k scaled to unit L2 norm per token and head.
   backward.recurrent_backward : gradients (dq, dk, dv, dbeta, dg, dh0) by
       autograd through the fp64 token recurrence (PyTorch CPU)
   backward.chunked_backward : the chunkwise backward steps with the gate
       terms (numpy fp64), pinned to the former.
+  backward.activation_backward, l2_normalize_backward : the chain rules of
+      the input activation and of the L2 normalisation.
 """
 from .recurrence import recurrent_forward, recurrent_step, as_f64  # noqa: F401
 from .chunked import chunked_forward  # noqa: F401

@@ -12,6 +12,13 @@ and A_log per head (the pages give the per-head form only; this is the
 elementwise reading).
 
 The inputs here are the raw logits a = W_alpha x_t and b = W_beta x_t.
+
+q and k are L2-normalised per token and head ("TileLang 实战" §1.2: with
+||k_t|| = 1 the write's eigenvalues are {1 - beta_t} and 1; "Gated Delta
+Network（GDN）", implementation notes: q and k are L2-normalised).  The pages
+give no epsilon; the reading taken here is x / sqrt(sum x^2 + 1e-6) over the
+head dimension, which is x / ||x|| up to a relative 5e-7 for unit-scale rows
+and stays finite for an all-zero row.
 """
 from __future__ import annotations
 
@@ -49,3 +56,12 @@ def beta_from_logits(b, neg_eig=False):
     """beta = sigmoid(b), or 2 sigmoid(b) in (0, 2) with neg_eig."""
     s = sigmoid(b)
     return 2.0 * s if neg_eig else s
+
+
+L2_EPS = 1e-6
+
+
+def l2_normalize(x, eps=L2_EPS):
+    """x / sqrt(sum(x^2) + eps) over the last axis (the head dimension)."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)

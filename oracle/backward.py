@@ -234,3 +234,14 @@ def activation_backward(a, b, A_log, dt_bias, dg, dbeta, neg_eig=False):
     dA_log = np.sum(dg * lg, axis=tuple(range(dg.ndim - 1)))
     ddt_bias = np.sum(da, axis=tuple(range(da.ndim - 1)))
     return da, db, dA_log, ddt_bias
+
+
+def l2_normalize_backward(x, dy, eps=None):
+    """Gradient with respect to x of <dy, l2_normalize(x)>: with n2 = sum x^2
+    + eps over the head dimension, y = x / sqrt(n2) has the symmetric Jacobian
+    (I - x x^T / n2) / sqrt(n2), so dx = (dy - x (x . dy) / n2) / sqrt(n2)."""
+    from .activation import L2_EPS
+    eps = L2_EPS if eps is None else eps
+    x, dy = as_f64(x), as_f64(dy)
+    n2 = np.sum(x * x, axis=-1, keepdims=True) + eps
+    return (dy - x * (np.sum(x * dy, axis=-1, keepdims=True) / n2)) / np.sqrt(n2)

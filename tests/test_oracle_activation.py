@@ -146,3 +146,25 @@ def test_brute_force_and_chunked_negative_eigenvalues(per_key):
                                    gate=e["gate"], chunk=chunk)
         for x, y in zip(b[:2], a):
             assert np.max(np.abs(x - y)) < 1e-10 * np.max(np.abs(y))
+
+
+def test_l2_normalize_pins():
+    """l2_normalize: unit norm and the same direction (up to the epsilon's
+    relative 5e-7 at unit scale), exactly unit norm with eps = 0, scale
+    invariance, per-row independence, and a zero row stays zero."""
+    rng = np.random.default_rng(95)
+    x = rng.standard_normal((3, 5, 2, 16)) * rng.uniform(0.5, 3.0, (3, 5, 2, 1))
+    y = act.l2_normalize(x)
+    n = np.linalg.norm(x, axis=-1, keepdims=True)
+    assert np.allclose(np.linalg.norm(y, axis=-1), 1.0, rtol=0, atol=1e-6)
+    assert np.allclose(y, x / n, rtol=0, atol=1e-6)
+    y0 = act.l2_normalize(x, eps=0.0)
+    assert np.allclose(np.linalg.norm(y0, axis=-1), 1.0, rtol=0, atol=1e-14)
+    assert np.allclose(act.l2_normalize(7.5 * x, eps=0.0), y0, rtol=0, atol=1e-14)
+    # each (token, head) row on its own: normalising a slice gives the same
+    assert np.array_equal(act.l2_normalize(x[1:2, 3:4, 1:2]), y[1:2, 3:4, 1:2])
+    z = act.l2_normalize(np.zeros((2, 16)))
+    assert np.all(z == 0.0)
+    # the eps reading: x / sqrt(|x|^2 + 1e-6), checked on a row of norm 1e-3
+    small = np.full(4, 5e-4)
+    assert np.allclose(act.l2_normalize(small), small / np.sqrt(1e-6 + 1e-6), rtol=1e-14)

@@ -231,3 +231,29 @@ def test_activation_backward_matches_finite_differences(neg_eig):
             x[idx] = keep
             fd[idx] = (lp - lm) / (2 * eps)
         assert np.max(np.abs(got[which] - fd)) <= 1e-7 * max(np.max(np.abs(fd)), 1.0), which
+
+
+def test_l2_normalize_backward_matches_finite_differences():
+    """The L2 normalisation's chain rule against central differences of
+    <dy, l2_normalize(x)> (every element), and for eps = 0 the gradient is
+    orthogonal to x (the normalised output does not change along x)."""
+    from oracle import activation as act
+    from oracle.backward import l2_normalize_backward
+    rng = np.random.default_rng(96)
+    x = rng.standard_normal((2, 3, 2, 8)) * 0.7
+    x[0, 0, 0] *= 1e-2    # a short row, where the epsilon matters more
+    dy = rng.standard_normal(x.shape)
+    got = l2_normalize_backward(x, dy)
+    fd = np.zeros_like(x)
+    h = 1e-7
+    for idx in np.ndindex(x.shape):
+        keep = x[idx]
+        x[idx] = keep + h
+        lp = float(np.sum(dy * act.l2_normalize(x)))
+        x[idx] = keep - h
+        lm = float(np.sum(dy * act.l2_normalize(x)))
+        x[idx] = keep
+        fd[idx] = (lp - lm) / (2 * h)
+    assert np.max(np.abs(got - fd)) <= 1e-6 * max(np.max(np.abs(fd)), 1.0)
+    g0 = l2_normalize_backward(x, dy, eps=0.0)
+    assert np.max(np.abs(np.sum(g0 * x, axis=-1))) <= 1e-12
