@@ -13,7 +13,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_SCALAR, GATE_PER_KEY = 0, 1
@@ -21,12 +21,13 @@ STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE", 3: "GDN_ER
           4: "GDN_ERR_UNSUPPORTED", 5: "GDN_ERR_WORKSPACE_TOO_SMALL", 6: "GDN_ERR_MISALIGNED",
           7: "GDN_ERR_HIP"}
 EXPORTS = sorted(["gdn_abi_version", "gdn_status_str", "gdn_last_error",
-                  "gdn_chunk_fwd_workspace", "gdn_chunk_fwd", "gdn_workspace_layout_of",
+                  "gdn_chunk_fwd_workspace", "gdn_chunk_fwd_workspace_act", "gdn_chunk_fwd",
+                  "gdn_workspace_layout_of",
                   "gdn_chunk_intra", "gdn_chunk_scan", "gdn_recurrent_step",
                   "gdn_chunk_fwd_act", "gdn_recurrent_step_act",
                   "gdn_chunk_bwd_workspace", "gdn_chunk_bwd", "gdn_chunk_bwd_act"])
 INTRA_STORE_AINV = 1
-ACT_GATE, ACT_BETA_SIGMOID, ACT_BETA_NEG_EIG = 1, 2, 4
+ACT_GATE, ACT_BETA_SIGMOID, ACT_BETA_NEG_EIG, ACT_QK_L2NORM = 1, 2, 4, 8
 
 
 class FwdDesc(ctypes.Structure):
@@ -80,6 +81,9 @@ def load(path: str = LIB_PATH):
     lib.gdn_last_error.restype = ctypes.c_char_p
     lib.gdn_chunk_fwd_workspace.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(ctypes.c_size_t)]
     lib.gdn_chunk_fwd_workspace.restype = S
+    lib.gdn_chunk_fwd_workspace_act.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(Activation),
+                                                ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdn_chunk_fwd_workspace_act.restype = S
     lib.gdn_workspace_layout_of.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(WorkspaceLayout)]
     lib.gdn_workspace_layout_of.restype = S
     lib.gdn_chunk_fwd.argtypes = [ctypes.POINTER(FwdDesc), P, P, P, P, P, P, P, P, P, P,
@@ -161,21 +165,26 @@ def workspace_layout(desc: FwdDesc) -> WorkspaceLayout:
     return out
 
 
-def workspace_bytes(desc: FwdDesc) -> int:
+def workspace_bytes(desc: FwdDesc, act=None) -> int:
     lib = load()
     n = ctypes.c_size_t()
-    _check(lib.gdn_chunk_fwd_workspace(ctypes.byref(desc), ctypes.byref(n)))
+    if act is None:
+        _check(lib.gdn_chunk_fwd_workspace(ctypes.byref(desc), ctypes.byref(n)))
+    else:
+        _check(lib.gdn_chunk_fwd_workspace_act(ctypes.byref(desc), ctypes.byref(act), ctypes.byref(n)))
     return n.value
 
 
-def activation(gate_logits=False, beta_sigmoid=False, neg_eig=False, A_log=None, dt_bias=None):
+def activation(gate_logits=False, beta_sigmoid=False, neg_eig=False, A_log=None, dt_bias=None,
+               qk_l2norm=False):
     """The optional in-kernel input activation (gdn_activation): with
     gate_logits, g holds raw logits a and log alpha = -exp(A_log) softplus(a +
     dt_bias) (A_log [H], dt_bias [H] or [H, K] float32 device tensors); with
     beta_sigmoid, beta holds raw logits b and beta = sigmoid(b), times 2 with
-    neg_eig (beta in (0, 2))."""
+    neg_eig (beta in (0, 2)); with qk_l2norm, q and k are L2-normalised per
+    token and head inside the kernels."""
     flags = (ACT_GATE if gate_logits else 0) | (ACT_BETA_SIGMOID if beta_sigmoid else 0) | \
-        (ACT_BETA_NEG_EIG if neg_eig else 0)
+        (ACT_BETA_NEG_EIG if neg_eig else 0) | (ACT_QK_L2NORM if qk_l2norm else 0)
     if gate_logits:
         _need(A_log, "A_log", torch.float32)
         _need(dt_bias, "dt_bias", torch.float32)
@@ -228,7 +237,7 @@ def chunk_fwd(q, k, v, beta, g, scale=None, h0=None, cu_seqlens=None, chunk=64,
         o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
     if output_final_state and ht is None:
         ht = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device)
-    nbytes = workspace_bytes(desc)
+    nbytes = workspace_bytes(desc, act)
     if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0), _ptr(cu_seqlens), _ptr(o),

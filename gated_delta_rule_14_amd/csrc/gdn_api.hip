@@ -157,7 +157,10 @@ gdn_status check_bwd_desc(const gdn_fwd_desc* d, bool packed) {
 
 // gdn_chunk_fwd runs the fused kernel for these shapes; its workspace holds
 // only the per-sequence records of packed input
-bool fused_path(const gdn_fwd_desc* d) {
+// (q/k L2 normalisation runs on the two-stage route, whose intra-chunk stage
+// normalises the rows as it loads them)
+bool fused_path(const gdn_fwd_desc* d, int act_flags = 0) {
+    if (act_flags & GDN_ACT_QK_L2NORM) return false;
     gdn::FusedLaunch f{};
     f.bf16 = d->qkv_dtype == GDN_DTYPE_BF16;
     f.per_key = d->gate == GDN_GATE_PER_KEY;
@@ -181,14 +184,14 @@ struct Prepared {
 };
 
 static_assert(GDN_ACT_GATE == gdn::ACT_GATE && GDN_ACT_BETA_SIGMOID == gdn::ACT_BETA_SIGMOID &&
-                  GDN_ACT_BETA_NEG_EIG == gdn::ACT_BETA_NEG_EIG,
+                  GDN_ACT_BETA_NEG_EIG == gdn::ACT_BETA_NEG_EIG && GDN_ACT_QK_L2NORM == gdn::ACT_QK_L2NORM,
               "activation bits");
 
 // the optional input activation (NULL: g and beta are used as given)
 gdn_status check_act(const gdn_activation* act, gdn::Act* out) {
     *out = gdn::Act{};
     if (!act || act->flags == 0) return GDN_OK;
-    const int known = GDN_ACT_GATE | GDN_ACT_BETA_SIGMOID | GDN_ACT_BETA_NEG_EIG;
+    const int known = GDN_ACT_GATE | GDN_ACT_BETA_SIGMOID | GDN_ACT_BETA_NEG_EIG | GDN_ACT_QK_L2NORM;
     if (act->flags & ~known) return fail(GDN_ERR_UNSUPPORTED, "activation flags 0x%x", act->flags);
     if ((act->flags & GDN_ACT_BETA_NEG_EIG) && !(act->flags & GDN_ACT_BETA_SIGMOID))
         return fail(GDN_ERR_UNSUPPORTED, "GDN_ACT_BETA_NEG_EIG needs GDN_ACT_BETA_SIGMOID");
@@ -311,13 +314,21 @@ gdn_status gdn_workspace_layout_of(const gdn_fwd_desc* d, gdn_workspace_layout* 
     return ok();
 }
 
-gdn_status gdn_chunk_fwd_workspace(const gdn_fwd_desc* d, size_t* bytes) {
+gdn_status gdn_chunk_fwd_workspace_act(const gdn_fwd_desc* d, const gdn_activation* act_in,
+                                       size_t* bytes) {
     if (!bytes) return fail(GDN_ERR_NULL_ARG, "bytes is NULL");
-    gdn_workspace_layout L;
-    gdn_status s = gdn_workspace_layout_of(d, &L);
+    gdn::Act act;
+    gdn_status s = check_act(act_in, &act);
     if (s != GDN_OK) return s;
-    *bytes = fused_path(d) ? fused_workspace(d, d->num_seqs > 0) : L.total;
+    gdn_workspace_layout L;
+    s = gdn_workspace_layout_of(d, &L);
+    if (s != GDN_OK) return s;
+    *bytes = fused_path(d, act.flags) ? fused_workspace(d, d->num_seqs > 0) : L.total;
     return ok();
+}
+
+gdn_status gdn_chunk_fwd_workspace(const gdn_fwd_desc* d, size_t* bytes) {
+    return gdn_chunk_fwd_workspace_act(d, nullptr, bytes);
 }
 
 gdn_status gdn_chunk_intra(const gdn_fwd_desc* d, const void* q, const void* k, const void* v,
@@ -457,7 +468,7 @@ gdn_status gdn_chunk_fwd_act(const gdn_fwd_desc* d, const gdn_activation* act_in
     if (!aligned16(o) || !aligned4(h0) || !aligned4(ht))
         return fail(GDN_ERR_MISALIGNED, "o needs 16-byte, h0 and ht 4-byte alignment");
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (fused_path(d)) return fused_fwd(d, q, k, v, beta, g, h0, cu_seqlens, o, ht, workspace,
+    if (fused_path(d, act.flags)) return fused_fwd(d, q, k, v, beta, g, h0, cu_seqlens, o, ht, workspace,
                                         workspace_bytes, st, act);
     Prepared P;
     s = prepare(d, q, k, v, beta, g, cu_seqlens, workspace, workspace_bytes, false, st, &P, act);
@@ -666,6 +677,19 @@ gdn_status gdn_chunk_bwd_act(const gdn_fwd_desc* d, const gdn_activation* act_in
             sl.part = reinterpret_cast<const float*>(ws + L.dk_part);
             sl.out = dk;
             if ((e = gdn::launch_gva_sum(sl)) != hipSuccess) return hip_fail(e, "dk group sum launch");
+        }
+        if (act.flags & gdn::ACT_QK_L2NORM) {   // the normalisation's chain rule, in place
+            gdn::L2BwdLaunch l;
+            l.rows = d->batch * d->seq_len * Hq;
+            l.K = (int)d->key_dim;
+            l.bf16 = bf16;
+            l.stream = st;
+            l.x = q;
+            l.dx = dq;
+            if ((e = gdn::launch_l2norm_bwd(l)) != hipSuccess) return hip_fail(e, "dq normalisation launch");
+            l.x = k;
+            l.dx = dk;
+            if ((e = gdn::launch_l2norm_bwd(l)) != hipSuccess) return hip_fail(e, "dk normalisation launch");
         }
     }
     if (act_gate) {   // dA_log, ddt_bias (zeros when there are no tokens)

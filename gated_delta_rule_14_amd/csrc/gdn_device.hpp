@@ -386,4 +386,40 @@ __device__ __forceinline__ float act_beta(float b, bool neg_eig) {
     return neg_eig ? 2.f * s : s;
 }
 
+// q/k L2 normalisation per token and head ("TileLang 实战" §1.2: unit-norm
+// keys keep the write's eigenvalues in [-1, 1]): x / sqrt(sum x^2 + 1e-6),
+// the epsilon being this library's reading.  Rows are held as 16-byte pieces
+// of T by LPR consecutive lanes (a power of two dividing 64, all 64 lanes
+// active); every lane gets its piece scaled by its row's factor.
+constexpr float L2_EPS = 1e-6f;
+template <typename T, int LPR>
+__device__ __forceinline__ u32x4 l2norm_piece(u32x4 p) {
+    constexpr int N = 16 / sizeof(T);
+    float x[N];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (sizeof(T) == 2) {
+            x[2 * e] = __uint_as_float(p[e] << 16);
+            x[2 * e + 1] = __uint_as_float(p[e] & 0xffff0000u);
+        } else {
+            x[e] = __uint_as_float(p[e]);
+        }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < N; ++e) ss += x[e] * x[e];
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) ss += __shfl_xor(ss, off, 64);
+    const float inv = 1.f / sqrtf(ss + L2_EPS);
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (sizeof(T) == 2)
+            r[e] = pack_bf16x2(x[2 * e] * inv, x[2 * e + 1] * inv);
+        else
+            r[e] = __float_as_uint(x[e] * inv);
+    }
+    return r;
+}
+
 }  // namespace gdn

@@ -10,8 +10,9 @@ namespace gdn {
 
 // In-kernel input activation (the same bits as GDN_ACT_* in gdn.h): the gate
 // and beta inputs hold raw logits ("Gated Delta Network（GDN）" §3.1 eq. 5,
-// §5 gate fusion).
-enum { ACT_GATE = 1, ACT_BETA_SIGMOID = 2, ACT_BETA_NEG_EIG = 4 };
+// §5 gate fusion); with ACT_QK_L2NORM q and k are L2-normalised per token
+// and head as they are read.
+enum { ACT_GATE = 1, ACT_BETA_SIGMOID = 2, ACT_BETA_NEG_EIG = 4, ACT_QK_L2NORM = 8 };
 struct Act {
     int flags = 0;
     const float* A_log = nullptr;     // [H]
@@ -193,5 +194,18 @@ hipError_t launch_bwd_scan(const BwdScanLaunch& a);
 hipError_t launch_bwd_local(const BwdLocalLaunch& a);
 hipError_t launch_gva_sum(const GvaSumLaunch& a);
 hipError_t launch_act_reduce(const ActReduceLaunch& a);
+
+// Chain rule of the q/k L2 normalisation, in place: dx = (dy - x (x.dy) / n2)
+// / sqrt(n2) with n2 = sum x^2 + 1e-6 per row of K elements (x raw, dy the
+// gradient of the normalised row, both of the element type).
+struct L2BwdLaunch {
+    const void* x;
+    void* dx;               // holds dy on entry
+    int64_t rows;
+    int K;
+    bool bf16;
+    hipStream_t stream;
+};
+hipError_t launch_l2norm_bwd(const L2BwdLaunch& a);
 
 }  // namespace gdn

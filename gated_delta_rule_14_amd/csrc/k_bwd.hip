@@ -625,11 +625,12 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
     };
     // the loaded inputs to LDS
     auto put = [&](const Item& x) {
+        const bool l2 = a.act.flags & ACT_QK_L2NORM;   // a row is K / EV consecutive lanes
 #pragma unroll
         for (int p = 0; p < Item::NKQ; ++p) {
             const int i = tid + BLOCAL_THREADS * p, r = i / (K / EV), cv = (i % (K / EV)) * EV;
-            *reinterpret_cast<u32x4*>(sQ + r * LDK + cv) = x.q[p];
-            *reinterpret_cast<u32x4*>(sK + r * LDK + cv) = x.k[p];
+            *reinterpret_cast<u32x4*>(sQ + r * LDK + cv) = l2 ? l2norm_piece<T, K / EV>(x.q[p]) : x.q[p];
+            *reinterpret_cast<u32x4*>(sK + r * LDK + cv) = l2 ? l2norm_piece<T, K / EV>(x.k[p]) : x.k[p];
         }
 #pragma unroll
         for (int p = 0; p < Item::NVV; ++p) {
@@ -1064,6 +1065,70 @@ __global__ __launch_bounds__(256) void act_reduce_kernel(ActReduceLaunch a) {
 hipError_t launch_act_reduce(const ActReduceLaunch& a) {
     if (a.H <= 0) return hipSuccess;
     hipLaunchKernelGGL(act_reduce_kernel, dim3((unsigned)a.H), dim3(256), 0, a.stream, a);
+    return hipGetLastError();
+}
+
+// dx = (dy - x (x.dy) / n2) / sqrt(n2) per row, in place over dy: 16-byte
+// pieces, K / EV consecutive lanes per row.
+template <typename T, int K>
+__global__ __launch_bounds__(256) void l2norm_bwd_kernel(L2BwdLaunch a) {
+    constexpr int EV = 16 / sizeof(T), LPR = K / EV;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool live = i < a.rows * LPR;
+    const int64_t off = (live ? i : 0) * EV;   // idle lanes read piece 0 and store nothing
+    const u32x4 xp = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.x) + off);
+    const u32x4 dp = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dx) + off);
+    float x[EV], dy[EV];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (sizeof(T) == 2) {
+            x[2 * e] = __uint_as_float(xp[e] << 16);
+            x[2 * e + 1] = __uint_as_float(xp[e] & 0xffff0000u);
+            dy[2 * e] = __uint_as_float(dp[e] << 16);
+            dy[2 * e + 1] = __uint_as_float(dp[e] & 0xffff0000u);
+        } else {
+            x[e] = __uint_as_float(xp[e]);
+            dy[e] = __uint_as_float(dp[e]);
+        }
+    }
+    float ss = 0.f, xd = 0.f;
+#pragma unroll
+    for (int e = 0; e < EV; ++e) {
+        ss += x[e] * x[e];
+        xd += x[e] * dy[e];
+    }
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) {
+        ss += __shfl_xor(ss, o, 64);
+        xd += __shfl_xor(xd, o, 64);
+    }
+    const float n2 = ss + L2_EPS, c = xd / n2, inv = 1.f / sqrtf(n2);
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (sizeof(T) == 2)
+            r[e] = pack_bf16x2((dy[2 * e] - x[2 * e] * c) * inv, (dy[2 * e + 1] - x[2 * e + 1] * c) * inv);
+        else
+            r[e] = __float_as_uint((dy[e] - x[e] * c) * inv);
+    }
+    if (live) *reinterpret_cast<u32x4*>(static_cast<T*>(a.dx) + off) = r;
+}
+
+hipError_t launch_l2norm_bwd(const L2BwdLaunch& a) {
+    if (a.rows <= 0) return hipSuccess;
+    const int ev = a.bf16 ? 8 : 4;
+    const int64_t n = a.rows * (a.K / ev);
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (a.bf16 && a.K == 128)
+        hipLaunchKernelGGL((l2norm_bwd_kernel<bf16, 128>), grid, dim3(256), 0, a.stream, a);
+    else if (a.bf16 && a.K == 64)
+        hipLaunchKernelGGL((l2norm_bwd_kernel<bf16, 64>), grid, dim3(256), 0, a.stream, a);
+    else if (!a.bf16 && a.K == 128)
+        hipLaunchKernelGGL((l2norm_bwd_kernel<float, 128>), grid, dim3(256), 0, a.stream, a);
+    else if (!a.bf16 && a.K == 64)
+        hipLaunchKernelGGL((l2norm_bwd_kernel<float, 64>), grid, dim3(256), 0, a.stream, a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

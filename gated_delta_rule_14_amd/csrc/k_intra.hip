@@ -141,6 +141,13 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
         const int i = tid + NT * p, r = min(i / (V / EV), n - 1), cv = i % (V / EV);
         vr[p] = *reinterpret_cast<const u32x4*>(v + ((t0 + r) * H + h) * V + cv * EV);
     }
+    if (a.act.flags & ACT_QK_L2NORM) {   // a row is K / EV consecutive lanes
+#pragma unroll
+        for (int p = 0; p < PKQ; ++p) {
+            kr[p] = l2norm_piece<T, K / EV>(kr[p]);
+            qr[p] = l2norm_piece<T, K / EV>(qr[p]);
+        }
+    }
 
     // ---- a1: gates and beta; cumulative log2 gate (rows >= n: g = 0, beta = 0)
     if (!PK) {

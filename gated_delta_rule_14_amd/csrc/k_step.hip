@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void step_kernel(const T* __restrict__ q, cons
 
     __shared__ float s_k[K], s_q[K], s_d[K], s_v[V];
     __shared__ float4 s_p[RG][CG], s_s[RG][CG];
-    __shared__ float s_kq[RG];
+    __shared__ float s_kq[RG], s_kk[RG], s_qq[RG];
 
     float4* st = reinterpret_cast<float4*>(state + pair * (int64_t)(K * V));
     // issue the state loads first: they are the whole cost of the step
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(256) void step_kernel(const T* __restrict__ q, cons
     __syncthreads();
 
     float4 p = {0.f, 0.f, 0.f, 0.f}, s = {0.f, 0.f, 0.f, 0.f};
-    float kq = 0.f;
+    float kq = 0.f, kk = 0.f, qq = 0.f;
 #pragma unroll
     for (int i = 0; i < ROWS; ++i) {
         const int r = rg * ROWS + i;
@@ -77,21 +77,36 @@ __global__ __launch_bounds__(256) void step_kernel(const T* __restrict__ q, cons
         p.x += h[i].x * kr; p.y += h[i].y * kr; p.z += h[i].z * kr; p.w += h[i].w * kr;
         s.x += h[i].x * qr; s.y += h[i].y * qr; s.z += h[i].z * qr; s.w += h[i].w * qr;
         kq += kr * qr;
+        kk += kr * kr;
+        qq += qr * qr;
     }
     s_p[rg][cg] = p;
     s_s[rg][cg] = s;
-    if (cg == 0) s_kq[rg] = kq;
+    if (cg == 0) {
+        s_kq[rg] = kq;
+        s_kk[rg] = kk;
+        s_qq[rg] = qq;
+    }
     __syncthreads();
 
     float4 P = {0.f, 0.f, 0.f, 0.f}, S = {0.f, 0.f, 0.f, 0.f};
-    float KQ = 0.f;
+    float KQ = 0.f, KK = 0.f, QQ = 0.f;
 #pragma unroll
     for (int j = 0; j < RG; ++j) {
         const float4 a = s_p[j][cg], b = s_s[j][cg];
         P.x += a.x; P.y += a.y; P.z += a.z; P.w += a.w;
         S.x += b.x; S.y += b.y; S.z += b.z; S.w += b.w;
         KQ += s_kq[j];
+        KK += s_kk[j];
+        QQ += s_qq[j];
     }
+    // q, k L2-normalised: every product above is linear in k and in q, so the
+    // factors 1/|k| and 1/|q| are applied to the sums
+    const bool l2 = act.flags & ACT_QK_L2NORM;
+    const float ik = l2 ? 1.f / sqrtf(KK + L2_EPS) : 1.f, iq = l2 ? 1.f / sqrtf(QQ + L2_EPS) : 1.f;
+    P.x *= ik; P.y *= ik; P.z *= ik; P.w *= ik;
+    S.x *= iq; S.y *= iq; S.z *= iq; S.w *= iq;
+    KQ *= ik * iq;
     const float bt = (act.flags & ACT_BETA_SIGMOID)
                          ? act_beta(beta[pair], act.flags & ACT_BETA_NEG_EIG)
                          : beta[pair];
@@ -103,7 +118,7 @@ __global__ __launch_bounds__(256) void step_kernel(const T* __restrict__ q, cons
 
 #pragma unroll
     for (int i = 0; i < ROWS; ++i) {                          // write
-        const float kr = s_k[rg * ROWS + i];
+        const float kr = s_k[rg * ROWS + i] * ik;
         float4 x = h[i];
         x.x += kr * r.x; x.y += kr * r.y; x.z += kr * r.z; x.w += kr * r.w;
         // non-temporal: the state is not read again before it has left the

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 typedef int32_t gdn_status;
 enum {
@@ -117,11 +117,17 @@ typedef struct gdn_step_desc {
  *   GDN_ACT_BETA_NEG_EIG  with GDN_ACT_BETA_SIGMOID: beta = 2 sigmoid(b), in
  *                         (0, 2), so the eigenvalue 1 - beta of the write
  *                         ranges over (-1, 1)
+ *   GDN_ACT_QK_L2NORM     q and k are L2-normalised per token and head as
+ *                         they are read: x / sqrt(sum_K x^2 + 1e-6) ("TileLang
+ *                         实战" §1.2: unit-norm keys keep the write's
+ *                         eigenvalues in [-1, 1]; the pages fix no epsilon)
  * A_log [H] and dt_bias ([H] or [H, K]) are float device arrays, required
  * with GDN_ACT_GATE and otherwise ignored.  Unknown bits, or NEG_EIG without
- * BETA_SIGMOID, give GDN_ERR_UNSUPPORTED.
+ * BETA_SIGMOID, give GDN_ERR_UNSUPPORTED.  With GDN_ACT_QK_L2NORM the
+ * prefill always runs as two stages: size its workspace with
+ * gdn_chunk_fwd_workspace_act.
  */
-enum { GDN_ACT_GATE = 1, GDN_ACT_BETA_SIGMOID = 2, GDN_ACT_BETA_NEG_EIG = 4 };
+enum { GDN_ACT_GATE = 1, GDN_ACT_BETA_SIGMOID = 2, GDN_ACT_BETA_NEG_EIG = 4, GDN_ACT_QK_L2NORM = 8 };
 typedef struct gdn_activation {
     int32_t flags;           /* GDN_ACT_* */
     const float *A_log;      /* [H] */
@@ -149,6 +155,11 @@ const char *gdn_last_error(void);
  * gdn_workspace_layout_of().total.
  */
 gdn_status gdn_chunk_fwd_workspace(const gdn_fwd_desc *d, size_t *bytes);
+
+/* The same for gdn_chunk_fwd_act with the activation *act (NULL: exactly
+ * gdn_chunk_fwd_workspace); GDN_ACT_QK_L2NORM needs the two-stage layout. */
+gdn_status gdn_chunk_fwd_workspace_act(const gdn_fwd_desc *d, const gdn_activation *act,
+                                       size_t *bytes);
 
 /*
  * Chunked forward pass ("TileLang 实战" §2.2.4-2.3: UT transform and gated
@@ -363,7 +374,10 @@ gdn_status gdn_chunk_bwd(const gdn_fwd_desc *d,
  *            sum over the tokens of dlog_alpha * log_alpha
  *   ddt_bias [H_V] float, written with GDN_ACT_GATE (required then):
  *            sum over the tokens of d/da
- * Both are ignored without GDN_ACT_GATE.  Only the scalar gate is supported
+ * Both are ignored without GDN_ACT_GATE.  With GDN_ACT_QK_L2NORM, dq and dk
+ * are the gradients of the raw q and k: the normalisation's chain rule
+ * dx = (dy - x (x.dy) / n2) / sqrt(n2), n2 = sum_K x^2 + 1e-6, is applied to
+ * the gradients of the normalised rows.  Only the scalar gate is supported
  * (dt_bias [H_V]); the rest is as for gdn_chunk_bwd, with the same workspace.
  */
 gdn_status gdn_chunk_bwd_act(const gdn_fwd_desc *d, const gdn_activation *act,

@@ -146,7 +146,7 @@ def test_activation_rejects_before_launch(lib):
         return lib.gdn_recurrent_step_act(ctypes.byref(s), ctypes.byref(a), *([FAKE] * 7), None)
 
     for fn in (fwd, step):
-        assert fn(8, None, None) == 4            # unknown bit
+        assert fn(16, None, None) == 4           # unknown bit
         assert fn(4, None, None) == 4            # NEG_EIG without BETA_SIGMOID
         assert fn(1, None, FAKE) == 1            # GATE needs A_log
         assert fn(1 | 2, FAKE, None) == 1        # ... and dt_bias
@@ -202,7 +202,7 @@ def test_chunk_bwd_act_rejects_before_launch(lib):
         return lib.gdn_chunk_bwd_act(ctypes.byref(desc), ctypes.byref(a), FAKE, FAKE, FAKE, FAKE,
                                      FAKE, None, None, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
                                      None, dA_log, ddt_bias, FAKE, 1 << 40, None)
-    assert bwd(8) == 4                           # unknown bit
+    assert bwd(16) == 4                          # unknown bit
     assert bwd(4) == 4                           # NEG_EIG without BETA_SIGMOID
     assert bwd(1, A_log=None) == 1               # GATE needs A_log, dt_bias
     assert bwd(1, dA_log=None) == 1              # ... and the dA_log, ddt_bias outputs
@@ -210,3 +210,24 @@ def test_chunk_bwd_act_rejects_before_launch(lib):
     assert bwd(1, dA_log=odd) == 6
     assert bwd(1, desc=_desc(gate=1)) == 4       # scalar gate only
     assert lib.gdn_last_error().decode() != ""
+
+
+def test_l2norm_flag_and_workspace(lib):
+    """GDN_ACT_QK_L2NORM is a known bit; with it the fused kernel's shape
+    runs as two stages, so gdn_chunk_fwd_workspace_act asks for the whole
+    two-stage layout; an unknown bit is refused before anything else."""
+    d = _desc()
+    n = ctypes.c_size_t()
+
+    def ws(flags):
+        a = gdn.Activation(flags, None, None)
+        return lib.gdn_chunk_fwd_workspace_act(ctypes.byref(d), ctypes.byref(a), ctypes.byref(n))
+    assert ws(0) == 0 and n.value == gdn.workspace_bytes(d) == 256
+    assert ws(8) == 0 and n.value == gdn.workspace_layout(d).total
+    assert ws(16) == 4
+    assert lib.gdn_chunk_fwd_workspace_act(ctypes.byref(d), None, ctypes.byref(n)) == 0
+    assert n.value == 256
+    # the two-stage route with the flag still needs the whole layout
+    a = gdn.Activation(8, None, None)
+    assert lib.gdn_chunk_fwd_act(ctypes.byref(d), ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 None, None, FAKE, None, FAKE, 256, None) == 5
