@@ -22,8 +22,11 @@
 // chunkwise section): every 2^{G_i - G_j} sits inside the sum over the key
 // channel d.  Off-diagonal 16x16 blocks (I > J) factor through the first token
 // b of block I:  sum_d (k_id 2^{G_id - G_bd}) (k_jd 2^{G_bd - G_jd}), both
-// exponents <= 0, so they run on MFMA without overflow; the diagonal blocks
-// are summed pair by pair.  gamma and gamma_C/gamma become per-channel.
+// exponents <= 0, so they run on MFMA without overflow.  Inside a diagonal
+// block the same holds for its lower-left 8x8 quadrant (rows 8..15, columns
+// 0..7) with b its row 8, so that quadrant runs on MFMA too; the two 8x8
+// triangles left are summed pair by pair.  gamma and gamma_C/gamma become
+// per-channel.
 //
 // Layout choices: K, Q and V stay row-major (key- or value-contiguous) in
 // LDS.  Products that contract over tokens read them with transposing LDS
@@ -49,7 +52,9 @@ struct IntraSmem {
     // different banks
     static constexpr int LDG = PK ? K + 8 : 1;
     static constexpr int NB = C / 16;
-    static constexpr int SCR_ROWS = 32 + C - 16;   // per-key scaled operands (>= C)
+    // per-key scaled operands: 32 + C - 16 rows for an off-diagonal block
+    // row, 3 x C / 2 for the diagonal blocks' quadrants (and >= C)
+    static constexpr int SCR_ROWS = (32 + C - 16) > 3 * C / 2 ? 32 + C - 16 : 3 * C / 2;
     static constexpr size_t o_K = 0;
     static constexpr size_t o_Q = o_K + sizeof(T) * C * LDK;
     static constexpr size_t o_V = o_Q + sizeof(T) * C * LDK;
@@ -424,28 +429,83 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                 }
             }
         }
+        // lower-left 8x8 quadrant of each diagonal block, with b = 16 I + 8:
+        // rows [0, C/2): the 8 later K rows of each block, K 2^{G - G_b};
+        // [C/2, C): the same Q rows; [C, 3C/2): the 8 earlier K rows,
+        // K 2^{G_b - G}.  One 16x16 tile covers two blocks; its two
+        // cross-block quadrants are dropped.
+        static_assert(NB % 2 == 0, "diagonal blocks in pairs");
+        __syncthreads();   // the last off-diagonal tiles have read the scratch
+        for (int i = tid; i < (3 * C / 2) * (K / EV); i += NT) {
+            const int r = i / (K / EV), d0 = (i - r * (K / EV)) * EV;
+            const int set = r / (C / 2), rr = r - set * (C / 2), Ib = rr / 8;
+            const int b = 16 * Ib + 8, tok = set < 2 ? b + (rr & 7) : 16 * Ib + (rr & 7);
+            const uint4 xv = *reinterpret_cast<const uint4*>((set == 1 ? sQ : sK) + tok * LDK + d0);
+            float f[EV];
+#pragma unroll
+            for (int e4 = 0; e4 < EV; e4 += 4) {
+                const float4 gt = *reinterpret_cast<const float4*>(sG + tok * LDG + d0 + e4);
+                const float4 gb = *reinterpret_cast<const float4*>(sG + b * LDG + d0 + e4);
+                const float dt[4] = {gt.x - gb.x, gt.y - gb.y, gt.z - gb.z, gt.w - gb.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    f[e4 + e] = Vec16<T>::get(xv, e4 + e) * exp2_hw(fminf(set < 2 ? dt[e] : -dt[e], 0.f));
+            }
+            *reinterpret_cast<uint4*>(sS + r * LDK + d0) = Vec16<T>::pack(f);
+        }
+        __syncthreads();
+        if (wave < NB) {   // job (pair P of blocks, A or Aqk)
+            const int P = wave % (NB / 2);
+            const bool isq = wave >= NB / 2;
+            const int g4 = lane >> 4;
+            if (!isq) {
+                // rows: later K of blocks 2P, 2P+1; columns: their earlier K
+                const f32x4 acc = mma_tile<T>(sS + 16 * P * LDK, LDK, sS + (C + 16 * P) * LDK, LDK, K,
+                                              lane, zero4());
+                const int cc = acc_col(lane);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int rr = acc_row(lane, e);
+                    if (rr / 8 == cc / 8) {
+                        const int Ib = 2 * P + rr / 8, i = 16 * Ib + 8 + (rr & 7), j = 16 * Ib + (cc & 7);
+                        sA[i * LDA + j] = sB[i] * acc[e];
+                    }
+                }
+            } else {
+                // Aqk^T: rows the earlier K (j), columns the later Q (i)
+                f32x4 acc = mma_tile<T>(sS + (C + 16 * P) * LDK, LDK, sS + (C / 2 + 16 * P) * LDK, LDK,
+                                        K, lane, zero4());
+                const int cc = acc_col(lane);
+                if (g4 / 2 == cc / 8) {   // rows 4 g4 .. 4 g4 + 3 lie in column cc's block
+                    const int Ib = 2 * P + cc / 8;
+                    acc *= a.scale;
+                    store4_frag(gaqk, 16 * Ib + 8 + (cc & 7), 16 * Ib + 4 * (g4 & 1), C, acc);
+                }
+            }
+        }
         // upper blocks of Aqk: zeros (those of A are masked when Ainv is read)
         for (int i = tid; i < C * C; i += NT) {
             const int r = i / C, j = i - r * C;
             if (j / 16 > r / 16) Elem<T>::store(gaqk + FragOrder<T>::off(r, j, C), 0.f);
         }
-        // diagonal 16x16 blocks, pair by pair: thread = (block, row i, a
-        // contiguous slice of CH channels); row i's keys, queries and gates
-        // stay in registers while j runs over the block, K_j and G_j are
-        // vector reads shared by the wave's 8 rows, and the slice sums are
-        // added over the SL = 8 neighbouring lanes with DPP (the total lands
-        // in slice SL-1).  Wave w takes rows 8(w/4) .. 8(w/4)+7 of block
-        // w%4 and runs j only up to its last row, so the two waves that share
-        // a SIMD (w, w+4) do 8 + 16 steps; pairs j > i inside that range are
-        // computed and dropped (valid pairs have G_i <= G_j, so the decay
-        // exponent needs no clamp there).
+        // the two 8x8 triangles of each diagonal block, pair by pair: thread
+        // = (block, row i, a contiguous slice of CH channels); row i's keys,
+        // queries and gates stay in registers while j runs over the row's
+        // half of the block, K_j and G_j are vector reads shared by the
+        // wave's 8 rows, and the slice sums are added over the SL = 8
+        // neighbouring lanes with DPP (the total lands in slice SL-1).  Wave
+        // w takes rows 8(w/4) .. 8(w/4)+7 of block w%4 and columns of the
+        // same half, so the two waves that share a SIMD (w, w+4) do 8 + 8
+        // steps; pairs j > i inside that range are computed and dropped
+        // (valid pairs have G_i <= G_j, so the decay exponent needs no clamp
+        // there).
         {
             constexpr int SL = NT / (NB * 16);      // threads per row
             constexpr int CH = K / SL;              // channels per thread
             static_assert(SL == 8 && CH % EV == 0 && CH % 4 == 0, "8 lanes per row, whole vectors");
             static_assert(NW == 2 * NB, "two waves per diagonal block");
             const int I = wave % NB, half = wave / NB, i = 16 * I + 8 * half + lane / SL, s = lane % SL;
-            const int c0 = CH * s, jend = 16 * I + 8 * half + 8;
+            const int c0 = CH * s, jbeg = 16 * I + 8 * half, jend = jbeg + 8;
             auto sum8 = [](float x) {
                 x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));  // quad_perm 1,0,3,2
                 x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));  // quad_perm 2,3,0,1
@@ -482,8 +542,8 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                 for (int v = 0; v < CH / 4; ++v)
                     ng[v] = *reinterpret_cast<const float4*>(sG + j * LDG + c0 + 4 * v);
             };
-            fetch(16 * I);
-            for (int j = 16 * I; j < jend; ++j) {
+            fetch(jbeg);
+            for (int j = jbeg; j < jend; ++j) {
                 uint4 ck[CH / EV];
                 float gjv[CH];
 #pragma unroll
