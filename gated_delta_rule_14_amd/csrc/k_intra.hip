@@ -134,6 +134,18 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
     constexpr int NKV = C * K / EV, NVV = C * V / EV;
     static_assert(NKV % NT == 0 && NVV % NT == 0, "whole passes");
     constexpr int PKQ = NKV / NT, PV = NVV / NT;
+    // the per-key gate first: the gate scan below needs only it, and runs
+    // while K, Q and V are still arriving
+    constexpr int TPC = NT / K, RPT = C / TPC;   // threads per channel, rows per thread
+    float graw[PK ? RPT : 1];
+    if constexpr (PK) {
+        const int d = tid % K, qq = tid / K;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = qq * RPT + i;
+            graw[i] = r < n ? a.g[((t0 + r) * H + h) * K + d] : 0.f;
+        }
+    }
     u32x4 kr[PKQ], qr[PKQ], vr[PV];
 #pragma unroll
     for (int p = 0; p < PKQ; ++p) {
@@ -145,13 +157,6 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
     for (int p = 0; p < PV; ++p) {
         const int i = tid + NT * p, r = min(i / (V / EV), n - 1), cv = i % (V / EV);
         vr[p] = *reinterpret_cast<const u32x4*>(v + ((t0 + r) * H + h) * V + cv * EV);
-    }
-    if (a.act.flags & ACT_QK_L2NORM) {   // a row is K / EV consecutive lanes
-#pragma unroll
-        for (int p = 0; p < PKQ; ++p) {
-            kr[p] = l2norm_piece<T, K / EV>(kr[p]);
-            qr[p] = l2norm_piece<T, K / EV>(qr[p]);
-        }
     }
 
     // ---- a1: gates and beta; cumulative log2 gate (rows >= n: g = 0, beta = 0)
@@ -179,15 +184,11 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
         // Thread (quarter qq, channel d) loads and scans rows qq*RPT ..
         // (qq+1)*RPT-1 (all its loads in flight together); the quarter totals
         // go through LDS (the sP scratch) and each quarter adds those before it.
-        constexpr int TPC = NT / K, RPT = C / TPC;
         static_assert(TPC * RPT == C && TPC * K <= 4 * 16 * 17, "gate scan split");
         const int d = tid % K, qq = tid / K;
         float gv[RPT];
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int r = qq * RPT + i;
-            gv[i] = r < n ? a.g[((t0 + r) * H + h) * K + d] : 0.f;
-        }
+        for (int i = 0; i < RPT; ++i) gv[i] = graw[i];
         float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
@@ -209,6 +210,13 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
             sB[r] = r >= n ? 0.f
                     : (a.act.flags & ACT_BETA_SIGMOID) ? act_beta(br, a.act.flags & ACT_BETA_NEG_EIG)
                                                         : br;
+        }
+    }
+    if (a.act.flags & ACT_QK_L2NORM) {   // a row is K / EV consecutive lanes
+#pragma unroll
+        for (int p = 0; p < PKQ; ++p) {
+            kr[p] = l2norm_piece<T, K / EV>(kr[p]);
+            qr[p] = l2norm_piece<T, K / EV>(qr[p]);
         }
     }
 #pragma unroll
