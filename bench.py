@@ -292,6 +292,56 @@ def bench_kda(args, gdn):
                                         "traffic": measured_traffic("kda_scan_kernel")}}}
 
 
+def bench_variants(args, gdn):
+    """The prefill workload (B=4, T=4096, H=16, d=128, bf16) with each input
+    option of the forward: raw gate and beta logits activated inside the
+    kernel, beta in (0, 2), two value heads per q/k head (16 value heads on 8
+    q/k heads) and q/k L2 normalisation (which runs as two stages).  Whole
+    calls, timed with an event pair around back-to-back calls of the C entry
+    point on arguments marshalled once (the binding's per-call checks would
+    otherwise take longer than the kernel)."""
+    import ctypes
+    from gated_delta_rule_14_amd import _binding as B
+    lib = gdn.load()
+    spec = gdn_synth.PREFILL[1]
+    log("generating", spec.name, "(raw logits)")
+    d = gdn_synth.make_prefill(spec, 1, logits=True)
+    x = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    q, k, v, beta, g, h0 = (x[n] for n in ("q", "k", "v", "beta", "g", "h0"))
+    o, ht = torch.empty_like(v), torch.empty_like(h0)
+    A_log, dt_bias = x["A_log"], x["dt_bias"]
+    logits = gdn.activation(gate_logits=True, beta_sigmoid=True, A_log=A_log, dt_bias=dt_bias)
+    # the same gates activated beforehand (input preparation), for the cases
+    # that take activated g and beta
+    g_act = -torch.exp(A_log) * torch.nn.functional.softplus(g + dt_bias)
+    b_act = torch.sigmoid(beta)
+    cases = {"plain": (q, k, g_act, b_act, None),
+             "gate_beta_logits": (q, k, g, beta, logits),
+             "neg_eig": (q, k, g, beta, gdn.activation(gate_logits=True, beta_sigmoid=True,
+                                                       neg_eig=True, A_log=A_log, dt_bias=dt_bias)),
+             "qk_l2norm": (q, k, g_act, b_act, gdn.activation(qk_l2norm=True)),
+             "gva_m2": (q[:, :, ::2].contiguous(), k[:, :, ::2].contiguous(), g, beta, logits)}
+    reps = max(args.steps // 5, 20)
+    out = {"workload": spec.name}
+    first = True
+    for name, (qq, kk, gg, bb, act) in cases.items():
+        desc = gdn.fwd_desc(qq, v, "scalar", spec.chunk, d["scale"])
+        nbytes = gdn.workspace_bytes(desc, act)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        cargs = (ctypes.byref(desc), ctypes.byref(act) if act is not None else None,
+                 B._ptr(qq), B._ptr(kk), B._ptr(v), B._ptr(bb), B._ptr(gg), B._ptr(h0), None,
+                 B._ptr(o), B._ptr(ht), B._ptr(ws), nbytes, B._stream(None))
+        B._check(lib.gdn_chunk_fwd_act(*cargs))
+        if first:   # the clock settles again after the host-side input generation
+            for _ in range(args.warmup):
+                lib.gdn_chunk_fwd_act(*cargs)
+            first = False
+        out[name + "_us"] = 1e6 * events_time(lambda: lib.gdn_chunk_fwd_act(*cargs), reps)
+    log("input options: " + ", ".join("%s %.1f us" % (n[:-3], t) for n, t in out.items()
+                                     if n.endswith("_us")))
+    return out
+
+
 def bench_varlen(args, gdn):
     """The packed variable-length workload (fused route; the longest
     sequence, 65 536 tokens, sets the time): whole calls, events."""
@@ -355,6 +405,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-kda", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (a known-size kernel to scale "
                          "hardware byte counters by)")
@@ -378,6 +429,7 @@ def main():
     backward = None if args.no_backward else bench_backward(args, gdn, d)
     kda = None if args.no_kda else bench_kda(args, gdn)
     varlen = None if args.no_varlen else bench_varlen(args, gdn)
+    variants = None if args.no_variants else bench_variants(args, gdn)
     cpu = None if args.no_cpu else cpu_baseline(d)
     line = {
         "metric": METRIC,
@@ -404,6 +456,7 @@ def main():
         "backward": backward,
         "kda": kda,
         "varlen": varlen,
+        "input_options": variants,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line), flush=True)
