@@ -18,9 +18,10 @@
  *
  * The output of step t reads the state after token t's own write.  q and k are
  * used as given: L2 normalisation is the caller's precondition ("TileLang
- * 实战" §0 and §1.2).  beta is used as given (normally in (0, 1); any value in
- * (0, 2) gives the write a negative eigenvalue 1 - beta), unless the
- * *_act entry points are asked to activate it (gdn_activation below).
+ * 实战" §0 and §1.2), unless the *_act entry points are asked to normalise
+ * them (GDN_ACT_QK_L2NORM below).  beta is used as given (normally in (0, 1);
+ * any value in (0, 2) gives the write a negative eigenvalue 1 - beta), unless
+ * the *_act entry points are asked to activate it (gdn_activation below).
  *
  * Conventions shared by every entry point
  *  - Every pointer argument is device memory owned by the caller (any memory
