@@ -63,13 +63,29 @@ gdn_status check_desc(const gdn_fwd_desc* d, bool packed) {
         return fail(GDN_ERR_BAD_SHAPE, "num_v_heads %lld must be 0 or a multiple of num_heads %lld",
                     (long long)d->num_v_heads, (long long)d->num_heads);
     if (d->chunk != 64)
-        return fail(GDN_ERR_UNSUPPORTED, "chunk %d (this build implements 64)", d->chunk);
+        return fail(GDN_ERR_UNSUPPORTED,
+                    d->chunk == 16 || d->chunk == 32
+                        ? "chunk %d: the entry points that expose per-chunk intermediates use 64"
+                        : "chunk %d (supported: 16, 32, 64)",
+                    d->chunk);
     if (!dim_ok(d->key_dim) || !dim_ok(d->value_dim))
         return fail(GDN_ERR_UNSUPPORTED, "K=%lld V=%lld (supported: 64, 128)",
                     (long long)d->key_dim, (long long)d->value_dim);
     if (d->qkv_dtype == GDN_DTYPE_F32 && d->gate == GDN_GATE_PER_KEY && d->key_dim == 128)
         return fail(GDN_ERR_UNSUPPORTED, "fp32 q/k/v with the per-key gate needs K = 64");
     return GDN_OK;
+}
+
+// The entry points that return only o, ht or gradients accept chunk 16, 32
+// or 64: the chunked form reaches the recurrence's result whatever the chunk
+// size ("TileLang 实战" §2.3), so they compute with the 64-token tiling, and
+// the chunk size changes rounding only.  The layout query and gdn_chunk_intra
+// / gdn_chunk_scan, whose workspace holds per-chunk intermediates, take 64.
+const gdn_fwd_desc* tiled(const gdn_fwd_desc* d, gdn_fwd_desc* tmp) {
+    if (!d || (d->chunk != 16 && d->chunk != 32)) return d;
+    *tmp = *d;
+    tmp->chunk = 64;
+    return tmp;
 }
 
 int64_t max_chunks_of(const gdn_fwd_desc* d, bool packed) {
@@ -314,8 +330,10 @@ gdn_status gdn_workspace_layout_of(const gdn_fwd_desc* d, gdn_workspace_layout* 
     return ok();
 }
 
-gdn_status gdn_chunk_fwd_workspace_act(const gdn_fwd_desc* d, const gdn_activation* act_in,
+gdn_status gdn_chunk_fwd_workspace_act(const gdn_fwd_desc* d_in, const gdn_activation* act_in,
                                        size_t* bytes) {
+    gdn_fwd_desc tmp;
+    const gdn_fwd_desc* d = tiled(d_in, &tmp);
     if (!bytes) return fail(GDN_ERR_NULL_ARG, "bytes is NULL");
     gdn::Act act;
     gdn_status s = check_act(act_in, &act);
@@ -454,10 +472,12 @@ static gdn_status fused_fwd(const gdn_fwd_desc* d, const void* q, const void* k,
     return ok();
 }
 
-gdn_status gdn_chunk_fwd_act(const gdn_fwd_desc* d, const gdn_activation* act_in, const void* q,
+gdn_status gdn_chunk_fwd_act(const gdn_fwd_desc* d_in, const gdn_activation* act_in, const void* q,
                              const void* k, const void* v, const float* beta, const float* g,
                              const float* h0, const int64_t* cu_seqlens, void* o, float* ht,
                              void* workspace, size_t workspace_bytes, void* stream) {
+    gdn_fwd_desc tmp;
+    const gdn_fwd_desc* d = tiled(d_in, &tmp);
     const bool packed = cu_seqlens != nullptr;
     gdn_status s = check_desc(d, packed);
     if (s != GDN_OK) return s;
@@ -484,8 +504,10 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_desc* d, const void* q, const void* k, co
                              workspace_bytes, stream);
 }
 
-gdn_status gdn_chunk_bwd_workspace(const gdn_fwd_desc* d, size_t* bytes) {
+gdn_status gdn_chunk_bwd_workspace(const gdn_fwd_desc* d_in, size_t* bytes) {
     if (!bytes) return fail(GDN_ERR_NULL_ARG, "bytes is NULL");
+    gdn_fwd_desc tmp;
+    const gdn_fwd_desc* d = tiled(d_in, &tmp);
     const bool packed = d && d->num_seqs > 0;
     gdn_status s = check_bwd_desc(d, packed);
     if (s != GDN_OK) return s;
@@ -495,12 +517,14 @@ gdn_status gdn_chunk_bwd_workspace(const gdn_fwd_desc* d, size_t* bytes) {
     return ok();
 }
 
-gdn_status gdn_chunk_bwd_act(const gdn_fwd_desc* d, const gdn_activation* act_in, const void* q,
+gdn_status gdn_chunk_bwd_act(const gdn_fwd_desc* d_in, const gdn_activation* act_in, const void* q,
                              const void* k, const void* v, const float* beta, const float* g,
                              const float* h0, const int64_t* cu_seqlens, const void* dout,
                              const float* dht, void* dq, void* dk, void* dv, float* dbeta,
                              float* dg, float* dh0, float* dA_log, float* ddt_bias,
                              void* workspace, size_t workspace_bytes, void* stream) {
+    gdn_fwd_desc tmp;
+    const gdn_fwd_desc* d = tiled(d_in, &tmp);
     const bool packed = cu_seqlens != nullptr;
     gdn_status s = check_bwd_desc(d, packed);
     if (s != GDN_OK) return s;

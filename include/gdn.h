@@ -77,12 +77,22 @@ typedef struct gdn_fwd_desc {
     int64_t key_dim;    /* K, in {64, 128} */
     int64_t value_dim;  /* V, in {64, 128} */
     int64_t num_seqs;   /* N packed sequences when cu_seqlens is given, else 0 */
-    int32_t chunk;      /* C in {16, 32, 64} */
+    int32_t chunk;      /* C in {16, 32, 64}; see "Chunk size" below */
     int32_t qkv_dtype;  /* GDN_DTYPE_* of q, k, v, o */
     int32_t gate;       /* GDN_GATE_* */
     float scale;        /* multiplies q (usually 1/sqrt(K)) */
     int64_t num_v_heads;  /* H_V value heads (0: H_V = H); see GVA below */
 } gdn_fwd_desc;
+
+/*
+ * Chunk size.  The chunked form reaches the recurrence's result whatever the
+ * chunk size ("TileLang 实战" §2.3; the pages allow 16, 32 and 64), so the
+ * entry points that return only outputs, states or gradients
+ * (gdn_chunk_fwd[_act], gdn_chunk_bwd[_act] and their workspace queries)
+ * accept 16, 32 and 64 and compute with their 64-token tiling: the chunk size
+ * changes rounding only.  gdn_workspace_layout_of, gdn_chunk_intra and
+ * gdn_chunk_scan, whose workspace holds per-chunk intermediates, need 64.
+ */
 
 /* Shape of a single-token (decode) step over N independent sequences. */
 typedef struct gdn_step_desc {

@@ -50,7 +50,7 @@ def _status(fn, *args):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(chunk=32), 4), (dict(chunk=128), 4), (dict(key_dim=96), 4), (dict(value_dim=256), 4),
+    (dict(chunk=48), 4), (dict(chunk=128), 4), (dict(chunk=8), 4), (dict(key_dim=96), 4), (dict(value_dim=256), 4),
     (dict(qkv_dtype=7), 3), (dict(gate=5), 3), (dict(batch=0), 2), (dict(num_heads=0), 2),
     (dict(seq_len=-1), 2), (dict(qkv_dtype=0, gate=1, key_dim=128), 4),
     (dict(batch=2, num_seqs=3), 2), (dict(num_heads=4, num_v_heads=6), 2),
@@ -167,7 +167,8 @@ def test_chunk_bwd_rejects_before_launch(lib):
     assert ws(_desc(num_v_heads=6)) == 2                # not a multiple of H
     assert ws(_desc(qkv_dtype=0)) == 4                  # fp32 needs K = V = 64
     assert ws(_desc(qkv_dtype=0, key_dim=64, value_dim=64)) == 0
-    assert ws(_desc(chunk=32)) == 4
+    assert ws(_desc(chunk=48)) == 4
+    assert ws(_desc(chunk=32)) == 0 and n.value == base          # computed with 64-token tiles
     # the workspace grows with the per-chunk states: above the forward layout
     assert n.value > gdn.workspace_layout(_desc(qkv_dtype=0, key_dim=64, value_dim=64)).total
     d = _desc()
@@ -231,3 +232,20 @@ def test_l2norm_flag_and_workspace(lib):
     a = gdn.Activation(8, None, None)
     assert lib.gdn_chunk_fwd_act(ctypes.byref(d), ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE,
                                  None, None, FAKE, None, FAKE, 256, None) == 5
+
+
+def test_chunk_sizes(lib):
+    """chunk 16 and 32 are accepted where only outputs come back (computed
+    with the 64-token tiling: same workspace) and refused, before any launch,
+    where the workspace holds per-chunk intermediates."""
+    n = ctypes.c_size_t()
+    for c in (16, 32):
+        assert gdn.workspace_bytes(_desc(chunk=c)) == gdn.workspace_bytes(_desc())
+        assert gdn.workspace_bytes(_desc(chunk=c, qkv_dtype=0)) == gdn.workspace_bytes(_desc(qkv_dtype=0))
+        L = gdn.WorkspaceLayout()
+        assert lib.gdn_workspace_layout_of(ctypes.byref(_desc(chunk=c)), ctypes.byref(L)) == 4
+        assert lib.gdn_chunk_intra(ctypes.byref(_desc(chunk=c)), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                   FAKE, 1 << 40, 0, None) == 4
+        assert lib.gdn_chunk_scan(ctypes.byref(_desc(chunk=c)), None, None, FAKE, None, FAKE, 1 << 40,
+                                  None) == 4
+        assert "per-chunk" in lib.gdn_last_error().decode()
