@@ -13,19 +13,20 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_SCALAR, GATE_PER_KEY = 0, 1
 STATUS = {0: "GDN_OK", 1: "GDN_ERR_NULL_ARG", 2: "GDN_ERR_BAD_SHAPE", 3: "GDN_ERR_BAD_DTYPE",
           4: "GDN_ERR_UNSUPPORTED", 5: "GDN_ERR_WORKSPACE_TOO_SMALL", 6: "GDN_ERR_MISALIGNED",
-          7: "GDN_ERR_HIP"}
+          7: "GDN_ERR_HIP", 8: "GDN_ERR_BAD_SEQLENS"}
 EXPORTS = sorted(["gdn_abi_version", "gdn_status_str", "gdn_last_error",
                   "gdn_chunk_fwd_workspace", "gdn_chunk_fwd_workspace_act", "gdn_chunk_fwd",
                   "gdn_workspace_layout_of",
                   "gdn_chunk_intra", "gdn_chunk_scan", "gdn_recurrent_step",
                   "gdn_chunk_fwd_act", "gdn_recurrent_step_act",
-                  "gdn_chunk_bwd_workspace", "gdn_chunk_bwd", "gdn_chunk_bwd_act"])
+                  "gdn_chunk_bwd_workspace", "gdn_chunk_bwd", "gdn_chunk_bwd_act",
+                  "gdn_seqlens_status_offset"])
 INTRA_STORE_AINV = 1
 ACT_GATE, ACT_BETA_SIGMOID, ACT_BETA_NEG_EIG, ACT_QK_L2NORM = 1, 2, 4, 8
 
@@ -109,6 +110,9 @@ def load(path: str = LIB_PATH):
     lib.gdn_chunk_bwd_act.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(Activation)] + \
         [P] * 18 + [ctypes.c_size_t, P]
     lib.gdn_chunk_bwd_act.restype = S
+    lib.gdn_seqlens_status_offset.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(Activation),
+                                              ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdn_seqlens_status_offset.restype = S
     v = lib.gdn_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError("libgdn.so ABI %d, binding expects %d" % (v, ABI_VERSION))
@@ -119,6 +123,25 @@ def load(path: str = LIB_PATH):
 def _check(status: int):
     if status != 0:
         raise GdnError(status, _lib.gdn_last_error().decode())
+
+
+def _debug():
+    return os.environ.get("GDN_DEBUG", "") not in ("", "0")
+
+
+def seqlens_status(desc, workspace, act=None, backward=False):
+    """The check of cu_seqlens that a packed call left in its workspace
+    (gdn_seqlens_status_offset): raises GdnError(GDN_ERR_BAD_SEQLENS) if the
+    offsets did not start at 0, decreased or did not end at T.  Waits for the
+    current stream.  chunk_fwd and chunk_bwd call it when GDN_DEBUG is set."""
+    lib = load()
+    off = ctypes.c_size_t()
+    _check(lib.gdn_seqlens_status_offset(ctypes.byref(desc),
+                                         ctypes.byref(act) if act is not None else None,
+                                         1 if backward else 0, ctypes.byref(off)))
+    word = int(workspace[off.value:off.value + 4].view(torch.int32).item())
+    if word != 0:
+        raise GdnError(8, "cu_seqlens must start at 0, never decrease and end at T")
 
 
 def _ptr(t):
@@ -248,6 +271,8 @@ def chunk_fwd(q, k, v, beta, g, scale=None, h0=None, cu_seqlens=None, chunk=64,
     else:
         _act_shapes(act, H, K, gate)
         _check(lib.gdn_chunk_fwd_act(ctypes.byref(desc), ctypes.byref(act), *args))
+    if cu_seqlens is not None and _debug():
+        seqlens_status(desc, workspace, act)
     return o, (ht if output_final_state else None)
 
 
@@ -312,6 +337,8 @@ def chunk_bwd(q, k, v, beta, g, do, scale=None, h0=None, dht=None, cu_seqlens=No
         _check(lib.gdn_chunk_bwd_act(ctypes.byref(desc), ctypes.byref(act), *args,
                                      _ptr(out.get("dA_log")) if act_gate else None,
                                      _ptr(out.get("ddt_bias")) if act_gate else None, *tail))
+    if cu_seqlens is not None and _debug():
+        seqlens_status(desc, workspace, act, backward=True)
     return out
 
 

@@ -115,7 +115,8 @@ void layout(const gdn_fwd_desc* d, bool packed, gdn_workspace_layout* L) {
     off = align256(off + blocks * C * C * 4);
     L->chunks = off;
     L->seqs = off + (size_t)mc * 16;
-    off = align256(off + (size_t)mc * 16 + (size_t)(packed ? d->num_seqs : 0) * 16);
+    // (packed: the per-sequence records, then the offsets' check word)
+    off = align256(off + (size_t)mc * 16 + (size_t)(packed ? d->num_seqs + 1 : 0) * 16);
     L->total = off;
     L->max_chunks = mc;
 }
@@ -187,7 +188,7 @@ bool fused_path(const gdn_fwd_desc* d, int act_flags = 0) {
 }
 
 size_t fused_workspace(const gdn_fwd_desc* d, bool packed) {
-    return align256((size_t)(packed ? d->num_seqs : 1) * 16);
+    return align256((size_t)(packed ? d->num_seqs + 1 : 1) * 16);
 }
 
 gdn_status hip_fail(hipError_t e, const char* what) {
@@ -315,6 +316,7 @@ const char* gdn_status_str(gdn_status s) {
         case GDN_ERR_WORKSPACE_TOO_SMALL: return "GDN_ERR_WORKSPACE_TOO_SMALL";
         case GDN_ERR_MISALIGNED: return "GDN_ERR_MISALIGNED";
         case GDN_ERR_HIP: return "GDN_ERR_HIP";
+        case GDN_ERR_BAD_SEQLENS: return "GDN_ERR_BAD_SEQLENS";
         default: return "GDN_ERR_UNKNOWN";
     }
 }
@@ -342,6 +344,32 @@ gdn_status gdn_chunk_fwd_workspace_act(const gdn_fwd_desc* d_in, const gdn_activ
     s = gdn_workspace_layout_of(d, &L);
     if (s != GDN_OK) return s;
     *bytes = fused_path(d, act.flags) ? fused_workspace(d, d->num_seqs > 0) : L.total;
+    return ok();
+}
+
+gdn_status gdn_seqlens_status_offset(const gdn_fwd_desc* d_in, const gdn_activation* act_in,
+                                     int32_t backward, size_t* offset) {
+    if (!offset) return fail(GDN_ERR_NULL_ARG, "offset is NULL");
+    gdn_fwd_desc tmp;
+    const gdn_fwd_desc* d = tiled(d_in, &tmp);
+    gdn_status s = backward ? check_bwd_desc(d, true) : check_desc(d, true);
+    if (s != GDN_OK) return s;
+    gdn::Act act;
+    s = check_act(act_in, &act);
+    if (s != GDN_OK) return s;
+    // the word follows the num_seqs 16-byte records of the sequence table
+    const size_t rec = (size_t)d->num_seqs * 16;
+    if (backward) {
+        BwdLayout L;
+        bwd_layout(d, true, &L);
+        *offset = L.f.seqs + rec;
+    } else if (fused_path(d, act.flags)) {
+        *offset = rec;
+    } else {
+        gdn_workspace_layout L;
+        layout(d, true, &L);
+        *offset = L.seqs + rec;
+    }
     return ok();
 }
 

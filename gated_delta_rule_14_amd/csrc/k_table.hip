@@ -10,6 +10,8 @@
 // offsets can give wrong results but never an out-of-bounds access.
 //   seqs[n]  = (first token, length, first chunk, order[n])
 //   table[c] = (first token, token count, sequence, 0); unused rows have count 0
+//   the int32 after seqs[N-1]: 0 if the offsets start at 0, never decrease
+//   and end at T, else 1
 // order[r] is the sequence of rank r by length, longest first (ties by
 // index): the kernels that walk one sequence's chunks serially take their
 // workgroups longest first, so the longest chain starts with the first wave
@@ -27,15 +29,21 @@ __global__ __launch_bounds__(256) void table_kernel(TableLaunch a) {
     __shared__ int64_t s_part[256];
     __shared__ int64_t s_carry;
     __shared__ int s_len[ORDER_MAX];
+    __shared__ int s_bad;
     const int tid = threadIdx.x;
-    if (tid == 0) s_carry = 0;
+    if (tid == 0) {
+        s_carry = 0;
+        s_bad = 0;
+    }
     __syncthreads();
     for (int64_t base = 0; base < a.N; base += 256) {
         const int64_t n = base + tid;
         int64_t s = 0, len = 0, nc = 0;
         if (n < a.N) {
-            s = min(max(a.cu_seqlens[n], (int64_t)0), a.T);
-            const int64_t e = min(max(a.cu_seqlens[n + 1], s), a.T);
+            const int64_t rs = a.cu_seqlens[n], re = a.cu_seqlens[n + 1];
+            if (re < rs || (n == 0 && rs != 0) || (n == a.N - 1 && re != a.T)) atomicOr(&s_bad, 1);
+            s = min(max(rs, (int64_t)0), a.T);
+            const int64_t e = min(max(re, s), a.T);
             len = e - s;
             nc = (len + a.C - 1) / a.C;
         }
@@ -65,6 +73,8 @@ __global__ __launch_bounds__(256) void table_kernel(TableLaunch a) {
     if (a.table)
         for (int64_t c = s_carry + tid; c < a.max_chunks; c += 256)
             a.table[c] = make_int4(0, 0, -1, 0);
+    __syncthreads();   // every thread's offset check is in s_bad
+    if (tid == 0) *reinterpret_cast<int*>(a.seqs + a.N) = s_bad;
     if (a.N <= ORDER_MAX) {   // rank by length: order[rank(n)] = n
         __syncthreads();      // s_len complete, and the identity orders written above
         const int N = (int)a.N;

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 typedef int32_t gdn_status;
 enum {
@@ -61,7 +61,10 @@ enum {
     GDN_ERR_UNSUPPORTED = 4,     /* chunk not in {16,32,64}; K, V not in {64,128} */
     GDN_ERR_WORKSPACE_TOO_SMALL = 5,
     GDN_ERR_MISALIGNED = 6,      /* a pointer lacks the alignment stated below */
-    GDN_ERR_HIP = 7              /* a kernel launch failed; see gdn_last_error() */
+    GDN_ERR_HIP = 7,             /* a kernel launch failed; see gdn_last_error() */
+    GDN_ERR_BAD_SEQLENS = 8      /* packed offsets invalid: found on the device, read
+                                    through gdn_seqlens_status_offset (never returned
+                                    by a compute call, which does not wait for it) */
 };
 
 /* element type of q, k, v and o */
@@ -145,6 +148,23 @@ typedef struct gdn_activation {
     const float *dt_bias;    /* [H] (scalar gate) or [H, K] (per-key gate) */
 } gdn_activation;
 
+/*
+ * Where a packed call leaves its check of cu_seqlens in the workspace (byte
+ * offset from the workspace start, written to *offset): an int32 that the
+ * call's chunk-table kernel sets to 0 when the offsets start at 0, never
+ * decrease and end at seq_len, and to 1 otherwise (invalid offsets are also
+ * clamped into [0, seq_len], so they never cause an access out of bounds;
+ * the results are then undefined).  backward = 0: gdn_chunk_fwd[_act] with
+ * *act (NULL allowed), gdn_chunk_intra and gdn_chunk_scan use the
+ * two-stage layout's word, which is the same unless the call ran as the
+ * single-pass kernel; backward = 1: gdn_chunk_bwd[_act].  The word is valid
+ * once the call's stream has reached it; reading it is the caller's (a
+ * debugging aid: it needs a wait on the stream).  d must describe packed
+ * input (num_seqs > 0).
+ */
+gdn_status gdn_seqlens_status_offset(const gdn_fwd_desc *d, const gdn_activation *act,
+                                     int32_t backward, size_t *offset);
+
 /* Integer version of this ABI (GDN_ABI_VERSION), for binding checks. */
 int gdn_abi_version(void);
 
@@ -194,8 +214,10 @@ gdn_status gdn_chunk_fwd_workspace_act(const gdn_fwd_desc *d, const gdn_activati
  *          offsets, starting at 0, nondecreasing, ending at T (B must be 1).
  *          Chunks restart at every sequence start and every sequence starts
  *          from its own h0 ("Gated Delta Network（GDN）", terminology note:
- *          a chunk boundary is not a sequence boundary).  Offsets are not
- *          checked on the device: bad offsets give undefined results.
+ *          a chunk boundary is not a sequence boundary).  Offsets are
+ *          checked on the device without stopping the call: bad offsets
+ *          give undefined results (never an access out of bounds) and set
+ *          the word of gdn_seqlens_status_offset.
  *   o      [B, T, H, V]   qkv_dtype, output
  *   ht     [N, H, K, V]   float, final state; NULL means not returned.
  *          ht may equal h0 (in-place carry); no other aliasing is allowed.

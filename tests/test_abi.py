@@ -249,3 +249,26 @@ def test_chunk_sizes(lib):
         assert lib.gdn_chunk_scan(ctypes.byref(_desc(chunk=c)), None, None, FAKE, None, FAKE, 1 << 40,
                                   None) == 4
         assert "per-chunk" in lib.gdn_last_error().decode()
+
+
+def test_seqlens_status_offset(lib):
+    """Where a packed call leaves its check of cu_seqlens: after the
+    per-sequence records, inside the workspace the call is sized for."""
+    off = ctypes.c_size_t()
+
+    def where(d, act=None, backward=0):
+        return lib.gdn_seqlens_status_offset(ctypes.byref(d), ctypes.byref(act) if act else None,
+                                             backward, ctypes.byref(off))
+    d = _desc(batch=1, seq_len=300, num_seqs=5)                 # the single-pass kernel's shape
+    assert where(d) == 0 and off.value == 5 * 16
+    assert off.value + 4 <= gdn.workspace_bytes(d)
+    d2 = _desc(batch=1, seq_len=300, num_seqs=5, qkv_dtype=0)   # two stages
+    assert where(d2) == 0 and off.value == gdn.workspace_layout(d2).seqs + 5 * 16
+    assert off.value + 4 <= gdn.workspace_bytes(d2)
+    a8 = gdn.Activation(8, None, None)                          # L2 flag: two stages
+    assert where(d, a8) == 0 and off.value == gdn.workspace_layout(d).seqs + 5 * 16
+    assert where(d, backward=1) == 0 and off.value % 16 == 0
+    assert off.value + 4 <= gdn.bwd_workspace_bytes(d)
+    assert where(_desc()) == 2                                  # not packed
+    assert lib.gdn_seqlens_status_offset(ctypes.byref(d), None, 0, None) == 1
+    assert lib.gdn_status_str(8).decode() == "GDN_ERR_BAD_SEQLENS"
