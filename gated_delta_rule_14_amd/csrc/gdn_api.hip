@@ -174,10 +174,8 @@ gdn_status check_bwd_desc(const gdn_fwd_desc* d, bool packed) {
 
 // gdn_chunk_fwd runs the fused kernel for these shapes; its workspace holds
 // only the per-sequence records of packed input
-// (q/k L2 normalisation runs on the two-stage route, whose intra-chunk stage
-// normalises the rows as it loads them)
 bool fused_path(const gdn_fwd_desc* d, int act_flags = 0) {
-    if (act_flags & GDN_ACT_QK_L2NORM) return false;
+    (void)act_flags;   // every activation runs on either route
     gdn::FusedLaunch f{};
     f.bf16 = d->qkv_dtype == GDN_DTYPE_BF16;
     f.per_key = d->gate == GDN_GATE_PER_KEY;

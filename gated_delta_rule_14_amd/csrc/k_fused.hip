@@ -102,11 +102,13 @@ constexpr int o_TT = o_AQ + 2 * SZ_AQ;
 constexpr int o_A = o_TT + SZ_TT;            // 2 slots
 constexpr int o_D = o_A + 2 * SZ_A;
 constexpr int o_DT = o_D + 4 * SZ_DB;
-constexpr int o_F = o_DT + 4 * SZ_DT;        // signal words
+constexpr int SZ_NRM = 128 * 4;              // per product wave: |k|^2, |q|^2 of a chunk's tokens
+constexpr int o_NRM = o_DT + 4 * SZ_DT;      // 4 (the key wave and the three query waves)
+constexpr int o_F = o_NRM + 4 * SZ_NRM;      // signal words
 constexpr int BYTES = o_F + 64;
 static_assert(BYTES <= 160 * 1024, "LDS budget of one workgroup");
 static_assert(o_V % 16 == 0 && o_RAW % 16 == 0 && o_G % 16 == 0 && o_AQ % 16 == 0 && o_TT % 16 == 0 &&
-                  o_A % 16 == 0 && o_D % 16 == 0 && o_DT % 16 == 0 && o_F % 16 == 0,
+                  o_A % 16 == 0 && o_D % 16 == 0 && o_DT % 16 == 0 && o_NRM % 16 == 0 && o_F % 16 == 0,
               "alignment");
 
 // Gate arrays, per token r of a chunk: GA_G the cumulative log2 gate G_r;
@@ -244,6 +246,11 @@ struct Ctx {
         return reinterpret_cast<float*>(sm + o_D + SZ_DB * b);
     }
     __device__ __forceinline__ char* sDT(int b) const { return sm + o_DT + SZ_DT * b; }
+    // squared norms of the current chunk's tokens, per product wave (slot 0:
+    // the key wave, 1 + s: query set s)
+    __device__ __forceinline__ float* nrm(int slot) const {
+        return reinterpret_cast<float*>(sm + o_NRM + SZ_NRM * slot);
+    }
     __device__ __forceinline__ lds_int* tflag() const { return (lds_int*)(sm + o_F); }
     __device__ __forceinline__ lds_int* dflag() const { return (lds_int*)(sm + o_F) + 1; }
     __device__ __forceinline__ lds_int* lflag() const { return (lds_int*)(sm + o_F) + 5; }
@@ -272,6 +279,20 @@ struct Ctx {
 __device__ __forceinline__ constexpr int frag_ix(int t, int p) { return t < 2 ? t : 2 * t - 2 + p; }
 // index of the off-diagonal A block (I, J), J < I
 __device__ __forceinline__ constexpr int ab_ix(int I, int J) { return I * (I - 1) / 2 + J; }
+
+// q/k L2 normalisation folded into the products (ACT_QK_L2NORM): every
+// product is linear in each row, so 1/|x_t| = rsq(x_t.x_t + 1e-6) scales the
+// results.  x_t.x_t is the diagonal of a 16x16 Gram tile gt = X_I X_I^T (lane
+// 16g+n holds gt[n][4g+e]: row n's diagonal entry sits in lane 16(n/4)+n,
+// element n%4), copied to dst[n] by those 16 lanes.
+__device__ __forceinline__ void diag_to(float* dst, const f32x4& gt, int lane) {
+    const int n = lane & 15, k = n & 3;
+    if ((lane >> 4) == (n >> 2)) dst[n] = k == 0 ? gt[0] : k == 1 ? gt[1] : k == 2 ? gt[2] : gt[3];
+}
+__device__ __forceinline__ float l2_rsq(float xx) { return __builtin_amdgcn_rsqf(xx + L2_EPS); }
+__device__ __forceinline__ float4 l2_rsq4(float4 v) {
+    return make_float4(l2_rsq(v.x), l2_rsq(v.y), l2_rsq(v.z), l2_rsq(v.w));
+}
 
 // ---------------------------------------------------------------- wave 6: loads and gates
 __device__ __forceinline__ void role_load(const Ctx& x) {
@@ -392,6 +413,28 @@ __device__ __forceinline__ void role_keys(const Ctx& x) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) sd[I] = mma32(kf[I][kk], kf[I][kk], sd[I]);
             }
+            // q/k L2 normalisation: 1/|k| of the rows (16I+m) and columns
+            // (16I+4g+e) of the diagonal blocks, from their own diagonals
+            const bool l2 = x.act.flags & ACT_QK_L2NORM;
+            float rkr[4] = {1.f, 1.f, 1.f, 1.f};
+            float4 rkc[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) rkc[I] = make_float4(1.f, 1.f, 1.f, 1.f);
+            float* nk = x.nrm(0);
+            if (l2) {
+#pragma unroll
+                for (int I = 0; I < 4; ++I) diag_to(nk + 16 * I, sd[I], lane);
+                own_lds_sync();
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    rkr[I] = l2_rsq(nk[16 * I + m]);
+                    rkc[I] = l2_rsq4(ldf4(nk + 16 * I + 4 * g));
+                }
+#pragma unroll
+                for (int I = 0; I < 4; ++I)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sd[I][e] *= rkr[I] * (&rkc[I].x)[e];
+            }
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 float4 ad;
@@ -414,11 +457,20 @@ __device__ __forceinline__ void role_keys(const Ctx& x) {
                     for (int kk = 0; kk < 4; ++kk) s = mma32(kf[J][kk], kf[I][kk], s);
                     const float4 cj = ldf4(colI + 16 * J + 4 * g);
                     f32x4 av;
+                    if (l2) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) s[e] *= rkr[I] * (&rkc[J].x)[e];
+                    }
 #pragma unroll
                     for (int e = 0; e < 4; ++e) av[e] = bri * (&cj.x)[e] * s[e];
                     *reinterpret_cast<u32x2*>(x.sA(c) + ab_ix(I, J) * SZ_AB + m * (LDAB * 2) + 8 * g) =
                         pk4(av);
                 }
+            }
+            if (l2) {   // the state pass's K h and K^T V_new rows: 1/|k| into beta gamma and the tail
+                const float rk = l2_rsq(nk[lane]);
+                x.gate(c, GA_BG)[lane] *= rk;
+                x.gate(c, GA_TAIL)[lane] *= rk;
             }
         }
         wg_barrier();
@@ -455,12 +507,49 @@ __device__ __forceinline__ void role_queries(const Ctx& x) {
                     if (needq[J]) qf[J][kk] = ld16(qb + kq_off(16 * J + m, 4 * kk + g));
                 }
             __builtin_amdgcn_sched_barrier(0);
+            // q/k L2 normalisation: 1/|q| of the rows of the blocks' I and
+            // 1/|k| of the columns of their J, from Gram diagonals
+            const bool l2 = x.act.flags & ACT_QK_L2NORM;
+            float rqr[4] = {1.f, 1.f, 1.f, 1.f};
+            float4 rkc[4];
+#pragma unroll
+            for (int J = 0; J < 4; ++J) rkc[J] = make_float4(1.f, 1.f, 1.f, 1.f);
+            if (l2) {
+                float* nq = x.nrm(1 + SET);   // [0, 64): |k|^2, [64, 128): |q|^2
+#pragma unroll
+                for (int J = 0; J < 4; ++J) {
+                    if (needk[J]) {
+                        f32x4 gk = zero4();
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) gk = mma32(kf[J][kk], kf[J][kk], gk);
+                        diag_to(nq + 16 * J, gk, lane);
+                    }
+                    if (needq[J]) {
+                        f32x4 gq = zero4();
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) gq = mma32(qf[J][kk], qf[J][kk], gq);
+                        diag_to(nq + 64 + 16 * J, gq, lane);
+                    }
+                }
+                own_lds_sync();
+#pragma unroll
+                for (int J = 0; J < 4; ++J) {
+                    if (needk[J]) rkc[J] = l2_rsq4(ldf4(nq + 16 * J + 4 * g));
+                    if (needq[J]) rqr[J] = l2_rsq(nq[64 + 16 * J + m]);
+                }
+                // the set with every query block: 1/|q| into the output's scale gamma
+                if (SET == 0) x.gate(c, GA_OUT)[lane] *= l2_rsq(nq[64 + lane]);
+            }
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 const int I = BI[SET][b], J = BJ[SET][b];
                 f32x4 s = zero4();
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) s = mma32(kf[J][kk], qf[I][kk], s);
+                if (l2) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s[e] *= rqr[I] * (&rkc[J].x)[e];
+                }
                 f32x4 q;
                 if (J == I) {
                     const float Gi = x.gate(c, GA_G)[16 * I + m];

@@ -137,9 +137,8 @@ typedef struct gdn_step_desc {
  *                         eigenvalues in [-1, 1]; the pages fix no epsilon)
  * A_log [H] and dt_bias ([H] or [H, K]) are float device arrays, required
  * with GDN_ACT_GATE and otherwise ignored.  Unknown bits, or NEG_EIG without
- * BETA_SIGMOID, give GDN_ERR_UNSUPPORTED.  With GDN_ACT_QK_L2NORM the
- * prefill always runs as two stages: size its workspace with
- * gdn_chunk_fwd_workspace_act.
+ * BETA_SIGMOID, give GDN_ERR_UNSUPPORTED.  Every flag runs on both prefill
+ * routes; the workspace does not depend on the activation.
  */
 enum { GDN_ACT_GATE = 1, GDN_ACT_BETA_SIGMOID = 2, GDN_ACT_BETA_NEG_EIG = 4, GDN_ACT_QK_L2NORM = 8 };
 typedef struct gdn_activation {
@@ -188,7 +187,7 @@ const char *gdn_last_error(void);
 gdn_status gdn_chunk_fwd_workspace(const gdn_fwd_desc *d, size_t *bytes);
 
 /* The same for gdn_chunk_fwd_act with the activation *act (NULL: exactly
- * gdn_chunk_fwd_workspace); GDN_ACT_QK_L2NORM needs the two-stage layout. */
+ * gdn_chunk_fwd_workspace; no flag changes the size at present). */
 gdn_status gdn_chunk_fwd_workspace_act(const gdn_fwd_desc *d, const gdn_activation *act,
                                        size_t *bytes);
 

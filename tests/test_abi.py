@@ -214,23 +214,25 @@ def test_chunk_bwd_act_rejects_before_launch(lib):
 
 
 def test_l2norm_flag_and_workspace(lib):
-    """GDN_ACT_QK_L2NORM is a known bit; with it the fused kernel's shape
-    runs as two stages, so gdn_chunk_fwd_workspace_act asks for the whole
-    two-stage layout; an unknown bit is refused before anything else."""
+    """GDN_ACT_QK_L2NORM is a known bit and runs on either route, so the
+    workspace does not depend on it; an unknown bit is refused before
+    anything else."""
     d = _desc()
     n = ctypes.c_size_t()
 
-    def ws(flags):
+    def ws(flags, desc=d):
         a = gdn.Activation(flags, None, None)
-        return lib.gdn_chunk_fwd_workspace_act(ctypes.byref(d), ctypes.byref(a), ctypes.byref(n))
+        return lib.gdn_chunk_fwd_workspace_act(ctypes.byref(desc), ctypes.byref(a), ctypes.byref(n))
     assert ws(0) == 0 and n.value == gdn.workspace_bytes(d) == 256
-    assert ws(8) == 0 and n.value == gdn.workspace_layout(d).total
+    assert ws(8) == 0 and n.value == 256
+    f32 = _desc(qkv_dtype=0)
+    assert ws(8, f32) == 0 and n.value == gdn.workspace_layout(f32).total
     assert ws(16) == 4
     assert lib.gdn_chunk_fwd_workspace_act(ctypes.byref(d), None, ctypes.byref(n)) == 0
     assert n.value == 256
-    # the two-stage route with the flag still needs the whole layout
+    # the two-stage route with the flag still checks its workspace
     a = gdn.Activation(8, None, None)
-    assert lib.gdn_chunk_fwd_act(ctypes.byref(d), ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE,
+    assert lib.gdn_chunk_fwd_act(ctypes.byref(f32), ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE,
                                  None, None, FAKE, None, FAKE, 256, None) == 5
 
 
@@ -265,8 +267,8 @@ def test_seqlens_status_offset(lib):
     d2 = _desc(batch=1, seq_len=300, num_seqs=5, qkv_dtype=0)   # two stages
     assert where(d2) == 0 and off.value == gdn.workspace_layout(d2).seqs + 5 * 16
     assert off.value + 4 <= gdn.workspace_bytes(d2)
-    a8 = gdn.Activation(8, None, None)                          # L2 flag: two stages
-    assert where(d, a8) == 0 and off.value == gdn.workspace_layout(d).seqs + 5 * 16
+    a8 = gdn.Activation(8, None, None)                          # L2 flag: the same route
+    assert where(d, a8) == 0 and off.value == 5 * 16
     assert where(d, backward=1) == 0 and off.value % 16 == 0
     assert off.value + 4 <= gdn.bwd_workspace_bytes(d)
     assert where(_desc()) == 2                                  # not packed

@@ -35,7 +35,7 @@ def _normalised(d):
 
 
 @pytest.mark.parametrize("cid,dt,gate,K,V,logits", [
-    (1, "bf16", "scalar", 128, 128, False),    # the fused kernel's shape: runs as two stages
+    (1, "bf16", "scalar", 128, 128, False),    # the fused kernel's shape
     (1, "bf16", "scalar", 128, 128, True),     # with the gate and beta activations too
     (0, "f32", "per_key", 64, 64, False),
     (1, "bf16", "per_key", 128, 64, True),
