@@ -102,13 +102,16 @@ constexpr int o_TT = o_AQ + 2 * SZ_AQ;
 constexpr int o_A = o_TT + SZ_TT;            // 2 slots
 constexpr int o_D = o_A + 2 * SZ_A;
 constexpr int o_DT = o_D + 4 * SZ_DB;
-constexpr int SZ_NRM = 128 * 4;              // per product wave: |k|^2, |q|^2 of a chunk's tokens
-constexpr int o_NRM = o_DT + 4 * SZ_DT;      // 4 (the key wave and the three query waves)
-constexpr int o_F = o_NRM + 4 * SZ_NRM;      // signal words
+constexpr int o_F = o_DT + 4 * SZ_DT;        // signal words
 constexpr int BYTES = o_F + 64;
-static_assert(BYTES <= 160 * 1024, "LDS budget of one workgroup");
+// the q/k L2-normalising instantiation only: per product wave (the key wave
+// and the three query waves), |k|^2 and |q|^2 of the chunk's tokens
+constexpr int SZ_NRM = 128 * 4;
+constexpr int o_NRM = BYTES;
+constexpr int BYTES_L2 = o_NRM + 4 * SZ_NRM;
+static_assert(BYTES_L2 <= 160 * 1024, "LDS budget of one workgroup");
 static_assert(o_V % 16 == 0 && o_RAW % 16 == 0 && o_G % 16 == 0 && o_AQ % 16 == 0 && o_TT % 16 == 0 &&
-                  o_A % 16 == 0 && o_D % 16 == 0 && o_DT % 16 == 0 && o_NRM % 16 == 0 && o_F % 16 == 0,
+                  o_A % 16 == 0 && o_D % 16 == 0 && o_DT % 16 == 0 && o_F % 16 == 0 && o_NRM % 16 == 0,
               "alignment");
 
 // Gate arrays, per token r of a chunk: GA_G the cumulative log2 gate G_r;
@@ -385,6 +388,7 @@ __device__ __forceinline__ void role_load(const Ctx& x) {
 
 // wave 3: A = beta_i 2^{G_i - G_j} k_i.k_j, the four diagonal blocks first
 // (signalled to the inverse), then the six below them
+template <bool L2>
 __device__ __forceinline__ void role_keys(const Ctx& x) {
     const int lane = x.lane, m = lane & 15, g = lane >> 4;
     for (int j = -2; j < x.nch; ++j) {
@@ -415,13 +419,13 @@ __device__ __forceinline__ void role_keys(const Ctx& x) {
             }
             // q/k L2 normalisation: 1/|k| of the rows (16I+m) and columns
             // (16I+4g+e) of the diagonal blocks, from their own diagonals
-            const bool l2 = x.act.flags & ACT_QK_L2NORM;
+            constexpr bool l2 = L2;
             float rkr[4] = {1.f, 1.f, 1.f, 1.f};
             float4 rkc[4];
 #pragma unroll
             for (int I = 0; I < 4; ++I) rkc[I] = make_float4(1.f, 1.f, 1.f, 1.f);
             float* nk = x.nrm(0);
-            if (l2) {
+            if constexpr (l2) {
 #pragma unroll
                 for (int I = 0; I < 4; ++I) diag_to(nk + 16 * I, sd[I], lane);
                 own_lds_sync();
@@ -457,7 +461,7 @@ __device__ __forceinline__ void role_keys(const Ctx& x) {
                     for (int kk = 0; kk < 4; ++kk) s = mma32(kf[J][kk], kf[I][kk], s);
                     const float4 cj = ldf4(colI + 16 * J + 4 * g);
                     f32x4 av;
-                    if (l2) {
+                    if constexpr (l2) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) s[e] *= rkr[I] * (&rkc[J].x)[e];
                     }
@@ -467,7 +471,7 @@ __device__ __forceinline__ void role_keys(const Ctx& x) {
                         pk4(av);
                 }
             }
-            if (l2) {   // the state pass's K h and K^T V_new rows: 1/|k| into beta gamma and the tail
+            if constexpr (l2) {   // the state pass's K h and K^T V_new rows: 1/|k| into beta gamma and the tail
                 const float rk = l2_rsq(nk[lane]);
                 x.gate(c, GA_BG)[lane] *= rk;
                 x.gate(c, GA_TAIL)[lane] *= rk;
@@ -480,7 +484,7 @@ __device__ __forceinline__ void role_keys(const Ctx& x) {
 // waves 7, 4, 5: Aqk = scale 2^{G_i - G_j} q_i.k_j (j <= i), as the state
 // pass's 16x16x32 operand fragments.  Set 0 takes the diagonal blocks and
 // (1,0), set 1 (2,0) and (2,1), set 2 (3,0), (3,1) and (3,2).
-template <int SET>
+template <int SET, bool L2>
 __device__ __forceinline__ void role_queries(const Ctx& x) {
     constexpr int NB = SET == 0 ? 5 : SET == 1 ? 2 : 3;
     constexpr int BI[3][5] = {{0, 1, 2, 3, 1}, {2, 2, 0, 0, 0}, {3, 3, 3, 0, 0}};
@@ -509,12 +513,12 @@ __device__ __forceinline__ void role_queries(const Ctx& x) {
             __builtin_amdgcn_sched_barrier(0);
             // q/k L2 normalisation: 1/|q| of the rows of the blocks' I and
             // 1/|k| of the columns of their J, from Gram diagonals
-            const bool l2 = x.act.flags & ACT_QK_L2NORM;
+            constexpr bool l2 = L2;
             float rqr[4] = {1.f, 1.f, 1.f, 1.f};
             float4 rkc[4];
 #pragma unroll
             for (int J = 0; J < 4; ++J) rkc[J] = make_float4(1.f, 1.f, 1.f, 1.f);
-            if (l2) {
+            if constexpr (l2) {
                 float* nq = x.nrm(1 + SET);   // [0, 64): |k|^2, [64, 128): |q|^2
 #pragma unroll
                 for (int J = 0; J < 4; ++J) {
@@ -546,7 +550,7 @@ __device__ __forceinline__ void role_queries(const Ctx& x) {
                 f32x4 s = zero4();
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) s = mma32(kf[J][kk], qf[I][kk], s);
-                if (l2) {
+                if constexpr (l2) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) s[e] *= rqr[I] * (&rkc[J].x)[e];
                 }
@@ -873,8 +877,9 @@ __device__ __forceinline__ void role_state(const Ctx& x, const FusedLaunch& a, i
 }
 
 // ---------------------------------------------------------------- the kernel
+template <bool L2>
 __global__ __launch_bounds__(NT) void fused_kernel(FusedLaunch a) {
-    __shared__ __attribute__((aligned(16))) char smem[BYTES];
+    __shared__ __attribute__((aligned(16))) char smem[L2 ? BYTES_L2 : BYTES];
     const int64_t bid = blockIdx.x;
     // the four value slices of a (sequence, head) run on one XCD (workgroups
     // are dealt to the eight XCDs round-robin), where they share K, Q in L2
@@ -929,10 +934,10 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedLaunch a) {
         case 1: role_state(x, a, n); break;
         case 2: role_inverse(x); break;
         case 6: role_load(x); break;
-        case 3: role_keys(x); break;
-        case 7: role_queries<0>(x); break;
-        case 4: role_queries<1>(x); break;
-        default: role_queries<2>(x); break;
+        case 3: role_keys<L2>(x); break;
+        case 7: role_queries<0, L2>(x); break;
+        case 4: role_queries<1, L2>(x); break;
+        default: role_queries<2, L2>(x); break;
     }
 }
 
@@ -946,7 +951,10 @@ hipError_t launch_fused(const FusedLaunch& a) {
     if (!fused_supported(a)) return hipErrorInvalidValue;
     const int64_t chains = a.N * a.H;
     const int64_t nblk = ((chains + 7) / 8) * 8 * fz::NVT;
-    hipLaunchKernelGGL(fz::fused_kernel, dim3((unsigned)nblk), dim3(fz::NT), 0, a.stream, a);
+    if (a.act.flags & ACT_QK_L2NORM)
+        hipLaunchKernelGGL(fz::fused_kernel<true>, dim3((unsigned)nblk), dim3(fz::NT), 0, a.stream, a);
+    else
+        hipLaunchKernelGGL(fz::fused_kernel<false>, dim3((unsigned)nblk), dim3(fz::NT), 0, a.stream, a);
     return hipGetLastError();
 }
 
