@@ -347,8 +347,9 @@ def chunk_intra(q, k, v, beta, g, scale=None, cu_seqlens=None, chunk=64, gate="s
     """gdn_chunk_intra: the intra-chunk stage alone.  Returns a dict: gcum and
     ainv (views into the workspace), w, u, qs, ks, aqk (row-major copies of
     the workspace arrays, which the library keeps in MFMA fragment /
-    accumulator order), max_chunks, workspace and desc.  views=False skips
-    the arrays (no work beyond the library call)."""
+    accumulator order), max_chunks, workspace and desc.  With the per-key
+    gate only gcum[:, :, C - 1] is written.  views=False skips the arrays
+    (no work beyond the library call)."""
     lib = load()
     _inputs(q, k, v, beta, g, cu_seqlens, gate)
     N = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1

@@ -300,8 +300,15 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                 col_group(sQ, true, gqs, task - NQG - NKG);
             }
         }
+        // the state pass needs only the chunk's last row of the per-key
+        // cumulative gate (the decay of the carried state); the scalar gate's
+        // whole column also serves the backward
         float* gg = a.ws.gcum + blk * C * (PK ? K : 1);
-        for (int i = tid; i < C * (PK ? K : 1); i += NT) gg[i] = PK ? sG[(i / K) * LDG + i % K] : sG[i];
+        if (PK) {
+            for (int i = tid; i < K; i += NT) gg[(C - 1) * K + i] = sG[(C - 1) * LDG + i];
+        } else {
+            for (int i = tid; i < C; i += NT) gg[i] = sG[i];
+        }
     }
 
     // ---- a2: beta-scaled decay-masked strictly-lower K K^T -> sA (fp32), and

@@ -253,7 +253,9 @@ gdn_status gdn_chunk_fwd_act(const gdn_fwd_desc *d, const gdn_activation *act,
  * sequence b is slot b * ceil(T / C) + j without cu_seqlens, and slot
  * (first chunk of the sequence) + j with it.  With G the inclusive cumulative
  * log2 gate inside the chunk and gamma = 2^G:
- *   gcum  float [H][mc][C]  (scalar gate) or [H][mc][C][K] (per-key gate): G
+ *   gcum  float [H][mc][C]  (scalar gate) or [H][mc][C][K] (per-key gate): G;
+ *         with the per-key gate only row C-1 (G at the chunk's last token,
+ *         the decay of the carried state) is written
  *   w     [H][mc] x (C x K)  W = (I+A)^{-1} diag(beta) diag(gamma) K      F
  *   u     [H][mc] x (C x V)  U = (I+A)^{-1} diag(beta) V                  A
  *   qs    [H][mc] x (C x K)  scale * diag(gamma) Q                        F
