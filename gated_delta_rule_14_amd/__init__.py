@@ -8,8 +8,10 @@ without a GPU, every compute call needs the built library and a device.
 from ._binding import (ABI_VERSION, EXPORTS, LIB_PATH, Activation, FwdDesc, GdnError,  # noqa: F401
                        StepDesc, WorkspaceLayout, activation, bwd_workspace_bytes, chunk_bwd,
                        chunk_fwd, chunk_intra, chunk_scan, fwd_desc, load, recurrent_step,
-                       seqlens_status, workspace_bytes, workspace_layout)
+                       seqlens_status, sync_status, sync_status_offset, workspace_bytes,
+                       workspace_layout)
 
 __all__ = ["load", "activation", "chunk_fwd", "chunk_bwd", "chunk_intra", "chunk_scan",
            "recurrent_step", "workspace_bytes", "bwd_workspace_bytes", "workspace_layout",
-           "fwd_desc", "seqlens_status", "GdnError", "LIB_PATH", "EXPORTS"]
+           "fwd_desc", "seqlens_status", "sync_status", "sync_status_offset", "GdnError",
+           "LIB_PATH", "EXPORTS"]

@@ -13,7 +13,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_SCALAR, GATE_PER_KEY = 0, 1
@@ -26,7 +26,7 @@ EXPORTS = sorted(["gdn_abi_version", "gdn_status_str", "gdn_last_error",
                   "gdn_chunk_intra", "gdn_chunk_scan", "gdn_recurrent_step",
                   "gdn_chunk_fwd_act", "gdn_recurrent_step_act",
                   "gdn_chunk_bwd_workspace", "gdn_chunk_bwd", "gdn_chunk_bwd_act",
-                  "gdn_seqlens_status_offset"])
+                  "gdn_seqlens_status_offset", "gdn_sync_status_offset"])
 INTRA_STORE_AINV = 1
 ACT_GATE, ACT_BETA_SIGMOID, ACT_BETA_NEG_EIG, ACT_QK_L2NORM = 1, 2, 4, 8
 
@@ -113,6 +113,9 @@ def load(path: str = LIB_PATH):
     lib.gdn_seqlens_status_offset.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(Activation),
                                               ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
     lib.gdn_seqlens_status_offset.restype = S
+    lib.gdn_sync_status_offset.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(Activation),
+                                           ctypes.POINTER(ctypes.c_size_t)]
+    lib.gdn_sync_status_offset.restype = S
     v = lib.gdn_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError("libgdn.so ABI %d, binding expects %d" % (v, ABI_VERSION))
@@ -129,19 +132,66 @@ def _debug():
     return os.environ.get("GDN_DEBUG", "") not in ("", "0")
 
 
-def seqlens_status(desc, workspace, act=None, backward=False):
+def _word(workspace, off, stream):
+    """The int32 at byte offset `off` of the workspace, once `stream` (None:
+    the current stream) has reached everything enqueued so far."""
+    (stream or torch.cuda.current_stream()).synchronize()
+    return int(workspace[off:off + 4].view(torch.int32).cpu().item())
+
+
+def seqlens_status(desc, workspace, act=None, backward=False, stream=None):
     """The check of cu_seqlens that a packed call left in its workspace
     (gdn_seqlens_status_offset): raises GdnError(GDN_ERR_BAD_SEQLENS) if the
-    offsets did not start at 0, decreased or did not end at T.  Waits for the
-    current stream.  chunk_fwd and chunk_bwd call it when GDN_DEBUG is set."""
+    offsets did not start at 0, decreased or did not end at T.  Waits for
+    `stream` (None: the current stream).  chunk_fwd and chunk_bwd call it
+    when GDN_DEBUG is set."""
     lib = load()
     off = ctypes.c_size_t()
     _check(lib.gdn_seqlens_status_offset(ctypes.byref(desc),
                                          ctypes.byref(act) if act is not None else None,
                                          1 if backward else 0, ctypes.byref(off)))
-    word = int(workspace[off.value:off.value + 4].view(torch.int32).item())
-    if word != 0:
+    if _word(workspace, off.value, stream) != 0:
         raise GdnError(8, "cu_seqlens must start at 0, never decrease and end at T")
+
+
+def sync_status_offset(desc, act=None):
+    """gdn_sync_status_offset: byte offset of the single-pass kernel's
+    synchronisation status word in the workspace, or None for shapes that run
+    the two-stage route (which has no waits between waves)."""
+    lib = load()
+    off = ctypes.c_size_t()
+    st = lib.gdn_sync_status_offset(ctypes.byref(desc), ctypes.byref(act) if act is not None else None,
+                                    ctypes.byref(off))
+    if st == 4:
+        return None
+    _check(st)
+    return off.value
+
+
+def sync_status(desc, workspace, act=None, stream=None):
+    """The single-pass kernel's synchronisation status word (0: every wait
+    between its waves was met; 1: a wait gave up and the results are wrong).
+    The library never clears the word: the binding allocates its workspaces
+    zeroed.  Waits for `stream`.  0 for shapes without the single-pass
+    kernel.  chunk_fwd raises on a nonzero word when GDN_DEBUG is set."""
+    off = sync_status_offset(desc, act)
+    return 0 if off is None else _word(workspace, off, stream)
+
+
+class _on:
+    """Context: allocations go to `stream` (None: the current stream)."""
+
+    def __init__(self, stream):
+        self.ctx = torch.cuda.stream(stream) if stream is not None else None
+
+    def __enter__(self):
+        if self.ctx is not None:
+            self.ctx.__enter__()
+
+    def __exit__(self, *exc):
+        if self.ctx is not None:
+            return self.ctx.__exit__(*exc)
+        return False
 
 
 def _ptr(t):
@@ -256,13 +306,17 @@ def chunk_fwd(q, k, v, beta, g, scale=None, h0=None, cu_seqlens=None, chunk=64,
         _need(h0, "h0", torch.float32)
         if tuple(h0.shape) != (N, H, K, V):
             raise ValueError("h0 must have shape %s" % ((N, H, K, V),))
-    if o is None:
-        o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
-    if output_final_state and ht is None:
-        ht = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device)
     nbytes = workspace_bytes(desc, act)
-    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    # what is allocated here is allocated on the stream the kernels run on,
+    # so the caching allocator never hands it out while they still use it
+    with _on(stream):
+        if o is None:
+            o = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+        if output_final_state and ht is None:
+            ht = torch.empty((N, H, K, V), dtype=torch.float32, device=q.device)
+        if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+            # zeroed: the single-pass kernel's synchronisation word starts clear
+            workspace = torch.zeros(nbytes, dtype=torch.uint8, device=q.device)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0), _ptr(cu_seqlens), _ptr(o),
             _ptr(ht) if output_final_state else None, _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(stream))
@@ -271,8 +325,11 @@ def chunk_fwd(q, k, v, beta, g, scale=None, h0=None, cu_seqlens=None, chunk=64,
     else:
         _act_shapes(act, H, K, gate)
         _check(lib.gdn_chunk_fwd_act(ctypes.byref(desc), ctypes.byref(act), *args))
-    if cu_seqlens is not None and _debug():
-        seqlens_status(desc, workspace, act)
+    if _debug():
+        if cu_seqlens is not None:
+            seqlens_status(desc, workspace, act, stream=stream)
+        if sync_status(desc, workspace, act, stream=stream) != 0:
+            raise GdnError(7, "a wait between the single-pass kernel's waves gave up: wrong results")
     return o, (ht if output_final_state else None)
 
 
@@ -307,26 +364,27 @@ def chunk_bwd(q, k, v, beta, g, do, scale=None, h0=None, dht=None, cu_seqlens=No
                 raise ValueError("%s must have shape %s" % (name, (N, H, K, V)))
     out = dict(out or {})
     dev = q.device
-    for name, shape, dt in (("dq", q.shape, q.dtype), ("dk", k.shape, q.dtype),
-                            ("dv", v.shape, q.dtype), ("dbeta", beta.shape, torch.float32),
-                            ("dg", g.shape, torch.float32)):
-        if out.get(name) is None:
-            out[name] = torch.empty(shape, dtype=dt, device=dev)
-        _need(out[name], name, dt)
-    if want_dh0 and out.get("dh0") is None:
-        out["dh0"] = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
-    if not want_dh0:
-        out["dh0"] = None
     act_gate = act is not None and bool(act.flags & ACT_GATE)
-    if act_gate:
-        _act_shapes(act, H, K, "scalar")
-        for name in ("dA_log", "ddt_bias"):
-            if out.get(name) is None:
-                out[name] = torch.empty((H,), dtype=torch.float32, device=dev)
-            _need(out[name], name, torch.float32)
     nbytes = bwd_workspace_bytes(desc)
-    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    with _on(stream):   # allocated on the kernels' stream (see chunk_fwd)
+        for name, shape, dt in (("dq", q.shape, q.dtype), ("dk", k.shape, q.dtype),
+                                ("dv", v.shape, q.dtype), ("dbeta", beta.shape, torch.float32),
+                                ("dg", g.shape, torch.float32)):
+            if out.get(name) is None:
+                out[name] = torch.empty(shape, dtype=dt, device=dev)
+            _need(out[name], name, dt)
+        if want_dh0 and out.get("dh0") is None:
+            out["dh0"] = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+        if not want_dh0:
+            out["dh0"] = None
+        if act_gate:
+            _act_shapes(act, H, K, "scalar")
+            for name in ("dA_log", "ddt_bias"):
+                if out.get(name) is None:
+                    out[name] = torch.empty((H,), dtype=torch.float32, device=dev)
+                _need(out[name], name, torch.float32)
+        if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0), _ptr(cu_seqlens), _ptr(do),
             _ptr(dht), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
             _ptr(out["dg"]), _ptr(out["dh0"])]
@@ -338,7 +396,7 @@ def chunk_bwd(q, k, v, beta, g, do, scale=None, h0=None, dht=None, cu_seqlens=No
                                      _ptr(out.get("dA_log")) if act_gate else None,
                                      _ptr(out.get("ddt_bias")) if act_gate else None, *tail))
     if cu_seqlens is not None and _debug():
-        seqlens_status(desc, workspace, act, backward=True)
+        seqlens_status(desc, workspace, act, backward=True, stream=stream)
     return out
 
 
@@ -356,7 +414,8 @@ def chunk_intra(q, k, v, beta, g, scale=None, cu_seqlens=None, chunk=64, gate="s
     desc = fwd_desc(q, v, gate, chunk, scale, 0 if cu_seqlens is None else N)
     L = workspace_layout(desc)
     if workspace is None or workspace.numel() * workspace.element_size() < L.total:
-        workspace = torch.zeros(L.total, dtype=torch.uint8, device=q.device)
+        with _on(stream):   # allocated on the kernels' stream (see chunk_fwd)
+            workspace = torch.zeros(L.total, dtype=torch.uint8, device=q.device)
     ws = workspace
     _check(lib.gdn_chunk_intra(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                                _ptr(g), _ptr(cu_seqlens), _ptr(ws),
@@ -441,7 +500,8 @@ def recurrent_step(q, k, v, beta, g, state, scale=None, gate="scalar", o=None, s
     if tuple(g.shape) != want_g or tuple(beta.shape) != (N, H) or H % Hq != 0:
         raise ValueError("beta/g shape mismatch")
     if o is None:
-        o = torch.empty((N, H, V), dtype=q.dtype, device=q.device)
+        with _on(stream):   # allocated on the kernel's stream (see chunk_fwd)
+            o = torch.empty((N, H, V), dtype=q.dtype, device=q.device)
     desc = StepDesc(N, Hq, K, V, _dtype_code(q),
                     GATE_PER_KEY if gate == "per_key" else GATE_SCALAR,
                     float(K ** -0.5 if scale is None else scale), H if H != Hq else 0)

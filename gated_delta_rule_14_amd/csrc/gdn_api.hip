@@ -63,29 +63,13 @@ gdn_status check_desc(const gdn_fwd_desc* d, bool packed) {
         return fail(GDN_ERR_BAD_SHAPE, "num_v_heads %lld must be 0 or a multiple of num_heads %lld",
                     (long long)d->num_v_heads, (long long)d->num_heads);
     if (d->chunk != 64)
-        return fail(GDN_ERR_UNSUPPORTED,
-                    d->chunk == 16 || d->chunk == 32
-                        ? "chunk %d: the entry points that expose per-chunk intermediates use 64"
-                        : "chunk %d (supported: 16, 32, 64)",
-                    d->chunk);
+        return fail(GDN_ERR_UNSUPPORTED, "chunk %d: only the 64-token tiling is built", d->chunk);
     if (!dim_ok(d->key_dim) || !dim_ok(d->value_dim))
         return fail(GDN_ERR_UNSUPPORTED, "K=%lld V=%lld (supported: 64, 128)",
                     (long long)d->key_dim, (long long)d->value_dim);
     if (d->qkv_dtype == GDN_DTYPE_F32 && d->gate == GDN_GATE_PER_KEY && d->key_dim == 128)
         return fail(GDN_ERR_UNSUPPORTED, "fp32 q/k/v with the per-key gate needs K = 64");
     return GDN_OK;
-}
-
-// The entry points that return only o, ht or gradients accept chunk 16, 32
-// or 64: the chunked form reaches the recurrence's result whatever the chunk
-// size ("TileLang 实战" §2.3), so they compute with the 64-token tiling, and
-// the chunk size changes rounding only.  The layout query and gdn_chunk_intra
-// / gdn_chunk_scan, whose workspace holds per-chunk intermediates, take 64.
-const gdn_fwd_desc* tiled(const gdn_fwd_desc* d, gdn_fwd_desc* tmp) {
-    if (!d || (d->chunk != 16 && d->chunk != 32)) return d;
-    *tmp = *d;
-    tmp->chunk = 64;
-    return tmp;
 }
 
 int64_t max_chunks_of(const gdn_fwd_desc* d, bool packed) {
@@ -185,9 +169,13 @@ bool fused_path(const gdn_fwd_desc* d, int act_flags = 0) {
     return gdn::fused_supported(f);
 }
 
-size_t fused_workspace(const gdn_fwd_desc* d, bool packed) {
+// Single-pass workspace: the per-sequence records of packed input and the
+// check word of cu_seqlens, then a 256-byte block whose first int32 is the
+// synchronisation status word (gdn_sync_status_offset)
+size_t fused_sync_offset(const gdn_fwd_desc* d, bool packed) {
     return align256((size_t)(packed ? d->num_seqs + 1 : 1) * 16);
 }
+size_t fused_workspace(const gdn_fwd_desc* d, bool packed) { return fused_sync_offset(d, packed) + 256; }
 
 gdn_status hip_fail(hipError_t e, const char* what) {
     return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -330,10 +318,8 @@ gdn_status gdn_workspace_layout_of(const gdn_fwd_desc* d, gdn_workspace_layout* 
     return ok();
 }
 
-gdn_status gdn_chunk_fwd_workspace_act(const gdn_fwd_desc* d_in, const gdn_activation* act_in,
+gdn_status gdn_chunk_fwd_workspace_act(const gdn_fwd_desc* d, const gdn_activation* act_in,
                                        size_t* bytes) {
-    gdn_fwd_desc tmp;
-    const gdn_fwd_desc* d = tiled(d_in, &tmp);
     if (!bytes) return fail(GDN_ERR_NULL_ARG, "bytes is NULL");
     gdn::Act act;
     gdn_status s = check_act(act_in, &act);
@@ -345,11 +331,9 @@ gdn_status gdn_chunk_fwd_workspace_act(const gdn_fwd_desc* d_in, const gdn_activ
     return ok();
 }
 
-gdn_status gdn_seqlens_status_offset(const gdn_fwd_desc* d_in, const gdn_activation* act_in,
+gdn_status gdn_seqlens_status_offset(const gdn_fwd_desc* d, const gdn_activation* act_in,
                                      int32_t backward, size_t* offset) {
     if (!offset) return fail(GDN_ERR_NULL_ARG, "offset is NULL");
-    gdn_fwd_desc tmp;
-    const gdn_fwd_desc* d = tiled(d_in, &tmp);
     gdn_status s = backward ? check_bwd_desc(d, true) : check_desc(d, true);
     if (s != GDN_OK) return s;
     gdn::Act act;
@@ -368,6 +352,21 @@ gdn_status gdn_seqlens_status_offset(const gdn_fwd_desc* d_in, const gdn_activat
         layout(d, true, &L);
         *offset = L.seqs + rec;
     }
+    return ok();
+}
+
+gdn_status gdn_sync_status_offset(const gdn_fwd_desc* d, const gdn_activation* act_in,
+                                  size_t* offset) {
+    if (!offset) return fail(GDN_ERR_NULL_ARG, "offset is NULL");
+    const bool packed = d && d->num_seqs > 0;
+    gdn_status s = check_desc(d, packed);
+    if (s != GDN_OK) return s;
+    gdn::Act act;
+    s = check_act(act_in, &act);
+    if (s != GDN_OK) return s;
+    if (!fused_path(d, act.flags))
+        return fail(GDN_ERR_UNSUPPORTED, "this shape runs the two-stage route, which has no waits");
+    *offset = fused_sync_offset(d, packed);
     return ok();
 }
 
@@ -467,6 +466,7 @@ static gdn_status fused_fwd(const gdn_fwd_desc* d, const void* q, const void* k,
     a.ht = ht;
     a.o = o;
     a.seqs = nullptr;
+    a.sync_status = reinterpret_cast<int*>(static_cast<char*>(workspace) + fused_sync_offset(d, packed));
     a.T = d->seq_len;
     a.N = packed ? d->num_seqs : d->batch;
     a.H = vheads(d);
@@ -498,12 +498,10 @@ static gdn_status fused_fwd(const gdn_fwd_desc* d, const void* q, const void* k,
     return ok();
 }
 
-gdn_status gdn_chunk_fwd_act(const gdn_fwd_desc* d_in, const gdn_activation* act_in, const void* q,
+gdn_status gdn_chunk_fwd_act(const gdn_fwd_desc* d, const gdn_activation* act_in, const void* q,
                              const void* k, const void* v, const float* beta, const float* g,
                              const float* h0, const int64_t* cu_seqlens, void* o, float* ht,
                              void* workspace, size_t workspace_bytes, void* stream) {
-    gdn_fwd_desc tmp;
-    const gdn_fwd_desc* d = tiled(d_in, &tmp);
     const bool packed = cu_seqlens != nullptr;
     gdn_status s = check_desc(d, packed);
     if (s != GDN_OK) return s;
@@ -530,10 +528,8 @@ gdn_status gdn_chunk_fwd(const gdn_fwd_desc* d, const void* q, const void* k, co
                              workspace_bytes, stream);
 }
 
-gdn_status gdn_chunk_bwd_workspace(const gdn_fwd_desc* d_in, size_t* bytes) {
+gdn_status gdn_chunk_bwd_workspace(const gdn_fwd_desc* d, size_t* bytes) {
     if (!bytes) return fail(GDN_ERR_NULL_ARG, "bytes is NULL");
-    gdn_fwd_desc tmp;
-    const gdn_fwd_desc* d = tiled(d_in, &tmp);
     const bool packed = d && d->num_seqs > 0;
     gdn_status s = check_bwd_desc(d, packed);
     if (s != GDN_OK) return s;
@@ -543,14 +539,12 @@ gdn_status gdn_chunk_bwd_workspace(const gdn_fwd_desc* d_in, size_t* bytes) {
     return ok();
 }
 
-gdn_status gdn_chunk_bwd_act(const gdn_fwd_desc* d_in, const gdn_activation* act_in, const void* q,
+gdn_status gdn_chunk_bwd_act(const gdn_fwd_desc* d, const gdn_activation* act_in, const void* q,
                              const void* k, const void* v, const float* beta, const float* g,
                              const float* h0, const int64_t* cu_seqlens, const void* dout,
                              const float* dht, void* dq, void* dk, void* dv, float* dbeta,
                              float* dg, float* dh0, float* dA_log, float* ddt_bias,
                              void* workspace, size_t workspace_bytes, void* stream) {
-    gdn_fwd_desc tmp;
-    const gdn_fwd_desc* d = tiled(d_in, &tmp);
     const bool packed = cu_seqlens != nullptr;
     gdn_status s = check_bwd_desc(d, packed);
     if (s != GDN_OK) return s;

@@ -38,7 +38,8 @@ struct StepLaunch {
 // With packed offsets a device-built table gives (first token, count, seq).
 struct ChunkMap {
     const int4* table;      // [max_chunks] (t0, n, seq, 0) or nullptr
-    const int4* seqs;       // [N] (t0, len, first chunk, nchunks) or nullptr
+    const int4* seqs;       // [N] (t0, len, first chunk, order[n]: the sequence of
+                            // rank n by length, longest first) or nullptr
     int64_t T;              // tokens per sequence when table == nullptr
     int64_t nt;             // chunks per sequence when table == nullptr
     int64_t max_chunks;     // rows of every per-chunk workspace array
@@ -166,6 +167,7 @@ struct FusedLaunch {
     float* ht;
     void* o;
     const int4* seqs;       // [N] (t0, len, ...) for packed input, else nullptr
+    int* sync_status;       // set to 1 by a wave whose bounded wait gave up, or nullptr
     int64_t T;              // tokens per sequence when seqs == nullptr
     int64_t N, H;
     int K, V, C;

@@ -186,17 +186,19 @@ __device__ __forceinline__ float lane_of(float v, int l) {
 
 // Signals between waves: a release store after the data it covers, an
 // acquire poll before the data is read.  The poll gives up after a bounded
-// number of tries (a schedule error then shows as wrong results, never as a
-// wave that does not finish).
+// number of tries, so a schedule error can never leave a wave that does not
+// finish; a poll that gives up sets the caller's status word (`sync_status`,
+// never cleared here), so the wrong results it leads to are reported.
 typedef __attribute__((address_space(3))) int lds_int;
 __device__ __forceinline__ void signal(lds_int* f, int v) {
     __hip_atomic_store(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
-__device__ __forceinline__ void wait_for(lds_int* f, int v) {
+__device__ __forceinline__ void wait_for(lds_int* f, int v, int* sync_status) {
     for (int it = 0; it < (1 << 16); ++it) {
-        if (__hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= v) break;
+        if (__hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= v) return;
         __builtin_amdgcn_s_sleep(1);
     }
+    if (sync_status && (threadIdx.x & 63) == 0) atomicOr(sync_status, 1);
 }
 // Workgroup barrier that waits for this wave's LDS traffic only (loads into
 // LDS stay in flight across it; they are covered by signals).
@@ -233,6 +235,7 @@ struct Ctx {
     float scale;
     Act act;
     float a_log, dt_bias;   // this head's gate-activation parameters
+    int* sync_status;       // set when a wait gives up (nullptr: not reported)
 
     // slot accessors take chunk indices >= 0
     __device__ __forceinline__ char* sK(int c) const { return sm + o_K + SZ_KQ * (c % 3); }
@@ -262,7 +265,10 @@ struct Ctx {
     __device__ __forceinline__ int rows(int c) const {
         return (int)min((int64_t)C, len - (int64_t)c * C);
     }
-    __device__ __forceinline__ int clampc(int c) const { return min(max(c, 0), nch - 1); }
+    // chunk index clamped into the sequence; an empty sequence (nch = 0)
+    // maps to chunk 0, whose row count rows(0) = 0 makes every buffer load
+    // of it read zeros without touching memory
+    __device__ __forceinline__ int clampc(int c) const { return max(min(c, nch - 1), 0); }
     // byte offset of row r (clamped to the chunk's last row) from the chunk's
     // first row; rows are H*D elements of `eb` bytes apart
     __device__ __forceinline__ uint32_t roff(int c, int r, int D, int eb) const {
@@ -394,7 +400,7 @@ __device__ __forceinline__ void role_keys(const Ctx& x) {
     for (int j = -2; j < x.nch; ++j) {
         const int c = j + 1;
         if (x.valid(c)) {
-            wait_for(x.lflag(), c + 1);   // K, Q of chunk c have landed
+            wait_for(x.lflag(), c + 1, x.sync_status);   // K, Q of chunk c have landed
             const char* kb = x.sK(c);
             u32x4 kf[4][4];
 #pragma unroll
@@ -493,7 +499,7 @@ __device__ __forceinline__ void role_queries(const Ctx& x) {
     for (int j = -2; j < x.nch; ++j) {
         const int c = j + 1;
         if (x.valid(c)) {
-            wait_for(x.lflag(), c + 1);   // K, Q of chunk c have landed
+            wait_for(x.lflag(), c + 1, x.sync_status);   // K, Q of chunk c have landed
             const char* kb = x.sK(c);
             const char* qb = x.sQ(c);
             u32x4 kf[4][4], qf[4][4];
@@ -689,7 +695,7 @@ __device__ __forceinline__ void role_inverse(const Ctx& x) {
         if (x.valid(j)) compose(x, j, tbb);
         const int c = j + 1;
         if (x.valid(c)) {
-            wait_for(x.dflag(), c + 1);   // the diagonal blocks of A
+            wait_for(x.dflag(), c + 1, x.sync_status);   // the diagonal blocks of A
             diag_inverse(x, tbb);
         }
         wg_barrier();
@@ -781,7 +787,7 @@ __device__ __forceinline__ void role_state(const Ctx& x, const FusedLaunch& a, i
 #pragma unroll
             for (int p = 0; p < 2; ++p) rb[p] = pk8(rt[2 * p], rt[2 * p + 1]);
             // ---- V_new = T R; the later steps' operands are read meanwhile
-            wait_for(x.tflag(), j + 1);
+            wait_for(x.tflag(), j + 1, x.sync_status);
             const char* tt = x.sTT();
             u32x4 tf[4][2];
 #pragma unroll
@@ -906,6 +912,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedLaunch a) {
     x.wave = wave_id();
     x.scale = a.scale;
     x.act = a.act;
+    x.sync_status = a.sync_status;
     x.a_log = (a.act.flags & ACT_GATE) ? a.act.A_log[x.h] : 0.f;
     x.dt_bias = (a.act.flags & ACT_GATE) ? a.act.dt_bias[x.h] : 0.f;
     if (a.seqs) {

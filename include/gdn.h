@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 7
+#define GDN_ABI_VERSION 8
 
 typedef int32_t gdn_status;
 enum {
@@ -58,7 +58,7 @@ enum {
     GDN_ERR_NULL_ARG = 1,        /* a required pointer is NULL */
     GDN_ERR_BAD_SHAPE = 2,       /* negative/zero sizes, B != 1 with cu_seqlens, ... */
     GDN_ERR_BAD_DTYPE = 3,       /* unknown dtype or gate code */
-    GDN_ERR_UNSUPPORTED = 4,     /* chunk not in {16,32,64}; K, V not in {64,128} */
+    GDN_ERR_UNSUPPORTED = 4,     /* chunk != 64; K, V not in {64,128} */
     GDN_ERR_WORKSPACE_TOO_SMALL = 5,
     GDN_ERR_MISALIGNED = 6,      /* a pointer lacks the alignment stated below */
     GDN_ERR_HIP = 7,             /* a kernel launch failed; see gdn_last_error() */
@@ -80,7 +80,7 @@ typedef struct gdn_fwd_desc {
     int64_t key_dim;    /* K, in {64, 128} */
     int64_t value_dim;  /* V, in {64, 128} */
     int64_t num_seqs;   /* N packed sequences when cu_seqlens is given, else 0 */
-    int32_t chunk;      /* C in {16, 32, 64}; see "Chunk size" below */
+    int32_t chunk;      /* C: 64; see "Chunk size" below */
     int32_t qkv_dtype;  /* GDN_DTYPE_* of q, k, v, o */
     int32_t gate;       /* GDN_GATE_* */
     float scale;        /* multiplies q (usually 1/sqrt(K)) */
@@ -88,13 +88,12 @@ typedef struct gdn_fwd_desc {
 } gdn_fwd_desc;
 
 /*
- * Chunk size.  The chunked form reaches the recurrence's result whatever the
- * chunk size ("TileLang 实战" §2.3; the pages allow 16, 32 and 64), so the
- * entry points that return only outputs, states or gradients
- * (gdn_chunk_fwd[_act], gdn_chunk_bwd[_act] and their workspace queries)
- * accept 16, 32 and 64 and compute with their 64-token tiling: the chunk size
- * changes rounding only.  gdn_workspace_layout_of, gdn_chunk_intra and
- * gdn_chunk_scan, whose workspace holds per-chunk intermediates, need 64.
+ * Chunk size.  Only the 64-token tiling is built.  The pages allow 16, 32 and
+ * 64 ("Gated Delta Network（GDN）" §4.1(d)); every entry point returns
+ * GDN_ERR_UNSUPPORTED for any chunk other than 64, before launching anything.
+ * (The chunked form reaches the recurrence's result whatever the chunk size,
+ * "TileLang 实战" §2.3, so a caller asking for 16 or 32 loses nothing but
+ * rounding order by passing 64.)
  */
 
 /* Shape of a single-token (decode) step over N independent sequences. */
@@ -164,6 +163,24 @@ typedef struct gdn_activation {
 gdn_status gdn_seqlens_status_offset(const gdn_fwd_desc *d, const gdn_activation *act,
                                      int32_t backward, size_t *offset);
 
+/*
+ * Where the single-pass kernel of gdn_chunk_fwd[_act] reports a failed
+ * hand-off between its waves (byte offset from the workspace start, written
+ * to *offset).  The waves of one workgroup pass each chunk's products to
+ * each other through flags in local memory; every wait for a flag polls a
+ * bounded number of times (about 2^16 polls, several milliseconds, against a
+ * chunk step of a few microseconds), so a wave never waits forever.  A wait
+ * that gives up sets this int32 to 1 (the call's results are then wrong) and
+ * leaves it at 1: the library never clears it.  A caller that wants to know
+ * clears it before the call (e.g. allocates the workspace zeroed) and reads
+ * it once the stream has reached the call.  d (with *act, NULL allowed) must
+ * describe a shape that runs the single-pass kernel (bf16, scalar gate,
+ * K = V = 128, chunk 64); other shapes run the two-stage route, which has no
+ * such waits, and give GDN_ERR_UNSUPPORTED.
+ */
+gdn_status gdn_sync_status_offset(const gdn_fwd_desc *d, const gdn_activation *act,
+                                  size_t *offset);
+
 /* Integer version of this ABI (GDN_ABI_VERSION), for binding checks. */
 int gdn_abi_version(void);
 
@@ -177,8 +194,10 @@ const char *gdn_last_error(void);
  * Bytes of device workspace gdn_chunk_fwd needs for the shape *d (written to
  * *bytes).  A descriptor with num_seqs > 0 describes packed input.
  *   - bf16 inputs, scalar gate, K = V = 128, chunk 64 (the single-pass
- *     kernel): only the per-sequence table of packed input, 16 bytes per
- *     sequence rounded up to 256 (256 bytes without cu_seqlens).
+ *     kernel): the per-sequence table of packed input, 16 bytes per
+ *     sequence and one more record rounded up to 256 (256 bytes without
+ *     cu_seqlens), then 256 bytes that hold the synchronisation status word
+ *     of gdn_sync_status_offset.
  *   - every other shape (two stages): the per-chunk products of the
  *     intra-chunk stage and the chunk table, gdn_workspace_layout_of().total.
  * gdn_chunk_intra and gdn_chunk_scan always need

@@ -22,3 +22,12 @@ def gpu_lib():
     import gated_delta_rule_14_amd as gdn
     gdn.load()          # raises if the HIP library is missing: no fallback
     return gdn
+
+
+@pytest.fixture(autouse=True)
+def _gdn_debug(request, monkeypatch):
+    """GPU tests run with GDN_DEBUG set: after every prefill call the binding
+    reads the single-pass kernel's synchronisation status word (and, for
+    packed input, the check of cu_seqlens) and raises if it is set."""
+    if request.node.get_closest_marker("gpu"):
+        monkeypatch.setenv("GDN_DEBUG", "1")

@@ -76,8 +76,9 @@ def test_workspace_size_and_layout(lib):
     # (bf16, scalar gate, K = V = 128) only the per-sequence records
     assert gdn.workspace_bytes(_desc(qkv_dtype=0)) == gdn.workspace_layout(_desc(qkv_dtype=0)).total
     assert gdn.workspace_bytes(_desc(gate=1)) == gdn.workspace_layout(_desc(gate=1)).total
-    assert gdn.workspace_bytes(d) == 256
-    assert gdn.workspace_bytes(_desc(batch=1, seq_len=300, num_seqs=40)) == 768
+    # (then 256 bytes for the synchronisation status word)
+    assert gdn.workspace_bytes(d) == 256 + 256
+    assert gdn.workspace_bytes(_desc(batch=1, seq_len=300, num_seqs=40)) == 768 + 256
     # packed: one extra chunk slot per sequence
     P = gdn.workspace_layout(_desc(batch=1, seq_len=300, num_seqs=3))
     assert P.max_chunks == 5 + 3
@@ -101,6 +102,7 @@ def test_chunk_fwd_rejects_before_launch(lib):
     assert _fwd(lib, d, h0=ctypes.c_void_p((1 << 20) + 2)) == 6
     assert _fwd(lib, d, ws=ctypes.c_void_p((1 << 20) + 64)) == 6
     assert _fwd(lib, d, wsb=128) == 5
+    assert _fwd(lib, d, wsb=256) == 5                               # no room for the status word
     assert _fwd(lib, _desc(qkv_dtype=0), wsb=1024) == 5
     assert _fwd(lib, _desc(batch=2, num_seqs=2), cu=FAKE) == 2      # packed needs B == 1
     assert _fwd(lib, _desc(batch=1), cu=FAKE) == 2                  # packed needs num_seqs
@@ -168,7 +170,7 @@ def test_chunk_bwd_rejects_before_launch(lib):
     assert ws(_desc(qkv_dtype=0)) == 4                  # fp32 needs K = V = 64
     assert ws(_desc(qkv_dtype=0, key_dim=64, value_dim=64)) == 0
     assert ws(_desc(chunk=48)) == 4
-    assert ws(_desc(chunk=32)) == 0 and n.value == base          # computed with 64-token tiles
+    assert ws(_desc(chunk=32)) == 4 and ws(_desc(chunk=16)) == 4  # only the 64-token tiling
     # the workspace grows with the per-chunk states: above the forward layout
     assert n.value > gdn.workspace_layout(_desc(qkv_dtype=0, key_dim=64, value_dim=64)).total
     d = _desc()
@@ -223,13 +225,13 @@ def test_l2norm_flag_and_workspace(lib):
     def ws(flags, desc=d):
         a = gdn.Activation(flags, None, None)
         return lib.gdn_chunk_fwd_workspace_act(ctypes.byref(desc), ctypes.byref(a), ctypes.byref(n))
-    assert ws(0) == 0 and n.value == gdn.workspace_bytes(d) == 256
-    assert ws(8) == 0 and n.value == 256
+    assert ws(0) == 0 and n.value == gdn.workspace_bytes(d) == 512
+    assert ws(8) == 0 and n.value == 512
     f32 = _desc(qkv_dtype=0)
     assert ws(8, f32) == 0 and n.value == gdn.workspace_layout(f32).total
     assert ws(16) == 4
     assert lib.gdn_chunk_fwd_workspace_act(ctypes.byref(d), None, ctypes.byref(n)) == 0
-    assert n.value == 256
+    assert n.value == 512
     # the two-stage route with the flag still checks its workspace
     a = gdn.Activation(8, None, None)
     assert lib.gdn_chunk_fwd_act(ctypes.byref(f32), ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE,
@@ -237,20 +239,54 @@ def test_l2norm_flag_and_workspace(lib):
 
 
 def test_chunk_sizes(lib):
-    """chunk 16 and 32 are accepted where only outputs come back (computed
-    with the 64-token tiling: same workspace) and refused, before any launch,
-    where the workspace holds per-chunk intermediates."""
+    """Only the 64-token tiling is built: chunk 16 and 32 are refused with
+    GDN_ERR_UNSUPPORTED by every entry point, before any launch."""
     n = ctypes.c_size_t()
+    L = gdn.WorkspaceLayout()
+    a = gdn.Activation(0, None, None)
     for c in (16, 32):
-        assert gdn.workspace_bytes(_desc(chunk=c)) == gdn.workspace_bytes(_desc())
-        assert gdn.workspace_bytes(_desc(chunk=c, qkv_dtype=0)) == gdn.workspace_bytes(_desc(qkv_dtype=0))
-        L = gdn.WorkspaceLayout()
-        assert lib.gdn_workspace_layout_of(ctypes.byref(_desc(chunk=c)), ctypes.byref(L)) == 4
-        assert lib.gdn_chunk_intra(ctypes.byref(_desc(chunk=c)), FAKE, FAKE, FAKE, FAKE, FAKE, None,
-                                   FAKE, 1 << 40, 0, None) == 4
-        assert lib.gdn_chunk_scan(ctypes.byref(_desc(chunk=c)), None, None, FAKE, None, FAKE, 1 << 40,
-                                  None) == 4
-        assert "per-chunk" in lib.gdn_last_error().decode()
+        for kw in (dict(), dict(qkv_dtype=0), dict(gate=1)):
+            d = _desc(chunk=c, **kw)
+            assert lib.gdn_chunk_fwd_workspace(ctypes.byref(d), ctypes.byref(n)) == 4
+            assert lib.gdn_chunk_fwd_workspace_act(ctypes.byref(d), ctypes.byref(a), ctypes.byref(n)) == 4
+            assert lib.gdn_workspace_layout_of(ctypes.byref(d), ctypes.byref(L)) == 4
+            assert _fwd(lib, d) == 4
+            assert lib.gdn_chunk_fwd_act(ctypes.byref(d), ctypes.byref(a), FAKE, FAKE, FAKE, FAKE,
+                                         FAKE, None, None, FAKE, None, FAKE, 1 << 40, None) == 4
+            assert lib.gdn_chunk_intra(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                       FAKE, 1 << 40, 0, None) == 4
+            assert lib.gdn_chunk_scan(ctypes.byref(d), None, None, FAKE, None, FAKE, 1 << 40,
+                                      None) == 4
+            assert "64-token" in lib.gdn_last_error().decode()
+        d = _desc(chunk=c)
+        assert lib.gdn_chunk_bwd_workspace(ctypes.byref(d), ctypes.byref(n)) == 4
+        assert lib.gdn_chunk_bwd(ctypes.byref(d), *([FAKE] * 5), None, None, FAKE, None,
+                                 *([FAKE] * 5), None, FAKE, 1 << 40, None) == 4
+        assert lib.gdn_sync_status_offset(ctypes.byref(d), None, ctypes.byref(n)) == 4
+
+
+def test_sync_status_offset(lib):
+    """The single-pass kernel's synchronisation status word: inside the
+    workspace it is sized for, after the packed-input records and their
+    check word; shapes that run the two-stage route have none."""
+    off = ctypes.c_size_t()
+
+    def where(d, act=None):
+        return lib.gdn_sync_status_offset(ctypes.byref(d), ctypes.byref(act) if act else None,
+                                          ctypes.byref(off))
+    d = _desc()
+    assert where(d) == 0 and off.value == 256 and off.value + 4 <= gdn.workspace_bytes(d)
+    p = _desc(batch=1, seq_len=300, num_seqs=40)
+    assert where(p) == 0 and off.value == 768 and off.value + 4 <= gdn.workspace_bytes(p)
+    so = ctypes.c_size_t()
+    assert lib.gdn_seqlens_status_offset(ctypes.byref(p), None, 0, ctypes.byref(so)) == 0
+    assert so.value + 4 <= off.value                            # the two words do not overlap
+    assert where(d, gdn.Activation(8, None, None)) == 0 and off.value == 256
+    assert where(_desc(qkv_dtype=0)) == 4                       # two stages: no waits
+    assert where(_desc(gate=1)) == 4
+    assert where(_desc(key_dim=64)) == 4
+    assert lib.gdn_sync_status_offset(ctypes.byref(d), None, None) == 1
+    assert gdn.sync_status_offset(d) == 256 and gdn.sync_status_offset(_desc(gate=1)) is None
 
 
 def test_seqlens_status_offset(lib):
