@@ -13,7 +13,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdn.so")
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GATE_SCALAR, GATE_PER_KEY = 0, 1
@@ -26,7 +26,8 @@ EXPORTS = sorted(["gdn_abi_version", "gdn_status_str", "gdn_last_error",
                   "gdn_chunk_intra", "gdn_chunk_scan", "gdn_recurrent_step",
                   "gdn_chunk_fwd_act", "gdn_recurrent_step_act",
                   "gdn_chunk_bwd_workspace", "gdn_chunk_bwd", "gdn_chunk_bwd_act",
-                  "gdn_seqlens_status_offset", "gdn_sync_status_offset"])
+                  "gdn_seqlens_status_offset", "gdn_sync_status_offset",
+                  "gdn_chunk_fwd_noalloc"])
 INTRA_STORE_AINV = 1
 ACT_GATE, ACT_BETA_SIGMOID, ACT_BETA_NEG_EIG, ACT_QK_L2NORM = 1, 2, 4, 8
 
@@ -116,6 +117,9 @@ def load(path: str = LIB_PATH):
     lib.gdn_sync_status_offset.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(Activation),
                                            ctypes.POINTER(ctypes.c_size_t)]
     lib.gdn_sync_status_offset.restype = S
+    lib.gdn_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(FwdDesc), ctypes.POINTER(Activation),
+                                          P, P, P, P, P, P, P, P, P, P]
+    lib.gdn_chunk_fwd_noalloc.restype = S
     v = lib.gdn_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError("libgdn.so ABI %d, binding expects %d" % (v, ABI_VERSION))

@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/gdn.h"
 #include "gdn_launch.hpp"
 
@@ -286,6 +288,37 @@ gdn_status prepare(const gdn_fwd_desc* d, const void* q, const void* k, const vo
     return GDN_OK;
 }
 
+// ---- the allocation-free variant of the single-pass forward
+// Its scratch (the per-sequence records of packed input and the check word
+// of cu_seqlens) lives in this file-scope device array: each GPU the library
+// runs on holds its own copy until the process ends.  Host code never uses
+// the array's name as an address: the address of the current device's copy
+// comes from hipGetSymbolAddress, once per device.
+constexpr int64_t NOALLOC_MAX_SEQS = GDN_NOALLOC_MAX_SEQS;
+constexpr size_t NOALLOC_BYTES = ((NOALLOC_MAX_SEQS + 1) * 16 + 255) / 256 * 256 + 256;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[MAX_DEVICES] = {};
+
+gdn_status scratch_of_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= MAX_DEVICES) return fail(GDN_ERR_UNSUPPORTED, "device %d", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(GDN_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -440,7 +473,8 @@ gdn_status gdn_chunk_scan(const gdn_fwd_desc* d, const float* h0, const int64_t*
 static gdn_status fused_fwd(const gdn_fwd_desc* d, const void* q, const void* k, const void* v,
                             const float* beta, const float* g, const float* h0,
                             const int64_t* cu_seqlens, void* o, float* ht, void* workspace,
-                            size_t workspace_bytes, hipStream_t st, const gdn::Act& act) {
+                            size_t workspace_bytes, hipStream_t st, const gdn::Act& act,
+                            bool report_sync = true) {
     const bool packed = cu_seqlens != nullptr;
     if (!packed && d->num_seqs != 0)
         return fail(GDN_ERR_BAD_SHAPE, "num_seqs must be 0 without cu_seqlens");
@@ -466,7 +500,9 @@ static gdn_status fused_fwd(const gdn_fwd_desc* d, const void* q, const void* k,
     a.ht = ht;
     a.o = o;
     a.seqs = nullptr;
-    a.sync_status = reinterpret_cast<int*>(static_cast<char*>(workspace) + fused_sync_offset(d, packed));
+    a.sync_status = report_sync ? reinterpret_cast<int*>(static_cast<char*>(workspace) +
+                                                         fused_sync_offset(d, packed))
+                                : nullptr;
     a.T = d->seq_len;
     a.N = packed ? d->num_seqs : d->batch;
     a.H = vheads(d);
@@ -518,6 +554,36 @@ gdn_status gdn_chunk_fwd_act(const gdn_fwd_desc* d, const gdn_activation* act_in
     s = prepare(d, q, k, v, beta, g, cu_seqlens, workspace, workspace_bytes, false, st, &P, act);
     if (s != GDN_OK) return s;
     return scan(d, h0, cu_seqlens, o, ht, workspace, workspace_bytes, st);
+}
+
+gdn_status gdn_chunk_fwd_noalloc(const gdn_fwd_desc* d, const gdn_activation* act_in,
+                                 const void* q, const void* k, const void* v, const float* beta,
+                                 const float* g, const float* h0, const int64_t* cu_seqlens,
+                                 void* o, float* ht, void* stream) {
+    const bool packed = cu_seqlens != nullptr;
+    gdn_status s = check_desc(d, packed);
+    if (s != GDN_OK) return s;
+    gdn::Act act;
+    s = check_act(act_in, &act);
+    if (s != GDN_OK) return s;
+    if (!fused_path(d, act.flags))
+        return fail(GDN_ERR_UNSUPPORTED,
+                    "gdn_chunk_fwd_noalloc runs the single-pass kernel only (bf16 q/k/v, scalar "
+                    "gate, K = V = 128, chunk 64)");
+    if (packed && d->num_seqs > NOALLOC_MAX_SEQS)
+        return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_fwd_noalloc takes at most %lld packed sequences "
+                    "(got %lld)", (long long)NOALLOC_MAX_SEQS, (long long)d->num_seqs);
+    if (!o) return fail(GDN_ERR_NULL_ARG, "o is NULL");
+    if (!aligned16(o) || !aligned4(h0) || !aligned4(ht))
+        return fail(GDN_ERR_MISALIGNED, "o needs 16-byte, h0 and ht 4-byte alignment");
+    if (fused_workspace(d, packed) > NOALLOC_BYTES)
+        return fail(GDN_ERR_UNSUPPORTED, "scratch of %zu bytes exceeds the library's %zu",
+                    fused_workspace(d, packed), NOALLOC_BYTES);
+    void* ws = nullptr;
+    s = scratch_of_current_device(&ws);
+    if (s != GDN_OK) return s;
+    return fused_fwd(d, q, k, v, beta, g, h0, cu_seqlens, o, ht, ws, NOALLOC_BYTES,
+                     static_cast<hipStream_t>(stream), act, /*report_sync=*/false);
 }
 
 gdn_status gdn_chunk_fwd(const gdn_fwd_desc* d, const void* q, const void* k, const void* v,

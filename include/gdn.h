@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 8
+#define GDN_ABI_VERSION 9
 
 typedef int32_t gdn_status;
 enum {
@@ -263,6 +263,31 @@ gdn_status gdn_chunk_fwd_act(const gdn_fwd_desc *d, const gdn_activation *act,
                              void *o, float *ht,
                              void *workspace, size_t workspace_bytes,
                              void *stream);
+
+/*
+ * gdn_chunk_fwd_act without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It runs the single-pass kernel only:
+ * d must describe bf16 q/k/v, the scalar gate, K = V = 128, chunk 64, and
+ * at most GDN_NOALLOC_MAX_SEQS packed sequences; other shapes give
+ * GDN_ERR_UNSUPPORTED before anything is launched.  Arguments, layouts and
+ * results are those of gdn_chunk_fwd_act (act may be NULL).
+ * Its scratch (the per-sequence records of packed input) is a device array
+ * inside the library, about 66 KB, one per GPU, held until the process
+ * ends; its address on the current device is looked up on the first call on
+ * that device.  The call itself allocates nothing.  Every call on one GPU
+ * uses the same scratch: calls that may overlap on one GPU (on different
+ * streams, or from several threads without ordering) race and give wrong
+ * results; calls ordered on one stream do not.  The device-side check of
+ * cu_seqlens and the synchronisation status word of gdn_chunk_fwd are not
+ * reported by this entry point.
+ */
+#define GDN_NOALLOC_MAX_SEQS 4096
+gdn_status gdn_chunk_fwd_noalloc(const gdn_fwd_desc *d, const gdn_activation *act,
+                                 const void *q, const void *k, const void *v,
+                                 const float *beta, const float *g, const float *h0,
+                                 const int64_t *cu_seqlens,
+                                 void *o, float *ht, void *stream);
 
 /*
  * Where gdn_chunk_intra / gdn_chunk_scan (and the two-stage route of
