@@ -14,8 +14,19 @@ and h0 from seeded dO and dht), the per-key-gate (KDA) prefill B=2, T=8192,
 H=16 (two-stage route), the packed variable-length prefill (16 sequences,
 137 491 tokens, H=32; fused route), and the fp64 CPU oracle on the host cores.
 
+Every leg first runs its own call back to back for a fixed wall time
+(--settle-s): the shader clock drops during the host's pauses (input
+generation, the previous leg's host work) and needs a few milliseconds of
+load to come back to its sustained rate, which a handful of warm-up launches
+does not give.  Then W warm-up launches and the K timed ones.  The record
+also carries the device (CU count, ROCm), the shader and memory clocks
+sampled under the prefill's load, an Infinity-Cache-flushed median next to
+the back-to-back prefill time, and the fp64 oracle timed on the host cores on
+every workload.
+
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-decode]
-                  [--no-backward] [--no-kda] [--no-varlen]
+                  [--no-backward] [--no-kda] [--no-varlen] [--no-variants]
+                  [--only LEG]
 """
 from __future__ import annotations
 
@@ -86,6 +97,98 @@ def measured_traffic(kernel):
     return rec["bytes_per_launch"] if h.hexdigest()[:16] == rec["source_sha"] else None
 
 
+def settle(fn, seconds):
+    """Run fn() back to back for `seconds` of wall time, so that the GPU's
+    clock is at its sustained rate when the timing starts."""
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(16):
+            fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return
+
+
+class ClockSampler:
+    """Samples the shader (sclk) and memory (mclk) clocks with rocm-smi in a
+    background thread while the GPU works; empty if the tool is absent."""
+
+    def __init__(self):
+        import threading
+        self.samples, self.stop, self.th = [], False, threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        import re
+        import subprocess
+        while not self.stop:
+            try:
+                r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                                   text=True, timeout=20)
+                card = next(iter(json.loads(r.stdout).values()))
+                mhz = lambda k: int(re.search(r"(\d+)", card[k]).group(1))  # noqa: E731
+                self.samples.append((mhz("sclk clock speed:"), mhz("mclk clock speed:")))
+            except Exception:
+                return
+
+    def __enter__(self):
+        self.th.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop = True
+        self.th.join()
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return None
+        sc = sorted(x[0] for x in self.samples)
+        mc = sorted(x[1] for x in self.samples)
+        return {"samples": len(sc), "sclk_mhz_min": sc[0], "sclk_mhz_median": sc[len(sc) // 2],
+                "sclk_mhz_max": sc[-1], "mclk_mhz_min": mc[0], "mclk_mhz_max": mc[-1],
+                "source": "rocm-smi --showclocks, sampled while the prefill leg ran back to back"}
+
+
+def flushed_median(fn, reps, flush_bytes=512 << 20):
+    """Median duration of fn() when a flush_bytes scratch write (larger than
+    the 256 MB Infinity Cache) runs right before each launch, outside the
+    timed events: fn's inputs then come from HBM."""
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for r in range(reps):
+        scratch.fill_(r & 0xff)
+        ev[r][0].record()
+        fn()
+        ev[r][1].record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) / 1e3 for a, b in ev)
+    del scratch
+    return t[len(t) // 2]
+
+
+def device_info():
+    import platform
+    p = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        pass
+    cpu = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count, "hbm_bytes": p.total_memory,
+            "rocm": rocm, "torch_hip": torch.version.hip, "host_cpu": cpu,
+            "host_affinity_cpus": len(os.sched_getaffinity(0)), "host": platform.machine()}
+
+
 def events_time(fn, reps):
     """Average duration of fn() over reps back-to-back launches, from HIP
     events recorded on the current stream (the stream the kernels use)."""
@@ -130,9 +233,12 @@ def bench_prefill(args, gdn):
     desc = gdn.fwd_desc(q, v, "scalar", 64, d["scale"])
     ws = torch.empty(gdn.workspace_bytes(desc), dtype=torch.uint8, device="cuda")
 
+    ws.zero_()
+
     def step():
         gdn.chunk_fwd(q, k, v, beta, g, d["scale"], h0=h0, o=o, ht=ht, workspace=ws)
 
+    settle(step, args.settle_s)
     for _ in range(args.warmup):
         step()
     # timed region: wall clock around the K steps, and a HIP event pair on the
@@ -149,6 +255,18 @@ def bench_prefill(args, gdn):
     dt = (time.perf_counter() - t0) / args.steps
     t_fused = ev[0].elapsed_time(ev[1]) / args.steps / 1e3
     log("prefill step %.1f us (fused kernel %.1f us)" % (dt * 1e6, t_fused * 1e6))
+    # the single-pass kernel's synchronisation word: 0 unless a wait between
+    # its waves gave up (results then wrong)
+    sync_word = gdn.sync_status(desc, ws)
+    if sync_word != 0:
+        raise RuntimeError("the fused kernel reported a failed hand-off between its waves")
+    t_flushed = flushed_median(step, 20)
+    log("prefill with the Infinity Cache flushed before each call: %.1f us (median of 20)"
+        % (t_flushed * 1e6))
+    # the clocks under this leg's load, sampled after the timed region (the
+    # sampler's last rocm-smi call leaves the GPU idle for a while)
+    with ClockSampler() as clocks:
+        settle(step, 1.0)
 
     # the two-stage path on the same inputs, for comparison: per-kernel
     # durations inside its step sequence (intra, scan, intra, ...)
@@ -157,10 +275,11 @@ def bench_prefill(args, gdn):
     o2 = torch.empty_like(o)
     ht2 = torch.empty_like(ht)
     reps = max(args.steps, 10)
-    t_intra, t_scan = step_kernel_times(
-        lambda: gdn.chunk_intra(q, k, v, beta, g, d["scale"], store_ainv=False, workspace=ws2,
-                                views=False),
-        lambda: gdn.chunk_scan(desc, ws2, o2, h0=h0, ht=ht2), reps)
+    two = (lambda: gdn.chunk_intra(q, k, v, beta, g, d["scale"], store_ainv=False, workspace=ws2,
+                                   views=False),
+           lambda: gdn.chunk_scan(desc, ws2, o2, h0=h0, ht=ht2))
+    settle(lambda: (two[0](), two[1]()), args.settle_s)
+    t_intra, t_scan = step_kernel_times(two[0], two[1], reps)
     del ws2
     log("two-stage path: intra %.1f us, scan %.1f us" % (t_intra * 1e6, t_scan * 1e6))
 
@@ -171,7 +290,10 @@ def bench_prefill(args, gdn):
     kernels = {
         "fused_kernel": {"us": t_fused * 1e6, "alg_bytes": b_all, "GBps": b_all / t_fused / 1e9,
                          "TFLOPs": flops / t_fused / 1e12,
-                         "frac_mfma_bf16": flops / t_fused / BF16_PEAK},
+                         "frac_mfma_bf16": flops / t_fused / BF16_PEAK,
+                         "flushed_median_us": t_flushed * 1e6,
+                         "flushed_frac_hbm": b_all / t_flushed / HBM_PEAK,
+                         "sync_status": sync_word},
     }
     two_stage = {
         "intra_kernel": {"us": t_intra * 1e6, "alg_bytes": b_in, "GBps": b_in / t_intra / 1e9},
@@ -185,7 +307,7 @@ def bench_prefill(args, gdn):
         two_stage[name]["traffic"] = measured_traffic(name)
     path = {"alg_bytes": b_all, "GBps": b_all / dt / 1e9, "frac_hbm": b_all / dt / HBM_PEAK,
             "alg_flops": flops, "TFLOPs": flops / dt / 1e12, "frac_mfma_bf16": flops / dt / BF16_PEAK}
-    return spec, dt, roof, path, kernels, two_stage, d
+    return spec, dt, roof, path, kernels, two_stage, d, clocks.summary()
 
 
 def bench_decode(args, gdn):
@@ -201,13 +323,14 @@ def bench_decode(args, gdn):
             gdn.recurrent_step(x["q"][s], x["k"][s], x["v"][s], x["beta"][s], x["g"][s], state,
                                d["scale"], o=o)
 
+    settle(run_steps, args.settle_s)
     t = events_time(run_steps, 1) / spec.steps
     es = 2 if spec.dtype == "bf16" else 4
     pairs = spec.N * spec.H
     gate = 4 * (spec.K if spec.gate == "per_key" else 1)
     step_bytes = pairs * (2 * 4 * spec.K * spec.V + (2 * spec.K + 2 * spec.V) * es + 4 + gate)
     log("decode step %.1f us" % (t * 1e6))
-    return {"workload": spec.name, "us_per_step": t * 1e6, "steps": spec.steps,
+    return d, {"workload": spec.name, "us_per_step": t * 1e6, "steps": spec.steps,
             "tokens_per_s": spec.N / t,
             "roofline": {"bound": "hbm", "kernel": "step_kernel",
                          "achieved": step_bytes / t / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
@@ -232,6 +355,7 @@ def bench_backward(args, gdn, d):
     def call():
         gdn.chunk_bwd(q, k, v, beta, g, do, d["scale"], h0=h0, dht=dht, workspace=ws, out=out)
 
+    settle(call, args.settle_s)
     for _ in range(max(args.warmup // 10, 5)):
         call()
     reps = max(args.steps // 5, 5)
@@ -271,19 +395,21 @@ def bench_kda(args, gdn):
     def call():
         gdn.chunk_fwd(q, k, v, beta, g, d["scale"], gate="per_key", o=o, ht=ht, workspace=ws)
 
+    settle(call, args.settle_s)
     for _ in range(10):
         call()
     reps = max(args.steps // 5, 10)
     t = events_time(call, reps)
+    t_flushed = flushed_median(call, 20)
     t_intra, t_scan = step_kernel_times(
         lambda: gdn.chunk_intra(q, k, v, beta, g, d["scale"], gate="per_key", store_ainv=False,
                                 workspace=ws, views=False),
         lambda: gdn.chunk_scan(desc, ws, o, ht=ht), reps)
     b_in, b_out = prefill_bytes(spec, spec.B)
     log("KDA prefill %.1f us per call (intra %.1f, scan %.1f)" % (t * 1e6, t_intra * 1e6, t_scan * 1e6))
-    return {"workload": spec.name, "us_per_call": t * 1e6, "tokens_per_s": spec.B * spec.T / t,
+    return d, {"workload": spec.name, "us_per_call": t * 1e6, "tokens_per_s": spec.B * spec.T / t,
             "alg_bytes": b_in + b_out, "GBps": (b_in + b_out) / t / 1e9,
-            "frac_hbm": (b_in + b_out) / t / HBM_PEAK,
+            "frac_hbm": (b_in + b_out) / t / HBM_PEAK, "flushed_median_us": t_flushed * 1e6,
             "kernels": {"intra_kernel": {"us": t_intra * 1e6, "alg_bytes": b_in,
                                          "GBps": b_in / t_intra / 1e9,
                                          "traffic": measured_traffic("kda_intra_kernel")},
@@ -333,6 +459,7 @@ def bench_variants(args, gdn):
                  B._ptr(o), B._ptr(ht), B._ptr(ws), nbytes, B._stream(None))
         B._check(lib.gdn_chunk_fwd_act(*cargs))
         if first:   # the clock settles again after the host-side input generation
+            settle(lambda: lib.gdn_chunk_fwd_act(*cargs), args.settle_s)
             for _ in range(args.warmup):
                 lib.gdn_chunk_fwd_act(*cargs)
             first = False
@@ -352,46 +479,110 @@ def bench_varlen(args, gdn):
     q, k, v, beta, g, cu = (x[n] for n in ("q", "k", "v", "beta", "g", "cu_seqlens"))
     N = cu.numel() - 1
     desc = gdn.fwd_desc(q, v, "scalar", spec.chunk, d["scale"], N)
-    ws = torch.empty(gdn.workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(gdn.workspace_bytes(desc), dtype=torch.uint8, device="cuda")
     o = torch.empty_like(v)
     ht = torch.empty((N, spec.H, spec.K, spec.V), dtype=torch.float32, device="cuda")
 
     def call():
         gdn.chunk_fwd(q, k, v, beta, g, d["scale"], cu_seqlens=cu, o=o, ht=ht, workspace=ws)
 
+    settle(call, args.settle_s)
     for _ in range(5):
         call()
     reps = 10
     t = events_time(call, reps)
+    sync_word = gdn.sync_status(desc, ws)
+    if sync_word != 0:
+        raise RuntimeError("the fused kernel reported a failed hand-off between its waves")
     tokens = int(q.shape[1])
     es = 2
     alg = tokens * spec.H * ((2 * spec.K + 2 * spec.V) * es + 8) + 4 * spec.K * spec.V * spec.H * N
     longest = max(d["lengths"])
     log("varlen prefill %.1f us per call (%d tokens, longest sequence %d)" % (t * 1e6, tokens, longest))
-    return {"workload": spec.name, "us_per_call": t * 1e6, "tokens": tokens, "sequences": N,
+    return d, {"workload": spec.name, "us_per_call": t * 1e6, "tokens": tokens, "sequences": N,
+            "sync_status": sync_word,
             "longest": longest, "tokens_per_s": tokens / t, "alg_bytes": alg,
             "GBps": alg / t / 1e9, "frac_hbm": alg / t / HBM_PEAK,
             "us_per_chunk_of_longest": t * 1e6 / ((longest + spec.chunk - 1) // spec.chunk),
             "traffic": measured_traffic("varlen_fused_kernel")}
 
 
-def cpu_baseline(d, min_s=10.0):
+def oracle_threads():
+    """Host threads for the oracle: every CPU this process may run on, but no
+    more than OMP_NUM_THREADS when the environment sets it (the host's share
+    of CPUs for one GPU)."""
+    cores = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return min(cores, int(env)) if env.isdigit() and int(env) > 0 else cores
+
+
+def _repeat(fn, min_s, max_s=30.0):
+    done, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= min_s or el / done * (done + 1) > max_s:
+            return done, el
+
+
+def cpu_baseline(d, threads, min_s=8.0):
+    """The fp64 token recurrence over the whole prefill workload, repeated
+    for >= min_s of wall time; conversions to fp64 are not timed."""
     import oracle
-    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    cores = min(cores, 16)
     args = [oracle.as_f64(d[n]) for n in ("q", "k", "v", "beta", "g")]
     h0 = oracle.as_f64(d["h0"])
     B, T = d["q"].shape[:2]
-    done, t0 = 0, time.perf_counter()
-    while True:
-        oracle.recurrent_forward(*args, d["scale"], h0=h0, threads=cores)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= min_s or el / done * (done + 1) > 30.0:
-            break
-    return {"value": done * B * T / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    done, el = _repeat(lambda: oracle.recurrent_forward(*args, d["scale"], h0=h0, threads=threads),
+                       min_s)
+    return {"value": done * B * T / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "the whole workload (B=4, T=4096, H=16, d=128) run %d times by the fp64 "
                       "token recurrence, %.1f s wall" % (done, el)}
+
+
+def cpu_baselines_other(varlen_d, kda_d, decode_d, threads, budget_s=6.0):
+    """The oracle on the other workloads, each a bounded sample of about
+    budget_s seconds, scaled to whole-workload tokens/s."""
+    import oracle
+    out = {}
+    if varlen_d is not None:    # packed: groups of heads over all 16 sequences
+        d = varlen_d
+        H = d["q"].shape[2]
+        T = d["q"].shape[1]
+        heads, el, grp = 0, 0.0, 8
+        while heads < H and el < budget_s:
+            sl = slice(heads, heads + grp)
+            a = [oracle.as_f64(d[n][:, :, sl]) for n in ("q", "k", "v", "beta", "g")]
+            t0 = time.perf_counter()
+            oracle.recurrent_forward(*a, d["scale"], cu_seqlens=d["cu_seqlens"], threads=threads)
+            el += time.perf_counter() - t0
+            heads += grp
+            del a
+        out["varlen"] = {"value": T * heads / H / el, "unit": "tokens/s", "cores": threads,
+                         "kind": "oracle", "sample": "heads 0-%d of %d over all %d packed sequences "
+                         "(%d tokens), %.1f s wall" % (heads - 1, H, d["cu_seqlens"].numel() - 1, T, el)}
+    if kda_d is not None:
+        d = kda_d
+        a = [oracle.as_f64(d[n]) for n in ("q", "k", "v", "beta", "g")]
+        B, T = d["q"].shape[:2]
+        done, el = _repeat(lambda: oracle.recurrent_forward(*a, d["scale"], gate="per_key",
+                                                            threads=threads), budget_s)
+        out["kda"] = {"value": done * B * T / el, "unit": "tokens/s", "cores": threads,
+                      "kind": "oracle", "sample": "the whole per-key-gate workload (B=2, T=8192, "
+                      "H=16) run %d times, %.1f s wall" % (done, el)}
+        del a
+    if decode_d is not None:    # 64 steps of every sequence = a 64-token recurrence each
+        d = decode_d
+        a = [oracle.as_f64(d[n].transpose(0, 1).contiguous()) for n in ("q", "k", "v", "beta", "g")]
+        st = oracle.as_f64(d["state"])
+        S, N = d["q"].shape[:2]
+        done, el = _repeat(lambda: oracle.recurrent_forward(*a, d["scale"], h0=st, threads=threads),
+                           budget_s)
+        out["decode"] = {"value": done * N / (el / S), "unit": "tokens/s (sequences per step time)",
+                         "cores": threads, "kind": "oracle",
+                         "sample": "all %d sequences x 32 heads, %d consecutive steps (as one %d-token "
+                         "recurrence per sequence), run %d times, %.1f s wall" % (N, S, S, done, el)}
+    return out
 
 
 def main():
@@ -406,6 +597,10 @@ def main():
     ap.add_argument("--no-kda", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="seconds of back-to-back calls before each leg's warm-up and timing")
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "kda", "varlen", "variants"],
+                    help="run the prefill leg and this one only (for per-leg profiles)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (a known-size kernel to scale "
                          "hardware byte counters by)")
@@ -424,13 +619,25 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    spec, dt, roof, path, kernels, two_stage, d = bench_prefill(args, gdn)
-    decode = None if args.no_decode else bench_decode(args, gdn)
+    if args.only:
+        for leg in ("decode", "backward", "kda", "varlen", "variants"):
+            if leg != args.only:
+                setattr(args, "no_" + leg, True)
+        args.no_cpu = True
+    dev = device_info()
+    spec, dt, roof, path, kernels, two_stage, d, clocks = bench_prefill(args, gdn)
+    dec_d, decode = (None, None) if args.no_decode else bench_decode(args, gdn)
     backward = None if args.no_backward else bench_backward(args, gdn, d)
-    kda = None if args.no_kda else bench_kda(args, gdn)
-    varlen = None if args.no_varlen else bench_varlen(args, gdn)
+    kda_d, kda = (None, None) if args.no_kda else bench_kda(args, gdn)
+    var_d, varlen = (None, None) if args.no_varlen else bench_varlen(args, gdn)
     variants = None if args.no_variants else bench_variants(args, gdn)
-    cpu = None if args.no_cpu else cpu_baseline(d)
+    cpu, cpu_other = None, None
+    if not args.no_cpu:
+        threads = oracle_threads()
+        cpu = cpu_baseline(d, threads)
+        cpu_other = cpu_baselines_other(var_d, kda_d, dec_d, threads)
+        log("oracle on the host: %s" % ", ".join("%s %.0f tokens/s" % (n, r["value"])
+                                                for n, r in [("prefill", cpu)] + list(cpu_other.items())))
     line = {
         "metric": METRIC,
         "value": spec.B * spec.T / dt,
@@ -448,6 +655,10 @@ def main():
                    "V": spec.V, "chunk": spec.chunk, "gate": spec.gate, "h0": "N(0,0.02^2)"},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "cpu_baselines_other": cpu_other,
+        "device_info": dev,
+        "clocks_under_load": clocks,
+        "settle_s": args.settle_s,
         "path": path,
         "mfma_pct_of_bf16_peak": 100.0 * path["frac_mfma_bf16"],
         "kernels": kernels,
@@ -457,7 +668,6 @@ def main():
         "kda": kda,
         "varlen": varlen,
         "input_options": variants,
-        "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line), flush=True)
 

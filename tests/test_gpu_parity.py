@@ -155,14 +155,33 @@ def test_kda_prefill_full_size(gpu_lib):
     _roundtrip(gdn_synth.PREFILL[3], 3)
 
 
-def test_varlen_prefill_full_size_sampled_heads(gpu_lib):
-    """16 packed sequences (one of 65536 tokens), H=32: every sequence, the
-    first and last head computed by the oracle."""
-    _roundtrip(gdn_synth.PREFILL[2], 2, heads=(0, 31))
+def test_varlen_prefill_full_size(gpu_lib):
+    """16 packed sequences (one of 65536 tokens), H=32: every output of every
+    head and every sequence.  The oracle runs on groups of 8 heads at a time
+    (to bound host memory); the bar is taken over the whole output."""
+    d = gdn_synth.make_prefill(gdn_synth.PREFILL[2], 2)
+    print("case: packed full size, all heads", flush=True)
+    o, ht = run_gpu(d)
+    o = o.float().cpu()
+    ht = ht.cpu()
+    H = d["q"].shape[2]
+    num = {"o": 0.0, "ht": 0.0}
+    den = {"o": 0.0, "ht": 0.0}
+    for h0 in range(0, H, 8):
+        heads = list(range(h0, min(h0 + 8, H)))
+        o_ref, ht_ref = run_oracle(d, heads)
+        for name, got, want in (("o", o[:, :, heads], o_ref), ("ht", ht[:, heads], ht_ref)):
+            num[name] = max(num[name], float(np.abs(got.double().numpy() - want).max()))
+            den[name] = max(den[name], float(np.abs(want).max()))
+        print("  heads %d-%d done" % (heads[0], heads[-1]), flush=True)
+    for name in ("o", "ht"):
+        err = num[name] / den[name]
+        print("  %s relative error %.2e" % (name, err), flush=True)
+        assert np.isfinite(err) and err <= TOL["bf16"], (name, err)
 
 
 # ------------------------------------------------------------------ decode
-def _decode_case(spec, seed, check_pairs=None):
+def _decode_case(spec, seed):
     import gated_delta_rule_14_amd as gdn
     d = gdn_synth.make_decode(spec, seed)
     print("case:", spec, "seed", seed, flush=True)
@@ -174,25 +193,14 @@ def _decode_case(spec, seed, check_pairs=None):
                                        state, scale=d["scale"], gate=d["gate"]))
     torch.cuda.synchronize()
     o = torch.stack(outs).float().cpu()
-    st = state.cpu()
-    if check_pairs is None:
-        sel = slice(None)
-    else:
-        sel = list(check_pairs)
-    N = spec.N
     ref_state = oracle.as_f64(d["state"])
     tol = TOL[spec.dtype]
     for s in range(spec.steps):
         q, k, v, beta, g = (d[n][s] for n in ("q", "k", "v", "beta", "g"))
-        if check_pairs is not None:
-            q, k, v, beta, g = (t[sel] for t in (q, k, v, beta, g))
-            prev = ref_state[sel] if s == 0 else ref_state
-        else:
-            prev = ref_state
-        o_ref, ref_state = oracle.recurrent_step(q, k, v, beta, g, d["scale"], prev,
+        o_ref, ref_state = oracle.recurrent_step(q, k, v, beta, g, d["scale"], ref_state,
                                                  gate=d["gate"])
-        assert rel_err(o[s][sel], o_ref) <= tol, ("step", s)
-    assert rel_err(st[sel], ref_state) <= tol
+        assert rel_err(o[s], o_ref) <= tol, ("step", s)
+    assert rel_err(state.cpu(), ref_state) <= tol
 
 
 @pytest.mark.parametrize("dt,gate,K,V", [("bf16", "scalar", 128, 128), ("f32", "scalar", 64, 64),
@@ -202,10 +210,32 @@ def test_decode_steps(gpu_lib, dt, gate, K, V):
     _decode_case(spec, 21)
 
 
-def test_decode_full_size_sampled(gpu_lib):
-    """256 sequences x 32 heads, 64 steps in place; 24 sequences checked by
-    the oracle at every step, and their final state."""
-    _decode_case(gdn_synth.DECODE[4], 4, check_pairs=range(0, 256, 11))
+def test_decode_full_size(gpu_lib):
+    """256 sequences x 32 heads, 64 steps in place: the output of every
+    sequence and head at every step, and the final state, against the oracle.
+    The 64 steps of one sequence are its token recurrence over 64 tokens, so
+    the oracle runs them as one 64-token sequence per (sequence, head) (the
+    same function the single-step oracle calls, on all steps at once)."""
+    import gated_delta_rule_14_amd as gdn
+    spec = gdn_synth.DECODE[4]
+    d = gdn_synth.make_decode(spec, 4)
+    print("case: decode full size, every sequence and step", flush=True)
+    x = to_dev(d)
+    state = x["state"].clone()
+    outs = []
+    for s in range(spec.steps):
+        outs.append(gdn.recurrent_step(x["q"][s], x["k"][s], x["v"][s], x["beta"][s], x["g"][s],
+                                       state, scale=d["scale"], gate=d["gate"]))
+    torch.cuda.synchronize()
+    o = torch.stack(outs, 1).float().cpu()          # [N, steps, H, V]
+    seq = [d[n].transpose(0, 1).contiguous() for n in ("q", "k", "v", "beta", "g")]
+    o_ref, st_ref = oracle.recurrent_forward(*seq, d["scale"], h0=d["state"], gate=d["gate"])
+    eo, es = rel_err(o, o_ref), rel_err(state, st_ref)
+    print("  o relative error %.2e, state %.2e" % (eo, es), flush=True)
+    assert eo <= TOL[spec.dtype] and es <= TOL[spec.dtype]
+    # every step separately meets the bar too
+    for s in range(spec.steps):
+        assert rel_err(o[:, s], o_ref[:, s]) <= TOL[spec.dtype], ("step", s)
 
 
 def test_stages_compose_to_forward(gpu_lib):
