@@ -507,6 +507,12 @@ static gdn_status fused_fwd(const gdn_fwd_desc* d, const void* q, const void* k,
     a.N = packed ? d->num_seqs : d->batch;
     a.H = vheads(d);
     a.Hq = d->num_heads;
+    {   // inputs beyond the 256 MB Infinity Cache are read from HBM
+        const double tokens = (double)d->batch * (double)d->seq_len;
+        const double in_bytes = tokens * ((double)(2 * d->num_heads * d->key_dim) * 2 +
+                                          (double)(a.H * d->value_dim) * 2 + (double)a.H * 8);
+        a.loads_first = in_bytes > (double)(256u << 20);
+    }
     a.K = (int)d->key_dim;
     a.V = (int)d->value_dim;
     a.C = d->chunk;

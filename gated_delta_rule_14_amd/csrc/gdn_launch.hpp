@@ -168,6 +168,7 @@ struct FusedLaunch {
     void* o;
     const int4* seqs;       // [N] (t0, len, ...) for packed input, else nullptr
     int* sync_status;       // set to 1 by a wave whose bounded wait gave up, or nullptr
+    bool loads_first = false;   // issue each chunk's loads before its gate arrays
     int64_t T;              // tokens per sequence when seqs == nullptr
     int64_t N, H;
     int K, V, C;

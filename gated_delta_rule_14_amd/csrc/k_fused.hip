@@ -236,6 +236,7 @@ struct Ctx {
     Act act;
     float a_log, dt_bias;   // this head's gate-activation parameters
     int* sync_status;       // set when a wait gives up (nullptr: not reported)
+    bool loads_first;       // issue each chunk's loads before deriving its gates
 
     // slot accessors take chunk indices >= 0
     __device__ __forceinline__ char* sK(int c) const { return sm + o_K + SZ_KQ * (c % 3); }
@@ -336,52 +337,67 @@ __device__ __forceinline__ void role_load(const Ctx& x) {
         // (signalled to the product waves) and g, beta of chunk j+2
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         signal(x.lflag(), j + 2);
-        // gate arrays of chunk j+2, read from the next iteration on
         const int c2 = j + 2;
-        if (x.valid(c2)) {
-            const float* raw = reinterpret_cast<const float*>(x.sRaw(c2));
-            float gl = raw[lane], bt = raw[C + lane];
-            if (x.act.flags) {
-                // raw logits: rows past a ragged end must stay g = 0, beta = 0
-                const bool in = lane < x.rows(c2);
-                if (x.act.flags & ACT_GATE) gl = in ? act_log_gate(gl, x.a_log, x.dt_bias) : 0.f;
-                if (x.act.flags & ACT_BETA_SIGMOID)
-                    bt = in ? act_beta(bt, x.act.flags & ACT_BETA_NEG_EIG) : 0.f;
+        // gate arrays of chunk j+2, read from the next iteration on
+        auto gates = [&]() __attribute__((always_inline)) {
+            if (x.valid(c2)) {
+                const float* raw = reinterpret_cast<const float*>(x.sRaw(c2));
+                float gl = raw[lane], bt = raw[C + lane];
+                if (x.act.flags) {
+                    // raw logits: rows past a ragged end must stay g = 0, beta = 0
+                    const bool in = lane < x.rows(c2);
+                    if (x.act.flags & ACT_GATE) gl = in ? act_log_gate(gl, x.a_log, x.dt_bias) : 0.f;
+                    if (x.act.flags & ACT_BETA_SIGMOID)
+                        bt = in ? act_beta(bt, x.act.flags & ACT_BETA_NEG_EIG) : 0.f;
+                }
+                const float G = wave_scan(gl * LOG2E);
+                const float Gc = lane_of(G, C - 1);
+                const float gam = exp2_hw(G);
+                x.gate(c2, GA_G)[lane] = G;
+                x.gate(c2, GA_B)[lane] = bt;
+                x.gate(c2, GA_BG)[lane] = bt * gam;
+                x.gate(c2, GA_TAIL)[lane] = exp2_hw(fminf(Gc - G, 0.f));
+                x.gate(c2, GA_OUT)[lane] = x.scale * gam;
+                float Gs[4];
+#pragma unroll
+                for (int I = 0; I < 4; ++I) Gs[I] = lane_of(G, 16 * I);
+                const int bl = lane >> 4;
+                const float Gb = bl == 0 ? Gs[0] : bl == 1 ? Gs[1] : bl == 2 ? Gs[2] : Gs[3];
+                x.gate(c2, GA_ROW)[lane] = exp2_hw(fminf(G - Gb, 0.f));
+#pragma unroll
+                for (int I = 1; I < 4; ++I)
+                    x.gate(c2, GA_COL + I - 1)[lane] = exp2_hw(fminf(Gs[I] - G, 0.f));
+                x.gate(c2, GA_END)[lane] = exp2_hw(Gc);
             }
-            const float G = wave_scan(gl * LOG2E);
-            const float Gc = lane_of(G, C - 1);
-            const float gam = exp2_hw(G);
-            x.gate(c2, GA_G)[lane] = G;
-            x.gate(c2, GA_B)[lane] = bt;
-            x.gate(c2, GA_BG)[lane] = bt * gam;
-            x.gate(c2, GA_TAIL)[lane] = exp2_hw(fminf(Gc - G, 0.f));
-            x.gate(c2, GA_OUT)[lane] = x.scale * gam;
-            float Gs[4];
+        };
+        auto issue = [&]() __attribute__((always_inline)) {
+            // start the loads of K, Q, V of chunk j+2 and g, beta of chunk j+3 (a
+            // clamped duplicate past the end: its slot is free either way)
+            const int ck = x.clampc(c2);
+            const uint32_t nr = (uint32_t)x.rows(ck);
+            const __amdgpu_buffer_rsrc_t rk = rsrc(x.row0_qk(x.k, ck), nr * skq);
+            const __amdgpu_buffer_rsrc_t rq = rsrc(x.row0_qk(x.q, ck), nr * skq);
+            const __amdgpu_buffer_rsrc_t rv = rsrc(x.row0(x.v, ck, V), nr * sv);
 #pragma unroll
-            for (int I = 0; I < 4; ++I) Gs[I] = lane_of(G, 16 * I);
-            const int bl = lane >> 4;
-            const float Gb = bl == 0 ? Gs[0] : bl == 1 ? Gs[1] : bl == 2 ? Gs[2] : Gs[3];
-            x.gate(c2, GA_ROW)[lane] = exp2_hw(fminf(G - Gb, 0.f));
+            for (int s = 0; s < 16; ++s) {
+                to_lds16(rk, x.sK(c2) + 1024 * s, okq[s]);
+                to_lds16(rq, x.sQ(c2) + 1024 * s, okq[s]);
+            }
 #pragma unroll
-            for (int I = 1; I < 4; ++I)
-                x.gate(c2, GA_COL + I - 1)[lane] = exp2_hw(fminf(Gs[I] - G, 0.f));
-            x.gate(c2, GA_END)[lane] = exp2_hw(Gc);
+            for (int s = 0; s < 4; ++s) to_lds16(rv, x.sV(c2) + 1024 * s, ov[s]);
+            load_raw(j + 3);
+        };
+        // Inputs larger than the Infinity Cache come from HBM: their loads
+        // are issued first, which gives them the whole step to land.  Cache
+        // hits land early enough either way, and issued after the gate arrays
+        // their LDS writes meet less of the state waves' first reads.
+        if (x.loads_first) {
+            issue();
+            gates();
+        } else {
+            gates();
+            issue();
         }
-        // start the loads of K, Q, V of chunk j+2 and g, beta of chunk j+3 (a
-        // clamped duplicate past the end: its slot is free either way)
-        const int ck = x.clampc(c2);
-        const uint32_t nr = (uint32_t)x.rows(ck);
-        const __amdgpu_buffer_rsrc_t rk = rsrc(x.row0_qk(x.k, ck), nr * skq);
-        const __amdgpu_buffer_rsrc_t rq = rsrc(x.row0_qk(x.q, ck), nr * skq);
-        const __amdgpu_buffer_rsrc_t rv = rsrc(x.row0(x.v, ck, V), nr * sv);
-#pragma unroll
-        for (int s = 0; s < 16; ++s) {
-            to_lds16(rk, x.sK(c2) + 1024 * s, okq[s]);
-            to_lds16(rq, x.sQ(c2) + 1024 * s, okq[s]);
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) to_lds16(rv, x.sV(c2) + 1024 * s, ov[s]);
-        load_raw(j + 3);
         wg_barrier();
     }
     // no load may land in LDS after the workgroup has ended
@@ -913,6 +929,7 @@ __global__ __launch_bounds__(NT) void fused_kernel(FusedLaunch a) {
     x.scale = a.scale;
     x.act = a.act;
     x.sync_status = a.sync_status;
+    x.loads_first = a.loads_first;
     x.a_log = (a.act.flags & ACT_GATE) ? a.act.A_log[x.h] : 0.f;
     x.dt_bias = (a.act.flags & ACT_GATE) ? a.act.dt_bias[x.h] : 0.f;
     if (a.seqs) {
