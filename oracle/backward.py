@@ -24,8 +24,11 @@ chunked_backward
     Every decay ratio is taken in the log domain (gamma_C / gamma_i as
     exp(G_C - G_i)), as the forward's Gamma is: with strong gates gamma
     itself underflows to 0.
-    Scalar gate only.  It is pinned to recurrent_backward, which is in turn
-    pinned by central finite differences of the independent C recurrence.
+    With the per-key-channel gate (KDA) every Gamma-weighted product becomes a
+    per-channel decayed sum, (M o_E X)_id = sum_j M_ij X_jd exp(G_id - G_jd),
+    the carried state gradient decays row by row, and dG is per channel.
+    Both gates are pinned to recurrent_backward, which is in turn pinned by
+    central finite differences of the independent C recurrence.
 """
 from __future__ import annotations
 
@@ -162,13 +165,76 @@ def _chunk_bwd(Qc, Kc, Vc, bc, f, dOc, dH, scale):
     return dQ, dK, dV, dbeta, dg, dH_in, dVnew
 
 
+def _chunk_fwd_pk(Qc, Kc, Vc, bc, gc, h, scale):
+    """Forward of one chunk with the per-key-channel gate (gc [n, K]): every
+    decay ratio E[i, j, d] = exp(G_id - G_jd) (j <= i) sits inside the sum over
+    the key channel d ("DeltaNet 系列线性注意力变体的推导之旅", chunkwise KDA),
+    taken in the log domain and masked before the exponential."""
+    n = Kc.shape[0]
+    G = np.cumsum(gc, axis=0)                                 # [n, K]
+    incl = np.tril(np.ones((n, n), dtype=bool))[:, :, None]
+    D = G[:, None, :] - G[None, :, :]                          # [n, n, K]
+    E = np.where(incl, np.exp(np.where(incl, D, 0.0)), 0.0)
+    gam = np.exp(G)
+    end = gam[-1]                                             # [K]
+    rest = np.exp(G[-1][None, :] - G)
+    A = np.tril(bc[:, None] * np.einsum("id,jd,ijd->ij", Kc, Kc, E), -1)
+    Ainv = np.linalg.inv(np.eye(n) + A)
+    Aqk = scale * np.einsum("id,jd,ijd->ij", Qc, Kc, E)
+    Kg = gam * Kc
+    Y_of = lambda hh: Vc - Kg @ hh                            # noqa: E731
+    Vnew = Ainv @ (bc[:, None] * Y_of(h))
+    Ks = rest * Kc
+    return dict(G=G, E=E, gam=gam, end=end, rest=rest, A=A, Ainv=Ainv, Aqk=Aqk, Kg=Kg,
+                Y=Y_of(h), Vnew=Vnew, Ks=Ks, h_in=h, h_out=end[:, None] * h + Ks.T @ Vnew)
+
+
+def _chunk_bwd_pk(Qc, Kc, Vc, bc, f, dOc, dH, scale):
+    """Backward of one chunk with the per-key-channel gate; the same steps as
+    _chunk_bwd with each Gamma-weighted product taken per channel:
+    (M o_E X)_id = sum_j M_ij X_jd E_ijd.  Returns (dq, dk, dv, dbeta, dg,
+    dH entering, dVnew)."""
+    E, gam, end, rest = f["E"], f["gam"], f["end"], f["rest"]
+    h, Ainv, Aqk, Kg, Y, Vnew, Ks = (f[x] for x in ("h_in", "Ainv", "Aqk", "Kg", "Y", "Vnew", "Ks"))
+    n = Kc.shape[0]
+    incl = np.tril(np.ones((n, n), dtype=bool))
+    W = Ainv @ (bc[:, None] * Kg)
+    # the reverse recurrence (Steps 3-4): the carried gradient decays by row
+    dVnew = Aqk.T @ dOc + Ks @ dH
+    Qs = scale * gam * Qc
+    dH_in = end[:, None] * dH + Qs.T @ dOc - W.T @ dVnew
+    # Step 5: the output's products and the state update's decayed keys
+    dAqk = np.where(incl, dOc @ Vnew.T, 0.0)
+    dQs = dOc @ h.T
+    Pq = scale * np.einsum("ij,jd,ijd->id", dAqk, Kc, E)
+    Pk = scale * np.einsum("ij,id,ijd->jd", dAqk, Qc, E)
+    dKs = Vnew @ dH.T
+    # Step 6: V_new = Ainv diag(beta) Y with Y = V - (K * gamma) h
+    AtdU = Ainv.T @ dVnew
+    dY = bc[:, None] * AtdU
+    dKg = -dY @ h.T
+    dA = np.tril(-Ainv.T @ (dVnew @ (bc[:, None] * Y).T) @ Ainv.T, -1)
+    Pa1 = np.einsum("ij,jd,ijd->id", dA, Kc, E)
+    Pa2 = np.einsum("ij,i,id,ijd->jd", dA, bc, Kc, E)
+    dQ = scale * gam * dQs + Pq
+    dK = rest * dKs + gam * dKg + Pk + bc[:, None] * Pa1 + Pa2
+    dV = dY
+    dbeta = np.sum(AtdU * Y, axis=1) + np.sum(Kc * Pa1, axis=1)
+    # the gate: every place G_id enters, then the reverse cumulative sum
+    dG = (Qs * dQs + Qc * Pq - Kc * Pk - Ks * dKs + Kg * dKg
+          + bc[:, None] * Kc * Pa1 - Kc * Pa2)
+    dG[-1] += end * np.sum(h * dH, axis=1) + np.sum(Ks * dKs, axis=0)
+    dg = np.cumsum(dG[::-1], axis=0)[::-1]
+    return dQ, dK, dV, dbeta, dg, dH_in, dVnew
+
+
 def chunked_backward(q, k, v, beta, g, scale, do, h0=None, dht=None, cu_seqlens=None,
-                     chunk=64, keep=False):
-    """Chunkwise backward (scalar gate), fp64.  Arguments as
-    recurrent_backward plus the chunk length.  Returns the same dict (without
-    o, ht); with keep=True also 'dH_out' and 'h_in': dicts (seq, head, chunk)
-    -> the state gradient leaving / the state entering that chunk, and
-    'dVnew' [B,T,H,V]."""
+                     chunk=64, keep=False, gate="scalar"):
+    """Chunkwise backward, fp64.  Arguments as recurrent_backward plus the
+    chunk length.  Returns the same dict (without o, ht); with keep=True also
+    'dH_out' and 'h_in': dicts (seq, head, chunk) -> the state gradient
+    leaving / the state entering that chunk, and 'dVnew' [B,T,H,V]."""
+    fwd, bwd = (_chunk_fwd_pk, _chunk_bwd_pk) if gate == "per_key" else (_chunk_fwd, _chunk_bwd)
     q, k, v, beta, g, do = (as_f64(x) for x in (q, k, v, beta, g, do))
     B, T, H, K = q.shape
     V = v.shape[-1]
@@ -187,8 +253,8 @@ def chunked_backward(q, k, v, beta, g, scale, do, h0=None, dht=None, cu_seqlens=
             fw = []
             for c0 in range(s0, s1, chunk):
                 sl = slice(c0, min(c0 + chunk, s1))
-                f = _chunk_fwd(q[b, sl, hh], k[b, sl, hh], v[b, sl, hh], beta[b, sl, hh],
-                               g[b, sl, hh], h, scale)
+                f = fwd(q[b, sl, hh], k[b, sl, hh], v[b, sl, hh], beta[b, sl, hh],
+                        g[b, sl, hh], h, scale)
                 fw.append((sl, f))
                 h = f["h_out"]
             # Steps 3-6, last chunk first.
@@ -198,7 +264,7 @@ def chunked_backward(q, k, v, beta, g, scale, do, h0=None, dht=None, cu_seqlens=
                 if keep:
                     out["dH_out"][(n, hh, ci)] = dH.copy()
                     out["h_in"][(n, hh, ci)] = f["h_in"].copy()
-                dQ, dK, dV, dbt, dg, dH, dVn = _chunk_bwd(
+                dQ, dK, dV, dbt, dg, dH, dVn = bwd(
                     q[b, sl, hh], k[b, sl, hh], v[b, sl, hh], beta[b, sl, hh], f,
                     do[b, sl, hh], dH, scale)
                 out["dq"][b, sl, hh] = dQ

@@ -10,7 +10,9 @@ things outside itself:
     gradients of k and v vanish; dbeta at beta = 0 is the first-order effect
     of one write, derived by hand below.
 The chunked backward (the pages' six steps with the gate terms) is then
-pinned to the autograd oracle to 1e-10 at several chunk lengths.
+pinned to the autograd oracle to 1e-10 at several chunk lengths, for the
+scalar gate and for the per-key-channel gate (whose chunked form decays
+every product channel by channel).
 """
 import numpy as np
 import pytest
@@ -127,45 +129,49 @@ def _rel(a, b):
     return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
 
 
+@pytest.mark.parametrize("per_key", [False, True], ids=["gdn", "kda"])
 @pytest.mark.parametrize("chunk", [4, 16, 64])
 @pytest.mark.parametrize("T", [1, 63, 64, 150])
-def test_chunked_backward_matches_autograd(chunk, T):
-    d = draw(30 + T, B=2, T=T, H=2, K=8, V=6, A=(0.5, 8.0))
+def test_chunked_backward_matches_autograd(chunk, T, per_key):
+    d = draw(30 + T, B=2, T=T, H=2, K=8, V=6, A=(0.5, 8.0), per_key=per_key)
     do, dht = _extras(30 + T, d, 2)
     ref = recurrent_backward(d["q"], d["k"], d["v"], d["beta"], d["g"], 0.35, do,
-                             h0=d["h0"], dht=dht)
+                             h0=d["h0"], dht=dht, gate=d["gate"])
     got = chunked_backward(d["q"], d["k"], d["v"], d["beta"], d["g"], 0.35, do,
-                           h0=d["h0"], dht=dht, chunk=chunk)
+                           h0=d["h0"], dht=dht, chunk=chunk, gate=d["gate"])
     for name in NAMES:
         assert _rel(got[name], ref[name]) < 1e-10, name
 
 
-def test_chunked_backward_strong_decay():
+@pytest.mark.parametrize("per_key", [False, True], ids=["gdn", "kda"])
+def test_chunked_backward_strong_decay(per_key):
     """The pages' strongest gates (A up to 16): gamma underflows to 0 inside
     a 64-token chunk, and the chunked backward still matches (no 0/0)."""
-    d = draw(45, B=1, T=150, H=2, K=8, V=6, A=(8.0, 16.0))
+    d = draw(45, B=1, T=150, H=2, K=8, V=6, A=(8.0, 16.0), per_key=per_key)
     do, dht = _extras(45, d, 1)
     ref = recurrent_backward(d["q"], d["k"], d["v"], d["beta"], d["g"], 0.35, do,
-                             h0=d["h0"], dht=dht)
-    with np.errstate(divide="raise", invalid="raise"):
+                             h0=d["h0"], dht=dht, gate=d["gate"])
+    with np.errstate(divide="raise", invalid="raise", under="ignore"):
         got = chunked_backward(d["q"], d["k"], d["v"], d["beta"], d["g"], 0.35, do,
-                               h0=d["h0"], dht=dht, chunk=64)
-    assert np.exp(np.cumsum(d["g"][0, :64, 0]))[-1] == 0.0   # the case is the underflowing one
+                               h0=d["h0"], dht=dht, chunk=64, gate=d["gate"])
+    # the case is the underflowing one
+    assert np.any(np.exp(np.cumsum(d["g"][0, :64, 0], axis=0))[-1] == 0.0)
     for name in NAMES:
         assert _rel(got[name], ref[name]) < 1e-10, name
 
 
-def test_chunked_backward_packed_wide_beta():
-    d = draw(40, B=1, T=90, H=2, K=6, V=5)
+@pytest.mark.parametrize("per_key", [False, True], ids=["gdn", "kda"])
+def test_chunked_backward_packed_wide_beta(per_key):
+    d = draw(40, B=1, T=90, H=2, K=6, V=5, per_key=per_key)
     rng = np.random.default_rng(40)
     d["beta"] = rng.uniform(0.05, 1.95, size=d["beta"].shape)
     cu = np.array([0, 17, 17, 70, 90])
     d["h0"] = rng.standard_normal((4, 2, 6, 5)) * 0.3
     do, dht = _extras(40, d, 4)
     ref = recurrent_backward(d["q"], d["k"], d["v"], d["beta"], d["g"], 0.4, do,
-                             h0=d["h0"], dht=dht, cu_seqlens=cu)
+                             h0=d["h0"], dht=dht, cu_seqlens=cu, gate=d["gate"])
     got = chunked_backward(d["q"], d["k"], d["v"], d["beta"], d["g"], 0.4, do,
-                           h0=d["h0"], dht=dht, cu_seqlens=cu, chunk=16)
+                           h0=d["h0"], dht=dht, cu_seqlens=cu, chunk=16, gate=d["gate"])
     for name in NAMES:
         assert _rel(got[name], ref[name]) < 1e-10, name
 
@@ -257,3 +263,29 @@ def test_l2_normalize_backward_matches_finite_differences():
     assert np.max(np.abs(got - fd)) <= 1e-6 * max(np.max(np.abs(fd)), 1.0)
     g0 = l2_normalize_backward(x, dy, eps=0.0)
     assert np.max(np.abs(np.sum(g0 * x, axis=-1))) <= 1e-12
+
+
+@pytest.mark.parametrize("drop", ["row_decay", "gate_state_term"])
+def test_chunked_backward_per_key_mutations_fail(drop, monkeypatch):
+    """With the per-key gate, carrying the state gradient back with one mean
+    decay instead of row by row, or dropping the per-channel state term of
+    the last row's gate gradient, breaks the match with the autograd oracle."""
+    import oracle.backward as ob
+    real = ob._chunk_bwd_pk
+
+    def planted(Qc, Kc, Vc, bc, f, dOc, dH, scale):
+        dQ, dK, dV, dbt, dg, dH_in, dVn = real(Qc, Kc, Vc, bc, f, dOc, dH, scale)
+        if drop == "row_decay":
+            dH_in = dH_in - f["end"][:, None] * dH + np.mean(f["end"]) * dH
+        else:
+            dg = dg - (f["end"] * np.sum(f["h_in"] * dH, axis=1))[None, :]
+        return dQ, dK, dV, dbt, dg, dH_in, dVn
+
+    monkeypatch.setattr(ob, "_chunk_bwd_pk", planted)
+    d = draw(51, B=1, T=40, H=1, K=6, V=5, A=(0.02, 0.3), per_key=True)
+    do, dht = _extras(51, d, 1)
+    ref = recurrent_backward(d["q"], d["k"], d["v"], d["beta"], d["g"], 0.5, do,
+                             h0=d["h0"], dht=dht, gate="per_key")
+    got = ob.chunked_backward(d["q"], d["k"], d["v"], d["beta"], d["g"], 0.5, do,
+                              h0=d["h0"], dht=dht, chunk=8, gate="per_key")
+    assert max(_rel(got[n], ref[n]) for n in NAMES) > 1e-4
