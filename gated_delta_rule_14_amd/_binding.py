@@ -345,21 +345,22 @@ def bwd_workspace_bytes(desc: FwdDesc) -> int:
 
 
 def chunk_bwd(q, k, v, beta, g, do, scale=None, h0=None, dht=None, cu_seqlens=None, chunk=64,
-              want_dh0=True, workspace=None, out=None, stream=None, act=None):
+              want_dh0=True, workspace=None, out=None, stream=None, act=None, gate="scalar"):
     """gdn_chunk_bwd (gdn_chunk_bwd_act when act, from activation(), is
     given): gradients of <do, o> + <dht, ht> of the chunked forward with
-    respect to q, k, v, beta, g (scalar gate) and h0.  Returns a dict dq, dk,
-    dv (dtype of q), dbeta, dg, dh0 (float32; dh0 None unless want_dh0).
-    With act, beta and g are the raw logits, dbeta and dg their gradients,
-    and with the gate activation the dict also holds dA_log and ddt_bias
-    ([H] float32).  `out` may supply any of these tensors."""
+    respect to q, k, v, beta, g (scalar or, bf16 only, per-key gate) and h0.
+    Returns a dict dq, dk, dv (dtype of q), dbeta, dg (the shape of g), dh0
+    (float32; dh0 None unless want_dh0).  With act, beta and g are the raw
+    logits, dbeta and dg their gradients, and with the gate activation the
+    dict also holds dA_log ([H]) and ddt_bias (the shape of dt_bias), float32.
+    `out` may supply any of these tensors."""
     lib = load()
-    _inputs(q, k, v, beta, g, cu_seqlens, "scalar")
+    _inputs(q, k, v, beta, g, cu_seqlens, gate)
     _need(do, "do", q.dtype)
     if do.shape != v.shape:
         raise ValueError("do must have the shape of v")
     N = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
-    desc = fwd_desc(q, v, "scalar", chunk, scale, 0 if cu_seqlens is None else N)
+    desc = fwd_desc(q, v, gate, chunk, scale, 0 if cu_seqlens is None else N)
     H, K, V = v.shape[2], q.shape[3], v.shape[3]
     for t, name in ((h0, "h0"), (dht, "dht")):
         if t is not None:
@@ -382,10 +383,10 @@ def chunk_bwd(q, k, v, beta, g, do, scale=None, h0=None, dht=None, cu_seqlens=No
         if not want_dh0:
             out["dh0"] = None
         if act_gate:
-            _act_shapes(act, H, K, "scalar")
-            for name in ("dA_log", "ddt_bias"):
+            _act_shapes(act, H, K, gate)
+            for name, shape in (("dA_log", (H,)), ("ddt_bias", (H, K) if gate == "per_key" else (H,))):
                 if out.get(name) is None:
-                    out[name] = torch.empty((H,), dtype=torch.float32, device=dev)
+                    out[name] = torch.empty(shape, dtype=torch.float32, device=dev)
                 _need(out[name], name, torch.float32)
         if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)

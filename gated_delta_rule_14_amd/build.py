@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdn.so")
 SOURCES = ["gdn_api.hip", "k_step.hip", "k_table.hip", "k_intra.hip", "k_scan.hip", "k_bwd.hip",
-           "k_fused.hip"]
+           "k_bwd_kda.hip", "k_fused.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -143,16 +143,17 @@ void bwd_layout(const gdn_fwd_desc* d, bool packed, BwdLayout* L) {
     L->dk_part = off;
     off = align256(off + (gva ? rows * H * K * 4 : 0));
     // input activation: per (head, chunk slot) terms of dA_log and ddt_bias
+    // (per-key gate: ddt_bias per channel)
     L->act_part = off;
-    off = align256(off + blocks * 2 * 4);
+    off = align256(off + blocks * (d->gate == GDN_GATE_PER_KEY ? K + 2 : 2) * 4);
     L->total = off;
 }
 
 gdn_status check_bwd_desc(const gdn_fwd_desc* d, bool packed) {
     gdn_status s = check_desc(d, packed);
     if (s != GDN_OK) return s;
-    if (d->gate != GDN_GATE_SCALAR)
-        return fail(GDN_ERR_UNSUPPORTED, "the backward pass implements the scalar gate");
+    if (d->gate == GDN_GATE_PER_KEY && d->qkv_dtype != GDN_DTYPE_BF16)
+        return fail(GDN_ERR_UNSUPPORTED, "the per-key gate's backward needs bf16 q/k/v");
     if (d->qkv_dtype == GDN_DTYPE_F32 && (d->key_dim != 64 || d->value_dim != 64))
         return fail(GDN_ERR_UNSUPPORTED, "fp32 backward needs K = V = 64");
     return GDN_OK;
@@ -668,6 +669,7 @@ gdn_status gdn_chunk_bwd_act(const gdn_fwd_desc* d, const gdn_activation* act_in
     const int64_t H = vheads(d), Hq = d->num_heads;   // value heads, q/k heads
     const int64_t N = packed ? d->num_seqs : d->batch;
     const bool gva = H > Hq;
+    const bool per_key = d->gate == GDN_GATE_PER_KEY;
     hipError_t e;
     if (packed) {
         gdn::TableLaunch t;
@@ -698,7 +700,7 @@ gdn_status gdn_chunk_bwd_act(const gdn_fwd_desc* d, const gdn_activation* act_in
         a.C = d->chunk;
         a.scale = d->scale;
         a.bf16 = bf16;
-        a.per_key = false;
+        a.per_key = per_key;
         a.bwd = true;
         a.act = act;
         a.stream = st;
@@ -719,7 +721,7 @@ gdn_status gdn_chunk_bwd_act(const gdn_fwd_desc* d, const gdn_activation* act_in
         a.V = (int)d->value_dim;
         a.C = d->chunk;
         a.bf16 = bf16;
-        a.per_key = false;
+        a.per_key = per_key;
         a.stream = st;
         if ((e = gdn::launch_scan(a)) != hipSuccess) return hip_fail(e, "state pass launch");
     }
@@ -742,6 +744,7 @@ gdn_status gdn_chunk_bwd_act(const gdn_fwd_desc* d, const gdn_activation* act_in
         a.V = (int)d->value_dim;
         a.C = d->chunk;
         a.bf16 = bf16;
+        a.per_key = per_key;
         a.stream = st;
         if ((e = gdn::launch_bwd_scan(a)) != hipSuccess) return hip_fail(e, "reverse pass launch");
     }
@@ -776,6 +779,7 @@ gdn_status gdn_chunk_bwd_act(const gdn_fwd_desc* d, const gdn_activation* act_in
         a.C = d->chunk;
         a.scale = d->scale;
         a.bf16 = bf16;
+        a.per_key = per_key;
         a.stream = st;
         if ((e = gdn::launch_bwd_local(a)) != hipSuccess)
             return hip_fail(e, "per-chunk gradient launch");
@@ -816,6 +820,7 @@ gdn_status gdn_chunk_bwd_act(const gdn_fwd_desc* d, const gdn_activation* act_in
         r.dA_log = dA_log;
         r.ddt_bias = ddt_bias;
         r.H = H;
+        r.K = per_key ? (int)d->key_dim : 0;
         r.stream = st;
         if ((e = gdn::launch_act_reduce(r)) != hipSuccess) return hip_fail(e, "dA_log sum launch");
     }

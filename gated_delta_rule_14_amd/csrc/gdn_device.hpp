@@ -308,6 +308,32 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+// Sum over the 16 lanes of each DPP row (lanes 16g .. 16g+15) of each of the
+// 4 values a lane holds: an inclusive scan by row shifts, whose total lands
+// in the row's last lane (l % 16 == 15).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ f32x4 row_sum16(f32x4 v) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float x = v[e];
+        x = dpp_add<0x111>(x);   // row_shr:1
+        x = dpp_add<0x112>(x);   // row_shr:2
+        x = dpp_add<0x114>(x);   // row_shr:4
+        x = dpp_add<0x118>(x);   // row_shr:8
+        v[e] = x;
+    }
+    return v;
+}
+// Sum over the 4 lanes l % 16 == c of one value each (valid in every lane).
+__device__ __forceinline__ float sum_groups(float x) {
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
 // Store an R x D matrix X, of which an LDS buffer holds the VT columns
 // v0 .. v0+VT transposed (X^T rows, pitch ld elements), as fragment-order
 // groups of rows 16 rt0 .. 16 (rt0 + nrt) - 1: one 16-byte group per lane,

@@ -71,7 +71,7 @@ struct IntraLaunch {
     int K, V, C;
     float scale;
     bool bf16, per_key;
-    bool bwd = false;       // write the backward operand orders (scalar gate only)
+    bool bwd = false;       // write the backward operand orders (and the whole per-key gate)
     hipStream_t stream;
 };
 
@@ -93,7 +93,7 @@ struct ScanLaunch {
 // (sequence, head), last chunk first, parallel over value slices.
 struct BwdScanLaunch {
     ChunkMap map;
-    const float* gcum;      // [H][mc][C] cumulative log2 gate
+    const float* gcum;      // [H][mc][C] (or [H][mc][C][K]) cumulative log2 gate
     const void* ksr;        // Ks, Aqk^T, Qs^T, W^T per chunk in fragment order
     const void* aqkt;
     const void* qst;
@@ -106,6 +106,7 @@ struct BwdScanLaunch {
     int64_t N, H;
     int K, V, C;
     bool bf16;
+    bool per_key = false;   // the carried gradient decays row by row
     hipStream_t stream;
 };
 
@@ -113,7 +114,7 @@ struct BwdScanLaunch {
 struct BwdLocalLaunch {
     ChunkMap map;
     const void *q, *k, *v, *dout;
-    const float *beta, *gcum;
+    const float *beta, *gcum;   // gcum [H][mc][C] or, per-key gate, [H][mc][C][K]
     const void* ainv;       // [H][mc][C][C] (I + A)^{-1}, element type, row-major
     const void *hs, *dhs, *vn, *dvn;
     void *dq, *dk, *dv;
@@ -124,8 +125,9 @@ struct BwdLocalLaunch {
     float *dq_part = nullptr, *dk_part = nullptr;
     // input activation: beta and g hold raw logits; dbeta and dg are then the
     // gradients of the logits, and each (head, chunk slot) leaves its sums of
-    // dg * log alpha and of d(logit a) in act_part[h][slot][2] for
-    // launch_act_reduce
+    // dg * log alpha and of d(logit a) in act_part[h][slot][2] (per-key gate:
+    // [h][slot][K + 2], the sum of dg * log alpha first, the K per-channel
+    // sums from index 2) for launch_act_reduce
     Act act;
     const float* g = nullptr;   // the raw gate logits [B*T][H] (with ACT_GATE)
     float* act_part = nullptr;
@@ -134,15 +136,17 @@ struct BwdLocalLaunch {
     int K, V, C;
     float scale;
     bool bf16;
+    bool per_key = false;
     hipStream_t stream;
 };
 
-// dA_log[h], ddt_bias[h]: the sums of the per-chunk terms over the used slots
+// dA_log[h], ddt_bias[h] (or [h][K]): the sums of the per-chunk terms over the used slots
 struct ActReduceLaunch {
     ChunkMap map;
-    const float* part;      // [H][max_chunks][2]
+    const float* part;      // [H][max_chunks][2], or [H][max_chunks][K + 2] per-key
     float *dA_log, *ddt_bias;
     int64_t H;
+    int K = 0;              // per-key gate: the channels; 0 for the scalar gate
     hipStream_t stream;
 };
 
@@ -194,7 +198,8 @@ hipError_t launch_scan(const ScanLaunch& a);
 bool fused_supported(const FusedLaunch& a);
 hipError_t launch_fused(const FusedLaunch& a);
 hipError_t launch_bwd_scan(const BwdScanLaunch& a);
-hipError_t launch_bwd_local(const BwdLocalLaunch& a);
+hipError_t launch_bwd_local(const BwdLocalLaunch& a);       // dispatches per_key to the next
+hipError_t launch_bwd_local_kda(const BwdLocalLaunch& a);
 hipError_t launch_gva_sum(const GvaSumLaunch& a);
 hipError_t launch_act_reduce(const ActReduceLaunch& a);
 

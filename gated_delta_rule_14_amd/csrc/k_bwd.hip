@@ -51,9 +51,10 @@ namespace gdn {
 
 constexpr int BSCAN_MAX_THREADS = 512;
 
-template <typename T, int K_, int V_, int VT_, int PD_>
+template <typename T, int K_, int V_, int VT_, int PD_, bool PK_ = false>
 struct BScanCfg {
     typedef T Elt;
+    static constexpr bool PK = PK_;   // per-key gate: the carried dH decays row by row
     typedef Mma<T> M;
     typedef FragOrder<T> F;
     static constexpr int K = K_, V = V_, C = 64, VT = VT_, PD = PD_;
@@ -231,10 +232,11 @@ struct BScanDH {
     typedef typename Cfg::M M;
     typedef typename Cfg::F F;
     static constexpr int K = Cfg::K, V = Cfg::V, C = Cfg::C, CT = Cfg::CT, GC = Cfg::GC;
+    static constexpr bool PK = Cfg::PK;
     struct Pre {
         u32x4 qs[2][GC];
         u32x4 wt[2][GC];
-        float d;   // log2 chunk-end decay
+        float d[PK ? 8 : 1];   // log2 chunk-end decay (per key row for the per-key gate)
     };
     const BChain<Cfg>& ch;
     int p;
@@ -255,7 +257,15 @@ struct BScanDH {
                 q.qs[r][sg] = gq[((2 * p + r) * GC + sg) * 64 + ch.lane];
                 q.wt[r][sg] = gw[((2 * p + r) * GC + sg) * 64 + ch.lane];
             }
-        q.d = ch.a.gcum[b * C + (C - 1)];
+        if (PK) {
+            const float* gd = ch.a.gcum + (b * C + (C - 1)) * K;
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) q.d[PK ? 4 * r + e : 0] = gd[row(r, e)];
+        } else {
+            q.d[0] = ch.a.gcum[b * C + (C - 1)];
+        }
     }
 
     // dH <- dht (or 0); publish dH^T
@@ -297,7 +307,11 @@ struct BScanDH {
                     acc[1][ct] = M::mma(a1, bo, acc[1][ct]);
                 }
             }
-        const float dec = exp2_hw(cur.d);
+        float dec[2][4];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dec[r][e] = exp2_hw(cur.d[PK ? 4 * r + e : 0]);
         lds_barrier();   // dVn^T published
         // W^T dVn
 #pragma unroll
@@ -318,7 +332,9 @@ struct BScanDH {
         for (int r = 0; r < 2; ++r)
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-                hacc[r][ct] = dec * hacc[r][ct] + acc[r][ct] - neg[r][ct];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    hacc[r][ct][e] = dec[r][e] * hacc[r][ct][e] + acc[r][ct][e] - neg[r][ct][e];
                 store_acc_t(ch.shT + 16 * ct * Cfg::LDH + 16 * (2 * p + r), Cfg::LDH, ch.lane,
                             hacc[r][ct]);
             }
@@ -396,17 +412,22 @@ static hipError_t launch_bscan_cfg(const BwdScanLaunch& a) {
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_scan(const BwdScanLaunch& a) {
-    if (a.C != 64) return hipErrorInvalidValue;
+template <bool PK>
+static hipError_t launch_bwd_scan_g(const BwdScanLaunch& a) {
     if (!a.bf16) {   // the fp32 backward covers K = V = 64 (the per-chunk kernel's LDS)
-        if (a.K == 64 && a.V == 64) return launch_bscan_cfg<BScanCfg<float, 64, 64, 32, 1>>(a);
+        if (a.K == 64 && a.V == 64 && !PK) return launch_bscan_cfg<BScanCfg<float, 64, 64, 32, 1>>(a);
         return hipErrorInvalidValue;
     }
-    if (a.K == 64 && a.V == 64) return launch_bscan_cfg<BScanCfg<bf16, 64, 64, 32, 2>>(a);
-    if (a.K == 64 && a.V == 128) return launch_bscan_cfg<BScanCfg<bf16, 64, 128, 32, 2>>(a);
-    if (a.K == 128 && a.V == 64) return launch_bscan_cfg<BScanCfg<bf16, 128, 64, 32, 2>>(a);
-    if (a.K == 128 && a.V == 128) return launch_bscan_cfg<BScanCfg<bf16, 128, 128, 32, 2>>(a);
+    if (a.K == 64 && a.V == 64) return launch_bscan_cfg<BScanCfg<bf16, 64, 64, 32, 2, PK>>(a);
+    if (a.K == 64 && a.V == 128) return launch_bscan_cfg<BScanCfg<bf16, 64, 128, 32, 2, PK>>(a);
+    if (a.K == 128 && a.V == 64) return launch_bscan_cfg<BScanCfg<bf16, 128, 64, 32, 2, PK>>(a);
+    if (a.K == 128 && a.V == 128) return launch_bscan_cfg<BScanCfg<bf16, 128, 128, 32, 2, PK>>(a);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_scan(const BwdScanLaunch& a) {
+    if (a.C != 64) return hipErrorInvalidValue;
+    return a.per_key ? launch_bwd_scan_g<true>(a) : launch_bwd_scan_g<false>(a);
 }
 
 // =====================================================================
@@ -450,32 +471,6 @@ struct LocalSmem {
     static constexpr size_t bytes = o_RG + 4 * NW * C;
     static_assert(bytes <= 160 * 1024, "LDS");
 };
-
-// Sum over the 16 lanes of each DPP row (lanes 16g .. 16g+15) of each of the
-// 4 values a lane holds: an inclusive scan by row shifts, whose total lands
-// in the row's last lane (l % 16 == 15).
-template <int CTRL>
-__device__ __forceinline__ float dpp_add(float v) {
-    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-__device__ __forceinline__ f32x4 row_sum16(f32x4 v) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        float x = v[e];
-        x = dpp_add<0x111>(x);   // row_shr:1
-        x = dpp_add<0x112>(x);   // row_shr:2
-        x = dpp_add<0x114>(x);   // row_shr:4
-        x = dpp_add<0x118>(x);   // row_shr:8
-        v[e] = x;
-    }
-    return v;
-}
-// Sum over the 4 lanes l % 16 == c of one value each (valid in every lane).
-__device__ __forceinline__ float sum_groups(float x) {
-    x += __shfl_xor(x, 16, 64);
-    x += __shfl_xor(x, 32, 64);
-    return x;
-}
 
 // Inputs of one (chunk slot, head) item, held in registers from their loads
 // to their LDS stores.
@@ -1002,6 +997,7 @@ static hipError_t launch_blocal_t(const BwdLocalLaunch& a) {
 
 hipError_t launch_bwd_local(const BwdLocalLaunch& a) {
     if (a.C != 64) return hipErrorInvalidValue;
+    if (a.per_key) return launch_bwd_local_kda(a);
     if (!a.bf16) {
         // fp32 operands fit the LDS only at K = V = 64
         if (a.K == 64 && a.V == 64) return launch_blocal_t<float, 64, 64>(a);
@@ -1062,9 +1058,32 @@ __global__ __launch_bounds__(256) void act_reduce_kernel(ActReduceLaunch a) {
     }
 }
 
+// Per-key gate: thread u of head h's workgroup sums column u of the
+// per-chunk terms over the used slots, in slot order (u = 0: dA_log[h];
+// u = 2 + d: ddt_bias[h][d]).
+__global__ __launch_bounds__(256) void act_reduce_pk_kernel(ActReduceLaunch a) {
+    const int64_t h = blockIdx.x, mc = a.map.max_chunks;
+    const int S = a.K + 2;
+    for (int u = threadIdx.x; u < S; u += 256) {
+        if (u == 1) continue;
+        float s = 0.f;
+        for (int64_t c = 0; c < mc; ++c) {
+            if (a.map.table && a.map.table[c].y <= 0) continue;
+            s += a.part[(h * mc + c) * S + u];
+        }
+        if (u == 0)
+            a.dA_log[h] = s;
+        else
+            a.ddt_bias[h * a.K + (u - 2)] = s;
+    }
+}
+
 hipError_t launch_act_reduce(const ActReduceLaunch& a) {
     if (a.H <= 0) return hipSuccess;
-    hipLaunchKernelGGL(act_reduce_kernel, dim3((unsigned)a.H), dim3(256), 0, a.stream, a);
+    if (a.K > 0)
+        hipLaunchKernelGGL(act_reduce_pk_kernel, dim3((unsigned)a.H), dim3(256), 0, a.stream, a);
+    else
+        hipLaunchKernelGGL(act_reduce_kernel, dim3((unsigned)a.H), dim3(256), 0, a.stream, a);
     return hipGetLastError();
 }
 

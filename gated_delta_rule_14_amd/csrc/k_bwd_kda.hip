@@ -1,0 +1,671 @@
+// Backward pass, per-chunk gradients, with the per-key-channel gate (Kimi
+// Delta Attention): Steps 5-6 of "阅读笔记：DeltaNet 在 FLA 中的代码实现笔记"
+// (二、反向传播) and the gate, with every decay ratio inside the sum over the
+// key channel d ("DeltaNet 系列线性注意力变体的推导之旅", chunkwise KDA).
+//
+// Per chunk of n <= C tokens, with G[r][d] the inclusive cumulative log2 gate
+// of channel d, gamma = 2^G, rest = 2^{G_{C-1} - G}, T = (I + A)^{-1},
+// Kg = gamma * K, h the state entering the chunk, dH the gradient of the one
+// leaving it, dVn the gradient of V_new (from the reverse pass), and the
+// per-channel decayed product
+//     (M o_E X)[i][d] = sum_j M[i][j] X[j][d] 2^{G[i][d] - G[j][d]}:
+//   Pm  = scale (dO Vn^T), j <= i          dA = -T^T (dVn (beta V)^T + dW (beta Kg)^T) T^T, j < i
+//   dW  = -dVn h^T
+//   dQ  = scale gamma * (dO h^T) + Pm o_E K
+//   dK  = rest * (Vn dH^T) + gamma * beta * (T^T dW) + (Pm^T o_E Q) + beta * (dA o_E K)
+//         + (dA^T o_E (beta K))
+//   dV  = beta * (T^T dVn)
+//   dbeta_i = (T^T dVn)_i . v_i + (T^T dW)_i . Kg_i + k_i . (dA o_E K)_i
+//   dG  = Q * dQ_state + Q * Pq - K * Pk - Ks * dKs + Kg * dKg + beta K * Pa1 - K * Pa2
+//         (+ in the last row, per channel: gamma_C <h, dH>_row + sum_rows Ks * dKs)
+//   dg  = the reverse cumulative sum of dG over the chunk's rows, per channel
+// (the four o_E products named Pq, Pk, Pa1, Pa2 in that order).
+//
+// The o_E products split by 16-token blocks.  For an off-diagonal pair of
+// blocks (J < I) the decay factors through a token between them:
+//   row side (output row i in block I):  2^{G_i - G_e} (M_IJ (X_J 2^{G_e - G_J}))
+//     with e = 16J + 15, the last token of block J;
+//   column side (output row j in block J): 2^{G_s - G_j} (M_IJ^T (X_I 2^{G_I - G_s}))
+//     with s = 16I, the first token of block I.
+// Every exponent is <= 0, so the scaled operands (one copy each of K, Q and
+// beta K) are bf16 MFMA operands (v_mfma_f32_16x16x16_bf16, one 16-token
+// block per instruction) and nothing overflows.  Inside a diagonal block the
+// decay of each pair is taken exactly: the 16 tokens of a tile sit in the 16
+// lanes of a DPP row, token j = i - o reaches token i's lane by a row shift
+// of o, and the column-side terms go back by the opposite shift.
+//
+// One 512-thread workgroup (8 waves) per (chunk, head); everything in LDS
+// except the per-lane gates, h and dH, which load straight into registers.
+// A wave owns the C x K output tiles of key tile kt = wave % (K/16), in the
+// transposed MFMA orientation: lane l holds token 16 rt + l%16 and the 4
+// consecutive keys kc .. kc+3, so every per-element factor (gamma, rest, the
+// block decays) is a register, and per-token sums are in-lane plus two
+// shuffles.
+#include "gdn_device.hpp"
+#include "gdn_launch.hpp"
+
+namespace gdn {
+
+namespace {
+
+constexpr int KDA_THREADS = 512;
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// C(16x16) += A(16x16) B(16x16), bf16: lane l holds A[l%16][4(l/16) + e] and
+// B[4(l/16) + e][l%16]; the result layout is that of the 16x16x32 form.
+__device__ __forceinline__ f32x4 mma16(i16x4 a, i16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+// Operand of a k-major LDS tile X[k][m] (x at (k0, m0)): lane 16g+i receives
+// X[k0 + 4g + e][m0 + i] (one transposing ds_read_b64_tr_b16; lane j
+// addresses row 4g + j/4, columns 4(j%4) .. +3).
+__device__ __forceinline__ i16x4 frag16_t(const bf16* x, int ld, int lane) {
+    const int g = lane >> 4, j = lane & 15;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(x + (4 * g + (j >> 2)) * ld + 4 * (j & 3)));
+}
+// Operand of an m-major LDS tile (row l%16 at x + (l%16) ld, k contiguous):
+// lane l receives X[l%16][4(l/16) + e] (one 8-byte read).
+__device__ __forceinline__ i16x4 frag16(const bf16* x, int ld, int lane) {
+    return *reinterpret_cast<const i16x4*>(x + (lane & 15) * ld + 4 * (lane >> 4));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Offset O of a diagonal block: the lane of token i (gate gi, key ki, query
+// qi, beta bi of its 4 channels) pairs with token j = i - O of its tile.
+// Row side: Pq_i += Pm_ij E K_j, Pa1_i += dA_ij E K_j; column side, sent to
+// the lane of token j: Pk_j += Pm_ij E Q_i, Pa2_j += dA_ij beta_i E K_i, with
+// E = 2^{G_i - G_j} per channel.  Lanes with i < O read an upper-triangle
+// entry of Pm and dA (zero) and a clamped E, so they add nothing; row shifts
+// from outside the 16-lane row deliver zero.
+struct DiagPair {
+    f32x4 gi, ki, qi;
+    float bi;
+    const bf16* pmr;   // row i of Pm, at the block's first column
+    const bf16* dar;   // row i of dA, likewise
+    int tl;
+    f32x4 pq, pa1, pk, pa2;
+
+    template <int O>
+    __device__ __forceinline__ void step() {
+        f32x4 gj, kj;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (O == 0) {
+                gj[e] = gi[e];
+                kj[e] = ki[e];
+            } else {
+                gj[e] = dpp_mov<0x110 + O>(gi[e]);   // row_shr:O
+                kj[e] = dpp_mov<0x110 + O>(ki[e]);
+            }
+        }
+        const int jj = (tl - O) & 15;
+        const float m1 = Elem<bf16>::load(pmr + jj);
+        const float m2 = Elem<bf16>::load(dar + jj);
+        f32x4 t1, t2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float E = exp2_hw(fminf(gi[e] - gj[e], 0.f));
+            const float a1 = m1 * E, a2 = m2 * E;
+            pq[e] += a1 * kj[e];
+            pa1[e] += a2 * kj[e];
+            t1[e] = a1 * qi[e];
+            t2[e] = a2 * bi * ki[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (O == 0) {
+                pk[e] += t1[e];
+                pa2[e] += t2[e];
+            } else {
+                pk[e] += dpp_mov<0x100 + O>(t1[e]);   // row_shl:O
+                pa2[e] += dpp_mov<0x100 + O>(t2[e]);
+            }
+        }
+    }
+    // the accumulators are pinned after every offset: left alone, the
+    // compiler defers the column-side sums to the end and keeps every
+    // shifted term live until then
+    template <int O>
+    __device__ __forceinline__ void fenced() {
+        step<O>();
+        asm volatile("" : "+v"(pq), "+v"(pa1), "+v"(pk), "+v"(pa2));
+    }
+    __device__ __forceinline__ void run() {
+        fenced<0>(); fenced<1>(); fenced<2>(); fenced<3>(); fenced<4>(); fenced<5>(); fenced<6>(); fenced<7>();
+        fenced<8>(); fenced<9>(); fenced<10>(); fenced<11>(); fenced<12>(); fenced<13>(); fenced<14>(); fenced<15>();
+    }
+};
+
+template <int K, int V>
+struct KdaSmem {
+    static constexpr int C = 64, NW = KDA_THREADS / 64;
+    static constexpr int LDK = K + 8, LDV = V + 8, LDC = C + 8;
+    static constexpr int LDX = (K > V ? K : V) + 8;
+    static constexpr int LDD = K + 4;                              // fp32 dG rows
+    static constexpr size_t X = sizeof(bf16) * C * LDX;            // one reusable region
+    static constexpr size_t o_Q = 0;
+    static constexpr size_t o_K = o_Q + sizeof(bf16) * C * LDK;
+    static constexpr size_t o_R1 = o_K + sizeof(bf16) * C * LDK;   // V, then K scaled to block ends; dG over R1+R2
+    static constexpr size_t o_R2 = o_R1 + X;                       // dVn, then Q scaled from block starts
+    static constexpr size_t o_R3 = o_R2 + X;                       // dO, dW, beta K scaled; the scan's partials
+    static constexpr size_t o_R4 = o_R3 + X;                       // Vn, then Kg, then Y
+    static constexpr size_t o_T = o_R4 + X;
+    static constexpr size_t o_PM = o_T + sizeof(bf16) * C * LDC;
+    static constexpr size_t o_DA = o_PM + sizeof(bf16) * C * LDC;  // dAinv, then dA
+    static constexpr size_t o_GS = o_DA + sizeof(bf16) * C * LDC;  // [4][K] G at tokens 16I
+    static constexpr size_t o_GE = o_GS + 4 * 4 * K;               // [4][K] G at tokens 16J + 15
+    static constexpr size_t o_B = o_GE + 4 * 4 * K;                // [C] beta
+    static constexpr size_t o_RB = o_B + 4 * C;                    // [NW][C] dbeta partials
+    static constexpr size_t o_LAST = o_RB + 4 * NW * C;            // [2][K] sum_rows Ks * dKs
+    static constexpr size_t o_HD = o_LAST + 4 * 2 * K;             // [K] gamma_C <h, dH>_row
+    static constexpr size_t bytes = o_HD + 4 * K;
+    static_assert((size_t)C * LDD * 4 <= 2 * X, "dG fits R1 + R2");
+    static_assert(3 * (size_t)KDA_THREADS * 4 <= X, "the scan's partials fit R3");
+    static_assert(bytes <= 160 * 1024, "LDS");
+};
+
+template <int K, int V>
+__global__ __launch_bounds__(KDA_THREADS) void bwd_local_kda_kernel(BwdLocalLaunch a) {
+    typedef bf16 T;
+    typedef KdaSmem<K, V> L;
+    typedef Mma<T> M;
+    typedef typename M::frag Frag;
+    typedef FragOrder<T> F;
+    constexpr int C = 64, NW = L::NW, KS = M::KSTEP, EV = 8;
+    constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC, LDD = L::LDD;
+    constexpr int NKT = K / 16, NVT = V / 16;
+    constexpr int TPK = NKT * (C / 16) / NW, TPV = NVT * (C / 16) / NW;
+    constexpr int NS = V / KS, NG = V / F::KG, NGRP = NW / NKT;
+    static_assert(F::KG == KS, "one k-step per fragment group");
+    static_assert(TPK >= 1 && TPV >= 1 && NW % NKT == 0 && NW % NVT == 0 && NGRP <= 2, "tile split");
+    __shared__ __attribute__((aligned(16))) char smem[L::bytes];
+    T* sQ = reinterpret_cast<T*>(smem + L::o_Q);
+    T* sK = reinterpret_cast<T*>(smem + L::o_K);
+    T* sV = reinterpret_cast<T*>(smem + L::o_R1);
+    T* sKe = sV;
+    float* sDG = reinterpret_cast<float*>(smem + L::o_R1);
+    T* sDVN = reinterpret_cast<T*>(smem + L::o_R2);
+    T* sQl = sDVN;
+    T* sDO = reinterpret_cast<T*>(smem + L::o_R3);
+    T* sDW = sDO;
+    T* sKl = sDO;
+    float* sSP = reinterpret_cast<float*>(smem + L::o_R3);
+    T* sVN = reinterpret_cast<T*>(smem + L::o_R4);
+    T* sKg = sVN;
+    T* sY = sVN;
+    T* sT = reinterpret_cast<T*>(smem + L::o_T);
+    T* sPM = reinterpret_cast<T*>(smem + L::o_PM);
+    T* sDA = reinterpret_cast<T*>(smem + L::o_DA);
+    float* sGS = reinterpret_cast<float*>(smem + L::o_GS);
+    float* sGE = reinterpret_cast<float*>(smem + L::o_GE);
+    float* sB = reinterpret_cast<float*>(smem + L::o_B);
+    float* sRB = reinterpret_cast<float*>(smem + L::o_RB);
+    float* sLast = reinterpret_cast<float*>(smem + L::o_LAST);
+    float* sHD = reinterpret_cast<float*>(smem + L::o_HD);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int64_t H = a.H, Hq = a.Hq > 0 ? a.Hq : a.H;
+    const int64_t c = blockIdx.x / H, h = blockIdx.x - c * H, hq = h / (H / Hq);
+    int64_t t0;
+    int n;
+    if (a.map.table) {
+        const int4 e = a.map.table[c];
+        t0 = e.x;
+        n = e.y;
+    } else {
+        const int64_t b = c / a.map.nt, j = c - b * a.map.nt;
+        t0 = b * a.map.T + j * C;
+        n = (int)min((int64_t)C, a.map.T - j * C);
+    }
+    if (n <= 0) return;   // an unused chunk slot (uniform over the workgroup)
+    const int64_t blk = h * a.map.max_chunks + c;
+    const float* gc = a.gcum + blk * C * K;
+
+    const int kt = wave % NKT, tl = lane & 15, kc = 16 * kt + 4 * (lane >> 4);
+    int rtk[TPK];
+#pragma unroll
+    for (int j = 0; j < TPK; ++j) rtk[j] = wave / NKT + NGRP * j;
+
+    // ---- loads.  The gates of this lane's elements and the h, dH rows of
+    // key tile kt go to registers; the rest to LDS (rows >= n as zero; the
+    // gate rows there repeat G_{n-1}, as the intra stage leaves them).
+    f32x4 gq[TPK];
+#pragma unroll
+    for (int j = 0; j < TPK; ++j) gq[j] = *reinterpret_cast<const f32x4*>(gc + (16 * rtk[j] + tl) * K + kc);
+    u32x4 hg[NG], dg[NG];
+    {
+        const u32x4* hsrc = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.hs) + blk * K * V);
+        const u32x4* dsrc = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dhs) + blk * K * V);
+#pragma unroll
+        for (int sg = 0; sg < NG; ++sg) {
+            hg[sg] = hsrc[(kt * NG + sg) * 64 + lane];
+            dg[sg] = dsrc[(kt * NG + sg) * 64 + lane];
+        }
+    }
+    {
+        constexpr int NKQ = C * K / EV / KDA_THREADS, NVV = C * V / EV / KDA_THREADS;
+        constexpr int NGW = (C / 16) * NG / NW;
+        static_assert(NKQ * EV * KDA_THREADS == C * K && NVV * EV * KDA_THREADS == C * V &&
+                          NGW * NW == (C / 16) * NG,
+                      "whole pieces");
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const T* q = static_cast<const T*>(a.q);
+        const T* k = static_cast<const T*>(a.k);
+        const T* v = static_cast<const T*>(a.v);
+        const T* dout = static_cast<const T*>(a.dout);
+        u32x4 xq[NKQ], xk[NKQ], xv[NVV], xo[NVV], xn[NGW], xd[NGW], xt;
+#pragma unroll
+        for (int p = 0; p < NKQ; ++p) {
+            const int i = tid + KDA_THREADS * p, r = i / (K / EV), cv = (i % (K / EV)) * EV;
+            const int64_t g = ((t0 + r) * Hq + hq) * K + cv;
+            xq[p] = r < n ? *reinterpret_cast<const u32x4*>(q + g) : z;
+            xk[p] = r < n ? *reinterpret_cast<const u32x4*>(k + g) : z;
+        }
+#pragma unroll
+        for (int p = 0; p < NVV; ++p) {
+            const int i = tid + KDA_THREADS * p, r = i / (V / EV), cv = (i % (V / EV)) * EV;
+            const int64_t g = ((t0 + r) * H + h) * V + cv;
+            xv[p] = r < n ? *reinterpret_cast<const u32x4*>(v + g) : z;
+            xo[p] = r < n ? *reinterpret_cast<const u32x4*>(dout + g) : z;
+        }
+        const u32x4* vn = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.vn) + blk * C * V);
+        const u32x4* dvn = reinterpret_cast<const u32x4*>(static_cast<const T*>(a.dvn) + blk * C * V);
+#pragma unroll
+        for (int p = 0; p < NGW; ++p) {
+            const int gi = wave + NW * p, r = 16 * (gi / NG) + tl;
+            xn[p] = r < n ? vn[gi * 64 + lane] : z;
+            xd[p] = r < n ? dvn[gi * 64 + lane] : z;
+        }
+        static_assert(C * C == KDA_THREADS * EV, "one 16-byte piece of T per thread");
+        xt = *reinterpret_cast<const u32x4*>(static_cast<const T*>(a.ainv) + blk * C * C + tid * EV);
+        for (int i = tid; i < 8 * K; i += KDA_THREADS) {
+            const int set = i / (4 * K), I = (i / K) % 4, d = i % K;
+            (set ? sGE : sGS)[I * K + d] = gc[(16 * I + (set ? 15 : 0)) * K + d];
+        }
+        if (tid < C) {
+            float bv = a.beta[(t0 + min(tid, n - 1)) * H + h];
+            if (a.act.flags & ACT_BETA_SIGMOID) bv = act_beta(bv, a.act.flags & ACT_BETA_NEG_EIG);
+            sB[tid] = tid < n ? bv : 0.f;
+        }
+        for (int i = tid; i < NW * C; i += KDA_THREADS) sRB[i] = 0.f;
+        const bool l2 = a.act.flags & ACT_QK_L2NORM;   // a row is K / EV consecutive lanes
+#pragma unroll
+        for (int p = 0; p < NKQ; ++p) {
+            const int i = tid + KDA_THREADS * p, r = i / (K / EV), cv = (i % (K / EV)) * EV;
+            *reinterpret_cast<u32x4*>(sQ + r * LDK + cv) = l2 ? l2norm_piece<T, K / EV>(xq[p]) : xq[p];
+            *reinterpret_cast<u32x4*>(sK + r * LDK + cv) = l2 ? l2norm_piece<T, K / EV>(xk[p]) : xk[p];
+        }
+#pragma unroll
+        for (int p = 0; p < NVV; ++p) {
+            const int i = tid + KDA_THREADS * p, r = i / (V / EV), cv = (i % (V / EV)) * EV;
+            *reinterpret_cast<u32x4*>(sV + r * LDV + cv) = xv[p];
+            *reinterpret_cast<u32x4*>(sDO + r * LDV + cv) = xo[p];
+        }
+#pragma unroll
+        for (int p = 0; p < NGW; ++p) {   // fragment-order groups to row-major LDS
+            const int gi = wave + NW * p, r = 16 * (gi / NG) + tl, c0 = F::KG * (gi % NG);
+            *reinterpret_cast<u32x4*>(sVN + r * LDV + c0 + F::col(lane, 0)) = xn[p];
+            *reinterpret_cast<u32x4*>(sDVN + r * LDV + c0 + F::col(lane, 0)) = xd[p];
+        }
+        *reinterpret_cast<u32x4*>(sT + (tid / (C / EV)) * LDC + (tid % (C / EV)) * EV) = xt;
+    }
+    lds_barrier();
+
+    float* myRB = sRB + wave * C;
+    // this lane's partial of token r0 + l%16 (transposed tile): summed over
+    // the 4 lanes of that token, added by lanes 0..15
+    auto add_tok = [&](float* dst, int r0, float x) {
+        x = sum_groups(x);
+        if (lane < 16) dst[r0 + lane] += x;
+    };
+    auto quad = [&](const T* p) { return Quad<T>::get(Quad<T>::load(p)); };
+
+    // ================= phase A: the products with h and dH, and Pm
+    const f32x4 gend = *reinterpret_cast<const f32x4*>(sGE + 3 * K + kc);
+    f32x4 dq[TPK], dk[TPK], dw[TPK], dG[TPK], gam[TPK];
+    {
+        f32x4 dks[TPK];
+#pragma unroll
+        for (int j = 0; j < TPK; ++j) dq[j] = dks[j] = dw[j] = zero4();
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const Frag bh = F::frag(hg[s], 0), bd = F::frag(dg[s], 0);
+#pragma unroll
+            for (int j = 0; j < TPK; ++j) {
+                const int r = 16 * rtk[j] + tl;
+                dq[j] = M::mma(bh, M::load(sDO + r * LDV + s * KS, lane), dq[j]);
+                dks[j] = M::mma(bd, M::load(sVN + r * LDV + s * KS, lane), dks[j]);
+                dw[j] = M::mma(bh, M::load(sDVN + r * LDV + s * KS, lane), dw[j]);
+            }
+        }
+        // gamma_C <h, dH> of each key row (h and dH rows of key tile kt: lane
+        // l holds row l%16), by the waves of the first token group
+        if (wave < NKT) {
+            float hd = 0.f;
+#pragma unroll
+            for (int sg = 0; sg < NG; ++sg)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    hd += __uint_as_float(hg[sg][e] << 16) * __uint_as_float(dg[sg][e] << 16) +
+                          __uint_as_float(hg[sg][e] & 0xffff0000u) * __uint_as_float(dg[sg][e] & 0xffff0000u);
+            hd = sum_groups(hd);
+            if (lane < 16) sHD[16 * kt + lane] = hd * exp2_hw(sGE[3 * K + 16 * kt + lane]);
+        }
+        // dQ's state term, dK's Ks term and their gate terms
+        f32x4 lastp = zero4();
+#pragma unroll
+        for (int j = 0; j < TPK; ++j) {
+            const int r = 16 * rtk[j] + tl;
+            const f32x4 qv = quad(sQ + r * LDK + kc), kv = quad(sK + r * LDK + kc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                gam[j][e] = exp2_hw(gq[j][e]);
+                const float ks = exp2_hw(fminf(gend[e] - gq[j][e], 0.f)) * dks[j][e];
+                dq[j][e] *= a.scale * gam[j][e];
+                dG[j][e] = qv[e] * dq[j][e] - kv[e] * ks;
+                lastp[e] += kv[e] * ks;
+                dk[j][e] = ks;
+            }
+        }
+        lastp = row_sum16(lastp);   // over the tokens of the wave's tiles
+        if ((lane & 15) == 15) *reinterpret_cast<f32x4*>(sLast + (wave / NKT) * K + kc) = lastp;
+    }
+    // Pm = scale (dO Vn^T), j <= i: the lower tiles of the wave's pair
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int id = 2 * wave + u, I = id / 4, J = id % 4;
+        if (J > I) continue;   // upper tiles are never read
+        const f32x4 x = mma_tile<T>(sDO + 16 * I * LDV, LDV, sVN + 16 * J * LDV, LDV, V, lane, zero4());
+        const int jc = 16 * J + acc_col(lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * I + acc_row(lane, e);
+            Elem<T>::store(sPM + i * LDC + jc, jc <= i ? a.scale * x[e] : 0.f);
+        }
+    }
+    lds_barrier();   // dO and Vn are read: their regions take dW and Kg
+#pragma unroll
+    for (int j = 0; j < TPK; ++j) {
+        const int r = 16 * rtk[j] + tl;
+        const f32x4 kv = quad(sK + r * LDK + kc);
+        store4(sDW + r * LDK + kc, -dw[j]);
+        store4(sKg + r * LDK + kc, gam[j] * kv);
+    }
+    lds_barrier();
+
+    // ================= phase B: T^T dW, dV, dAinv
+    {
+        f32x4 atdw[TPK];
+#pragma unroll
+        for (int j = 0; j < TPK; ++j) atdw[j] = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += KS) {
+            const Frag bw = M::load_t(sDW + k0 * LDK + 16 * kt, LDK, lane);
+#pragma unroll
+            for (int j = 0; j < TPK; ++j)
+                atdw[j] = M::mma(bw, M::load_t(sT + k0 * LDC + 16 * rtk[j], LDC, lane), atdw[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < TPK; ++j) {
+            const int r = 16 * rtk[j] + tl;
+            const float bt = sB[r];
+            const f32x4 kv = quad(sK + r * LDK + kc);
+            float kx = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float kg = gam[j][e] * kv[e];
+                dk[j][e] += gam[j][e] * bt * atdw[j][e];
+                dG[j][e] += kg * bt * atdw[j][e];
+                kx += kg * atdw[j][e];
+            }
+            add_tok(myRB, 16 * rtk[j], kx);
+        }
+    }
+    {   // dV = beta T^T dVn (transposed tiles), and its dbeta term
+        const int vt = wave % NVT, vc = 16 * vt + 4 * (lane >> 4);
+        T* gdv = static_cast<T*>(a.dv);
+#pragma unroll
+        for (int j = 0; j < TPV; ++j) {
+            const int r0 = 16 * (wave / NVT + (NW / NVT) * j), r = r0 + tl;
+            f32x4 x = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < C; k0 += KS)
+                x = M::mma(M::load_t(sDVN + k0 * LDV + 16 * vt, LDV, lane),
+                           M::load_t(sT + k0 * LDC + r0, LDC, lane), x);
+            const f32x4 vv = quad(sV + r * LDV + vc);
+            add_tok(myRB, r0, x[0] * vv[0] + x[1] * vv[1] + x[2] * vv[2] + x[3] * vv[3]);
+            if (r < n) store4(gdv + ((t0 + r) * H + h) * V + vc, sB[r] * x);
+        }
+    }
+    // dAinv = (dVn V^T + dW Kg^T) diag(beta)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int id = 2 * wave + u, I = id / 4, J = id % 4;
+        const f32x4 x1 = mma_tile<T>(sDVN + 16 * I * LDV, LDV, sV + 16 * J * LDV, LDV, V, lane, zero4());
+        const f32x4 x2 = mma_tile<T>(sDW + 16 * I * LDK, LDK, sKg + 16 * J * LDK, LDK, K, lane, x1);
+        const int jc = 16 * J + acc_col(lane);
+        const float bj = sB[jc];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Elem<T>::store(sDA + (16 * I + acc_row(lane, e)) * LDC + jc, bj * x2[e]);
+    }
+    lds_barrier();   // V, dVn, dW and Kg are read
+
+    // ================= phase C: Y = dAinv T^T; the block-scaled operands
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int id = 2 * wave + u, I = id / 4, J = id % 4;
+        const f32x4 y = mma_tile<T>(sDA + 16 * I * LDC, LDC, sT + 16 * J * LDC, LDC, C, lane, zero4());
+        store_acc(sY + 16 * I * LDC + 16 * J, LDC, lane, y);
+    }
+    // Ke = K 2^{G_e - G} (e the last token of the row's block), Ql = Q 2^{G - G_s},
+    // Kl = beta K 2^{G - G_s} (s the first token of the row's block)
+#pragma unroll
+    for (int j = 0; j < TPK; ++j) {
+        const int rt = rtk[j], r = 16 * rt + tl;
+        const f32x4 kv = quad(sK + r * LDK + kc), qv = quad(sQ + r * LDK + kc);
+        const f32x4 ge = *reinterpret_cast<const f32x4*>(sGE + rt * K + kc);
+        const f32x4 gs = *reinterpret_cast<const f32x4*>(sGS + rt * K + kc);
+        const float bt = sB[r];
+        f32x4 ke, ql, kl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float fs = exp2_hw(fminf(gq[j][e] - gs[e], 0.f));
+            ke[e] = kv[e] * exp2_hw(fminf(ge[e] - gq[j][e], 0.f));
+            ql[e] = qv[e] * fs;
+            kl[e] = bt * kv[e] * fs;
+        }
+        store4(sKe + r * LDK + kc, ke);
+        store4(sQl + r * LDK + kc, ql);
+        store4(sKl + r * LDK + kc, kl);
+    }
+    lds_barrier();
+
+    // ================= phase D: dA = -T^T Y, strictly lower
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int id = 2 * wave + u, I = id / 4, J = id % 4;
+        if (J > I) continue;   // upper tiles are never read
+        f32x4 x = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += KS)
+            x = M::mma(M::load_t(sT + k0 * LDC + 16 * I, LDC, lane),
+                       M::load_t(sY + k0 * LDC + 16 * J, LDC, lane), x);
+        const int jc = 16 * J + acc_col(lane);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * I + acc_row(lane, e);
+            Elem<T>::store(sDA + i * LDC + jc, jc < i ? -x[e] : 0.f);
+        }
+    }
+    lds_barrier();
+
+    // ================= phase E: the four o_E products; dQ, dK stores
+    T* gdq = static_cast<T*>(a.dq);
+    T* gdk = static_cast<T*>(a.dk);
+#pragma unroll
+    for (int j = 0; j < TPK; ++j) {
+        const int I = rtk[j], r = 16 * I + tl;
+        DiagPair dp;
+        dp.pq = dp.pa1 = dp.pk = dp.pa2 = zero4();
+        for (int J = 0; J < I; ++J) {   // row side
+            const i16x4 ak = frag16_t(sKe + 16 * J * LDK + 16 * kt, LDK, lane);
+            const f32x4 t1 = mma16(ak, frag16(sPM + 16 * I * LDC + 16 * J, LDC, lane), zero4());
+            const f32x4 t2 = mma16(ak, frag16(sDA + 16 * I * LDC + 16 * J, LDC, lane), zero4());
+            const f32x4 ge = *reinterpret_cast<const f32x4*>(sGE + J * K + kc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float f = exp2_hw(fminf(gq[j][e] - ge[e], 0.f));
+                dp.pq[e] += f * t1[e];
+                dp.pa1[e] += f * t2[e];
+            }
+        }
+        for (int I2 = I + 1; I2 < C / 16; ++I2) {   // column side
+            const i16x4 aq = frag16_t(sQl + 16 * I2 * LDK + 16 * kt, LDK, lane);
+            const i16x4 al = frag16_t(sKl + 16 * I2 * LDK + 16 * kt, LDK, lane);
+            const f32x4 t1 = mma16(aq, frag16_t(sPM + 16 * I2 * LDC + 16 * I, LDC, lane), zero4());
+            const f32x4 t2 = mma16(al, frag16_t(sDA + 16 * I2 * LDC + 16 * I, LDC, lane), zero4());
+            const f32x4 gs = *reinterpret_cast<const f32x4*>(sGS + I2 * K + kc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float f = exp2_hw(fminf(gs[e] - gq[j][e], 0.f));
+                dp.pk[e] += f * t1[e];
+                dp.pa2[e] += f * t2[e];
+            }
+        }
+        // the diagonal block
+        dp.gi = gq[j];
+        dp.ki = quad(sK + r * LDK + kc);
+        dp.qi = quad(sQ + r * LDK + kc);
+        dp.bi = sB[r];
+        dp.pmr = sPM + r * LDC + 16 * I;
+        dp.dar = sDA + r * LDC + 16 * I;
+        dp.tl = tl;
+        dp.run();
+        // assemble
+        float kx = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float kv = dp.ki[e];
+            dq[j][e] += dp.pq[e];
+            dk[j][e] += dp.pk[e] + dp.bi * dp.pa1[e] + dp.pa2[e];
+            dG[j][e] += dp.qi[e] * dp.pq[e] - kv * dp.pk[e] + dp.bi * kv * dp.pa1[e] - kv * dp.pa2[e];
+            kx += kv * dp.pa1[e];
+        }
+        add_tok(myRB, 16 * I, kx);
+        if (r < n) {
+            if (a.dq_part) {
+                *reinterpret_cast<f32x4*>(a.dq_part + ((t0 + r) * H + h) * K + kc) = dq[j];
+                *reinterpret_cast<f32x4*>(a.dk_part + ((t0 + r) * H + h) * K + kc) = dk[j];
+            } else {
+                store4(gdq + ((t0 + r) * H + h) * K + kc, dq[j]);
+                store4(gdk + ((t0 + r) * H + h) * K + kc, dk[j]);
+            }
+        }
+    }
+    lds_barrier();   // the scaled operands are read: dG takes their regions
+#pragma unroll
+    for (int j = 0; j < TPK; ++j)
+        *reinterpret_cast<f32x4*>(sDG + (16 * rtk[j] + tl) * LDD + kc) = dG[j];
+    lds_barrier();
+
+    // dbeta (with the sigmoid's chain rule when beta holds logits)
+    if (wave == 0) {
+        float db = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) db += sRB[w * C + lane];
+        if (a.act.flags & ACT_BETA_SIGMOID) {
+            const float braw = a.beta[(t0 + min(lane, n - 1)) * H + h];
+            const float m = (a.act.flags & ACT_BETA_NEG_EIG) ? 2.f : 1.f;
+            db *= m / ((1.f + expf(-braw)) * (1.f + expf(braw)));
+        }
+        if (lane < n) a.dbeta[(t0 + lane) * H + h] = db;
+    }
+    // dg: the reverse cumulative sum of dG per channel (the last row's state
+    // terms entering at the end).  Thread (quarter qq, channel d) walks rows
+    // qq*RPT .. (qq+1)*RPT-1 after adding the totals of the quarters after it.
+    {
+        constexpr int TPC = KDA_THREADS / K, RPT = C / TPC;
+        static_assert(TPC * RPT == C, "whole row ranges");
+        const int d = tid % K, qq = tid / K;
+        float* sP = sSP;                      // [TPC][K]
+        float* sPL = sSP + KDA_THREADS;       // [TPC][K]
+        float* sPD = sSP + 2 * KDA_THREADS;   // [TPC][K]
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) part += sDG[(qq * RPT + i) * LDD + d];
+        sP[qq * K + d] = part;
+        lds_barrier();
+        float suf = sHD[d];
+#pragma unroll
+        for (int g = 0; g < NGRP; ++g) suf += sLast[g * K + d];
+        for (int q2 = TPC - 1; q2 > qq; --q2) suf += sP[q2 * K + d];
+        const bool act_gate = a.act.flags & ACT_GATE;
+        const float el = act_gate ? expf(a.act.A_log[h]) : 0.f;
+        const float dtb = act_gate ? a.act.dt_bias[h * K + d] : 0.f;
+        float pl = 0.f, pd = 0.f;
+        for (int i = RPT - 1; i >= 0; --i) {
+            const int rr = qq * RPT + i;
+            suf += sDG[rr * LDD + d];
+            if (rr < n) {
+                float out = suf;
+                if (act_gate) {
+                    // log alpha = -e^{A_log} softplus(x), x = a + dt_bias:
+                    // d/da = -e^{A_log} sigmoid(x), d/dA_log = log alpha
+                    const float xa = a.g[((t0 + rr) * H + h) * K + d] + dtb;
+                    out = -suf * el / (1.f + expf(-xa));
+                    pl -= suf * el * softplus_f(xa);
+                    pd += out;
+                }
+                a.dg[((t0 + rr) * H + h) * K + d] = out;
+            }
+        }
+        if (act_gate) {   // this chunk's dA_log and ddt_bias terms, in a fixed order
+            sPL[qq * K + d] = pl;
+            sPD[qq * K + d] = pd;
+            lds_barrier();
+            float* ap = a.act_part + blk * (K + 2);
+            if (tid < K) {
+                float l = 0.f, s = 0.f;
+                for (int q2 = 0; q2 < TPC; ++q2) {
+                    l += sPL[q2 * K + tid];
+                    s += sPD[q2 * K + tid];
+                }
+                ap[2 + tid] = s;
+                sPL[tid] = l;   // only this thread reads or writes column tid here
+            }
+            lds_barrier();
+            if (tid == 0) {
+                float l = 0.f;
+                for (int i = 0; i < K; ++i) l += sPL[i];
+                ap[0] = l;
+            }
+        }
+    }
+}
+
+template <int K, int V>
+hipError_t launch_kda_kv(const BwdLocalLaunch& a) {
+    const int64_t items = a.map.max_chunks * a.H;
+    if (items <= 0) return hipSuccess;
+    hipLaunchKernelGGL((bwd_local_kda_kernel<K, V>), dim3((unsigned)items), dim3(KDA_THREADS), 0,
+                       a.stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_local_kda(const BwdLocalLaunch& a) {
+    if (a.C != 64 || !a.bf16) return hipErrorInvalidValue;
+    if (a.K == 64 && a.V == 64) return launch_kda_kv<64, 64>(a);
+    if (a.K == 64 && a.V == 128) return launch_kda_kv<64, 128>(a);
+    if (a.K == 128 && a.V == 64) return launch_kda_kv<128, 64>(a);
+    if (a.K == 128 && a.V == 128) return launch_kda_kv<128, 128>(a);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace gdn

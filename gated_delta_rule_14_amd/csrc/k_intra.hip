@@ -73,7 +73,6 @@ struct IntraSmem {
 
 template <typename T, int K, int V, int C, bool PK, bool STORE_AINV, bool BWD = false>
 __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
-    static_assert(!(BWD && PK), "the backward mode is for the scalar gate");
     typedef IntraSmem<T, K, V, C, PK> L;
     typedef Mma<T> M;
     constexpr int NT = INTRA_THREADS, NW = NT / 64;
@@ -301,10 +300,12 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
             }
         }
         // the state pass needs only the chunk's last row of the per-key
-        // cumulative gate (the decay of the carried state); the scalar gate's
-        // whole column also serves the backward
+        // cumulative gate (the decay of the carried state); the backward
+        // takes the whole gate, of either kind
         float* gg = a.ws.gcum + blk * C * (PK ? K : 1);
-        if (PK) {
+        if (PK && BWD) {
+            for (int i = tid; i < C * K; i += NT) gg[i] = sG[(i / K) * LDG + i % K];
+        } else if (PK) {
             for (int i = tid; i < K; i += NT) gg[(C - 1) * K + i] = sG[(C - 1) * LDG + i];
         } else {
             for (int i = tid; i < C; i += NT) gg[i] = sG[i];
@@ -435,12 +436,19 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                         const int i = 16 * I + acc_row(lane, e), j = 16 * J + acc_col(lane);
                         sA[i * LDA + j] = sB[i] * acc[e];
                     }
-                } else {
+                } else if (!BWD) {
                     // Aqk^T tile: rows j (block J), columns i (block I)
                     f32x4 acc = mma_tile<T>(sS + (32 + 16 * J) * LDK, LDK, sS + 16 * LDK, LDK, K,
                                             lane, zero4());
                     acc *= a.scale;
                     store4_frag(gaqk, 16 * I + acc_col(lane), 16 * J + 4 * (lane >> 4), C, acc);
+                } else {
+                    // backward mode: the Aqk tile (rows i, columns j), stored
+                    // as 4 consecutive columns of Aqk^T
+                    f32x4 acc = mma_tile<T>(sS + 16 * LDK, LDK, sS + (32 + 16 * J) * LDK, LDK, K,
+                                            lane, zero4());
+                    acc *= a.scale;
+                    store4_frag(gaqk, 16 * J + acc_col(lane), 16 * I + 4 * (lane >> 4), C, acc);
                 }
             }
         }
@@ -486,7 +494,7 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                         sA[i * LDA + j] = sB[i] * acc[e];
                     }
                 }
-            } else {
+            } else if (!BWD) {
                 // Aqk^T: rows the earlier K (j), columns the later Q (i)
                 f32x4 acc = mma_tile<T>(sS + (C + 16 * P) * LDK, LDK, sS + (C / 2 + 16 * P) * LDK, LDK,
                                         K, lane, zero4());
@@ -496,12 +504,25 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                     acc *= a.scale;
                     store4_frag(gaqk, 16 * Ib + 8 + (cc & 7), 16 * Ib + 4 * (g4 & 1), C, acc);
                 }
+            } else {
+                // backward mode, Aqk: rows the later Q (i), columns the
+                // earlier K (j); 4 consecutive columns of Aqk^T per lane
+                f32x4 acc = mma_tile<T>(sS + (C / 2 + 16 * P) * LDK, LDK, sS + (C + 16 * P) * LDK, LDK,
+                                        K, lane, zero4());
+                const int cc = acc_col(lane);
+                if (g4 / 2 == cc / 8) {
+                    const int Ib = 2 * P + cc / 8;
+                    acc *= a.scale;
+                    store4_frag(gaqk, 16 * Ib + (cc & 7), 16 * Ib + 8 + 4 * (g4 & 1), C, acc);
+                }
             }
         }
-        // upper blocks of Aqk: zeros (those of A are masked when Ainv is read)
+        // upper blocks of Aqk (lower blocks of Aqk^T in the backward mode):
+        // zeros (those of A are masked when Ainv is read)
         for (int i = tid; i < C * C; i += NT) {
             const int r = i / C, j = i - r * C;
-            if (j / 16 > r / 16) Elem<T>::store(gaqk + FragOrder<T>::off(r, j, C), 0.f);
+            if (BWD ? j / 16 < r / 16 : j / 16 > r / 16)
+                Elem<T>::store(gaqk + FragOrder<T>::off(r, j, C), 0.f);
         }
         // the two 8x8 triangles of each diagonal block, pair by pair: thread
         // = (block, row i, a contiguous slice of CH channels); row i's keys,
@@ -582,12 +603,14 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                 aqk = sum8(aqk);
                 if (s == SL - 1) {
                     sA[i * LDA + j] = j < i ? sB[i] * akk : 0.f;
-                    Elem<T>::store(gaqk + FragOrder<T>::off(i, j, C), j <= i ? a.scale * aqk : 0.f);
+                    Elem<T>::store(gaqk + (BWD ? FragOrder<T>::off(j, i, C) : FragOrder<T>::off(i, j, C)),
+                                   j <= i ? a.scale * aqk : 0.f);
                 }
             }
             // rows of the upper half's columns that the lower half never reached
             if (half == 0 && s == SL - 1)
-                for (int j = jend; j < 16 * I + 16; ++j) Elem<T>::store(gaqk + FragOrder<T>::off(i, j, C), 0.f);
+                for (int j = jend; j < 16 * I + 16; ++j)
+                    Elem<T>::store(gaqk + (BWD ? FragOrder<T>::off(j, i, C) : FragOrder<T>::off(i, j, C)), 0.f);
         }
     }
     __syncthreads();
@@ -763,13 +786,10 @@ template <typename T, int K, int V, int C, bool PK>
 static hipError_t launch_intra_t(const IntraLaunch& a) {
     dim3 grid((unsigned)(a.map.max_chunks * a.H));
     if (a.bwd) {
-        if constexpr (!PK) {
-            if (!a.ws.ainv || !a.ws.ksr || !a.ws.wt) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((intra_kernel<T, K, V, C, false, true, true>), grid,
-                               dim3(INTRA_THREADS), 0, a.stream, a);
-            return hipGetLastError();
-        }
-        return hipErrorInvalidValue;
+        if (!a.ws.ainv || !a.ws.ksr || !a.ws.wt) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((intra_kernel<T, K, V, C, PK, true, true>), grid, dim3(INTRA_THREADS), 0,
+                           a.stream, a);
+        return hipGetLastError();
     }
     if (a.ws.ainv)
         hipLaunchKernelGGL((intra_kernel<T, K, V, C, PK, true>), grid, dim3(INTRA_THREADS), 0,

@@ -279,26 +279,34 @@ def chunked_backward(q, k, v, beta, g, scale, do, h0=None, dht=None, cu_seqlens=
 
 
 def activation_backward(a, b, A_log, dt_bias, dg, dbeta, neg_eig=False):
-    """Chain rule through the input activation (scalar gate), fp64.
+    """Chain rule through the input activation, fp64.
 
-    a, b [B, T, H]: the raw gate and beta logits; A_log, dt_bias [H]; dg,
-    dbeta [B, T, H]: the gradients with respect to log alpha and beta (as
+    a, b [B, T, H]: the raw gate and beta logits (a [B, T, H, K] for the
+    per-key gate); A_log [H]; dt_bias [H] ([H, K] per-key); dg (the shape of
+    a), dbeta [B, T, H]: the gradients with respect to log alpha and beta (as
     the backward produces them).  With log alpha = -e^{A_log} softplus(a +
     dt_bias) and beta = sigmoid(b) (2 sigmoid(b) with neg_eig)
-    ("Gated Delta Network（GDN）" §3.1 eq. 5, §5):
+    ("Gated Delta Network（GDN）" §3.1 eq. 5, §5; per channel for the
+    per-key gate):
       d/da       = dg * (-e^{A_log} sigmoid(a + dt_bias))   (softplus' = sigmoid)
       d/db       = dbeta * s (1 - s) (times 2 with neg_eig),  s = sigmoid(b)
-      d/dA_log   = sum over tokens of dg * log alpha        (d log alpha / d A_log = log alpha)
+      d/dA_log   = sum over tokens (and channels) of dg * log alpha
+                   (d log alpha / d A_log = log alpha)
       d/ddt_bias = sum over tokens of d/da
-    Returns (da, db, dA_log [H], ddt_bias [H])."""
+    Returns (da, db, dA_log [H], ddt_bias (the shape of dt_bias))."""
     from .activation import log_gate, sigmoid
     a, b, A_log, dt_bias, dg, dbeta = (as_f64(x) for x in (a, b, A_log, dt_bias, dg, dbeta))
-    da = dg * (-np.exp(A_log) * sigmoid(a + dt_bias))
+    per_key = dt_bias.ndim == 2
+    el = np.exp(A_log)[:, None] if per_key else np.exp(A_log)
+    da = dg * (-el * sigmoid(a + dt_bias))
     s = sigmoid(b)
     db = dbeta * s * (1.0 - s) * (2.0 if neg_eig else 1.0)
     lg = log_gate(a, A_log, dt_bias)
-    dA_log = np.sum(dg * lg, axis=tuple(range(dg.ndim - 1)))
-    ddt_bias = np.sum(da, axis=tuple(range(da.ndim - 1)))
+    tok = tuple(range(dg.ndim - (2 if per_key else 1)))
+    dA_log = np.sum(dg * lg, axis=tok)
+    if per_key:
+        dA_log = np.sum(dA_log, axis=-1)
+    ddt_bias = np.sum(da, axis=tok)
     return da, db, dA_log, ddt_bias
 
 

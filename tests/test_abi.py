@@ -161,7 +161,10 @@ def test_chunk_bwd_rejects_before_launch(lib):
     n = ctypes.c_size_t()
     ws = lambda d: lib.gdn_chunk_bwd_workspace(ctypes.byref(d), ctypes.byref(n))  # noqa: E731
     assert ws(_desc()) == 0 and n.value > 0
-    assert ws(_desc(gate=1)) == 4                       # scalar gate only
+    base = n.value
+    assert ws(_desc(gate=1)) == 0                       # the per-key gate, bf16
+    assert n.value > base                               # (its gate is per channel)
+    assert ws(_desc(gate=1, qkv_dtype=0, key_dim=64, value_dim=64)) == 4   # ... bf16 only
     assert ws(_desc(num_v_heads=4)) == 0                # H_V == H
     base = n.value
     assert ws(_desc(num_v_heads=8)) == 0                # grouped value heads
@@ -189,7 +192,7 @@ def test_chunk_bwd_rejects_before_launch(lib):
     assert bwd(dht=ctypes.c_void_p((1 << 20) + 2)) == 6
     assert bwd(ws=ctypes.c_void_p((1 << 20) + 64)) == 6
     assert bwd(wsb=1024) == 5
-    assert bwd(desc=_desc(gate=1)) == 4
+    assert bwd(desc=_desc(gate=1, qkv_dtype=0, key_dim=64, value_dim=64)) == 4   # per-key: bf16
     assert bwd(desc=_desc(batch=1), cu=FAKE) == 2
     assert lib.gdn_last_error().decode() != ""
 
@@ -211,7 +214,7 @@ def test_chunk_bwd_act_rejects_before_launch(lib):
     assert bwd(1, dA_log=None) == 1              # ... and the dA_log, ddt_bias outputs
     assert bwd(1 | 2, ddt_bias=None) == 1
     assert bwd(1, dA_log=odd) == 6
-    assert bwd(1, desc=_desc(gate=1)) == 4       # scalar gate only
+    assert bwd(1, desc=_desc(gate=1, qkv_dtype=0, key_dim=64, value_dim=64)) == 4   # per-key: bf16
     assert lib.gdn_last_error().decode() != ""
 
 

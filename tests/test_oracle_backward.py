@@ -206,18 +206,22 @@ def test_chunked_backward_mutations_fail(drop, monkeypatch):
     assert max(_rel(got[n], ref[n]) for n in NAMES) > 1e-4
 
 
+@pytest.mark.parametrize("per_key", [False, True], ids=["gdn", "kda"])
 @pytest.mark.parametrize("neg_eig", [False, True])
-def test_activation_backward_matches_finite_differences(neg_eig):
+def test_activation_backward_matches_finite_differences(neg_eig, per_key):
     """The activation's chain rule against central differences of
     L = <dg, log_gate(a, A_log, dt_bias)> + <dbeta, beta_from_logits(b)>
-    through oracle.activation (every element of a, b, A_log, dt_bias)."""
+    through oracle.activation (every element of a, b, A_log, dt_bias); the
+    per-key gate has a and dt_bias per channel and A_log per head."""
     from oracle import activation as act
     from oracle.backward import activation_backward
     rng = np.random.default_rng(90)
-    B, T, H = 2, 5, 3
-    a, b = rng.standard_normal((B, T, H)) * 2, rng.standard_normal((B, T, H)) * 2
-    A_log, dt_bias = np.log(rng.uniform(0.5, 16, H)), rng.standard_normal(H)
-    dg, dbeta = rng.standard_normal((B, T, H)), rng.standard_normal((B, T, H))
+    B, T, H, K = 2, 5, 3, 4
+    ga = (B, T, H, K) if per_key else (B, T, H)
+    a, b = rng.standard_normal(ga) * 2, rng.standard_normal((B, T, H)) * 2
+    A_log = np.log(rng.uniform(0.5, 16, H))
+    dt_bias = rng.standard_normal((H, K) if per_key else H)
+    dg, dbeta = rng.standard_normal(ga), rng.standard_normal((B, T, H))
 
     def loss(a_, b_, A_, d_):
         return float(np.sum(dg * act.log_gate(a_, A_, d_)) +
