@@ -11,8 +11,9 @@ stream, the two-stage path (intra-chunk stage + state pass) for comparison,
 the decode step (256 sequences x 32 heads, fp32 state in place, 64 steps),
 the chunked backward on the prefill workload (gradients of q, k, v, beta, g
 and h0 from seeded dO and dht), the per-key-gate (KDA) prefill B=2, T=8192,
-H=16 (two-stage route), the packed variable-length prefill (16 sequences,
-137 491 tokens, H=32; fused route), and the fp64 CPU oracle on the host cores.
+H=16 (two-stage route) and its backward, the packed variable-length prefill
+(16 sequences, 137 491 tokens, H=32; fused route), and the fp64 CPU oracle on
+the host cores.
 
 Every leg first runs its own call back to back for a fixed wall time
 (--settle-s): the shader clock drops during the host's pauses (input
@@ -25,7 +26,8 @@ the back-to-back prefill time, and the fp64 oracle timed on the host cores on
 every workload.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-decode]
-                  [--no-backward] [--no-kda] [--no-varlen] [--no-variants]
+                  [--no-backward] [--no-kda] [--no-kda-backward] [--no-varlen]
+                  [--no-variants]
                   [--only LEG]
 """
 from __future__ import annotations
@@ -77,6 +79,10 @@ KERNEL_SOURCES = {"fused_kernel": ["k_fused.hip", "gdn_device.hpp"],
                   "bwd_local_kernel": ["k_bwd.hip", "gdn_device.hpp"],
                   "kda_intra_kernel": ["k_intra.hip", "gdn_device.hpp"],
                   "kda_scan_kernel": ["k_scan.hip", "gdn_device.hpp"],
+                  "kda_bwd_intra_kernel": ["k_intra.hip", "gdn_device.hpp"],
+                  "kda_bwd_state_scan_kernel": ["k_scan.hip", "gdn_device.hpp"],
+                  "kda_bwd_scan_kernel": ["k_bwd.hip", "gdn_device.hpp"],
+                  "kda_bwd_local_kernel": ["k_bwd_kda.hip", "gdn_device.hpp"],
                   "varlen_fused_kernel": ["k_fused.hip", "gdn_device.hpp"]}
 
 
@@ -338,22 +344,25 @@ def bench_decode(args, gdn):
                          "traffic": measured_traffic("step_kernel")}}
 
 
-def bench_backward(args, gdn, d):
-    """The chunked backward on the prefill workload: four kernels per call
-    (intra-chunk recompute, state recompute, reverse state-gradient pass,
-    per-chunk gradients), timed with HIP events over back-to-back calls."""
+def bench_backward(args, gdn, d, seed=1):
+    """The chunked backward on a prefill workload (d: the scalar-gate prefill,
+    or the per-key one): four kernels per call (intra-chunk recompute, state
+    recompute, reverse state-gradient pass, per-chunk gradients), timed with
+    HIP events over back-to-back calls."""
     spec = d["spec"]
-    gr = gdn_synth.make_grads(d, 1)
+    gate = spec.gate
+    gr = gdn_synth.make_grads(d, seed)
     x = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
     q, k, v, beta, g, h0 = (x[n] for n in ("q", "k", "v", "beta", "g", "h0"))
     do, dht = gr["do"].cuda(), gr["dht"].cuda()
     out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
-               dbeta=torch.empty_like(beta), dg=torch.empty_like(g), dh0=torch.empty_like(h0))
-    desc = gdn.fwd_desc(q, v, "scalar", spec.chunk, d["scale"])
+               dbeta=torch.empty_like(beta), dg=torch.empty_like(g), dh0=torch.empty_like(dht))
+    desc = gdn.fwd_desc(q, v, gate, spec.chunk, d["scale"])
     ws = torch.empty(gdn.bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
 
     def call():
-        gdn.chunk_bwd(q, k, v, beta, g, do, d["scale"], h0=h0, dht=dht, workspace=ws, out=out)
+        gdn.chunk_bwd(q, k, v, beta, g, do, d["scale"], h0=h0, dht=dht, workspace=ws, out=out,
+                      gate=gate)
 
     settle(call, args.settle_s)
     for _ in range(max(args.warmup // 10, 5)):
@@ -363,11 +372,13 @@ def bench_backward(args, gdn, d):
     th = spec.B * spec.T * spec.H
     es = 2 if spec.dtype == "bf16" else 4
     state = 4 * spec.K * spec.V * spec.H * spec.B
-    # inputs q, k, v, dO, beta, g, h0, dht; outputs dq, dk, dv, dbeta, dg, dh0
-    alg_bytes = th * ((2 * spec.K + 2 * spec.V) * es + 8) + 2 * state + \
-        th * ((2 * spec.K + spec.V) * es + 8) + state
+    gb = 4 + 4 * (spec.K if gate == "per_key" else 1)   # beta and g of a token-head
+    # inputs q, k, v, dO, beta, g, h0 (if any), dht; outputs dq, dk, dv, dbeta, dg, dh0
+    alg_bytes = th * ((2 * spec.K + 2 * spec.V) * es + gb) + (2 if h0 is not None else 1) * state + \
+        th * ((2 * spec.K + spec.V) * es + gb) + state
     flops = gdn_synth.bwd_flops_per_token_head(spec.K, spec.V, spec.chunk) * th
-    log("backward %.1f us per call" % (t * 1e6))
+    log("%s backward %.1f us per call" % (gate, t * 1e6))
+    pre = "kda_" if gate == "per_key" else ""
     return {"workload": spec.name, "us_per_call": t * 1e6, "calls": reps,
             "tokens_per_s": spec.B * spec.T / t, "alg_flops": flops,
             "TFLOPs": flops / t / 1e12, "frac_mfma_bf16": flops / t / BF16_PEAK,
@@ -375,8 +386,9 @@ def bench_backward(args, gdn, d):
             "workspace_bytes": ws.numel(),
             # HBM bytes per launch of each of its kernels, from the committed
             # counter summary (None where the source changed since)
-            "traffic": {k: measured_traffic(k) for k in ("bwd_intra_kernel", "bwd_state_scan_kernel",
-                                                         "bwd_scan_kernel", "bwd_local_kernel")}}
+            "traffic": {pre + k: measured_traffic(pre + k)
+                        for k in ("bwd_intra_kernel", "bwd_state_scan_kernel", "bwd_scan_kernel",
+                                  "bwd_local_kernel")}}
 
 
 def bench_kda(args, gdn):
@@ -595,11 +607,13 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-kda", action="store_true")
+    ap.add_argument("--no-kda-backward", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--settle-s", type=float, default=0.3,
                     help="seconds of back-to-back calls before each leg's warm-up and timing")
-    ap.add_argument("--only", choices=["prefill", "decode", "backward", "kda", "varlen", "variants"],
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "kda", "kda_backward", "varlen",
+                                       "variants"],
                     help="run the prefill leg and this one only (for per-leg profiles)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (a known-size kernel to scale "
@@ -620,8 +634,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if args.only:
-        for leg in ("decode", "backward", "kda", "varlen", "variants"):
-            if leg != args.only:
+        for leg in ("decode", "backward", "kda", "kda_backward", "varlen", "variants"):
+            if leg != args.only and not (leg == "kda" and args.only == "kda_backward"):
                 setattr(args, "no_" + leg, True)
         args.no_cpu = True
     dev = device_info()
@@ -629,6 +643,7 @@ def main():
     dec_d, decode = (None, None) if args.no_decode else bench_decode(args, gdn)
     backward = None if args.no_backward else bench_backward(args, gdn, d)
     kda_d, kda = (None, None) if args.no_kda else bench_kda(args, gdn)
+    kda_backward = None if (args.no_kda_backward or kda_d is None) else bench_backward(args, gdn, kda_d, 3)
     var_d, varlen = (None, None) if args.no_varlen else bench_varlen(args, gdn)
     variants = None if args.no_variants else bench_variants(args, gdn)
     cpu, cpu_other = None, None
@@ -666,6 +681,7 @@ def main():
         "decode": decode,
         "backward": backward,
         "kda": kda,
+        "kda_backward": kda_backward,
         "varlen": varlen,
         "input_options": variants,
     }

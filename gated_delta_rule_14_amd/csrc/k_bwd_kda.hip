@@ -32,7 +32,8 @@
 // block per instruction) and nothing overflows.  Inside a diagonal block the
 // decay of each pair is taken exactly: the 16 tokens of a tile sit in the 16
 // lanes of a DPP row, token j = i - o reaches token i's lane by a row shift
-// of o, and the column-side terms go back by the opposite shift.
+// of o, the column-side terms go back by the opposite shift, and the decay
+// grows by one gate factor per offset.
 //
 // One 512-thread workgroup (8 waves) per (chunk, head); everything in LDS
 // except the per-lane gates, h and dH, which load straight into registers.
@@ -75,46 +76,50 @@ __device__ __forceinline__ float dpp_mov(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
 
-// Offset O of a diagonal block: the lane of token i (gate gi, key ki, query
-// qi, beta bi of its 4 channels) pairs with token j = i - O of its tile.
-// Row side: Pq_i += Pm_ij E K_j, Pa1_i += dA_ij E K_j; column side, sent to
-// the lane of token j: Pk_j += Pm_ij E Q_i, Pa2_j += dA_ij beta_i E K_i, with
-// E = 2^{G_i - G_j} per channel.  Lanes with i < O read an upper-triangle
-// entry of Pm and dA (zero) and a clamped E, so they add nothing; row shifts
+// Offset O of a diagonal block: the lane of token i (key ki, query qi, beta
+// bi of its 4 channels) pairs with token j = i - O of its tile.  Row side:
+// Pq_i += Pm_ij E K_j, Pa1_i += dA_ij E K_j, with E = 2^{G_i - G_j} per
+// channel and K_j brought from lane j by a row shift of O; column side, sent
+// to the lane of token j by the opposite shift: Pk_j += Pm_ij E Q_i,
+// Pa2_j += dA_ij beta_i E K_i.  E is a running product over the offsets,
+// E(O) = E(O-1) alpha_{i-O+1} with alpha_t = 2^{G_t - G_{t-1}} <= 1 (the
+// gate factor of token t, a row shift of O-1 away), so no exponential is
+// taken per pair and nothing overflows.  Lanes with i < O read an
+// upper-triangle entry of Pm and dA (zero), so they add nothing; row shifts
 // from outside the 16-lane row deliver zero.
 struct DiagPair {
-    f32x4 gi, ki, qi;
+    f32x4 ai, ki, qi;   // ai: alpha of the lane's token, per channel
     float bi;
     const bf16* pmr;   // row i of Pm, at the block's first column
     const bf16* dar;   // row i of dA, likewise
     int tl;
-    f32x4 pq, pa1, pk, pa2;
+    f32x4 pq, pa1, pk, pa2, E;
 
     template <int O>
     __device__ __forceinline__ void step() {
-        f32x4 gj, kj;
+        f32x4 kj;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             if constexpr (O == 0) {
-                gj[e] = gi[e];
                 kj[e] = ki[e];
+                E[e] = 1.f;
             } else {
-                gj[e] = dpp_mov<0x110 + O>(gi[e]);   // row_shr:O
-                kj[e] = dpp_mov<0x110 + O>(ki[e]);
+                kj[e] = dpp_mov<0x110 + O>(ki[e]);   // row_shr:O
+                E[e] *= O == 1 ? ai[e] : dpp_mov<0x110 + O - 1>(ai[e]);   // row_shr:O-1
             }
         }
         const int jj = (tl - O) & 15;
         const float m1 = Elem<bf16>::load(pmr + jj);
         const float m2 = Elem<bf16>::load(dar + jj);
+        const float mb = m2 * bi;
         f32x4 t1, t2;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float E = exp2_hw(fminf(gi[e] - gj[e], 0.f));
-            const float a1 = m1 * E, a2 = m2 * E;
+            const float a1 = m1 * E[e], a2 = m2 * E[e];
             pq[e] += a1 * kj[e];
             pa1[e] += a2 * kj[e];
             t1[e] = a1 * qi[e];
-            t2[e] = a2 * bi * ki[e];
+            t2[e] = (mb * E[e]) * ki[e];
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -133,7 +138,7 @@ struct DiagPair {
     template <int O>
     __device__ __forceinline__ void fenced() {
         step<O>();
-        asm volatile("" : "+v"(pq), "+v"(pa1), "+v"(pk), "+v"(pa2));
+        asm volatile("" : "+v"(pq), "+v"(pa1), "+v"(pk), "+v"(pa2), "+v"(E));
     }
     __device__ __forceinline__ void run() {
         fenced<0>(); fenced<1>(); fenced<2>(); fenced<3>(); fenced<4>(); fenced<5>(); fenced<6>(); fenced<7>();
@@ -537,8 +542,11 @@ __global__ __launch_bounds__(KDA_THREADS) void bwd_local_kda_kernel(BwdLocalLaun
                 dp.pa2[e] += f * t2[e];
             }
         }
-        // the diagonal block
-        dp.gi = gq[j];
+        // the diagonal block; alpha of token i from G_i - G_{i-1} (the
+        // block's first lane gets a value it never uses)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            dp.ai[e] = exp2_hw(fminf(gq[j][e] - dpp_mov<0x111>(gq[j][e]), 0.f));   // row_shr:1
         dp.ki = quad(sK + r * LDK + kc);
         dp.qi = quad(sQ + r * LDK + kc);
         dp.bi = sB[r];
