@@ -411,6 +411,10 @@ gdn_status gdn_recurrent_step_act(const gdn_step_desc *d, const gdn_activation *
  * L = <dout, o> + <dht, ht> with respect to q, k, v, beta, g and h0.  The
  * forward quantities (U, W, the chunk entry states) are recomputed from the
  * inputs, as the pages' Steps 1-2 do; nothing is kept from a forward call.
+ * With the per-key-channel gate (GDN_GATE_PER_KEY) every decay ratio of those
+ * steps sits inside the sum over the key channel, as in the chunkwise KDA
+ * section of "DeltaNet 系列线性注意力变体的推导之旅"; the carried state
+ * gradient then decays row by row and dg is per channel.
  *
  *   q, k, v, beta, g, h0, cu_seqlens, scale: as for gdn_chunk_fwd
  *   dout       [B, T, H, V]  qkv_dtype
@@ -418,14 +422,15 @@ gdn_status gdn_recurrent_step_act(const gdn_step_desc *d, const gdn_activation *
  *   dq, dk     [B, T, H, K]  qkv_dtype, written
  *   dv         [B, T, H, V]  qkv_dtype, written
  *   dbeta      [B, T, H]     float, written
- *   dg         [B, T, H]     float, written: the gradient of the natural-log gate
+ *   dg         [B, T, H] or [B, T, H, K] (the shape of g)  float, written: the
+ *              gradient of the natural-log gate
  *   dh0        [N, H, K, V]  float, written, or NULL: not computed
  *
- * Supported: the scalar gate, chunk 64, grouped value heads (see GVA
- * above: v, dv, beta, dbeta, g, dg, h0, dht, dh0 have H_V heads; q, k, dq, dk
- * have H, and dq, dk of a q/k head sum the terms of its H_V/H value heads);
- * bf16 q/k/v with K, V in {64, 128}, fp32 with K = V = 64.  Other shapes give
- * GDN_ERR_UNSUPPORTED.  dout, dq, dk, dv need 16-byte alignment.
+ * Supported: chunk 64, grouped value heads (see GVA above: v, dv, beta,
+ * dbeta, g, dg, h0, dht, dh0 have H_V heads; q, k, dq, dk have H, and dq, dk
+ * of a q/k head sum the terms of its H_V/H value heads); bf16 q/k/v with K, V
+ * in {64, 128} for either gate; fp32 with K = V = 64 for the scalar gate.
+ * Other shapes give GDN_ERR_UNSUPPORTED.  dout, dq, dk, dv need 16-byte alignment.
  * The workspace (gdn_chunk_bwd_workspace bytes, 256-byte aligned) holds the
  * recomputed per-chunk quantities, the chunk entry states and the state
  * gradients; its contents on return are unspecified.  No output may alias an
@@ -449,14 +454,16 @@ gdn_status gdn_chunk_bwd(const gdn_fwd_desc *d,
  *   dbeta  d/db = dbeta_act * m sigmoid(b) sigmoid(-b)          with GDN_ACT_BETA_SIGMOID
  *          (m = 2 with GDN_ACT_BETA_NEG_EIG, else 1)
  *   dA_log   [H_V] float, written with GDN_ACT_GATE (required then):
- *            sum over the tokens of dlog_alpha * log_alpha
- *   ddt_bias [H_V] float, written with GDN_ACT_GATE (required then):
- *            sum over the tokens of d/da
+ *            sum over the tokens (and, per-key gate, the channels) of
+ *            dlog_alpha * log_alpha
+ *   ddt_bias [H_V] ([H_V, K] for the per-key gate) float, written with
+ *            GDN_ACT_GATE (required then): sum over the tokens of d/da
  * Both are ignored without GDN_ACT_GATE.  With GDN_ACT_QK_L2NORM, dq and dk
  * are the gradients of the raw q and k: the normalisation's chain rule
  * dx = (dy - x (x.dy) / n2) / sqrt(n2), n2 = sum_K x^2 + 1e-6, is applied to
- * the gradients of the normalised rows.  Only the scalar gate is supported
- * (dt_bias [H_V]); the rest is as for gdn_chunk_bwd, with the same workspace.
+ * the gradients of the normalised rows.  The per-key gate takes dt_bias
+ * [H_V, K] and applies the chain rule per channel; the rest is as for
+ * gdn_chunk_bwd, with the same workspace.
  */
 gdn_status gdn_chunk_bwd_act(const gdn_fwd_desc *d, const gdn_activation *act,
                              const void *q, const void *k, const void *v,
