@@ -344,7 +344,27 @@ __device__ __forceinline__ void store_frag_groups(const T* xt, int ld, T* dst, i
                                                   int rt0, int nrt, int lane) {
     typedef FragOrder<T> F;
     constexpr int KG = F::KG, VE = F::VE;
-    static_assert(VT % KG == 0, "whole groups");
+    if constexpr (sizeof(T) == 2 && VT == 16) {
+        // half of each 32-column group: lane 16g+n of the group holds columns
+        // 8g..8g+7, so the lanes of g = 2hv, 2hv+1 (hv = which half v0 is)
+        // store; the others read rows 0..15 of the buffer too (the
+        // transposing read addresses rows 8(g%2)..) and drop them
+        const int g = lane >> 4, j = lane & 15, hv = (v0 >> 4) & 1;
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+        for (int rt = rt0; rt < rt0 + nrt; ++rt) {
+            const T* p = xt + (8 * (g & 1) + (j >> 2)) * ld + 16 * rt + 4 * (j & 3);
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p);
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p + 4 * ld));
+            typedef short i16x8 __attribute__((ext_vector_type(8)));
+            const u32x4 grp = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            if ((g >> 1) == hv) {
+                const int sg = v0 / KG;
+                *reinterpret_cast<u32x4*>(dst + ((int64_t)(rt * (D / KG) + sg) * 64 + lane) * VE) = grp;
+            }
+        }
+        return;
+    }
+    static_assert(VT % KG == 0 || (sizeof(T) == 2 && VT == 16), "whole or half groups");
     for (int rt = rt0; rt < rt0 + nrt; ++rt) {
 #pragma unroll
         for (int q = 0; q < VT / KG; ++q) {

@@ -412,17 +412,26 @@ static hipError_t launch_bscan_cfg(const BwdScanLaunch& a) {
     return hipGetLastError();
 }
 
+template <bool PK, int VT>
+static hipError_t launch_bwd_scan_vt(const BwdScanLaunch& a) {
+    if (a.K == 64 && a.V == 64) return launch_bscan_cfg<BScanCfg<bf16, 64, 64, VT, 2, PK>>(a);
+    if (a.K == 64 && a.V == 128) return launch_bscan_cfg<BScanCfg<bf16, 64, 128, VT, 2, PK>>(a);
+    if (a.K == 128 && a.V == 64) return launch_bscan_cfg<BScanCfg<bf16, 128, 64, VT, 2, PK>>(a);
+    if (a.K == 128 && a.V == 128) return launch_bscan_cfg<BScanCfg<bf16, 128, 128, VT, 2, PK>>(a);
+    return hipErrorInvalidValue;
+}
+
 template <bool PK>
 static hipError_t launch_bwd_scan_g(const BwdScanLaunch& a) {
     if (!a.bf16) {   // the fp32 backward covers K = V = 64 (the per-chunk kernel's LDS)
         if (a.K == 64 && a.V == 64 && !PK) return launch_bscan_cfg<BScanCfg<float, 64, 64, 32, 1>>(a);
         return hipErrorInvalidValue;
     }
-    if (a.K == 64 && a.V == 64) return launch_bscan_cfg<BScanCfg<bf16, 64, 64, 32, 2, PK>>(a);
-    if (a.K == 64 && a.V == 128) return launch_bscan_cfg<BScanCfg<bf16, 64, 128, 32, 2, PK>>(a);
-    if (a.K == 128 && a.V == 64) return launch_bscan_cfg<BScanCfg<bf16, 128, 64, 32, 2, PK>>(a);
-    if (a.K == 128 && a.V == 128) return launch_bscan_cfg<BScanCfg<bf16, 128, 128, 32, 2, PK>>(a);
-    return hipErrorInvalidValue;
+    // 16-wide value slices when even they give at most one workgroup per CU
+    // (few long chains of unpacked input): the CUs the 32-wide ones would
+    // leave idle share the state
+    if (!a.map.seqs && a.N * a.H * (a.V / 16) <= 256) return launch_bwd_scan_vt<PK, 16>(a);
+    return launch_bwd_scan_vt<PK, 32>(a);
 }
 
 hipError_t launch_bwd_scan(const BwdScanLaunch& a) {

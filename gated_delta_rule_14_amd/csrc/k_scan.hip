@@ -377,14 +377,14 @@ struct ScanStore {
     int w;   // 0 or 1
     __device__ __forceinline__ void issue(Pre&, int) const {}
     __device__ __forceinline__ void step(int j, const Pre&, Pre&) const {
-        // (16-wide slices are never chosen with the stores on)
-        if constexpr (Cfg::VT % FragOrder<T>::KG == 0) {
+        constexpr bool whole = Cfg::VT % FragOrder<T>::KG == 0 || (sizeof(T) == 2 && Cfg::VT == 16);
+        if constexpr (whole) {
             if (ch.a.hs)
                 store_frag_groups<T, Cfg::VT>(ch.shT, Cfg::LDH, static_cast<T*>(ch.a.hs) + ch.blk(j) * K * V,
                                               V, ch.v0, w * (K / 32), K / 32, ch.lane);
         }
         lds_barrier();   // V_new^T published
-        if constexpr (Cfg::VT % FragOrder<T>::KG == 0) {
+        if constexpr (whole) {
             if (ch.a.vn)
                 store_frag_groups<T, Cfg::VT>(ch.sVn, Cfg::LDV, static_cast<T*>(ch.a.vn) + ch.blk(j) * C * V,
                                               V, ch.v0, w * (C / 32), C / 32, ch.lane);
@@ -439,9 +439,9 @@ static hipError_t launch_scan_cfg(const ScanLaunch& a) {
 static int scan_vt(const ScanLaunch& a, bool bf16) {
     if (!bf16) return 32;
     // 16-wide slices when even they give at most one workgroup per CU (few
-    // long chains); not for the stores of the backward, which write whole
-    // 32-column fragment groups
-    if (!a.map.seqs && !a.hs && !a.vn && a.N * a.H * (a.V / 16) <= 256) return 16;
+    // long chains; with the backward's per-chunk stores too, which then
+    // write half fragment groups)
+    if (!a.map.seqs && a.N * a.H * (a.V / 16) <= 256) return 16;
     const int min_nvt = (a.K == 128 && a.V == 128) ? 2 : 1;
     int nvt = a.V / 32;
     if (!a.map.seqs)
