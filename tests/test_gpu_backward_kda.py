@@ -179,3 +179,31 @@ def test_kda_bwd_full_size_sampled(gpu_lib):
     d, gr, got = _case(spec, 3)
     for b, h in ((0, 0), (1, 13)):
         _check(got, _ref(d, gr, heads=[h], batch=b), heads=[h], batch=b)
+
+
+def test_kda_bwd_activation_packed_with_empty_sequences(gpu_lib):
+    """Gate and beta logits on packed input with empty sequences: the unused
+    chunk slots of the packed table must not enter dA_log or ddt_bias."""
+    import gated_delta_rule_14_amd as gdn
+    spec = _spec(H=2, K=64, V=64, rand_lengths=None, lengths=(0, 70, 0, 129, 64, 1), h0_std=0.05)
+    print("case: kda backward activation, packed", spec, flush=True)
+    d = gdn_synth.make_prefill(spec, 181, logits=True)
+    H, K = d["v"].shape[2], d["q"].shape[3]
+    d["dt_bias"] = d["dt_bias"] + torch.linspace(-0.5, 0.5, H * K, dtype=torch.float32).reshape(H, K)
+    gr = gdn_synth.make_grads(d, 181)
+    x = to_dev(d)
+    a = gdn.activation(gate_logits=True, beta_sigmoid=True, A_log=d["A_log"].cuda(),
+                       dt_bias=d["dt_bias"].cuda())
+    got = gdn.chunk_bwd(x["q"], x["k"], x["v"], x["beta"], x["g"], gr["do"].cuda(), d["scale"],
+                        h0=x["h0"], dht=gr["dht"].cuda(), cu_seqlens=x["cu_seqlens"], act=a,
+                        gate="per_key")
+    torch.cuda.synchronize()
+    f64 = oracle.as_f64
+    g_act = act.log_gate(f64(d["g"]), f64(d["A_log"]), f64(d["dt_bias"]))
+    b_act = act.beta_from_logits(f64(d["beta"]))
+    ref = chunked_backward(d["q"], d["k"], d["v"], b_act, g_act, d["scale"], gr["do"], h0=d["h0"],
+                           dht=gr["dht"], cu_seqlens=d["cu_seqlens"], chunk=d["chunk"],
+                           gate="per_key")
+    ref["dg"], ref["dbeta"], ref["dA_log"], ref["ddt_bias"] = activation_backward(
+        d["g"], d["beta"], d["A_log"], d["dt_bias"], ref["dg"], ref["dbeta"])
+    _check(got, ref, names=NAMES + ("dA_log", "ddt_bias"))
