@@ -477,9 +477,10 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
             *reinterpret_cast<uint4*>(sS + r * LDK + d0) = Vec16<T>::pack(f);
         }
         __syncthreads();
-        if (wave < NB) {   // job (pair P of blocks, A or Aqk)
-            const int P = wave % (NB / 2);
-            const bool isq = wave >= NB / 2;
+        if (wave >= NB && wave < 2 * NB) {   // job (pair P of blocks, A or Aqk); waves
+                                             // 0..NB-1 take the triangles meanwhile
+            const int P = (wave - NB) % (NB / 2);
+            const bool isq = wave - NB >= NB / 2;
             const int g4 = lane >> 4;
             if (!isq) {
                 // rows: later K of blocks 2P, 2P+1; columns: their earlier K
@@ -517,100 +518,168 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                 }
             }
         }
-        // upper blocks of Aqk (lower blocks of Aqk^T in the backward mode):
-        // zeros (those of A are masked when Ainv is read)
-        for (int i = tid; i < C * C; i += NT) {
-            const int r = i / C, j = i - r * C;
-            if (BWD ? j / 16 < r / 16 : j / 16 > r / 16)
-                Elem<T>::store(gaqk + FragOrder<T>::off(r, j, C), 0.f);
+        // zeros of Aqk's strict upper triangle (Aqk^T's lower one in the
+        // backward mode), by the waves of the quadrant jobs: every 8-column
+        // piece of a row that lies wholly on the zero side; the pieces the
+        // diagonal crosses are written whole by the triangles below.  (A's
+        // upper triangle is never read: the substitution reads below the
+        // diagonal only, and Ainv's upper blocks are masked.)
+        if (wave >= NB) {
+            if constexpr (sizeof(T) == 2) {   // a piece is one 16-byte group of the fragment order
+                for (int pc = tid - 64 * NB; pc < C * C / 8; pc += NT - 64 * NB) {
+                    const int r = pc >> 3, p8 = 8 * (pc & 7);
+                    if (BWD ? p8 + 7 < r : p8 > r)
+                        *reinterpret_cast<uint4*>(gaqk + FragOrder<T>::off(r, p8, C)) = uint4{0u, 0u, 0u, 0u};
+                }
+            } else {
+                for (int i = tid - 64 * NB; i < C * C; i += NT - 64 * NB) {
+                    const int r = i / C, j = i - r * C;
+                    if ((BWD ? j < r : j > r) && (j >> 3) != (r >> 3))
+                        Elem<T>::store(gaqk + FragOrder<T>::off(r, j, C), 0.f);
+                }
+            }
         }
-        // the two 8x8 triangles of each diagonal block, pair by pair: thread
-        // = (block, row i, a contiguous slice of CH channels); row i's keys,
-        // queries and gates stay in registers while j runs over the row's
-        // half of the block, K_j and G_j are vector reads shared by the
-        // wave's 8 rows, and the slice sums are added over the SL = 8
-        // neighbouring lanes with DPP (the total lands in slice SL-1).  Wave
-        // w takes rows 8(w/4) .. 8(w/4)+7 of block w%4 and columns of the
-        // same half, so the two waves that share a SIMD (w, w+4) do 8 + 8
-        // steps; pairs j > i inside that range are computed and dropped
-        // (valid pairs have G_i <= G_j, so the decay exponent needs no clamp
-        // there).
-        {
-            constexpr int SL = NT / (NB * 16);      // threads per row
-            constexpr int CH = K / SL;              // channels per thread
-            static_assert(SL == 8 && CH % EV == 0 && CH % 4 == 0, "8 lanes per row, whole vectors");
-            static_assert(NW == 2 * NB, "two waves per diagonal block");
-            const int I = wave % NB, half = wave / NB, i = 16 * I + 8 * half + lane / SL, s = lane % SL;
-            const int c0 = CH * s, jbeg = 16 * I + 8 * half, jend = jbeg + 8;
-            auto sum8 = [](float x) {
-                x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));  // quad_perm 1,0,3,2
-                x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));  // quad_perm 2,3,0,1
-                x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, false)); // row_shr:4
-                return x;
+        // the two 8x8 triangles of each diagonal block (pairs j <= i inside
+        // one 8-token half), wave I taking block I: lane (token t of the
+        // block, channel quarter cq) holds its token's key, query and gate
+        // for CQ channels.  Offset O pairs token t with j = t - O: K_j comes
+        // from lane t - O by a row shift (DPP, inside the 16-lane row of one
+        // channel quarter), and 2^{G_t - G_j} per channel is the running
+        // product E(O) = E(O-1) alpha_{t-O+1} of the gate factors
+        // alpha_s = 2^{G_s - G_{s-1}} <= 1 (a row shift of O-1 away), so no
+        // exponential is taken per pair and nothing overflows.  Offsets past
+        // the half's first token (O > t % 8) are computed and dropped.  The
+        // quarters' sums meet by row swaps, after which every lane holds
+        // them all: lane (t, cq) writes A for offsets 2cq, 2cq + 1 and two
+        // of the eight entries of the 8-column piece of Aqk (or Aqk^T) that
+        // holds its token's row of the half, zeros included.
+        if (wave < NB) {
+            constexpr int CQ = K / 4;
+            static_assert(CQ % EV == 0 && CQ % 4 == 0, "whole vectors per lane");
+            const int I = wave, t = lane & 15, cq = lane >> 4, i = 16 * I + t, c0 = CQ * cq;
+            auto shr = [](float x, auto o) {   // the value of lane t - o of the row, 0 outside
+                return __int_as_float(
+                    __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + decltype(o)::value, 0xf, 0xf, true));
             };
-            float ki[CH], qi[CH], gi[CH];
+            auto shl = [](float x, auto o) {   // the value of lane t + o of the row, 0 outside
+                return __int_as_float(
+                    __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 + decltype(o)::value, 0xf, 0xf, true));
+            };
+            // the sum over the wave's four rows (channel quarters), in every lane
+            auto rows_sum = [](float x) {
+                const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+                const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+                const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+                return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+            };
+            float kf[CQ], qf[CQ], al[CQ], E[CQ];
 #pragma unroll
-            for (int v = 0; v < CH / EV; ++v) {
+            for (int v = 0; v < CQ / EV; ++v) {
                 const uint4 xk = *reinterpret_cast<const uint4*>(sK + i * LDK + c0 + v * EV);
                 const uint4 xq = *reinterpret_cast<const uint4*>(sQ + i * LDK + c0 + v * EV);
 #pragma unroll
                 for (int e = 0; e < EV; ++e) {
-                    ki[v * EV + e] = Vec16<T>::get(xk, e);
-                    qi[v * EV + e] = Vec16<T>::get(xq, e);
+                    kf[v * EV + e] = Vec16<T>::get(xk, e);
+                    qf[v * EV + e] = Vec16<T>::get(xq, e);
                 }
             }
 #pragma unroll
-            for (int v = 0; v < CH / 4; ++v) {
+            for (int v = 0; v < CQ / 4; ++v) {
                 const float4 x = *reinterpret_cast<const float4*>(sG + i * LDG + c0 + 4 * v);
-                gi[4 * v] = x.x;
-                gi[4 * v + 1] = x.y;
-                gi[4 * v + 2] = x.z;
-                gi[4 * v + 3] = x.w;
+                const float gx[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    al[4 * v + e] = exp2_hw(fminf(gx[e] - shr(gx[e], std::integral_constant<int, 1>()), 0.f));
             }
-            // K_j and G_j of the next j are read while this one computes
-            uint4 nk[CH / EV];
-            float4 ng[CH / 4];
-            auto fetch = [&](int j) {
+            float akk[8], aqk[8];
+            auto offset = [&](auto oc) {
+                constexpr int O = decltype(oc)::value;
+                float sk0 = 0.f, sk1 = 0.f, sq0 = 0.f, sq1 = 0.f;
 #pragma unroll
-                for (int v = 0; v < CH / EV; ++v)
-                    nk[v] = *reinterpret_cast<const uint4*>(sK + j * LDK + c0 + v * EV);
+                for (int c = 0; c < CQ; ++c) {
+                    float kj;
+                    if constexpr (O == 0) {
+                        kj = kf[c];
+                    } else {
+                        if constexpr (O == 1) E[c] = al[c];
+                        else E[c] *= shr(al[c], std::integral_constant<int, O - 1>());
+                        kj = shr(kf[c], std::integral_constant<int, O>()) * E[c];
+                    }
+                    if (c & 1) {
+                        sk1 += kf[c] * kj;
+                        sq1 += qf[c] * kj;
+                    } else {
+                        sk0 += kf[c] * kj;
+                        sq0 += qf[c] * kj;
+                    }
+                }
+                akk[O] = sk0 + sk1;
+                aqk[O] = sq0 + sq1;
+                // keep the offsets in order: left alone, the compiler hoists
+                // the row shifts of later offsets and keeps them all live
+                asm volatile("" : "+v"(akk[O]), "+v"(aqk[O]));
 #pragma unroll
-                for (int v = 0; v < CH / 4; ++v)
-                    ng[v] = *reinterpret_cast<const float4*>(sG + j * LDG + c0 + 4 * v);
+                for (int c = 0; c < CQ; ++c) asm volatile("" : "+v"(E[c]));
             };
-            fetch(jbeg);
-            for (int j = jbeg; j < jend; ++j) {
-                uint4 ck[CH / EV];
-                float gjv[CH];
+            offset(std::integral_constant<int, 0>());
+            offset(std::integral_constant<int, 1>());
+            offset(std::integral_constant<int, 2>());
+            offset(std::integral_constant<int, 3>());
+            offset(std::integral_constant<int, 4>());
+            offset(std::integral_constant<int, 5>());
+            offset(std::integral_constant<int, 6>());
+            offset(std::integral_constant<int, 7>());
 #pragma unroll
-                for (int v = 0; v < CH / EV; ++v) ck[v] = nk[v];
-#pragma unroll
-                for (int v = 0; v < CH / 4; ++v) {
-                    gjv[4 * v] = ng[v].x;
-                    gjv[4 * v + 1] = ng[v].y;
-                    gjv[4 * v + 2] = ng[v].z;
-                    gjv[4 * v + 3] = ng[v].w;
-                }
-                fetch(min(j + 1, jend - 1));
-                float akk = 0.f, aqk = 0.f;
-#pragma unroll
-                for (int c = 0; c < CH; ++c) {
-                    const float kj = Vec16<T>::get(ck[c / EV], c % EV) * exp2_hw(gi[c] - gjv[c]);
-                    akk += ki[c] * kj;
-                    aqk += qi[c] * kj;
-                }
-                akk = sum8(akk);
-                aqk = sum8(aqk);
-                if (s == SL - 1) {
-                    sA[i * LDA + j] = j < i ? sB[i] * akk : 0.f;
-                    Elem<T>::store(gaqk + (BWD ? FragOrder<T>::off(j, i, C) : FragOrder<T>::off(i, j, C)),
-                                   j <= i ? a.scale * aqk : 0.f);
-                }
+            for (int O = 0; O < 8; ++O) {
+                akk[O] = rows_sum(akk[O]);
+                aqk[O] = rows_sum(aqk[O]) * a.scale;
             }
-            // rows of the upper half's columns that the lower half never reached
-            if (half == 0 && s == SL - 1)
-                for (int j = jend; j < 16 * I + 16; ++j)
-                    Elem<T>::store(gaqk + (BWD ? FragOrder<T>::off(j, i, C) : FragOrder<T>::off(i, j, C)), 0.f);
+            // the pairs of the stored row: (token t, t - O) in the forward
+            // mode; (t + O, t) in the backward mode, whose row is a column
+            // of Aqk (a row shift of O brings pair (t + O, t) to lane t)
+            float pv[8];
+            pv[0] = aqk[0];
+            if constexpr (BWD) {
+                pv[1] = shl(aqk[1], std::integral_constant<int, 1>());
+                pv[2] = shl(aqk[2], std::integral_constant<int, 2>());
+                pv[3] = shl(aqk[3], std::integral_constant<int, 3>());
+                pv[4] = shl(aqk[4], std::integral_constant<int, 4>());
+                pv[5] = shl(aqk[5], std::integral_constant<int, 5>());
+                pv[6] = shl(aqk[6], std::integral_constant<int, 6>());
+                pv[7] = shl(aqk[7], std::integral_constant<int, 7>());
+            } else {
+#pragma unroll
+                for (int O = 1; O < 8; ++O) pv[O] = aqk[O];
+            }
+            const int tt = t & 7;
+            float ev[2], av[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int e = 2 * cq + u;        // column 8(t/8) + e of the piece
+                const int O = BWD ? e - tt : tt - e;
+                float x = 0.f, y = 0.f;
+#pragma unroll
+                for (int o = 0; o < 8; ++o) {
+                    x = o == O ? pv[o] : x;
+                    y = o == e ? akk[o] : y;
+                }
+                ev[u] = x;
+                av[u] = y;
+            }
+            // A: offsets 2cq, 2cq + 1 of token t (j = i - O > the half's start - 1)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int O = 2 * cq + u;
+                if (O > 0 && O <= tt) sA[i * LDA + i - O] = sB[i] * av[u];
+            }
+            // Aqk: entries 2cq, 2cq + 1 of the piece (4 bytes)
+            const int col = 16 * I + 8 * (t >> 3) + 2 * cq;
+            if constexpr (sizeof(T) == 2) {
+                *reinterpret_cast<uint32_t*>(gaqk + FragOrder<T>::off(i, col, C)) = pack_bf16x2(ev[0], ev[1]);
+            } else {
+                Elem<T>::store(gaqk + FragOrder<T>::off(i, col, C), ev[0]);
+                Elem<T>::store(gaqk + FragOrder<T>::off(i, col + 1, C), ev[1]);
+            }
         }
     }
     __syncthreads();
