@@ -689,17 +689,26 @@ __device__ __forceinline__ void diag_inverse(const Ctx& x, f32x4 (&tbb)[4]) {
         *reinterpret_cast<u32x2*>(dt + 24) = s ? w1 : z;
     }
     own_lds_sync();
-    // T_bb = D - D (X D), X = the lower-left 8x8 block of A_bb
+    // T_bb = D - D (X D), X = the lower-left 8x8 block of A_bb.  The reads of
+    // all four blocks are issued first (every lane's addresses lie inside
+    // the blocks; lanes outside X only zero their value), so the four
+    // blocks cost one LDS latency, not three each.
     const int g = lane >> 4, mrow = lane & 15;
+    const bool live = mrow >= 8 && g < 2;
+    float4 xr[4];
+    u32x2 db[4], da[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-        const float4 xr = ldf4(x.sD(b) + mrow * LDD + 4 * g);
-        const bool live = mrow >= 8 && g < 2;
-        const u32x2 xa = live ? pk4(xr) : u32x2{0u, 0u};
-        const u32x2 db = ld8(x.sDT(b) + mrow * (LDDT * 2) + 8 * g);   // D[4g+e][n], n = lane & 15
-        const f32x4 y = mma16(xa, db, zero4());
-        const u32x2 da = tr_read(x.sDT(b) + (4 * g + (mrow >> 2)) * (LDDT * 2) + 8 * (mrow & 3));
-        tbb[b] = mma16(da, neg4(y), unpk4(db));
+        xr[b] = ldf4(x.sD(b) + mrow * LDD + 4 * g);
+        db[b] = ld8(x.sDT(b) + mrow * (LDDT * 2) + 8 * g);   // D[4g+e][n], n = lane & 15
+        da[b] = tr_read(x.sDT(b) + (4 * g + (mrow >> 2)) * (LDDT * 2) + 8 * (mrow & 3));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const u32x2 xa = live ? pk4(xr[b]) : u32x2{0u, 0u};
+        const f32x4 y = mma16(xa, db[b], zero4());
+        tbb[b] = mma16(da[b], neg4(y), unpk4(db[b]));
     }
 }
 
