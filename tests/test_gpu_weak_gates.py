@@ -69,3 +69,45 @@ def test_weak_gates_backward_per_key(gpu_lib):
     d = gdn_synth.make_prefill(spec, 26)
     gr = gdn_synth.make_grads(d, 26)
     _check(d, kda._gpu(d, gr), kda._ref(d, gr))
+
+
+@pytest.mark.parametrize("cid,dt,K,V", [(1, "bf16", 128, 128), (3, "bf16", 64, 128)])
+def test_weak_gates_activation(gpu_lib, cid, dt, K, V):
+    """Raw gate and beta logits activated in the kernels (A_log = log A),
+    beta in (0, 2): the single-pass kernel and the per-key two-stage route."""
+    from test_gpu_activation import _prefill
+    spec = gdn_synth.prefill_spec(cid, dtype=dt, B=2, T=600, H=2, K=K, V=V, A_range=WEAK, h0_std=0.02)
+    print("relative errors: o %.2e ht %.2e" % _prefill(spec, 27, True, True, True), flush=True)
+
+
+def test_weak_gates_gva(gpu_lib):
+    """Two value heads per q/k head on the single-pass kernel, with the
+    activation."""
+    from test_gpu_gva import _gva_prefill
+    _gva_prefill(gdn_synth.prefill_spec(1, B=2, T=600, H=4, A_range=WEAK), 2, 28, with_act=True)
+
+
+def test_weak_gates_l2norm(gpu_lib):
+    """q/k normalised in the single-pass kernel (rows first rescaled by seeded
+    factors in [0.25, 4]), with the gate and beta activations."""
+    import torch
+    import gated_delta_rule_14_amd as gdn
+    import oracle
+    from oracle import activation as act
+    from parity_util import TOL, rel_err, to_dev
+    from test_gpu_l2norm import _normalised, _rescale
+    spec = gdn_synth.prefill_spec(1, B=2, T=600, H=3, A_range=WEAK, h0_std=0.05)
+    print("case: l2norm", spec, flush=True)
+    d = _rescale(gdn_synth.make_prefill(spec, 29, logits=True), 30)
+    x = to_dev(d)
+    a = gdn.activation(gate_logits=True, beta_sigmoid=True, qk_l2norm=True, A_log=d["A_log"].cuda(),
+                       dt_bias=d["dt_bias"].cuda())
+    o, ht = gdn.chunk_fwd(x["q"], x["k"], x["v"], x["beta"], x["g"], d["scale"], h0=x["h0"], act=a)
+    torch.cuda.synchronize()
+    g = act.log_gate(oracle.as_f64(d["g"]), oracle.as_f64(d["A_log"]), oracle.as_f64(d["dt_bias"]))
+    b = act.beta_from_logits(oracle.as_f64(d["beta"]))
+    qn, kn = _normalised(d)
+    o_ref, ht_ref = oracle.recurrent_forward(qn, kn, d["v"], b, g, d["scale"], h0=d["h0"])
+    eo, eh = rel_err(o, o_ref), rel_err(ht, ht_ref)
+    print("relative errors: o %.2e ht %.2e" % (eo, eh), flush=True)
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
