@@ -52,8 +52,9 @@ struct IntraSmem {
     // different banks
     static constexpr int LDG = PK ? K + 8 : 1;
     static constexpr int NB = C / 16;
-    // per-key scaled operands: 32 + C - 16 rows for an off-diagonal block
-    // row, 3 x C / 2 for the diagonal blocks' quadrants (and >= C)
+    // per-key scaled operands, two buffers of SCR_ROWS rows: 32 + C - 16
+    // rows for an off-diagonal block row, 3 x C / 2 for the diagonal blocks'
+    // quadrants (and >= C)
     static constexpr int SCR_ROWS = (32 + C - 16) > 3 * C / 2 ? 32 + C - 16 : 3 * C / 2;
     static constexpr size_t o_K = 0;
     static constexpr size_t o_Q = o_K + sizeof(T) * C * LDK;
@@ -65,7 +66,7 @@ struct IntraSmem {
     static constexpr size_t o_F = o_E + sizeof(float) * C;     // 2^{G_C-1 - G_r}
     static constexpr size_t o_P = o_F + sizeof(float) * C;
     static constexpr size_t o_S = o_P + sizeof(float) * 4 * 16 * 17;
-    static constexpr size_t bytes = o_S + (PK ? sizeof(T) * SCR_ROWS * LDK : 0);
+    static constexpr size_t bytes = o_S + (PK ? 2 * sizeof(T) * SCR_ROWS * LDK : 0);   // two buffers
     // Ainv diag(beta gamma) goes where Q was, Ainv diag(beta) where A was
     static_assert(C * LDC * sizeof(T) <= C * LDK * sizeof(T), "A1 fits the Q region");
     static_assert(C * LDC * sizeof(T) <= C * LDA * sizeof(float), "A2 fits the A region");
@@ -401,10 +402,18 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
             }
         }
     } else {
-        T* sS = reinterpret_cast<T*>(smem + L::o_S);
-        for (int I = 1; I < NB; ++I) {
+        // Off-diagonal block rows I = 1 .. NB-1, then the diagonal blocks'
+        // quadrants, each from decay-scaled operands built in a scratch
+        // buffer.  Two buffers alternate: while the products of round I read
+        // one, the operands of the next round are built in the other, so
+        // the waves without a tile of round I go on building and one barrier
+        // separates the rounds.
+        T* const sS0 = reinterpret_cast<T*>(smem + L::o_S);
+        T* const sS1 = sS0 + L::SCR_ROWS * LDK;
+        auto buf = [&](int I) { return (I & 1) ? sS0 : sS1; };   // round NB: the quadrants
+        auto build_offdiag = [&](int I) {
             const int b = 16 * I;
-            __syncthreads();   // previous I's tiles have read the scratch
+            T* sS = buf(I);
             // rows [0,16): K_I 2^{G_I - G_b}; [16,32): Q_I 2^{G_I - G_b};
             // [32, 32 + b): K_J 2^{G_b - G_J} for all J < I
             for (int i = tid; i < (32 + b) * (K / EV); i += NT) {   // one 16-byte vector each
@@ -424,7 +433,9 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                 }
                 *reinterpret_cast<uint4*>(sS + r * LDK + d0) = Vec16<T>::pack(f);
             }
-            __syncthreads();
+        };
+        auto tiles_offdiag = [&](int I) {
+            const T* sS = buf(I);
             for (int job = wave; job < 2 * I; job += NW) {
                 const bool isq = job >= I;
                 const int J = isq ? job - I : job;
@@ -451,32 +462,44 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
                     store4_frag(gaqk, 16 * J + acc_col(lane), 16 * I + 4 * (lane >> 4), C, acc);
                 }
             }
-        }
+        };
         // lower-left 8x8 quadrant of each diagonal block, with b = 16 I + 8:
         // rows [0, C/2): the 8 later K rows of each block, K 2^{G - G_b};
         // [C/2, C): the same Q rows; [C, 3C/2): the 8 earlier K rows,
         // K 2^{G_b - G}.  One 16x16 tile covers two blocks; its two
         // cross-block quadrants are dropped.
-        static_assert(NB % 2 == 0, "diagonal blocks in pairs");
-        __syncthreads();   // the last off-diagonal tiles have read the scratch
-        for (int i = tid; i < (3 * C / 2) * (K / EV); i += NT) {
-            const int r = i / (K / EV), d0 = (i - r * (K / EV)) * EV;
-            const int set = r / (C / 2), rr = r - set * (C / 2), Ib = rr / 8;
-            const int b = 16 * Ib + 8, tok = set < 2 ? b + (rr & 7) : 16 * Ib + (rr & 7);
-            const uint4 xv = *reinterpret_cast<const uint4*>((set == 1 ? sQ : sK) + tok * LDK + d0);
-            float f[EV];
+        auto build_quadrants = [&]() {
+            T* sS = buf(NB);
+            for (int i = tid; i < (3 * C / 2) * (K / EV); i += NT) {
+                const int r = i / (K / EV), d0 = (i - r * (K / EV)) * EV;
+                const int set = r / (C / 2), rr = r - set * (C / 2), Ib = rr / 8;
+                const int b = 16 * Ib + 8, tok = set < 2 ? b + (rr & 7) : 16 * Ib + (rr & 7);
+                const uint4 xv = *reinterpret_cast<const uint4*>((set == 1 ? sQ : sK) + tok * LDK + d0);
+                float f[EV];
 #pragma unroll
-            for (int e4 = 0; e4 < EV; e4 += 4) {
-                const float4 gt = *reinterpret_cast<const float4*>(sG + tok * LDG + d0 + e4);
-                const float4 gb = *reinterpret_cast<const float4*>(sG + b * LDG + d0 + e4);
-                const float dt[4] = {gt.x - gb.x, gt.y - gb.y, gt.z - gb.z, gt.w - gb.w};
+                for (int e4 = 0; e4 < EV; e4 += 4) {
+                    const float4 gt = *reinterpret_cast<const float4*>(sG + tok * LDG + d0 + e4);
+                    const float4 gb = *reinterpret_cast<const float4*>(sG + b * LDG + d0 + e4);
+                    const float dt[4] = {gt.x - gb.x, gt.y - gb.y, gt.z - gb.z, gt.w - gb.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    f[e4 + e] = Vec16<T>::get(xv, e4 + e) * exp2_hw(fminf(set < 2 ? dt[e] : -dt[e], 0.f));
+                    for (int e = 0; e < 4; ++e)
+                        f[e4 + e] = Vec16<T>::get(xv, e4 + e) * exp2_hw(fminf(set < 2 ? dt[e] : -dt[e], 0.f));
+                }
+                *reinterpret_cast<uint4*>(sS + r * LDK + d0) = Vec16<T>::pack(f);
             }
-            *reinterpret_cast<uint4*>(sS + r * LDK + d0) = Vec16<T>::pack(f);
-        }
+        };
+        static_assert(NB % 2 == 0, "diagonal blocks in pairs");
+        build_offdiag(1);
         __syncthreads();
+        for (int I = 1; I < NB; ++I) {
+            tiles_offdiag(I);
+            if (I + 1 < NB)
+                build_offdiag(I + 1);
+            else
+                build_quadrants();
+            __syncthreads();
+        }
+        const T* sS = buf(NB);
         if (wave >= NB && wave < 2 * NB) {   // job (pair P of blocks, A or Aqk); waves
                                              // 0..NB-1 take the triangles meanwhile
             const int P = (wave - NB) % (NB / 2);
