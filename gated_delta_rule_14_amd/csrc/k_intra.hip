@@ -714,12 +714,14 @@ __global__ __launch_bounds__(INTRA_THREADS) void intra_kernel(IntraLaunch a) {
         float* blkA = sA + 16 * wave * LDA + 16 * wave;
         float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = (r == lane) ? 1.f : 0.f;
+        for (int r = 0; r < 16; ++r) x[r] = (r == lane) ? 1.f : 0.f;
+        // right-looking: once x[m] is final it is taken out of every later
+        // row, so the dependent chain is 16 steps long rather than 120 (each
+        // x[r] still subtracts its terms in the order m = 0, 1, ...)
 #pragma unroll
-            for (int m = 0; m < r; ++m) acc -= blkA[r * LDA + m] * x[m];
-            x[r] = acc;
-        }
+        for (int m = 0; m < 16; ++m)
+#pragma unroll
+            for (int r = m + 1; r < 16; ++r) x[r] -= blkA[r * LDA + m] * x[m];
         // the block is only touched by this wave, whose LDS accesses stay in order
 #pragma unroll
         for (int r = 0; r < 16; ++r) blkA[r * LDA + lane] = x[r];
