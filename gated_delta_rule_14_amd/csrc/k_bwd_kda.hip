@@ -94,9 +94,17 @@ struct DiagPair {
     const bf16* dar;   // row i of dA, likewise
     int tl;
     f32x4 pq, pa1, pk, pa2, E;
+    // Pm_ij and dA_ij of offset O (bf16 bits, dA in the high half).  The
+    // fences between offsets are scheduling barriers, so a value read in its
+    // own offset would wait for the LDS there: each is read two offsets ahead.
+    __device__ __forceinline__ uint32_t fetch(int O) const {
+        const int jj = (tl - O) & 15;
+        return (uint32_t)*reinterpret_cast<const unsigned short*>(pmr + jj) |
+               ((uint32_t)*reinterpret_cast<const unsigned short*>(dar + jj) << 16);
+    }
 
     template <int O>
-    __device__ __forceinline__ void step() {
+    __device__ __forceinline__ void step(uint32_t mv) {
         f32x4 kj;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -108,9 +116,7 @@ struct DiagPair {
                 E[e] *= O == 1 ? ai[e] : dpp_mov<0x110 + O - 1>(ai[e]);   // row_shr:O-1
             }
         }
-        const int jj = (tl - O) & 15;
-        const float m1 = Elem<bf16>::load(pmr + jj);
-        const float m2 = Elem<bf16>::load(dar + jj);
+        const float m1 = __uint_as_float(mv << 16), m2 = __uint_as_float(mv & 0xffff0000u);
         const float mb = m2 * bi;
         f32x4 t1, t2;
 #pragma unroll
@@ -136,13 +142,18 @@ struct DiagPair {
     // compiler defers the column-side sums to the end and keeps every
     // shifted term live until then
     template <int O>
-    __device__ __forceinline__ void fenced() {
-        step<O>();
+    __device__ __forceinline__ void fenced(uint32_t (&mv)[3]) {
+        if constexpr (O + 2 < 16) mv[(O + 2) % 3] = fetch(O + 2);
+        step<O>(mv[O % 3]);
         asm volatile("" : "+v"(pq), "+v"(pa1), "+v"(pk), "+v"(pa2), "+v"(E));
     }
     __device__ __forceinline__ void run() {
-        fenced<0>(); fenced<1>(); fenced<2>(); fenced<3>(); fenced<4>(); fenced<5>(); fenced<6>(); fenced<7>();
-        fenced<8>(); fenced<9>(); fenced<10>(); fenced<11>(); fenced<12>(); fenced<13>(); fenced<14>(); fenced<15>();
+        uint32_t mv[3];
+        mv[0] = fetch(0);
+        mv[1] = fetch(1);
+        fenced<0>(mv); fenced<1>(mv); fenced<2>(mv); fenced<3>(mv); fenced<4>(mv); fenced<5>(mv);
+        fenced<6>(mv); fenced<7>(mv); fenced<8>(mv); fenced<9>(mv); fenced<10>(mv); fenced<11>(mv);
+        fenced<12>(mv); fenced<13>(mv); fenced<14>(mv); fenced<15>(mv);
     }
 };
 
