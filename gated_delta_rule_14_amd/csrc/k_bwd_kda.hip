@@ -90,6 +90,7 @@ __device__ __forceinline__ float dpp_mov(float x) {
 struct DiagPair {
     f32x4 ai, ki, qi;   // ai: alpha of the lane's token, per channel
     float bi;
+    f32x4 bki;         // beta_i K_i, fixed over the walk
     const bf16* pmr;   // row i of Pm, at the block's first column
     const bf16* dar;   // row i of dA, likewise
     int tl;
@@ -117,7 +118,6 @@ struct DiagPair {
             }
         }
         const float m1 = __uint_as_float(mv << 16), m2 = __uint_as_float(mv & 0xffff0000u);
-        const float mb = m2 * bi;
         f32x4 t1, t2;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -125,7 +125,7 @@ struct DiagPair {
             pq[e] += a1 * kj[e];
             pa1[e] += a2 * kj[e];
             t1[e] = a1 * qi[e];
-            t2[e] = (mb * E[e]) * ki[e];
+            t2[e] = a2 * bki[e];
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -148,6 +148,8 @@ struct DiagPair {
         asm volatile("" : "+v"(pq), "+v"(pa1), "+v"(pk), "+v"(pa2), "+v"(E));
     }
     __device__ __forceinline__ void run() {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bki[e] = bi * ki[e];
         uint32_t mv[3];
         mv[0] = fetch(0);
         mv[1] = fetch(1);
