@@ -126,6 +126,11 @@ class ClockSampler:
     def _run(self):
         import re
         import subprocess
+        # under a profiler its preloaded library would start with rocm-smi
+        # (a Python script), initialise the GPU there and then exec the
+        # interpreter; profiled runs do not report clocks
+        if "rocprof" in os.environ.get("LD_PRELOAD", ""):
+            return
         while not self.stop:
             try:
                 r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
