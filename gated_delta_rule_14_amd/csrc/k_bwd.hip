@@ -768,11 +768,16 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
         stot = wave_sum(stot);
         if (lane == 0) myRG[C - 1] += stot + exp2_hw(Gend) * hd;
     }
-    // C x C tiles of this wave: (I, J) = divmod(2 * wave + u, 4); lower ones only
+    // C x C tiles of this wave: (I, J) = divmod(LOWER[2 * wave + u], 4).  Only
+    // the 10 tiles on and below the diagonal carry products (here and in
+    // phase D); the table gives the SIMDs (waves w and w + 4) 3, 3, 2 and 2
+    // of them, and the slots left over zero the 6 upper tiles of Pm.
+    static_assert(NW == 8 && C == 64, "tile table");
+    constexpr int LOWER[16] = {15, 10, 14, 5, 13, 1, 12, 2, 9, 3, 8, 6, 4, 7, 0, 11};
     f32x4 kk[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int id = 2 * wave + u, I = id / 4, J = id % 4;
+        const int id = LOWER[2 * wave + u], I = id / 4, J = id % 4;
         kk[u] = zero4();
         if (J > I) {
 #pragma unroll
@@ -885,10 +890,11 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
     }
     lds_barrier();
 
-    // ================= phase D: dA = -T^T Y, strictly lower, gated
+    // ================= phase D: dA = -T^T Y, strictly lower, gated (phase A's
+    // tiles, whose K K^T each wave still holds)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int id = 2 * wave + u, I = id / 4, J = id % 4;
+        const int id = LOWER[2 * wave + u], I = id / 4, J = id % 4;
         if (J > I) continue;
         f32x4 x = zero4();
 #pragma unroll
