@@ -813,6 +813,9 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
         f32x4 atdw[TPK];
 #pragma unroll
         for (int j = 0; j < TPK; ++j) atdw[j] = zero4();
+        // Pm and T are lower triangular: Pm K takes the tokens k <= r of its
+        // row, Pm^T Q and T^T dW those k >= r, so a k step wholly on the
+        // zero side of a token tile is skipped
 #pragma unroll
         for (int k0 = 0; k0 < C; k0 += KS) {
             const Frag bk = M::load_t(sK + k0 * LDK + 16 * kt, LDK, lane);
@@ -820,10 +823,12 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
             const Frag bw = M::load_t(sDW + k0 * LDK + 16 * kt, LDK, lane);
 #pragma unroll
             for (int j = 0; j < TPK; ++j) {
-                const int r0 = 16 * rtk[j];
-                dq[j] = M::mma(bk, M::load(sPM + (r0 + tl) * LDC + k0, lane), dq[j]);
-                dk[j] = M::mma(bq, M::load_t(sPM + k0 * LDC + r0, LDC, lane), dk[j]);
-                atdw[j] = M::mma(bw, M::load_t(sT + k0 * LDC + r0, LDC, lane), atdw[j]);
+                const int r0 = 16 * (NW == NKT ? j : rtk[j]);   // every wave has all token tiles then
+                if (k0 <= r0 + 15) dq[j] = M::mma(bk, M::load(sPM + (r0 + tl) * LDC + k0, lane), dq[j]);
+                if (k0 + KS > r0) {
+                    dk[j] = M::mma(bq, M::load_t(sPM + k0 * LDC + r0, LDC, lane), dk[j]);
+                    atdw[j] = M::mma(bw, M::load_t(sT + k0 * LDC + r0, LDC, lane), atdw[j]);
+                }
             }
         }
         T* gdq = static_cast<T*>(a.dq);
@@ -851,21 +856,30 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
         T* gdv = static_cast<T*>(a.dv);
 #pragma unroll
         for (int j = 0; j < TPV; ++j) {
-            const int r0 = 16 * (wave / NVT + (NW / NVT) * j), r = r0 + tl;
+            const int r0 = 16 * (NW == NVT ? j : wave / NVT + (NW / NVT) * j), r = r0 + tl;
             f32x4 x = zero4();
 #pragma unroll
             for (int k0 = 0; k0 < C; k0 += KS)
-                x = M::mma(M::load_t(sDVN + k0 * LDV + 16 * vt, LDV, lane),
-                           M::load_t(sT + k0 * LDC + r0, LDC, lane), x);
+                if (k0 + KS > r0)   // T^T takes the tokens k >= r
+                    x = M::mma(M::load_t(sDVN + k0 * LDV + 16 * vt, LDV, lane),
+                               M::load_t(sT + k0 * LDC + r0, LDC, lane), x);
             const f32x4 vv = Quad<T>::get(Quad<T>::load(sV + r * LDV + vc));
             add_tok(myRB, r0, x[0] * vv[0] + x[1] * vv[1] + x[2] * vv[2] + x[3] * vv[3]);
             if (r < n) store4(gdv + ((t0 + r) * H + h) * V + vc, sB[r] * x);
         }
     }
-    // dAinv = dVn (diag(beta) V)^T + dW (diag(beta gamma) K)^T
+    // dAinv = dVn (diag(beta) V)^T + dW (diag(beta gamma) K)^T: only its
+    // tiles on and below the diagonal reach dA (below); the upper ones are
+    // zeroed, as phase C multiplies them by zeros of T
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int id = 2 * wave + u, I = id / 4, J = id % 4;
+        const int id = LOWER[2 * wave + u], I = id / 4, J = id % 4;
+        if (J > I) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                Elem<T>::store(sDA + (16 * I + acc_row(lane, e)) * LDC + 16 * J + acc_col(lane), 0.f);
+            continue;
+        }
         const f32x4 x1 = mma_tile<T>(sDVN + 16 * I * LDV, LDV, sV + 16 * J * LDV, LDV, V, lane, zero4());
         const f32x4 x2 = mma_tile<T>(sDW + 16 * I * LDK, LDK, sK + 16 * J * LDK, LDK, K, lane, zero4());
         const int j = 16 * J + acc_col(lane);
@@ -881,11 +895,16 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
     issue_state(cur);
     issue_small(cur);
 
-    // ================= phase C: Y = dAinv T^T
+    // ================= phase C: Y = dAinv T^T, its tiles on and below the
+    // diagonal (phase D reads no other); Y takes Pm's region, whose upper
+    // tiles phase A zeroed.  T is lower triangular, so tile (I, J) takes
+    // the k <= 16 J + 15 of dAinv's rows.
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int id = 2 * wave + u, I = id / 4, J = id % 4;
-        const f32x4 y = mma_tile<T>(sDA + 16 * I * LDC, LDC, sT + 16 * J * LDC, LDC, C, lane, zero4());
+        const int id = LOWER[2 * wave + u], I = id / 4, J = id % 4;
+        if (J > I) continue;
+        const f32x4 y = J < 2 ? mma_tile<T>(sDA + 16 * I * LDC, LDC, sT + 16 * J * LDC, LDC, 32, lane, zero4())
+                              : mma_tile<T>(sDA + 16 * I * LDC, LDC, sT + 16 * J * LDC, LDC, C, lane, zero4());
         store_acc(sY + 16 * I * LDC + 16 * J, LDC, lane, y);
     }
     lds_barrier();
@@ -899,8 +918,9 @@ __global__ __launch_bounds__(BLOCAL_THREADS) void bwd_local_kernel(BwdLocalLaunc
         f32x4 x = zero4();
 #pragma unroll
         for (int k0 = 0; k0 < C; k0 += KS)
-            x = M::mma(M::load_t(sT + k0 * LDC + 16 * I, LDC, lane),
-                       M::load_t(sY + k0 * LDC + 16 * J, LDC, lane), x);
+            if (k0 + KS > 16 * I)   // T^T's rows i take the m >= i
+                x = M::mma(M::load_t(sT + k0 * LDC + 16 * I, LDC, lane),
+                           M::load_t(sY + k0 * LDC + 16 * J, LDC, lane), x);
         const int j = 16 * J + acc_col(lane);
         f32x4 rb, rr;
 #pragma unroll
