@@ -393,10 +393,16 @@ __global__ __launch_bounds__(KDA_THREADS) void bwd_local_kda_kernel(BwdLocalLaun
         lastp = row_sum16(lastp);   // over the tokens of the wave's tiles
         if ((lane & 15) == 15) *reinterpret_cast<f32x4*>(sLast + (wave / NKT) * K + kc) = lastp;
     }
-    // Pm = scale (dO Vn^T), j <= i: the lower tiles of the wave's pair
+    // C x C tiles: (I, J) = divmod(LOWER[2 * wave + u], 4).  The products
+    // needed only on and below the diagonal (Pm, dAinv, Y, dA) take the 10
+    // lower tiles, which the table spreads as 3, 3, 2, 2 over the SIMDs
+    // (waves w and w + 4); the slots left over take the upper tiles.
+    static_assert(NW == 8 && C == 64, "tile table");
+    constexpr int LOWER[16] = {15, 10, 14, 5, 13, 1, 12, 2, 9, 3, 8, 6, 4, 7, 0, 11};
+    // Pm = scale (dO Vn^T), j <= i
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int id = 2 * wave + u, I = id / 4, J = id % 4;
+        const int id = LOWER[2 * wave + u], I = id / 4, J = id % 4;
         if (J > I) continue;   // upper tiles are never read
         const f32x4 x = mma_tile<T>(sDO + 16 * I * LDV, LDV, sVN + 16 * J * LDV, LDV, V, lane, zero4());
         const int jc = 16 * J + acc_col(lane);
@@ -421,12 +427,15 @@ __global__ __launch_bounds__(KDA_THREADS) void bwd_local_kda_kernel(BwdLocalLaun
         f32x4 atdw[TPK];
 #pragma unroll
         for (int j = 0; j < TPK; ++j) atdw[j] = zero4();
+        // T is lower triangular: T^T dW takes the tokens k >= r of its row
 #pragma unroll
         for (int k0 = 0; k0 < C; k0 += KS) {
             const Frag bw = M::load_t(sDW + k0 * LDK + 16 * kt, LDK, lane);
 #pragma unroll
-            for (int j = 0; j < TPK; ++j)
-                atdw[j] = M::mma(bw, M::load_t(sT + k0 * LDC + 16 * rtk[j], LDC, lane), atdw[j]);
+            for (int j = 0; j < TPK; ++j) {
+                const int r0 = 16 * (NW == NKT ? j : rtk[j]);   // every wave has all token tiles then
+                if (k0 + KS > r0) atdw[j] = M::mma(bw, M::load_t(sT + k0 * LDC + r0, LDC, lane), atdw[j]);
+            }
         }
 #pragma unroll
         for (int j = 0; j < TPK; ++j) {
@@ -449,21 +458,30 @@ __global__ __launch_bounds__(KDA_THREADS) void bwd_local_kda_kernel(BwdLocalLaun
         T* gdv = static_cast<T*>(a.dv);
 #pragma unroll
         for (int j = 0; j < TPV; ++j) {
-            const int r0 = 16 * (wave / NVT + (NW / NVT) * j), r = r0 + tl;
+            const int r0 = 16 * (NW == NVT ? j : wave / NVT + (NW / NVT) * j), r = r0 + tl;
             f32x4 x = zero4();
 #pragma unroll
             for (int k0 = 0; k0 < C; k0 += KS)
-                x = M::mma(M::load_t(sDVN + k0 * LDV + 16 * vt, LDV, lane),
-                           M::load_t(sT + k0 * LDC + r0, LDC, lane), x);
+                if (k0 + KS > r0)   // T^T takes the tokens k >= r
+                    x = M::mma(M::load_t(sDVN + k0 * LDV + 16 * vt, LDV, lane),
+                               M::load_t(sT + k0 * LDC + r0, LDC, lane), x);
             const f32x4 vv = quad(sV + r * LDV + vc);
             add_tok(myRB, r0, x[0] * vv[0] + x[1] * vv[1] + x[2] * vv[2] + x[3] * vv[3]);
             if (r < n) store4(gdv + ((t0 + r) * H + h) * V + vc, sB[r] * x);
         }
     }
-    // dAinv = (dVn V^T + dW Kg^T) diag(beta)
+    // dAinv = (dVn V^T + dW Kg^T) diag(beta): only its tiles on and below the
+    // diagonal reach dA; the upper ones are zeroed, as phase C multiplies
+    // them by zeros of T
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int id = 2 * wave + u, I = id / 4, J = id % 4;
+        const int id = LOWER[2 * wave + u], I = id / 4, J = id % 4;
+        if (J > I) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                Elem<T>::store(sDA + (16 * I + acc_row(lane, e)) * LDC + 16 * J + acc_col(lane), 0.f);
+            continue;
+        }
         const f32x4 x1 = mma_tile<T>(sDVN + 16 * I * LDV, LDV, sV + 16 * J * LDV, LDV, V, lane, zero4());
         const f32x4 x2 = mma_tile<T>(sDW + 16 * I * LDK, LDK, sKg + 16 * J * LDK, LDK, K, lane, x1);
         const int jc = 16 * J + acc_col(lane);
@@ -473,11 +491,17 @@ __global__ __launch_bounds__(KDA_THREADS) void bwd_local_kda_kernel(BwdLocalLaun
     }
     lds_barrier();   // V, dVn, dW and Kg are read
 
-    // ================= phase C: Y = dAinv T^T; the block-scaled operands
+    // ================= phase C: Y = dAinv T^T; the block-scaled operands.
+    // Phase D reads Y's tiles on and below the diagonal; the upper ones,
+    // multiplied there by zeros of T, are zeroed.  T is lower triangular, so
+    // tile (I, J) takes the k <= 16 J + 15 of dAinv's rows.
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int id = 2 * wave + u, I = id / 4, J = id % 4;
-        const f32x4 y = mma_tile<T>(sDA + 16 * I * LDC, LDC, sT + 16 * J * LDC, LDC, C, lane, zero4());
+        const int id = LOWER[2 * wave + u], I = id / 4, J = id % 4;
+        f32x4 y = zero4();
+        if (J <= I)
+            y = J < 2 ? mma_tile<T>(sDA + 16 * I * LDC, LDC, sT + 16 * J * LDC, LDC, 32, lane, zero4())
+                      : mma_tile<T>(sDA + 16 * I * LDC, LDC, sT + 16 * J * LDC, LDC, C, lane, zero4());
         store_acc(sY + 16 * I * LDC + 16 * J, LDC, lane, y);
     }
     // Ke = K 2^{G_e - G} (e the last token of the row's block), Ql = Q 2^{G - G_s},
@@ -506,13 +530,14 @@ __global__ __launch_bounds__(KDA_THREADS) void bwd_local_kda_kernel(BwdLocalLaun
     // ================= phase D: dA = -T^T Y, strictly lower
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int id = 2 * wave + u, I = id / 4, J = id % 4;
+        const int id = LOWER[2 * wave + u], I = id / 4, J = id % 4;
         if (J > I) continue;   // upper tiles are never read
         f32x4 x = zero4();
 #pragma unroll
         for (int k0 = 0; k0 < C; k0 += KS)
-            x = M::mma(M::load_t(sT + k0 * LDC + 16 * I, LDC, lane),
-                       M::load_t(sY + k0 * LDC + 16 * J, LDC, lane), x);
+            if (k0 + KS > 16 * I)   // T^T's rows i take the m >= i
+                x = M::mma(M::load_t(sT + k0 * LDC + 16 * I, LDC, lane),
+                           M::load_t(sY + k0 * LDC + 16 * J, LDC, lane), x);
         const int jc = 16 * J + acc_col(lane);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
