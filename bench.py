@@ -69,7 +69,7 @@ def prefill_bytes(spec, n_seqs):
     return intra, scan
 
 
-KERNEL_SOURCES = {"fused_kernel": ["k_fused.hip", "gdn_device.hpp"],
+KERNEL_SOURCES = {"fused_kernel": ["k_fused.hip", "k_fused_body.hpp", "gdn_device.hpp"],
                   "intra_kernel": ["k_intra.hip", "gdn_device.hpp"],
                   "scan_kernel": ["k_scan.hip", "gdn_device.hpp"],
                   "step_kernel": ["k_step.hip", "gdn_device.hpp"],
@@ -83,7 +83,7 @@ KERNEL_SOURCES = {"fused_kernel": ["k_fused.hip", "gdn_device.hpp"],
                   "kda_bwd_state_scan_kernel": ["k_scan.hip", "gdn_device.hpp"],
                   "kda_bwd_scan_kernel": ["k_bwd.hip", "gdn_device.hpp"],
                   "kda_bwd_local_kernel": ["k_bwd_kda.hip", "gdn_device.hpp"],
-                  "varlen_fused_kernel": ["k_fused.hip", "gdn_device.hpp"]}
+                  "varlen_fused_kernel": ["k_fused.hip", "k_fused_body.hpp", "gdn_device.hpp"]}
 
 
 def measured_traffic(kernel):
@@ -439,10 +439,11 @@ def bench_variants(args, gdn):
     """The prefill workload (B=4, T=4096, H=16, d=128, bf16) with each input
     option of the forward: raw gate and beta logits activated inside the
     kernel, beta in (0, 2), two value heads per q/k head (16 value heads on 8
-    q/k heads) and q/k L2 normalisation (which runs as two stages).  Whole
-    calls, timed with an event pair around back-to-back calls of the C entry
-    point on arguments marshalled once (the binding's per-call checks would
-    otherwise take longer than the kernel)."""
+    q/k heads) and q/k L2 normalisation; then the same workload at the other
+    head sizes the single-pass kernel is built for, (K, V) = (64, 64),
+    (128, 64), (64, 128).  Whole calls, timed with an event pair around
+    back-to-back calls of the C entry point on arguments marshalled once (the
+    binding's per-call checks would otherwise take longer than the kernel)."""
     import ctypes
     from gated_delta_rule_14_amd import _binding as B
     lib = gdn.load()
@@ -481,6 +482,20 @@ def bench_variants(args, gdn):
                 lib.gdn_chunk_fwd_act(*cargs)
             first = False
         out[name + "_us"] = 1e6 * events_time(lambda: lib.gdn_chunk_fwd_act(*cargs), reps)
+    for K, V in ((64, 64), (128, 64), (64, 128)):
+        sp = gdn_synth.prefill_spec(1, K=K, V=V)
+        log("generating", sp.name, "at K=%d V=%d" % (K, V))
+        dk = gdn_synth.make_prefill(sp, 1)
+        xk = {n: dk[n].cuda() for n in ("q", "k", "v", "beta", "g", "h0")}
+        ok, htk = torch.empty_like(xk["v"]), torch.empty_like(xk["h0"])
+        desc = gdn.fwd_desc(xk["q"], xk["v"], "scalar", sp.chunk, dk["scale"])
+        nbytes = gdn.workspace_bytes(desc)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        cargs = (ctypes.byref(desc), None, *(B._ptr(xk[n]) for n in ("q", "k", "v", "beta", "g", "h0")),
+                 None, B._ptr(ok), B._ptr(htk), B._ptr(ws), nbytes, B._stream(None))
+        B._check(lib.gdn_chunk_fwd_act(*cargs))
+        settle(lambda: lib.gdn_chunk_fwd_act(*cargs), args.settle_s)
+        out["head_k%d_v%d_us" % (K, V)] = 1e6 * events_time(lambda: lib.gdn_chunk_fwd_act(*cargs), reps)
     log("input options: " + ", ".join("%s %.1f us" % (n[:-3], t) for n, t in out.items()
                                      if n.endswith("_us")))
     return out

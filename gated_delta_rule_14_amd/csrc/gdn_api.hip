@@ -576,7 +576,7 @@ gdn_status gdn_chunk_fwd_noalloc(const gdn_fwd_desc* d, const gdn_activation* ac
     if (!fused_path(d, act.flags))
         return fail(GDN_ERR_UNSUPPORTED,
                     "gdn_chunk_fwd_noalloc runs the single-pass kernel only (bf16 q/k/v, scalar "
-                    "gate, K = V = 128, chunk 64)");
+                    "gate, K and V each 64 or 128, chunk 64)");
     if (packed && d->num_seqs > NOALLOC_MAX_SEQS)
         return fail(GDN_ERR_UNSUPPORTED, "gdn_chunk_fwd_noalloc takes at most %lld packed sequences "
                     "(got %lld)", (long long)NOALLOC_MAX_SEQS, (long long)d->num_seqs);

@@ -160,8 +160,8 @@ struct GvaSumLaunch {
     hipStream_t stream;
 };
 
-// The fused forward (bf16 q/k/v, scalar gate, K = V = 128, C = 64): one
-// kernel per call, no per-chunk intermediates in HBM.
+// The fused forward (bf16 q/k/v, scalar gate, K and V each 64 or 128, C = 64):
+// one kernel per call, no per-chunk intermediates in HBM.
 struct FusedLaunch {
     Act act;
     int64_t Hq = 0;         // q/k heads (value heads H are a multiple of it)

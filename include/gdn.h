@@ -175,8 +175,8 @@ gdn_status gdn_seqlens_status_offset(const gdn_fwd_desc *d, const gdn_activation
  * clears it before the call (e.g. allocates the workspace zeroed) and reads
  * it once the stream has reached the call.  d (with *act, NULL allowed) must
  * describe a shape that runs the single-pass kernel (bf16, scalar gate,
- * K = V = 128, chunk 64); other shapes run the two-stage route, which has no
- * such waits, and give GDN_ERR_UNSUPPORTED.
+ * K and V each 64 or 128, chunk 64); other shapes run the two-stage route,
+ * which has no such waits, and give GDN_ERR_UNSUPPORTED.
  */
 gdn_status gdn_sync_status_offset(const gdn_fwd_desc *d, const gdn_activation *act,
                                   size_t *offset);
@@ -193,8 +193,8 @@ const char *gdn_last_error(void);
 /*
  * Bytes of device workspace gdn_chunk_fwd needs for the shape *d (written to
  * *bytes).  A descriptor with num_seqs > 0 describes packed input.
- *   - bf16 inputs, scalar gate, K = V = 128, chunk 64 (the single-pass
- *     kernel): the per-sequence table of packed input, 16 bytes per
+ *   - bf16 inputs, scalar gate, K and V each 64 or 128, chunk 64 (the
+ *     single-pass kernel): the per-sequence table of packed input, 16 bytes per
  *     sequence and one more record rounded up to 256 (256 bytes without
  *     cu_seqlens), then 256 bytes that hold the synchronisation status word
  *     of gdn_sync_status_offset.
@@ -216,8 +216,8 @@ gdn_status gdn_chunk_fwd_workspace_act(const gdn_fwd_desc *d, const gdn_activati
  * forward Steps 1-5; signature of its chunk_delta_rule_fwd: q, k, v, beta,
  * scale, initial_state, output_final_state, cu_seqlens).
  *
- * bf16 inputs with the scalar gate at K = V = 128, chunk 64 run as one
- * kernel that builds each chunk's intra-chunk products on chip while it
+ * bf16 inputs with the scalar gate, K and V each 64 or 128, chunk 64 run as
+ * one kernel that builds each chunk's intra-chunk products on chip while it
  * carries the state; every other shape runs gdn_chunk_intra then
  * gdn_chunk_scan.  The two routes compute the same quantities in a
  * different order: they agree to rounding, not bit for bit.
@@ -268,9 +268,9 @@ gdn_status gdn_chunk_fwd_act(const gdn_fwd_desc *d, const gdn_activation *act,
  * gdn_chunk_fwd_act without a workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  It runs the single-pass kernel only:
- * d must describe bf16 q/k/v, the scalar gate, K = V = 128, chunk 64, and
- * at most GDN_NOALLOC_MAX_SEQS packed sequences; other shapes give
- * GDN_ERR_UNSUPPORTED before anything is launched.  Arguments, layouts and
+ * d must describe bf16 q/k/v, the scalar gate, K and V each 64 or 128,
+ * chunk 64, and at most GDN_NOALLOC_MAX_SEQS packed sequences; other shapes
+ * give GDN_ERR_UNSUPPORTED before anything is launched.  Arguments, layouts and
  * results are those of gdn_chunk_fwd_act (act may be NULL).
  * Its scratch (the per-sequence records of packed input) is a device array
  * inside the library, about 66 KB, one per GPU, held until the process

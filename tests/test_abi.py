@@ -73,7 +73,7 @@ def test_workspace_size_and_layout(lib):
     offs = [L.gcum, L.w, L.u, L.qs, L.ks, L.aqk, L.ainv, L.chunks, L.total]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     # the two-stage path (here fp32) needs the whole layout; the fused path
-    # (bf16, scalar gate, K = V = 128) only the per-sequence records
+    # (bf16, scalar gate, K and V each 64 or 128) only the per-sequence records
     assert gdn.workspace_bytes(_desc(qkv_dtype=0)) == gdn.workspace_layout(_desc(qkv_dtype=0)).total
     assert gdn.workspace_bytes(_desc(gate=1)) == gdn.workspace_layout(_desc(gate=1)).total
     # (then 256 bytes for the synchronisation status word)
@@ -287,7 +287,7 @@ def test_sync_status_offset(lib):
     assert where(d, gdn.Activation(8, None, None)) == 0 and off.value == 256
     assert where(_desc(qkv_dtype=0)) == 4                       # two stages: no waits
     assert where(_desc(gate=1)) == 4
-    assert where(_desc(key_dim=64)) == 4
+    assert where(_desc(key_dim=64)) == 0 and off.value == 256    # the single-pass kernel at K = 64 too
     assert lib.gdn_sync_status_offset(ctypes.byref(d), None, None) == 1
     assert gdn.sync_status_offset(d) == 256 and gdn.sync_status_offset(_desc(gate=1)) is None
 

@@ -49,7 +49,7 @@ def test_gva_fused_packed_with_activation(gpu_lib):
 
 
 @pytest.mark.parametrize("dt,cid,K,V,m", [("f32", 1, 64, 64, 2), ("bf16", 3, 64, 128, 2),
-                                          ("bf16", 1, 128, 64, 4)])
+                                          ("bf16", 3, 128, 64, 4)])
 def test_gva_two_stage(gpu_lib, dt, cid, K, V, m):
     _gva_prefill(gdn_synth.prefill_spec(cid, dtype=dt, B=2, T=150, H=4, K=K, V=V, h0_std=0.02),
                  m, 43)

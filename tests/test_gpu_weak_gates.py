@@ -32,8 +32,8 @@ def _fwd(spec, seed):
 @pytest.mark.parametrize("dt,K,V", [("bf16", 128, 128), ("bf16", 64, 64), ("bf16", 128, 64),
                                     ("f32", 128, 128), ("f32", 64, 64)])
 def test_weak_gates_routes(gpu_lib, dt, K, V):
-    """bf16 K = V = 128 is the single-pass kernel; the other shapes and fp32
-    the two-stage route.  600 tokens: ten chunks, the last one ragged."""
+    """bf16 runs the single-pass kernel at each of these head sizes, fp32 the
+    two-stage route.  600 tokens: ten chunks, the last one ragged."""
     _fwd(gdn_synth.prefill_spec(1, dtype=dt, B=2, T=600, H=2, K=K, V=V, A_range=WEAK), 21)
 
 

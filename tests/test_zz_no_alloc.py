@@ -55,6 +55,8 @@ def test_noalloc_matches_chunk_fwd(gpu_lib):
     _case(big, 150, want_oracle=True)
     _case(small, 151)
     _case(gdn_synth.prefill_spec(1, B=2, T=200, H=2), 152)
+    # the other head sizes run the same entry point (K = V = 64 here)
+    _case(gdn_synth.prefill_spec(2, H=2, K=64, V=64, rand_lengths=None, lengths=(130, 5)), 153)
 
 
 def test_noalloc_refuses_other_shapes(gpu_lib):
@@ -62,7 +64,7 @@ def test_noalloc_refuses_other_shapes(gpu_lib):
     from gated_delta_rule_14_amd import _binding as B
     lib = gdn.load()
     fake = ctypes.c_void_p(1 << 20)
-    for kw in (dict(qkv_dtype=0), dict(gate=1), dict(key_dim=64), dict(chunk=32)):
+    for kw in (dict(qkv_dtype=0), dict(gate=1), dict(key_dim=96), dict(chunk=32)):
         a = dict(batch=1, seq_len=64, num_heads=2, key_dim=128, value_dim=128, num_seqs=0, chunk=64,
                  qkv_dtype=1, gate=0, scale=0.088)
         a.update(kw)
