@@ -46,8 +46,9 @@ constexpr int o_D = o_A + 2 * SZ_A;
 constexpr int o_DT = o_D + 4 * SZ_DB;
 constexpr int o_F = o_DT + 4 * SZ_DT;        // signal words
 constexpr int BYTES = o_F + 64;
-// the q/k L2-normalising instantiation only: per product wave (the key wave
-// and the three query waves), |k|^2 and |q|^2 of the chunk's tokens
+// the q/k L2-normalising instantiation only: per product wave, squared
+// norms of the chunk's tokens: the key wave's |k|^2 (read by the query waves
+// too, once signalled) and each query set's |q|^2 (in [64, 128))
 constexpr int SZ_NRM = 128 * 4;
 constexpr int o_NRM = BYTES;
 constexpr int BYTES_L2 = o_NRM + 4 * SZ_NRM;
@@ -203,6 +204,8 @@ struct Ctx {
     __device__ __forceinline__ lds_int* tflag() const { return (lds_int*)(sm + o_F); }
     __device__ __forceinline__ lds_int* dflag() const { return (lds_int*)(sm + o_F) + 1; }
     __device__ __forceinline__ lds_int* lflag() const { return (lds_int*)(sm + o_F) + 5; }
+    // q/k L2 normalisation: the key wave's |k|^2 of the chunk are in nrm(0)
+    __device__ __forceinline__ lds_int* nflag() const { return (lds_int*)(sm + o_F) + 6; }
 
     __device__ __forceinline__ bool valid(int c) const { return c >= 0 && c < nch; }
     __device__ __forceinline__ int rows(int c) const {
@@ -394,6 +397,7 @@ __device__ __forceinline__ void role_keys(const Ctx& x) {
 #pragma unroll
                 for (int I = 0; I < 4; ++I) diag_to(nk + 16 * I, sd[I], lane);
                 own_lds_sync();
+                signal(x.nflag(), c + 1);   // the query waves read them too
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
                     rkr[I] = l2_rsq(nk[16 * I + m]);
@@ -476,23 +480,18 @@ __device__ __forceinline__ void role_queries(const Ctx& x) {
                     if (needq[J]) qf[J][kk] = ld16(qb + kq_off(16 * J + m, 4 * kk + g));
                 }
             __builtin_amdgcn_sched_barrier(0);
-            // q/k L2 normalisation: 1/|q| of the rows of the blocks' I and
-            // 1/|k| of the columns of their J, from Gram diagonals
+            // q/k L2 normalisation: 1/|q| of the rows of the blocks' I from
+            // the diagonals of their Q Q^T blocks, 1/|k| of the columns of
+            // their J from the key wave's K K^T diagonals
             constexpr bool l2 = L2;
             float rqr[4] = {1.f, 1.f, 1.f, 1.f};
             float4 rkc[4];
 #pragma unroll
             for (int J = 0; J < 4; ++J) rkc[J] = make_float4(1.f, 1.f, 1.f, 1.f);
             if constexpr (l2) {
-                float* nq = x.nrm(1 + SET);   // [0, 64): |k|^2, [64, 128): |q|^2
+                float* nq = x.nrm(1 + SET);   // [64, 128): |q|^2
 #pragma unroll
                 for (int J = 0; J < 4; ++J) {
-                    if (needk[J]) {
-                        f32x4 gk = zero4();
-#pragma unroll
-                        for (int kk = 0; kk < NKK; ++kk) gk = mma32(kf[J][kk], kf[J][kk], gk);
-                        diag_to(nq + 16 * J, gk, lane);
-                    }
                     if (needq[J]) {
                         f32x4 gq = zero4();
 #pragma unroll
@@ -501,9 +500,11 @@ __device__ __forceinline__ void role_queries(const Ctx& x) {
                     }
                 }
                 own_lds_sync();
+                wait_for(x.nflag(), c + 1, x.sync_status);
+                const float* nk = x.nrm(0);
 #pragma unroll
                 for (int J = 0; J < 4; ++J) {
-                    if (needk[J]) rkc[J] = l2_rsq4(ldf4(nq + 16 * J + 4 * g));
+                    if (needk[J]) rkc[J] = l2_rsq4(ldf4(nk + 16 * J + 4 * g));
                     if (needq[J]) rqr[J] = l2_rsq(nq[64 + 16 * J + m]);
                 }
                 // the set with every query block: 1/|q| into the output's scale gamma
