@@ -100,3 +100,15 @@ def test_routes_agree(gpu_lib, K, V):
     check(d, o, ht, o_ref, ht_ref)
     check(d, o2, ht2, o_ref, ht_ref)
     check(d, o2, ht2, o.double().cpu().numpy(), ht.double().cpu().numpy())
+
+
+@pytest.mark.parametrize("K,V", HEADS)
+def test_no_state_in_or_out(gpu_lib, K, V):
+    """No initial state (zeros) and no final state requested: o alone, ragged."""
+    spec = gdn_synth.prefill_spec(1, B=2, T=150, H=2, K=K, V=V, h0_std=None)
+    d = gdn_synth.make_prefill(spec, 156)
+    print("case: no h0, no ht", spec, flush=True)
+    o, ht = run_gpu(d, output_final_state=False)
+    assert ht is None
+    o_ref, ht_ref = run_oracle(d)
+    print("relative error: o %.2e" % check(d, o, None, o_ref, None)[0], flush=True)
