@@ -12,7 +12,11 @@ constexpr int NKK = K / 32, NST = K / 16, GPR = K / 8;
 
 // ---------------------------------------------------------------- LDS layout
 // K, Q: 64 rows of 2K bytes; the 16-byte group holding columns 8q..8q+7 of
-// row r sits at position q ^ (2r mod K/8).  V (the 32-column slice): 64 rows of
+// row r sits at position q ^ (2r mod 16) for K = 128 and q ^ (r & 6) for
+// K = 64, whose 128-byte rows cover half the banks, so rows r and r + 1 sit
+// in different halves and the permutation only has to separate rows of equal
+// parity (measured: 36 % of LDS cycles in bank conflicts with q ^ (2r mod 8),
+// 22 % with this one, as at K = 128).  V (the 32-column slice): 64 rows of
 // 64 bytes, group q of row r at q ^ 2((r/4)%2).  Pitches and permutations are
 // the ones measured free of LDS bank conflicts on gfx950 for the reads made
 // here: 16-byte row fragments need rows an odd multiple of 32 bytes apart
@@ -103,7 +107,7 @@ __device__ __forceinline__ u32x4 ld16(const char* p) { return *reinterpret_cast<
 __device__ __forceinline__ u32x2 ld8(const char* p) { return *reinterpret_cast<const u32x2*>(p); }
 __device__ __forceinline__ float4 ldf4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
-__device__ __forceinline__ int kq_sw(int r) { return (2 * r) & (K / 8 - 2); }
+__device__ __forceinline__ int kq_sw(int r) { return K == 128 ? (2 * r) & 14 : r & 6; }
 // byte offset of 16-byte group `grp` of row r of a K/Q slot
 __device__ __forceinline__ int kq_off(int r, int grp) { return r * 2 * K + ((grp ^ kq_sw(r)) << 4); }
 
