@@ -460,7 +460,10 @@ constexpr int BLOCAL_THREADS = 512;
 template <typename T, int K, int V>
 struct LocalSmem {
     static constexpr int C = 64, NW = BLOCAL_THREADS / 64;
-    static constexpr int P = 16 / sizeof(T);
+    // rows padded by 32 bytes (measured on the B=4, T=4096, H=16, d=128
+    // backward: 16 bytes cost 10 us more per call, 48 bytes 5 us; the results
+    // are the same)
+    static constexpr int P = 32 / sizeof(T);
     static constexpr int LDK = K + P, LDV = V + P, LDC = C + P;
     static constexpr int LDX = (K > V ? K : V) + P;
     static constexpr int LDN = LDV > LDC ? LDV : LDC;
