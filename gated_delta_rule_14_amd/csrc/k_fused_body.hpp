@@ -456,12 +456,15 @@ __device__ __forceinline__ void role_keys(const Ctx& x) {
 
 // waves 7, 4, 5: Aqk = scale 2^{G_i - G_j} q_i.k_j (j <= i), as the state
 // pass's 16x16x32 operand fragments.  Set 0 takes the diagonal blocks and
-// (1,0), set 1 (2,0) and (2,1), set 2 (3,0), (3,1) and (3,2).
+// (1,0), set 1 (2,0) and (2,1), set 2 (3,0), (3,1) and (3,2).  With q/k L2
+// normalisation each set also forms the Q Q^T diagonal blocks of its block
+// rows, so the sets split by block row instead (set 0 rows 0-1, set 1 row 2,
+// set 2 row 3) and each folds 1/|q| of its own rows into the output's scale.
 template <int SET, bool L2>
 __device__ __forceinline__ void role_queries(const Ctx& x) {
-    constexpr int NB = SET == 0 ? 5 : SET == 1 ? 2 : 3;
-    constexpr int BI[3][5] = {{0, 1, 2, 3, 1}, {2, 2, 0, 0, 0}, {3, 3, 3, 0, 0}};
-    constexpr int BJ[3][5] = {{0, 1, 2, 3, 0}, {0, 1, 0, 0, 0}, {0, 1, 2, 0, 0}};
+    constexpr int NB = L2 ? (SET == 2 ? 4 : 3) : SET == 0 ? 5 : SET == 1 ? 2 : 3;
+    constexpr int BI[3][5] = {{0, 1, L2 ? 1 : 2, 3, 1}, {2, 2, 2, 0, 0}, {3, 3, 3, 3, 0}};
+    constexpr int BJ[3][5] = {{0, 1, L2 ? 0 : 2, 3, 0}, {0, 1, 2, 0, 0}, {0, 1, 2, 3, 0}};
     const int lane = x.lane, m = lane & 15, g = lane >> 4;
     for (int j = -2; j < x.nch; ++j) {
         const int c = j + 1;
@@ -511,8 +514,8 @@ __device__ __forceinline__ void role_queries(const Ctx& x) {
                     if (needk[J]) rkc[J] = l2_rsq4(ldf4(nk + 16 * J + 4 * g));
                     if (needq[J]) rqr[J] = l2_rsq(nq[64 + 16 * J + m]);
                 }
-                // the set with every query block: 1/|q| into the output's scale gamma
-                if (SET == 0) x.gate(c, GA_OUT)[lane] *= l2_rsq(nq[64 + lane]);
+                // 1/|q| of this set's rows into the output's scale gamma
+                if (needq[lane >> 4]) x.gate(c, GA_OUT)[lane] *= l2_rsq(nq[64 + lane]);
             }
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
